@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Throughput of the SAD hot path on one MI355X.
+
+One step = one fit iteration over the whole image: one propagation pass of the
+candidate map (sad_topk_propagate), the render forward (sad_render_fwd), the
+render backward with the per-tile hash reduction (sad_render_bwd) and Adam
+(sad_adam_step), K = 8.  Default workload: the Kodak-shaped fit, 768x512 RGB
+float32, N = 50,000 sites, 4 injected candidates per pixel, cold start with the
+coarse-to-fine jump schedule 512, 256, ..., 1, 1, ...  Inputs are synthetic and
+seeded (sites: uniform positions, colours U[0,1]^3, r U[0,2] px, a N(0,0.5),
+direction U[0,pi), log tau U[2,5]; target: hard render of a second seeded site
+set plus N(0, 0.01) noise).
+
+The K timed steps replay one HIP graph holding the K iterations (the launches of
+a step depend only on the step index, so the whole fit is captured once); the
+state is reset to the cold start before the timed replay.  Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(P, N):
+    """Compulsory HBM bytes per launch (each tensor byte read once, written once).
+
+    propagate: map in + map out (64 B/px) + site geometry x,y,r,dir,a (24 B/site)
+    forward:   map (32 B/px) + image out (12 B/px) + all ten site fields (40 B/site)
+    backward:  map (32 B/px) + target (12 B/px) + site fields (40 B/site) + one
+               read-modify-write flush of 11 accumulators (44 B/site)
+    adam:      params, m, v read and written (240 B/site) + 10 grad planes read
+               and zeroed (80 B/site)
+    """
+    return {
+        "propagate": 64 * P + 24 * N,
+        "fwd": 44 * P + 40 * N,
+        "bwd": 44 * P + 84 * N,
+        "adam": 320 * N,
+    }
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def make_inputs(wl, dev):
+    import torch
+
+    import soft_voronoi_render_amd as sad
+    import synth
+
+    W, H, n = wl.W, wl.H, wl.n_sites
+    S = synth.random_sites(n, W, H, synth.SEED_MODEL, wl.capacity)
+    S2 = synth.random_sites(n, W, H, synth.SEED_TARGET_SITES)
+    noise = synth.pixel_noise(W, H, synth.SEED_NOISE)
+    # target: hard (argmin) render of the second site set = colour of the first
+    # entry of its exact top-K map (brute force on the GPU), plus noise
+    S2_d = torch.from_numpy(S2).to(dev)
+    ex = sad.new_map(W, H, dev)
+    sad.topk_exact(S2_d, n, ex, W, H)
+    first = ex[:, :, 0].long()
+    col = S2_d[4:7].t()  # [n][3]
+    tgt = torch.where((first >= 0)[..., None], col[first.clamp(min=0)], torch.zeros(1, device=dev))
+    tgt = (tgt + torch.from_numpy(noise).to(dev)).contiguous()
+    return S, tgt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="kodak768")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of one graph replay")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the SAD hot path here is built and measured on a single "
+              "MI355X (multi-GPU banding is a design note, not part of this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import soft_voronoi_render_amd as sad
+    import synth
+
+    sad.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    W, H, N, P = wl.W, wl.H, wl.n_sites, wl.P
+    S0, tgt = make_inputs(wl, dev)
+    S0_d = torch.from_numpy(S0).to(dev)
+    fit = sad.Fitter(S0_d.clone(), N, tgt, W, H, n_inject=wl.n_inject, seed=synth.SEED_INJECT)
+    stream = torch.cuda.current_stream()
+
+    def reset():
+        fit.sites.copy_(S0_d)
+        fit.m.zero_()
+        fit.v.zero_()
+        fit.grad.zero_()
+        fit.maps[0].fill_(-1)
+        fit.maps[1].fill_(-1)
+        fit.cur = 0
+        fit.it = 0
+        fit.loss.zero_()
+
+    # warm-up (untimed): the first iterations of the fit
+    for _ in range(args.warmup):
+        fit.step()
+    torch.cuda.synchronize()
+
+    # timed region: K iterations from the cold start
+    reset()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                fit.step()
+        reset()
+        torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(args.steps):
+            fit.step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1)
+    ms_per_step = ms / args.steps
+    value = P * args.steps / (ms * 1e-3) / 1e6
+
+    # quality after the fit: loss of one more iteration
+    fit.it = args.steps
+    fit.loss.zero_()
+    fit.step()
+    torch.cuda.synchronize()
+    mse = fit.loss.item() / (3 * P)
+    psnr = 10 * np.log10(1.0 / max(mse, 1e-30))
+    # recall of the maintained map against the exact top-K (brute force on the GPU)
+    ex = sad.new_map(W, H, dev)
+    sad.topk_exact(fit.sites, N, ex, W, H)
+    cur = fit.cand
+    a, _ = torch.sort(cur.view(-1, 8), dim=1)
+    b, _ = torch.sort(ex.view(-1, 8), dim=1)
+    exact_frac = (a == b).all(dim=1).float().mean().item()
+
+    # per-kernel average launch duration: R back-to-back launches of each kernel
+    # on the fitted state, one graph replay bracketed by events on this stream
+    kb = algorithmic_bytes(P, N)
+    kdur = {}
+    R = args.kernel_reps
+    launches = {
+        "propagate": lambda i: sad.topk_propagate(fit.sites, N, fit.maps[i % 2], fit.maps[1 - i % 2], W, H, 1,
+                                                  1000 + i, synth.SEED_INJECT, wl.n_inject),
+        "fwd": lambda i: sad.render_fwd(fit.sites, N, fit.cand, W, H, fit.rgb),
+        "bwd": lambda i: sad.render_bwd(fit.sites, N, fit.cand, fit.target, W, H, fit.grad, fit.loss),
+        "adam": lambda i: sad.adam_step(fit.sites, fit.m, fit.v, fit.grad, N, 500 + i, P, W, H, fit.adam),
+    }
+    for name, fn in launches.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kdur[name] = e0.elapsed_time(e1) / R * 1e-3  # s per launch
+    dominant = max(kdur, key=kdur.get)
+    achieved = kb[dominant] / kdur[dominant] / 1e9
+    kernels = {k: {"us": round(kdur[k] * 1e6, 3), "GBps": round(kb[k] / kdur[k] / 1e9, 1),
+                   "hbm_frac": round(kb[k] / kdur[k] / 1e9 / HBM_PEAK_GBS, 4)} for k in kdur}
+
+    out = {
+        "metric": "Mpixel-iters/s (propagate+fwd+bwd+Adam, K=8) and % of HBM peak",
+        "value": round(value, 2),
+        "unit": "Mpixel-iters/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "W": W, "H": H, "n_sites": N, "K": 8, "n_inject": wl.n_inject,
+            "schedule": "cold start, jumps B/2..1 then 1", "graph": graph is not None,
+            "hbm_frac_whole_step": round(sum(kb.values()) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "psnr_db_after": round(float(psnr), 3), "exact_top8_fraction_after": round(exact_frac, 4),
+            "kernels": kernels,
+        },
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, S0, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, S0, budget_s):
+    """The oracle's own iteration (propagate, forward, backward, Adam) on the same
+    sites, timed on the host cores, for as many iterations as fit the budget."""
+    import oracle
+    import synth
+
+    oracle.build(force=False)
+    cores = os.cpu_count() or 1
+    oracle.set_threads(cores)
+    W, H, N, P = wl.W, wl.H, wl.n_sites, wl.P
+    S = S0.copy()
+    tgt = (synth.pixel_noise(W, H, 99, 0.25) + 0.5).astype(np.float32)
+    cand = synth.empty_map(W, H)
+    params = S.astype(np.float64)
+    m = np.zeros((10, S.shape[1]))
+    v = np.zeros((10, S.shape[1]))
+    grad = np.zeros((11, S.shape[1]))
+    lr = np.array([0.1, 0.1, 0.02, 0.05, 0.01, 0.01, 0.01, 0.02, 0.02, 0.02])
+    sched = oracle.jump_schedule(W, H, 10_000)
+    it, t_used = 0, 0.0
+    while t_used < budget_s and it < 10_000:
+        t0 = time.perf_counter()
+        S32 = params.astype(np.float32)
+        cand = oracle.propagate(S32, N, cand, W, H, sched[it], it, synth.SEED_INJECT, wl.n_inject)
+        oracle.render_fwd(params, N, cand, W, H)
+        oracle.render_bwd(params, N, cand, tgt, W, H, grad=grad)
+        oracle.adam_step(params, m, v, grad, N, it + 1, P, lr, 0.9, 0.999, 1e-8, W, H)
+        t_used += time.perf_counter() - t0
+        it += 1
+    return {"value": round(P * it / t_used / 1e6, 4), "unit": "Mpixel-iters/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {it} iterations of the {wl.name} fit ({W}x{H}, N={N}), same sites; target replaced "
+                      f"by seeded noise (the oracle's cost does not depend on target values); {t_used:.1f} s",
+            "cpu": cpu_model()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * sad.h -- C ABI of libsad, the MI355X (gfx950) hot path of Soft Anisotropic
+ * Diagrams (SAD): per-pixel top-K candidate maintenance, the temperature-softmax
+ * render, its analytic backward, and Adam.
+ *
+ * Sources (the pages the method is described on):
+ *   [SUM]   paperlayer.ai summary of arXiv:2604.21984v2, sections 3-5 and Appendix B
+ *   [NOTE]  woaixuexisr.github.io reading note, "Key designs" 1-4
+ *   [PROJ]  luckyiyi.github.io/SAD project page, "Method"
+ *   [PRESS] 69574.cn article, sections 3-5
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership.  The caller owns every buffer.  The library allocates no memory and
+ *   keeps no state between calls, so calls are reentrant.
+ * Pointers.  Arguments named `sites`, `cand*`, `out_rgb`, `target`, `grad`, `m`,
+ *   `v` and `loss_sum` are DEVICE pointers (HBM of the current HIP device).
+ *   `cfg` is a HOST pointer, read before the call returns.
+ * Streams.  Device work is enqueued asynchronously on `stream` (a hipStream_t
+ *   passed as void*; NULL = the legacy default stream).  A return of SAD_OK means
+ *   the launch was accepted, not that the kernel finished.
+ * Errors.  Every call returns SAD_OK (0) or a negative sad_status.  Arguments
+ *   are checked on the host before anything is launched; on an argument error
+ *   nothing is launched and no buffer is touched.  A launch failure reported by
+ *   the HIP runtime returns SAD_ERR_DEVICE.  No C++ exception crosses the ABI.
+ *
+ * Layouts
+ * -------
+ * sites : float [SAD_NPARAM][stride] -- ten planes ("structure of arrays"), the
+ *         ten float32 values per site of [SUM] B.2, in the field order of
+ *         [PRESS] 5: x, y, log_tau, r, R, G, B, dir_x, dir_y, a.  Positions and r
+ *         are in pixels; tau = exp(log_tau).  Slots [0, n_slots) are in use; a slot
+ *         whose x < 0 is inactive and every kernel ignores it ([SUM] B.2, B.5).
+ * cand  : uint32 [H][W][SAD_K] -- per-pixel candidate site IDs ([SUM] B.2 keeps
+ *         K = 8 IDs per pixel in two 4-channel textures; here one 32-byte record
+ *         per pixel), SAD_INVALID marks an empty entry.  16-byte aligned.  Lists
+ *         written by this library hold distinct IDs in ascending (d, ID) order.
+ * images: float [H][W][3] (RGB, linear).
+ * grad  : float [SAD_NACC][stride] -- ten gradient planes in the site order, then
+ *         the removal delta ([SUM] B.4: 11 accumulators per site).
+ * m, v  : float [SAD_NPARAM][stride] Adam moments.
+ * Pixel (col,row) is evaluated at (col+0.5, row+0.5) px ([SUM] B.3 evaluates at
+ * centred cells).  Limits: 1 <= W, H <= 65535 (W or H = 0 is an empty image: a
+ * no-op returning SAD_OK after the scalar arguments are checked; its pointers
+ * may then be NULL); 0 <= n_slots <= stride.
+ *
+ * Score ([NOTE] design 1, [PROJ] "Method"):
+ *   d(x,i) = s * ||x - p_i||_{G_i} - s * r_i,  s = 1 / max(H, W),
+ *   G_i = e^{a_i} u u^T + e^{-a_i} v v^T,  u = dir/|dir| (u = (1,0) if |dir|^2 < 1e-30),
+ *   v = (-u_y, u_x), so det G_i = 1 ([SUM] section 4).
+ */
+#ifndef SAD_H
+#define SAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAD_ABI_VERSION 1
+#define SAD_K 8
+#define SAD_INVALID 0xffffffffu
+#define SAD_NPARAM 10
+#define SAD_NACC 11
+#define SAD_MAX_INJECT 16
+#define SAD_MAX_DIM 65535
+
+enum sad_status {
+    SAD_OK = 0,
+    SAD_ERR_ARG = -1,           /* a size, count or pointer argument is invalid        */
+    SAD_ERR_ALIGN = -2,         /* a pointer is not aligned as its layout requires     */
+    SAD_ERR_DEVICE = -3,        /* the HIP runtime rejected a launch                    */
+    SAD_ERR_CAPACITY = -4,      /* reserved: a result would not fit the given capacity */
+    SAD_ERR_UNIMPLEMENTED = -5  /* reserved                                             */
+};
+
+enum sad_param { SAD_X, SAD_Y, SAD_LOGTAU, SAD_R, SAD_CR, SAD_CG, SAD_CB, SAD_DIRX, SAD_DIRY, SAD_A };
+
+/* Adam hyper-parameters: one learning rate per site parameter, in site order. */
+typedef struct sad_adam_cfg {
+    float lr[SAD_NPARAM];
+    float beta1, beta2, eps;
+} sad_adam_cfg;
+
+/* SAD_ABI_VERSION of the loaded library. */
+int sad_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *sad_status_string(int status);
+
+/*
+ * sad_topk_propagate -- one propagation pass of the candidate map.
+ * [NOTE] design 3: C~_t(x) = C_{t-1}(x) U P_t(x) U G_t(x), keep the top-K under d;
+ * [SUM] section 4: self plus 4 neighbours at the current jump, plus a small
+ * random set of global IDs; [SUM] B.3 packs the pass index (low 16 bits) and the
+ * jump (high 16 bits) into one word that, with the pixel ID, seeds xorshift.
+ *
+ * For every pixel x the candidates are: its own list in cand_in, the lists of the
+ * pixels x +- (jump, 0) and x +- (0, jump) that lie inside the image, and
+ * `n_inject` IDs drawn as follows (identical on every implementation):
+ *   pw = (jump << 16) | (pass_index & 0xffff);  pix = row*W + col;
+ *   h  = pcg(pcg(pcg(seed) ^ pw) ^ pix)   (pcg: Jarzynski & Olano, JCGT 2020)
+ *   x  = h ? h : 0x9e3779b9;  repeat n_inject times: x = xorshift32(x) (13,17,5);
+ *   id = (uint32)(((uint64)x * n_slots) >> 32).
+ * Sentinels, IDs >= n_slots, inactive sites, non-finite scores and duplicates are
+ * dropped; the K smallest by (d, ID) are written to cand_out in ascending order,
+ * padded with SAD_INVALID.  The pass reads cand_in and writes cand_out (Jacobi).
+ * The host chooses the schedule: jumps B/2, B/4, ..., 1 then 1 ([SUM] section 4).
+ *
+ *   sites     device, [10][stride] float, read-only
+ *   cand_in   device, [H][W][8] uint32, read-only, 16-byte aligned
+ *   cand_out  device, [H][W][8] uint32, written; must not overlap cand_in
+ *   jump      1..65535;  n_inject 0..SAD_MAX_INJECT
+ * Errors: SAD_ERR_ARG (bad sizes, jump, n_inject, NULL, overlapping maps),
+ *         SAD_ERR_ALIGN (cand not 16-byte aligned), SAD_ERR_DEVICE.
+ */
+int sad_topk_propagate(const float *sites, int n_slots, int stride, const uint32_t *cand_in, uint32_t *cand_out,
+                       int W, int H, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream);
+
+/*
+ * sad_topk_exact -- the exact top-K map by brute force over every slot: the list
+ * that propagation approximates ([NOTE] design 3; [SUM] section 4 "Candidate
+ * maintenance").  Used to (re)initialise a map and to measure recall.  Cost
+ * O(W*H*n_slots).  Same output convention as sad_topk_propagate.
+ *   sites device [10][stride] read-only;  cand_out device [H][W][8], written.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
+ */
+int sad_topk_exact(const float *sites, int n_slots, int stride, uint32_t *cand_out, int W, int H, void *stream);
+
+/*
+ * sad_render_fwd -- the temperature-softmax blend of each pixel's list.
+ * [NOTE] design 2, [PROJ] "Method": l_i = -tau_i d_i, w = softmax over the list,
+ * c(x) = sum_i w_i c_i; max-subtracted, invalid IDs skipped, non-finite entries
+ * skipped ([SUM] B.4).  A pixel with no usable entry renders (0,0,0).
+ *   cand device [H][W][8] read-only; out_rgb device [H][W][3] float, written.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
+ */
+int sad_render_fwd(const float *sites, int n_slots, int stride, const uint32_t *cand, int W, int H, float *out_rgb,
+                   void *stream);
+
+/*
+ * sad_render_bwd -- hand-derived gradients of L = sum_x ||c(x) - t(x)||^2 with
+ * the map held fixed ([SUM] section 5 and B.4; [NOTE] design 4), accumulated
+ * (+=) into `grad`.  Per pixel, g = 2(c - t); per usable entry k:
+ *   dc_k = w_k g;  gamma_k = w_k g.(c_k - c);  dlog_tau_k = gamma_k l_k;
+ *   dd_k = -tau_k gamma_k;  then through d = s q - s r to p, r, dir, a.
+ * Plane 10 receives the removal delta ||c_{-k} - t||^2 - ||c - t||^2, c_{-k} the
+ * blend of the other entries renormalised (0 if none carries weight)
+ * ([SUM] B.4-B.5).  Non-finite contributions are dropped.  Contributions are
+ * summed per 16x16 tile in an LDS hash table keyed by site ID (256 slots,
+ * multiplicative hash, at most 8 linear probes, CAS insert) and flushed with one
+ * atomic per site and accumulator per tile; an entry that finds no slot goes
+ * straight to global atomics ([SUM] section 5, B.4).  Float atomics make the
+ * summation order, hence the last bits, vary from run to run.
+ *   target device [H][W][3] read-only; grad device [11][stride] float, +=;
+ *   loss_sum device float or NULL, += sum_x ||c - t||^2.
+ * The caller zeroes `grad` once; sad_adam_step re-zeroes planes 0..9 each step;
+ * plane 10 keeps accumulating until the caller resets it.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
+ */
+int sad_render_bwd(const float *sites, int n_slots, int stride, const uint32_t *cand, const float *target, int W,
+                   int H, float *grad, float *loss_sum, void *stream);
+
+/*
+ * sad_adam_step -- Adam (Kingma & Ba 2015) on the ten site parameters, with the
+ * accumulated gradients divided by the pixel count ([SUM] B.4).  For each slot
+ * i < n_slots with x >= 0 and each parameter j:
+ *   g = grad[j][i] / n_pixels (non-finite -> 0);  m = b1 m + (1-b1) g;
+ *   v = b2 v + (1-b2) g^2;  p -= lr_j (m / (1-b1^step)) / (sqrt(v / (1-b2^step)) + eps);
+ * then x is clamped to [0, W] and y to [0, H].  Planes 0..9 of grad are zeroed
+ * for every slot < n_slots; plane 10 is left alone.  Inactive slots keep p, m, v.
+ *   sites, m, v device [10][stride] float (in/out); grad device [11][stride];
+ *   step >= 1 (global, 1-based); n_pixels >= 1; cfg HOST pointer.
+ * Errors: SAD_ERR_ARG, SAD_ERR_DEVICE.
+ */
+int sad_adam_step(float *sites, float *m, float *v, float *grad, int n_slots, int stride, int step, int n_pixels,
+                  int W, int H, const sad_adam_cfg *cfg, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAD_H */

@@ -1,0 +1,268 @@
+"""soft_voronoi_render_amd -- MI355X (gfx950) hot path of Soft Anisotropic Diagrams (SAD).
+
+The compute lives in ``libsad.so`` (hand-written HIP kernels behind the C ABI of
+``include/sad.h``).  This module is argument marshalling only: it takes torch
+tensors that already live on the GPU, checks dtype/shape/device, and passes raw
+device pointers and the caller's HIP stream to the library.  There is no CPU
+fallback: if the library is not built, or a tensor is not on a GPU, the call
+raises.
+
+Layouts (see include/sad.h): sites float32 [10][stride], candidate map uint32
+[H][W][8] (torch int32 storage reinterpreted), images float32 [H][W][3], grad
+float32 [11][stride], Adam moments float32 [10][stride].
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import subprocess
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_PATH = os.path.join(HERE, "libsad.so")
+SOURCES = [os.path.join(HERE, "csrc", "sad_kernels.hip")]
+INCLUDE = os.path.join(ROOT, "include")
+
+K = 8
+INVALID = 0xFFFFFFFF
+NPARAM = 10
+NACC = 11
+MAX_INJECT = 16
+
+STATUS = {0: "ok", -1: "invalid argument", -2: "misaligned pointer", -3: "HIP launch failed",
+          -4: "capacity exceeded", -5: "not implemented"}
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-munsafe-fp-atomics",
+    # packed FP32 instructions are kept out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+class SadError(RuntimeError):
+    def __init__(self, fn: str, rc: int):
+        super().__init__(f"{fn}: {STATUS.get(rc, 'unknown status')} ({rc})")
+        self.rc = rc
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libsad.so for gfx950 in-tree with hipcc."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["hipcc", *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, *SOURCES]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    if verbose:
+        print(" ".join(cmd))
+    os.replace(tmp, LIB_PATH)
+    global _lib
+    _lib = None
+    return LIB_PATH
+
+
+class AdamCfg(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float * NPARAM), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsad.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (soft_voronoi_render_amd.build()); "
+                               "there is no CPU fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, u32, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p
+        L.sad_abi_version.restype = i32
+        L.sad_abi_version.argtypes = []
+        L.sad_status_string.restype = ctypes.c_char_p
+        L.sad_status_string.argtypes = [i32]
+        L.sad_topk_propagate.restype = i32
+        L.sad_topk_propagate.argtypes = [fp, i32, i32, vp, vp, i32, i32, i32, u32, u32, i32, vp]
+        L.sad_topk_exact.restype = i32
+        L.sad_topk_exact.argtypes = [fp, i32, i32, vp, i32, i32, vp]
+        L.sad_render_fwd.restype = i32
+        L.sad_render_fwd.argtypes = [fp, i32, i32, vp, i32, i32, fp, vp]
+        L.sad_render_bwd.restype = i32
+        L.sad_render_bwd.argtypes = [fp, i32, i32, vp, fp, i32, i32, fp, fp, vp]
+        L.sad_adam_step.restype = i32
+        L.sad_adam_step.argtypes = [fp, fp, fp, fp, i32, i32, i32, i32, i32, i32, ctypes.POINTER(AdamCfg), vp]
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("sad_abi_version", "sad_status_string", "sad_topk_propagate", "sad_topk_exact", "sad_render_fwd",
+            "sad_render_bwd", "sad_adam_step")
+
+
+# --------------------------------------------------------------- marshalling
+def _dev(t: torch.Tensor, name: str, dtypes, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU fallback)")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise SadError(fn, rc)
+
+
+_F32 = (torch.float32,)
+_U32 = (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
+
+
+def _sites(sites: torch.Tensor, n_slots: int):
+    if sites.dim() != 2 or sites.shape[0] != NPARAM:
+        raise ValueError("sites must be float32 [10][stride]")
+    ptr = _dev(sites, "sites", _F32)
+    stride = sites.shape[1]
+    if not 0 <= n_slots <= stride:
+        raise ValueError("need 0 <= n_slots <= stride")
+    return ptr, stride
+
+
+def topk_propagate(sites, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed, n_inject, stream=None):
+    """One propagation pass: cand_in -> cand_out (see sad_topk_propagate)."""
+    sp, stride = _sites(sites, n_slots)
+    a = _dev(cand_in, "cand_in", _U32, (H, W, K))
+    b = _dev(cand_out, "cand_out", _U32, (H, W, K))
+    _check("sad_topk_propagate", lib().sad_topk_propagate(sp, n_slots, stride, a, b, W, H, jump,
+                                                          pass_index & 0xFFFFFFFF, seed & 0xFFFFFFFF, n_inject,
+                                                          _stream(stream)))
+
+
+def topk_exact(sites, n_slots, cand_out, W, H, stream=None):
+    """Brute-force exact top-K map (see sad_topk_exact)."""
+    sp, stride = _sites(sites, n_slots)
+    b = _dev(cand_out, "cand_out", _U32, (H, W, K))
+    _check("sad_topk_exact", lib().sad_topk_exact(sp, n_slots, stride, b, W, H, _stream(stream)))
+
+
+def render_fwd(sites, n_slots, cand, W, H, out_rgb, stream=None):
+    sp, stride = _sites(sites, n_slots)
+    c = _dev(cand, "cand", _U32, (H, W, K))
+    o = _dev(out_rgb, "out_rgb", _F32, (H, W, 3))
+    _check("sad_render_fwd", lib().sad_render_fwd(sp, n_slots, stride, c, W, H, o, _stream(stream)))
+
+
+def render_bwd(sites, n_slots, cand, target, W, H, grad, loss_sum=None, stream=None):
+    sp, stride = _sites(sites, n_slots)
+    c = _dev(cand, "cand", _U32, (H, W, K))
+    t = _dev(target, "target", _F32, (H, W, 3))
+    g = _dev(grad, "grad", _F32, (NACC, stride))
+    ls = _dev(loss_sum, "loss_sum", _F32) if loss_sum is not None else None
+    _check("sad_render_bwd", lib().sad_render_bwd(sp, n_slots, stride, c, t, W, H, g, ls, _stream(stream)))
+
+
+@dataclasses.dataclass
+class AdamConfig:
+    """Adam settings.  The pages do not reproduce their learning rates; these
+    defaults (px units for x, y, r) are ours."""
+    lr: tuple = (0.1, 0.1, 0.02, 0.05, 0.01, 0.01, 0.01, 0.02, 0.02, 0.02)
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+
+    def to_c(self) -> AdamCfg:
+        c = AdamCfg()
+        for j in range(NPARAM):
+            c.lr[j] = float(self.lr[j])
+        c.beta1, c.beta2, c.eps = self.beta1, self.beta2, self.eps
+        return c
+
+
+def adam_step(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamConfig | AdamCfg | None = None,
+              stream=None):
+    sp, stride = _sites(sites, n_slots)
+    mp = _dev(m, "m", _F32, (NPARAM, stride))
+    vp = _dev(v, "v", _F32, (NPARAM, stride))
+    g = _dev(grad, "grad", _F32, (NACC, stride))
+    c = cfg.to_c() if isinstance(cfg, AdamConfig) else (cfg if cfg is not None else AdamConfig().to_c())
+    _check("sad_adam_step", lib().sad_adam_step(sp, mp, vp, g, n_slots, stride, step, n_pixels, W, H,
+                                                ctypes.byref(c), _stream(stream)))
+
+
+def jump_schedule(W: int, H: int, n: int) -> list:
+    """Jumps for n passes: B/2, B/4, ..., 1, then 1, with B = 2^ceil(log2 max(W,H))
+    (paperlayer.ai summary, section 4 "Candidate maintenance"; B is our reading)."""
+    B = 1 << max(0, (max(W, H) - 1).bit_length())
+    out, k = [], B // 2
+    for _ in range(n):
+        out.append(max(k, 1))
+        k //= 2
+    return out
+
+
+def new_map(W: int, H: int, device="cuda") -> torch.Tensor:
+    """An all-sentinel candidate map (uint32 [H][W][8] held as int32)."""
+    return torch.full((H, W, K), -1, dtype=torch.int32, device=device)
+
+
+class Fitter:
+    """One SAD fitting state on the GPU and its iteration: propagate (one pass),
+    render forward, render backward, Adam.  Everything runs in libsad kernels on
+    one stream; nothing crosses to the host inside an iteration."""
+
+    def __init__(self, sites: torch.Tensor, n_slots: int, target: torch.Tensor, W: int, H: int,
+                 n_inject: int = 4, seed: int = 4, adam: AdamConfig | None = None, cand: torch.Tensor | None = None):
+        dev = sites.device
+        self.W, self.H, self.n_slots, self.n_inject, self.seed = W, H, n_slots, n_inject, seed
+        self.sites = sites
+        self.target = target
+        stride = sites.shape[1]
+        self.m = torch.zeros((NPARAM, stride), dtype=torch.float32, device=dev)
+        self.v = torch.zeros((NPARAM, stride), dtype=torch.float32, device=dev)
+        self.grad = torch.zeros((NACC, stride), dtype=torch.float32, device=dev)
+        self.maps = [cand if cand is not None else new_map(W, H, dev), new_map(W, H, dev)]
+        self.cur = 0
+        self.rgb = torch.empty((H, W, 3), dtype=torch.float32, device=dev)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.adam = (adam or AdamConfig()).to_c()
+        self.it = 0
+        self.sched_cache: dict = {}
+
+    @property
+    def cand(self) -> torch.Tensor:
+        return self.maps[self.cur]
+
+    def jump_at(self, it: int) -> int:
+        B = 1 << max(0, (max(self.W, self.H) - 1).bit_length())
+        return max(1, (B // 2) >> it) if it < 64 else 1
+
+    def propagate(self, jump: int, pass_index: int, stream=None):
+        topk_propagate(self.sites, self.n_slots, self.maps[self.cur], self.maps[1 - self.cur], self.W, self.H,
+                       jump, pass_index, self.seed, self.n_inject, stream)
+        self.cur = 1 - self.cur
+
+    def step(self, stream=None):
+        """One iteration (the hot path): propagate, forward, backward, Adam."""
+        it = self.it
+        self.propagate(self.jump_at(it), it, stream)
+        render_fwd(self.sites, self.n_slots, self.cand, self.W, self.H, self.rgb, stream)
+        render_bwd(self.sites, self.n_slots, self.cand, self.target, self.W, self.H, self.grad, self.loss, stream)
+        adam_step(self.sites, self.m, self.v, self.grad, self.n_slots, it + 1, self.W * self.H, self.W, self.H,
+                  self.adam, stream)
+        self.it += 1

@@ -1,0 +1,722 @@
+// sad_kernels.hip -- gfx950 kernels and the C ABI of libsad (declared in include/sad.h).
+//
+// Soft Anisotropic Diagrams (SAD): per-pixel top-K candidate maintenance, the
+// temperature-softmax render, its analytic backward and Adam.  Formulas follow
+// the woaixuexisr.github.io reading note ("Key designs" 1-4), the luckyiyi.github.io
+// project page ("Method") and the paperlayer.ai summary (sections 4-5, Appendix B);
+// each kernel names the passage it implements.
+//
+// Execution model: image-space kernels cover the image with 16x16-pixel tiles,
+// one 256-thread workgroup (four wave64s) per tile, one pixel per lane.  Tiles
+// are handed out so that each XCD (workgroup IDs are dealt round-robin over the
+// 8 XCDs) receives one contiguous band of tiles, which keeps the site gathers and
+// neighbour-list re-reads of a band inside that XCD's L2.  Per-site kernels use
+// 256 threads per workgroup, one slot per thread.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sad.h"
+
+namespace {
+
+constexpr int K = SAD_K;
+constexpr uint32_t NONE = SAD_INVALID;
+constexpr int TILE = 16;
+constexpr int BLOCK = TILE * TILE;
+constexpr int NXCD = 8;
+constexpr int HASH_SLOTS = 256;
+constexpr int HASH_PROBES = 8;
+
+// Site planes (order of the site buffer).
+constexpr int PX = SAD_X, PY = SAD_Y, PLT = SAD_LOGTAU, PR = SAD_R, PCR = SAD_CR, PCG = SAD_CG, PCB = SAD_CB,
+              PDX = SAD_DIRX, PDY = SAD_DIRY, PA = SAD_A;
+
+// Workgroup ID -> logical tile so that the workgroups of one XCD cover a
+// contiguous run of tiles (a bijection on [0, nb)).
+__device__ __forceinline__ int xcd_band(int bid, int nb)
+{
+    const int q = nb / NXCD, rem = nb % NXCD;
+    const int x = bid % NXCD, i = bid / NXCD;
+    return x * q + min(x, rem) + i;
+}
+
+__device__ __forceinline__ bool finitef(float v) { return __builtin_isfinite(v); }
+
+// Ranking key (d ascending, then site ID ascending): a total order.
+__device__ __forceinline__ bool key_less(float da, uint32_t ia, float db, uint32_t ib)
+{
+    return da < db || (da == db && ia < ib);
+}
+
+// Metric frame of one site: u = dir/|dir| (u = (1,0) if |dir|^2 < 1e-30) and e^{+-a}.
+struct Frame {
+    float ux, uy, E, iE;
+};
+
+__device__ __forceinline__ Frame make_frame(float dx, float dy, float a)
+{
+    Frame f;
+    const float n2 = dx * dx + dy * dy;
+    f.ux = 1.0f;
+    f.uy = 0.0f;
+    if (n2 >= 1e-30f) {
+        const float inv = rsqrtf(n2);
+        f.ux = dx * inv;
+        f.uy = dy * inv;
+    }
+    f.E = __expf(a);
+    f.iE = __expf(-a);
+    return f;
+}
+
+// d = s*||x - p||_G - s*r with ||delta||_G^2 = e^a (u.delta)^2 + e^-a (v.delta)^2,
+// v = (-u_y, u_x)  (reading note, key design 1).
+__device__ __forceinline__ float score_frame(const Frame &f, float px, float py, float r, float X, float Y, float s)
+{
+    const float ex = X - px, ey = Y - py;
+    const float al = f.ux * ex + f.uy * ey;
+    const float be = f.ux * ey - f.uy * ex;
+    const float q = sqrtf(f.E * al * al + f.iE * be * be);
+    return s * q - s * r;
+}
+
+// Score of slot `id` read straight from the SoA planes (6 gathers).
+__device__ __forceinline__ float score_site(const float *__restrict__ S, long stride, uint32_t id, float X, float Y,
+                                            float s, bool &usable)
+{
+    const float px = S[id];
+    usable = !(px < 0.0f);
+    const float py = S[stride + id];
+    const float r = S[PR * stride + id];
+    const Frame f = make_frame(S[PDX * stride + id], S[PDY * stride + id], S[PA * stride + id]);
+    return score_frame(f, px, py, r, X, Y, s);
+}
+
+// ---------------------------------------------------------------------------
+// Counter-based injection (paperlayer.ai summary, Appendix B.3: the pass word and
+// the pixel ID seed xorshift).  pcg hash: Jarzynski & Olano, JCGT 2020;
+// xorshift32 (13,17,5): Marsaglia 2003; range: Lemire's multiply-shift.
+__device__ __forceinline__ uint32_t pcg_hash(uint32_t v)
+{
+    const uint32_t state = v * 747796405u + 2891336453u;
+    const uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+    return (word >> 22u) ^ word;
+}
+
+__device__ __forceinline__ uint32_t xorshift32(uint32_t x)
+{
+    x ^= x << 13;
+    x ^= x >> 17;
+    x ^= x << 5;
+    return x;
+}
+
+// Sorted top-K held in registers; insert keeps ascending (d, ID) order.
+struct TopK {
+    float d[K];
+    uint32_t id[K];
+
+    __device__ __forceinline__ void clear()
+    {
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            d[j] = __builtin_inff();
+            id[j] = NONE;
+        }
+    }
+    __device__ __forceinline__ bool contains(uint32_t c) const
+    {
+        bool hit = false;
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            hit |= (id[j] == c);
+        return hit;
+    }
+    // Precondition: key_less(dc, c, d[K-1], id[K-1]) and c not present.
+    __device__ __forceinline__ void insert(float dc, uint32_t c)
+    {
+#pragma unroll
+        for (int j = K - 1; j >= 0; --j) {
+            const bool shift = (j > 0) && key_less(dc, c, d[j - 1], id[j - 1]);
+            const bool here = key_less(dc, c, d[j], id[j]);
+            const float nd = shift ? d[j - 1] : (here ? dc : d[j]);
+            const uint32_t ni = shift ? id[j - 1] : (here ? c : id[j]);
+            d[j] = nd;
+            id[j] = ni;
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Propagation pass (reading note, key design 3; summary, section 4 and B.3).
+// One lane per pixel.  Candidates are visited own list -> 4 neighbour lists ->
+// injected IDs; a candidate already in the running list is skipped (a repeat of
+// one that was rejected or evicted is rejected again, since the K-th key only
+// decreases), so the result equals the top-K of the deduplicated union.
+__global__ __launch_bounds__(BLOCK) void k_propagate(const float *__restrict__ S, uint32_t n_slots, int stride,
+                                                     const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
+                                                     int H, int jump, uint32_t pw, uint32_t seed_h, int n_inject,
+                                                     float s, int tiles_x, int nb)
+{
+    const int t = xcd_band(blockIdx.x, nb);
+    const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
+    const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
+    if (col >= W || row >= H)
+        return;
+    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    TopK best;
+    best.clear();
+
+    auto consider = [&](uint32_t c) {
+        if (c >= n_slots || best.contains(c))
+            return;
+        bool usable;
+        const float dc = score_site(S, stride, c, X, Y, s, usable);
+        if (!usable || !finitef(dc) || !key_less(dc, c, best.d[K - 1], best.id[K - 1]))
+            return;
+        best.insert(dc, c);
+    };
+    auto consider_list = [&](int c_, int r_) {
+        const long p = (long)r_ * W + c_;
+        const uint4 a = cin[2 * p], b = cin[2 * p + 1];
+        consider(a.x);
+        consider(a.y);
+        consider(a.z);
+        consider(a.w);
+        consider(b.x);
+        consider(b.y);
+        consider(b.z);
+        consider(b.w);
+    };
+
+    consider_list(col, row);
+    if (col - jump >= 0)
+        consider_list(col - jump, row);
+    if (col + jump < W)
+        consider_list(col + jump, row);
+    if (row - jump >= 0)
+        consider_list(col, row - jump);
+    if (row + jump < H)
+        consider_list(col, row + jump);
+    if (n_inject > 0) {
+        const uint32_t h = pcg_hash(seed_h ^ ((uint32_t)row * (uint32_t)W + (uint32_t)col));
+        uint32_t x = h ? h : 0x9E3779B9u;
+        for (int j = 0; j < n_inject; ++j) {
+            x = xorshift32(x);
+            consider((uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32));
+        }
+    }
+    const long p = (long)row * W + col;
+    cout[2 * p] = make_uint4(best.id[0], best.id[1], best.id[2], best.id[3]);
+    cout[2 * p + 1] = make_uint4(best.id[4], best.id[5], best.id[6], best.id[7]);
+}
+
+// ---------------------------------------------------------------------------
+// Exact top-K by brute force: every slot is scored for every pixel.  Sites are
+// staged through LDS 256 at a time (x, y, r and the metric frame).
+__global__ __launch_bounds__(BLOCK) void k_topk_exact(const float *__restrict__ S, uint32_t n_slots, int stride,
+                                                      uint4 *__restrict__ cout, int W, int H, float s, int tiles_x,
+                                                      int nb)
+{
+    __shared__ float lpx[BLOCK], lpy[BLOCK], lr[BLOCK], lux[BLOCK], luy[BLOCK], lE[BLOCK], liE[BLOCK];
+    const int t = xcd_band(blockIdx.x, nb);
+    const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
+    const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
+    const bool inside = col < W && row < H;
+    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    TopK best;
+    best.clear();
+    for (uint32_t base = 0; base < n_slots; base += BLOCK) {
+        const uint32_t i = base + threadIdx.x;
+        float px = -1.0f;
+        Frame f{1.0f, 0.0f, 1.0f, 1.0f};
+        float py = 0.0f, r = 0.0f;
+        if (i < n_slots) {
+            px = S[i];
+            py = S[stride + i];
+            r = S[PR * (long)stride + i];
+            f = make_frame(S[PDX * (long)stride + i], S[PDY * (long)stride + i], S[PA * (long)stride + i]);
+        }
+        __syncthreads();
+        lpx[threadIdx.x] = px;
+        lpy[threadIdx.x] = py;
+        lr[threadIdx.x] = r;
+        lux[threadIdx.x] = f.ux;
+        luy[threadIdx.x] = f.uy;
+        lE[threadIdx.x] = f.E;
+        liE[threadIdx.x] = f.iE;
+        __syncthreads();
+        if (inside) {
+            const int cnt = min((int)(n_slots - base), BLOCK);
+            for (int j = 0; j < cnt; ++j) {
+                const float sx = lpx[j];
+                if (sx < 0.0f)
+                    continue;
+                const Frame fj{lux[j], luy[j], lE[j], liE[j]};
+                const float dc = score_frame(fj, sx, lpy[j], lr[j], X, Y, s);
+                const uint32_t c = base + j;
+                if (finitef(dc) && key_less(dc, c, best.d[K - 1], best.id[K - 1]))
+                    best.insert(dc, c);
+            }
+        }
+    }
+    if (inside) {
+        const long p = (long)row * W + col;
+        cout[2 * p] = make_uint4(best.id[0], best.id[1], best.id[2], best.id[3]);
+        cout[2 * p + 1] = make_uint4(best.id[4], best.id[5], best.id[6], best.id[7]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-pixel forward state shared by the forward and backward kernels: the blend
+// of one list (reading note, key design 2; summary B.4: max-subtracted, invalid
+// and non-finite entries skipped).
+struct PixelBlend {
+    uint32_t id[K];
+    float l[K], e[K], c0[K], c1[K], c2[K];
+    float Z, chat0, chat1, chat2;
+    bool any;
+};
+
+__device__ __forceinline__ void blend_pixel(const float *__restrict__ S, long stride, uint32_t n_slots,
+                                            const uint4 a, const uint4 b, float X, float Y, float s,
+                                            PixelBlend &B)
+{
+    const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const uint32_t c = ids[k];
+        B.id[k] = NONE;
+        B.l[k] = -__builtin_inff();
+        B.c0[k] = B.c1[k] = B.c2[k] = 0.0f;
+        if (c < n_slots) {
+            bool usable;
+            const float d = score_site(S, stride, c, X, Y, s, usable);
+            const float tau = __expf(S[PLT * stride + c]);
+            const float l = -tau * d;
+            const float r0 = S[PCR * stride + c], r1 = S[PCG * stride + c], r2 = S[PCB * stride + c];
+            if (usable && finitef(l) && finitef(r0) && finitef(r1) && finitef(r2)) {
+                B.id[k] = c;
+                B.l[k] = l;
+                B.c0[k] = r0;
+                B.c1[k] = r1;
+                B.c2[k] = r2;
+                mx = fmaxf(mx, l);
+            }
+        }
+    }
+    B.any = mx > -__builtin_inff();
+    B.Z = 0.0f;
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float e = B.id[k] != NONE ? __expf(B.l[k] - mx) : 0.0f;
+        B.e[k] = e;
+        B.Z += e;
+        a0 += e * B.c0[k];
+        a1 += e * B.c1[k];
+        a2 += e * B.c2[k];
+    }
+    const float iZ = B.any ? 1.0f / B.Z : 0.0f;
+    B.chat0 = a0 * iZ;
+    B.chat1 = a1 * iZ;
+    B.chat2 = a2 * iZ;
+}
+
+// Render forward (reading note, key design 2; project page "Method").
+__global__ __launch_bounds__(BLOCK) void k_render_fwd(const float *__restrict__ S, uint32_t n_slots, int stride,
+                                                      const uint4 *__restrict__ cand, int W, int H,
+                                                      float *__restrict__ out, float s, int tiles_x, int nb)
+{
+    const int t = xcd_band(blockIdx.x, nb);
+    const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
+    const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
+    if (col >= W || row >= H)
+        return;
+    const long p = (long)row * W + col;
+    PixelBlend B;
+    blend_pixel(S, stride, n_slots, cand[2 * p], cand[2 * p + 1], (float)col + 0.5f, (float)row + 0.5f, s, B);
+    out[3 * p] = B.chat0;
+    out[3 * p + 1] = B.chat1;
+    out[3 * p + 2] = B.chat2;
+}
+
+// ---------------------------------------------------------------------------
+// Render backward with per-tile LDS hash reduction (summary, section 5 and B.4;
+// press article section 5: 16x16 tiles).
+__global__ __launch_bounds__(BLOCK) void k_render_bwd(const float *__restrict__ S, uint32_t n_slots, int stride,
+                                                      const uint4 *__restrict__ cand,
+                                                      const float *__restrict__ target, int W, int H,
+                                                      float *__restrict__ grad, float *__restrict__ loss_sum,
+                                                      float s, int tiles_x, int nb)
+{
+    __shared__ uint32_t hkey[HASH_SLOTS];
+    __shared__ float hacc[SAD_NACC][HASH_SLOTS];
+    __shared__ float wloss[BLOCK / 64];
+
+    hkey[threadIdx.x] = NONE;
+#pragma unroll
+    for (int a = 0; a < SAD_NACC; ++a)
+        hacc[a][threadIdx.x] = 0.0f;
+    __syncthreads();
+
+    const int t = xcd_band(blockIdx.x, nb);
+    const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
+    const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
+    const bool inside = col < W && row < H;
+    const long stride_l = stride;
+    float err = 0.0f;
+
+    if (inside) {
+        const long p = (long)row * W + col;
+        const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+        PixelBlend B;
+        blend_pixel(S, stride_l, n_slots, cand[2 * p], cand[2 * p + 1], X, Y, s, B);
+        const float t0 = target[3 * p], t1 = target[3 * p + 1], t2 = target[3 * p + 2];
+        const float r0 = B.chat0 - t0, r1 = B.chat1 - t1, r2 = B.chat2 - t2;
+        err = r0 * r0 + r1 * r1 + r2 * r2;
+        if (B.any) {
+            const float g0 = 2.0f * r0, g1 = 2.0f * r1, g2 = 2.0f * r2;
+            const float iZ = 1.0f / B.Z;
+            // exclusive prefix/suffix sums of e and e*c: the blend without entry k
+            float pe[K], p0[K], p1[K], p2[K];
+            {
+                float se = 0.0f, s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    pe[k] = se;
+                    p0[k] = s0;
+                    p1[k] = s1;
+                    p2[k] = s2;
+                    se += B.e[k];
+                    s0 += B.e[k] * B.c0[k];
+                    s1 += B.e[k] * B.c1[k];
+                    s2 += B.e[k] * B.c2[k];
+                }
+                se = s0 = s1 = s2 = 0.0f;
+#pragma unroll
+                for (int k = K - 1; k >= 0; --k) {
+                    pe[k] += se;
+                    p0[k] += s0;
+                    p1[k] += s1;
+                    p2[k] += s2;
+                    se += B.e[k];
+                    s0 += B.e[k] * B.c0[k];
+                    s1 += B.e[k] * B.c1[k];
+                    s2 += B.e[k] * B.c2[k];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const uint32_t c = B.id[k];
+                if (c == NONE)
+                    continue;
+                const float w = B.e[k] * iZ;
+                float acc[SAD_NACC];
+                acc[PCR] = w * g0;
+                acc[PCG] = w * g1;
+                acc[PCB] = w * g2;
+                const float gamma = w * (g0 * (B.c0[k] - B.chat0) + g1 * (B.c1[k] - B.chat1) + g2 * (B.c2[k] - B.chat2));
+                const float tau = __expf(S[PLT * stride_l + c]);
+                acc[PLT] = gamma * B.l[k];
+                acc[PR] = tau * gamma * s;
+                const float eta = -tau * gamma * s;  // dL/dq
+                // geometry of entry k (same arithmetic as the score)
+                const float px = S[c], py = S[stride_l + c];
+                const float dx = S[PDX * stride_l + c], dy = S[PDY * stride_l + c];
+                const Frame f = make_frame(dx, dy, S[PA * stride_l + c]);
+                const float ex = X - px, ey = Y - py;
+                const float al = f.ux * ex + f.uy * ey;
+                const float be = f.ux * ey - f.uy * ex;
+                const float q = sqrtf(f.E * al * al + f.iE * be * be);
+                acc[PX] = acc[PY] = acc[PA] = acc[PDX] = acc[PDY] = 0.0f;
+                if (q > 0.0f) {
+                    const float fq = eta / q;
+                    const float Ea = f.E * al, Eb = f.iE * be;
+                    // dp = -(eta/q) (E al u + e^-a be v),  v = (-u_y, u_x)
+                    acc[PX] = -fq * (Ea * f.ux - Eb * f.uy);
+                    acc[PY] = -fq * (Ea * f.uy + Eb * f.ux);
+                    acc[PA] = 0.5f * fq * (Ea * al - Eb * be);
+                    const float n2 = dx * dx + dy * dy;
+                    if (n2 >= 1e-30f) {
+                        const float gux = fq * (Ea * ex + Eb * ey);
+                        const float guy = fq * (Ea * ey - Eb * ex);
+                        const float proj = f.ux * gux + f.uy * guy;
+                        const float in = rsqrtf(n2);
+                        acc[PDX] = (gux - proj * f.ux) * in;
+                        acc[PDY] = (guy - proj * f.uy) * in;
+                    }
+                }
+                // removal delta
+                const float Zo = pe[k];
+                const float iZo = Zo > 0.0f ? 1.0f / Zo : 0.0f;
+                const float m0 = p0[k] * iZo - t0, m1 = p1[k] * iZo - t1, m2 = p2[k] * iZo - t2;
+                acc[10] = (m0 * m0 + m1 * m1 + m2 * m2) - err;
+#pragma unroll
+                for (int a = 0; a < SAD_NACC; ++a)
+                    acc[a] = finitef(acc[a]) ? acc[a] : 0.0f;
+                // LDS hash insert (multiplicative hash, <= 8 linear probes, CAS)
+                int slot = -1;
+                const uint32_t h0 = (c * 2654435761u) >> 24;
+                for (int pr = 0; pr < HASH_PROBES; ++pr) {
+                    const uint32_t sl = (h0 + pr) & (HASH_SLOTS - 1);
+                    const uint32_t prev = atomicCAS(&hkey[sl], NONE, c);
+                    if (prev == NONE || prev == c) {
+                        slot = (int)sl;
+                        break;
+                    }
+                }
+                if (slot >= 0) {
+#pragma unroll
+                    for (int a = 0; a < SAD_NACC; ++a)
+                        atomicAdd(&hacc[a][slot], acc[a]);
+                } else {
+#pragma unroll
+                    for (int a = 0; a < SAD_NACC; ++a)
+                        unsafeAtomicAdd(&grad[a * stride_l + c], acc[a]);
+                }
+            }
+        }
+    }
+    // per-pixel loss: wave reduction, then one atomic per workgroup
+    if (loss_sum) {
+        float v = err;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+            v += __shfl_xor(v, o, 64);
+        if ((threadIdx.x & 63) == 0)
+            wloss[threadIdx.x >> 6] = v;
+    }
+    __syncthreads();
+    if (loss_sum && threadIdx.x == 0) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < BLOCK / 64; ++w)
+            v += wloss[w];
+        unsafeAtomicAdd(loss_sum, v);
+    }
+    // flush: one atomic per (site, accumulator) present in the tile
+    const uint32_t key = hkey[threadIdx.x];
+    if (key != NONE) {
+#pragma unroll
+        for (int a = 0; a < SAD_NACC; ++a) {
+            const float v = hacc[a][threadIdx.x];
+            if (v != 0.0f)
+                unsafeAtomicAdd(&grad[a * stride_l + key], v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Adam (Kingma & Ba 2015) on the ten site parameters, gradients divided by the
+// pixel count (summary, B.4), gradient planes 0..9 zeroed in the same pass.
+struct AdamArgs {
+    float lr[SAD_NPARAM];
+    float b1, b2, eps, bc1, bc2, inv_p, W, H;
+};
+
+__global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__restrict__ M, float *__restrict__ V,
+                                              float *__restrict__ G, int n_slots, int stride, AdamArgs A)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_slots)
+        return;
+    const long st = stride;
+    const bool active = !(S[i] < 0.0f);
+#pragma unroll
+    for (int j = 0; j < SAD_NPARAM; ++j) {
+        const long o = j * st + i;
+        float g = G[o];
+        G[o] = 0.0f;
+        if (active) {
+            g *= A.inv_p;
+            if (!finitef(g))
+                g = 0.0f;
+            const float m = A.b1 * M[o] + (1.0f - A.b1) * g;
+            const float v = A.b2 * V[o] + (1.0f - A.b2) * g * g;
+            M[o] = m;
+            V[o] = v;
+            S[o] = S[o] - A.lr[j] * (m / A.bc1) / (sqrtf(v / A.bc2) + A.eps);
+        }
+    }
+    if (active) {
+        const float x = S[i], y = S[st + i];
+        S[i] = x < 0.0f ? 0.0f : (x > A.W ? A.W : x);
+        S[st + i] = y < 0.0f ? 0.0f : (y > A.H ? A.H : y);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host helpers.
+inline int check_image(int W, int H)
+{
+    if (W < 0 || H < 0 || W > SAD_MAX_DIM || H > SAD_MAX_DIM)
+        return SAD_ERR_ARG;
+    return SAD_OK;
+}
+
+inline int check_sites(int n_slots, int stride)
+{
+    if (n_slots < 0 || stride < 1 || n_slots > stride)
+        return SAD_ERR_ARG;
+    return SAD_OK;
+}
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline float scale_of(int W, int H) { return 1.0f / (float)(W > H ? W : H); }
+
+struct TileGrid {
+    int tiles_x, nb;
+};
+
+inline TileGrid tile_grid(int W, int H)
+{
+    TileGrid g;
+    g.tiles_x = (W + TILE - 1) / TILE;
+    g.nb = g.tiles_x * ((H + TILE - 1) / TILE);
+    return g;
+}
+
+inline int launched()
+{
+    return hipGetLastError() == hipSuccess ? SAD_OK : SAD_ERR_DEVICE;
+}
+
+uint32_t host_pcg_hash(uint32_t v)
+{
+    const uint32_t state = v * 747796405u + 2891336453u;
+    const uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+    return (word >> 22u) ^ word;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sad_abi_version(void) { return SAD_ABI_VERSION; }
+
+const char *sad_status_string(int status)
+{
+    switch (status) {
+    case SAD_OK: return "ok";
+    case SAD_ERR_ARG: return "invalid argument";
+    case SAD_ERR_ALIGN: return "misaligned pointer";
+    case SAD_ERR_DEVICE: return "HIP launch failed";
+    case SAD_ERR_CAPACITY: return "capacity exceeded";
+    case SAD_ERR_UNIMPLEMENTED: return "not implemented";
+    default: return "unknown status";
+    }
+}
+
+int sad_topk_propagate(const float *sites, int n_slots, int stride, const uint32_t *cand_in, uint32_t *cand_out,
+                       int W, int H, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
+        return rc;
+    if (jump < 1 || jump > 0xFFFF || n_inject < 0 || n_inject > SAD_MAX_INJECT)
+        return SAD_ERR_ARG;
+    if (W == 0 || H == 0)
+        return SAD_OK;
+    if (!sites || !cand_in || !cand_out)
+        return SAD_ERR_ARG;
+    const size_t bytes = (size_t)W * H * K * sizeof(uint32_t);
+    const uintptr_t a0 = (uintptr_t)cand_in, a1 = (uintptr_t)cand_out;
+    if (bytes && a0 < a1 + bytes && a1 < a0 + bytes)
+        return SAD_ERR_ARG;
+    if (!aligned16(cand_in) || !aligned16(cand_out))
+        return SAD_ERR_ALIGN;
+    const TileGrid g = tile_grid(W, H);
+    const uint32_t pw = ((uint32_t)jump << 16) | (pass_index & 0xFFFFu);
+    const uint32_t seed_h = host_pcg_hash(host_pcg_hash(seed) ^ pw);
+    hipLaunchKernelGGL(k_propagate, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, sites, (uint32_t)n_slots, stride,
+                       (const uint4 *)cand_in, (uint4 *)cand_out, W, H, jump, pw, seed_h, n_inject, scale_of(W, H),
+                       g.tiles_x, g.nb);
+    return launched();
+}
+
+int sad_topk_exact(const float *sites, int n_slots, int stride, uint32_t *cand_out, int W, int H, void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
+        return rc;
+    if (W == 0 || H == 0)
+        return SAD_OK;
+    if (!sites || !cand_out)
+        return SAD_ERR_ARG;
+    if (!aligned16(cand_out))
+        return SAD_ERR_ALIGN;
+    const TileGrid g = tile_grid(W, H);
+    hipLaunchKernelGGL(k_topk_exact, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, sites, (uint32_t)n_slots,
+                       stride, (uint4 *)cand_out, W, H, scale_of(W, H), g.tiles_x, g.nb);
+    return launched();
+}
+
+int sad_render_fwd(const float *sites, int n_slots, int stride, const uint32_t *cand, int W, int H, float *out_rgb,
+                   void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
+        return rc;
+    if (W == 0 || H == 0)
+        return SAD_OK;
+    if (!sites || !cand || !out_rgb)
+        return SAD_ERR_ARG;
+    if (!aligned16(cand))
+        return SAD_ERR_ALIGN;
+    const TileGrid g = tile_grid(W, H);
+    hipLaunchKernelGGL(k_render_fwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, sites, (uint32_t)n_slots,
+                       stride, (const uint4 *)cand, W, H, out_rgb, scale_of(W, H), g.tiles_x, g.nb);
+    return launched();
+}
+
+int sad_render_bwd(const float *sites, int n_slots, int stride, const uint32_t *cand, const float *target, int W,
+                   int H, float *grad, float *loss_sum, void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
+        return rc;
+    if (W == 0 || H == 0)
+        return SAD_OK;
+    if (!sites || !cand || !target || !grad)
+        return SAD_ERR_ARG;
+    if (!aligned16(cand))
+        return SAD_ERR_ALIGN;
+    const TileGrid g = tile_grid(W, H);
+    hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, sites, (uint32_t)n_slots,
+                       stride, (const uint4 *)cand, target, W, H, grad, loss_sum, scale_of(W, H), g.tiles_x, g.nb);
+    return launched();
+}
+
+int sad_adam_step(float *sites, float *m, float *v, float *grad, int n_slots, int stride, int step, int n_pixels,
+                  int W, int H, const sad_adam_cfg *cfg, void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
+        return rc;
+    if (!sites || !m || !v || !grad || !cfg || step < 1 || n_pixels < 1)
+        return SAD_ERR_ARG;
+    if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f && cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f && cfg->eps >= 0.0f))
+        return SAD_ERR_ARG;
+    if (n_slots == 0)
+        return SAD_OK;
+    AdamArgs A;
+    for (int j = 0; j < SAD_NPARAM; ++j)
+        A.lr[j] = cfg->lr[j];
+    A.b1 = cfg->beta1;
+    A.b2 = cfg->beta2;
+    A.eps = cfg->eps;
+    A.bc1 = (float)(1.0 - __builtin_pow((double)cfg->beta1, (double)step));
+    A.bc2 = (float)(1.0 - __builtin_pow((double)cfg->beta2, (double)step));
+    A.inv_p = 1.0f / (float)n_pixels;
+    A.W = (float)W;
+    A.H = (float)H;
+    hipLaunchKernelGGL(k_adam, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, m, v, grad,
+                       n_slots, stride, A);
+    return launched();
+}
+
+}  // extern "C"

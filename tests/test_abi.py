@@ -1,0 +1,108 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+function include/sad.h declares, and rejects bad arguments before launching
+anything (the dummy pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import soft_voronoi_render_amd as sad
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sad.h")
+
+ERR_ARG, ERR_ALIGN = -1, -2
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sad.LIB_PATH):
+        sad.build()
+    return sad.lib()
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(sad_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_hot_path():
+    names = _declared()
+    for fn in ("sad_topk_propagate", "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_topk_exact",
+               "sad_abi_version", "sad_status_string"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for fn in _declared():
+        assert hasattr(L, fn), fn
+    assert set(_declared()) == set(sad.EXPORTED)
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.sad_abi_version() == 1
+    assert L.sad_status_string(0) == b"ok"
+    assert L.sad_status_string(ERR_ALIGN) == b"misaligned pointer"
+    assert L.sad_status_string(12345) == b"unknown status"
+
+
+P = 0x10000  # a 16-byte aligned dummy address; never dereferenced on these paths
+Q = 0x90000
+
+
+def test_propagate_rejects_bad_arguments(L):
+    f = L.sad_topk_propagate
+    ok = dict(sites=P, n=4, stride=8, a=P, b=Q, W=16, H=16, jump=1, pidx=0, seed=0, m=4)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["sites"], a["n"], a["stride"], a["a"], a["b"], a["W"], a["H"], a["jump"], a["pidx"], a["seed"],
+                 a["m"], None)
+
+    assert call(jump=0) == ERR_ARG
+    assert call(jump=65536) == ERR_ARG
+    assert call(m=-1) == ERR_ARG
+    assert call(m=17) == ERR_ARG
+    assert call(n=9) == ERR_ARG          # n_slots > stride
+    assert call(n=-1) == ERR_ARG
+    assert call(W=-1) == ERR_ARG
+    assert call(H=70000) == ERR_ARG
+    assert call(sites=0) == ERR_ARG
+    assert call(sites=0, W=0) == 0       # empty image: pointers are not needed
+    assert call(b=P) == ERR_ARG          # in place
+    assert call(b=P + 32) == ERR_ARG     # overlapping maps
+    assert call(a=P + 4, b=Q) == ERR_ALIGN
+    assert call(W=0) == 0                # empty image: no-op, nothing launched
+    assert call(H=0, b=P) == 0        # empty: zero bytes cannot overlap
+
+
+def test_render_and_adam_reject_bad_arguments(L):
+    assert L.sad_render_fwd(P, 4, 8, P + 8, 16, 16, Q, None) == ERR_ALIGN
+    assert L.sad_render_fwd(P, 4, 8, 0, 16, 16, Q, None) == ERR_ARG
+    assert L.sad_render_fwd(P, 9, 8, P, 16, 16, Q, None) == ERR_ARG
+    assert L.sad_render_fwd(P, 4, 8, P, 0, 16, Q, None) == 0
+    assert L.sad_render_bwd(P, 4, 8, P, 0, 16, 16, Q, None, None) == ERR_ARG  # target NULL
+    assert L.sad_render_bwd(P, 4, 8, P + 4, Q, 16, 16, Q, None, None) == ERR_ALIGN
+    assert L.sad_topk_exact(P, 4, 8, P + 4, 16, 16, None) == ERR_ALIGN
+    cfg = sad.AdamConfig().to_c()
+    assert L.sad_adam_step(P, P, P, P, 4, 8, 0, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # step 0
+    assert L.sad_adam_step(P, P, P, P, 4, 8, 1, 0, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # no pixels
+    assert L.sad_adam_step(P, P, P, P, 4, 8, 1, 10, 4, 4, None, None) == ERR_ARG
+    bad = sad.AdamConfig(beta1=1.0).to_c()
+    assert L.sad_adam_step(P, P, P, P, 4, 8, 1, 10, 4, 4, ctypes.byref(bad), None) == ERR_ARG
+    assert L.sad_adam_step(P, P, P, P, 0, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == 0  # no slots: no-op
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    s = torch.zeros((10, 4))
+    with pytest.raises(ValueError):
+        sad.render_fwd(s, 4, torch.zeros((2, 2, 8), dtype=torch.int32), 2, 2, torch.zeros((2, 2, 3)))
+
+
+def test_jump_schedule():
+    assert sad.jump_schedule(768, 512, 12) == [512, 256, 128, 64, 32, 16, 8, 4, 2, 1, 1, 1]
+    assert sad.jump_schedule(4096, 4096, 13)[:12] == [2048 >> i for i in range(12)]
+    assert sad.jump_schedule(1, 1, 3) == [1, 1, 1]
