@@ -269,60 +269,186 @@ __global__ __launch_bounds__(BLOCK) void k_topk_exact(const float *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Per-pixel forward state shared by the forward and backward kernels: the blend
-// of one list (reading note, key design 2; summary B.4: max-subtracted, invalid
-// and non-finite entries skipped).
+// Per-tile site table.  A 16x16 tile's lists name only a few dozen distinct
+// sites, so each distinct site is gathered from the SoA planes once per tile
+// and its derived record kept in LDS: scattered per-lane gathers are what
+// limits these kernels otherwise.  The table is an LDS hash keyed by site ID
+// (multiplicative hash, <= 8 linear probes, CAS insert -- summary, B.4).  An ID
+// that finds no slot takes the "spill" path and is read from global memory.
+constexpr int TBL = 256;
+constexpr int NREC = 12;  // px py r ux uy E iE tau R G B inv_n
+
+enum { R_PX, R_PY, R_R, R_UX, R_UY, R_E, R_IE, R_TAU, R_C0, R_C1, R_C2, R_INVN };
+
+// Derived record of one site: the metric frame, tau = exp(log tau), the colour
+// and 1/|dir| (0 for a degenerate direction).  A site that cannot take part --
+// inactive (x < 0, summary B.2) or with a non-finite colour -- gets px = NaN, so
+// every logit it produces is non-finite and the entry is dropped.
+struct SiteRec {
+    float v[NREC];
+};
+
+__device__ __forceinline__ SiteRec load_rec_global(const float *__restrict__ S, long st, uint32_t c)
+{
+    SiteRec R;
+    const float x = S[c], y = S[st + c], lt = S[PLT * st + c], r = S[PR * st + c];
+    const float c0 = S[PCR * st + c], c1 = S[PCG * st + c], c2 = S[PCB * st + c];
+    const float dx = S[PDX * st + c], dy = S[PDY * st + c], a = S[PA * st + c];
+    const Frame f = make_frame(dx, dy, a);
+    const float n2 = dx * dx + dy * dy;
+    const bool ok = !(x < 0.0f) && finitef(c0) && finitef(c1) && finitef(c2);
+    R.v[R_PX] = ok ? x : __builtin_nanf("");
+    R.v[R_PY] = y;
+    R.v[R_R] = r;
+    R.v[R_UX] = f.ux;
+    R.v[R_UY] = f.uy;
+    R.v[R_E] = f.E;
+    R.v[R_IE] = f.iE;
+    R.v[R_TAU] = __expf(lt);
+    R.v[R_C0] = c0;
+    R.v[R_C1] = c1;
+    R.v[R_C2] = c2;
+    R.v[R_INVN] = n2 >= 1e-30f ? rsqrtf(n2) : 0.0f;
+    return R;
+}
+
+struct TileTable {
+    uint32_t key[TBL];
+    float rec[NREC][TBL];
+};
+
+__device__ __forceinline__ int table_insert(uint32_t *key, uint32_t c)
+{
+    const uint32_t h0 = (c * 2654435761u) >> 24;
+    for (int pr = 0; pr < HASH_PROBES; ++pr) {
+        const uint32_t sl = (h0 + pr) & (TBL - 1);
+        const uint32_t prev = atomicCAS(&key[sl], NONE, c);
+        if (prev == NONE || prev == c)
+            return (int)sl;
+    }
+    return -1;
+}
+
+// Phases 1-2 shared by forward and backward: insert the pixel's IDs, then one
+// thread per occupied slot fills its record.  slot[k]: table slot, -1 = spill,
+// -2 = no site (sentinel or ID >= n_slots).  Ends with a barrier.
+__device__ __forceinline__ void build_tile_table(TileTable &T, const float *__restrict__ S, long st,
+                                                 uint32_t n_slots, const uint32_t (&ids)[K], int (&slot)[K])
+{
+    T.key[threadIdx.x] = NONE;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        slot[k] = ids[k] < n_slots ? table_insert(T.key, ids[k]) : -2;
+    __syncthreads();
+    const uint32_t c = T.key[threadIdx.x];
+    if (c != NONE) {
+        const SiteRec R = load_rec_global(S, st, c);
+#pragma unroll
+        for (int j = 0; j < NREC; ++j)
+            T.rec[j][threadIdx.x] = R.v[j];
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ SiteRec table_rec(const TileTable &T, int sl)
+{
+    SiteRec R;
+#pragma unroll
+    for (int j = 0; j < NREC; ++j)
+        R.v[j] = T.rec[j][sl];
+    return R;
+}
+
+__device__ __forceinline__ float rec_score(const SiteRec &R, float X, float Y, float s)
+{
+    const Frame f{R.v[R_UX], R.v[R_UY], R.v[R_E], R.v[R_IE]};
+    return score_frame(f, R.v[R_PX], R.v[R_PY], R.v[R_R], X, Y, s);
+}
+
+// The blend of one pixel's list (reading note, key design 2; summary B.4:
+// max-subtracted softmax, invalid and non-finite entries skipped).
 struct PixelBlend {
-    uint32_t id[K];
     float l[K], e[K], c0[K], c1[K], c2[K];
+    bool use[K];
     float Z, chat0, chat1, chat2;
     bool any;
 };
 
-__device__ __forceinline__ void blend_pixel(const float *__restrict__ S, long stride, uint32_t n_slots,
-                                            const uint4 a, const uint4 b, float X, float Y, float s,
-                                            PixelBlend &B)
+
+// Record of list entry k: from the tile table, from global memory for a spilled
+// ID, or an unusable placeholder (px = NaN) for an empty entry.
+__device__ __forceinline__ SiteRec fetch_rec(const TileTable &T, const float *__restrict__ S, long st, uint32_t id,
+                                            int sl)
 {
-    const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    if (sl >= 0)
+        return table_rec(T, sl);
+    if (sl == -1)
+        return load_rec_global(S, st, id);
+    SiteRec R;
+#pragma unroll
+    for (int j = 0; j < NREC; ++j)
+        R.v[j] = 0.0f;
+    R.v[R_PX] = __builtin_nanf("");
+    return R;
+}
+
+__device__ __forceinline__ void blend_pixel(const TileTable &T, const float *__restrict__ S, long st,
+                                            const uint32_t (&ids)[K], const int (&slot)[K], float X, float Y,
+                                            float s, PixelBlend &B)
+{
     float mx = -__builtin_inff();
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const uint32_t c = ids[k];
-        B.id[k] = NONE;
-        B.l[k] = -__builtin_inff();
-        B.c0[k] = B.c1[k] = B.c2[k] = 0.0f;
-        if (c < n_slots) {
-            bool usable;
-            const float d = score_site(S, stride, c, X, Y, s, usable);
-            const float tau = __expf(S[PLT * stride + c]);
-            const float l = -tau * d;
-            const float r0 = S[PCR * stride + c], r1 = S[PCG * stride + c], r2 = S[PCB * stride + c];
-            if (usable && finitef(l) && finitef(r0) && finitef(r1) && finitef(r2)) {
-                B.id[k] = c;
-                B.l[k] = l;
-                B.c0[k] = r0;
-                B.c1[k] = r1;
-                B.c2[k] = r2;
-                mx = fmaxf(mx, l);
-            }
-        }
+        const SiteRec R = fetch_rec(T, S, st, ids[k], slot[k]);
+        const float l = -R.v[R_TAU] * rec_score(R, X, Y, s);
+        B.use[k] = finitef(l);
+        B.l[k] = l;
+        B.c0[k] = B.use[k] ? R.v[R_C0] : 0.0f;
+        B.c1[k] = B.use[k] ? R.v[R_C1] : 0.0f;
+        B.c2[k] = B.use[k] ? R.v[R_C2] : 0.0f;
+        mx = B.use[k] ? fmaxf(mx, l) : mx;
     }
     B.any = mx > -__builtin_inff();
-    B.Z = 0.0f;
-    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
+    float Z = 0.0f, a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const float e = B.id[k] != NONE ? __expf(B.l[k] - mx) : 0.0f;
+        const float e = B.use[k] ? __expf(B.l[k] - mx) : 0.0f;
         B.e[k] = e;
-        B.Z += e;
+        Z += e;
         a0 += e * B.c0[k];
         a1 += e * B.c1[k];
         a2 += e * B.c2[k];
     }
-    const float iZ = B.any ? 1.0f / B.Z : 0.0f;
+    B.Z = Z;
+    const float iZ = B.any ? 1.0f / Z : 0.0f;
     B.chat0 = a0 * iZ;
     B.chat1 = a1 * iZ;
     B.chat2 = a2 * iZ;
+}
+
+__device__ __forceinline__ void tile_pixel(int nb, int tiles_x, int &col, int &row)
+{
+    const int t = xcd_band(blockIdx.x, nb);
+    col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
+    row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
+}
+
+__device__ __forceinline__ void load_ids(const uint4 *__restrict__ cand, long p, bool inside, uint32_t (&ids)[K])
+{
+    uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
+    if (inside) {
+        a = cand[2 * p];
+        b = cand[2 * p + 1];
+    }
+    ids[0] = a.x;
+    ids[1] = a.y;
+    ids[2] = a.z;
+    ids[3] = a.w;
+    ids[4] = b.x;
+    ids[5] = b.y;
+    ids[6] = b.z;
+    ids[7] = b.w;
 }
 
 // Render forward (reading note, key design 2; project page "Method").
@@ -330,181 +456,336 @@ __global__ __launch_bounds__(BLOCK) void k_render_fwd(const float *__restrict__ 
                                                       const uint4 *__restrict__ cand, int W, int H,
                                                       float *__restrict__ out, float s, int tiles_x, int nb)
 {
-    const int t = xcd_band(blockIdx.x, nb);
-    const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
-    const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
-    if (col >= W || row >= H)
-        return;
+    __shared__ TileTable T;
+    int col, row;
+    tile_pixel(nb, tiles_x, col, row);
+    const bool inside = col < W && row < H;
     const long p = (long)row * W + col;
+    const long st = stride;
+    uint32_t ids[K];
+    int slot[K];
+    load_ids(cand, p, inside, ids);
+    build_tile_table(T, S, st, n_slots, ids, slot);
+    if (!inside)
+        return;
     PixelBlend B;
-    blend_pixel(S, stride, n_slots, cand[2 * p], cand[2 * p + 1], (float)col + 0.5f, (float)row + 0.5f, s, B);
+    blend_pixel(T, S, st, ids, slot, (float)col + 0.5f, (float)row + 0.5f, s, B);
     out[3 * p] = B.chat0;
     out[3 * p + 1] = B.chat1;
     out[3 * p + 2] = B.chat2;
 }
 
 // ---------------------------------------------------------------------------
-// Render backward with per-tile LDS hash reduction (summary, section 5 and B.4;
-// press article section 5: 16x16 tiles).
+// Render backward (summary, section 5 and B.4; press article section 5: 16x16
+// tiles).  Per-entry gradients of L = sum ||c - t||^2, 11 accumulators per site
+// (10 parameters + removal delta).
+//
+// The per-tile reduction avoids LDS float atomics (same-site entries of a tile
+// collide on one address and serialise): entries are counting-sorted by table
+// slot (one integer atomic per entry), each thread then sums a fixed chunk of 8
+// sorted entries -- runs of one site -- in registers, and one thread per site
+// adds the chunk partials of its run and issues one global atomic per
+// accumulator.  Runs that lie strictly inside a chunk are flushed by the chunk
+// thread.  Either way a site gets one global atomic per accumulator per tile.
+constexpr int CHUNK = 8;
+
+// Staged entries live field-major with the 8 entries of one chunk interleaved:
+// sorted entry e sits at column e / CHUNK of row e % CHUNK, so when every thread
+// reads the j-th entry of its chunk the 64 lanes touch 64 consecutive words
+// (no bank conflicts).  The chunk partials alias the same storage column by
+// column: thread t only ever overwrites its own column.
+__device__ __forceinline__ int stage_pos(uint32_t e) { return (int)((e % CHUNK) * BLOCK + e / CHUNK); }
+
+struct BwdShared {
+    TileTable T;
+    uint32_t cnt[TBL];
+    uint32_t off[TBL];
+    float g[3][BLOCK];
+    union {
+        struct {
+            uint32_t ps[BLOCK * K];  // pixel | slot << 8
+            float w[BLOCK * K];
+            float gamma[BLOCK * K];
+            float rdelta[BLOCK * K];
+        } e;
+        float part[2 * SAD_NACC][BLOCK];  // [0,11): head partial, [11,22): tail partial
+    } u;
+    float wsum[BLOCK / 64];
+    uint32_t total;
+};
+
+// The 11 contributions of one entry given its site record, pixel position and
+// the per-entry softmax quantities (derivation: reading note, key designs 1-2).
+__device__ __forceinline__ void entry_grads(const SiteRec &R, float X, float Y, float s, float w, float gamma,
+                                            float rdelta, float g0, float g1, float g2, float (&acc)[SAD_NACC])
+{
+    const float tau = R.v[R_TAU];
+    const float ex = X - R.v[R_PX], ey = Y - R.v[R_PY];
+    const float ux = R.v[R_UX], uy = R.v[R_UY], E = R.v[R_E], iE = R.v[R_IE];
+    const float al = ux * ex + uy * ey;
+    const float be = ux * ey - uy * ex;
+    const float q = sqrtf(E * al * al + iE * be * be);
+    const float d = s * q - s * R.v[R_R];
+    acc[PCR] = w * g0;
+    acc[PCG] = w * g1;
+    acc[PCB] = w * g2;
+    acc[PLT] = gamma * (-tau * d);
+    acc[PR] = tau * gamma * s;
+    acc[PX] = acc[PY] = acc[PA] = acc[PDX] = acc[PDY] = 0.0f;
+    if (q > 0.0f) {
+        const float fq = (-tau * gamma * s) / q;  // (dL/dq) / q
+        const float Ea = E * al, Eb = iE * be;
+        acc[PX] = -fq * (Ea * ux - Eb * uy);
+        acc[PY] = -fq * (Ea * uy + Eb * ux);
+        acc[PA] = 0.5f * fq * (Ea * al - Eb * be);
+        const float in = R.v[R_INVN];
+        if (in > 0.0f) {
+            const float gux = fq * (Ea * ex + Eb * ey);
+            const float guy = fq * (Ea * ey - Eb * ex);
+            const float proj = ux * gux + uy * guy;
+            acc[PDX] = (gux - proj * ux) * in;
+            acc[PDY] = (guy - proj * uy) * in;
+        }
+    }
+    acc[10] = rdelta;
+#pragma unroll
+    for (int a = 0; a < SAD_NACC; ++a)
+        acc[a] = finitef(acc[a]) ? acc[a] : 0.0f;
+}
+
+__device__ __forceinline__ void flush_global(float *__restrict__ grad, long st, uint32_t c, const float (&acc)[SAD_NACC])
+{
+#pragma unroll
+    for (int a = 0; a < SAD_NACC; ++a)
+        if (acc[a] != 0.0f)
+            unsafeAtomicAdd(&grad[a * st + c], acc[a]);
+}
+
 __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float *__restrict__ S, uint32_t n_slots, int stride,
                                                       const uint4 *__restrict__ cand,
                                                       const float *__restrict__ target, int W, int H,
                                                       float *__restrict__ grad, float *__restrict__ loss_sum,
                                                       float s, int tiles_x, int nb)
 {
-    __shared__ uint32_t hkey[HASH_SLOTS];
-    __shared__ float hacc[SAD_NACC][HASH_SLOTS];
-    __shared__ float wloss[BLOCK / 64];
-
-    hkey[threadIdx.x] = NONE;
-#pragma unroll
-    for (int a = 0; a < SAD_NACC; ++a)
-        hacc[a][threadIdx.x] = 0.0f;
-    __syncthreads();
-
-    const int t = xcd_band(blockIdx.x, nb);
-    const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
-    const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
+    __shared__ BwdShared L;
+    const int tid = threadIdx.x;
+    int col, row;
+    tile_pixel(nb, tiles_x, col, row);
+    const int col0 = col - (tid & (TILE - 1)), row0 = row - tid / TILE;
     const bool inside = col < W && row < H;
-    const long stride_l = stride;
-    float err = 0.0f;
+    const long p = (long)row * W + col;
+    const long st = stride;
+    uint32_t ids[K];
+    int slot[K];
+    load_ids(cand, p, inside, ids);
+    L.cnt[tid] = 0;
+    build_tile_table(L.T, S, st, n_slots, ids, slot);
 
+    // phase 3: blend, per-entry softmax quantities, spill entries straight to global
+    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    float err = 0.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
+    float wk[K], gk[K], dk[K];
+    uint32_t pos[K];
+    bool stage[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        stage[k] = false;
     if (inside) {
-        const long p = (long)row * W + col;
-        const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
         PixelBlend B;
-        blend_pixel(S, stride_l, n_slots, cand[2 * p], cand[2 * p + 1], X, Y, s, B);
+        blend_pixel(L.T, S, st, ids, slot, X, Y, s, B);
         const float t0 = target[3 * p], t1 = target[3 * p + 1], t2 = target[3 * p + 2];
         const float r0 = B.chat0 - t0, r1 = B.chat1 - t1, r2 = B.chat2 - t2;
         err = r0 * r0 + r1 * r1 + r2 * r2;
+        g0 = 2.0f * r0;
+        g1 = 2.0f * r1;
+        g2 = 2.0f * r2;
         if (B.any) {
-            const float g0 = 2.0f * r0, g1 = 2.0f * r1, g2 = 2.0f * r2;
             const float iZ = 1.0f / B.Z;
-            // exclusive prefix/suffix sums of e and e*c: the blend without entry k
-            float pe[K], p0[K], p1[K], p2[K];
-            {
-                float se = 0.0f, s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
+            // exclusive sums of e and e*c over the other entries (removal delta)
+            float xe[K], x0[K], x1[K], x2[K];
+            float se = 0.0f, s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    pe[k] = se;
-                    p0[k] = s0;
-                    p1[k] = s1;
-                    p2[k] = s2;
-                    se += B.e[k];
-                    s0 += B.e[k] * B.c0[k];
-                    s1 += B.e[k] * B.c1[k];
-                    s2 += B.e[k] * B.c2[k];
-                }
-                se = s0 = s1 = s2 = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                xe[k] = se;
+                x0[k] = s0;
+                x1[k] = s1;
+                x2[k] = s2;
+                se += B.e[k];
+                s0 += B.e[k] * B.c0[k];
+                s1 += B.e[k] * B.c1[k];
+                s2 += B.e[k] * B.c2[k];
+            }
+            se = s0 = s1 = s2 = 0.0f;
 #pragma unroll
-                for (int k = K - 1; k >= 0; --k) {
-                    pe[k] += se;
-                    p0[k] += s0;
-                    p1[k] += s1;
-                    p2[k] += s2;
-                    se += B.e[k];
-                    s0 += B.e[k] * B.c0[k];
-                    s1 += B.e[k] * B.c1[k];
-                    s2 += B.e[k] * B.c2[k];
-                }
+            for (int k = K - 1; k >= 0; --k) {
+                xe[k] += se;
+                x0[k] += s0;
+                x1[k] += s1;
+                x2[k] += s2;
+                se += B.e[k];
+                s0 += B.e[k] * B.c0[k];
+                s1 += B.e[k] * B.c1[k];
+                s2 += B.e[k] * B.c2[k];
             }
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const uint32_t c = B.id[k];
-                if (c == NONE)
+                if (!B.use[k])
                     continue;
                 const float w = B.e[k] * iZ;
-                float acc[SAD_NACC];
-                acc[PCR] = w * g0;
-                acc[PCG] = w * g1;
-                acc[PCB] = w * g2;
-                const float gamma = w * (g0 * (B.c0[k] - B.chat0) + g1 * (B.c1[k] - B.chat1) + g2 * (B.c2[k] - B.chat2));
-                const float tau = __expf(S[PLT * stride_l + c]);
-                acc[PLT] = gamma * B.l[k];
-                acc[PR] = tau * gamma * s;
-                const float eta = -tau * gamma * s;  // dL/dq
-                // geometry of entry k (same arithmetic as the score)
-                const float px = S[c], py = S[stride_l + c];
-                const float dx = S[PDX * stride_l + c], dy = S[PDY * stride_l + c];
-                const Frame f = make_frame(dx, dy, S[PA * stride_l + c]);
-                const float ex = X - px, ey = Y - py;
-                const float al = f.ux * ex + f.uy * ey;
-                const float be = f.ux * ey - f.uy * ex;
-                const float q = sqrtf(f.E * al * al + f.iE * be * be);
-                acc[PX] = acc[PY] = acc[PA] = acc[PDX] = acc[PDY] = 0.0f;
-                if (q > 0.0f) {
-                    const float fq = eta / q;
-                    const float Ea = f.E * al, Eb = f.iE * be;
-                    // dp = -(eta/q) (E al u + e^-a be v),  v = (-u_y, u_x)
-                    acc[PX] = -fq * (Ea * f.ux - Eb * f.uy);
-                    acc[PY] = -fq * (Ea * f.uy + Eb * f.ux);
-                    acc[PA] = 0.5f * fq * (Ea * al - Eb * be);
-                    const float n2 = dx * dx + dy * dy;
-                    if (n2 >= 1e-30f) {
-                        const float gux = fq * (Ea * ex + Eb * ey);
-                        const float guy = fq * (Ea * ey - Eb * ex);
-                        const float proj = f.ux * gux + f.uy * guy;
-                        const float in = rsqrtf(n2);
-                        acc[PDX] = (gux - proj * f.ux) * in;
-                        acc[PDY] = (guy - proj * f.uy) * in;
-                    }
-                }
-                // removal delta
-                const float Zo = pe[k];
-                const float iZo = Zo > 0.0f ? 1.0f / Zo : 0.0f;
-                const float m0 = p0[k] * iZo - t0, m1 = p1[k] * iZo - t1, m2 = p2[k] * iZo - t2;
-                acc[10] = (m0 * m0 + m1 * m1 + m2 * m2) - err;
-#pragma unroll
-                for (int a = 0; a < SAD_NACC; ++a)
-                    acc[a] = finitef(acc[a]) ? acc[a] : 0.0f;
-                // LDS hash insert (multiplicative hash, <= 8 linear probes, CAS)
-                int slot = -1;
-                const uint32_t h0 = (c * 2654435761u) >> 24;
-                for (int pr = 0; pr < HASH_PROBES; ++pr) {
-                    const uint32_t sl = (h0 + pr) & (HASH_SLOTS - 1);
-                    const uint32_t prev = atomicCAS(&hkey[sl], NONE, c);
-                    if (prev == NONE || prev == c) {
-                        slot = (int)sl;
-                        break;
-                    }
-                }
-                if (slot >= 0) {
-#pragma unroll
-                    for (int a = 0; a < SAD_NACC; ++a)
-                        atomicAdd(&hacc[a][slot], acc[a]);
+                wk[k] = w;
+                gk[k] = w * (g0 * (B.c0[k] - B.chat0) + g1 * (B.c1[k] - B.chat1) + g2 * (B.c2[k] - B.chat2));
+                const float iZo = xe[k] > 0.0f ? 1.0f / xe[k] : 0.0f;
+                const float m0 = x0[k] * iZo - t0, m1 = x1[k] * iZo - t1, m2 = x2[k] * iZo - t2;
+                dk[k] = (m0 * m0 + m1 * m1 + m2 * m2) - err;
+                if (slot[k] >= 0) {
+                    stage[k] = true;
+                    pos[k] = atomicAdd(&L.cnt[slot[k]], 1u);
                 } else {
-#pragma unroll
-                    for (int a = 0; a < SAD_NACC; ++a)
-                        unsafeAtomicAdd(&grad[a * stride_l + c], acc[a]);
+                    float acc[SAD_NACC];
+                    entry_grads(load_rec_global(S, st, ids[k]), X, Y, s, wk[k], gk[k], dk[k], g0, g1, g2, acc);
+                    flush_global(grad, st, ids[k], acc);
                 }
             }
         }
     }
-    // per-pixel loss: wave reduction, then one atomic per workgroup
-    if (loss_sum) {
+    L.g[0][tid] = g0;
+    L.g[1][tid] = g1;
+    L.g[2][tid] = g2;
+    // per-pixel loss: wave sums
+    {
         float v = err;
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1)
             v += __shfl_xor(v, o, 64);
-        if ((threadIdx.x & 63) == 0)
-            wloss[threadIdx.x >> 6] = v;
+        if ((tid & 63) == 0)
+            L.wsum[tid >> 6] = v;
     }
     __syncthreads();
-    if (loss_sum && threadIdx.x == 0) {
-        float v = 0.0f;
+
+    // exclusive scan of the slot counts -> bucket offsets
+    {
+        const uint32_t c = L.cnt[tid];
+        uint32_t incl = c;
 #pragma unroll
-        for (int w = 0; w < BLOCK / 64; ++w)
-            v += wloss[w];
-        unsafeAtomicAdd(loss_sum, v);
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t v = __shfl_up(incl, o, 64);
+            if ((tid & 63) >= o)
+                incl += v;
+        }
+        if ((tid & 63) == 63)
+            L.off[tid] = incl;  // wave total, parked at the wave's last lane
+        __syncthreads();
+        uint32_t base = 0;
+        for (int w = 0; w < (tid >> 6); ++w)
+            base += L.off[w * 64 + 63];
+        const uint32_t tot = L.off[3 * 64 + 63] + L.off[2 * 64 + 63] + L.off[64 + 63] + L.off[63];
+        __syncthreads();
+        L.off[tid] = base + incl - c;
+        if (tid == 0) {
+            L.total = tot;
+            if (loss_sum)
+                unsafeAtomicAdd(loss_sum, L.wsum[0] + L.wsum[1] + L.wsum[2] + L.wsum[3]);
+        }
+        __syncthreads();
     }
-    // flush: one atomic per (site, accumulator) present in the tile
-    const uint32_t key = hkey[threadIdx.x];
-    if (key != NONE) {
+    // stage the entries in slot order
 #pragma unroll
-        for (int a = 0; a < SAD_NACC; ++a) {
-            const float v = hacc[a][threadIdx.x];
-            if (v != 0.0f)
-                unsafeAtomicAdd(&grad[a * stride_l + key], v);
+    for (int k = 0; k < K; ++k) {
+        if (stage[k]) {
+            const int q = stage_pos(L.off[slot[k]] + pos[k]);
+            L.u.e.ps[q] = (uint32_t)tid | ((uint32_t)slot[k] << 8);
+            L.u.e.w[q] = wk[k];
+            L.u.e.gamma[q] = gk[k];
+            L.u.e.rdelta[q] = dk[k];
+        }
+    }
+    __syncthreads();
+
+    // phase 4: chunk of 8 sorted entries per thread, runs summed in registers
+    const uint32_t total = L.total;
+    const uint32_t b0 = (uint32_t)tid * CHUNK;
+    uint32_t mps[CHUNK];
+    float mw[CHUNK], mg[CHUNK], md[CHUNK];
+    int nmine = 0;
+    if (b0 < total) {
+        nmine = min((int)(total - b0), CHUNK);
+#pragma unroll
+        for (int j = 0; j < CHUNK; ++j) {
+            if (j < nmine) {
+                const int q = j * BLOCK + tid;  // stage_pos(b0 + j)
+                mps[j] = L.u.e.ps[q];
+                mw[j] = L.u.e.w[q];
+                mg[j] = L.u.e.gamma[q];
+                md[j] = L.u.e.rdelta[q];
+            }
+        }
+    }
+    // from here on this thread's column of the staging area holds its partials
+    if (nmine > 0) {
+        float run[SAD_NACC];
+#pragma unroll
+        for (int a = 0; a < SAD_NACC; ++a)
+            run[a] = 0.0f;
+        int cur = (int)(mps[0] >> 8);
+        SiteRec Rc = table_rec(L.T, cur);
+        bool first = true;
+#pragma unroll
+        for (int j = 0; j < CHUNK; ++j) {
+            if (j < nmine) {
+                const int sl = (int)(mps[j] >> 8);
+                if (sl != cur) {
+                    // close the run of `cur`: the chunk's first run becomes its head
+                    // partial; a later run is a whole bucket and is flushed here
+                    if (first) {
+#pragma unroll
+                        for (int a = 0; a < SAD_NACC; ++a)
+                            L.u.part[a][tid] = run[a];
+                        first = false;
+                    } else {
+                        flush_global(grad, st, L.T.key[cur], run);
+                    }
+#pragma unroll
+                    for (int a = 0; a < SAD_NACC; ++a)
+                        run[a] = 0.0f;
+                    cur = sl;
+                    Rc = table_rec(L.T, cur);
+                }
+                const int pp = (int)(mps[j] & 0xFFu);
+                const float Xp = (float)(col0 + (pp & (TILE - 1))) + 0.5f;
+                const float Yp = (float)(row0 + pp / TILE) + 0.5f;
+                float acc[SAD_NACC];
+                entry_grads(Rc, Xp, Yp, s, mw[j], mg[j], md[j], L.g[0][pp], L.g[1][pp], L.g[2][pp], acc);
+#pragma unroll
+                for (int a = 0; a < SAD_NACC; ++a)
+                    run[a] += acc[a];
+            }
+        }
+        // the last run: head if it is also the first, else tail
+#pragma unroll
+        for (int a = 0; a < SAD_NACC; ++a)
+            L.u.part[(first ? 0 : SAD_NACC) + a][tid] = run[a];
+    }
+    __syncthreads();
+
+    // phase 5: one thread per site combines the chunk partials of its bucket
+    const uint32_t c = L.cnt[tid];
+    if (c > 0) {
+        const uint32_t b = L.off[tid], e = b + c - 1;
+        const uint32_t t0 = b / CHUNK, t1 = e / CHUNK;
+        const uint32_t end0 = min(t0 * CHUNK + CHUNK, total) - 1;
+        const bool starts_chunk = (b == t0 * CHUNK);
+        if (t0 != t1 || starts_chunk || e == end0) {
+            float acc[SAD_NACC];
+            const int h0 = starts_chunk ? 0 : SAD_NACC;
+#pragma unroll
+            for (int a = 0; a < SAD_NACC; ++a)
+                acc[a] = L.u.part[h0 + a][t0];
+            for (uint32_t t = t0 + 1; t <= t1; ++t) {
+#pragma unroll
+                for (int a = 0; a < SAD_NACC; ++a)
+                    acc[a] += L.u.part[a][t];
+            }
+            flush_global(grad, st, L.T.key[tid], acc);
         }
     }
 }
