@@ -37,8 +37,8 @@ def algorithmic_bytes(P, N):
     forward:   map (32 B/px) + image out (12 B/px) + all ten site fields (40 B/site)
     backward:  map (32 B/px) + target (12 B/px) + site fields (40 B/site) + one
                read-modify-write flush of 11 accumulators (44 B/site)
-    adam:      params, m, v read and written (240 B/site) + 10 grad planes read
-               and zeroed (80 B/site)
+    adam:      params, m, v read and written (240 B/site) + the 10 gradients of
+               the site's record read and zeroed (80 B/site)
     """
     return {
         "propagate": 64 * P + 24 * N,

@@ -36,8 +36,11 @@
  *         per pixel), SAD_INVALID marks an empty entry.  16-byte aligned.  Lists
  *         written by this library hold distinct IDs in ascending (d, ID) order.
  * images: float [H][W][3] (RGB, linear).
- * grad  : float [SAD_NACC][stride] -- ten gradient planes in the site order, then
- *         the removal delta ([SUM] B.4: 11 accumulators per site).
+ * grad  : float [stride][SAD_GRAD_LD] -- one 64-byte record per site: the ten
+ *         gradients in site order at [0,10), the removal delta at [10] ([SUM] B.4:
+ *         11 accumulators per site), words [11,16) unused and never written.
+ *         16-byte aligned.  (A record per site lets the atomics that flush one
+ *         site's 11 sums share one cache line.)
  * m, v  : float [SAD_NPARAM][stride] Adam moments.
  * Pixel (col,row) is evaluated at (col+0.5, row+0.5) px ([SUM] B.3 evaluates at
  * centred cells).  Limits: 1 <= W, H <= 65535 (W or H = 0 is an empty image: a
@@ -63,6 +66,7 @@ extern "C" {
 #define SAD_INVALID 0xffffffffu
 #define SAD_NPARAM 10
 #define SAD_NACC 11
+#define SAD_GRAD_LD 16
 #define SAD_MAX_INJECT 16
 #define SAD_MAX_DIM 65535
 
@@ -145,7 +149,7 @@ int sad_render_fwd(const float *sites, int n_slots, int stride, const uint32_t *
  * (+=) into `grad`.  Per pixel, g = 2(c - t); per usable entry k:
  *   dc_k = w_k g;  gamma_k = w_k g.(c_k - c);  dlog_tau_k = gamma_k l_k;
  *   dd_k = -tau_k gamma_k;  then through d = s q - s r to p, r, dir, a.
- * Plane 10 receives the removal delta ||c_{-k} - t||^2 - ||c - t||^2, c_{-k} the
+ * Accumulator 10 receives the removal delta ||c_{-k} - t||^2 - ||c - t||^2, c_{-k} the
  * blend of the other entries renormalised (0 if none carries weight)
  * ([SUM] B.4-B.5).  Non-finite contributions are dropped.  Contributions are
  * summed per 16x16 tile in an LDS hash table keyed by site ID (256 slots,
@@ -153,11 +157,11 @@ int sad_render_fwd(const float *sites, int n_slots, int stride, const uint32_t *
  * atomic per site and accumulator per tile; an entry that finds no slot goes
  * straight to global atomics ([SUM] section 5, B.4).  Float atomics make the
  * summation order, hence the last bits, vary from run to run.
- *   target device [H][W][3] read-only; grad device [11][stride] float, +=;
+ *   target device [H][W][3] read-only; grad device [stride][16] float, +=;
  *   loss_sum device float or NULL, += sum_x ||c - t||^2.
- * The caller zeroes `grad` once; sad_adam_step re-zeroes planes 0..9 each step;
- * plane 10 keeps accumulating until the caller resets it.
- * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
+ * The caller zeroes `grad` once; sad_adam_step re-zeroes accumulators 0..9 each
+ * step; accumulator 10 keeps accumulating until the caller resets it.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN (cand or grad not 16-byte aligned), SAD_ERR_DEVICE.
  */
 int sad_render_bwd(const float *sites, int n_slots, int stride, const uint32_t *cand, const float *target, int W,
                    int H, float *grad, float *loss_sum, void *stream);
@@ -166,13 +170,14 @@ int sad_render_bwd(const float *sites, int n_slots, int stride, const uint32_t *
  * sad_adam_step -- Adam (Kingma & Ba 2015) on the ten site parameters, with the
  * accumulated gradients divided by the pixel count ([SUM] B.4).  For each slot
  * i < n_slots with x >= 0 and each parameter j:
- *   g = grad[j][i] / n_pixels (non-finite -> 0);  m = b1 m + (1-b1) g;
+ *   g = grad[i][j] / n_pixels (non-finite -> 0);  m = b1 m + (1-b1) g;
  *   v = b2 v + (1-b2) g^2;  p -= lr_j (m / (1-b1^step)) / (sqrt(v / (1-b2^step)) + eps);
- * then x is clamped to [0, W] and y to [0, H].  Planes 0..9 of grad are zeroed
- * for every slot < n_slots; plane 10 is left alone.  Inactive slots keep p, m, v.
- *   sites, m, v device [10][stride] float (in/out); grad device [11][stride];
- *   step >= 1 (global, 1-based); n_pixels >= 1; cfg HOST pointer.
- * Errors: SAD_ERR_ARG, SAD_ERR_DEVICE.
+ * then x is clamped to [0, W] and y to [0, H].  Accumulators 0..9 of grad are
+ * zeroed for every slot < n_slots; accumulator 10 is left alone.  Inactive slots
+ * keep p, m, v.
+ *   sites, m, v device [10][stride] float (in/out); grad device [stride][16],
+ *   16-byte aligned; step >= 1 (global, 1-based); n_pixels >= 1; cfg HOST pointer.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
 int sad_adam_step(float *sites, float *m, float *v, float *grad, int n_slots, int stride, int step, int n_pixels,
                   int W, int H, const sad_adam_cfg *cfg, void *stream);

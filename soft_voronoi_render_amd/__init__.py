@@ -9,7 +9,8 @@ raises.
 
 Layouts (see include/sad.h): sites float32 [10][stride], candidate map uint32
 [H][W][8] (torch int32 storage reinterpreted), images float32 [H][W][3], grad
-float32 [11][stride], Adam moments float32 [10][stride].
+float32 [stride][16] (one 64-byte record per site: 10 gradients, the removal
+delta, 5 unused words), Adam moments float32 [10][stride].
 """
 from __future__ import annotations
 
@@ -30,6 +31,7 @@ K = 8
 INVALID = 0xFFFFFFFF
 NPARAM = 10
 NACC = 11
+GRAD_LD = 16
 MAX_INJECT = 16
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "misaligned pointer", -3: "HIP launch failed",
@@ -172,7 +174,7 @@ def render_bwd(sites, n_slots, cand, target, W, H, grad, loss_sum=None, stream=N
     sp, stride = _sites(sites, n_slots)
     c = _dev(cand, "cand", _U32, (H, W, K))
     t = _dev(target, "target", _F32, (H, W, 3))
-    g = _dev(grad, "grad", _F32, (NACC, stride))
+    g = _dev(grad, "grad", _F32, (stride, GRAD_LD))
     ls = _dev(loss_sum, "loss_sum", _F32) if loss_sum is not None else None
     _check("sad_render_bwd", lib().sad_render_bwd(sp, n_slots, stride, c, t, W, H, g, ls, _stream(stream)))
 
@@ -199,7 +201,7 @@ def adam_step(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamConfig 
     sp, stride = _sites(sites, n_slots)
     mp = _dev(m, "m", _F32, (NPARAM, stride))
     vp = _dev(v, "v", _F32, (NPARAM, stride))
-    g = _dev(grad, "grad", _F32, (NACC, stride))
+    g = _dev(grad, "grad", _F32, (stride, GRAD_LD))
     c = cfg.to_c() if isinstance(cfg, AdamConfig) else (cfg if cfg is not None else AdamConfig().to_c())
     _check("sad_adam_step", lib().sad_adam_step(sp, mp, vp, g, n_slots, stride, step, n_pixels, W, H,
                                                 ctypes.byref(c), _stream(stream)))
@@ -214,6 +216,16 @@ def jump_schedule(W: int, H: int, n: int) -> list:
         out.append(max(k, 1))
         k //= 2
     return out
+
+
+def new_grad(stride: int, device="cuda") -> torch.Tensor:
+    """Zeroed gradient accumulators, float32 [stride][16]."""
+    return torch.zeros((stride, GRAD_LD), dtype=torch.float32, device=device)
+
+
+def grad_planes(grad: torch.Tensor):
+    """The 11 accumulators as planes [11][stride] (a host-side view for inspection)."""
+    return grad[:, :NACC].t()
 
 
 def new_map(W: int, H: int, device="cuda") -> torch.Tensor:
@@ -235,7 +247,7 @@ class Fitter:
         stride = sites.shape[1]
         self.m = torch.zeros((NPARAM, stride), dtype=torch.float32, device=dev)
         self.v = torch.zeros((NPARAM, stride), dtype=torch.float32, device=dev)
-        self.grad = torch.zeros((NACC, stride), dtype=torch.float32, device=dev)
+        self.grad = torch.zeros((stride, GRAD_LD), dtype=torch.float32, device=dev)
         self.maps = [cand if cand is not None else new_map(W, H, dev), new_map(W, H, dev)]
         self.cur = 0
         self.rgb = torch.empty((H, W, 3), dtype=torch.float32, device=dev)

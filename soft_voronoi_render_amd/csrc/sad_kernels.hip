@@ -508,7 +508,10 @@ struct BwdShared {
             float gamma[BLOCK * K];
             float rdelta[BLOCK * K];
         } e;
-        float part[2 * SAD_NACC][BLOCK];  // [0,11): head partial, [11,22): tail partial
+        struct {
+            float part[2 * SAD_NACC][BLOCK];  // per chunk: [0,11) head partial, [11,22) tail partial
+            float fin[SAD_NACC][TBL];         // per table slot: the tile's total
+        } r;
     } u;
     float wsum[BLOCK / 64];
     uint32_t total;
@@ -553,12 +556,14 @@ __device__ __forceinline__ void entry_grads(const SiteRec &R, float X, float Y, 
         acc[a] = finitef(acc[a]) ? acc[a] : 0.0f;
 }
 
-__device__ __forceinline__ void flush_global(float *__restrict__ grad, long st, uint32_t c, const float (&acc)[SAD_NACC])
+// One lane adds the 11 accumulators of one site (used for spilled entries only;
+// the regular path flushes cooperatively, see phase 6 below).
+__device__ __forceinline__ void flush_global(float *__restrict__ grad, uint32_t c, const float (&acc)[SAD_NACC])
 {
 #pragma unroll
     for (int a = 0; a < SAD_NACC; ++a)
         if (acc[a] != 0.0f)
-            unsafeAtomicAdd(&grad[a * st + c], acc[a]);
+            unsafeAtomicAdd(&grad[(long)c * SAD_GRAD_LD + a], acc[a]);
 }
 
 __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float *__restrict__ S, uint32_t n_slots, int stride,
@@ -643,7 +648,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float *__restrict__ 
                 } else {
                     float acc[SAD_NACC];
                     entry_grads(load_rec_global(S, st, ids[k]), X, Y, s, wk[k], gk[k], dk[k], g0, g1, g2, acc);
-                    flush_global(grad, st, ids[k], acc);
+                    flush_global(grad, ids[k], acc);
                 }
             }
         }
@@ -720,7 +725,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float *__restrict__ 
             }
         }
     }
-    // from here on this thread's column of the staging area holds its partials
+    __syncthreads();  // the staging area is reused for the partials and totals below
     if (nmine > 0) {
         float run[SAD_NACC];
 #pragma unroll
@@ -735,18 +740,16 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float *__restrict__ 
                 const int sl = (int)(mps[j] >> 8);
                 if (sl != cur) {
                     // close the run of `cur`: the chunk's first run becomes its head
-                    // partial; a later run is a whole bucket and is flushed here
-                    if (first) {
+                    // partial; a later run is a whole bucket: its total is final
 #pragma unroll
-                        for (int a = 0; a < SAD_NACC; ++a)
-                            L.u.part[a][tid] = run[a];
-                        first = false;
-                    } else {
-                        flush_global(grad, st, L.T.key[cur], run);
-                    }
-#pragma unroll
-                    for (int a = 0; a < SAD_NACC; ++a)
+                    for (int a = 0; a < SAD_NACC; ++a) {
+                        if (first)
+                            L.u.r.part[a][tid] = run[a];
+                        else
+                            L.u.r.fin[a][cur] = run[a];
                         run[a] = 0.0f;
+                    }
+                    first = false;
                     cur = sl;
                     Rc = table_rec(L.T, cur);
                 }
@@ -763,29 +766,44 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float *__restrict__ 
         // the last run: head if it is also the first, else tail
 #pragma unroll
         for (int a = 0; a < SAD_NACC; ++a)
-            L.u.part[(first ? 0 : SAD_NACC) + a][tid] = run[a];
+            L.u.r.part[(first ? 0 : SAD_NACC) + a][tid] = run[a];
     }
     __syncthreads();
 
-    // phase 5: one thread per site combines the chunk partials of its bucket
+    // phase 5: one thread per site adds up the chunk partials of its bucket
     const uint32_t c = L.cnt[tid];
     if (c > 0) {
         const uint32_t b = L.off[tid], e = b + c - 1;
         const uint32_t t0 = b / CHUNK, t1 = e / CHUNK;
         const uint32_t end0 = min(t0 * CHUNK + CHUNK, total) - 1;
         const bool starts_chunk = (b == t0 * CHUNK);
-        if (t0 != t1 || starts_chunk || e == end0) {
+        if (t0 != t1 || starts_chunk || e == end0) {  // else: a middle run, already final
             float acc[SAD_NACC];
             const int h0 = starts_chunk ? 0 : SAD_NACC;
 #pragma unroll
             for (int a = 0; a < SAD_NACC; ++a)
-                acc[a] = L.u.part[h0 + a][t0];
+                acc[a] = L.u.r.part[h0 + a][t0];
             for (uint32_t t = t0 + 1; t <= t1; ++t) {
 #pragma unroll
                 for (int a = 0; a < SAD_NACC; ++a)
-                    acc[a] += L.u.part[a][t];
+                    acc[a] += L.u.r.part[a][t];
             }
-            flush_global(grad, st, L.T.key[tid], acc);
+#pragma unroll
+            for (int a = 0; a < SAD_NACC; ++a)
+                L.u.r.fin[a][tid] = acc[a];
+        }
+    }
+    __syncthreads();
+
+    // phase 6: cooperative flush -- consecutive lanes take consecutive accumulators
+    // of one site, so the lanes of an atomic instruction share the site's 64-byte
+    // gradient record instead of touching one cache line each
+    for (int i = tid; i < TBL * SAD_NACC; i += BLOCK) {
+        const int sl = i / SAD_NACC, a = i - sl * SAD_NACC;
+        if (L.cnt[sl] > 0) {
+            const float v = L.u.r.fin[a][sl];
+            if (v != 0.0f)
+                unsafeAtomicAdd(&grad[(long)L.T.key[sl] * SAD_GRAD_LD + a], v);
         }
     }
 }
@@ -806,11 +824,16 @@ __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__re
         return;
     const long st = stride;
     const bool active = !(S[i] < 0.0f);
+    float4 *gr = reinterpret_cast<float4 *>(G + (long)i * SAD_GRAD_LD);
+    const float4 ga = gr[0], gb = gr[1], gc = gr[2];
+    const float gv[SAD_NPARAM] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w, gc.x, gc.y};
+    gr[0] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    gr[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    reinterpret_cast<float2 *>(gr + 2)[0] = make_float2(0.0f, 0.0f);
 #pragma unroll
     for (int j = 0; j < SAD_NPARAM; ++j) {
         const long o = j * st + i;
-        float g = G[o];
-        G[o] = 0.0f;
+        float g = gv[j];
         if (active) {
             g *= A.inv_p;
             if (!finitef(g))
@@ -964,7 +987,7 @@ int sad_render_bwd(const float *sites, int n_slots, int stride, const uint32_t *
         return SAD_OK;
     if (!sites || !cand || !target || !grad)
         return SAD_ERR_ARG;
-    if (!aligned16(cand))
+    if (!aligned16(cand) || !aligned16(grad))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
     hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, sites, (uint32_t)n_slots,
@@ -982,6 +1005,8 @@ int sad_adam_step(float *sites, float *m, float *v, float *grad, int n_slots, in
         return SAD_ERR_ARG;
     if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f && cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f && cfg->eps >= 0.0f))
         return SAD_ERR_ARG;
+    if (!aligned16(grad))
+        return SAD_ERR_ALIGN;
     if (n_slots == 0)
         return SAD_OK;
     AdamArgs A;

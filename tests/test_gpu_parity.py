@@ -136,13 +136,15 @@ def _bwd(S, n, cand, tgt, W, H, grad0=None):
     S_d = to_dev(S)
     c = to_dev(cand)
     t = to_dev(tgt)
-    g = torch.zeros((11, S.shape[1]), dtype=torch.float32, device=S_d.device)
+    g = sad.new_grad(S.shape[1], S_d.device)
     if grad0 is not None:
-        g.copy_(torch.from_numpy(grad0))
+        g[:, :11].copy_(torch.from_numpy(grad0).t())
     loss = torch.zeros(1, dtype=torch.float32, device=S_d.device)
     sad.render_bwd(S_d, n, c, t, W, H, g, loss)
     torch.cuda.synchronize()
-    return g.cpu().numpy().astype(np.float64), float(loss.item())
+    gh = g.cpu().numpy().astype(np.float64)
+    assert (gh[:, 11:] == 0).all(), "unused words of the gradient records were written"
+    return np.ascontiguousarray(gh[:, :11].T), float(loss.item())
 
 
 def _check_grads(got, ref, planes=range(11)):
@@ -198,10 +200,17 @@ def test_render_bwd_edge_inputs_and_accumulation(orc):
 
 
 def _adam_gpu(S, m, v, G, n, step, P, W, H, cfg):
-    S_d, m_d, v_d, g_d = (to_dev(np.ascontiguousarray(a, dtype=np.float32)) for a in (S, m, v, G))
+    """G: planes [11][stride]; the library takes per-site records [stride][16]."""
+    S_d, m_d, v_d = (to_dev(np.ascontiguousarray(a, dtype=np.float32)) for a in (S, m, v))
+    rec = np.zeros((S.shape[1], 16), dtype=np.float32)
+    rec[:, :11] = G.T
+    rec[:, 11:] = 7.0  # unused words: must survive untouched
+    g_d = to_dev(rec)
     sad.adam_step(S_d, m_d, v_d, g_d, n, step, P, W, H, cfg)
     torch.cuda.synchronize()
-    return [t.cpu().numpy().astype(np.float64) for t in (S_d, m_d, v_d, g_d)]
+    gh = g_d.cpu().numpy()
+    assert (gh[:, 11:] == 7.0).all()
+    return [t.cpu().numpy().astype(np.float64) for t in (S_d, m_d, v_d)] + [np.ascontiguousarray(gh[:, :11].T).astype(np.float64)]
 
 
 @pytest.mark.parametrize("step", [1, 2, 10, 1000])
@@ -236,7 +245,7 @@ def test_empty_image_and_no_sites_are_noops():
     sad.topk_propagate(z, 4, m0, sad.new_map(0, 0), 0, 0, 1, 0, 0, 4)
     out = torch.empty((0, 0, 3), dtype=torch.float32, device="cuda")
     sad.render_fwd(z, 4, m0, 0, 0, out)
-    g = torch.zeros((11, 4), dtype=torch.float32, device="cuda")
+    g = sad.new_grad(4)
     sad.adam_step(z, torch.zeros_like(z), torch.zeros_like(z), g, 0, 1, 1, 1, 1)
     torch.cuda.synchronize()
 
