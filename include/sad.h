@@ -42,6 +42,15 @@
  *         16-byte aligned.  (A record per site lets the atomics that flush one
  *         site's 11 sums share one cache line.)
  * m, v  : float [SAD_NPARAM][stride] Adam moments.
+ * geom  : float [n_slots][SAD_GEOM_LD] -- the scoring record of each site, derived
+ *         from `sites` by sad_site_geometry and refreshed by sad_adam_step: the
+ *         fp32 counterpart of the compact per-site buffer the candidate-update
+ *         kernels read in the pages ([SUM] B.2 "Packed candidate sites"):
+ *           (x, y, r, Ux, Uy, Vx, Vy, 0),  U = e^{a/2} u,  V = e^{-a/2} u,
+ *         so ||delta||_G^2 = (U.delta)^2 + (Vx delta_y - Vy delta_x)^2.  A slot with
+ *         x < 0 stays inactive.  16-byte aligned.  It is a cache the caller keeps
+ *         in step with `sites`: recompute it after any change made outside
+ *         sad_adam_step.
  * Pixel (col,row) is evaluated at (col+0.5, row+0.5) px ([SUM] B.3 evaluates at
  * centred cells).  Limits: 1 <= W, H <= 65535 (W or H = 0 is an empty image: a
  * no-op returning SAD_OK after the scalar arguments are checked; its pointers
@@ -67,6 +76,7 @@ extern "C" {
 #define SAD_NPARAM 10
 #define SAD_NACC 11
 #define SAD_GRAD_LD 16
+#define SAD_GEOM_LD 8
 #define SAD_MAX_INJECT 16
 #define SAD_MAX_DIM 65535
 
@@ -94,6 +104,14 @@ int sad_abi_version(void);
 const char *sad_status_string(int status);
 
 /*
+ * sad_site_geometry -- writes the scoring record (see `geom` above) of slots
+ * [0, n_slots) from the site planes.
+ *   sites device [10][stride] read-only; geom device [n_slots][8] float, written.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN (geom not 16-byte aligned), SAD_ERR_DEVICE.
+ */
+int sad_site_geometry(const float *sites, int n_slots, int stride, float *geom, void *stream);
+
+/*
  * sad_topk_propagate -- one propagation pass of the candidate map.
  * [NOTE] design 3: C~_t(x) = C_{t-1}(x) U P_t(x) U G_t(x), keep the top-K under d;
  * [SUM] section 4: self plus 4 neighbours at the current jump, plus a small
@@ -112,25 +130,25 @@ const char *sad_status_string(int status);
  * padded with SAD_INVALID.  The pass reads cand_in and writes cand_out (Jacobi).
  * The host chooses the schedule: jumps B/2, B/4, ..., 1 then 1 ([SUM] section 4).
  *
- *   sites     device, [10][stride] float, read-only
+ *   geom      device, [n_slots][8] float scoring records, read-only
  *   cand_in   device, [H][W][8] uint32, read-only, 16-byte aligned
  *   cand_out  device, [H][W][8] uint32, written; must not overlap cand_in
  *   jump      1..65535;  n_inject 0..SAD_MAX_INJECT
  * Errors: SAD_ERR_ARG (bad sizes, jump, n_inject, NULL, overlapping maps),
- *         SAD_ERR_ALIGN (cand not 16-byte aligned), SAD_ERR_DEVICE.
+ *         SAD_ERR_ALIGN (a pointer not 16-byte aligned), SAD_ERR_DEVICE.
  */
-int sad_topk_propagate(const float *sites, int n_slots, int stride, const uint32_t *cand_in, uint32_t *cand_out,
-                       int W, int H, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream);
+int sad_topk_propagate(const float *geom, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
+                       int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream);
 
 /*
  * sad_topk_exact -- the exact top-K map by brute force over every slot: the list
  * that propagation approximates ([NOTE] design 3; [SUM] section 4 "Candidate
  * maintenance").  Used to (re)initialise a map and to measure recall.  Cost
  * O(W*H*n_slots).  Same output convention as sad_topk_propagate.
- *   sites device [10][stride] read-only;  cand_out device [H][W][8], written.
+ *   geom device [n_slots][8] read-only;  cand_out device [H][W][8], written.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_topk_exact(const float *sites, int n_slots, int stride, uint32_t *cand_out, int W, int H, void *stream);
+int sad_topk_exact(const float *geom, int n_slots, uint32_t *cand_out, int W, int H, void *stream);
 
 /*
  * sad_render_fwd -- the temperature-softmax blend of each pixel's list.
@@ -174,13 +192,15 @@ int sad_render_bwd(const float *sites, int n_slots, int stride, const uint32_t *
  *   v = b2 v + (1-b2) g^2;  p -= lr_j (m / (1-b1^step)) / (sqrt(v / (1-b2^step)) + eps);
  * then x is clamped to [0, W] and y to [0, H].  Accumulators 0..9 of grad are
  * zeroed for every slot < n_slots; accumulator 10 is left alone.  Inactive slots
- * keep p, m, v.
+ * keep p, m, v.  If geom is not NULL the scoring records of slots [0, n_slots)
+ * are rewritten from the updated sites in the same pass.
  *   sites, m, v device [10][stride] float (in/out); grad device [stride][16],
- *   16-byte aligned; step >= 1 (global, 1-based); n_pixels >= 1; cfg HOST pointer.
+ *   16-byte aligned; geom device [n_slots][8] or NULL; step >= 1 (global,
+ *   1-based); n_pixels >= 1; cfg HOST pointer.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_adam_step(float *sites, float *m, float *v, float *grad, int n_slots, int stride, int step, int n_pixels,
-                  int W, int H, const sad_adam_cfg *cfg, void *stream);
+int sad_adam_step(float *sites, float *m, float *v, float *grad, float *geom, int n_slots, int stride, int step,
+                  int n_pixels, int W, int H, const sad_adam_cfg *cfg, void *stream);
 
 #ifdef __cplusplus
 }

@@ -94,6 +94,54 @@ __device__ __forceinline__ float score_site(const float *__restrict__ S, long st
 }
 
 // ---------------------------------------------------------------------------
+// Scoring record of one site, 32 bytes, the fp32 counterpart of the pages'
+// compact candidate-site buffer (summary, Appendix B.2 "Packed candidate sites"):
+//   (x, y, r, Ux) (Uy, Vx, Vy, 0)  with  U = e^{a/2} u,  V = e^{-a/2} u,
+// so that ||delta||_G^2 = (U.delta)^2 + (V x delta)^2 = e^a alpha^2 + e^-a beta^2 --
+// a sum of squares, as in the definition, with no cancellation.  A candidate
+// costs two 16-byte loads and no transcendental besides the square root.
+constexpr int GLD = SAD_GEOM_LD;
+
+__device__ __forceinline__ void make_geom(float x, float y, float r, float dx, float dy, float a, float4 &g0,
+                                          float4 &g1)
+{
+    const Frame f = make_frame(dx, dy, a);
+    const float sE = __expf(0.5f * a), siE = __expf(-0.5f * a);
+    g0 = make_float4(x, y, r, sE * f.ux);
+    g1 = make_float4(sE * f.uy, siE * f.ux, siE * f.uy, 0.0f);
+}
+
+__device__ __forceinline__ float geom_score(const float4 &g0, const float4 &g1, float X, float Y, float s)
+{
+    const float ex = X - g0.x, ey = Y - g0.y;
+    const float t1 = g0.w * ex + g1.x * ey;  // e^{a/2} (u . delta)
+    const float t2 = g1.y * ey - g1.z * ex;  // e^{-a/2} (u x delta)
+    const float q = sqrtf(t1 * t1 + t2 * t2);
+    return s * q - s * g0.z;
+}
+
+__device__ __forceinline__ float geom_score_id(const float4 *__restrict__ G, uint32_t id, float X, float Y, float s,
+                                               bool &usable)
+{
+    const float4 g0 = G[2 * (size_t)id], g1 = G[2 * (size_t)id + 1];
+    usable = !(g0.x < 0.0f);
+    return geom_score(g0, g1, X, Y, s);
+}
+
+__global__ __launch_bounds__(256) void k_site_geometry(const float *__restrict__ S, int n_slots, int stride,
+                                                       float4 *__restrict__ G)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_slots)
+        return;
+    const long st = stride;
+    float4 g0, g1;
+    make_geom(S[i], S[st + i], S[PR * st + i], S[PDX * st + i], S[PDY * st + i], S[PA * st + i], g0, g1);
+    G[2 * (size_t)i] = g0;
+    G[2 * (size_t)i + 1] = g1;
+}
+
+// ---------------------------------------------------------------------------
 // Counter-based injection (paperlayer.ai summary, Appendix B.3: the pass word and
 // the pixel ID seed xorshift).  pcg hash: Jarzynski & Olano, JCGT 2020;
 // xorshift32 (13,17,5): Marsaglia 2003; range: Lemire's multiply-shift.
@@ -149,122 +197,365 @@ struct TopK {
 };
 
 // ---------------------------------------------------------------------------
-// Propagation pass (reading note, key design 3; summary, section 4 and B.3).
-// One lane per pixel.  Candidates are visited own list -> 4 neighbour lists ->
-// injected IDs; a candidate already in the running list is skipped (a repeat of
-// one that was rejected or evicted is rejected again, since the K-th key only
-// decreases), so the result equals the top-K of the deduplicated union.
-__global__ __launch_bounds__(BLOCK) void k_propagate(const float *__restrict__ S, uint32_t n_slots, int stride,
-                                                     const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
-                                                     int H, int jump, uint32_t pw, uint32_t seed_h, int n_inject,
-                                                     float s, int tiles_x, int nb)
+// Inserts one list's IDs into an LDS hash table of TB slots keyed by site ID
+// (multiplicative hash, <= HASH_PROBES linear probes, CAS insert -- summary,
+// B.4).  refs[k]: the slot, REF_SPILL | ID if every probe is taken by other IDs,
+// REF_NONE when ids[k] >= n_slots.  (Measured on gfx950: one CAS per probe, ID
+// by ID, beats reading the slot first and beats issuing the CAS of all IDs of a
+// list at once -- same-address atomics from many lanes serialise.)
+constexpr uint32_t REF_NONE = 0xFFFFFFFFu;
+constexpr uint32_t REF_SPILL = 0x80000000u;  // | site ID
+
+template <int TB>
+__device__ __forceinline__ void table_insert_ids(uint32_t *key, const uint32_t (&ids)[K], uint32_t n_slots,
+                                                 uint32_t (&refs)[K])
 {
+    constexpr int SHIFT = TB == 256 ? 24 : 23;
+    static_assert(TB == 256 || TB == 512, "table size");
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const uint32_t c = ids[k];
+        uint32_t r = REF_NONE;
+        if (c < n_slots) {
+            r = REF_SPILL | c;
+            const uint32_t h0 = (c * 2654435761u) >> SHIFT;
+            for (int pr = 0; pr < HASH_PROBES; ++pr) {
+                const uint32_t sl = (h0 + pr) & (TB - 1);
+                const uint32_t prev = atomicCAS(&key[sl], NONE, c);
+                if (prev == NONE || prev == c) {
+                    r = sl;
+                    break;
+                }
+            }
+        }
+        refs[k] = r;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Propagation pass (reading note, key design 3; summary, section 4 and B.3).
+//
+// One 16x16 tile per workgroup, one pixel per lane.  A pixel's candidates are
+// its own list, the lists at +-jump in x and y (skipped outside the image) and
+// n_inject injected IDs.  The lists the tile needs -- its own block plus four
+// strips of width min(jump, 16) beyond its edges -- are loaded once; every ID in
+// them goes into an LDS site table (hash keyed by ID, read-then-CAS insert) and
+// each list entry is replaced by its table slot.  Each distinct site is then
+// gathered once per tile and its metric frame computed once, so scoring a list
+// candidate costs two LDS reads instead of six scattered global loads.  IDs the
+// table cannot hold ("spills") and injected IDs are read from global memory.
+//
+// Selection: candidates are ranked by a 64-bit key (order-preserving bits of d,
+// then the ID) -- the (d, ID) order.  A candidate is inserted when its key beats
+// the current K-th and its ID is not yet held; a repeat of an ID that was
+// rejected or evicted earlier is rejected again (the K-th key only decreases),
+// so the result is the top-K of the deduplicated union.
+__device__ __forceinline__ uint64_t rank_key(float d, uint32_t id)
+{
+    uint32_t u = __float_as_uint(d + 0.0f);  // -0 -> +0
+    u ^= (u & 0x80000000u) ? 0xFFFFFFFFu : 0x80000000u;
+    return ((uint64_t)u << 32) | id;
+}
+
+__device__ __forceinline__ void cswap(uint64_t &a, uint64_t &b)
+{
+    const bool lt = b < a;
+    const uint64_t lo = lt ? b : a, hi = lt ? a : b;
+    a = lo;
+    b = hi;
+}
+
+struct TopK64 {
+    uint64_t k[K];
+
+    // Sorts 8 keys with Batcher's odd-even merge network (19 comparators).
+    __device__ __forceinline__ void set_sorted(uint64_t (&v)[K])
+    {
+        cswap(v[0], v[1]); cswap(v[2], v[3]); cswap(v[4], v[5]); cswap(v[6], v[7]);
+        cswap(v[0], v[2]); cswap(v[1], v[3]); cswap(v[4], v[6]); cswap(v[5], v[7]);
+        cswap(v[1], v[2]); cswap(v[5], v[6]); cswap(v[0], v[4]); cswap(v[3], v[7]);
+        cswap(v[1], v[5]); cswap(v[2], v[6]); cswap(v[1], v[4]); cswap(v[3], v[6]);
+        cswap(v[2], v[4]); cswap(v[3], v[5]); cswap(v[3], v[4]);
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            k[j] = v[j];
+    }
+    __device__ __forceinline__ bool holds(uint32_t id) const
+    {
+        bool hit = false;
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            hit |= ((uint32_t)k[j] == id);
+        return hit;
+    }
+    // Precondition: key < k[K-1] and the key's ID is not held.
+    __device__ __forceinline__ void insert(uint64_t key)
+    {
+#pragma unroll
+        for (int j = K - 1; j > 0; --j)
+            k[j] = (key < k[j - 1]) ? k[j - 1] : ((key < k[j]) ? key : k[j]);
+        k[0] = (key < k[0]) ? key : k[0];
+    }
+    // A candidate known not to be held.
+    __device__ __forceinline__ void consider_new(uint32_t id, float d, bool usable)
+    {
+        if (!usable || !finitef(d))
+            return;
+        const uint64_t key = rank_key(d, id);
+        if (key < k[K - 1])
+            insert(key);
+    }
+    // A candidate that may already be held.
+    __device__ __forceinline__ void consider(uint32_t id, float d, bool usable)
+    {
+        if (!usable || !finitef(d))
+            return;
+        const uint64_t key = rank_key(d, id);
+        if (key < k[K - 1] && !holds(id))
+            insert(key);
+    }
+};
+
+template <int KK, int TB>
+struct PropShared {
+    uint32_t key[TB];
+    float rec[7][TB];                           // px py r ux uy E iE
+    uint32_t ref[(BLOCK + 4 * TILE * KK) * K];  // per region list: 8 slots / spilled IDs
+    uint32_t seen[TB / 32][BLOCK];              // per pixel: slots already taken (word-major)
+};
+
+// Absolute pixel of region list r: the own block, then the left, right, top and
+// bottom strips, each KK lists across by 16 along the tile edge (only the first
+// min(jump, 16) across are used).
+__device__ __forceinline__ void region_pixel(int r, int c0, int r0, int jump, int strip_len, int &col, int &row,
+                                             int &across)
+{
+    if (r < BLOCK) {
+        col = c0 + (r & (TILE - 1));
+        row = r0 + r / TILE;
+        across = 0;
+        return;
+    }
+    const int q = r - BLOCK;
+    const int sidx = q / strip_len, w = q - sidx * strip_len;
+    const int i = w / TILE, j = w - i * TILE;
+    const int far = max(TILE, jump);
+    across = i;
+    switch (sidx) {
+    case 0: col = c0 - jump + i; row = r0 + j; break;
+    case 1: col = c0 + far + i; row = r0 + j; break;
+    case 2: col = c0 + j; row = r0 - jump + i; break;
+    default: col = c0 + j; row = r0 + far + i; break;
+    }
+}
+
+template <int KK, int TB>
+__global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ G, uint32_t n_slots,
+                                                     const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
+                                                     int H, int jump, uint32_t seed_h, int n_inject, float s,
+                                                     int tiles_x, int nb)
+{
+    __shared__ PropShared<KK, TB> L;
+    const int tid = threadIdx.x;
     const int t = xcd_band(blockIdx.x, nb);
-    const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
-    const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
+    const int c0 = (t % tiles_x) * TILE, r0 = (t / tiles_x) * TILE;
+    const int lc = tid & (TILE - 1), lr = tid / TILE;
+    const int col = c0 + lc, row = r0 + lr;
+    const int kk = min(jump, TILE);
+    const int strip_len = TILE * KK;
+    const int nlists = BLOCK + 4 * strip_len;
+
+    for (int sl = tid; sl < TB; sl += BLOCK)
+        L.key[sl] = NONE;
+#pragma unroll
+    for (int w = 0; w < TB / 32; ++w)
+        L.seen[w][tid] = 0u;
+    __syncthreads();
+
+    // phase 1: region lists -> table slots
+    for (int r = tid; r < nlists; r += BLOCK) {
+        int pc, pr, across;
+        region_pixel(r, c0, r0, jump, strip_len, pc, pr, across);
+        uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
+        if (across < kk && pc >= 0 && pc < W && pr >= 0 && pr < H) {
+            const long p = (long)pr * W + pc;
+            a = cin[2 * p];
+            b = cin[2 * p + 1];
+        }
+        const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t refs[K];
+        table_insert_ids<TB>(L.key, ids, n_slots, refs);
+        uint4 *dst = reinterpret_cast<uint4 *>(&L.ref[r * K]);
+        dst[0] = make_uint4(refs[0], refs[1], refs[2], refs[3]);
+        dst[1] = make_uint4(refs[4], refs[5], refs[6], refs[7]);
+    }
+    __syncthreads();
+
+    // phase 2: one scoring record per occupied slot
+    for (int sl = tid; sl < TB; sl += BLOCK) {
+        const uint32_t c = L.key[sl];
+        if (c != NONE) {
+            const float4 g0 = G[2 * (size_t)c], g1 = G[2 * (size_t)c + 1];
+            L.rec[0][sl] = g0.x;
+            L.rec[1][sl] = g0.y;
+            L.rec[2][sl] = g0.z;
+            L.rec[3][sl] = g0.w;
+            L.rec[4][sl] = g1.x;
+            L.rec[5][sl] = g1.y;
+            L.rec[6][sl] = g1.z;
+        }
+    }
+    __syncthreads();
+
     if (col >= W || row >= H)
         return;
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
-    TopK best;
-    best.clear();
-
-    auto consider = [&](uint32_t c) {
-        if (c >= n_slots || best.contains(c))
-            return;
-        bool usable;
-        const float dc = score_site(S, stride, c, X, Y, s, usable);
-        if (!usable || !finitef(dc) || !key_less(dc, c, best.d[K - 1], best.id[K - 1]))
-            return;
-        best.insert(dc, c);
+    auto rec_score_slot = [&](uint32_t sl, bool &usable) {
+        const float4 g0 = make_float4(L.rec[0][sl], L.rec[1][sl], L.rec[2][sl], L.rec[3][sl]);
+        const float4 g1 = make_float4(L.rec[4][sl], L.rec[5][sl], L.rec[6][sl], 0.0f);
+        usable = !(g0.x < 0.0f);
+        return geom_score(g0, g1, X, Y, s);
     };
-    auto consider_list = [&](int c_, int r_) {
-        const long p = (long)r_ * W + c_;
-        const uint4 a = cin[2 * p], b = cin[2 * p + 1];
-        consider(a.x);
-        consider(a.y);
-        consider(a.z);
-        consider(a.w);
-        consider(b.x);
-        consider(b.y);
-        consider(b.z);
-        consider(b.w);
+    // marks slot sl as taken by this pixel; true if it was not taken before
+    auto take = [&](uint32_t sl) {
+        const uint32_t bit = 1u << (sl & 31u);
+        return (atomicOr(&L.seen[sl >> 5][tid], bit) & bit) == 0u;
     };
 
-    consider_list(col, row);
-    if (col - jump >= 0)
-        consider_list(col - jump, row);
-    if (col + jump < W)
-        consider_list(col + jump, row);
-    if (row - jump >= 0)
-        consider_list(col, row - jump);
-    if (row + jump < H)
-        consider_list(col, row + jump);
+    TopK64 best;
+    // own list: score its (deduplicated) table entries and sort them with a network
+    const uint4 *own = reinterpret_cast<const uint4 *>(&L.ref[tid * K]);
+    const uint4 oa = own[0], ob = own[1];
+    const uint32_t orefs[K] = {oa.x, oa.y, oa.z, oa.w, ob.x, ob.y, ob.z, ob.w};
+    {
+        uint64_t v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t ref = orefs[k];
+            v[k] = ~0ull;
+            if (ref < (uint32_t)TB && take(ref)) {
+                bool usable;
+                const float d = rec_score_slot(ref, usable);
+                if (usable && finitef(d))
+                    v[k] = rank_key(d, L.key[ref]);
+            }
+        }
+        best.set_sorted(v);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const uint32_t ref = orefs[k];
+        if (ref != REF_NONE && ref >= (uint32_t)TB) {
+            const uint32_t c = ref & ~REF_SPILL;
+            bool usable;
+            const float d = geom_score_id(G, c, X, Y, s, usable);
+            best.consider(c, d, usable);
+        }
+    }
+    // the four neighbour lists: only entries this pixel has not seen yet
+    const int far = max(TILE, jump);
+    const int r_l = col - jump >= 0 ? (lc - jump >= 0 ? lr * TILE + lc - jump : BLOCK + lc * TILE + lr) : -1;
+    const int r_r = col + jump < W
+                        ? (lc + jump < TILE ? lr * TILE + lc + jump : BLOCK + strip_len + (lc + jump - far) * TILE + lr)
+                        : -1;
+    const int r_t = row - jump >= 0 ? (lr - jump >= 0 ? (lr - jump) * TILE + lc : BLOCK + 2 * strip_len + lr * TILE + lc)
+                                    : -1;
+    const int r_b = row + jump < H ? (lr + jump < TILE ? (lr + jump) * TILE + lc
+                                                       : BLOCK + 3 * strip_len + (lr + jump - far) * TILE + lc)
+                                   : -1;
+    for (int li = 0; li < 4; ++li) {
+        const int r = li == 0 ? r_l : li == 1 ? r_r : li == 2 ? r_t : r_b;
+        if (r < 0)
+            continue;
+        const uint4 *src = reinterpret_cast<const uint4 *>(&L.ref[r * K]);
+        const uint4 a = src[0], b = src[1];
+        const uint32_t refs[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t fresh = 0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t ref = refs[k];
+            const bool f = ref < (uint32_t)TB ? take(ref) : ref != REF_NONE;
+            fresh |= f ? (1u << k) : 0u;
+        }
+        while (fresh) {
+            const int j = __builtin_ctz(fresh);
+            fresh &= fresh - 1u;
+            uint32_t ref = refs[0];
+#pragma unroll
+            for (int k = 1; k < K; ++k)
+                ref = j == k ? refs[k] : ref;
+            bool usable;
+            if (ref < (uint32_t)TB) {
+                const float d = rec_score_slot(ref, usable);
+                best.consider_new(L.key[ref], d, usable);
+            } else {
+                const uint32_t c = ref & ~REF_SPILL;
+                const float d = geom_score_id(G, c, X, Y, s, usable);
+                best.consider(c, d, usable);
+            }
+        }
+    }
+    // injected IDs (summary, B.3)
     if (n_inject > 0) {
         const uint32_t h = pcg_hash(seed_h ^ ((uint32_t)row * (uint32_t)W + (uint32_t)col));
         uint32_t x = h ? h : 0x9E3779B9u;
         for (int j = 0; j < n_inject; ++j) {
             x = xorshift32(x);
-            consider((uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32));
+            const uint32_t c = (uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32);
+            if (c < n_slots) {
+                bool usable;
+                const float d = geom_score_id(G, c, X, Y, s, usable);
+                best.consider(c, d, usable);
+            }
         }
     }
     const long p = (long)row * W + col;
-    cout[2 * p] = make_uint4(best.id[0], best.id[1], best.id[2], best.id[3]);
-    cout[2 * p + 1] = make_uint4(best.id[4], best.id[5], best.id[6], best.id[7]);
+    cout[2 * p] = make_uint4((uint32_t)best.k[0], (uint32_t)best.k[1], (uint32_t)best.k[2], (uint32_t)best.k[3]);
+    cout[2 * p + 1] = make_uint4((uint32_t)best.k[4], (uint32_t)best.k[5], (uint32_t)best.k[6], (uint32_t)best.k[7]);
 }
 
 // ---------------------------------------------------------------------------
-// Exact top-K by brute force: every slot is scored for every pixel.  Sites are
-// staged through LDS 256 at a time (x, y, r and the metric frame).
-__global__ __launch_bounds__(BLOCK) void k_topk_exact(const float *__restrict__ S, uint32_t n_slots, int stride,
+// Exact top-K by brute force: every slot is scored for every pixel.  Scoring
+// records are staged through LDS 256 at a time.
+__global__ __launch_bounds__(BLOCK) void k_topk_exact(const float4 *__restrict__ G, uint32_t n_slots,
                                                       uint4 *__restrict__ cout, int W, int H, float s, int tiles_x,
                                                       int nb)
 {
-    __shared__ float lpx[BLOCK], lpy[BLOCK], lr[BLOCK], lux[BLOCK], luy[BLOCK], lE[BLOCK], liE[BLOCK];
+    __shared__ float4 l0[BLOCK], l1[BLOCK];
     const int t = xcd_band(blockIdx.x, nb);
     const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
     const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
     const bool inside = col < W && row < H;
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
-    TopK best;
-    best.clear();
+    TopK64 best;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+        best.k[j] = ~0ull;
     for (uint32_t base = 0; base < n_slots; base += BLOCK) {
         const uint32_t i = base + threadIdx.x;
-        float px = -1.0f;
-        Frame f{1.0f, 0.0f, 1.0f, 1.0f};
-        float py = 0.0f, r = 0.0f;
+        float4 g0 = make_float4(-1.0f, 0.0f, 0.0f, 0.0f), g1 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (i < n_slots) {
-            px = S[i];
-            py = S[stride + i];
-            r = S[PR * (long)stride + i];
-            f = make_frame(S[PDX * (long)stride + i], S[PDY * (long)stride + i], S[PA * (long)stride + i]);
+            g0 = G[2 * (size_t)i];
+            g1 = G[2 * (size_t)i + 1];
         }
         __syncthreads();
-        lpx[threadIdx.x] = px;
-        lpy[threadIdx.x] = py;
-        lr[threadIdx.x] = r;
-        lux[threadIdx.x] = f.ux;
-        luy[threadIdx.x] = f.uy;
-        lE[threadIdx.x] = f.E;
-        liE[threadIdx.x] = f.iE;
+        l0[threadIdx.x] = g0;
+        l1[threadIdx.x] = g1;
         __syncthreads();
         if (inside) {
             const int cnt = min((int)(n_slots - base), BLOCK);
             for (int j = 0; j < cnt; ++j) {
-                const float sx = lpx[j];
-                if (sx < 0.0f)
-                    continue;
-                const Frame fj{lux[j], luy[j], lE[j], liE[j]};
-                const float dc = score_frame(fj, sx, lpy[j], lr[j], X, Y, s);
-                const uint32_t c = base + j;
-                if (finitef(dc) && key_less(dc, c, best.d[K - 1], best.id[K - 1]))
-                    best.insert(dc, c);
+                const float4 a0 = l0[j];
+                const float d = geom_score(a0, l1[j], X, Y, s);
+                best.consider_new(base + j, d, !(a0.x < 0.0f));
             }
         }
     }
     if (inside) {
         const long p = (long)row * W + col;
-        cout[2 * p] = make_uint4(best.id[0], best.id[1], best.id[2], best.id[3]);
-        cout[2 * p + 1] = make_uint4(best.id[4], best.id[5], best.id[6], best.id[7]);
+        cout[2 * p] = make_uint4((uint32_t)best.k[0], (uint32_t)best.k[1], (uint32_t)best.k[2], (uint32_t)best.k[3]);
+        cout[2 * p + 1] =
+            make_uint4((uint32_t)best.k[4], (uint32_t)best.k[5], (uint32_t)best.k[6], (uint32_t)best.k[7]);
     }
 }
 
@@ -317,18 +608,6 @@ struct TileTable {
     float rec[NREC][TBL];
 };
 
-__device__ __forceinline__ int table_insert(uint32_t *key, uint32_t c)
-{
-    const uint32_t h0 = (c * 2654435761u) >> 24;
-    for (int pr = 0; pr < HASH_PROBES; ++pr) {
-        const uint32_t sl = (h0 + pr) & (TBL - 1);
-        const uint32_t prev = atomicCAS(&key[sl], NONE, c);
-        if (prev == NONE || prev == c)
-            return (int)sl;
-    }
-    return -1;
-}
-
 // Phases 1-2 shared by forward and backward: insert the pixel's IDs, then one
 // thread per occupied slot fills its record.  slot[k]: table slot, -1 = spill,
 // -2 = no site (sentinel or ID >= n_slots).  Ends with a barrier.
@@ -337,9 +616,13 @@ __device__ __forceinline__ void build_tile_table(TileTable &T, const float *__re
 {
     T.key[threadIdx.x] = NONE;
     __syncthreads();
+    {
+        uint32_t refs[K];
+        table_insert_ids<TBL>(T.key, ids, n_slots, refs);
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-        slot[k] = ids[k] < n_slots ? table_insert(T.key, ids[k]) : -2;
+        for (int k = 0; k < K; ++k)
+            slot[k] = refs[k] == REF_NONE ? -2 : (refs[k] & REF_SPILL) ? -1 : (int)refs[k];
+    }
     __syncthreads();
     const uint32_t c = T.key[threadIdx.x];
     if (c != NONE) {
@@ -817,7 +1100,8 @@ struct AdamArgs {
 };
 
 __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__restrict__ M, float *__restrict__ V,
-                                              float *__restrict__ G, int n_slots, int stride, AdamArgs A)
+                                              float *__restrict__ G, float4 *__restrict__ geom, int n_slots,
+                                              int stride, AdamArgs A)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= n_slots)
@@ -849,6 +1133,12 @@ __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__re
         const float x = S[i], y = S[st + i];
         S[i] = x < 0.0f ? 0.0f : (x > A.W ? A.W : x);
         S[st + i] = y < 0.0f ? 0.0f : (y > A.H ? A.H : y);
+    }
+    if (geom) {
+        float4 g0, g1;
+        make_geom(S[i], S[st + i], S[PR * st + i], S[PDX * st + i], S[PDY * st + i], S[PA * st + i], g0, g1);
+        geom[2 * (size_t)i] = g0;
+        geom[2 * (size_t)i + 1] = g1;
     }
 }
 
@@ -915,47 +1205,78 @@ const char *sad_status_string(int status)
     }
 }
 
-int sad_topk_propagate(const float *sites, int n_slots, int stride, const uint32_t *cand_in, uint32_t *cand_out,
-                       int W, int H, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream)
+int sad_site_geometry(const float *sites, int n_slots, int stride, float *geom, void *stream)
 {
     int rc;
-    if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
+    if ((rc = check_sites(n_slots, stride)))
         return rc;
-    if (jump < 1 || jump > 0xFFFF || n_inject < 0 || n_inject > SAD_MAX_INJECT)
+    if (n_slots == 0)
+        return SAD_OK;
+    if (!sites || !geom)
+        return SAD_ERR_ARG;
+    if (!aligned16(geom))
+        return SAD_ERR_ALIGN;
+    hipLaunchKernelGGL(k_site_geometry, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, n_slots,
+                       stride, (float4 *)geom);
+    return launched();
+}
+
+int sad_topk_propagate(const float *geom, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
+                       int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)))
+        return rc;
+    if (n_slots < 0 || jump < 1 || jump > 0xFFFF || n_inject < 0 || n_inject > SAD_MAX_INJECT)
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
-    if (!sites || !cand_in || !cand_out)
+    if ((!geom && n_slots > 0) || !cand_in || !cand_out)
         return SAD_ERR_ARG;
     const size_t bytes = (size_t)W * H * K * sizeof(uint32_t);
     const uintptr_t a0 = (uintptr_t)cand_in, a1 = (uintptr_t)cand_out;
-    if (bytes && a0 < a1 + bytes && a1 < a0 + bytes)
+    if (a0 < a1 + bytes && a1 < a0 + bytes)
         return SAD_ERR_ARG;
-    if (!aligned16(cand_in) || !aligned16(cand_out))
+    if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(geom))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
     const uint32_t pw = ((uint32_t)jump << 16) | (pass_index & 0xFFFFu);
     const uint32_t seed_h = host_pcg_hash(host_pcg_hash(seed) ^ pw);
-    hipLaunchKernelGGL(k_propagate, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, sites, (uint32_t)n_slots, stride,
-                       (const uint4 *)cand_in, (uint4 *)cand_out, W, H, jump, pw, seed_h, n_inject, scale_of(W, H),
-                       g.tiles_x, g.nb);
+    // Narrow strips (small jumps) need a smaller region buffer and site table, so
+    // more workgroups fit on a CU.
+    const float sc = scale_of(W, H);
+    const hipStream_t hs = (hipStream_t)stream;
+    const float4 *G = (const float4 *)geom;
+    const uint4 *ci = (const uint4 *)cand_in;
+    uint4 *co = (uint4 *)cand_out;
+    if (jump == 1)
+        hipLaunchKernelGGL((k_propagate<1, 256>), dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, W, H,
+                           jump, seed_h, n_inject, sc, g.tiles_x, g.nb);
+    else if (jump <= 4)
+        hipLaunchKernelGGL((k_propagate<4, 512>), dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, W, H,
+                           jump, seed_h, n_inject, sc, g.tiles_x, g.nb);
+    else
+        hipLaunchKernelGGL((k_propagate<TILE, 512>), dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, W,
+                           H, jump, seed_h, n_inject, sc, g.tiles_x, g.nb);
     return launched();
 }
 
-int sad_topk_exact(const float *sites, int n_slots, int stride, uint32_t *cand_out, int W, int H, void *stream)
+int sad_topk_exact(const float *geom, int n_slots, uint32_t *cand_out, int W, int H, void *stream)
 {
     int rc;
-    if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
+    if ((rc = check_image(W, H)))
         return rc;
+    if (n_slots < 0)
+        return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
-    if (!sites || !cand_out)
+    if ((!geom && n_slots > 0) || !cand_out)
         return SAD_ERR_ARG;
-    if (!aligned16(cand_out))
+    if (!aligned16(cand_out) || !aligned16(geom))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
-    hipLaunchKernelGGL(k_topk_exact, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, sites, (uint32_t)n_slots,
-                       stride, (uint4 *)cand_out, W, H, scale_of(W, H), g.tiles_x, g.nb);
+    hipLaunchKernelGGL(k_topk_exact, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)geom,
+                       (uint32_t)n_slots, (uint4 *)cand_out, W, H, scale_of(W, H), g.tiles_x, g.nb);
     return launched();
 }
 
@@ -995,8 +1316,8 @@ int sad_render_bwd(const float *sites, int n_slots, int stride, const uint32_t *
     return launched();
 }
 
-int sad_adam_step(float *sites, float *m, float *v, float *grad, int n_slots, int stride, int step, int n_pixels,
-                  int W, int H, const sad_adam_cfg *cfg, void *stream)
+int sad_adam_step(float *sites, float *m, float *v, float *grad, float *geom, int n_slots, int stride, int step,
+                  int n_pixels, int W, int H, const sad_adam_cfg *cfg, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
@@ -1005,7 +1326,7 @@ int sad_adam_step(float *sites, float *m, float *v, float *grad, int n_slots, in
         return SAD_ERR_ARG;
     if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f && cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f && cfg->eps >= 0.0f))
         return SAD_ERR_ARG;
-    if (!aligned16(grad))
+    if (!aligned16(grad) || !aligned16(geom))
         return SAD_ERR_ALIGN;
     if (n_slots == 0)
         return SAD_OK;
@@ -1021,7 +1342,7 @@ int sad_adam_step(float *sites, float *m, float *v, float *grad, int n_slots, in
     A.W = (float)W;
     A.H = (float)H;
     hipLaunchKernelGGL(k_adam, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, m, v, grad,
-                       n_slots, stride, A);
+                       (float4 *)geom, n_slots, stride, A);
     return launched();
 }
 

@@ -31,7 +31,7 @@ def _declared():
 def test_header_declares_the_hot_path():
     names = _declared()
     for fn in ("sad_topk_propagate", "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_topk_exact",
-               "sad_abi_version", "sad_status_string"):
+               "sad_site_geometry", "sad_abi_version", "sad_status_string"):
         assert fn in names
 
 
@@ -54,28 +54,27 @@ Q = 0x90000
 
 def test_propagate_rejects_bad_arguments(L):
     f = L.sad_topk_propagate
-    ok = dict(sites=P, n=4, stride=8, a=P, b=Q, W=16, H=16, jump=1, pidx=0, seed=0, m=4)
+    ok = dict(geom=P, n=4, a=P, b=Q, W=16, H=16, jump=1, pidx=0, seed=0, m=4)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["sites"], a["n"], a["stride"], a["a"], a["b"], a["W"], a["H"], a["jump"], a["pidx"], a["seed"],
-                 a["m"], None)
+        return f(a["geom"], a["n"], a["a"], a["b"], a["W"], a["H"], a["jump"], a["pidx"], a["seed"], a["m"], None)
 
     assert call(jump=0) == ERR_ARG
     assert call(jump=65536) == ERR_ARG
     assert call(m=-1) == ERR_ARG
     assert call(m=17) == ERR_ARG
-    assert call(n=9) == ERR_ARG          # n_slots > stride
     assert call(n=-1) == ERR_ARG
     assert call(W=-1) == ERR_ARG
     assert call(H=70000) == ERR_ARG
-    assert call(sites=0) == ERR_ARG
-    assert call(sites=0, W=0) == 0       # empty image: pointers are not needed
+    assert call(geom=0) == ERR_ARG
+    assert call(geom=0, W=0) == 0        # empty image: pointers are not needed
+    assert call(geom=P + 8) == ERR_ALIGN
     assert call(b=P) == ERR_ARG          # in place
     assert call(b=P + 32) == ERR_ARG     # overlapping maps
     assert call(a=P + 4, b=Q) == ERR_ALIGN
     assert call(W=0) == 0                # empty image: no-op, nothing launched
-    assert call(H=0, b=P) == 0        # empty: zero bytes cannot overlap
+    assert call(H=0, b=P) == 0           # empty: zero bytes cannot overlap
 
 
 def test_render_and_adam_reject_bad_arguments(L):
@@ -85,14 +84,23 @@ def test_render_and_adam_reject_bad_arguments(L):
     assert L.sad_render_fwd(P, 4, 8, P, 0, 16, Q, None) == 0
     assert L.sad_render_bwd(P, 4, 8, P, 0, 16, 16, Q, None, None) == ERR_ARG  # target NULL
     assert L.sad_render_bwd(P, 4, 8, P + 4, Q, 16, 16, Q, None, None) == ERR_ALIGN
-    assert L.sad_topk_exact(P, 4, 8, P + 4, 16, 16, None) == ERR_ALIGN
+    assert L.sad_render_bwd(P, 4, 8, P, Q, 16, 16, Q + 4, None, None) == ERR_ALIGN  # grad records
+    assert L.sad_topk_exact(P, 4, P + 4, 16, 16, None) == ERR_ALIGN
+    assert L.sad_topk_exact(P, -1, P, 16, 16, None) == ERR_ARG
+    assert L.sad_site_geometry(P, 4, 8, P + 4, None) == ERR_ALIGN
+    assert L.sad_site_geometry(P, 9, 8, P, None) == ERR_ARG
+    assert L.sad_site_geometry(0, 4, 8, P, None) == ERR_ARG
+    assert L.sad_site_geometry(0, 0, 8, 0, None) == 0  # no slots: no-op
     cfg = sad.AdamConfig().to_c()
-    assert L.sad_adam_step(P, P, P, P, 4, 8, 0, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # step 0
-    assert L.sad_adam_step(P, P, P, P, 4, 8, 1, 0, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # no pixels
-    assert L.sad_adam_step(P, P, P, P, 4, 8, 1, 10, 4, 4, None, None) == ERR_ARG
+    A = L.sad_adam_step
+    assert A(P, P, P, P, P, 4, 8, 0, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # step 0
+    assert A(P, P, P, P, P, 4, 8, 1, 0, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # no pixels
+    assert A(P, P, P, P, P, 4, 8, 1, 10, 4, 4, None, None) == ERR_ARG
+    assert A(P, P, P, P + 4, P, 4, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ALIGN
+    assert A(P, P, P, P, P + 4, 4, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ALIGN
     bad = sad.AdamConfig(beta1=1.0).to_c()
-    assert L.sad_adam_step(P, P, P, P, 4, 8, 1, 10, 4, 4, ctypes.byref(bad), None) == ERR_ARG
-    assert L.sad_adam_step(P, P, P, P, 0, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == 0  # no slots: no-op
+    assert A(P, P, P, P, P, 4, 8, 1, 10, 4, 4, ctypes.byref(bad), None) == ERR_ARG
+    assert A(P, P, P, P, None, 0, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == 0  # no slots: no-op
 
 
 def test_python_binding_refuses_cpu_tensors():

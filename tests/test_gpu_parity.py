@@ -21,11 +21,18 @@ def _case(W, H, n, seed=1):
     return S, cin
 
 
-def _gpu_propagate(S, n, cin, W, H, jump, pidx, seed, m, stride=None):
+def _geom(S, n):
     S_d = to_dev(S)
+    g = sad.new_geom(max(S.shape[1], 1), S_d.device)
+    sad.site_geometry(S_d, n, g)
+    return g
+
+
+def _gpu_propagate(S, n, cin, W, H, jump, pidx, seed, m):
+    g = _geom(S, n)
     a = to_dev(cin)
     b = sad.new_map(W, H, a.device)
-    sad.topk_propagate(S_d, n, a, b, W, H, jump, pidx, seed, m)
+    sad.topk_propagate(g, n, a, b, W, H, jump, pidx, seed, m)
     torch.cuda.synchronize()
     return map_to_host(b)
 
@@ -84,14 +91,40 @@ def test_propagate_schedule_from_empty_matches_oracle_each_pass(orc):
     assert recall > 0.99
 
 
+def test_site_geometry_encodes_the_score(orc):
+    """The scoring record reproduces the oracle's score: d = s*sqrt((U.delta)^2 +
+    (V x delta)^2) - s*r evaluated in float64 from the GPU record vs the oracle's
+    float32 score; inactive slots keep x < 0."""
+    W, H, n = 90, 70, 500
+    S = synth.random_sites(n, W, H, 21)
+    S[synth.DX] *= 3.0
+    S[synth.DX, 7] = 0.0
+    S[synth.DY, 7] = 0.0
+    S[synth.X, 9] = -1.0
+    g = _geom(S, n).cpu().numpy().astype(np.float64)
+    assert g[9, 0] < 0 and (g[:, 7] == 0).all()
+    rng = np.random.default_rng(0)
+    pix = rng.integers(0, W * H, 4000)
+    ids = rng.integers(0, n, 4000)
+    ids[ids == 9] = 8
+    ex = (pix % W) + 0.5 - g[ids, 0]
+    ey = (pix // W) + 0.5 - g[ids, 1]
+    t1 = g[ids, 3] * ex + g[ids, 4] * ey
+    t2 = g[ids, 5] * ey - g[ids, 6] * ex
+    s = 1.0 / max(W, H)
+    d = s * np.sqrt(t1 * t1 + t2 * t2) - s * g[ids, 2]
+    ref = orc.score_pairs(S, n, W, H, pix, ids)
+    assert np.abs(d - ref).max() < 1e-6
+
+
 @pytest.mark.parametrize("W,H,n", [(64, 64, 256), (77, 45, 300), (1, 1, 3), (50, 30, 5), (40, 40, 3000)])
 def test_topk_exact_matches_oracle(orc, W, H, n):
     print(f"exact W={W} H={H} n={n}", flush=True)
     S = synth.random_sites(n, W, H, 8)
     S[synth.X, ::7] = -1.0
-    S_d = to_dev(S)
-    out = sad.new_map(W, H, S_d.device)
-    sad.topk_exact(S_d, n, out, W, H)
+    g = _geom(S, n)
+    out = sad.new_map(W, H, g.device)
+    sad.topk_exact(g, n, out, W, H)
     torch.cuda.synchronize()
     got = map_to_host(out)
     ref = orc.topk_exact(S, n, W, H)
@@ -206,8 +239,14 @@ def _adam_gpu(S, m, v, G, n, step, P, W, H, cfg):
     rec[:, :11] = G.T
     rec[:, 11:] = 7.0  # unused words: must survive untouched
     g_d = to_dev(rec)
-    sad.adam_step(S_d, m_d, v_d, g_d, n, step, P, W, H, cfg)
+    geom = sad.new_geom(S.shape[1], S_d.device)
+    sad.adam_step(S_d, m_d, v_d, g_d, n, step, P, W, H, cfg, geom=geom)
     torch.cuda.synchronize()
+    # the refreshed scoring records equal a fresh derivation from the updated sites
+    fresh = sad.new_geom(S.shape[1], S_d.device)
+    sad.site_geometry(S_d, n, fresh)
+    torch.cuda.synchronize()
+    assert torch.equal(geom[:n], fresh[:n])
     gh = g_d.cpu().numpy()
     assert (gh[:, 11:] == 7.0).all()
     return [t.cpu().numpy().astype(np.float64) for t in (S_d, m_d, v_d)] + [np.ascontiguousarray(gh[:, :11].T).astype(np.float64)]
@@ -242,7 +281,7 @@ def test_adam_matches_oracle(orc, step):
 def test_empty_image_and_no_sites_are_noops():
     z = torch.zeros((10, 4), dtype=torch.float32, device="cuda")
     m0 = sad.new_map(0, 0)
-    sad.topk_propagate(z, 4, m0, sad.new_map(0, 0), 0, 0, 1, 0, 0, 4)
+    sad.topk_propagate(sad.new_geom(4), 4, m0, sad.new_map(0, 0), 0, 0, 1, 0, 0, 4)
     out = torch.empty((0, 0, 3), dtype=torch.float32, device="cuda")
     sad.render_fwd(z, 4, m0, 0, 0, out)
     g = sad.new_grad(4)
@@ -256,6 +295,7 @@ def test_fitter_iterations_reduce_loss(orc):
     S = synth.random_sites(n, W, H, synth.SEED_MODEL)
     tgt = orc.hard_render(synth.random_sites(n, W, H, synth.SEED_TARGET_SITES), n, W, H) + synth.pixel_noise(W, H)
     f = sad.Fitter(to_dev(S), n, to_dev(tgt), W, H)
+    assert torch.equal(f.geom[:n], _geom(S, n)[:n])
     losses = []
     for _ in range(60):
         f.loss.zero_()
