@@ -33,19 +33,21 @@ HBM_PEAK_GBS = 8000.0
 def algorithmic_bytes(P, N):
     """Compulsory HBM bytes per launch (each tensor byte read once, written once).
 
-    propagate: map in + map out (64 B/px) + one 32-byte scoring record per site
-    forward:   map (32 B/px) + image out (12 B/px) + all ten site fields (40 B/site)
-    backward:  map (32 B/px) + target (12 B/px) + site fields (40 B/site) + one
-               read-modify-write flush of 11 accumulators (44 B/site)
+    propagate: map in + map out (64 B/px) + the 32-byte scoring half of each
+               site record (32 B/site)
+    forward:   map (32 B/px) + image out (12 B/px) + the 44 bytes of the site
+               record the blend reads (x, y, r, frame, tau, colour) (44 B/site)
+    backward:  map (32 B/px) + target (12 B/px) + the site record (64 B/site)
+               + one read-modify-write flush of 11 accumulators (88 B/site)
     adam:      params, m, v read and written (240 B/site) + the 10 gradients of
-               the site's record read and zeroed (80 B/site) + the scoring record
-               written (32 B/site)
+               the site's record read and zeroed (80 B/site) + the site record
+               written (64 B/site)
     """
     return {
         "propagate": 64 * P + 32 * N,
-        "fwd": 44 * P + 40 * N,
-        "bwd": 44 * P + 84 * N,
-        "adam": 352 * N,
+        "fwd": 44 * P + 44 * N,
+        "bwd": 44 * P + 152 * N,
+        "adam": 384 * N,
     }
 
 
@@ -72,8 +74,8 @@ def make_inputs(wl, dev):
     # target: hard (argmin) render of the second site set = colour of the first
     # entry of its exact top-K map (brute force on the GPU), plus noise
     S2_d = torch.from_numpy(S2).to(dev)
-    g2 = sad.new_geom(n, dev)
-    sad.site_geometry(S2_d, n, g2)
+    g2 = sad.new_records(n, dev)
+    sad.site_records(S2_d, n, g2)
     ex = sad.new_map(W, H, dev)
     sad.topk_exact(g2, n, ex, W, H)
     first = ex[:, :, 0].long()
@@ -116,7 +118,7 @@ def main():
 
     def reset():
         fit.sites.copy_(S0_d)
-        fit.refresh_geometry()
+        fit.refresh_records()
         fit.m.zero_()
         fit.v.zero_()
         fit.grad.zero_()
@@ -168,7 +170,7 @@ def main():
     psnr = 10 * np.log10(1.0 / max(mse, 1e-30))
     # recall of the maintained map against the exact top-K (brute force on the GPU)
     ex = sad.new_map(W, H, dev)
-    sad.topk_exact(fit.geom, N, ex, W, H)
+    sad.topk_exact(fit.rec, N, ex, W, H)
     cur = fit.cand
     a, _ = torch.sort(cur.view(-1, 8), dim=1)
     b, _ = torch.sort(ex.view(-1, 8), dim=1)
@@ -180,11 +182,11 @@ def main():
     kdur = {}
     R = args.kernel_reps
     launches = {
-        "propagate": lambda i: sad.topk_propagate(fit.geom, N, fit.maps[i % 2], fit.maps[1 - i % 2], W, H, 1,
+        "propagate": lambda i: sad.topk_propagate(fit.rec, N, fit.maps[i % 2], fit.maps[1 - i % 2], W, H, 1,
                                                   1000 + i, synth.SEED_INJECT, wl.n_inject),
-        "fwd": lambda i: sad.render_fwd(fit.sites, N, fit.cand, W, H, fit.rgb),
-        "bwd": lambda i: sad.render_bwd(fit.sites, N, fit.cand, fit.target, W, H, fit.grad, fit.loss),
-        "adam": lambda i: sad.adam_step(fit.sites, fit.m, fit.v, fit.grad, N, 500 + i, P, W, H, fit.adam, fit.geom),
+        "fwd": lambda i: sad.render_fwd(fit.rec, N, fit.cand, W, H, fit.rgb),
+        "bwd": lambda i: sad.render_bwd(fit.rec, N, fit.cand, fit.target, W, H, fit.grad, fit.loss),
+        "adam": lambda i: sad.adam_step(fit.sites, fit.m, fit.v, fit.grad, N, 500 + i, P, W, H, fit.adam, fit.rec),
     }
     for name, fn in launches.items():
         g = torch.cuda.CUDAGraph()

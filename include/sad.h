@@ -13,8 +13,8 @@
  * ---------------------------------------
  * Ownership.  The caller owns every buffer.  The library allocates no memory and
  *   keeps no state between calls, so calls are reentrant.
- * Pointers.  Arguments named `sites`, `cand*`, `out_rgb`, `target`, `grad`, `m`,
- *   `v` and `loss_sum` are DEVICE pointers (HBM of the current HIP device).
+ * Pointers.  Arguments named `sites`, `rec`, `cand*`, `out_rgb`, `target`, `grad`,
+ *   `m`, `v` and `loss_sum` are DEVICE pointers (HBM of the current HIP device).
  *   `cfg` is a HOST pointer, read before the call returns.
  * Streams.  Device work is enqueued asynchronously on `stream` (a hipStream_t
  *   passed as void*; NULL = the legacy default stream).  A return of SAD_OK means
@@ -42,15 +42,20 @@
  *         16-byte aligned.  (A record per site lets the atomics that flush one
  *         site's 11 sums share one cache line.)
  * m, v  : float [SAD_NPARAM][stride] Adam moments.
- * geom  : float [n_slots][SAD_GEOM_LD] -- the scoring record of each site, derived
- *         from `sites` by sad_site_geometry and refreshed by sad_adam_step: the
- *         fp32 counterpart of the compact per-site buffer the candidate-update
- *         kernels read in the pages ([SUM] B.2 "Packed candidate sites"):
- *           (x, y, r, Ux, Uy, Vx, Vy, 0),  U = e^{a/2} u,  V = e^{-a/2} u,
- *         so ||delta||_G^2 = (U.delta)^2 + (Vx delta_y - Vy delta_x)^2.  A slot with
- *         x < 0 stays inactive.  16-byte aligned.  It is a cache the caller keeps
- *         in step with `sites`: recompute it after any change made outside
- *         sad_adam_step.
+ * rec   : float [n_slots][SAD_REC_LD] -- one 64-byte record per site, derived from
+ *         `sites` (sad_site_records) and refreshed by sad_adam_step; the image-
+ *         space kernels read sites only through it, so a random access to a site
+ *         costs a few contiguous loads:
+ *           [0..4)   x, y, r, Ux        [4..8)   Uy, Vx, Vy, tau
+ *           [8..12)  R, G, B, 1/|dir|   [12..16) ux, uy, E, 1/E
+ *         with u = dir/|dir| (u = (1,0) if |dir|^2 < 1e-30; 1/|dir| is then 0),
+ *         E = e^a, tau = e^{log tau}, U = e^{a/2} u, V = e^{-a/2} u, so that
+ *         ||delta||_G^2 = (U.delta)^2 + (Vx delta_y - Vy delta_x)^2.  The first
+ *         32 bytes are the fp32 counterpart of the compact per-site buffer the
+ *         pages' candidate-update kernels read ([SUM] B.2 "Packed candidate
+ *         sites").  A slot with x < 0 stays inactive.  16-byte aligned.  It is a
+ *         cache the caller keeps in step with `sites`: recompute it after any
+ *         change made outside sad_adam_step.
  * Pixel (col,row) is evaluated at (col+0.5, row+0.5) px ([SUM] B.3 evaluates at
  * centred cells).  Limits: 1 <= W, H <= 65535 (W or H = 0 is an empty image: a
  * no-op returning SAD_OK after the scalar arguments are checked; its pointers
@@ -76,7 +81,7 @@ extern "C" {
 #define SAD_NPARAM 10
 #define SAD_NACC 11
 #define SAD_GRAD_LD 16
-#define SAD_GEOM_LD 8
+#define SAD_REC_LD 16
 #define SAD_MAX_INJECT 16
 #define SAD_MAX_DIM 65535
 
@@ -104,12 +109,12 @@ int sad_abi_version(void);
 const char *sad_status_string(int status);
 
 /*
- * sad_site_geometry -- writes the scoring record (see `geom` above) of slots
- * [0, n_slots) from the site planes.
- *   sites device [10][stride] read-only; geom device [n_slots][8] float, written.
- * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN (geom not 16-byte aligned), SAD_ERR_DEVICE.
+ * sad_site_records -- writes the records (see `rec` above) of slots [0, n_slots)
+ * from the site planes.
+ *   sites device [10][stride] read-only; rec device [n_slots][16] float, written.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN (rec not 16-byte aligned), SAD_ERR_DEVICE.
  */
-int sad_site_geometry(const float *sites, int n_slots, int stride, float *geom, void *stream);
+int sad_site_records(const float *sites, int n_slots, int stride, float *rec, void *stream);
 
 /*
  * sad_topk_propagate -- one propagation pass of the candidate map.
@@ -130,14 +135,14 @@ int sad_site_geometry(const float *sites, int n_slots, int stride, float *geom, 
  * padded with SAD_INVALID.  The pass reads cand_in and writes cand_out (Jacobi).
  * The host chooses the schedule: jumps B/2, B/4, ..., 1 then 1 ([SUM] section 4).
  *
- *   geom      device, [n_slots][8] float scoring records, read-only
+ *   rec       device, [n_slots][16] float site records, read-only
  *   cand_in   device, [H][W][8] uint32, read-only, 16-byte aligned
  *   cand_out  device, [H][W][8] uint32, written; must not overlap cand_in
  *   jump      1..65535;  n_inject 0..SAD_MAX_INJECT
  * Errors: SAD_ERR_ARG (bad sizes, jump, n_inject, NULL, overlapping maps),
  *         SAD_ERR_ALIGN (a pointer not 16-byte aligned), SAD_ERR_DEVICE.
  */
-int sad_topk_propagate(const float *geom, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
+int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
                        int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream);
 
 /*
@@ -145,21 +150,21 @@ int sad_topk_propagate(const float *geom, int n_slots, const uint32_t *cand_in, 
  * that propagation approximates ([NOTE] design 3; [SUM] section 4 "Candidate
  * maintenance").  Used to (re)initialise a map and to measure recall.  Cost
  * O(W*H*n_slots).  Same output convention as sad_topk_propagate.
- *   geom device [n_slots][8] read-only;  cand_out device [H][W][8], written.
+ *   rec device [n_slots][16] read-only;  cand_out device [H][W][8], written.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_topk_exact(const float *geom, int n_slots, uint32_t *cand_out, int W, int H, void *stream);
+int sad_topk_exact(const float *rec, int n_slots, uint32_t *cand_out, int W, int H, void *stream);
 
 /*
  * sad_render_fwd -- the temperature-softmax blend of each pixel's list.
  * [NOTE] design 2, [PROJ] "Method": l_i = -tau_i d_i, w = softmax over the list,
  * c(x) = sum_i w_i c_i; max-subtracted, invalid IDs skipped, non-finite entries
  * skipped ([SUM] B.4).  A pixel with no usable entry renders (0,0,0).
- *   cand device [H][W][8] read-only; out_rgb device [H][W][3] float, written.
+ *   rec device [n_slots][16] read-only; cand device [H][W][8] read-only;
+ *   out_rgb device [H][W][3] float, written.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_render_fwd(const float *sites, int n_slots, int stride, const uint32_t *cand, int W, int H, float *out_rgb,
-                   void *stream);
+int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, int H, float *out_rgb, void *stream);
 
 /*
  * sad_render_bwd -- hand-derived gradients of L = sum_x ||c(x) - t(x)||^2 with
@@ -175,14 +180,15 @@ int sad_render_fwd(const float *sites, int n_slots, int stride, const uint32_t *
  * atomic per site and accumulator per tile; an entry that finds no slot goes
  * straight to global atomics ([SUM] section 5, B.4).  Float atomics make the
  * summation order, hence the last bits, vary from run to run.
- *   target device [H][W][3] read-only; grad device [stride][16] float, +=;
+ *   rec device [n_slots][16] read-only; target device [H][W][3] read-only;
+ *   grad device [>= n_slots][16] float, +=;
  *   loss_sum device float or NULL, += sum_x ||c - t||^2.
  * The caller zeroes `grad` once; sad_adam_step re-zeroes accumulators 0..9 each
  * step; accumulator 10 keeps accumulating until the caller resets it.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN (cand or grad not 16-byte aligned), SAD_ERR_DEVICE.
  */
-int sad_render_bwd(const float *sites, int n_slots, int stride, const uint32_t *cand, const float *target, int W,
-                   int H, float *grad, float *loss_sum, void *stream);
+int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
+                   float *grad, float *loss_sum, void *stream);
 
 /*
  * sad_adam_step -- Adam (Kingma & Ba 2015) on the ten site parameters, with the
@@ -192,14 +198,14 @@ int sad_render_bwd(const float *sites, int n_slots, int stride, const uint32_t *
  *   v = b2 v + (1-b2) g^2;  p -= lr_j (m / (1-b1^step)) / (sqrt(v / (1-b2^step)) + eps);
  * then x is clamped to [0, W] and y to [0, H].  Accumulators 0..9 of grad are
  * zeroed for every slot < n_slots; accumulator 10 is left alone.  Inactive slots
- * keep p, m, v.  If geom is not NULL the scoring records of slots [0, n_slots)
- * are rewritten from the updated sites in the same pass.
+ * keep p, m, v.  If rec is not NULL the site records of slots [0, n_slots) are
+ * rewritten from the updated sites in the same pass.
  *   sites, m, v device [10][stride] float (in/out); grad device [stride][16],
- *   16-byte aligned; geom device [n_slots][8] or NULL; step >= 1 (global,
+ *   16-byte aligned; rec device [n_slots][16] or NULL; step >= 1 (global,
  *   1-based); n_pixels >= 1; cfg HOST pointer.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_adam_step(float *sites, float *m, float *v, float *grad, float *geom, int n_slots, int stride, int step,
+int sad_adam_step(float *sites, float *m, float *v, float *grad, float *rec, int n_slots, int stride, int step,
                   int n_pixels, int W, int H, const sad_adam_cfg *cfg, void *stream);
 
 #ifdef __cplusplus

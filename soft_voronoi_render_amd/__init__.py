@@ -32,7 +32,7 @@ INVALID = 0xFFFFFFFF
 NPARAM = 10
 NACC = 11
 GRAD_LD = 16
-GEOM_LD = 8
+REC_LD = 16
 MAX_INJECT = 16
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "misaligned pointer", -3: "HIP launch failed",
@@ -87,23 +87,23 @@ def lib() -> ctypes.CDLL:
         L.sad_abi_version.argtypes = []
         L.sad_status_string.restype = ctypes.c_char_p
         L.sad_status_string.argtypes = [i32]
-        L.sad_site_geometry.restype = i32
-        L.sad_site_geometry.argtypes = [fp, i32, i32, fp, vp]
+        L.sad_site_records.restype = i32
+        L.sad_site_records.argtypes = [fp, i32, i32, fp, vp]
         L.sad_topk_propagate.restype = i32
         L.sad_topk_propagate.argtypes = [fp, i32, vp, vp, i32, i32, i32, u32, u32, i32, vp]
         L.sad_topk_exact.restype = i32
         L.sad_topk_exact.argtypes = [fp, i32, vp, i32, i32, vp]
         L.sad_render_fwd.restype = i32
-        L.sad_render_fwd.argtypes = [fp, i32, i32, vp, i32, i32, fp, vp]
+        L.sad_render_fwd.argtypes = [fp, i32, vp, i32, i32, fp, vp]
         L.sad_render_bwd.restype = i32
-        L.sad_render_bwd.argtypes = [fp, i32, i32, vp, fp, i32, i32, fp, fp, vp]
+        L.sad_render_bwd.argtypes = [fp, i32, vp, fp, i32, i32, fp, fp, vp]
         L.sad_adam_step.restype = i32
         L.sad_adam_step.argtypes = [fp, fp, fp, fp, fp, i32, i32, i32, i32, i32, i32, ctypes.POINTER(AdamCfg), vp]
         _lib = L
     return _lib
 
 
-EXPORTED = ("sad_abi_version", "sad_status_string", "sad_site_geometry", "sad_topk_propagate", "sad_topk_exact",
+EXPORTED = ("sad_abi_version", "sad_status_string", "sad_site_records", "sad_topk_propagate", "sad_topk_exact",
             "sad_render_fwd", "sad_render_bwd", "sad_adam_step")
 
 
@@ -149,54 +149,58 @@ def _sites(sites: torch.Tensor, n_slots: int):
     return ptr, stride
 
 
-def _geom(geom: torch.Tensor, n_slots: int) -> int:
-    if geom.dim() != 2 or geom.shape[1] != GEOM_LD or geom.shape[0] < n_slots:
-        raise ValueError("geom must be float32 [>= n_slots][8]")
-    return _dev(geom, "geom", _F32)
+def _rec(rec: torch.Tensor, n_slots: int) -> int:
+    if rec.dim() != 2 or rec.shape[1] != REC_LD or rec.shape[0] < n_slots:
+        raise ValueError("rec must be float32 [>= n_slots][16]")
+    return _dev(rec, "rec", _F32)
 
 
-def new_geom(capacity: int, device="cuda") -> torch.Tensor:
-    """Storage for the per-site scoring records, float32 [capacity][8]."""
-    return torch.zeros((capacity, GEOM_LD), dtype=torch.float32, device=device)
+def new_records(capacity: int, device="cuda") -> torch.Tensor:
+    """Storage for the per-site records, float32 [capacity][16]."""
+    return torch.zeros((max(capacity, 1), REC_LD), dtype=torch.float32, device=device)
 
 
-def site_geometry(sites, n_slots, geom, stream=None):
-    """Writes the scoring records of slots [0, n_slots) (see sad_site_geometry)."""
+def site_records(sites, n_slots, rec, stream=None):
+    """Writes the site records of slots [0, n_slots) (see sad_site_records)."""
     sp, stride = _sites(sites, n_slots)
-    g = _geom(geom, n_slots)
-    _check("sad_site_geometry", lib().sad_site_geometry(sp, n_slots, stride, g, _stream(stream)))
+    r = _rec(rec, n_slots)
+    _check("sad_site_records", lib().sad_site_records(sp, n_slots, stride, r, _stream(stream)))
 
 
-def topk_propagate(geom, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed, n_inject, stream=None):
+def topk_propagate(rec, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed, n_inject, stream=None):
     """One propagation pass: cand_in -> cand_out (see sad_topk_propagate)."""
-    g = _geom(geom, n_slots)
+    g = _rec(rec, n_slots)
     a = _dev(cand_in, "cand_in", _U32, (H, W, K))
     b = _dev(cand_out, "cand_out", _U32, (H, W, K))
     _check("sad_topk_propagate", lib().sad_topk_propagate(g, n_slots, a, b, W, H, jump, pass_index & 0xFFFFFFFF,
                                                           seed & 0xFFFFFFFF, n_inject, _stream(stream)))
 
 
-def topk_exact(geom, n_slots, cand_out, W, H, stream=None):
+def topk_exact(rec, n_slots, cand_out, W, H, stream=None):
     """Brute-force exact top-K map (see sad_topk_exact)."""
-    g = _geom(geom, n_slots)
+    g = _rec(rec, n_slots)
     b = _dev(cand_out, "cand_out", _U32, (H, W, K))
     _check("sad_topk_exact", lib().sad_topk_exact(g, n_slots, b, W, H, _stream(stream)))
 
 
-def render_fwd(sites, n_slots, cand, W, H, out_rgb, stream=None):
-    sp, stride = _sites(sites, n_slots)
+def render_fwd(rec, n_slots, cand, W, H, out_rgb, stream=None):
+    """Temperature-softmax render of each pixel's list (see sad_render_fwd)."""
+    r = _rec(rec, n_slots)
     c = _dev(cand, "cand", _U32, (H, W, K))
     o = _dev(out_rgb, "out_rgb", _F32, (H, W, 3))
-    _check("sad_render_fwd", lib().sad_render_fwd(sp, n_slots, stride, c, W, H, o, _stream(stream)))
+    _check("sad_render_fwd", lib().sad_render_fwd(r, n_slots, c, W, H, o, _stream(stream)))
 
 
-def render_bwd(sites, n_slots, cand, target, W, H, grad, loss_sum=None, stream=None):
-    sp, stride = _sites(sites, n_slots)
+def render_bwd(rec, n_slots, cand, target, W, H, grad, loss_sum=None, stream=None):
+    """Gradients of the squared error, accumulated into grad (see sad_render_bwd)."""
+    r = _rec(rec, n_slots)
     c = _dev(cand, "cand", _U32, (H, W, K))
     t = _dev(target, "target", _F32, (H, W, 3))
-    g = _dev(grad, "grad", _F32, (stride, GRAD_LD))
+    if grad.dim() != 2 or grad.shape[1] != GRAD_LD or grad.shape[0] < n_slots:
+        raise ValueError("grad must be float32 [>= n_slots][16]")
+    g = _dev(grad, "grad", _F32)
     ls = _dev(loss_sum, "loss_sum", _F32) if loss_sum is not None else None
-    _check("sad_render_bwd", lib().sad_render_bwd(sp, n_slots, stride, c, t, W, H, g, ls, _stream(stream)))
+    _check("sad_render_bwd", lib().sad_render_bwd(r, n_slots, c, t, W, H, g, ls, _stream(stream)))
 
 
 @dataclasses.dataclass
@@ -217,12 +221,12 @@ class AdamConfig:
 
 
 def adam_step(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamConfig | AdamCfg | None = None,
-              geom=None, stream=None):
+              rec=None, stream=None):
     sp, stride = _sites(sites, n_slots)
     mp = _dev(m, "m", _F32, (NPARAM, stride))
     vp = _dev(v, "v", _F32, (NPARAM, stride))
     g = _dev(grad, "grad", _F32, (stride, GRAD_LD))
-    gp = _geom(geom, n_slots) if geom is not None else None
+    gp = _rec(rec, n_slots) if rec is not None else None
     c = cfg.to_c() if isinstance(cfg, AdamConfig) else (cfg if cfg is not None else AdamConfig().to_c())
     _check("sad_adam_step", lib().sad_adam_step(sp, mp, vp, g, gp, n_slots, stride, step, n_pixels, W, H,
                                                 ctypes.byref(c), _stream(stream)))
@@ -256,8 +260,8 @@ def new_map(W: int, H: int, device="cuda") -> torch.Tensor:
 
 class Fitter:
     """One SAD fitting state on the GPU and its iteration: propagate (one pass),
-    render forward, render backward, Adam (which also refreshes the scoring
-    records the next pass reads).  Everything runs in libsad kernels on one
+    render forward, render backward, Adam (which also refreshes the site
+    records the image-space kernels read).  Everything runs in libsad kernels on one
     stream; nothing crosses to the host inside an iteration."""
 
     def __init__(self, sites: torch.Tensor, n_slots: int, target: torch.Tensor, W: int, H: int,
@@ -270,8 +274,8 @@ class Fitter:
         self.m = torch.zeros((NPARAM, stride), dtype=torch.float32, device=dev)
         self.v = torch.zeros((NPARAM, stride), dtype=torch.float32, device=dev)
         self.grad = torch.zeros((stride, GRAD_LD), dtype=torch.float32, device=dev)
-        self.geom = new_geom(stride, dev)
-        site_geometry(sites, n_slots, self.geom)
+        self.rec = new_records(stride, dev)
+        site_records(sites, n_slots, self.rec)
         self.maps = [cand if cand is not None else new_map(W, H, dev), new_map(W, H, dev)]
         self.cur = 0
         self.rgb = torch.empty((H, W, 3), dtype=torch.float32, device=dev)
@@ -288,12 +292,12 @@ class Fitter:
         B = 1 << max(0, (max(self.W, self.H) - 1).bit_length())
         return max(1, (B // 2) >> it) if it < 64 else 1
 
-    def refresh_geometry(self, stream=None):
-        """Recompute the scoring records after changing `sites` outside Adam."""
-        site_geometry(self.sites, self.n_slots, self.geom, stream)
+    def refresh_records(self, stream=None):
+        """Recompute the site records after changing `sites` outside Adam."""
+        site_records(self.sites, self.n_slots, self.rec, stream)
 
     def propagate(self, jump: int, pass_index: int, stream=None):
-        topk_propagate(self.geom, self.n_slots, self.maps[self.cur], self.maps[1 - self.cur], self.W, self.H,
+        topk_propagate(self.rec, self.n_slots, self.maps[self.cur], self.maps[1 - self.cur], self.W, self.H,
                        jump, pass_index, self.seed, self.n_inject, stream)
         self.cur = 1 - self.cur
 
@@ -301,8 +305,8 @@ class Fitter:
         """One iteration (the hot path): propagate, forward, backward, Adam."""
         it = self.it
         self.propagate(self.jump_at(it), it, stream)
-        render_fwd(self.sites, self.n_slots, self.cand, self.W, self.H, self.rgb, stream)
-        render_bwd(self.sites, self.n_slots, self.cand, self.target, self.W, self.H, self.grad, self.loss, stream)
+        render_fwd(self.rec, self.n_slots, self.cand, self.W, self.H, self.rgb, stream)
+        render_bwd(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, self.grad, self.loss, stream)
         adam_step(self.sites, self.m, self.v, self.grad, self.n_slots, it + 1, self.W * self.H, self.W, self.H,
-                  self.adam, self.geom, stream)
+                  self.adam, self.rec, stream)
         self.it += 1

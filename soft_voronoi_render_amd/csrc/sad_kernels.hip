@@ -94,21 +94,32 @@ __device__ __forceinline__ float score_site(const float *__restrict__ S, long st
 }
 
 // ---------------------------------------------------------------------------
-// Scoring record of one site, 32 bytes, the fp32 counterpart of the pages'
-// compact candidate-site buffer (summary, Appendix B.2 "Packed candidate sites"):
-//   (x, y, r, Ux) (Uy, Vx, Vy, 0)  with  U = e^{a/2} u,  V = e^{-a/2} u,
-// so that ||delta||_G^2 = (U.delta)^2 + (V x delta)^2 = e^a alpha^2 + e^-a beta^2 --
-// a sum of squares, as in the definition, with no cancellation.  A candidate
-// costs two 16-byte loads and no transcendental besides the square root.
-constexpr int GLD = SAD_GEOM_LD;
+// Site record, 64 bytes per site, derived from the ten parameters: everything an
+// image-space kernel needs about a site in one contiguous, 16-byte-aligned block,
+// so a random access costs a few vector loads instead of one gather per
+// parameter plane.  The first 32 bytes are the scoring record the candidate
+// search reads -- the fp32 counterpart of the pages' compact candidate-site
+// buffer (summary, Appendix B.2 "Packed candidate sites"):
+//   [0]  x   y   r   Ux     [1]  Uy  Vx  Vy  tau
+//   [2]  R   G   B   1/|dir|  [3]  ux  uy  E   1/E
+// with u = dir/|dir| (u = (1,0) when |dir|^2 < 1e-30), E = e^a, tau = e^{log tau},
+// U = e^{a/2} u and V = e^{-a/2} u, so ||delta||_G^2 = (U.delta)^2 + (V x delta)^2
+// = e^a alpha^2 + e^-a beta^2 -- a sum of squares, as in the definition (reading
+// note, key design 1).  1/|dir| is 0 for a degenerate direction.
+constexpr int RLD4 = SAD_REC_LD / 4;  // float4 per record
 
-__device__ __forceinline__ void make_geom(float x, float y, float r, float dx, float dy, float a, float4 &g0,
-                                          float4 &g1)
+__device__ __forceinline__ void make_record(const float *__restrict__ S, long st, int i, float4 (&o)[RLD4])
 {
+    const float x = S[i], y = S[st + i], lt = S[PLT * st + i], r = S[PR * st + i];
+    const float c0 = S[PCR * st + i], c1 = S[PCG * st + i], c2 = S[PCB * st + i];
+    const float dx = S[PDX * st + i], dy = S[PDY * st + i], a = S[PA * st + i];
     const Frame f = make_frame(dx, dy, a);
     const float sE = __expf(0.5f * a), siE = __expf(-0.5f * a);
-    g0 = make_float4(x, y, r, sE * f.ux);
-    g1 = make_float4(sE * f.uy, siE * f.ux, siE * f.uy, 0.0f);
+    const float n2 = dx * dx + dy * dy;
+    o[0] = make_float4(x, y, r, sE * f.ux);
+    o[1] = make_float4(sE * f.uy, siE * f.ux, siE * f.uy, __expf(lt));
+    o[2] = make_float4(c0, c1, c2, n2 >= 1e-30f ? rsqrtf(n2) : 0.0f);
+    o[3] = make_float4(f.ux, f.uy, f.E, f.iE);
 }
 
 __device__ __forceinline__ float geom_score(const float4 &g0, const float4 &g1, float X, float Y, float s)
@@ -123,22 +134,22 @@ __device__ __forceinline__ float geom_score(const float4 &g0, const float4 &g1, 
 __device__ __forceinline__ float geom_score_id(const float4 *__restrict__ G, uint32_t id, float X, float Y, float s,
                                                bool &usable)
 {
-    const float4 g0 = G[2 * (size_t)id], g1 = G[2 * (size_t)id + 1];
+    const float4 g0 = G[RLD4 * (size_t)id], g1 = G[RLD4 * (size_t)id + 1];
     usable = !(g0.x < 0.0f);
     return geom_score(g0, g1, X, Y, s);
 }
 
-__global__ __launch_bounds__(256) void k_site_geometry(const float *__restrict__ S, int n_slots, int stride,
-                                                       float4 *__restrict__ G)
+__global__ __launch_bounds__(256) void k_site_records(const float *__restrict__ S, int n_slots, int stride,
+                                                      float4 *__restrict__ G)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= n_slots)
         return;
-    const long st = stride;
-    float4 g0, g1;
-    make_geom(S[i], S[st + i], S[PR * st + i], S[PDX * st + i], S[PDY * st + i], S[PA * st + i], g0, g1);
-    G[2 * (size_t)i] = g0;
-    G[2 * (size_t)i + 1] = g1;
+    float4 o[RLD4];
+    make_record(S, stride, i, o);
+#pragma unroll
+    for (int j = 0; j < RLD4; ++j)
+        G[RLD4 * (size_t)i + j] = o[j];
 }
 
 // ---------------------------------------------------------------------------
@@ -395,7 +406,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
     for (int sl = tid; sl < TB; sl += BLOCK) {
         const uint32_t c = L.key[sl];
         if (c != NONE) {
-            const float4 g0 = G[2 * (size_t)c], g1 = G[2 * (size_t)c + 1];
+            const float4 g0 = G[RLD4 * (size_t)c], g1 = G[RLD4 * (size_t)c + 1];
             L.rec[0][sl] = g0.x;
             L.rec[1][sl] = g0.y;
             L.rec[2][sl] = g0.z;
@@ -535,8 +546,8 @@ __global__ __launch_bounds__(BLOCK) void k_topk_exact(const float4 *__restrict__
         const uint32_t i = base + threadIdx.x;
         float4 g0 = make_float4(-1.0f, 0.0f, 0.0f, 0.0f), g1 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (i < n_slots) {
-            g0 = G[2 * (size_t)i];
-            g1 = G[2 * (size_t)i + 1];
+            g0 = G[RLD4 * (size_t)i];
+            g1 = G[RLD4 * (size_t)i + 1];
         }
         __syncthreads();
         l0[threadIdx.x] = g0;
@@ -579,27 +590,24 @@ struct SiteRec {
     float v[NREC];
 };
 
-__device__ __forceinline__ SiteRec load_rec_global(const float *__restrict__ S, long st, uint32_t c)
+__device__ __forceinline__ SiteRec load_rec_global(const float4 *__restrict__ G, uint32_t c)
 {
+    const float4 a = G[RLD4 * (size_t)c], b = G[RLD4 * (size_t)c + 1], cc = G[RLD4 * (size_t)c + 2],
+                 d = G[RLD4 * (size_t)c + 3];
     SiteRec R;
-    const float x = S[c], y = S[st + c], lt = S[PLT * st + c], r = S[PR * st + c];
-    const float c0 = S[PCR * st + c], c1 = S[PCG * st + c], c2 = S[PCB * st + c];
-    const float dx = S[PDX * st + c], dy = S[PDY * st + c], a = S[PA * st + c];
-    const Frame f = make_frame(dx, dy, a);
-    const float n2 = dx * dx + dy * dy;
-    const bool ok = !(x < 0.0f) && finitef(c0) && finitef(c1) && finitef(c2);
-    R.v[R_PX] = ok ? x : __builtin_nanf("");
-    R.v[R_PY] = y;
-    R.v[R_R] = r;
-    R.v[R_UX] = f.ux;
-    R.v[R_UY] = f.uy;
-    R.v[R_E] = f.E;
-    R.v[R_IE] = f.iE;
-    R.v[R_TAU] = __expf(lt);
-    R.v[R_C0] = c0;
-    R.v[R_C1] = c1;
-    R.v[R_C2] = c2;
-    R.v[R_INVN] = n2 >= 1e-30f ? rsqrtf(n2) : 0.0f;
+    const bool ok = !(a.x < 0.0f) && finitef(cc.x) && finitef(cc.y) && finitef(cc.z);
+    R.v[R_PX] = ok ? a.x : __builtin_nanf("");
+    R.v[R_PY] = a.y;
+    R.v[R_R] = a.z;
+    R.v[R_UX] = d.x;
+    R.v[R_UY] = d.y;
+    R.v[R_E] = d.z;
+    R.v[R_IE] = d.w;
+    R.v[R_TAU] = b.w;
+    R.v[R_C0] = cc.x;
+    R.v[R_C1] = cc.y;
+    R.v[R_C2] = cc.z;
+    R.v[R_INVN] = cc.w;
     return R;
 }
 
@@ -611,8 +619,8 @@ struct TileTable {
 // Phases 1-2 shared by forward and backward: insert the pixel's IDs, then one
 // thread per occupied slot fills its record.  slot[k]: table slot, -1 = spill,
 // -2 = no site (sentinel or ID >= n_slots).  Ends with a barrier.
-__device__ __forceinline__ void build_tile_table(TileTable &T, const float *__restrict__ S, long st,
-                                                 uint32_t n_slots, const uint32_t (&ids)[K], int (&slot)[K])
+__device__ __forceinline__ void build_tile_table(TileTable &T, const float4 *__restrict__ G, uint32_t n_slots,
+                                                 const uint32_t (&ids)[K], int (&slot)[K])
 {
     T.key[threadIdx.x] = NONE;
     __syncthreads();
@@ -626,7 +634,7 @@ __device__ __forceinline__ void build_tile_table(TileTable &T, const float *__re
     __syncthreads();
     const uint32_t c = T.key[threadIdx.x];
     if (c != NONE) {
-        const SiteRec R = load_rec_global(S, st, c);
+        const SiteRec R = load_rec_global(G, c);
 #pragma unroll
         for (int j = 0; j < NREC; ++j)
             T.rec[j][threadIdx.x] = R.v[j];
@@ -661,13 +669,12 @@ struct PixelBlend {
 
 // Record of list entry k: from the tile table, from global memory for a spilled
 // ID, or an unusable placeholder (px = NaN) for an empty entry.
-__device__ __forceinline__ SiteRec fetch_rec(const TileTable &T, const float *__restrict__ S, long st, uint32_t id,
-                                            int sl)
+__device__ __forceinline__ SiteRec fetch_rec(const TileTable &T, const float4 *__restrict__ G, uint32_t id, int sl)
 {
     if (sl >= 0)
         return table_rec(T, sl);
     if (sl == -1)
-        return load_rec_global(S, st, id);
+        return load_rec_global(G, id);
     SiteRec R;
 #pragma unroll
     for (int j = 0; j < NREC; ++j)
@@ -676,14 +683,14 @@ __device__ __forceinline__ SiteRec fetch_rec(const TileTable &T, const float *__
     return R;
 }
 
-__device__ __forceinline__ void blend_pixel(const TileTable &T, const float *__restrict__ S, long st,
+__device__ __forceinline__ void blend_pixel(const TileTable &T, const float4 *__restrict__ G,
                                             const uint32_t (&ids)[K], const int (&slot)[K], float X, float Y,
                                             float s, PixelBlend &B)
 {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const SiteRec R = fetch_rec(T, S, st, ids[k], slot[k]);
+        const SiteRec R = fetch_rec(T, G, ids[k], slot[k]);
         const float l = -R.v[R_TAU] * rec_score(R, X, Y, s);
         B.use[k] = finitef(l);
         B.l[k] = l;
@@ -735,7 +742,7 @@ __device__ __forceinline__ void load_ids(const uint4 *__restrict__ cand, long p,
 }
 
 // Render forward (reading note, key design 2; project page "Method").
-__global__ __launch_bounds__(BLOCK) void k_render_fwd(const float *__restrict__ S, uint32_t n_slots, int stride,
+__global__ __launch_bounds__(BLOCK) void k_render_fwd(const float4 *__restrict__ G, uint32_t n_slots,
                                                       const uint4 *__restrict__ cand, int W, int H,
                                                       float *__restrict__ out, float s, int tiles_x, int nb)
 {
@@ -744,15 +751,14 @@ __global__ __launch_bounds__(BLOCK) void k_render_fwd(const float *__restrict__ 
     tile_pixel(nb, tiles_x, col, row);
     const bool inside = col < W && row < H;
     const long p = (long)row * W + col;
-    const long st = stride;
     uint32_t ids[K];
     int slot[K];
     load_ids(cand, p, inside, ids);
-    build_tile_table(T, S, st, n_slots, ids, slot);
+    build_tile_table(T, G, n_slots, ids, slot);
     if (!inside)
         return;
     PixelBlend B;
-    blend_pixel(T, S, st, ids, slot, (float)col + 0.5f, (float)row + 0.5f, s, B);
+    blend_pixel(T, G, ids, slot, (float)col + 0.5f, (float)row + 0.5f, s, B);
     out[3 * p] = B.chat0;
     out[3 * p + 1] = B.chat1;
     out[3 * p + 2] = B.chat2;
@@ -849,7 +855,7 @@ __device__ __forceinline__ void flush_global(float *__restrict__ grad, uint32_t 
             unsafeAtomicAdd(&grad[(long)c * SAD_GRAD_LD + a], acc[a]);
 }
 
-__global__ __launch_bounds__(BLOCK) void k_render_bwd(const float *__restrict__ S, uint32_t n_slots, int stride,
+__global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__ G, uint32_t n_slots,
                                                       const uint4 *__restrict__ cand,
                                                       const float *__restrict__ target, int W, int H,
                                                       float *__restrict__ grad, float *__restrict__ loss_sum,
@@ -862,12 +868,11 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float *__restrict__ 
     const int col0 = col - (tid & (TILE - 1)), row0 = row - tid / TILE;
     const bool inside = col < W && row < H;
     const long p = (long)row * W + col;
-    const long st = stride;
     uint32_t ids[K];
     int slot[K];
     load_ids(cand, p, inside, ids);
     L.cnt[tid] = 0;
-    build_tile_table(L.T, S, st, n_slots, ids, slot);
+    build_tile_table(L.T, G, n_slots, ids, slot);
 
     // phase 3: blend, per-entry softmax quantities, spill entries straight to global
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
@@ -880,7 +885,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float *__restrict__ 
         stage[k] = false;
     if (inside) {
         PixelBlend B;
-        blend_pixel(L.T, S, st, ids, slot, X, Y, s, B);
+        blend_pixel(L.T, G, ids, slot, X, Y, s, B);
         const float t0 = target[3 * p], t1 = target[3 * p + 1], t2 = target[3 * p + 2];
         const float r0 = B.chat0 - t0, r1 = B.chat1 - t1, r2 = B.chat2 - t2;
         err = r0 * r0 + r1 * r1 + r2 * r2;
@@ -930,7 +935,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float *__restrict__ 
                     pos[k] = atomicAdd(&L.cnt[slot[k]], 1u);
                 } else {
                     float acc[SAD_NACC];
-                    entry_grads(load_rec_global(S, st, ids[k]), X, Y, s, wk[k], gk[k], dk[k], g0, g1, g2, acc);
+                    entry_grads(load_rec_global(G, ids[k]), X, Y, s, wk[k], gk[k], dk[k], g0, g1, g2, acc);
                     flush_global(grad, ids[k], acc);
                 }
             }
@@ -1100,7 +1105,7 @@ struct AdamArgs {
 };
 
 __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__restrict__ M, float *__restrict__ V,
-                                              float *__restrict__ G, float4 *__restrict__ geom, int n_slots,
+                                              float *__restrict__ G, float4 *__restrict__ rec, int n_slots,
                                               int stride, AdamArgs A)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
@@ -1134,11 +1139,12 @@ __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__re
         S[i] = x < 0.0f ? 0.0f : (x > A.W ? A.W : x);
         S[st + i] = y < 0.0f ? 0.0f : (y > A.H ? A.H : y);
     }
-    if (geom) {
-        float4 g0, g1;
-        make_geom(S[i], S[st + i], S[PR * st + i], S[PDX * st + i], S[PDY * st + i], S[PA * st + i], g0, g1);
-        geom[2 * (size_t)i] = g0;
-        geom[2 * (size_t)i + 1] = g1;
+    if (rec) {
+        float4 o[RLD4];
+        make_record(S, st, i, o);
+#pragma unroll
+        for (int j = 0; j < RLD4; ++j)
+            rec[RLD4 * (size_t)i + j] = o[j];
     }
 }
 
@@ -1205,23 +1211,23 @@ const char *sad_status_string(int status)
     }
 }
 
-int sad_site_geometry(const float *sites, int n_slots, int stride, float *geom, void *stream)
+int sad_site_records(const float *sites, int n_slots, int stride, float *rec, void *stream)
 {
     int rc;
     if ((rc = check_sites(n_slots, stride)))
         return rc;
     if (n_slots == 0)
         return SAD_OK;
-    if (!sites || !geom)
+    if (!sites || !rec)
         return SAD_ERR_ARG;
-    if (!aligned16(geom))
+    if (!aligned16(rec))
         return SAD_ERR_ALIGN;
-    hipLaunchKernelGGL(k_site_geometry, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, n_slots,
-                       stride, (float4 *)geom);
+    hipLaunchKernelGGL(k_site_records, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, n_slots,
+                       stride, (float4 *)rec);
     return launched();
 }
 
-int sad_topk_propagate(const float *geom, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
+int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
                        int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream)
 {
     int rc;
@@ -1231,13 +1237,13 @@ int sad_topk_propagate(const float *geom, int n_slots, const uint32_t *cand_in, 
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
-    if ((!geom && n_slots > 0) || !cand_in || !cand_out)
+    if ((!rec && n_slots > 0) || !cand_in || !cand_out)
         return SAD_ERR_ARG;
     const size_t bytes = (size_t)W * H * K * sizeof(uint32_t);
     const uintptr_t a0 = (uintptr_t)cand_in, a1 = (uintptr_t)cand_out;
     if (a0 < a1 + bytes && a1 < a0 + bytes)
         return SAD_ERR_ARG;
-    if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(geom))
+    if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
     const uint32_t pw = ((uint32_t)jump << 16) | (pass_index & 0xFFFFu);
@@ -1246,7 +1252,7 @@ int sad_topk_propagate(const float *geom, int n_slots, const uint32_t *cand_in, 
     // more workgroups fit on a CU.
     const float sc = scale_of(W, H);
     const hipStream_t hs = (hipStream_t)stream;
-    const float4 *G = (const float4 *)geom;
+    const float4 *G = (const float4 *)rec;
     const uint4 *ci = (const uint4 *)cand_in;
     uint4 *co = (uint4 *)cand_out;
     if (jump == 1)
@@ -1261,7 +1267,7 @@ int sad_topk_propagate(const float *geom, int n_slots, const uint32_t *cand_in, 
     return launched();
 }
 
-int sad_topk_exact(const float *geom, int n_slots, uint32_t *cand_out, int W, int H, void *stream)
+int sad_topk_exact(const float *rec, int n_slots, uint32_t *cand_out, int W, int H, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
@@ -1270,53 +1276,57 @@ int sad_topk_exact(const float *geom, int n_slots, uint32_t *cand_out, int W, in
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
-    if ((!geom && n_slots > 0) || !cand_out)
+    if ((!rec && n_slots > 0) || !cand_out)
         return SAD_ERR_ARG;
-    if (!aligned16(cand_out) || !aligned16(geom))
+    if (!aligned16(cand_out) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
-    hipLaunchKernelGGL(k_topk_exact, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)geom,
+    hipLaunchKernelGGL(k_topk_exact, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
                        (uint32_t)n_slots, (uint4 *)cand_out, W, H, scale_of(W, H), g.tiles_x, g.nb);
     return launched();
 }
 
-int sad_render_fwd(const float *sites, int n_slots, int stride, const uint32_t *cand, int W, int H, float *out_rgb,
-                   void *stream)
+int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, int H, float *out_rgb, void *stream)
 {
     int rc;
-    if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
+    if ((rc = check_image(W, H)))
         return rc;
+    if (n_slots < 0)
+        return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
-    if (!sites || !cand || !out_rgb)
+    if ((!rec && n_slots > 0) || !cand || !out_rgb)
         return SAD_ERR_ARG;
-    if (!aligned16(cand))
+    if (!aligned16(cand) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
-    hipLaunchKernelGGL(k_render_fwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, sites, (uint32_t)n_slots,
-                       stride, (const uint4 *)cand, W, H, out_rgb, scale_of(W, H), g.tiles_x, g.nb);
+    hipLaunchKernelGGL(k_render_fwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
+                       (uint32_t)n_slots, (const uint4 *)cand, W, H, out_rgb, scale_of(W, H), g.tiles_x, g.nb);
     return launched();
 }
 
-int sad_render_bwd(const float *sites, int n_slots, int stride, const uint32_t *cand, const float *target, int W,
-                   int H, float *grad, float *loss_sum, void *stream)
+int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
+                   float *grad, float *loss_sum, void *stream)
 {
     int rc;
-    if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
+    if ((rc = check_image(W, H)))
         return rc;
+    if (n_slots < 0)
+        return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
-    if (!sites || !cand || !target || !grad)
+    if ((!rec && n_slots > 0) || !cand || !target || (!grad && n_slots > 0))
         return SAD_ERR_ARG;
-    if (!aligned16(cand) || !aligned16(grad))
+    if (!aligned16(cand) || !aligned16(grad) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
-    hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, sites, (uint32_t)n_slots,
-                       stride, (const uint4 *)cand, target, W, H, grad, loss_sum, scale_of(W, H), g.tiles_x, g.nb);
+    hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
+                       (uint32_t)n_slots, (const uint4 *)cand, target, W, H, grad, loss_sum, scale_of(W, H),
+                       g.tiles_x, g.nb);
     return launched();
 }
 
-int sad_adam_step(float *sites, float *m, float *v, float *grad, float *geom, int n_slots, int stride, int step,
+int sad_adam_step(float *sites, float *m, float *v, float *grad, float *rec, int n_slots, int stride, int step,
                   int n_pixels, int W, int H, const sad_adam_cfg *cfg, void *stream)
 {
     int rc;
@@ -1326,7 +1336,7 @@ int sad_adam_step(float *sites, float *m, float *v, float *grad, float *geom, in
         return SAD_ERR_ARG;
     if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f && cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f && cfg->eps >= 0.0f))
         return SAD_ERR_ARG;
-    if (!aligned16(grad) || !aligned16(geom))
+    if (!aligned16(grad) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     if (n_slots == 0)
         return SAD_OK;
@@ -1342,7 +1352,7 @@ int sad_adam_step(float *sites, float *m, float *v, float *grad, float *geom, in
     A.W = (float)W;
     A.H = (float)H;
     hipLaunchKernelGGL(k_adam, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, m, v, grad,
-                       (float4 *)geom, n_slots, stride, A);
+                       (float4 *)rec, n_slots, stride, A);
     return launched();
 }
 

@@ -31,7 +31,7 @@ def _declared():
 def test_header_declares_the_hot_path():
     names = _declared()
     for fn in ("sad_topk_propagate", "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_topk_exact",
-               "sad_site_geometry", "sad_abi_version", "sad_status_string"):
+               "sad_site_records", "sad_abi_version", "sad_status_string"):
         assert fn in names
 
 
@@ -54,11 +54,11 @@ Q = 0x90000
 
 def test_propagate_rejects_bad_arguments(L):
     f = L.sad_topk_propagate
-    ok = dict(geom=P, n=4, a=P, b=Q, W=16, H=16, jump=1, pidx=0, seed=0, m=4)
+    ok = dict(rec=P, n=4, a=P, b=Q, W=16, H=16, jump=1, pidx=0, seed=0, m=4)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["geom"], a["n"], a["a"], a["b"], a["W"], a["H"], a["jump"], a["pidx"], a["seed"], a["m"], None)
+        return f(a["rec"], a["n"], a["a"], a["b"], a["W"], a["H"], a["jump"], a["pidx"], a["seed"], a["m"], None)
 
     assert call(jump=0) == ERR_ARG
     assert call(jump=65536) == ERR_ARG
@@ -67,9 +67,9 @@ def test_propagate_rejects_bad_arguments(L):
     assert call(n=-1) == ERR_ARG
     assert call(W=-1) == ERR_ARG
     assert call(H=70000) == ERR_ARG
-    assert call(geom=0) == ERR_ARG
-    assert call(geom=0, W=0) == 0        # empty image: pointers are not needed
-    assert call(geom=P + 8) == ERR_ALIGN
+    assert call(rec=0) == ERR_ARG
+    assert call(rec=0, W=0) == 0         # empty image: pointers are not needed
+    assert call(rec=P + 8) == ERR_ALIGN
     assert call(b=P) == ERR_ARG          # in place
     assert call(b=P + 32) == ERR_ARG     # overlapping maps
     assert call(a=P + 4, b=Q) == ERR_ALIGN
@@ -78,19 +78,21 @@ def test_propagate_rejects_bad_arguments(L):
 
 
 def test_render_and_adam_reject_bad_arguments(L):
-    assert L.sad_render_fwd(P, 4, 8, P + 8, 16, 16, Q, None) == ERR_ALIGN
-    assert L.sad_render_fwd(P, 4, 8, 0, 16, 16, Q, None) == ERR_ARG
-    assert L.sad_render_fwd(P, 9, 8, P, 16, 16, Q, None) == ERR_ARG
-    assert L.sad_render_fwd(P, 4, 8, P, 0, 16, Q, None) == 0
-    assert L.sad_render_bwd(P, 4, 8, P, 0, 16, 16, Q, None, None) == ERR_ARG  # target NULL
-    assert L.sad_render_bwd(P, 4, 8, P + 4, Q, 16, 16, Q, None, None) == ERR_ALIGN
-    assert L.sad_render_bwd(P, 4, 8, P, Q, 16, 16, Q + 4, None, None) == ERR_ALIGN  # grad records
+    assert L.sad_render_fwd(P, 4, P + 8, 16, 16, Q, None) == ERR_ALIGN
+    assert L.sad_render_fwd(P + 8, 4, P, 16, 16, Q, None) == ERR_ALIGN
+    assert L.sad_render_fwd(P, 4, 0, 16, 16, Q, None) == ERR_ARG
+    assert L.sad_render_fwd(P, -1, P, 16, 16, Q, None) == ERR_ARG
+    assert L.sad_render_fwd(0, 4, P, 16, 16, Q, None) == ERR_ARG
+    assert L.sad_render_fwd(P, 4, P, 0, 16, Q, None) == 0
+    assert L.sad_render_bwd(P, 4, P, 0, 16, 16, Q, None, None) == ERR_ARG  # target NULL
+    assert L.sad_render_bwd(P, 4, P + 4, Q, 16, 16, Q, None, None) == ERR_ALIGN
+    assert L.sad_render_bwd(P, 4, P, Q, 16, 16, Q + 4, None, None) == ERR_ALIGN  # grad records
     assert L.sad_topk_exact(P, 4, P + 4, 16, 16, None) == ERR_ALIGN
     assert L.sad_topk_exact(P, -1, P, 16, 16, None) == ERR_ARG
-    assert L.sad_site_geometry(P, 4, 8, P + 4, None) == ERR_ALIGN
-    assert L.sad_site_geometry(P, 9, 8, P, None) == ERR_ARG
-    assert L.sad_site_geometry(0, 4, 8, P, None) == ERR_ARG
-    assert L.sad_site_geometry(0, 0, 8, 0, None) == 0  # no slots: no-op
+    assert L.sad_site_records(P, 4, 8, P + 4, None) == ERR_ALIGN
+    assert L.sad_site_records(P, 9, 8, P, None) == ERR_ARG
+    assert L.sad_site_records(0, 4, 8, P, None) == ERR_ARG
+    assert L.sad_site_records(0, 0, 8, 0, None) == 0  # no slots: no-op
     cfg = sad.AdamConfig().to_c()
     A = L.sad_adam_step
     assert A(P, P, P, P, P, 4, 8, 0, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # step 0
@@ -107,7 +109,10 @@ def test_python_binding_refuses_cpu_tensors():
     import torch
     s = torch.zeros((10, 4))
     with pytest.raises(ValueError):
-        sad.render_fwd(s, 4, torch.zeros((2, 2, 8), dtype=torch.int32), 2, 2, torch.zeros((2, 2, 3)))
+        sad.render_fwd(torch.zeros((4, 16)), 4, torch.zeros((2, 2, 8), dtype=torch.int32), 2, 2,
+                       torch.zeros((2, 2, 3)))
+    with pytest.raises(ValueError):
+        sad.site_records(s, 4, torch.zeros((4, 16)))
 
 
 def test_jump_schedule():

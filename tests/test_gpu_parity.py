@@ -21,15 +21,15 @@ def _case(W, H, n, seed=1):
     return S, cin
 
 
-def _geom(S, n):
+def _rec(S, n):
     S_d = to_dev(S)
-    g = sad.new_geom(max(S.shape[1], 1), S_d.device)
-    sad.site_geometry(S_d, n, g)
+    g = sad.new_records(S.shape[1], S_d.device)
+    sad.site_records(S_d, n, g)
     return g
 
 
 def _gpu_propagate(S, n, cin, W, H, jump, pidx, seed, m):
-    g = _geom(S, n)
+    g = _rec(S, n)
     a = to_dev(cin)
     b = sad.new_map(W, H, a.device)
     sad.topk_propagate(g, n, a, b, W, H, jump, pidx, seed, m)
@@ -91,18 +91,29 @@ def test_propagate_schedule_from_empty_matches_oracle_each_pass(orc):
     assert recall > 0.99
 
 
-def test_site_geometry_encodes_the_score(orc):
-    """The scoring record reproduces the oracle's score: d = s*sqrt((U.delta)^2 +
+def test_site_records_encode_the_score(orc):
+    """The record reproduces the oracle's score: d = s*sqrt((U.delta)^2 +
     (V x delta)^2) - s*r evaluated in float64 from the GPU record vs the oracle's
-    float32 score; inactive slots keep x < 0."""
+    float32 score; it carries tau = exp(log tau), the colour, u, e^{+-a} and
+    1/|dir|; inactive slots keep x < 0."""
     W, H, n = 90, 70, 500
     S = synth.random_sites(n, W, H, 21)
     S[synth.DX] *= 3.0
     S[synth.DX, 7] = 0.0
     S[synth.DY, 7] = 0.0
     S[synth.X, 9] = -1.0
-    g = _geom(S, n).cpu().numpy().astype(np.float64)
-    assert g[9, 0] < 0 and (g[:, 7] == 0).all()
+    g = _rec(S, n).cpu().numpy().astype(np.float64)
+    assert g[9, 0] < 0
+    S64 = S.astype(np.float64)
+    act = np.arange(n) != 9
+    assert np.allclose(g[act, 7], np.exp(S64[synth.LOGTAU, act]), rtol=2e-6)
+    assert np.array_equal(g[:, 8:11], S64[synth.CR:synth.CB + 1, :n].T)
+    nrm = np.hypot(S64[synth.DX], S64[synth.DY])
+    ok = nrm > 0
+    assert np.allclose(g[ok, 11], 1 / nrm[ok], rtol=1e-6) and g[7, 11] == 0 and g[7, 12] == 1 and g[7, 13] == 0
+    assert np.allclose(g[ok, 12], S64[synth.DX, ok] / nrm[ok], atol=1e-6)
+    assert np.allclose(g[:, 14], np.exp(S64[synth.A, :n]), rtol=2e-6)
+    assert np.allclose(g[:, 14] * g[:, 15], 1.0, rtol=4e-6)
     rng = np.random.default_rng(0)
     pix = rng.integers(0, W * H, 4000)
     ids = rng.integers(0, n, 4000)
@@ -122,7 +133,7 @@ def test_topk_exact_matches_oracle(orc, W, H, n):
     print(f"exact W={W} H={H} n={n}", flush=True)
     S = synth.random_sites(n, W, H, 8)
     S[synth.X, ::7] = -1.0
-    g = _geom(S, n)
+    g = _rec(S, n)
     out = sad.new_map(W, H, g.device)
     sad.topk_exact(g, n, out, W, H)
     torch.cuda.synchronize()
@@ -133,10 +144,10 @@ def test_topk_exact_matches_oracle(orc, W, H, n):
 
 
 def _fwd(S, n, cand, W, H):
-    S_d = to_dev(S)
+    R_d = _rec(S, n)
     c = to_dev(cand)
-    out = torch.empty((H, W, 3), dtype=torch.float32, device=S_d.device)
-    sad.render_fwd(S_d, n, c, W, H, out)
+    out = torch.empty((H, W, 3), dtype=torch.float32, device=R_d.device)
+    sad.render_fwd(R_d, n, c, W, H, out)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -166,14 +177,14 @@ def test_render_fwd_edge_inputs(orc):
 
 
 def _bwd(S, n, cand, tgt, W, H, grad0=None):
-    S_d = to_dev(S)
+    R_d = _rec(S, n)
     c = to_dev(cand)
     t = to_dev(tgt)
-    g = sad.new_grad(S.shape[1], S_d.device)
+    g = sad.new_grad(S.shape[1], R_d.device)
     if grad0 is not None:
         g[:, :11].copy_(torch.from_numpy(grad0).t())
-    loss = torch.zeros(1, dtype=torch.float32, device=S_d.device)
-    sad.render_bwd(S_d, n, c, t, W, H, g, loss)
+    loss = torch.zeros(1, dtype=torch.float32, device=R_d.device)
+    sad.render_bwd(R_d, n, c, t, W, H, g, loss)
     torch.cuda.synchronize()
     gh = g.cpu().numpy().astype(np.float64)
     assert (gh[:, 11:] == 0).all(), "unused words of the gradient records were written"
@@ -239,14 +250,14 @@ def _adam_gpu(S, m, v, G, n, step, P, W, H, cfg):
     rec[:, :11] = G.T
     rec[:, 11:] = 7.0  # unused words: must survive untouched
     g_d = to_dev(rec)
-    geom = sad.new_geom(S.shape[1], S_d.device)
-    sad.adam_step(S_d, m_d, v_d, g_d, n, step, P, W, H, cfg, geom=geom)
+    rec = sad.new_records(S.shape[1], S_d.device)
+    sad.adam_step(S_d, m_d, v_d, g_d, n, step, P, W, H, cfg, rec=rec)
     torch.cuda.synchronize()
-    # the refreshed scoring records equal a fresh derivation from the updated sites
-    fresh = sad.new_geom(S.shape[1], S_d.device)
-    sad.site_geometry(S_d, n, fresh)
+    # the refreshed records equal a fresh derivation from the updated sites
+    fresh = sad.new_records(S.shape[1], S_d.device)
+    sad.site_records(S_d, n, fresh)
     torch.cuda.synchronize()
-    assert torch.equal(geom[:n], fresh[:n])
+    assert torch.equal(rec[:n], fresh[:n])
     gh = g_d.cpu().numpy()
     assert (gh[:, 11:] == 7.0).all()
     return [t.cpu().numpy().astype(np.float64) for t in (S_d, m_d, v_d)] + [np.ascontiguousarray(gh[:, :11].T).astype(np.float64)]
@@ -281,9 +292,9 @@ def test_adam_matches_oracle(orc, step):
 def test_empty_image_and_no_sites_are_noops():
     z = torch.zeros((10, 4), dtype=torch.float32, device="cuda")
     m0 = sad.new_map(0, 0)
-    sad.topk_propagate(sad.new_geom(4), 4, m0, sad.new_map(0, 0), 0, 0, 1, 0, 0, 4)
+    sad.topk_propagate(sad.new_records(4), 4, m0, sad.new_map(0, 0), 0, 0, 1, 0, 0, 4)
     out = torch.empty((0, 0, 3), dtype=torch.float32, device="cuda")
-    sad.render_fwd(z, 4, m0, 0, 0, out)
+    sad.render_fwd(sad.new_records(4), 4, m0, 0, 0, out)
     g = sad.new_grad(4)
     sad.adam_step(z, torch.zeros_like(z), torch.zeros_like(z), g, 0, 1, 1, 1, 1)
     torch.cuda.synchronize()
@@ -295,7 +306,7 @@ def test_fitter_iterations_reduce_loss(orc):
     S = synth.random_sites(n, W, H, synth.SEED_MODEL)
     tgt = orc.hard_render(synth.random_sites(n, W, H, synth.SEED_TARGET_SITES), n, W, H) + synth.pixel_noise(W, H)
     f = sad.Fitter(to_dev(S), n, to_dev(tgt), W, H)
-    assert torch.equal(f.geom[:n], _geom(S, n)[:n])
+    assert torch.equal(f.rec[:n], _rec(S, n)[:n])
     losses = []
     for _ in range(60):
         f.loss.zero_()
