@@ -525,6 +525,60 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
     cout[2 * p + 1] = make_uint4((uint32_t)best.k[4], (uint32_t)best.k[5], (uint32_t)best.k[6], (uint32_t)best.k[7]);
 }
 
+// Propagation pass without the tile table, for large jumps: there each neighbour
+// list is read by exactly one pixel of the tile, so hashing it buys no sharing.
+// Every candidate is scored from its site record (two 16-byte loads) and goes
+// through the same (d, ID) selection with a duplicate check.
+__global__ __launch_bounds__(BLOCK) void k_propagate_direct(const float4 *__restrict__ G, uint32_t n_slots,
+                                                            const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
+                                                            int W, int H, int jump, uint32_t seed_h, int n_inject,
+                                                            float s, int tiles_x, int nb)
+{
+    const int t = xcd_band(blockIdx.x, nb);
+    const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
+    const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
+    if (col >= W || row >= H)
+        return;
+    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    TopK64 best;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+        best.k[j] = ~0ull;
+    for (int li = 0; li < 5; ++li) {
+        const int c = li == 1 ? col - jump : li == 2 ? col + jump : col;
+        const int r = li == 3 ? row - jump : li == 4 ? row + jump : row;
+        if (c < 0 || c >= W || r < 0 || r >= H)
+            continue;
+        const long q = (long)r * W + c;
+        const uint4 a = cin[2 * q], b = cin[2 * q + 1];
+        const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (ids[k] < n_slots) {
+                bool usable;
+                const float d = geom_score_id(G, ids[k], X, Y, s, usable);
+                best.consider(ids[k], d, usable);
+            }
+        }
+    }
+    if (n_inject > 0) {
+        const uint32_t h = pcg_hash(seed_h ^ ((uint32_t)row * (uint32_t)W + (uint32_t)col));
+        uint32_t x = h ? h : 0x9E3779B9u;
+        for (int j = 0; j < n_inject; ++j) {
+            x = xorshift32(x);
+            const uint32_t c = (uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32);
+            if (c < n_slots) {
+                bool usable;
+                const float d = geom_score_id(G, c, X, Y, s, usable);
+                best.consider(c, d, usable);
+            }
+        }
+    }
+    const long p = (long)row * W + col;
+    cout[2 * p] = make_uint4((uint32_t)best.k[0], (uint32_t)best.k[1], (uint32_t)best.k[2], (uint32_t)best.k[3]);
+    cout[2 * p + 1] = make_uint4((uint32_t)best.k[4], (uint32_t)best.k[5], (uint32_t)best.k[6], (uint32_t)best.k[7]);
+}
+
 // ---------------------------------------------------------------------------
 // Exact top-K by brute force: every slot is scored for every pixel.  Scoring
 // records are staged through LDS 256 at a time.
@@ -879,10 +933,10 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
     float err = 0.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     float wk[K], gk[K], dk[K];
     uint32_t pos[K];
-    bool stage[K];
+    bool stage[K], spill[K];
 #pragma unroll
     for (int k = 0; k < K; ++k)
-        stage[k] = false;
+        stage[k] = spill[k] = false;
     if (inside) {
         PixelBlend B;
         blend_pixel(L.T, G, ids, slot, X, Y, s, B);
@@ -922,9 +976,11 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
             }
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                if (!B.use[k])
-                    continue;
                 const float w = B.e[k] * iZ;
+                // a zero-weight entry changes nothing: all its gradients vanish and
+                // removing it leaves the blend as it is
+                if (!B.use[k] || w == 0.0f)
+                    continue;
                 wk[k] = w;
                 gk[k] = w * (g0 * (B.c0[k] - B.chat0) + g1 * (B.c1[k] - B.chat1) + g2 * (B.c2[k] - B.chat2));
                 const float iZo = xe[k] > 0.0f ? 1.0f / xe[k] : 0.0f;
@@ -934,11 +990,47 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
                     stage[k] = true;
                     pos[k] = atomicAdd(&L.cnt[slot[k]], 1u);
                 } else {
-                    float acc[SAD_NACC];
-                    entry_grads(load_rec_global(G, ids[k]), X, Y, s, wk[k], gk[k], dk[k], g0, g1, g2, acc);
-                    flush_global(grad, ids[k], acc);
+                    spill[k] = true;
                 }
             }
+        }
+    }
+    // Spilled entries (IDs the tile table could not hold): each wave stages the
+    // 11 sums of its lanes' k-th spilled entry in LDS and flushes them together,
+    // consecutive lanes taking consecutive accumulators of one site, so an atomic
+    // instruction touches a few 64-byte records instead of one per lane.  The
+    // staging area is idle until the counting sort below.
+    {
+        const int lane = tid & 63;
+        float *vals = &L.u.r.part[0][0] + (tid >> 6) * (64 * SAD_NACC + 64);
+        uint32_t *vid = reinterpret_cast<uint32_t *>(vals + 64 * SAD_NACC);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (!__any(spill[k]))
+                continue;
+            float acc[SAD_NACC];
+#pragma unroll
+            for (int a = 0; a < SAD_NACC; ++a)
+                acc[a] = 0.0f;
+            if (spill[k])
+                entry_grads(load_rec_global(G, ids[k]), X, Y, s, wk[k], gk[k], dk[k], g0, g1, g2, acc);
+#pragma unroll
+            for (int a = 0; a < SAD_NACC; ++a)
+                vals[lane * SAD_NACC + a] = acc[a];  // odd stride: no bank conflicts
+            vid[lane] = spill[k] ? ids[k] : NONE;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int i = lane; i < 64 * SAD_NACC; i += 64) {
+                const int e = i / SAD_NACC, a = i - e * SAD_NACC;
+                const uint32_t c = vid[e];
+                const float v = vals[i];
+                if (c != NONE && v != 0.0f)
+                    unsafeAtomicAdd(&grad[(size_t)c * SAD_GRAD_LD + a], v);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
     L.g[0][tid] = g0;
@@ -1255,15 +1347,15 @@ int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, u
     const float4 *G = (const float4 *)rec;
     const uint4 *ci = (const uint4 *)cand_in;
     uint4 *co = (uint4 *)cand_out;
+    // Measured on kodak768: the tile table pays off only at jump 1, where the
+    // neighbour lists are the tile's own lists; from jump 2 on the table-free pass
+    // is as fast or faster (random cold-start lists: 90 vs 113 us at jump 2).
     if (jump == 1)
         hipLaunchKernelGGL((k_propagate<1, 256>), dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, W, H,
                            jump, seed_h, n_inject, sc, g.tiles_x, g.nb);
-    else if (jump <= 4)
-        hipLaunchKernelGGL((k_propagate<4, 512>), dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, W, H,
-                           jump, seed_h, n_inject, sc, g.tiles_x, g.nb);
     else
-        hipLaunchKernelGGL((k_propagate<TILE, 512>), dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, W,
-                           H, jump, seed_h, n_inject, sc, g.tiles_x, g.nb);
+        hipLaunchKernelGGL(k_propagate_direct, dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, W, H,
+                           jump, seed_h, n_inject, sc, g.tiles_x, g.nb);
     return launched();
 }
 
