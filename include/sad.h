@@ -182,13 +182,16 @@ int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, i
  * summation order, hence the last bits, vary from run to run.
  *   rec device [n_slots][16] read-only; target device [H][W][3] read-only;
  *   grad device [>= n_slots][16] float, +=;
- *   loss_sum device float or NULL, += sum_x ||c - t||^2.
+ *   loss_sum device float or NULL, += sum_x ||c - t||^2;
+ *   out_rgb device [H][W][3] float or NULL: if given, the blend c(x) of every
+ *   pixel is written there too -- the same values sad_render_fwd writes -- so a
+ *   training step needs one pass over the map for forward and backward.
  * The caller zeroes `grad` once; sad_adam_step re-zeroes accumulators 0..9 each
  * step; accumulator 10 keeps accumulating until the caller resets it.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN (cand or grad not 16-byte aligned), SAD_ERR_DEVICE.
  */
 int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
-                   float *grad, float *loss_sum, void *stream);
+                   float *grad, float *loss_sum, float *out_rgb, void *stream);
 
 /*
  * sad_adam_step -- Adam (Kingma & Ba 2015) on the ten site parameters, with the

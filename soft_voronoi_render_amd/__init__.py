@@ -96,7 +96,7 @@ def lib() -> ctypes.CDLL:
         L.sad_render_fwd.restype = i32
         L.sad_render_fwd.argtypes = [fp, i32, vp, i32, i32, fp, vp]
         L.sad_render_bwd.restype = i32
-        L.sad_render_bwd.argtypes = [fp, i32, vp, fp, i32, i32, fp, fp, vp]
+        L.sad_render_bwd.argtypes = [fp, i32, vp, fp, i32, i32, fp, fp, fp, vp]
         L.sad_adam_step.restype = i32
         L.sad_adam_step.argtypes = [fp, fp, fp, fp, fp, i32, i32, i32, i32, i32, i32, ctypes.POINTER(AdamCfg), vp]
         _lib = L
@@ -191,8 +191,9 @@ def render_fwd(rec, n_slots, cand, W, H, out_rgb, stream=None):
     _check("sad_render_fwd", lib().sad_render_fwd(r, n_slots, c, W, H, o, _stream(stream)))
 
 
-def render_bwd(rec, n_slots, cand, target, W, H, grad, loss_sum=None, stream=None):
-    """Gradients of the squared error, accumulated into grad (see sad_render_bwd)."""
+def render_bwd(rec, n_slots, cand, target, W, H, grad, loss_sum=None, out_rgb=None, stream=None):
+    """Gradients of the squared error, accumulated into grad; optionally also the
+    rendered image (see sad_render_bwd)."""
     r = _rec(rec, n_slots)
     c = _dev(cand, "cand", _U32, (H, W, K))
     t = _dev(target, "target", _F32, (H, W, 3))
@@ -200,7 +201,8 @@ def render_bwd(rec, n_slots, cand, target, W, H, grad, loss_sum=None, stream=Non
         raise ValueError("grad must be float32 [>= n_slots][16]")
     g = _dev(grad, "grad", _F32)
     ls = _dev(loss_sum, "loss_sum", _F32) if loss_sum is not None else None
-    _check("sad_render_bwd", lib().sad_render_bwd(r, n_slots, c, t, W, H, g, ls, _stream(stream)))
+    o = _dev(out_rgb, "out_rgb", _F32, (H, W, 3)) if out_rgb is not None else None
+    _check("sad_render_bwd", lib().sad_render_bwd(r, n_slots, c, t, W, H, g, ls, o, _stream(stream)))
 
 
 @dataclasses.dataclass
@@ -302,11 +304,12 @@ class Fitter:
         self.cur = 1 - self.cur
 
     def step(self, stream=None):
-        """One iteration (the hot path): propagate, forward, backward, Adam."""
+        """One iteration (the hot path): propagate, render forward and backward
+        (one fused launch that writes the image and the gradients), Adam."""
         it = self.it
         self.propagate(self.jump_at(it), it, stream)
-        render_fwd(self.rec, self.n_slots, self.cand, self.W, self.H, self.rgb, stream)
-        render_bwd(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, self.grad, self.loss, stream)
+        render_bwd(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, self.grad, self.loss, self.rgb,
+                   stream)
         adam_step(self.sites, self.m, self.v, self.grad, self.n_slots, it + 1, self.W * self.H, self.W, self.H,
                   self.adam, self.rec, stream)
         self.it += 1

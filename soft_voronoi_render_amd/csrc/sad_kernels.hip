@@ -913,7 +913,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
                                                       const uint4 *__restrict__ cand,
                                                       const float *__restrict__ target, int W, int H,
                                                       float *__restrict__ grad, float *__restrict__ loss_sum,
-                                                      float s, int tiles_x, int nb)
+                                                      float *__restrict__ out_rgb, float s, int tiles_x, int nb)
 {
     __shared__ BwdShared L;
     const int tid = threadIdx.x;
@@ -940,6 +940,11 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
     if (inside) {
         PixelBlend B;
         blend_pixel(L.T, G, ids, slot, X, Y, s, B);
+        if (out_rgb) {  // the forward of the same map, for free
+            out_rgb[3 * p] = B.chat0;
+            out_rgb[3 * p + 1] = B.chat1;
+            out_rgb[3 * p + 2] = B.chat2;
+        }
         const float t0 = target[3 * p], t1 = target[3 * p + 1], t2 = target[3 * p + 2];
         const float r0 = B.chat0 - t0, r1 = B.chat1 - t1, r2 = B.chat2 - t2;
         err = r0 * r0 + r1 * r1 + r2 * r2;
@@ -1398,7 +1403,7 @@ int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, i
 }
 
 int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
-                   float *grad, float *loss_sum, void *stream)
+                   float *grad, float *loss_sum, float *out_rgb, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
@@ -1413,7 +1418,7 @@ int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const fl
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
     hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
-                       (uint32_t)n_slots, (const uint4 *)cand, target, W, H, grad, loss_sum, scale_of(W, H),
+                       (uint32_t)n_slots, (const uint4 *)cand, target, W, H, grad, loss_sum, out_rgb, scale_of(W, H),
                        g.tiles_x, g.nb);
     return launched();
 }

@@ -84,9 +84,9 @@ def test_render_and_adam_reject_bad_arguments(L):
     assert L.sad_render_fwd(P, -1, P, 16, 16, Q, None) == ERR_ARG
     assert L.sad_render_fwd(0, 4, P, 16, 16, Q, None) == ERR_ARG
     assert L.sad_render_fwd(P, 4, P, 0, 16, Q, None) == 0
-    assert L.sad_render_bwd(P, 4, P, 0, 16, 16, Q, None, None) == ERR_ARG  # target NULL
-    assert L.sad_render_bwd(P, 4, P + 4, Q, 16, 16, Q, None, None) == ERR_ALIGN
-    assert L.sad_render_bwd(P, 4, P, Q, 16, 16, Q + 4, None, None) == ERR_ALIGN  # grad records
+    assert L.sad_render_bwd(P, 4, P, 0, 16, 16, Q, None, None, None) == ERR_ARG  # target NULL
+    assert L.sad_render_bwd(P, 4, P + 4, Q, 16, 16, Q, None, None, None) == ERR_ALIGN
+    assert L.sad_render_bwd(P, 4, P, Q, 16, 16, Q + 4, None, None, None) == ERR_ALIGN  # grad records
     assert L.sad_topk_exact(P, 4, P + 4, 16, 16, None) == ERR_ALIGN
     assert L.sad_topk_exact(P, -1, P, 16, 16, None) == ERR_ARG
     assert L.sad_site_records(P, 4, 8, P + 4, None) == ERR_ALIGN

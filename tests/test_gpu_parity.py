@@ -184,10 +184,13 @@ def _bwd(S, n, cand, tgt, W, H, grad0=None):
     if grad0 is not None:
         g[:, :11].copy_(torch.from_numpy(grad0).t())
     loss = torch.zeros(1, dtype=torch.float32, device=R_d.device)
-    sad.render_bwd(R_d, n, c, t, W, H, g, loss)
+    rgb = torch.full((H, W, 3), -7.0, dtype=torch.float32, device=R_d.device)
+    sad.render_bwd(R_d, n, c, t, W, H, g, loss, out_rgb=rgb)
     torch.cuda.synchronize()
     gh = g.cpu().numpy().astype(np.float64)
     assert (gh[:, 11:] == 0).all(), "unused words of the gradient records were written"
+    # the fused forward output equals the standalone forward bit for bit
+    assert np.array_equal(rgb.cpu().numpy(), _fwd(S, n, cand, W, H))
     return np.ascontiguousarray(gh[:, :11].T), float(loss.item())
 
 
