@@ -17,6 +17,7 @@ a step depend only on the step index, so the whole fit is captured once); the
 state is reset to the cold start before the timed replay.  Prints one JSON line.
 """
 import argparse
+import hashlib
 import json
 import os
 import subprocess
@@ -29,6 +30,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "soft_voronoi_render_amd", "csrc", "sad_kernels.hip")
+# kernel symbol of each timed launch (as rocprofv3 names it)
+KERNEL_SYMBOL = {"propagate": "k_propagate", "fwd_bwd": "k_render_bwd", "adam": "k_adam", "fwd": "k_render_fwd"}
+
+
+def source_digest():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the same counters on a plain copy of
+    known size), or None when there is none for this kernel and workload or the
+    kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rows = {}
+    digest = None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("source_sha256:"):
+            digest = line.split(":", 1)[1].strip()
+        elif line.startswith("traffic "):
+            kv = dict(f.split("=", 1) for f in line.split()[1:])
+            rows[kv["kernel"]] = kv
+    if digest != source_digest() or KERNEL_SYMBOL[kernel] not in rows:
+        return None
+    return float(rows[KERNEL_SYMBOL[kernel]]["bytes_per_launch"])
 
 
 def algorithmic_bytes(P, N):
@@ -96,7 +127,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--kernel-reps", type=int, default=50)
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of one graph replay")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of graph replays (for counter collection)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (reference for the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -191,18 +225,33 @@ def main():
         "fwd": lambda i: sad.render_fwd(fit.rec, N, fit.cand, W, H, fit.rgb),
     }
     for name, fn in launches.items():
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(R):
-                fn(i)
+        g = None
+        if not args.no_graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(R):
+                    fn(i)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        g.replay()
+        if g is not None:
+            g.replay()
+        else:
+            for i in range(R):
+                fn(i)
         e1.record(stream)
         torch.cuda.synchronize()
         kdur[name] = e0.elapsed_time(e1) / R * 1e-3  # s per launch
+    if args.copy_calibration_mib > 0:
+        # a plain elementwise copy kernel: reads and writes exactly `nbytes`
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     step_kernels = ("propagate", "fwd_bwd", "adam")
     dominant = max(step_kernels, key=kdur.get)
     achieved = kb[dominant] / kdur[dominant] / 1e9
@@ -231,7 +280,9 @@ def main():
             "kernels": kernels,
         },
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(wl.name, dominant),
+                     "algorithmic_bytes_per_launch": kb[dominant]},
     }
 
     if not args.no_cpu_baseline:
@@ -246,8 +297,10 @@ def cpu_baseline(wl, S0, budget_s):
     import synth
 
     oracle.build(force=False)
-    cores = os.cpu_count() or 1
+    # the host's share of cores: OMP_NUM_THREADS where the environment sets it
+    cores = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1))
     oracle.set_threads(cores)
+    cores = oracle.get_threads()
     W, H, N, P = wl.W, wl.H, wl.n_sites, wl.P
     S = S0.copy()
     tgt = (synth.pixel_noise(W, H, 99, 0.25) + 0.5).astype(np.float32)

@@ -82,6 +82,7 @@ extern "C" {
 #define SAD_NACC 11
 #define SAD_GRAD_LD 16
 #define SAD_REC_LD 16
+#define SAD_STAT_LD 8
 #define SAD_MAX_INJECT 16
 #define SAD_MAX_DIM 65535
 
@@ -90,7 +91,7 @@ enum sad_status {
     SAD_ERR_ARG = -1,           /* a size, count or pointer argument is invalid        */
     SAD_ERR_ALIGN = -2,         /* a pointer is not aligned as its layout requires     */
     SAD_ERR_DEVICE = -3,        /* the HIP runtime rejected a launch                    */
-    SAD_ERR_CAPACITY = -4,      /* reserved: a result would not fit the given capacity */
+    SAD_ERR_CAPACITY = -4,      /* a result would not fit the given capacity           */
     SAD_ERR_UNIMPLEMENTED = -5  /* reserved                                             */
 };
 
@@ -101,6 +102,17 @@ typedef struct sad_adam_cfg {
     float lr[SAD_NPARAM];
     float beta1, beta2, eps;
 } sad_adam_cfg;
+
+/* Budget control ([SUM] B.5; [NOTE] design 4).  The pages do not reproduce their
+ * constants (Tables B11/B12 are referenced, not given); the defaults in the
+ * Python binding are ours. */
+typedef struct sad_budget_cfg {
+    float split_frac; /* fraction of the active sites split per call                  */
+    float prune_frac; /* fraction of the active sites pruned per call                 */
+    float alpha;      /* split score E / max(m, min_mass)^alpha                       */
+    float min_mass;   /* mass (in pixels) below which a site's covariance is not used */
+    float shrink;     /* children: r *= shrink, log tau += log(shrink)                */
+} sad_budget_cfg;
 
 /* SAD_ABI_VERSION of the loaded library. */
 int sad_abi_version(void);
@@ -192,6 +204,56 @@ int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, i
  */
 int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
                    float *grad, float *loss_sum, float *out_rgb, void *stream);
+
+/*
+ * sad_densify_stats -- per-site statistics for budget control ([SUM] B.5: the
+ * densification score combines per-site mass, energy and weighted second
+ * moments).  Over the pixels x whose list holds site i, with w its softmax weight
+ * at x, e(x) = ||c(x) - t(x)||^2 and delta = x - p_i, accumulates (+=) into the
+ * site's record of `stats`:
+ *   [0] sum w   [1] sum w e   [2] sum w e dx   [3] sum w e dy
+ *   [4] sum w e dx^2   [5] sum w e dx dy   [6] sum w e dy^2   [7] unused
+ *   rec device [n_slots][16]; cand device [H][W][8]; target device [H][W][3];
+ *   stats device [>= n_slots][SAD_STAT_LD] float, 16-byte aligned, +=.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
+ */
+int sad_densify_stats(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
+                      float *stats, void *stream);
+
+/*
+ * sad_densify_prune -- budget control on the HOST ([SUM] B.5; [NOTE] design 4;
+ * [PRESS] 4).  All pointers are HOST pointers; the arrays are modified in place.
+ * Active sites: i < *n_slots with x >= 0; A = their count.
+ *  (Counts below are computed in double from the float fields of cfg.)
+ *  1. Split set: the floor(split_frac*A) active sites with the largest score
+ *     S = stats[1] / max(stats[0], min_mass)^alpha (S > 0; ties -> lower ID).
+ *  2. Prune set: the floor(prune_frac*A) active sites outside the split set with
+ *     the smallest removal delta (ties -> lower ID; non-finite never pruned).
+ *  3. Pruned sites get x = y = -1 (every kernel then ignores them, [SUM] B.5) and
+ *     m = v = 0.
+ *  4. Each split parent becomes two children offset by -o and +o from its
+ *     position (clamped into [0,W]x[0,H]), along the principal axis of its
+ *     error-weighted covariance, o = sqrt(lambda_max)/2 * e_max (e_max oriented
+ *     with x > 0, or +y when vertical; equal eigenvalues give (1,0)).  When the mass is
+ *     below min_mass or the covariance is degenerate, the axis is the Sobel
+ *     gradient of the target's luminance at the parent's pixel ((1,0) if zero) and
+ *     |o| = sqrt(max(mass, 1)/pi)/2 ([SUM] B.5 "a local Sobel-like gradient").
+ *     Children: colour = the target at their pixel, r *= shrink,
+ *     log tau += log(shrink), other fields copied, m = v = 0 ([SUM] B.5).  Child A
+ *     keeps the parent's slot; child B takes the lowest inactive slot below
+ *     *n_slots, else slot *n_slots (then *n_slots grows) while below capacity.
+ *     Child B's ID is written into the last entry of the lists of the pixel that
+ *     contains it and of its 4 neighbours, so the next propagation pass sees it.
+ *  sites [10][stride], m/v [10][stride], stats [stride][8], removal [stride]
+ *  (the removal-delta accumulator, e.g. column 10 of the gradient records),
+ *  cand [H][W][8], target [H][W][3]; *n_slots in/out; n_split/n_pruned (out,
+ *  may be NULL) receive the numbers of splits and prunes done.
+ * Errors: SAD_ERR_ARG; SAD_ERR_CAPACITY when some selected sites could not be
+ *  split for want of a free slot (everything that fitted is done).
+ */
+int sad_densify_prune(float *sites, float *m, float *v, int stride, int capacity, int *n_slots, const float *stats,
+                      const float *removal, uint32_t *cand, int W, int H, const float *target,
+                      const sad_budget_cfg *cfg, int *n_split, int *n_pruned);
 
 /*
  * sad_adam_step -- Adam (Kingma & Ba 2015) on the ten site parameters, with the

@@ -72,6 +72,7 @@ def lib():
             "orc_render_bwd": (None, [f64p, c_int, c_int, u32p, f32p, c_int, c_int, f64p, f64p]),
             "orc_adam_step": (None, [f64p, f64p, f64p, f64p, c_int, c_int, c_int, c_int, f64p, c_dbl, c_dbl,
                                      c_dbl, c_int, c_int]),
+            "orc_densify_stats": (None, [f64p, c_int, c_int, u32p, f32p, c_int, c_int, f64p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -252,3 +253,20 @@ def adam_step(params, m, v, grad, n_slots, step, n_pixels, lr, b1, b2, eps, W, H
     lib().orc_adam_step(_p(params, ctypes.c_double), _p(m, ctypes.c_double), _p(v, ctypes.c_double),
                         _p(grad, ctypes.c_double), n_slots, params.shape[1], step, n_pixels,
                         _p(lr, ctypes.c_double), b1, b2, eps, W, H)
+
+
+# ------------------------------------------------------------ budget control
+def densify_stats(sites, n_slots, cand, target, W, H, stats=None):
+    """Per-site mass, energy and error-weighted moments, float64 [stride][8] (+=)."""
+    S = _f64(sites)
+    cand = _u32(cand)
+    T = _f32(target)
+    if stats is None:
+        stats = np.zeros((S.shape[1], 8), dtype=np.float64)
+    assert stats.dtype == np.float64 and stats.flags["C_CONTIGUOUS"] and stats.shape == (S.shape[1], 8)
+    lib().orc_densify_stats(_p(S, ctypes.c_double), n_slots, S.shape[1], _p(cand, ctypes.c_uint32),
+                            _p(T, ctypes.c_float), W, H, _p(stats, ctypes.c_double))
+    return stats
+
+
+from .densify import densify_prune  # noqa: E402  (pure Python, no C)

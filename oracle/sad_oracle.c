@@ -600,3 +600,42 @@ void orc_adam_step(double *params, double *m, double *v, double *grad, int n_slo
             grad[(long)j * stride + i] = 0.0;
     }
 }
+
+/* --------------------------------------------------- budget statistics -----
+ * [SUM] B.5: the densification score combines per-site mass, energy and
+ * weighted second moments.  Per site i, over the pixels x whose list holds it
+ * (w = its softmax weight at x, e = ||c(x) - t(x)||^2, delta = x - p_i):
+ *   [0] sum w  [1] sum w e  [2] sum w e dx  [3] sum w e dy
+ *   [4] sum w e dx^2  [5] sum w e dx dy  [6] sum w e dy^2  [7] unused
+ * stats: float64 [stride][8], accumulated (+=), serial in pixel order.
+ */
+void orc_densify_stats(const double *S, int n_slots, int stride, const uint32_t *cand, const float *target, int W,
+                       int H, double *stats)
+{
+    long P = (long)W * H;
+    for (long p = 0; p < P; ++p) {
+        pix64 X;
+        int col = (int)(p % W), row = (int)(p / W);
+        forward_pixel(S, (uint32_t)n_slots, stride, cand + p * ORC_K, W, H, col, row, &X);
+        if (X.n == 0)
+            continue;
+        double e = 0.0;
+        for (int c = 0; c < 3; ++c) {
+            double r = X.chat[c] - (double)target[p * 3 + c];
+            e += r * r;
+        }
+        for (int k = 0; k < X.n; ++k) {
+            double w = X.w[k], we = w * e;
+            double dx = ((double)col + 0.5) - S[(long)P_X * stride + X.id[k]];
+            double dy = ((double)row + 0.5) - S[(long)P_Y * stride + X.id[k]];
+            double *o = stats + (long)X.id[k] * 8;
+            o[0] += w;
+            o[1] += we;
+            o[2] += we * dx;
+            o[3] += we * dy;
+            o[4] += we * dx * dx;
+            o[5] += we * dx * dy;
+            o[6] += we * dy * dy;
+        }
+    }
+}

@@ -24,7 +24,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libsad.so")
-SOURCES = [os.path.join(HERE, "csrc", "sad_kernels.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "sad_kernels.hip"), os.path.join(HERE, "csrc", "sad_budget.cpp")]
 INCLUDE = os.path.join(ROOT, "include")
 
 K = 8
@@ -33,8 +33,10 @@ NPARAM = 10
 NACC = 11
 GRAD_LD = 16
 REC_LD = 16
+STAT_LD = 8
 MAX_INJECT = 16
 
+SAD_OK, SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE, SAD_ERR_CAPACITY, SAD_ERR_UNIMPLEMENTED = 0, -1, -2, -3, -4, -5
 STATUS = {0: "ok", -1: "invalid argument", -2: "misaligned pointer", -3: "HIP launch failed",
           -4: "capacity exceeded", -5: "not implemented"}
 
@@ -64,6 +66,11 @@ def build(verbose: bool = False) -> str:
     global _lib
     _lib = None
     return LIB_PATH
+
+
+class BudgetCfg(ctypes.Structure):
+    _fields_ = [("split_frac", ctypes.c_float), ("prune_frac", ctypes.c_float), ("alpha", ctypes.c_float),
+                ("min_mass", ctypes.c_float), ("shrink", ctypes.c_float)]
 
 
 class AdamCfg(ctypes.Structure):
@@ -97,6 +104,12 @@ def lib() -> ctypes.CDLL:
         L.sad_render_fwd.argtypes = [fp, i32, vp, i32, i32, fp, vp]
         L.sad_render_bwd.restype = i32
         L.sad_render_bwd.argtypes = [fp, i32, vp, fp, i32, i32, fp, fp, fp, vp]
+        L.sad_densify_stats.restype = i32
+        L.sad_densify_stats.argtypes = [fp, i32, vp, fp, i32, i32, fp, vp]
+        ip = ctypes.POINTER(ctypes.c_int)
+        L.sad_densify_prune.restype = i32
+        L.sad_densify_prune.argtypes = [fp, fp, fp, i32, i32, ip, fp, fp, vp, i32, i32, fp,
+                                        ctypes.POINTER(BudgetCfg), ip, ip]
         L.sad_adam_step.restype = i32
         L.sad_adam_step.argtypes = [fp, fp, fp, fp, fp, i32, i32, i32, i32, i32, i32, ctypes.POINTER(AdamCfg), vp]
         _lib = L
@@ -104,7 +117,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("sad_abi_version", "sad_status_string", "sad_site_records", "sad_topk_propagate", "sad_topk_exact",
-            "sad_render_fwd", "sad_render_bwd", "sad_adam_step")
+            "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_densify_stats", "sad_densify_prune")
 
 
 # --------------------------------------------------------------- marshalling
@@ -234,6 +247,60 @@ def adam_step(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamConfig 
                                                 ctypes.byref(c), _stream(stream)))
 
 
+def densify_stats(rec, n_slots, cand, target, W, H, stats, stream=None):
+    """Per-site mass, energy and error-weighted moments, accumulated into stats
+    [>= n_slots][8] (see sad_densify_stats)."""
+    r = _rec(rec, n_slots)
+    c = _dev(cand, "cand", _U32, (H, W, K))
+    t = _dev(target, "target", _F32, (H, W, 3))
+    if stats.dim() != 2 or stats.shape[1] != STAT_LD or stats.shape[0] < n_slots:
+        raise ValueError("stats must be float32 [>= n_slots][8]")
+    st = _dev(stats, "stats", _F32)
+    _check("sad_densify_stats", lib().sad_densify_stats(r, n_slots, c, t, W, H, st, _stream(stream)))
+
+
+@dataclasses.dataclass
+class BudgetConfig:
+    """Budget-control settings (ours: the pages do not give their constants)."""
+    split_frac: float = 0.05
+    prune_frac: float = 0.05
+    alpha: float = 0.5
+    min_mass: float = 1.0
+    shrink: float = 0.85
+
+    def to_c(self) -> BudgetCfg:
+        return BudgetCfg(self.split_frac, self.prune_frac, self.alpha, self.min_mass, self.shrink)
+
+
+def densify_prune(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, target,
+                  cfg: BudgetConfig | None = None):
+    """Host-side split/prune on numpy arrays, in place (see sad_densify_prune).
+
+    sites, m, v: float32 [10][stride]; stats float32 [stride][8]; removal float32
+    [stride]; cand uint32 [H][W][8]; target float32 [H][W][3].  Returns
+    (new n_slots, n_split, n_pruned, status) -- status is 0 or SAD_ERR_CAPACITY."""
+    import numpy as np
+    for name, a, dt in (("sites", sites, np.float32), ("m", m, np.float32), ("v", v, np.float32),
+                        ("stats", stats, np.float32), ("removal", removal, np.float32), ("cand", cand, np.uint32),
+                        ("target", target, np.float32)):
+        if not isinstance(a, np.ndarray) or a.dtype != dt or not a.flags["C_CONTIGUOUS"]:
+            raise TypeError(f"{name} must be a C-contiguous numpy {np.dtype(dt).name} array")
+    stride = sites.shape[1]
+    if m.shape != sites.shape or v.shape != sites.shape or stats.shape != (stride, STAT_LD) or \
+            removal.shape != (stride,) or cand.shape != (H, W, K) or target.shape != (H, W, 3):
+        raise ValueError("densify_prune: inconsistent shapes")
+    ns = ctypes.c_int(n_slots)
+    nsp = ctypes.c_int(0)
+    npr = ctypes.c_int(0)
+    c = (cfg or BudgetConfig()).to_c()
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rc = lib().sad_densify_prune(p(sites), p(m), p(v), stride, capacity, ctypes.byref(ns), p(stats), p(removal),
+                                 p(cand), W, H, p(target), ctypes.byref(c), ctypes.byref(nsp), ctypes.byref(npr))
+    if rc not in (SAD_OK, SAD_ERR_CAPACITY):
+        raise SadError("sad_densify_prune", rc)
+    return ns.value, nsp.value, npr.value, rc
+
+
 def jump_schedule(W: int, H: int, n: int) -> list:
     """Jumps for n passes: B/2, B/4, ..., 1, then 1, with B = 2^ceil(log2 max(W,H))
     (paperlayer.ai summary, section 4 "Candidate maintenance"; B is our reading)."""
@@ -313,3 +380,30 @@ class Fitter:
         adam_step(self.sites, self.m, self.v, self.grad, self.n_slots, it + 1, self.W * self.H, self.W, self.H,
                   self.adam, self.rec, stream)
         self.it += 1
+
+    def densify(self, cfg: BudgetConfig | None = None, stream=None):
+        """Budget control between iterations: per-site statistics on the GPU
+        (sad_densify_stats), split/prune on the host (sad_densify_prune) using the
+        removal deltas accumulated since the last call, then the site records are
+        rebuilt and the removal accumulators cleared.  Returns (n_split, n_pruned)."""
+        import numpy as np
+        dev = self.sites.device
+        stride = self.sites.shape[1]
+        stats = torch.zeros((stride, STAT_LD), dtype=torch.float32, device=dev)
+        densify_stats(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, stats, stream)
+        torch.cuda.synchronize(dev)
+        sites = self.sites.cpu().numpy()
+        m = self.m.cpu().numpy()
+        v = self.v.cpu().numpy()
+        cand = self.cand.cpu().numpy().view(np.uint32)
+        removal = np.ascontiguousarray(self.grad[:, NACC - 1].cpu().numpy())
+        n, n_split, n_pruned, _ = densify_prune(sites, m, v, self.n_slots, stride, stats.cpu().numpy(), removal,
+                                                cand, self.W, self.H, self.target.cpu().numpy(), cfg)
+        self.sites.copy_(torch.from_numpy(sites))
+        self.m.copy_(torch.from_numpy(m))
+        self.v.copy_(torch.from_numpy(v))
+        self.cand.copy_(torch.from_numpy(cand.view(np.int32)))
+        self.grad[:, NACC - 1].zero_()
+        self.n_slots = n
+        self.refresh_records(stream)
+        return n_split, n_pruned

@@ -1,0 +1,217 @@
+// sad_budget.cpp -- host-side budget control (densify / prune) of libsad.
+//
+// Selection and splitting follow the paperlayer.ai summary, Appendix B.5 (score
+// energy / mass^alpha, split along a covariance- or gradient-estimated axis,
+// children take target colours, reduced log tau and r, reset Adam states; prune
+// by the removal delta, pruned sites get position (-1, -1)), the reading note's
+// key design 4 and the press article's section 4.  The per-site statistics come
+// from sad_densify_stats on the GPU; this file only ranks, splits and prunes.
+// Readings where the pages are silent are stated in include/sad.h.
+
+#include <stdint.h>
+
+#include <algorithm>
+#include <cmath>
+#include <numeric>
+#include <vector>
+
+#include "sad.h"
+
+namespace {
+
+enum { PX, PY, PLT, PR, PCR, PCG, PCB, PDX, PDY, PA };
+
+struct Img {
+    const float *t;
+    int W, H;
+    float lum(int c, int r) const
+    {
+        c = std::min(std::max(c, 0), W - 1);
+        r = std::min(std::max(r, 0), H - 1);
+        const float *q = t + 3 * ((long)r * W + c);
+        return 0.299f * q[0] + 0.587f * q[1] + 0.114f * q[2];
+    }
+    int col(double x) const { return std::min(std::max((int)std::floor(x), 0), W - 1); }
+    int row(double y) const { return std::min(std::max((int)std::floor(y), 0), H - 1); }
+};
+
+// Principal axis of the 2x2 symmetric matrix [[a, b], [b, c]].
+void principal_axis(double a, double b, double c, double &lam, double &ex, double &ey)
+{
+    const double h = 0.5 * (a - c);
+    lam = 0.5 * (a + c) + std::sqrt(h * h + b * b);
+    if (std::fabs(b) > 1e-300) {
+        ex = lam - c;
+        ey = b;
+    } else {
+        ex = a >= c ? 1.0 : 0.0;
+        ey = a >= c ? 0.0 : 1.0;
+    }
+    const double n = std::sqrt(ex * ex + ey * ey);
+    ex /= n;
+    ey /= n;
+}
+
+}  // namespace
+
+extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, int capacity, int *n_slots,
+                                 const float *stats, const float *removal, uint32_t *cand, int W, int H,
+                                 const float *target, const sad_budget_cfg *cfg, int *n_split_out,
+                                 int *n_pruned_out)
+{
+    if (!sites || !m || !v || !n_slots || !stats || !removal || !cand || !target || !cfg)
+        return SAD_ERR_ARG;
+    const int n = *n_slots;
+    if (n < 0 || stride < 1 || n > stride || capacity < n || capacity > stride || W < 1 || H < 1 ||
+        W > SAD_MAX_DIM || H > SAD_MAX_DIM)
+        return SAD_ERR_ARG;
+    if (!(cfg->split_frac >= 0.0f && cfg->split_frac <= 1.0f && cfg->prune_frac >= 0.0f &&
+          cfg->prune_frac <= 1.0f && cfg->shrink > 0.0f && cfg->min_mass >= 0.0f))
+        return SAD_ERR_ARG;
+    const long st = stride;
+    auto P = [&](int j, int i) -> float & { return sites[j * st + i]; };
+
+    std::vector<int> active;
+    for (int i = 0; i < n; ++i)
+        if (!(P(PX, i) < 0.0f))
+            active.push_back(i);
+    const long A = (long)active.size();
+    const int n_split = (int)std::floor((double)cfg->split_frac * (double)A);
+    const int n_prune = (int)std::floor((double)cfg->prune_frac * (double)A);
+
+    // 1. split set: largest score, ties -> lower ID
+    std::vector<std::pair<double, int>> sc;
+    for (int i : active) {
+        const double mass = stats[(long)i * SAD_STAT_LD + 0], energy = stats[(long)i * SAD_STAT_LD + 1];
+        const double S = energy / std::pow(std::max(mass, (double)cfg->min_mass), (double)cfg->alpha);
+        if (std::isfinite(S) && S > 0.0)
+            sc.push_back({S, i});
+    }
+    std::sort(sc.begin(), sc.end(), [](const std::pair<double, int> &a, const std::pair<double, int> &b) {
+        return a.first > b.first || (a.first == b.first && a.second < b.second);
+    });
+    std::vector<int> split;
+    for (int j = 0; j < (int)sc.size() && j < n_split; ++j)
+        split.push_back(sc[j].second);
+    std::vector<char> is_split(n, 0);
+    for (int i : split)
+        is_split[i] = 1;
+
+    // 2. prune set: smallest removal delta among the others, ties -> lower ID
+    std::vector<std::pair<double, int>> rm;
+    for (int i : active)
+        if (!is_split[i] && std::isfinite(removal[i]))
+            rm.push_back({(double)removal[i], i});
+    std::sort(rm.begin(), rm.end(), [](const std::pair<double, int> &a, const std::pair<double, int> &b) {
+        return a.first < b.first || (a.first == b.first && a.second < b.second);
+    });
+    int pruned = 0;
+    for (int j = 0; j < (int)rm.size() && j < n_prune; ++j) {
+        const int i = rm[j].second;
+        P(PX, i) = -1.0f;
+        P(PY, i) = -1.0f;
+        for (int q = 0; q < SAD_NPARAM; ++q)
+            m[q * st + i] = v[q * st + i] = 0.0f;
+        ++pruned;
+    }
+
+    // free slots for the second children: inactive slots below n (ascending), then n, n+1, ...
+    std::vector<int> free_slots;
+    for (int i = 0; i < n; ++i)
+        if (P(PX, i) < 0.0f)
+            free_slots.push_back(i);
+    size_t next_free = 0;
+    int count = n;
+    auto take_slot = [&]() -> int {
+        if (next_free < free_slots.size())
+            return free_slots[next_free++];
+        if (count < capacity)
+            return count++;
+        return -1;
+    };
+
+    // 3. splits
+    const Img img{target, W, H};
+    const float lshrink = std::log(cfg->shrink);
+    int done = 0;
+    bool short_of_slots = false;
+    for (int i : split) {
+        const int b = take_slot();
+        if (b < 0) {
+            short_of_slots = true;
+            break;
+        }
+        const float *S = stats + (long)i * SAD_STAT_LD;
+        const double mass = S[0], E = S[1];
+        double ox = 0.0, oy = 0.0;
+        bool have_axis = false;
+        if (mass >= cfg->min_mass && E > 0.0) {
+            const double mx = S[2] / E, my = S[3] / E;
+            const double cxx = S[4] / E - mx * mx, cxy = S[5] / E - mx * my, cyy = S[6] / E - my * my;
+            double lam, ex, ey;
+            principal_axis(cxx, cxy, cyy, lam, ex, ey);
+            if (std::isfinite(lam) && lam > 0.0) {
+                const double h = 0.5 * std::sqrt(lam);
+                ox = h * ex;
+                oy = h * ey;
+                have_axis = true;
+            }
+        }
+        if (!have_axis) {
+            const int c = img.col(P(PX, i)), r = img.row(P(PY, i));
+            double gx = (img.lum(c + 1, r - 1) + 2.0 * img.lum(c + 1, r) + img.lum(c + 1, r + 1)) -
+                        (img.lum(c - 1, r - 1) + 2.0 * img.lum(c - 1, r) + img.lum(c - 1, r + 1));
+            double gy = (img.lum(c - 1, r + 1) + 2.0 * img.lum(c, r + 1) + img.lum(c + 1, r + 1)) -
+                        (img.lum(c - 1, r - 1) + 2.0 * img.lum(c, r - 1) + img.lum(c + 1, r - 1));
+            const double gn = std::sqrt(gx * gx + gy * gy);
+            if (gn > 0.0) {
+                gx /= gn;
+                gy /= gn;
+            } else {
+                gx = 1.0;
+                gy = 0.0;
+            }
+            const double h = 0.5 * std::sqrt(std::max(mass, 1.0) / M_PI);
+            ox = h * gx;
+            oy = h * gy;
+        }
+        const double px = P(PX, i), py = P(PY, i);
+        const double cx[2] = {px - ox, px + ox}, cy[2] = {py - oy, py + oy};
+        const int slot[2] = {i, b};
+        float par[SAD_NPARAM];
+        for (int q = 0; q < SAD_NPARAM; ++q)
+            par[q] = P(q, i);
+        for (int h = 0; h < 2; ++h) {
+            const int s = slot[h];
+            for (int q = 0; q < SAD_NPARAM; ++q) {
+                P(q, s) = par[q];
+                m[q * st + s] = v[q * st + s] = 0.0f;
+            }
+            const double x = std::min(std::max(cx[h], 0.0), (double)W);
+            const double y = std::min(std::max(cy[h], 0.0), (double)H);
+            P(PX, s) = (float)x;
+            P(PY, s) = (float)y;
+            P(PR, s) = par[PR] * cfg->shrink;
+            P(PLT, s) = par[PLT] + lshrink;
+            const float *tc = target + 3 * ((long)img.row(y) * W + img.col(x));
+            P(PCR, s) = tc[0];
+            P(PCG, s) = tc[1];
+            P(PCB, s) = tc[2];
+        }
+        // seed child B into its pixel's list and the 4 neighbours' (last entry)
+        const int bc = img.col(P(PX, b)), br = img.row(P(PY, b));
+        const int dc[5] = {0, -1, 1, 0, 0}, dr[5] = {0, 0, 0, -1, 1};
+        for (int q = 0; q < 5; ++q) {
+            const int c = bc + dc[q], r = br + dr[q];
+            if (c >= 0 && c < W && r >= 0 && r < H)
+                cand[((long)r * W + c) * SAD_K + (SAD_K - 1)] = (uint32_t)b;
+        }
+        ++done;
+    }
+    *n_slots = count;
+    if (n_split_out)
+        *n_split_out = done;
+    if (n_pruned_out)
+        *n_pruned_out = pruned;
+    return short_of_slots ? SAD_ERR_CAPACITY : SAD_OK;
+}

@@ -1194,6 +1194,87 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Budget-control statistics (summary, B.5: the densification score combines
+// per-site mass, energy and weighted second moments).  For each site, over the
+// pixels x whose list holds it, with w its softmax weight at x, e = ||c(x) - t(x)||^2
+// and delta = x - p (the site position, so the moments stay well conditioned):
+//   [0] sum w   [1] sum w e   [2] sum w e dx   [3] sum w e dy
+//   [4] sum w e dx^2   [5] sum w e dx dy   [6] sum w e dy^2   [7] unused
+// accumulated (+=) into float [n][SAD_STAT_LD].  Runs every few dozen
+// iterations, so it flushes every entry through the per-wave cooperative path.
+constexpr int NSTAT = 7;
+
+__global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restrict__ G, uint32_t n_slots,
+                                                         const uint4 *__restrict__ cand,
+                                                         const float *__restrict__ target, int W, int H,
+                                                         float *__restrict__ stats, float s, int tiles_x, int nb)
+{
+    __shared__ TileTable T;
+    __shared__ float stage[BLOCK / 64][64 * NSTAT + 64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    int col, row;
+    tile_pixel(nb, tiles_x, col, row);
+    const bool inside = col < W && row < H;
+    const long p = (long)row * W + col;
+    uint32_t ids[K];
+    int slot[K];
+    load_ids(cand, p, inside, ids);
+    build_tile_table(T, G, n_slots, ids, slot);
+    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    PixelBlend B;
+    float err = 0.0f, iZ = 0.0f;
+    bool any = false;
+    if (inside) {
+        blend_pixel(T, G, ids, slot, X, Y, s, B);
+        const float r0 = B.chat0 - target[3 * p], r1 = B.chat1 - target[3 * p + 1], r2 = B.chat2 - target[3 * p + 2];
+        err = r0 * r0 + r1 * r1 + r2 * r2;
+        any = B.any;
+        iZ = any ? 1.0f / B.Z : 0.0f;
+    }
+    float *vals = stage[tid >> 6];
+    uint32_t *vid = reinterpret_cast<uint32_t *>(vals + 64 * NSTAT);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const bool has = any && B.use[k] && B.e[k] > 0.0f;
+        if (!__any(has))
+            continue;
+        float acc[NSTAT];
+#pragma unroll
+        for (int a = 0; a < NSTAT; ++a)
+            acc[a] = 0.0f;
+        if (has) {
+            const SiteRec R = fetch_rec(T, G, ids[k], slot[k]);
+            const float w = B.e[k] * iZ, we = w * err;
+            const float dx = X - R.v[R_PX], dy = Y - R.v[R_PY];
+            acc[0] = w;
+            acc[1] = we;
+            acc[2] = we * dx;
+            acc[3] = we * dy;
+            acc[4] = we * dx * dx;
+            acc[5] = we * dx * dy;
+            acc[6] = we * dy * dy;
+        }
+#pragma unroll
+        for (int a = 0; a < NSTAT; ++a)
+            vals[lane * NSTAT + a] = finitef(acc[a]) ? acc[a] : 0.0f;
+        vid[lane] = has ? ids[k] : NONE;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int i = lane; i < 64 * NSTAT; i += 64) {
+            const int e = i / NSTAT, a = i - e * NSTAT;
+            const uint32_t c = vid[e];
+            const float v = vals[i];
+            if (c != NONE && v != 0.0f)
+                unsafeAtomicAdd(&stats[(size_t)c * SAD_STAT_LD + a], v);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Adam (Kingma & Ba 2015) on the ten site parameters, gradients divided by the
 // pixel count (summary, B.4), gradient planes 0..9 zeroed in the same pass.
 struct AdamArgs {
@@ -1420,6 +1501,26 @@ int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const fl
     hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
                        (uint32_t)n_slots, (const uint4 *)cand, target, W, H, grad, loss_sum, out_rgb, scale_of(W, H),
                        g.tiles_x, g.nb);
+    return launched();
+}
+
+int sad_densify_stats(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
+                      float *stats, void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)))
+        return rc;
+    if (n_slots < 0)
+        return SAD_ERR_ARG;
+    if (W == 0 || H == 0)
+        return SAD_OK;
+    if ((!rec && n_slots > 0) || !cand || !target || (!stats && n_slots > 0))
+        return SAD_ERR_ARG;
+    if (!aligned16(cand) || !aligned16(rec) || !aligned16(stats))
+        return SAD_ERR_ALIGN;
+    const TileGrid g = tile_grid(W, H);
+    hipLaunchKernelGGL(k_densify_stats, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
+                       (uint32_t)n_slots, (const uint4 *)cand, target, W, H, stats, scale_of(W, H), g.tiles_x, g.nb);
     return launched();
 }
 

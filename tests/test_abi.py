@@ -105,6 +105,28 @@ def test_render_and_adam_reject_bad_arguments(L):
     assert A(P, P, P, P, None, 0, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == 0  # no slots: no-op
 
 
+def test_densify_entry_points_reject_bad_arguments(L):
+    D = L.sad_densify_stats
+    assert D(P, -1, P, Q, 16, 16, Q, None) == ERR_ARG
+    assert D(P, 4, 0, Q, 16, 16, Q, None) == ERR_ARG        # cand NULL
+    assert D(P, 4, P, 0, 16, 16, Q, None) == ERR_ARG        # target NULL
+    assert D(P, 4, P, Q, 16, 16, 0, None) == ERR_ARG        # stats NULL
+    assert D(P, 4, P + 4, Q, 16, 16, Q, None) == ERR_ALIGN
+    assert D(P, 4, P, Q, 16, 16, Q + 4, None) == ERR_ALIGN
+    assert D(P, 4, P, Q, 0, 16, Q, None) == 0               # empty image: no-op
+    assert D(P, 4, P, Q, 16, 70000, Q, None) == ERR_ARG
+    cfg = sad.BudgetConfig().to_c()
+    n = ctypes.c_int(4)
+    F = L.sad_densify_prune
+    assert F(None, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert F(P, P, P, 8, 8, None, P, P, P, 4, 4, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, P, None, None, None) == ERR_ARG
+    assert F(P, P, P, 8, 3, ctypes.byref(n), P, P, P, 4, 4, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert F(P, P, P, 8, 9, ctypes.byref(n), P, P, P, 4, 4, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 0, 4, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert n.value == 4
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     s = torch.zeros((10, 4))
