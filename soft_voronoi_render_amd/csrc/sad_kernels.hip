@@ -26,7 +26,7 @@ constexpr int TILE = 16;
 constexpr int BLOCK = TILE * TILE;
 constexpr int NXCD = 8;
 constexpr int HASH_SLOTS = 256;
-constexpr int HASH_PROBES = 8;
+constexpr int HASH_PROBES = 12;
 
 // Site planes (order of the site buffer).
 constexpr int PX = SAD_X, PY = SAD_Y, PLT = SAD_LOGTAU, PR = SAD_R, PCR = SAD_CR, PCG = SAD_CG, PCB = SAD_CB,
@@ -209,8 +209,11 @@ struct TopK {
 
 // ---------------------------------------------------------------------------
 // Inserts one list's IDs into an LDS hash table of TB slots keyed by site ID
-// (multiplicative hash, <= HASH_PROBES linear probes, CAS insert -- summary,
-// B.4).  refs[k]: the slot, REF_SPILL | ID if every probe is taken by other IDs,
+// (multiplicative hash, CAS insert -- summary, B.4; double hashing with an odd
+// step, <= HASH_PROBES probes: at the ~30 % load of a converged map's tile no ID
+// then fails to find a slot, whereas linear probing's clusters made a few tiles
+// per launch take the slow spill path and finish last).  refs[k]: the slot,
+// REF_SPILL | ID if every probe is taken by other IDs,
 // REF_NONE when ids[k] >= n_slots.  (Measured on gfx950: one CAS per probe, ID
 // by ID, beats reading the slot first and beats issuing the CAS of all IDs of a
 // list at once -- same-address atomics from many lanes serialise.)
@@ -230,8 +233,9 @@ __device__ __forceinline__ void table_insert_ids(uint32_t *key, const uint32_t (
         if (c < n_slots) {
             r = REF_SPILL | c;
             const uint32_t h0 = (c * 2654435761u) >> SHIFT;
+            const uint32_t step = ((c * 0x85EBCA6Bu) >> SHIFT) | 1u;
             for (int pr = 0; pr < HASH_PROBES; ++pr) {
-                const uint32_t sl = (h0 + pr) & (TB - 1);
+                const uint32_t sl = (h0 + (uint32_t)pr * step) & (TB - 1);
                 const uint32_t prev = atomicCAS(&key[sl], NONE, c);
                 if (prev == NONE || prev == c) {
                     r = sl;
@@ -329,8 +333,13 @@ struct TopK64 {
 
 template <int KK, int TB>
 struct PropShared {
-    uint32_t key[TB];
-    float rec[7][TB];                           // px py r ux uy E iE
+    // The hash keys are needed until the records are loaded; from then on a
+    // slot's ID travels in the last float of its record (the scoring record's
+    // tau, which scoring does not use).
+    union {
+        uint32_t key[TB];
+        float4 rec[TB][2];                      // the 32-byte scoring record per slot
+    } t;
     uint32_t ref[(BLOCK + 4 * TILE * KK) * K];  // per region list: 8 slots / spilled IDs
     uint32_t seen[TB / 32][BLOCK];              // per pixel: slots already taken (word-major)
 };
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
     const int nlists = BLOCK + 4 * strip_len;
 
     for (int sl = tid; sl < TB; sl += BLOCK)
-        L.key[sl] = NONE;
+        L.t.key[sl] = NONE;
 #pragma unroll
     for (int w = 0; w < TB / 32; ++w)
         L.seen[w][tid] = 0u;
@@ -395,25 +404,27 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
         }
         const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         uint32_t refs[K];
-        table_insert_ids<TB>(L.key, ids, n_slots, refs);
+        table_insert_ids<TB>(L.t.key, ids, n_slots, refs);
         uint4 *dst = reinterpret_cast<uint4 *>(&L.ref[r * K]);
         dst[0] = make_uint4(refs[0], refs[1], refs[2], refs[3]);
         dst[1] = make_uint4(refs[4], refs[5], refs[6], refs[7]);
     }
     __syncthreads();
 
-    // phase 2: one scoring record per occupied slot
-    for (int sl = tid; sl < TB; sl += BLOCK) {
-        const uint32_t c = L.key[sl];
+    // phase 2: one scoring record per occupied slot (written over the keys)
+    static_assert(TB == BLOCK, "one slot per lane");
+    {
+        const uint32_t c = L.t.key[tid];
+        float4 g0, g1;
         if (c != NONE) {
-            const float4 g0 = G[RLD4 * (size_t)c], g1 = G[RLD4 * (size_t)c + 1];
-            L.rec[0][sl] = g0.x;
-            L.rec[1][sl] = g0.y;
-            L.rec[2][sl] = g0.z;
-            L.rec[3][sl] = g0.w;
-            L.rec[4][sl] = g1.x;
-            L.rec[5][sl] = g1.y;
-            L.rec[6][sl] = g1.z;
+            g0 = G[RLD4 * (size_t)c];
+            g1 = G[RLD4 * (size_t)c + 1];
+            g1.w = __uint_as_float(c);
+        }
+        __syncthreads();
+        if (c != NONE) {
+            L.t.rec[tid][0] = g0;
+            L.t.rec[tid][1] = g1;
         }
     }
     __syncthreads();
@@ -421,10 +432,10 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
     if (col >= W || row >= H)
         return;
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
-    auto rec_score_slot = [&](uint32_t sl, bool &usable) {
-        const float4 g0 = make_float4(L.rec[0][sl], L.rec[1][sl], L.rec[2][sl], L.rec[3][sl]);
-        const float4 g1 = make_float4(L.rec[4][sl], L.rec[5][sl], L.rec[6][sl], 0.0f);
+    auto rec_score_slot = [&](uint32_t sl, bool &usable, uint32_t &id) {
+        const float4 g0 = L.t.rec[sl][0], g1 = L.t.rec[sl][1];
         usable = !(g0.x < 0.0f);
+        id = __float_as_uint(g1.w);
         return geom_score(g0, g1, X, Y, s);
     };
     // marks slot sl as taken by this pixel; true if it was not taken before
@@ -446,9 +457,10 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
             v[k] = ~0ull;
             if (ref < (uint32_t)TB && take(ref)) {
                 bool usable;
-                const float d = rec_score_slot(ref, usable);
+                uint32_t id;
+                const float d = rec_score_slot(ref, usable, id);
                 if (usable && finitef(d))
-                    v[k] = rank_key(d, L.key[ref]);
+                    v[k] = rank_key(d, id);
             }
         }
         best.set_sorted(v);
@@ -497,8 +509,9 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
                 ref = j == k ? refs[k] : ref;
             bool usable;
             if (ref < (uint32_t)TB) {
-                const float d = rec_score_slot(ref, usable);
-                best.consider_new(L.key[ref], d, usable);
+                uint32_t id;
+                const float d = rec_score_slot(ref, usable, id);
+                best.consider_new(id, d, usable);
             } else {
                 const uint32_t c = ref & ~REF_SPILL;
                 const float d = geom_score_id(G, c, X, Y, s, usable);
@@ -632,9 +645,9 @@ __global__ __launch_bounds__(BLOCK) void k_topk_exact(const float4 *__restrict__
 // (multiplicative hash, <= 8 linear probes, CAS insert -- summary, B.4).  An ID
 // that finds no slot takes the "spill" path and is read from global memory.
 constexpr int TBL = 256;
-constexpr int NREC = 12;  // px py r ux uy E iE tau R G B inv_n
+constexpr int NREC = 12;  // (px py r tau) (ux uy E iE) (R G B inv_n): three float4
 
-enum { R_PX, R_PY, R_R, R_UX, R_UY, R_E, R_IE, R_TAU, R_C0, R_C1, R_C2, R_INVN };
+enum { R_PX, R_PY, R_R, R_TAU, R_UX, R_UY, R_E, R_IE, R_C0, R_C1, R_C2, R_INVN };
 
 // Derived record of one site: the metric frame, tau = exp(log tau), the colour
 // and 1/|dir| (0 for a degenerate direction).  A site that cannot take part --
@@ -665,9 +678,11 @@ __device__ __forceinline__ SiteRec load_rec_global(const float4 *__restrict__ G,
     return R;
 }
 
+// Records are kept slot-major as three float4, so a lane fetches a record with
+// three 16-byte LDS reads rather than one read per field.
 struct TileTable {
     uint32_t key[TBL];
-    float rec[NREC][TBL];
+    float4 rec[TBL][NREC / 4];
 };
 
 // Phases 1-2 shared by forward and backward: insert the pixel's IDs, then one
@@ -690,8 +705,8 @@ __device__ __forceinline__ void build_tile_table(TileTable &T, const float4 *__r
     if (c != NONE) {
         const SiteRec R = load_rec_global(G, c);
 #pragma unroll
-        for (int j = 0; j < NREC; ++j)
-            T.rec[j][threadIdx.x] = R.v[j];
+        for (int j = 0; j < NREC / 4; ++j)
+            T.rec[threadIdx.x][j] = make_float4(R.v[4 * j], R.v[4 * j + 1], R.v[4 * j + 2], R.v[4 * j + 3]);
     }
     __syncthreads();
 }
@@ -700,8 +715,13 @@ __device__ __forceinline__ SiteRec table_rec(const TileTable &T, int sl)
 {
     SiteRec R;
 #pragma unroll
-    for (int j = 0; j < NREC; ++j)
-        R.v[j] = T.rec[j][sl];
+    for (int j = 0; j < NREC / 4; ++j) {
+        const float4 q = T.rec[sl][j];
+        R.v[4 * j] = q.x;
+        R.v[4 * j + 1] = q.y;
+        R.v[4 * j + 2] = q.z;
+        R.v[4 * j + 3] = q.w;
+    }
     return R;
 }
 
@@ -909,6 +929,40 @@ __device__ __forceinline__ void flush_global(float *__restrict__ grad, uint32_t 
             unsafeAtomicAdd(&grad[(long)c * SAD_GRAD_LD + a], acc[a]);
 }
 
+// Gradients of one spilled entry per lane (id = NONE: none), flushed by the
+// whole wave together: the 11 sums of each lane are staged in LDS and
+// consecutive lanes take consecutive accumulators of one site, so an atomic
+// instruction touches a few 64-byte records instead of one per lane.
+__device__ __forceinline__ void spill_flush(const float4 *__restrict__ G, uint32_t id, float X, float Y,
+                                                      float s, float w, float gm, float dl, float g0, float g1,
+                                                      float g2, float *vals, float *__restrict__ grad, int lane)
+{
+    uint32_t *vid = reinterpret_cast<uint32_t *>(vals + 64 * SAD_NACC);
+    float acc[SAD_NACC];
+#pragma unroll
+    for (int a = 0; a < SAD_NACC; ++a)
+        acc[a] = 0.0f;
+    if (id != NONE)
+        entry_grads(load_rec_global(G, id), X, Y, s, w, gm, dl, g0, g1, g2, acc);
+#pragma unroll
+    for (int a = 0; a < SAD_NACC; ++a)
+        vals[lane * SAD_NACC + a] = acc[a];  // odd stride: no bank conflicts
+    vid[lane] = id;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = lane; i < 64 * SAD_NACC; i += 64) {
+        const int e = i / SAD_NACC, a = i - e * SAD_NACC;
+        const uint32_t c = vid[e];
+        const float v = vals[i];
+        if (c != NONE && v != 0.0f)
+            unsafeAtomicAdd(&grad[(size_t)c * SAD_GRAD_LD + a], v);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__ G, uint32_t n_slots,
                                                       const uint4 *__restrict__ cand,
                                                       const float *__restrict__ target, int W, int H,
@@ -1000,43 +1054,16 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
             }
         }
     }
-    // Spilled entries (IDs the tile table could not hold): each wave stages the
-    // 11 sums of its lanes' k-th spilled entry in LDS and flushes them together,
-    // consecutive lanes taking consecutive accumulators of one site, so an atomic
-    // instruction touches a few 64-byte records instead of one per lane.  The
-    // staging area is idle until the counting sort below.
+    // Spilled entries (IDs the tile table could not hold), k by k where any lane
+    // of the wave has one (see spill_flush; the staging area is idle until the
+    // counting sort below).
     {
         const int lane = tid & 63;
         float *vals = &L.u.r.part[0][0] + (tid >> 6) * (64 * SAD_NACC + 64);
-        uint32_t *vid = reinterpret_cast<uint32_t *>(vals + 64 * SAD_NACC);
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            if (!__any(spill[k]))
-                continue;
-            float acc[SAD_NACC];
-#pragma unroll
-            for (int a = 0; a < SAD_NACC; ++a)
-                acc[a] = 0.0f;
-            if (spill[k])
-                entry_grads(load_rec_global(G, ids[k]), X, Y, s, wk[k], gk[k], dk[k], g0, g1, g2, acc);
-#pragma unroll
-            for (int a = 0; a < SAD_NACC; ++a)
-                vals[lane * SAD_NACC + a] = acc[a];  // odd stride: no bank conflicts
-            vid[lane] = spill[k] ? ids[k] : NONE;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            for (int i = lane; i < 64 * SAD_NACC; i += 64) {
-                const int e = i / SAD_NACC, a = i - e * SAD_NACC;
-                const uint32_t c = vid[e];
-                const float v = vals[i];
-                if (c != NONE && v != 0.0f)
-                    unsafeAtomicAdd(&grad[(size_t)c * SAD_GRAD_LD + a], v);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
+        for (int k = 0; k < K; ++k)
+            if (__any(spill[k]))
+                spill_flush(G, spill[k] ? ids[k] : NONE, X, Y, s, wk[k], gk[k], dk[k], g0, g1, g2, vals, grad, lane);
     }
     L.g[0][tid] = g0;
     L.g[1][tid] = g1;
