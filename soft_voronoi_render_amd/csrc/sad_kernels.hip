@@ -851,6 +851,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_fwd(const float4 *__restrict__
 // accumulator.  Runs that lie strictly inside a chunk are flushed by the chunk
 // thread.  Either way a site gets one global atomic per accumulator per tile.
 constexpr int CHUNK = 8;
+constexpr int NSUM = 10;  // per-entry sums of the reduction (entry_sums)
 
 // Staged entries live field-major with the 8 entries of one chunk interleaved:
 // sorted entry e sits at column e / CHUNK of row e % CHUNK, so when every thread
@@ -863,7 +864,7 @@ struct BwdShared {
     TileTable T;
     uint32_t cnt[TBL];
     uint32_t off[TBL];
-    float g[3][BLOCK];
+    float4 g[BLOCK];  // per pixel: 2 (c - t), and 0
     union {
         struct {
             uint32_t ps[BLOCK * K];  // pixel | slot << 8
@@ -872,78 +873,97 @@ struct BwdShared {
             float rdelta[BLOCK * K];
         } e;
         struct {
-            float part[2 * SAD_NACC][BLOCK];  // per chunk: [0,11) head partial, [11,22) tail partial
-            float fin[SAD_NACC][TBL];         // per table slot: the tile's total
+            float part[2 * NSUM][BLOCK];  // per chunk: [0,10) head partial, [10,20) tail partial
+            float fin[SAD_NACC][TBL];     // per table slot: the tile's sums, then its 11 totals
         } r;
     } u;
     float wsum[BLOCK / 64];
     uint32_t total;
 };
 
-// The 11 contributions of one entry given its site record, pixel position and
-// the per-entry softmax quantities (derivation: reading note, key designs 1-2).
-__device__ __forceinline__ void entry_grads(const SiteRec &R, float X, float Y, float s, float w, float gamma,
-                                            float rdelta, float g0, float g1, float g2, float (&acc)[SAD_NACC])
+// The backward of one site over a set of entries is linear in ten per-entry
+// sums (derivation: reading note, key designs 1-2; alpha = u.delta,
+// beta = u x delta, q^2 = e^a alpha^2 + e^-a beta^2, t = gamma / q, 0 at q = 0):
+//   [0..2] w g   [3] gamma   [4] t alpha   [5] t beta   [6] t alpha^2
+//   [7] t beta^2   [8] t alpha beta   [9] removal delta
+// so the reduction adds these and site_grads turns a site's totals into its 11
+// gradient contributions once.  Non-finite sums of an entry are dropped.
+__device__ __forceinline__ void entry_sums(const SiteRec &R, float X, float Y, float w, float gamma, float rdelta,
+                                           const float4 &g, float (&v)[NSUM])
 {
-    const float tau = R.v[R_TAU];
     const float ex = X - R.v[R_PX], ey = Y - R.v[R_PY];
-    const float ux = R.v[R_UX], uy = R.v[R_UY], E = R.v[R_E], iE = R.v[R_IE];
-    const float al = ux * ex + uy * ey;
-    const float be = ux * ey - uy * ex;
-    const float q = sqrtf(E * al * al + iE * be * be);
-    const float d = s * q - s * R.v[R_R];
-    acc[PCR] = w * g0;
-    acc[PCG] = w * g1;
-    acc[PCB] = w * g2;
-    acc[PLT] = gamma * (-tau * d);
-    acc[PR] = tau * gamma * s;
-    acc[PX] = acc[PY] = acc[PA] = acc[PDX] = acc[PDY] = 0.0f;
-    if (q > 0.0f) {
-        const float fq = (-tau * gamma * s) / q;  // (dL/dq) / q
-        const float Ea = E * al, Eb = iE * be;
-        acc[PX] = -fq * (Ea * ux - Eb * uy);
-        acc[PY] = -fq * (Ea * uy + Eb * ux);
-        acc[PA] = 0.5f * fq * (Ea * al - Eb * be);
-        const float in = R.v[R_INVN];
-        if (in > 0.0f) {
-            const float gux = fq * (Ea * ex + Eb * ey);
-            const float guy = fq * (Ea * ey - Eb * ex);
-            const float proj = ux * gux + uy * guy;
-            acc[PDX] = (gux - proj * ux) * in;
-            acc[PDY] = (guy - proj * uy) * in;
-        }
+    const float ux = R.v[R_UX], uy = R.v[R_UY];
+    const float al = ux * ex + uy * ey, be = ux * ey - uy * ex;
+    const float q2 = R.v[R_E] * al * al + R.v[R_IE] * be * be;
+    const float t = q2 > 0.0f ? gamma * __builtin_amdgcn_rsqf(q2) : 0.0f;
+    const float tal = t * al, tbe = t * be;
+    v[0] = w * g.x;
+    v[1] = w * g.y;
+    v[2] = w * g.z;
+    v[3] = gamma;
+    v[4] = tal;
+    v[5] = tbe;
+    v[6] = tal * al;
+    v[7] = tbe * be;
+    v[8] = tal * be;
+    v[9] = rdelta;
+    float all = v[0];
+#pragma unroll
+    for (int a = 1; a < NSUM; ++a)
+        all += v[a];
+    if (!finitef(all)) {
+#pragma unroll
+        for (int a = 0; a < NSUM; ++a)
+            v[a] = finitef(v[a]) ? v[a] : 0.0f;
     }
-    acc[10] = rdelta;
+}
+
+// A site's 11 gradient contributions from its entry-sum totals v (entry_sums):
+//   colour: v[0..2]        r: tau s v[3]      log tau: -tau s (e^a v[6] + e^-a v[7] - r v[3])
+//   p: tau s (e^a u v[4] + e^-a (-u_y, u_x) v[5])      a: -tau s (e^a v[6] - e^-a v[7]) / 2
+//   dir: the gradient w.r.t. u projected off u and divided by |dir|, which for a
+//        unit u is tau s (e^a - e^-a) v[8] (u_y, -u_x) / |dir|
+//   removal delta: v[9]
+__device__ __forceinline__ void site_grads(const SiteRec &R, float s, const float (&v)[NSUM], float (&acc)[SAD_NACC])
+{
+    const float ts = R.v[R_TAU] * s, E = R.v[R_E], iE = R.v[R_IE], ux = R.v[R_UX], uy = R.v[R_UY];
+    acc[PCR] = v[0];
+    acc[PCG] = v[1];
+    acc[PCB] = v[2];
+    acc[PR] = ts * v[3];
+    acc[PLT] = -ts * (E * v[6] + iE * v[7] - R.v[R_R] * v[3]);
+    acc[PX] = ts * (E * ux * v[4] - iE * uy * v[5]);
+    acc[PY] = ts * (E * uy * v[4] + iE * ux * v[5]);
+    acc[PA] = -0.5f * ts * (E * v[6] - iE * v[7]);
+    const float in = R.v[R_INVN];
+    const float cd = in > 0.0f ? ts * (E - iE) * v[8] * in : 0.0f;
+    acc[PDX] = uy * cd;
+    acc[PDY] = -ux * cd;
+    acc[10] = v[9];
 #pragma unroll
     for (int a = 0; a < SAD_NACC; ++a)
         acc[a] = finitef(acc[a]) ? acc[a] : 0.0f;
-}
-
-// One lane adds the 11 accumulators of one site (used for spilled entries only;
-// the regular path flushes cooperatively, see phase 6 below).
-__device__ __forceinline__ void flush_global(float *__restrict__ grad, uint32_t c, const float (&acc)[SAD_NACC])
-{
-#pragma unroll
-    for (int a = 0; a < SAD_NACC; ++a)
-        if (acc[a] != 0.0f)
-            unsafeAtomicAdd(&grad[(long)c * SAD_GRAD_LD + a], acc[a]);
 }
 
 // Gradients of one spilled entry per lane (id = NONE: none), flushed by the
 // whole wave together: the 11 sums of each lane are staged in LDS and
 // consecutive lanes take consecutive accumulators of one site, so an atomic
 // instruction touches a few 64-byte records instead of one per lane.
-__device__ __forceinline__ void spill_flush(const float4 *__restrict__ G, uint32_t id, float X, float Y,
-                                                      float s, float w, float gm, float dl, float g0, float g1,
-                                                      float g2, float *vals, float *__restrict__ grad, int lane)
+__device__ __forceinline__ void spill_flush(const float4 *__restrict__ G, uint32_t id, float X, float Y, float s,
+                                            float w, float gm, float dl, const float4 &g, float *vals,
+                                            float *__restrict__ grad, int lane)
 {
     uint32_t *vid = reinterpret_cast<uint32_t *>(vals + 64 * SAD_NACC);
     float acc[SAD_NACC];
 #pragma unroll
     for (int a = 0; a < SAD_NACC; ++a)
         acc[a] = 0.0f;
-    if (id != NONE)
-        entry_grads(load_rec_global(G, id), X, Y, s, w, gm, dl, g0, g1, g2, acc);
+    if (id != NONE) {
+        const SiteRec R = load_rec_global(G, id);
+        float v[NSUM];
+        entry_sums(R, X, Y, w, gm, dl, g, v);
+        site_grads(R, s, v, acc);
+    }
 #pragma unroll
     for (int a = 0; a < SAD_NACC; ++a)
         vals[lane * SAD_NACC + a] = acc[a];  // odd stride: no bank conflicts
@@ -1063,11 +1083,10 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
 #pragma unroll
         for (int k = 0; k < K; ++k)
             if (__any(spill[k]))
-                spill_flush(G, spill[k] ? ids[k] : NONE, X, Y, s, wk[k], gk[k], dk[k], g0, g1, g2, vals, grad, lane);
+                spill_flush(G, spill[k] ? ids[k] : NONE, X, Y, s, wk[k], gk[k], dk[k], make_float4(g0, g1, g2, 0.0f),
+                            vals, grad, lane);
     }
-    L.g[0][tid] = g0;
-    L.g[1][tid] = g1;
-    L.g[2][tid] = g2;
+    L.g[tid] = make_float4(g0, g1, g2, 0.0f);
     // per-pixel loss: wave sums
     {
         float v = err;
@@ -1139,9 +1158,9 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
     }
     __syncthreads();  // the staging area is reused for the partials and totals below
     if (nmine > 0) {
-        float run[SAD_NACC];
+        float run[NSUM];
 #pragma unroll
-        for (int a = 0; a < SAD_NACC; ++a)
+        for (int a = 0; a < NSUM; ++a)
             run[a] = 0.0f;
         int cur = (int)(mps[0] >> 8);
         SiteRec Rc = table_rec(L.T, cur);
@@ -1154,7 +1173,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
                     // close the run of `cur`: the chunk's first run becomes its head
                     // partial; a later run is a whole bucket: its total is final
 #pragma unroll
-                    for (int a = 0; a < SAD_NACC; ++a) {
+                    for (int a = 0; a < NSUM; ++a) {
                         if (first)
                             L.u.r.part[a][tid] = run[a];
                         else
@@ -1168,42 +1187,49 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
                 const int pp = (int)(mps[j] & 0xFFu);
                 const float Xp = (float)(col0 + (pp & (TILE - 1))) + 0.5f;
                 const float Yp = (float)(row0 + pp / TILE) + 0.5f;
-                float acc[SAD_NACC];
-                entry_grads(Rc, Xp, Yp, s, mw[j], mg[j], md[j], L.g[0][pp], L.g[1][pp], L.g[2][pp], acc);
+                float v[NSUM];
+                entry_sums(Rc, Xp, Yp, mw[j], mg[j], md[j], L.g[pp], v);
 #pragma unroll
-                for (int a = 0; a < SAD_NACC; ++a)
-                    run[a] += acc[a];
+                for (int a = 0; a < NSUM; ++a)
+                    run[a] += v[a];
             }
         }
         // the last run: head if it is also the first, else tail
 #pragma unroll
-        for (int a = 0; a < SAD_NACC; ++a)
-            L.u.r.part[(first ? 0 : SAD_NACC) + a][tid] = run[a];
+        for (int a = 0; a < NSUM; ++a)
+            L.u.r.part[(first ? 0 : NSUM) + a][tid] = run[a];
     }
     __syncthreads();
 
-    // phase 5: one thread per site adds up the chunk partials of its bucket
+    // phase 5: one thread per site adds up the chunk partials of its bucket and
+    // turns the sums into the site's 11 gradient contributions
     const uint32_t c = L.cnt[tid];
     if (c > 0) {
         const uint32_t b = L.off[tid], e = b + c - 1;
         const uint32_t t0 = b / CHUNK, t1 = e / CHUNK;
         const uint32_t end0 = min(t0 * CHUNK + CHUNK, total) - 1;
         const bool starts_chunk = (b == t0 * CHUNK);
-        if (t0 != t1 || starts_chunk || e == end0) {  // else: a middle run, already final
-            float acc[SAD_NACC];
-            const int h0 = starts_chunk ? 0 : SAD_NACC;
+        float v[NSUM];
+        if (t0 != t1 || starts_chunk || e == end0) {
+            const int h0 = starts_chunk ? 0 : NSUM;
 #pragma unroll
-            for (int a = 0; a < SAD_NACC; ++a)
-                acc[a] = L.u.r.part[h0 + a][t0];
+            for (int a = 0; a < NSUM; ++a)
+                v[a] = L.u.r.part[h0 + a][t0];
             for (uint32_t t = t0 + 1; t <= t1; ++t) {
 #pragma unroll
-                for (int a = 0; a < SAD_NACC; ++a)
-                    acc[a] += L.u.r.part[a][t];
+                for (int a = 0; a < NSUM; ++a)
+                    v[a] += L.u.r.part[a][t];
             }
+        } else {  // a middle run: its total is already in place
 #pragma unroll
-            for (int a = 0; a < SAD_NACC; ++a)
-                L.u.r.fin[a][tid] = acc[a];
+            for (int a = 0; a < NSUM; ++a)
+                v[a] = L.u.r.fin[a][tid];
         }
+        float acc[SAD_NACC];
+        site_grads(table_rec(L.T, tid), s, v, acc);
+#pragma unroll
+        for (int a = 0; a < SAD_NACC; ++a)
+            L.u.r.fin[a][tid] = acc[a];
     }
     __syncthreads();
 
