@@ -43,6 +43,16 @@ __device__ __forceinline__ int xcd_band(int bid, int nb)
 
 __device__ __forceinline__ bool finitef(float v) { return __builtin_isfinite(v); }
 
+// Hardware square root, reciprocal and reciprocal square root (1 ulp).  The
+// scores, blends and updates here tolerate one ulp, while the correctly rounded
+// sequences the compiler emits for sqrtf and '/' cost 10-18 instructions each
+// and sit in the innermost loops.  Denormal inputs are not relied on: the
+// arguments are squared distances (where 1e-38 px^2 is immaterial) or sums
+// bounded below (see the call sites).
+__device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float hw_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+
 // Ranking key (d ascending, then site ID ascending): a total order.
 __device__ __forceinline__ bool key_less(float da, uint32_t ia, float db, uint32_t ib)
 {
@@ -61,7 +71,7 @@ __device__ __forceinline__ Frame make_frame(float dx, float dy, float a)
     f.ux = 1.0f;
     f.uy = 0.0f;
     if (n2 >= 1e-30f) {
-        const float inv = rsqrtf(n2);
+        const float inv = hw_rsq(n2);  // n2 >= 1e-30
         f.ux = dx * inv;
         f.uy = dy * inv;
     }
@@ -77,7 +87,7 @@ __device__ __forceinline__ float score_frame(const Frame &f, float px, float py,
     const float ex = X - px, ey = Y - py;
     const float al = f.ux * ex + f.uy * ey;
     const float be = f.ux * ey - f.uy * ex;
-    const float q = sqrtf(f.E * al * al + f.iE * be * be);
+    const float q = hw_sqrt(f.E * al * al + f.iE * be * be);
     return s * q - s * r;
 }
 
@@ -118,7 +128,7 @@ __device__ __forceinline__ void make_record(const float *__restrict__ S, long st
     const float n2 = dx * dx + dy * dy;
     o[0] = make_float4(x, y, r, sE * f.ux);
     o[1] = make_float4(sE * f.uy, siE * f.ux, siE * f.uy, __expf(lt));
-    o[2] = make_float4(c0, c1, c2, n2 >= 1e-30f ? rsqrtf(n2) : 0.0f);
+    o[2] = make_float4(c0, c1, c2, n2 >= 1e-30f ? hw_rsq(n2) : 0.0f);
     o[3] = make_float4(f.ux, f.uy, f.E, f.iE);
 }
 
@@ -127,7 +137,7 @@ __device__ __forceinline__ float geom_score(const float4 &g0, const float4 &g1, 
     const float ex = X - g0.x, ey = Y - g0.y;
     const float t1 = g0.w * ex + g1.x * ey;  // e^{a/2} (u . delta)
     const float t2 = g1.y * ey - g1.z * ex;  // e^{-a/2} (u x delta)
-    const float q = sqrtf(t1 * t1 + t2 * t2);
+    const float q = hw_sqrt(t1 * t1 + t2 * t2);
     return s * q - s * g0.z;
 }
 
@@ -785,7 +795,7 @@ __device__ __forceinline__ void blend_pixel(const TileTable &T, const float4 *__
         a2 += e * B.c2[k];
     }
     B.Z = Z;
-    const float iZ = B.any ? 1.0f / Z : 0.0f;
+    const float iZ = B.any ? hw_rcp(Z) : 0.0f;  // Z >= 1: the largest term is exp(0)
     B.chat0 = a0 * iZ;
     B.chat1 = a1 * iZ;
     B.chat2 = a2 * iZ;
@@ -1026,7 +1036,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
         g1 = 2.0f * r1;
         g2 = 2.0f * r2;
         if (B.any) {
-            const float iZ = 1.0f / B.Z;
+            const float iZ = hw_rcp(B.Z);
             // exclusive sums of e and e*c over the other entries (removal delta)
             float xe[K], x0[K], x1[K], x2[K];
             float se = 0.0f, s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
@@ -1053,6 +1063,21 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
                 s1 += B.e[k] * B.c1[k];
                 s2 += B.e[k] * B.c2[k];
             }
+            // 1 / (sum of the other entries' e): xe >= 2^-100 but for near-exclusive
+            // entries, which take the exact quotient (rarely: a wave-uniform branch)
+            float iZo[K];
+            bool tiny = false;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                iZo[k] = xe[k] > 0.0f ? hw_rcp(xe[k]) : 0.0f;
+                tiny |= xe[k] > 0.0f && xe[k] < 0x1p-100f;
+            }
+            if (__any(tiny)) {
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    if (xe[k] > 0.0f && xe[k] < 0x1p-100f)
+                        iZo[k] = 1.0f / xe[k];
+            }
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float w = B.e[k] * iZ;
@@ -1062,8 +1087,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
                     continue;
                 wk[k] = w;
                 gk[k] = w * (g0 * (B.c0[k] - B.chat0) + g1 * (B.c1[k] - B.chat1) + g2 * (B.c2[k] - B.chat2));
-                const float iZo = xe[k] > 0.0f ? 1.0f / xe[k] : 0.0f;
-                const float m0 = x0[k] * iZo - t0, m1 = x1[k] * iZo - t1, m2 = x2[k] * iZo - t2;
+                const float m0 = x0[k] * iZo[k] - t0, m1 = x1[k] * iZo[k] - t1, m2 = x2[k] * iZo[k] - t2;
                 dk[k] = (m0 * m0 + m1 * m1 + m2 * m2) - err;
                 if (slot[k] >= 0) {
                     stage[k] = true;
@@ -1282,7 +1306,7 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restric
         const float r0 = B.chat0 - target[3 * p], r1 = B.chat1 - target[3 * p + 1], r2 = B.chat2 - target[3 * p + 2];
         err = r0 * r0 + r1 * r1 + r2 * r2;
         any = B.any;
-        iZ = any ? 1.0f / B.Z : 0.0f;
+        iZ = any ? hw_rcp(B.Z) : 0.0f;
     }
     float *vals = stage[tid >> 6];
     uint32_t *vid = reinterpret_cast<uint32_t *>(vals + 64 * NSTAT);
@@ -1332,7 +1356,7 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restric
 // pixel count (summary, B.4), gradient planes 0..9 zeroed in the same pass.
 struct AdamArgs {
     float lr[SAD_NPARAM];
-    float b1, b2, eps, bc1, bc2, inv_p, W, H;
+    float b1, b2, eps, ibc1, ibc2, inv_p, W, H;  // ibc = 1 / (1 - beta^step)
 };
 
 __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__restrict__ M, float *__restrict__ V,
@@ -1362,7 +1386,7 @@ __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__re
             const float v = A.b2 * V[o] + (1.0f - A.b2) * g * g;
             M[o] = m;
             V[o] = v;
-            S[o] = S[o] - A.lr[j] * (m / A.bc1) / (sqrtf(v / A.bc2) + A.eps);
+            S[o] = S[o] - A.lr[j] * (m * A.ibc1) * hw_rcp(hw_sqrt(v * A.ibc2) + A.eps);
         }
     }
     if (active) {
@@ -1597,8 +1621,8 @@ int sad_adam_step(float *sites, float *m, float *v, float *grad, float *rec, int
     A.b1 = cfg->beta1;
     A.b2 = cfg->beta2;
     A.eps = cfg->eps;
-    A.bc1 = (float)(1.0 - __builtin_pow((double)cfg->beta1, (double)step));
-    A.bc2 = (float)(1.0 - __builtin_pow((double)cfg->beta2, (double)step));
+    A.ibc1 = (float)(1.0 / (1.0 - __builtin_pow((double)cfg->beta1, (double)step)));
+    A.ibc2 = (float)(1.0 / (1.0 - __builtin_pow((double)cfg->beta2, (double)step)));
     A.inv_p = 1.0f / (float)n_pixels;
     A.W = (float)W;
     A.H = (float)H;
