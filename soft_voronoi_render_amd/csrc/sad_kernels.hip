@@ -82,13 +82,15 @@ __device__ __forceinline__ Frame make_frame(float dx, float dy, float a)
 
 // d = s*||x - p||_G - s*r with ||delta||_G^2 = e^a (u.delta)^2 + e^-a (v.delta)^2,
 // v = (-u_y, u_x)  (reading note, key design 1).
+// (Multiply-adds are written as fmaf so that no contraction is left to the
+// compiler: the forward rounds the same way in every kernel that inlines it.)
 __device__ __forceinline__ float score_frame(const Frame &f, float px, float py, float r, float X, float Y, float s)
 {
     const float ex = X - px, ey = Y - py;
-    const float al = f.ux * ex + f.uy * ey;
-    const float be = f.ux * ey - f.uy * ex;
-    const float q = hw_sqrt(f.E * al * al + f.iE * be * be);
-    return s * q - s * r;
+    const float al = fmaf(f.ux, ex, f.uy * ey);
+    const float be = fmaf(f.ux, ey, -(f.uy * ex));
+    const float q = hw_sqrt(fmaf(f.E * al, al, f.iE * be * be));
+    return fmaf(s, q, -(s * r));
 }
 
 // Score of slot `id` read straight from the SoA planes (6 gathers).
@@ -425,12 +427,12 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
     static_assert(TB == BLOCK, "one slot per lane");
     {
         const uint32_t c = L.t.key[tid];
-        float4 g0, g1;
+        float4 g0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), g1 = g0;
         if (c != NONE) {
             g0 = G[RLD4 * (size_t)c];
             g1 = G[RLD4 * (size_t)c + 1];
-            g1.w = __uint_as_float(c);
         }
+        g1.w = __uint_as_float(c);
         __syncthreads();
         if (c != NONE) {
             L.t.rec[tid][0] = g0;
@@ -692,7 +694,7 @@ __device__ __forceinline__ SiteRec load_rec_global(const float4 *__restrict__ G,
 // three 16-byte LDS reads rather than one read per field.
 struct TileTable {
     uint32_t key[TBL];
-    float4 rec[TBL][NREC / 4];
+    float4 rec[TBL + 1][NREC / 4];  // slot TBL: the null record (px = NaN) for empty entries
 };
 
 // Phases 1-2 shared by forward and backward: insert the pixel's IDs, then one
@@ -718,6 +720,8 @@ __device__ __forceinline__ void build_tile_table(TileTable &T, const float4 *__r
         for (int j = 0; j < NREC / 4; ++j)
             T.rec[threadIdx.x][j] = make_float4(R.v[4 * j], R.v[4 * j + 1], R.v[4 * j + 2], R.v[4 * j + 3]);
     }
+    if (threadIdx.x < NREC / 4)
+        T.rec[TBL][threadIdx.x] = make_float4(threadIdx.x == 0 ? __builtin_nanf("") : 0.0f, 0.0f, 0.0f, 0.0f);
     __syncthreads();
 }
 
@@ -771,18 +775,32 @@ __device__ __forceinline__ void blend_pixel(const TileTable &T, const float4 *__
                                             const uint32_t (&ids)[K], const int (&slot)[K], float X, float Y,
                                             float s, PixelBlend &B)
 {
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const SiteRec R = fetch_rec(T, G, ids[k], slot[k]);
+    // every entry reads the table (empty and spilled ones the null record), then
+    // spilled entries, if the wave has any, are redone from their global records
+    auto entry = [&](int k, const SiteRec &R) {
         const float l = -R.v[R_TAU] * rec_score(R, X, Y, s);
         B.use[k] = finitef(l);
         B.l[k] = l;
         B.c0[k] = B.use[k] ? R.v[R_C0] : 0.0f;
         B.c1[k] = B.use[k] ? R.v[R_C1] : 0.0f;
         B.c2[k] = B.use[k] ? R.v[R_C2] : 0.0f;
-        mx = B.use[k] ? fmaxf(mx, l) : mx;
+    };
+    bool spilled = false;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        entry(k, table_rec(T, slot[k] >= 0 ? slot[k] : TBL));
+        spilled |= slot[k] == -1;
     }
+    if (__any(spilled)) {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (slot[k] == -1)
+                entry(k, load_rec_global(G, ids[k]));
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        mx = B.use[k] ? fmaxf(mx, B.l[k]) : mx;
     B.any = mx > -__builtin_inff();
     float Z = 0.0f, a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
 #pragma unroll
@@ -790,9 +808,9 @@ __device__ __forceinline__ void blend_pixel(const TileTable &T, const float4 *__
         const float e = B.use[k] ? __expf(B.l[k] - mx) : 0.0f;
         B.e[k] = e;
         Z += e;
-        a0 += e * B.c0[k];
-        a1 += e * B.c1[k];
-        a2 += e * B.c2[k];
+        a0 = fmaf(e, B.c0[k], a0);
+        a1 = fmaf(e, B.c1[k], a1);
+        a2 = fmaf(e, B.c2[k], a2);
     }
     B.Z = Z;
     const float iZ = B.any ? hw_rcp(Z) : 0.0f;  // Z >= 1: the largest term is exp(0)
