@@ -881,12 +881,12 @@ __global__ __launch_bounds__(BLOCK) void k_render_fwd(const float4 *__restrict__
 constexpr int CHUNK = 8;
 constexpr int NSUM = 10;  // per-entry sums of the reduction (entry_sums)
 
-// Staged entries live field-major with the 8 entries of one chunk interleaved:
-// sorted entry e sits at column e / CHUNK of row e % CHUNK, so when every thread
-// reads the j-th entry of its chunk the 64 lanes touch 64 consecutive words
-// (no bank conflicts).  The chunk partials alias the same storage column by
-// column: thread t only ever overwrites its own column.
-__device__ __forceinline__ int stage_pos(uint32_t e) { return (int)((e % CHUNK) * BLOCK + e / CHUNK); }
+// Staged entries live field-major, sorted entry e at word e ^ ((e >> 6) & 7).
+// Lanes that write one bucket write consecutive entries, and the swizzle keeps
+// those in distinct banks; when every thread reads the j-th entry of its chunk
+// (entries 8t + j, t = 0..63) the XOR with t / 8 spreads the 64 lanes over 64
+// banks as well.
+__device__ __forceinline__ int stage_pos(uint32_t e) { return (int)(e ^ ((e >> 6) & 7u)); }
 
 struct BwdShared {
     TileTable T;
@@ -1190,7 +1190,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
 #pragma unroll
         for (int j = 0; j < CHUNK; ++j) {
             if (j < nmine) {
-                const int q = j * BLOCK + tid;  // stage_pos(b0 + j)
+                const int q = stage_pos(b0 + j);
                 mps[j] = L.u.e.ps[q];
                 mw[j] = L.u.e.w[q];
                 mg[j] = L.u.e.gamma[q];
