@@ -700,19 +700,22 @@ struct TileTable {
 // Phases 1-2 shared by forward and backward: insert the pixel's IDs, then one
 // thread per occupied slot fills its record.  slot[k]: table slot, -1 = spill,
 // -2 = no site (sentinel or ID >= n_slots).  Ends with a barrier.
-__device__ __forceinline__ void build_tile_table(TileTable &T, const float4 *__restrict__ G, uint32_t n_slots,
-                                                 const uint32_t (&ids)[K], int (&slot)[K])
+__device__ __forceinline__ void table_insert_phase(TileTable &T, uint32_t n_slots, const uint32_t (&ids)[K],
+                                                   int (&slot)[K])
 {
     T.key[threadIdx.x] = NONE;
     __syncthreads();
-    {
-        uint32_t refs[K];
-        table_insert_ids<TBL>(T.key, ids, n_slots, refs);
+    uint32_t refs[K];
+    table_insert_ids<TBL>(T.key, ids, n_slots, refs);
 #pragma unroll
-        for (int k = 0; k < K; ++k)
-            slot[k] = refs[k] == REF_NONE ? -2 : (refs[k] & REF_SPILL) ? -1 : (int)refs[k];
-    }
-    __syncthreads();
+    for (int k = 0; k < K; ++k)
+        slot[k] = refs[k] == REF_NONE ? -2 : (refs[k] & REF_SPILL) ? -1 : (int)refs[k];
+}
+
+// One thread per slot: the slot's record (after a barrier that completes the
+// inserts), and the null record.  Ends with a barrier.
+__device__ __forceinline__ void table_load_phase(TileTable &T, const float4 *__restrict__ G)
+{
     const uint32_t c = T.key[threadIdx.x];
     if (c != NONE) {
         const SiteRec R = load_rec_global(G, c);
@@ -723,6 +726,14 @@ __device__ __forceinline__ void build_tile_table(TileTable &T, const float4 *__r
     if (threadIdx.x < NREC / 4)
         T.rec[TBL][threadIdx.x] = make_float4(threadIdx.x == 0 ? __builtin_nanf("") : 0.0f, 0.0f, 0.0f, 0.0f);
     __syncthreads();
+}
+
+__device__ __forceinline__ void build_tile_table(TileTable &T, const float4 *__restrict__ G, uint32_t n_slots,
+                                                 const uint32_t (&ids)[K], int (&slot)[K])
+{
+    table_insert_phase(T, n_slots, ids, slot);
+    __syncthreads();
+    table_load_phase(T, G);
 }
 
 __device__ __forceinline__ SiteRec table_rec(const TileTable &T, int sl)
@@ -906,7 +917,9 @@ struct BwdShared {
         } r;
     } u;
     float wsum[BLOCK / 64];
+    uint32_t wtot[BLOCK / 64];
     uint32_t total;
+    uint32_t nspill;
 };
 
 // The backward of one site over a set of entries is linear in ten per-entry
@@ -1028,17 +1041,56 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
     int slot[K];
     load_ids(cand, p, inside, ids);
     L.cnt[tid] = 0;
-    build_tile_table(L.T, G, n_slots, ids, slot);
+    if (tid == 0)
+        L.nspill = 0;
+    table_insert_phase(L.T, n_slots, ids, slot);
+    // every entry with a table slot gets its place in the slot-sorted staging now
+    // (a counting sort whose counts are complete at the next barrier), so the
+    // blend below can write its entries without another block-wide step
+    uint32_t pos[K];
+    uint32_t nsp = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        pos[k] = slot[k] >= 0 ? atomicAdd(&L.cnt[slot[k]], 1u) : 0u;
+        nsp += slot[k] == -1;
+    }
+    if (__any(nsp > 0) && (tid & 63) == 0)
+        atomicAdd(&L.nspill, 1u);
+    __syncthreads();
+    // bucket offsets: wave scans of the slot counts, then the waves' totals
+    const uint32_t cnt_me = L.cnt[tid];
+    uint32_t incl = cnt_me;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, 64);
+        if ((tid & 63) >= o)
+            incl += v;
+    }
+    if ((tid & 63) == 63)
+        L.wtot[tid >> 6] = incl;
+    table_load_phase(L.T, G);
+    {
+        uint32_t base = 0;
+        for (int w = 0; w < (tid >> 6); ++w)
+            base += L.wtot[w];
+        L.off[tid] = base + incl - cnt_me;
+        if (tid == 0)
+            L.total = L.wtot[0] + L.wtot[1] + L.wtot[2] + L.wtot[3];
+    }
+    const bool tile_spills = L.nspill > 0;  // the same for the whole block
+    __syncthreads();
 
-    // phase 3: blend, per-entry softmax quantities, spill entries straight to global
+    // phase 3: blend, per-entry softmax quantities; staged entries written in
+    // slot order, spilled entries flushed to global memory
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
     float err = 0.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     float wk[K], gk[K], dk[K];
-    uint32_t pos[K];
-    bool stage[K], spill[K];
+    bool spill[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-        stage[k] = spill[k] = false;
+    for (int k = 0; k < K; ++k) {
+        wk[k] = gk[k] = dk[k] = 0.0f;
+        spill[k] = false;
+    }
     if (inside) {
         PixelBlend B;
         blend_pixel(L.T, G, ids, slot, X, Y, s, B);
@@ -1100,26 +1152,36 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
             for (int k = 0; k < K; ++k) {
                 const float w = B.e[k] * iZ;
                 // a zero-weight entry changes nothing: all its gradients vanish and
-                // removing it leaves the blend as it is
+                // removing it leaves the blend as it is (it stays staged, as zeros)
                 if (!B.use[k] || w == 0.0f)
                     continue;
                 wk[k] = w;
                 gk[k] = w * (g0 * (B.c0[k] - B.chat0) + g1 * (B.c1[k] - B.chat1) + g2 * (B.c2[k] - B.chat2));
                 const float m0 = x0[k] * iZo[k] - t0, m1 = x1[k] * iZo[k] - t1, m2 = x2[k] * iZo[k] - t2;
                 dk[k] = (m0 * m0 + m1 * m1 + m2 * m2) - err;
-                if (slot[k] >= 0) {
-                    stage[k] = true;
-                    pos[k] = atomicAdd(&L.cnt[slot[k]], 1u);
-                } else {
-                    spill[k] = true;
-                }
+                spill[k] = slot[k] == -1;
             }
         }
     }
-    // Spilled entries (IDs the tile table could not hold), k by k where any lane
-    // of the wave has one (see spill_flush; the staging area is idle until the
-    // counting sort below).
-    {
+    auto stage_entries = [&]() {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (slot[k] >= 0) {
+                const int q = stage_pos(L.off[slot[k]] + pos[k]);
+                L.u.e.ps[q] = (uint32_t)tid | ((uint32_t)slot[k] << 8);
+                L.u.e.w[q] = wk[k];
+                L.u.e.gamma[q] = gk[k];
+                L.u.e.rdelta[q] = dk[k];
+            }
+        }
+    };
+    if (!tile_spills) {
+        stage_entries();
+    } else {
+        // Spilled entries (IDs the tile table could not hold), k by k where any
+        // lane of the wave has one (see spill_flush).  Their LDS staging shares the
+        // sort's storage, so the tile stages its entries only after all waves are
+        // done with it.
         const int lane = tid & 63;
         float *vals = &L.u.r.part[0][0] + (tid >> 6) * (64 * SAD_NACC + 64);
 #pragma unroll
@@ -1127,6 +1189,8 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
             if (__any(spill[k]))
                 spill_flush(G, spill[k] ? ids[k] : NONE, X, Y, s, wk[k], gk[k], dk[k], make_float4(g0, g1, g2, 0.0f),
                             vals, grad, lane);
+        __syncthreads();
+        stage_entries();
     }
     L.g[tid] = make_float4(g0, g1, g2, 0.0f);
     // per-pixel loss: wave sums
@@ -1139,45 +1203,8 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
             L.wsum[tid >> 6] = v;
     }
     __syncthreads();
-
-    // exclusive scan of the slot counts -> bucket offsets
-    {
-        const uint32_t c = L.cnt[tid];
-        uint32_t incl = c;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t v = __shfl_up(incl, o, 64);
-            if ((tid & 63) >= o)
-                incl += v;
-        }
-        if ((tid & 63) == 63)
-            L.off[tid] = incl;  // wave total, parked at the wave's last lane
-        __syncthreads();
-        uint32_t base = 0;
-        for (int w = 0; w < (tid >> 6); ++w)
-            base += L.off[w * 64 + 63];
-        const uint32_t tot = L.off[3 * 64 + 63] + L.off[2 * 64 + 63] + L.off[64 + 63] + L.off[63];
-        __syncthreads();
-        L.off[tid] = base + incl - c;
-        if (tid == 0) {
-            L.total = tot;
-            if (loss_sum)
-                unsafeAtomicAdd(loss_sum, L.wsum[0] + L.wsum[1] + L.wsum[2] + L.wsum[3]);
-        }
-        __syncthreads();
-    }
-    // stage the entries in slot order
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        if (stage[k]) {
-            const int q = stage_pos(L.off[slot[k]] + pos[k]);
-            L.u.e.ps[q] = (uint32_t)tid | ((uint32_t)slot[k] << 8);
-            L.u.e.w[q] = wk[k];
-            L.u.e.gamma[q] = gk[k];
-            L.u.e.rdelta[q] = dk[k];
-        }
-    }
-    __syncthreads();
+    if (tid == 0 && loss_sum)
+        unsafeAtomicAdd(loss_sum, L.wsum[0] + L.wsum[1] + L.wsum[2] + L.wsum[3]);
 
     // phase 4: chunk of 8 sorted entries per thread, runs summed in registers
     const uint32_t total = L.total;
