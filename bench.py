@@ -202,7 +202,7 @@ def main():
     fit.loss.zero_()
     fit.step()
     torch.cuda.synchronize()
-    mse = fit.loss.item() / (3 * P)
+    mse = fit.loss.sum().item() / (3 * P)
     psnr = 10 * np.log10(1.0 / max(mse, 1e-30))
     # recall of the maintained map against the exact top-K (brute force on the GPU)
     ex = sad.new_map(W, H, dev)

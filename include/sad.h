@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 1
+#define SAD_ABI_VERSION 2
 #define SAD_K 8
 #define SAD_INVALID 0xffffffffu
 #define SAD_NPARAM 10
@@ -85,6 +85,7 @@ extern "C" {
 #define SAD_STAT_LD 8
 #define SAD_MAX_INJECT 16
 #define SAD_MAX_DIM 65535
+#define SAD_LOSS_SLOTS 64 /* partial sums of the loss output of sad_render_bwd */
 
 enum sad_status {
     SAD_OK = 0,
@@ -188,13 +189,15 @@ int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, i
  * blend of the other entries renormalised (0 if none carries weight)
  * ([SUM] B.4-B.5).  Non-finite contributions are dropped.  Contributions are
  * summed per 16x16 tile in an LDS hash table keyed by site ID (256 slots,
- * multiplicative hash, at most 8 linear probes, CAS insert) and flushed with one
+ * multiplicative double hashing, at most 12 probes, CAS insert) and flushed with one
  * atomic per site and accumulator per tile; an entry that finds no slot goes
  * straight to global atomics ([SUM] section 5, B.4).  Float atomics make the
  * summation order, hence the last bits, vary from run to run.
  *   rec device [n_slots][16] read-only; target device [H][W][3] read-only;
  *   grad device [>= n_slots][16] float, +=;
- *   loss_sum device float or NULL, += sum_x ||c - t||^2;
+ *   loss_sum device float[SAD_LOSS_SLOTS] or NULL: each tile adds its sum of
+ *   ||c - t||^2 to one of the SAD_LOSS_SLOTS entries (spread by tile, because
+ *   a thousand atomics on one address serialise); the loss is the entries' sum;
  *   out_rgb device [H][W][3] float or NULL: if given, the blend c(x) of every
  *   pixel is written there too -- the same values sad_render_fwd writes -- so a
  *   training step needs one pass over the map for forward and backward.

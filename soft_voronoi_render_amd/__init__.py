@@ -34,6 +34,7 @@ NACC = 11
 GRAD_LD = 16
 REC_LD = 16
 STAT_LD = 8
+LOSS_SLOTS = 64
 MAX_INJECT = 16
 
 SAD_OK, SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE, SAD_ERR_CAPACITY, SAD_ERR_UNIMPLEMENTED = 0, -1, -2, -3, -4, -5
@@ -204,6 +205,12 @@ def render_fwd(rec, n_slots, cand, W, H, out_rgb, stream=None):
     _check("sad_render_fwd", lib().sad_render_fwd(r, n_slots, c, W, H, o, _stream(stream)))
 
 
+def new_loss(device) -> torch.Tensor:
+    """Zeroed loss accumulator for render_bwd: LOSS_SLOTS partial sums whose sum
+    is the loss."""
+    return torch.zeros(LOSS_SLOTS, dtype=torch.float32, device=device)
+
+
 def render_bwd(rec, n_slots, cand, target, W, H, grad, loss_sum=None, out_rgb=None, stream=None):
     """Gradients of the squared error, accumulated into grad; optionally also the
     rendered image (see sad_render_bwd)."""
@@ -213,6 +220,8 @@ def render_bwd(rec, n_slots, cand, target, W, H, grad, loss_sum=None, out_rgb=No
     if grad.dim() != 2 or grad.shape[1] != GRAD_LD or grad.shape[0] < n_slots:
         raise ValueError("grad must be float32 [>= n_slots][16]")
     g = _dev(grad, "grad", _F32)
+    if loss_sum is not None and loss_sum.numel() != LOSS_SLOTS:
+        raise ValueError(f"loss_sum must hold {LOSS_SLOTS} partial sums (see new_loss)")
     ls = _dev(loss_sum, "loss_sum", _F32) if loss_sum is not None else None
     o = _dev(out_rgb, "out_rgb", _F32, (H, W, 3)) if out_rgb is not None else None
     _check("sad_render_bwd", lib().sad_render_bwd(r, n_slots, c, t, W, H, g, ls, o, _stream(stream)))
@@ -348,7 +357,7 @@ class Fitter:
         self.maps = [cand if cand is not None else new_map(W, H, dev), new_map(W, H, dev)]
         self.cur = 0
         self.rgb = torch.empty((H, W, 3), dtype=torch.float32, device=dev)
-        self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.loss = new_loss(dev)
         self.adam = (adam or AdamConfig()).to_c()
         self.it = 0
         self.sched_cache: dict = {}

@@ -890,6 +890,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_fwd(const float4 *__restrict__
 // accumulator.  Runs that lie strictly inside a chunk are flushed by the chunk
 // thread.  Either way a site gets one global atomic per accumulator per tile.
 constexpr int CHUNK = 8;
+static_assert((SAD_LOSS_SLOTS & (SAD_LOSS_SLOTS - 1)) == 0, "loss slots: a power of two");
 constexpr int NSUM = 10;  // per-entry sums of the reduction (entry_sums)
 
 // Staged entries live field-major, sorted entry e at word e ^ ((e >> 6) & 7).
@@ -1204,7 +1205,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
     }
     __syncthreads();
     if (tid == 0 && loss_sum)
-        unsafeAtomicAdd(loss_sum, L.wsum[0] + L.wsum[1] + L.wsum[2] + L.wsum[3]);
+        unsafeAtomicAdd(loss_sum + (blockIdx.x & (SAD_LOSS_SLOTS - 1)), L.wsum[0] + L.wsum[1] + L.wsum[2] + L.wsum[3]);
 
     // phase 4: chunk of 8 sorted entries per thread, runs summed in registers
     const uint32_t total = L.total;

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.sad_abi_version() == 1
+    assert L.sad_abi_version() == 2
     assert L.sad_status_string(0) == b"ok"
     assert L.sad_status_string(ERR_ALIGN) == b"misaligned pointer"
     assert L.sad_status_string(12345) == b"unknown status"

@@ -81,7 +81,7 @@ def test_fit_with_budget_control(orc):
     for it in range(121):
         f.loss.zero_()
         f.step()
-        losses.append(f.loss.item())
+        losses.append(f.loss.sum().item())
         if it in (40, 80):
             before = f.n_slots
             active_before = int((f.sites[0, :before] >= 0).sum())

@@ -75,13 +75,13 @@ def test_fused_forward_backward_full_size(orc, name):
     c_d = to_dev(cand)
     t_d = to_dev(tgt)
     g_d = sad.new_grad(S.shape[1], S_d.device)
-    loss = torch.zeros(1, dtype=torch.float32, device=S_d.device)
+    loss = sad.new_loss(S_d.device)
     rgb = torch.empty((H, W, 3), dtype=torch.float32, device=S_d.device)
     sad.render_bwd(rec, n, c_d, t_d, W, H, g_d, loss, rgb)
     torch.cuda.synchronize()
     got_rgb = rgb.cpu().numpy().reshape(-1, 3)
     got_g = sad.grad_planes(g_d).cpu().numpy().astype(np.float64)
-    got_loss = loss.item()
+    got_loss = loss.sum().item()
     del c_d, t_d, rgb, g_d
     pix = _sample(W, H)
     ref_rgb = orc.render_fwd_pixels(S, n, cand, W, H, pix)

@@ -183,7 +183,7 @@ def _bwd(S, n, cand, tgt, W, H, grad0=None):
     g = sad.new_grad(S.shape[1], R_d.device)
     if grad0 is not None:
         g[:, :11].copy_(torch.from_numpy(grad0).t())
-    loss = torch.zeros(1, dtype=torch.float32, device=R_d.device)
+    loss = sad.new_loss(R_d.device)
     rgb = torch.full((H, W, 3), -7.0, dtype=torch.float32, device=R_d.device)
     sad.render_bwd(R_d, n, c, t, W, H, g, loss, out_rgb=rgb)
     torch.cuda.synchronize()
@@ -191,7 +191,7 @@ def _bwd(S, n, cand, tgt, W, H, grad0=None):
     assert (gh[:, 11:] == 0).all(), "unused words of the gradient records were written"
     # the fused forward output equals the standalone forward bit for bit
     assert np.array_equal(rgb.cpu().numpy(), _fwd(S, n, cand, W, H))
-    return np.ascontiguousarray(gh[:, :11].T), float(loss.item())
+    return np.ascontiguousarray(gh[:, :11].T), float(loss.sum().item())
 
 
 def _check_grads(got, ref, planes=range(11)):
@@ -314,6 +314,6 @@ def test_fitter_iterations_reduce_loss(orc):
     for _ in range(60):
         f.loss.zero_()
         f.step()
-        losses.append(f.loss.item())
+        losses.append(f.loss.sum().item())
     assert losses[-1] < 0.7 * losses[0]
     assert np.isfinite(losses).all()
