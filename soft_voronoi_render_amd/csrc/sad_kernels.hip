@@ -498,6 +498,11 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
     const int r_b = row + jump < H ? (lr + jump < TILE ? (lr + jump) * TILE + lc
                                                        : BLOCK + 3 * strip_len + (lr + jump - far) * TILE + lc)
                                    : -1;
+    // Entries new to this pixel, as one mask over the four lists (bit 8 li + k),
+    // then scored in a single loop: the wave runs as many iterations as its
+    // busiest lane has new entries in total, and each reads its ref from LDS.
+    uint32_t fresh = 0;
+#pragma unroll
     for (int li = 0; li < 4; ++li) {
         const int r = li == 0 ? r_l : li == 1 ? r_r : li == 2 ? r_t : r_b;
         if (r < 0)
@@ -505,30 +510,28 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
         const uint4 *src = reinterpret_cast<const uint4 *>(&L.ref[r * K]);
         const uint4 a = src[0], b = src[1];
         const uint32_t refs[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t fresh = 0;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const uint32_t ref = refs[k];
             const bool f = ref < (uint32_t)TB ? take(ref) : ref != REF_NONE;
-            fresh |= f ? (1u << k) : 0u;
+            fresh |= f ? (1u << (li * K + k)) : 0u;
         }
-        while (fresh) {
-            const int j = __builtin_ctz(fresh);
-            fresh &= fresh - 1u;
-            uint32_t ref = refs[0];
-#pragma unroll
-            for (int k = 1; k < K; ++k)
-                ref = j == k ? refs[k] : ref;
-            bool usable;
-            if (ref < (uint32_t)TB) {
-                uint32_t id;
-                const float d = rec_score_slot(ref, usable, id);
-                best.consider_new(id, d, usable);
-            } else {
-                const uint32_t c = ref & ~REF_SPILL;
-                const float d = geom_score_id(G, c, X, Y, s, usable);
-                best.consider(c, d, usable);
-            }
+    }
+    while (fresh) {
+        const int j = __builtin_ctz(fresh);
+        fresh &= fresh - 1u;
+        const int li = j / K;
+        const int r = li == 0 ? r_l : li == 1 ? r_r : li == 2 ? r_t : r_b;
+        const uint32_t ref = L.ref[r * K + (j % K)];
+        bool usable;
+        if (ref < (uint32_t)TB) {
+            uint32_t id;
+            const float d = rec_score_slot(ref, usable, id);
+            best.consider_new(id, d, usable);
+        } else {
+            const uint32_t c = ref & ~REF_SPILL;
+            const float d = geom_score_id(G, c, X, Y, s, usable);
+            best.consider(c, d, usable);
         }
     }
     // injected IDs (summary, B.3)
