@@ -348,11 +348,15 @@ struct PropShared {
     // The hash keys are needed until the records are loaded; from then on a
     // slot's ID travels in the last float of its record (the scoring record's
     // tau, which scoring does not use).
+    // Records and lists are split into 16-byte halves kept in separate arrays, so
+    // lanes reading consecutive lists (or slots) read consecutive 16-byte words.
     union {
         uint32_t key[TB];
-        float4 rec[TB][2];                      // the 32-byte scoring record per slot
+        float4 rec0[TB];                        // scoring record, bytes 0..15
     } t;
-    uint32_t ref[(BLOCK + 4 * TILE * KK) * K];  // per region list: 8 slots / spilled IDs
+    float4 rec1[TB];                            // scoring record, bytes 16..31
+    uint4 ref0[BLOCK + 4 * TILE * KK];          // per region list: entries 0..3 (slots / spilled IDs)
+    uint4 ref1[BLOCK + 4 * TILE * KK];          // entries 4..7
     uint32_t seen[TB / 32][BLOCK];              // per pixel: slots already taken (word-major)
 };
 
@@ -417,9 +421,8 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
         const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         uint32_t refs[K];
         table_insert_ids<TB>(L.t.key, ids, n_slots, refs);
-        uint4 *dst = reinterpret_cast<uint4 *>(&L.ref[r * K]);
-        dst[0] = make_uint4(refs[0], refs[1], refs[2], refs[3]);
-        dst[1] = make_uint4(refs[4], refs[5], refs[6], refs[7]);
+        L.ref0[r] = make_uint4(refs[0], refs[1], refs[2], refs[3]);
+        L.ref1[r] = make_uint4(refs[4], refs[5], refs[6], refs[7]);
     }
     __syncthreads();
 
@@ -435,8 +438,8 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
         g1.w = __uint_as_float(c);
         __syncthreads();
         if (c != NONE) {
-            L.t.rec[tid][0] = g0;
-            L.t.rec[tid][1] = g1;
+            L.t.rec0[tid] = g0;
+            L.rec1[tid] = g1;
         }
     }
     __syncthreads();
@@ -445,7 +448,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
         return;
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
     auto rec_score_slot = [&](uint32_t sl, bool &usable, uint32_t &id) {
-        const float4 g0 = L.t.rec[sl][0], g1 = L.t.rec[sl][1];
+        const float4 g0 = L.t.rec0[sl], g1 = L.rec1[sl];
         usable = !(g0.x < 0.0f);
         id = __float_as_uint(g1.w);
         return geom_score(g0, g1, X, Y, s);
@@ -458,8 +461,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
 
     TopK64 best;
     // own list: score its (deduplicated) table entries and sort them with a network
-    const uint4 *own = reinterpret_cast<const uint4 *>(&L.ref[tid * K]);
-    const uint4 oa = own[0], ob = own[1];
+    const uint4 oa = L.ref0[tid], ob = L.ref1[tid];
     const uint32_t orefs[K] = {oa.x, oa.y, oa.z, oa.w, ob.x, ob.y, ob.z, ob.w};
     {
         uint64_t v[K];
@@ -507,8 +509,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
         const int r = li == 0 ? r_l : li == 1 ? r_r : li == 2 ? r_t : r_b;
         if (r < 0)
             continue;
-        const uint4 *src = reinterpret_cast<const uint4 *>(&L.ref[r * K]);
-        const uint4 a = src[0], b = src[1];
+        const uint4 a = L.ref0[r], b = L.ref1[r];
         const uint32_t refs[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -522,7 +523,8 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
         fresh &= fresh - 1u;
         const int li = j / K;
         const int r = li == 0 ? r_l : li == 1 ? r_r : li == 2 ? r_t : r_b;
-        const uint32_t ref = L.ref[r * K + (j % K)];
+        const int e = j % K;
+        const uint32_t ref = reinterpret_cast<const uint32_t *>(e < 4 ? L.ref0 : L.ref1)[4 * r + (e & 3)];
         bool usable;
         if (ref < (uint32_t)TB) {
             uint32_t id;
