@@ -1046,6 +1046,13 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
     uint32_t ids[K];
     int slot[K];
     load_ids(cand, p, inside, ids);
+    // the target is read now, so its latency overlaps the table build
+    float t0 = 0.0f, t1 = 0.0f, t2 = 0.0f;
+    if (inside) {
+        t0 = target[3 * p];
+        t1 = target[3 * p + 1];
+        t2 = target[3 * p + 2];
+    }
     L.cnt[tid] = 0;
     if (tid == 0)
         L.nspill = 0;
@@ -1105,7 +1112,6 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
             out_rgb[3 * p + 1] = B.chat1;
             out_rgb[3 * p + 2] = B.chat2;
         }
-        const float t0 = target[3 * p], t1 = target[3 * p + 1], t2 = target[3 * p + 2];
         const float r0 = B.chat0 - t0, r1 = B.chat1 - t1, r2 = B.chat2 - t2;
         err = r0 * r0 + r1 * r1 + r2 * r2;
         g0 = 2.0f * r0;
