@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "soft_voronoi_render_amd", "csrc", "sad_kernels.hip")
 # kernel symbol of each timed launch (as rocprofv3 names it)
-KERNEL_SYMBOL = {"propagate": "k_propagate", "fwd_bwd": "k_render_bwd", "adam": "k_adam", "fwd": "k_render_fwd"}
+KERNEL_SYMBOL = {"propagate": "k_propagate<1,256>", "fwd_bwd": "k_render_bwd", "adam": "k_adam", "fwd": "k_render_fwd"}
 
 
 def source_digest():
