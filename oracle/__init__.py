@@ -73,6 +73,10 @@ def lib():
             "orc_adam_step": (None, [f64p, f64p, f64p, f64p, c_int, c_int, c_int, c_int, f64p, c_dbl, c_dbl,
                                      c_dbl, c_int, c_int]),
             "orc_densify_stats": (None, [f64p, c_int, c_int, u32p, f32p, c_int, c_int, f64p]),
+            "orc_jfa_seed": (None, [f32p, c_int, c_int, c_int, c_int, u32p]),
+            "orc_jfa_pass": (None, [f32p, c_int, c_int, u32p, u32p, c_int, c_int, c_int]),
+            "orc_jfa_pass_pixels": (None, [f32p, c_int, c_int, u32p, c_int, c_int, c_int, u32p, c_long, u32p]),
+            "orc_jfa_union_pixels": (None, [f32p, c_int, u32p, c_int, c_int, c_int, u32p, c_long, u32p, i32p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -267,6 +271,58 @@ def densify_stats(sites, n_slots, cand, target, W, H, stats=None):
     lib().orc_densify_stats(_p(S, ctypes.c_double), n_slots, S.shape[1], _p(cand, ctypes.c_uint32),
                             _p(T, ctypes.c_float), W, H, _p(stats, ctypes.c_double))
     return stats
+
+
+# ------------------------------------------------------------ JFA prepass
+def jfa_seed(sites, n_slots, W, H) -> np.ndarray:
+    """Seed pass: each active site into the list of its pixel, <= 4 per pixel."""
+    S = _f32(sites)
+    out = np.empty((H, W, K), dtype=np.uint32)
+    lib().orc_jfa_seed(_p(S, ctypes.c_float), n_slots, S.shape[1], W, H, _p(out, ctypes.c_uint32))
+    return out
+
+
+def jfa_pass(sites, n_slots, cin, W, H, step) -> np.ndarray:
+    S = _f32(sites)
+    cin = _u32(cin)
+    assert cin.shape == (H, W, K)
+    out = np.empty_like(cin)
+    lib().orc_jfa_pass(_p(S, ctypes.c_float), n_slots, S.shape[1], _p(cin, ctypes.c_uint32),
+                       _p(out, ctypes.c_uint32), W, H, step)
+    return out
+
+
+def jfa_pass_pixels(sites, n_slots, cin, W, H, step, pix) -> np.ndarray:
+    S = _f32(sites)
+    cin = _u32(cin)
+    pix = _u32(pix).ravel()
+    out = np.empty((pix.size, K), dtype=np.uint32)
+    lib().orc_jfa_pass_pixels(_p(S, ctypes.c_float), n_slots, S.shape[1], _p(cin, ctypes.c_uint32), W, H, step,
+                              _p(pix, ctypes.c_uint32), pix.size, _p(out, ctypes.c_uint32))
+    return out
+
+
+def jfa_union_pixels(sites, n_slots, cin, W, H, step, pix):
+    S = _f32(sites)
+    cin = _u32(cin)
+    pix = _u32(pix).ravel()
+    mu = lib().orc_max_union()
+    out = np.empty((pix.size, mu), dtype=np.uint32)
+    cnt = np.empty(pix.size, dtype=np.int32)
+    lib().orc_jfa_union_pixels(_p(S, ctypes.c_float), n_slots, _p(cin, ctypes.c_uint32), W, H, step,
+                               _p(pix, ctypes.c_uint32), pix.size, _p(out, ctypes.c_uint32),
+                               _p(cnt, ctypes.c_int))
+    return out, cnt
+
+
+def jfa_steps(W: int, H: int) -> list:
+    """The prepass's steps: B/2, ..., 1 with B = 2^ceil(log2 max(W, H)) (ceil(log2) passes)."""
+    B = 1 << max(0, (max(W, H) - 1).bit_length())
+    out, k = [], B // 2
+    while k >= 1:
+        out.append(k)
+        k //= 2
+    return out
 
 
 from .densify import densify_prune  # noqa: E402  (pure Python, no C)

@@ -639,3 +639,150 @@ void orc_densify_stats(const double *S, int n_slots, int stride, const uint32_t 
         }
     }
 }
+
+/* ------------------------------------------------------ JFA prepass ------
+ * [SUM] B.3 "Jump schedule": an optional jump-flood prepass for
+ * (re)initialisation -- a seed pass, then ceil(log2 max(W,H)) flood passes that
+ * sample 3x3 neighbourhoods and write the four closest sites.
+ * Readings (the pages give no more): the seed pass puts each active site with a
+ * finite position into the list of the pixel that contains it (the floor of its
+ * position, clamped into the image); a pixel keeps at most four of them, the
+ * best by (d, ID) at its centre.  A flood pass with step k takes, per pixel, the
+ * union of the first four entries of the lists at the offsets {-k, 0, k}^2 that
+ * lie inside the image, drops sentinels, IDs >= n_slots, inactive sites,
+ * non-finite scores and duplicates, and keeps the four best by (d, ID) in
+ * entries 0..3; entries 4..7 hold the sentinel.  A pass reads one map and writes
+ * another.  Selection runs in float32 like the propagation's.
+ */
+#define ORC_JFA_KEEP 4
+#define ORC_JFA_UNION (9 * ORC_JFA_KEEP)
+
+static void sort_by_score(float *d, uint32_t *u, int n)
+{
+    for (int i = 1; i < n; ++i) {
+        float dk = d[i];
+        uint32_t ik = u[i];
+        int j = i;
+        while (j > 0 && key_less(dk, ik, d[j - 1], u[j - 1])) {
+            d[j] = d[j - 1];
+            u[j] = u[j - 1];
+            --j;
+        }
+        d[j] = dk;
+        u[j] = ik;
+    }
+}
+
+void orc_jfa_seed(const float *S, int n_slots, int stride, int W, int H, uint32_t *cand)
+{
+    long P = (long)W * H;
+    for (long i = 0; i < P * ORC_K; ++i)
+        cand[i] = ORC_NONE;
+    for (uint32_t id = 0; id < (uint32_t)n_slots; ++id) {
+        if (!site_usable(S, id, (uint32_t)n_slots))
+            continue;
+        float x = S[id], y = S[(long)stride + id];
+        if (!isfinite(x) || !isfinite(y))
+            continue;
+        /* the pixel that contains the site, clamped into the image (in float first,
+         * so that any finite position converts) */
+        float cx = x < 0.0f ? 0.0f : (x > (float)(W - 1) ? (float)(W - 1) : x);
+        float cy = y < 0.0f ? 0.0f : (y > (float)(H - 1) ? (float)(H - 1) : y);
+        int col = (int)floorf(cx), row = (int)floorf(cy);
+        float d = score_f32(S, stride, id, col, row, W, H);
+        if (!isfinite(d))
+            continue;
+        uint32_t *lst = cand + ((long)row * W + col) * ORC_K;
+        float dd[ORC_JFA_KEEP + 1];
+        uint32_t uu[ORC_JFA_KEEP + 1];
+        int n = 0;
+        for (int k = 0; k < ORC_JFA_KEEP && lst[k] != ORC_NONE; ++k) {
+            uu[n] = lst[k];
+            dd[n] = score_f32(S, stride, lst[k], col, row, W, H);
+            ++n;
+        }
+        uu[n] = id;
+        dd[n] = d;
+        ++n;
+        sort_by_score(dd, uu, n);
+        for (int k = 0; k < ORC_JFA_KEEP; ++k)
+            lst[k] = k < n ? uu[k] : ORC_NONE;
+    }
+}
+
+static int jfa_union_pixel(const float *S, uint32_t n_slots, const uint32_t *cin, int W, int H, int col, int row,
+                           int step, uint32_t *u)
+{
+    int nu = 0;
+    for (int dy = -1; dy <= 1; ++dy)
+        for (int dx = -1; dx <= 1; ++dx) {
+            int c = col + dx * step, r = row + dy * step;
+            if (c < 0 || c >= W || r < 0 || r >= H)
+                continue;
+            const uint32_t *lst = cin + ((long)r * W + c) * ORC_K;
+            for (int k = 0; k < ORC_JFA_KEEP; ++k) {
+                uint32_t id = lst[k];
+                if (!site_usable(S, id, n_slots))
+                    continue;
+                int seen = 0;
+                for (int j = 0; j < nu; ++j)
+                    if (u[j] == id)
+                        seen = 1;
+                if (!seen)
+                    u[nu++] = id;
+            }
+        }
+    return nu;
+}
+
+static void jfa_pixel(const float *S, uint32_t n_slots, long stride, const uint32_t *cin, int W, int H, int col,
+                      int row, int step, uint32_t *out)
+{
+    uint32_t u[ORC_JFA_UNION];
+    float d[ORC_JFA_UNION];
+    int nu = jfa_union_pixel(S, n_slots, cin, W, H, col, row, step, u);
+    int nv = 0;
+    for (int i = 0; i < nu; ++i) {
+        float di = score_f32(S, stride, u[i], col, row, W, H);
+        if (!isfinite(di))
+            continue;
+        u[nv] = u[i];
+        d[nv] = di;
+        ++nv;
+    }
+    sort_by_score(d, u, nv);
+    for (int k = 0; k < ORC_K; ++k)
+        out[k] = (k < ORC_JFA_KEEP && k < nv) ? u[k] : ORC_NONE;
+}
+
+void orc_jfa_pass(const float *S, int n_slots, int stride, const uint32_t *cin, uint32_t *cout, int W, int H,
+                  int step)
+{
+    long P = (long)W * H;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (long p = 0; p < P; ++p)
+        jfa_pixel(S, (uint32_t)n_slots, stride, cin, W, H, (int)(p % W), (int)(p / W), step, cout + p * ORC_K);
+}
+
+void orc_jfa_pass_pixels(const float *S, int n_slots, int stride, const uint32_t *cin, int W, int H, int step,
+                         const uint32_t *pix, long n, uint32_t *out)
+{
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (long i = 0; i < n; ++i)
+        jfa_pixel(S, (uint32_t)n_slots, stride, cin, W, H, (int)(pix[i] % (uint32_t)W), (int)(pix[i] / (uint32_t)W),
+                  step, out + i * ORC_K);
+}
+
+/* The deduplicated union a flood pass selects from (padded to ORC_MAX_UNION). */
+void orc_jfa_union_pixels(const float *S, int n_slots, const uint32_t *cin, int W, int H, int step,
+                          const uint32_t *pix, long n, uint32_t *out, int *count)
+{
+    for (long i = 0; i < n; ++i) {
+        uint32_t u[ORC_JFA_UNION];
+        int nu = jfa_union_pixel(S, (uint32_t)n_slots, cin, W, H, (int)(pix[i] % (uint32_t)W),
+                                 (int)(pix[i] / (uint32_t)W), step, u);
+        for (int j = 0; j < ORC_MAX_UNION; ++j)
+            out[i * ORC_MAX_UNION + j] = j < nu ? u[j] : ORC_NONE;
+        count[i] = nu;
+    }
+}
