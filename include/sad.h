@@ -159,6 +159,34 @@ int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, u
                        int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream);
 
 /*
+ * sad_jfa_seed -- seed pass of the optional jump-flood prepass ([SUM] B.3 "Jump
+ * schedule": a seed pass, then flood passes over 3x3 neighbourhoods that keep the
+ * four closest sites; meant for (re)initialisation and after large edits).
+ * Every active site with a finite position is entered in the list of the pixel
+ * that contains it (floor of its position, clamped into the image); a pixel keeps
+ * at most four, the best by (d, ID) at its centre, in entries 0..3 (ascending);
+ * all other entries are SAD_INVALID.  The whole map is written.
+ *   rec device [n_slots][16] read-only; cand device [H][W][8], written.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
+ */
+int sad_jfa_seed(const float *rec, int n_slots, uint32_t *cand, int W, int H, void *stream);
+
+/*
+ * sad_jfa_pass -- one flood pass of the prepass with step `step` ([SUM] B.3):
+ * per pixel, the union of entries 0..3 of the lists at offsets {-step, 0,
+ * step}^2 that lie inside the image, without sentinels, IDs >= n_slots, inactive
+ * sites, non-finite scores and duplicates; the four best by (d, ID) go to entries
+ * 0..3 (ascending), SAD_INVALID to 4..7.  Jacobi: reads cand_in, writes cand_out.
+ * The prepass runs the steps B/2, B/4, ..., 1 (B = 2^ceil(log2 max(W,H))), i.e.
+ * ceil(log2 max(W,H)) passes, after sad_jfa_seed; sad_topk_propagate then fills
+ * the lists to K.
+ *   step in [1, 65535]; cand_in, cand_out device [H][W][8], not overlapping.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
+ */
+int sad_jfa_pass(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H, int step,
+                 void *stream);
+
+/*
  * sad_topk_exact -- the exact top-K map by brute force over every slot: the list
  * that propagation approximates ([NOTE] design 3; [SUM] section 4 "Candidate
  * maintenance").  Used to (re)initialise a map and to measure recall.  Cost

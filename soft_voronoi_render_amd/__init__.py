@@ -105,6 +105,10 @@ def lib() -> ctypes.CDLL:
         L.sad_render_fwd.argtypes = [fp, i32, vp, i32, i32, fp, vp]
         L.sad_render_bwd.restype = i32
         L.sad_render_bwd.argtypes = [fp, i32, vp, fp, i32, i32, fp, fp, fp, vp]
+        L.sad_jfa_seed.restype = i32
+        L.sad_jfa_seed.argtypes = [vp, i32, vp, i32, i32, vp]
+        L.sad_jfa_pass.restype = i32
+        L.sad_jfa_pass.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp]
         L.sad_densify_stats.restype = i32
         L.sad_densify_stats.argtypes = [fp, i32, vp, fp, i32, i32, fp, vp]
         ip = ctypes.POINTER(ctypes.c_int)
@@ -118,7 +122,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("sad_abi_version", "sad_status_string", "sad_site_records", "sad_topk_propagate", "sad_topk_exact",
-            "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_densify_stats", "sad_densify_prune")
+            "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_densify_stats", "sad_densify_prune", "sad_jfa_seed", "sad_jfa_pass")
 
 
 # --------------------------------------------------------------- marshalling
@@ -188,6 +192,41 @@ def topk_propagate(rec, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed
     b = _dev(cand_out, "cand_out", _U32, (H, W, K))
     _check("sad_topk_propagate", lib().sad_topk_propagate(g, n_slots, a, b, W, H, jump, pass_index & 0xFFFFFFFF,
                                                           seed & 0xFFFFFFFF, n_inject, _stream(stream)))
+
+
+def jfa_seed(rec, n_slots, cand, W, H, stream=None):
+    """Seed pass of the jump-flood prepass (see sad_jfa_seed)."""
+    g = _rec(rec, n_slots)
+    c = _dev(cand, "cand", _U32, (H, W, K))
+    _check("sad_jfa_seed", lib().sad_jfa_seed(g, n_slots, c, W, H, _stream(stream)))
+
+
+def jfa_pass(rec, n_slots, cand_in, cand_out, W, H, step, stream=None):
+    """One flood pass of the jump-flood prepass: cand_in -> cand_out (see sad_jfa_pass)."""
+    g = _rec(rec, n_slots)
+    a = _dev(cand_in, "cand_in", _U32, (H, W, K))
+    b = _dev(cand_out, "cand_out", _U32, (H, W, K))
+    _check("sad_jfa_pass", lib().sad_jfa_pass(g, n_slots, a, b, W, H, step, _stream(stream)))
+
+
+def jfa_steps(W: int, H: int) -> list:
+    """The prepass's flood steps B/2, ..., 1 with B = 2^ceil(log2 max(W, H))."""
+    B = 1 << max(0, (max(W, H) - 1).bit_length())
+    out, k = [], B // 2
+    while k >= 1:
+        out.append(k)
+        k //= 2
+    return out
+
+
+def jfa_prepass(rec, n_slots, a, b, W, H, stream=None):
+    """Seed pass into `a`, then the flood passes ping-ponging between `a` and `b`;
+    returns the map that holds the result (four closest per pixel)."""
+    jfa_seed(rec, n_slots, a, W, H, stream)
+    for k in jfa_steps(W, H):
+        jfa_pass(rec, n_slots, a, b, W, H, k, stream)
+        a, b = b, a
+    return a
 
 
 def topk_exact(rec, n_slots, cand_out, W, H, stream=None):

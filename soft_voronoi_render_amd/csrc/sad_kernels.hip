@@ -610,6 +610,101 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_direct(const float4 *__rest
 }
 
 // ---------------------------------------------------------------------------
+// Jump-flood prepass (summary, Appendix B.3 "Jump schedule": an optional prepass
+// for (re)initialisation -- a seed pass, then ceil(log2 max(W, H)) flood passes
+// over 3x3 neighbourhoods that keep the four closest sites).
+//
+// Seed: every active site with a finite position enters the list of the pixel
+// that contains it; a pixel keeps at most four, the best by (d, ID) at its
+// centre.  On the GPU the four places are filled in four rounds (one launch
+// each): in round r every site not already in places 0..r-1 offers its 64-bit
+// ranking key to place r with an atomic minimum, so place r ends up with the
+// r-th best key whatever the order of arrival.  The places are the four 8-byte
+// pairs of the pixel's 32-byte list; a last pass turns keys into IDs.
+constexpr int JFA_KEEP = 4;
+
+__global__ __launch_bounds__(256) void k_fill_map(uint4 *__restrict__ cand, long n4)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n4)
+        cand[i] = make_uint4(NONE, NONE, NONE, NONE);
+}
+
+__global__ __launch_bounds__(256) void k_jfa_seed_round(const float4 *__restrict__ G, uint32_t n_slots,
+                                                        unsigned long long *__restrict__ keys, int W, int H,
+                                                        float s, int round)
+{
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= n_slots)
+        return;
+    const float4 g0 = G[RLD4 * (size_t)i], g1 = G[RLD4 * (size_t)i + 1];
+    if (!(g0.x >= 0.0f) || !finitef(g0.x) || !finitef(g0.y))
+        return;  // inactive (x < 0), or no position
+    const int col = (int)floorf(fminf(g0.x, (float)(W - 1)));
+    const int row = (int)floorf(fminf(fmaxf(g0.y, 0.0f), (float)(H - 1)));
+    const float d = geom_score(g0, g1, (float)col + 0.5f, (float)row + 0.5f, s);
+    if (!finitef(d))
+        return;
+    const unsigned long long key = rank_key(d, i);
+    unsigned long long *pl = keys + ((size_t)row * W + col) * JFA_KEEP;
+    for (int r = 0; r < round; ++r)
+        if (pl[r] == key)
+            return;  // already placed
+    atomicMin(pl + round, key);
+}
+
+// keys -> IDs: the low word of a key is the site's ID (the sentinel where no key
+// arrived); entries 4..7 are the sentinel.
+__global__ __launch_bounds__(256) void k_jfa_seed_finish(uint4 *__restrict__ cand, long P)
+{
+    const long p = (long)blockIdx.x * 256 + threadIdx.x;
+    if (p >= P)
+        return;
+    const uint4 a = cand[2 * p], b = cand[2 * p + 1];
+    cand[2 * p] = make_uint4(a.x, a.z, b.x, b.z);
+    cand[2 * p + 1] = make_uint4(NONE, NONE, NONE, NONE);
+}
+
+// One flood pass with step `step`: the union of the first four entries of the 3x3
+// lists at offsets {-step, 0, step}^2 inside the image; the four best by (d, ID)
+// go to entries 0..3, the sentinel to 4..7.  Each list is read by at most one
+// pixel of a tile at steps >= 16, so candidates are scored straight from their
+// records, as in the table-free propagation.
+__global__ __launch_bounds__(BLOCK) void k_jfa_pass(const float4 *__restrict__ G, uint32_t n_slots,
+                                                    const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
+                                                    int H, int step, float s, int tiles_x, int nb)
+{
+    const int t = xcd_band(blockIdx.x, nb);
+    const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
+    const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
+    if (col >= W || row >= H)
+        return;
+    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    TopK64 best;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+        best.k[j] = ~0ull;
+    for (int li = 0; li < 9; ++li) {
+        const int c = col + (li % 3 - 1) * step, r = row + (li / 3 - 1) * step;
+        if (c < 0 || c >= W || r < 0 || r >= H)
+            continue;
+        const uint4 a = cin[2 * ((long)r * W + c)];
+        const uint32_t ids[JFA_KEEP] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int k = 0; k < JFA_KEEP; ++k) {
+            if (ids[k] < n_slots) {
+                bool usable;
+                const float d = geom_score_id(G, ids[k], X, Y, s, usable);
+                best.consider(ids[k], d, usable);
+            }
+        }
+    }
+    const long p = (long)row * W + col;
+    cout[2 * p] = make_uint4((uint32_t)best.k[0], (uint32_t)best.k[1], (uint32_t)best.k[2], (uint32_t)best.k[3]);
+    cout[2 * p + 1] = make_uint4(NONE, NONE, NONE, NONE);
+}
+
+// ---------------------------------------------------------------------------
 // Exact top-K by brute force: every slot is scored for every pixel.  Scoring
 // records are staged through LDS 256 at a time.
 __global__ __launch_bounds__(BLOCK) void k_topk_exact(const float4 *__restrict__ G, uint32_t n_slots,
@@ -1576,6 +1671,55 @@ int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, u
     else
         hipLaunchKernelGGL(k_propagate_direct, dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, W, H,
                            jump, seed_h, n_inject, sc, g.tiles_x, g.nb);
+    return launched();
+}
+
+int sad_jfa_seed(const float *rec, int n_slots, uint32_t *cand, int W, int H, void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)))
+        return rc;
+    if (n_slots < 0)
+        return SAD_ERR_ARG;
+    if (W == 0 || H == 0)
+        return SAD_OK;
+    if ((!rec && n_slots > 0) || !cand)
+        return SAD_ERR_ARG;
+    if (!aligned16(cand) || !aligned16(rec))
+        return SAD_ERR_ALIGN;
+    const long P = (long)W * H;
+    const hipStream_t hs = (hipStream_t)stream;
+    hipLaunchKernelGGL(k_fill_map, dim3((unsigned)((2 * P + 255) / 256)), dim3(256), 0, hs, (uint4 *)cand, 2 * P);
+    if (n_slots > 0)
+        for (int r = 0; r < JFA_KEEP; ++r)
+            hipLaunchKernelGGL(k_jfa_seed_round, dim3((n_slots + 255) / 256), dim3(256), 0, hs, (const float4 *)rec,
+                               (uint32_t)n_slots, (unsigned long long *)cand, W, H, scale_of(W, H), r);
+    hipLaunchKernelGGL(k_jfa_seed_finish, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, hs, (uint4 *)cand, P);
+    return launched();
+}
+
+int sad_jfa_pass(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H, int step,
+                 void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)))
+        return rc;
+    if (n_slots < 0 || step < 1 || step > 0xFFFF)
+        return SAD_ERR_ARG;
+    if (W == 0 || H == 0)
+        return SAD_OK;
+    if ((!rec && n_slots > 0) || !cand_in || !cand_out)
+        return SAD_ERR_ARG;
+    const size_t bytes = (size_t)W * H * K * sizeof(uint32_t);
+    const uintptr_t a0 = (uintptr_t)cand_in, a1 = (uintptr_t)cand_out;
+    if (a0 < a1 + bytes && a1 < a0 + bytes)
+        return SAD_ERR_ARG;
+    if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(rec))
+        return SAD_ERR_ALIGN;
+    const TileGrid g = tile_grid(W, H);
+    hipLaunchKernelGGL(k_jfa_pass, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
+                       (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, W, H, step, scale_of(W, H),
+                       g.tiles_x, g.nb);
     return launched();
 }
 

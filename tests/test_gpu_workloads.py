@@ -74,16 +74,37 @@ def test_edit4096_refresh_recall(orc):
     assert np.isfinite(loss.sum().item())
     rng = np.random.default_rng(4096)
     pix = np.unique(rng.choice(W * H, 4096, replace=False)).astype(np.uint32)
-    got = map_to_host(a.view(-1, 8)[torch.from_numpy(pix.astype(np.int64)).to(a.device)])
+    pix_d = torch.from_numpy(pix.astype(np.int64)).to(a.device)
+    got = map_to_host(a.view(-1, 8)[pix_d])
+    # the other route after a large edit: rebuild with the jump-flood prepass (seed
+    # pass + 12 flood passes keeping four), then 4 propagation passes at jump 1
+    print("edit4096: jump-flood reinitialisation", flush=True)
+    e4 = torch.cuda.Event(enable_timing=True)
+    e5 = torch.cuda.Event(enable_timing=True)
+    e4.record()
+    res = sad.jfa_prepass(rec, n, b, a, W, H)
+    oth = a if res.data_ptr() == b.data_ptr() else b
+    for t in range(4):
+        sad.topk_propagate(rec, n, res, oth, W, H, 1, 2000 + t, synth.SEED_INJECT, M)
+        res, oth = oth, res
+    e5.record()
+    torch.cuda.synchronize()
+    jfa_ms = e4.elapsed_time(e5)
+    got_jfa = map_to_host(res.view(-1, 8)[pix_d])
     print("edit4096: oracle exact top-8 on 4096 pixels", flush=True)
     t0 = time.time()
     ref = orc.topk_exact_pixels(S2, n, W, H, pix)
     exact = np.mean([set(x) == set(y) for x, y in zip(got, ref)])
     per_entry = np.mean([len(set(x) & set(y)) / 8.0 for x, y in zip(got, ref)])
+    exact_j = np.mean([set(x) == set(y) for x, y in zip(got_jfa, ref)])
+    per_entry_j = np.mean([len(set(x) & set(y)) / 8.0 for x, y in zip(got_jfa, ref)])
     print(f"edit4096: refresh {refresh_ms:.2f} ms (12 passes), fused fwd+bwd {fb_ms:.2f} ms, "
           f"exact-set recall {exact:.4f}, per-entry recall {per_entry:.4f} (oracle {time.time() - t0:.1f} s)",
           flush=True)
+    print(f"edit4096: jump-flood reinit + 4 passes {jfa_ms:.2f} ms, exact-set recall {exact_j:.4f}, "
+          f"per-entry recall {per_entry_j:.4f}", flush=True)
     assert per_entry > 0.9 and exact > 0.6
+    assert per_entry_j > 0.9
 
 
 def test_div2k2040_fit_with_budget_control():
