@@ -584,10 +584,12 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_direct(const float4 *__rest
         const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            if (ids[k] < n_slots) {
+            // an ID already held is skipped before its record is fetched (lists of
+            // nearby pixels share most of their sites)
+            if (ids[k] < n_slots && !best.holds(ids[k])) {
                 bool usable;
                 const float d = geom_score_id(G, ids[k], X, Y, s, usable);
-                best.consider(ids[k], d, usable);
+                best.consider_new(ids[k], d, usable);
             }
         }
     }
@@ -692,10 +694,11 @@ __global__ __launch_bounds__(BLOCK) void k_jfa_pass(const float4 *__restrict__ G
         const uint32_t ids[JFA_KEEP] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int k = 0; k < JFA_KEEP; ++k) {
-            if (ids[k] < n_slots) {
+            // an ID already held is skipped before its record is fetched
+            if (ids[k] < n_slots && !best.holds(ids[k])) {
                 bool usable;
                 const float d = geom_score_id(G, ids[k], X, Y, s, usable);
-                best.consider(ids[k], d, usable);
+                best.consider_new(ids[k], d, usable);
             }
         }
     }

@@ -105,6 +105,23 @@ def test_render_and_adam_reject_bad_arguments(L):
     assert A(P, P, P, P, None, 0, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == 0  # no slots: no-op
 
 
+def test_jfa_entry_points_reject_bad_arguments(L):
+    S, J = L.sad_jfa_seed, L.sad_jfa_pass
+    assert S(P, -1, P, 16, 16, None) == ERR_ARG
+    assert S(0, 4, P, 16, 16, None) == ERR_ARG
+    assert S(P, 4, 0, 16, 16, None) == ERR_ARG
+    assert S(P, 4, P + 4, 16, 16, None) == ERR_ALIGN
+    assert S(P + 8, 4, P, 16, 16, None) == ERR_ALIGN
+    assert S(P, 4, P, 70000, 16, None) == ERR_ARG
+    assert S(P, 4, P, 0, 16, None) == 0                      # empty image: no-op
+    assert J(P, 4, P, Q, 16, 16, 0, None) == ERR_ARG         # step 0
+    assert J(P, 4, P, Q, 16, 16, 65536, None) == ERR_ARG
+    assert J(P, 4, P, P + 32, 16, 16, 1, None) == ERR_ARG     # overlapping maps
+    assert J(P, 4, P + 4, Q, 16, 16, 1, None) == ERR_ALIGN
+    assert J(P, -1, P, Q, 16, 16, 1, None) == ERR_ARG
+    assert J(P, 4, P, Q, 16, 0, 1, None) == 0
+
+
 def test_densify_entry_points_reject_bad_arguments(L):
     D = L.sad_densify_stats
     assert D(P, -1, P, Q, 16, 16, Q, None) == ERR_ARG
