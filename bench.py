@@ -162,6 +162,8 @@ def main():
         fit.maps[1].fill_(-1)
         fit.cur = 0
         fit.it = 0
+        fit.passes = 0
+        fit.warm_end = 0
         fit.loss.zero_()
 
     # warm-up (untimed): the first iterations of the fit
@@ -199,6 +201,7 @@ def main():
 
     # quality after the fit: loss of one more iteration
     fit.it = args.steps
+    fit.passes = args.steps
     fit.loss.zero_()
     fit.step()
     torch.cuda.synchronize()

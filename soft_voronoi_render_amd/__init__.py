@@ -376,15 +376,29 @@ def new_map(W: int, H: int, device="cuda") -> torch.Tensor:
 
 
 class Fitter:
-    """One SAD fitting state on the GPU and its iteration: propagate (one pass),
-    render forward, render backward, Adam (which also refreshes the site
-    records the image-space kernels read).  Everything runs in libsad kernels on one
-    stream; nothing crosses to the host inside an iteration."""
+    """One SAD fitting state on the GPU and its iteration: propagate, render
+    forward, render backward, Adam (which also refreshes the site records the
+    image-space kernels read).  Everything runs in libsad kernels on one stream;
+    nothing crosses to the host inside an iteration.
+
+    The coarse-to-fine warm-up (jumps B/2 .. 1) runs one pass per iteration; after
+    it the candidate field is refreshed every `refresh_every` iterations with
+    `passes_per_refresh` propagation passes (paperlayer.ai summary, section 4 and
+    B.3: warm-up first, then updates; both the update frequency and the passes per
+    update are exposed, and 8-16 iterations between updates left the final PSNR
+    unchanged there).  The pass counter drives the jump schedule and the
+    injection's pass index."""
 
     def __init__(self, sites: torch.Tensor, n_slots: int, target: torch.Tensor, W: int, H: int,
-                 n_inject: int = 4, seed: int = 4, adam: AdamConfig | None = None, cand: torch.Tensor | None = None):
+                 n_inject: int = 4, seed: int = 4, adam: AdamConfig | None = None, cand: torch.Tensor | None = None,
+                 refresh_every: int = 1, passes_per_refresh: int = 1):
+        if refresh_every < 1 or passes_per_refresh < 0:
+            raise ValueError("refresh_every >= 1 and passes_per_refresh >= 0")
         dev = sites.device
         self.W, self.H, self.n_slots, self.n_inject, self.seed = W, H, n_slots, n_inject, seed
+        self.refresh_every, self.passes_per_refresh = refresh_every, passes_per_refresh
+        self.passes = 0
+        self.warm_end = 0  # first iteration after the warm-up passes
         self.sites = sites
         self.target = target
         stride = sites.shape[1]
@@ -422,7 +436,15 @@ class Fitter:
         """One iteration (the hot path): propagate, render forward and backward
         (one fused launch that writes the image and the gradients), Adam."""
         it = self.it
-        self.propagate(self.jump_at(it), it, stream)
+        warm = (max(self.W, self.H) - 1).bit_length()  # log2 B passes with jumps B/2 .. 1
+        if self.passes < warm:
+            self.propagate(self.jump_at(self.passes), self.passes, stream)
+            self.passes += 1
+            self.warm_end = it + 1
+        elif (it - self.warm_end) % self.refresh_every == 0:
+            for _ in range(self.passes_per_refresh):
+                self.propagate(self.jump_at(self.passes), self.passes, stream)
+                self.passes += 1
         render_bwd(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, self.grad, self.loss, self.rgb,
                    stream)
         adam_step(self.sites, self.m, self.v, self.grad, self.n_slots, it + 1, self.W * self.H, self.W, self.H,

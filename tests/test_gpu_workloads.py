@@ -137,3 +137,39 @@ def test_div2k2040_fit_with_budget_control():
     assert np.isfinite(losses).all()
     assert losses[-1] < 0.8 * losses[2]
     assert len(counts) == 5
+
+
+def test_kodak768_refresh_frequency():
+    """Candidate-field refresh every 1, 8 and 16 iterations (the summary's B.3
+    reports 8-16 iterations between updates leave the final PSNR unchanged): PSNR
+    of the 200-iteration kodak768 fit and time per iteration, reported; the
+    infrequent schedules must stay close in PSNR and be faster."""
+    wl = synth.WORKLOADS["kodak768"]
+    W, H, n = wl.W, wl.H, wl.n_sites
+    S, tgt = bench.make_inputs(wl, torch.device("cuda:0"))
+    res = {}
+    for every, passes in ((1, 1), (8, 1), (16, 1), (8, 2)):
+        f = sad.Fitter(to_dev(S), n, tgt, W, H, n_inject=wl.n_inject, seed=synth.SEED_INJECT,
+                       refresh_every=every, passes_per_refresh=passes)
+        for _ in range(3):  # warm the kernels up
+            f.step()
+        f = sad.Fitter(to_dev(S), n, tgt, W, H, n_inject=wl.n_inject, seed=synth.SEED_INJECT,
+                       refresh_every=every, passes_per_refresh=passes)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(wl.iters):
+            f.step()
+        e1.record()
+        f.loss.zero_()
+        f.step()
+        torch.cuda.synchronize()
+        psnr = 10 * np.log10(3 * W * H / f.loss.sum().item())
+        res[(every, passes)] = (psnr, e0.elapsed_time(e1) / wl.iters)
+        print(f"kodak768 refresh every {every} x {passes} pass: PSNR {psnr:.3f} dB, "
+              f"{res[(every, passes)][1] * 1e3:.1f} us per iteration", flush=True)
+    base_psnr, base_t = res[(1, 1)]
+    for key in ((8, 1), (16, 1)):
+        assert res[key][1] < base_t
+        assert res[key][0] > base_psnr - 0.5
