@@ -57,26 +57,29 @@ def lib():
             "orc_xorshift32": (c_u32, [c_u32]),
             "orc_pass_word": (c_u32, [c_int, c_u32]),
             "orc_inject_ids": (None, [c_u32, c_int, c_u32, c_u32, c_u32, c_int, u32p]),
-            "orc_score_pairs": (None, [f32p, c_int, c_int, c_int, c_int, u32p, u32p, c_long, f32p]),
-            "orc_topk_exact": (None, [f32p, c_int, c_int, c_int, c_int, u32p]),
-            "orc_topk_exact_pixels": (None, [f32p, c_int, c_int, c_int, c_int, u32p, c_long, u32p]),
+            "orc_score_pairs": (None, [f32p, c_int, c_int, c_int, c_int, c_int, u32p, u32p, c_long, f32p]),
+            "orc_topk_exact": (None, [f32p, c_int, c_int, c_int, c_int, c_int, u32p]),
+            "orc_topk_exact_pixels": (None, [f32p, c_int, c_int, c_int, c_int, c_int, u32p, c_long, u32p]),
             "orc_hard_render": (None, [f32p, c_int, c_int, c_int, c_int, f32p]),
-            "orc_propagate": (None, [f32p, c_int, c_int, u32p, u32p, c_int, c_int, c_int, c_u32, c_u32, c_int]),
-            "orc_propagate_pixels": (None, [f32p, c_int, c_int, u32p, c_int, c_int, c_int, c_u32, c_u32, c_int,
-                                            u32p, c_long, u32p]),
-            "orc_union_pixels": (None, [f32p, c_int, u32p, c_int, c_int, c_int, c_u32, c_u32, c_int, u32p, c_long,
-                                        u32p, i32p]),
+            "orc_propagate": (None, [f32p, c_int, c_int, u32p, u32p, c_int, c_int, c_int, c_int, c_u32, c_u32,
+                                     c_int]),
+            "orc_propagate_pixels": (None, [f32p, c_int, c_int, u32p, c_int, c_int, c_int, c_int, c_u32, c_u32,
+                                            c_int, u32p, c_long, u32p]),
+            "orc_union_pixels": (None, [f32p, c_int, u32p, c_int, c_int, c_int, c_int, c_u32, c_u32, c_int, u32p,
+                                        c_long, u32p, i32p]),
             "orc_max_union": (c_int, []),
-            "orc_render_fwd": (None, [f64p, c_int, c_int, u32p, c_int, c_int, f64p]),
-            "orc_render_fwd_pixels": (None, [f64p, c_int, c_int, u32p, c_int, c_int, u32p, c_long, f64p]),
-            "orc_render_bwd": (None, [f64p, c_int, c_int, u32p, f32p, c_int, c_int, f64p, f64p]),
+            "orc_render_fwd": (None, [f64p, c_int, c_int, u32p, c_int, c_int, c_int, f64p]),
+            "orc_render_fwd_pixels": (None, [f64p, c_int, c_int, u32p, c_int, c_int, c_int, u32p, c_long, f64p]),
+            "orc_render_bwd": (None, [f64p, c_int, c_int, u32p, f32p, c_int, c_int, c_int, f64p, f64p]),
             "orc_adam_step": (None, [f64p, f64p, f64p, f64p, c_int, c_int, c_int, c_int, f64p, c_dbl, c_dbl,
                                      c_dbl, c_int, c_int]),
-            "orc_densify_stats": (None, [f64p, c_int, c_int, u32p, f32p, c_int, c_int, f64p]),
-            "orc_jfa_seed": (None, [f32p, c_int, c_int, c_int, c_int, u32p]),
-            "orc_jfa_pass": (None, [f32p, c_int, c_int, u32p, u32p, c_int, c_int, c_int]),
-            "orc_jfa_pass_pixels": (None, [f32p, c_int, c_int, u32p, c_int, c_int, c_int, u32p, c_long, u32p]),
-            "orc_jfa_union_pixels": (None, [f32p, c_int, u32p, c_int, c_int, c_int, u32p, c_long, u32p, i32p]),
+            "orc_densify_stats": (None, [f64p, c_int, c_int, u32p, f32p, c_int, c_int, c_int, f64p]),
+            "orc_jfa_seed": (None, [f32p, c_int, c_int, c_int, c_int, c_int, u32p]),
+            "orc_jfa_pass": (None, [f32p, c_int, c_int, u32p, u32p, c_int, c_int, c_int, c_int]),
+            "orc_jfa_pass_pixels": (None, [f32p, c_int, c_int, u32p, c_int, c_int, c_int, c_int, u32p, c_long,
+                                           u32p]),
+            "orc_jfa_union_pixels": (None, [f32p, c_int, u32p, c_int, c_int, c_int, c_int, u32p, c_long, u32p,
+                                            i32p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -101,6 +104,11 @@ def _f64(a):
 
 def _u32(a):
     return np.ascontiguousarray(a, dtype=np.uint32)
+
+
+def map_shape(W: int, H: int, cell: int = 1) -> tuple:
+    """Shape of a candidate map on the grid of `cell` x `cell` pixel cells."""
+    return (-(-H // cell), -(-W // cell), K)
 
 
 def set_threads(n: int) -> None:
@@ -131,29 +139,30 @@ def inject_ids(seed: int, jump: int, pass_index: int, pix: int, n_slots: int, m:
 
 
 # ---------------------------------------------------------------- score
-def score_pairs(sites, n_slots, W, H, pix, ids) -> np.ndarray:
+def score_pairs(sites, n_slots, W, H, pix, ids, cell=1) -> np.ndarray:
+    """Selection scores of (map entry, ID) pairs (cell centres for cell > 1)."""
     S = _f32(sites)
     pix = _u32(pix).ravel()
     ids = _u32(ids).ravel()
     out = np.empty(pix.size, dtype=np.float32)
-    lib().orc_score_pairs(_p(S, ctypes.c_float), n_slots, S.shape[1], W, H, _p(pix, ctypes.c_uint32),
+    lib().orc_score_pairs(_p(S, ctypes.c_float), n_slots, S.shape[1], W, H, cell, _p(pix, ctypes.c_uint32),
                           _p(ids, ctypes.c_uint32), pix.size, _p(out, ctypes.c_float))
     return out
 
 
 # ------------------------------------------------------------ exact top-K
-def topk_exact(sites, n_slots, W, H) -> np.ndarray:
+def topk_exact(sites, n_slots, W, H, cell=1) -> np.ndarray:
     S = _f32(sites)
-    out = np.empty((H, W, K), dtype=np.uint32)
-    lib().orc_topk_exact(_p(S, ctypes.c_float), n_slots, S.shape[1], W, H, _p(out, ctypes.c_uint32))
+    out = np.empty(map_shape(W, H, cell), dtype=np.uint32)
+    lib().orc_topk_exact(_p(S, ctypes.c_float), n_slots, S.shape[1], W, H, cell, _p(out, ctypes.c_uint32))
     return out
 
 
-def topk_exact_pixels(sites, n_slots, W, H, pix) -> np.ndarray:
+def topk_exact_pixels(sites, n_slots, W, H, pix, cell=1) -> np.ndarray:
     S = _f32(sites)
     pix = _u32(pix).ravel()
     out = np.empty((pix.size, K), dtype=np.uint32)
-    lib().orc_topk_exact_pixels(_p(S, ctypes.c_float), n_slots, S.shape[1], W, H, _p(pix, ctypes.c_uint32),
+    lib().orc_topk_exact_pixels(_p(S, ctypes.c_float), n_slots, S.shape[1], W, H, cell, _p(pix, ctypes.c_uint32),
                                 pix.size, _p(out, ctypes.c_uint32))
     return out
 
@@ -166,46 +175,50 @@ def hard_render(sites, n_slots, W, H) -> np.ndarray:
 
 
 # ------------------------------------------------------------ propagation
-def propagate(sites, n_slots, cin, W, H, jump, pass_index, seed, m) -> np.ndarray:
+def propagate(sites, n_slots, cin, W, H, jump, pass_index, seed, m, cell=1) -> np.ndarray:
     S = _f32(sites)
     cin = _u32(cin)
-    assert cin.shape == (H, W, K)
+    assert cin.shape == map_shape(W, H, cell)
     out = np.empty_like(cin)
     lib().orc_propagate(_p(S, ctypes.c_float), n_slots, S.shape[1], _p(cin, ctypes.c_uint32),
-                        _p(out, ctypes.c_uint32), W, H, jump, pass_index & 0xFFFFFFFF, seed & 0xFFFFFFFF, m)
+                        _p(out, ctypes.c_uint32), W, H, cell, jump, pass_index & 0xFFFFFFFF, seed & 0xFFFFFFFF, m)
     return out
 
 
-def propagate_pixels(sites, n_slots, cin, W, H, jump, pass_index, seed, m, pix) -> np.ndarray:
+def propagate_pixels(sites, n_slots, cin, W, H, jump, pass_index, seed, m, pix, cell=1) -> np.ndarray:
     S = _f32(sites)
     cin = _u32(cin)
+    assert cin.shape == map_shape(W, H, cell)
     pix = _u32(pix).ravel()
     out = np.empty((pix.size, K), dtype=np.uint32)
-    lib().orc_propagate_pixels(_p(S, ctypes.c_float), n_slots, S.shape[1], _p(cin, ctypes.c_uint32), W, H, jump,
-                               pass_index & 0xFFFFFFFF, seed & 0xFFFFFFFF, m, _p(pix, ctypes.c_uint32), pix.size,
-                               _p(out, ctypes.c_uint32))
+    lib().orc_propagate_pixels(_p(S, ctypes.c_float), n_slots, S.shape[1], _p(cin, ctypes.c_uint32), W, H, cell,
+                               jump, pass_index & 0xFFFFFFFF, seed & 0xFFFFFFFF, m, _p(pix, ctypes.c_uint32),
+                               pix.size, _p(out, ctypes.c_uint32))
     return out
 
 
-def union_pixels(sites, n_slots, cin, W, H, jump, pass_index, seed, m, pix):
+def union_pixels(sites, n_slots, cin, W, H, jump, pass_index, seed, m, pix, cell=1):
     S = _f32(sites)
     cin = _u32(cin)
+    assert cin.shape == map_shape(W, H, cell)
     pix = _u32(pix).ravel()
     mu = lib().orc_max_union()
     out = np.empty((pix.size, mu), dtype=np.uint32)
     cnt = np.empty(pix.size, dtype=np.int32)
-    lib().orc_union_pixels(_p(S, ctypes.c_float), n_slots, _p(cin, ctypes.c_uint32), W, H, jump,
+    lib().orc_union_pixels(_p(S, ctypes.c_float), n_slots, _p(cin, ctypes.c_uint32), W, H, cell, jump,
                            pass_index & 0xFFFFFFFF, seed & 0xFFFFFFFF, m, _p(pix, ctypes.c_uint32), pix.size,
                            _p(out, ctypes.c_uint32), _p(cnt, ctypes.c_int))
     return out, cnt
 
 
-def jump_schedule(W: int, H: int, n_iters: int) -> list:
-    """Jumps B/2, B/4, ..., 1, then 1; B = 2^ceil(log2 max(W, H)).
+def jump_schedule(W: int, H: int, n_iters: int, cell: int = 1) -> list:
+    """Jumps B/2, B/4, ..., 1, then 1; B = 2^ceil(log2 max(Wm, Hm)) over the map's
+    entries (Wm = ceil(W / cell), Hm likewise).
 
     (pages: paperlayer.ai summary, section 4 "Candidate maintenance"; B is our
     reading, since the pages do not define it.)
     """
+    W, H = -(-W // cell), -(-H // cell)
     B = 1 << max(0, (max(W, H) - 1).bit_length())
     out, k = [], B // 2
     for _ in range(n_iters):
@@ -215,36 +228,39 @@ def jump_schedule(W: int, H: int, n_iters: int) -> list:
 
 
 # ---------------------------------------------------------------- render
-def render_fwd(sites, n_slots, cand, W, H) -> np.ndarray:
+def render_fwd(sites, n_slots, cand, W, H, cell=1) -> np.ndarray:
     S = _f64(sites)
     cand = _u32(cand)
+    assert cand.shape == map_shape(W, H, cell)
     out = np.empty((H, W, 3), dtype=np.float64)
-    lib().orc_render_fwd(_p(S, ctypes.c_double), n_slots, S.shape[1], _p(cand, ctypes.c_uint32), W, H,
+    lib().orc_render_fwd(_p(S, ctypes.c_double), n_slots, S.shape[1], _p(cand, ctypes.c_uint32), W, H, cell,
                          _p(out, ctypes.c_double))
     return out
 
 
-def render_fwd_pixels(sites, n_slots, cand, W, H, pix) -> np.ndarray:
+def render_fwd_pixels(sites, n_slots, cand, W, H, pix, cell=1) -> np.ndarray:
     S = _f64(sites)
     cand = _u32(cand)
+    assert cand.shape == map_shape(W, H, cell)
     pix = _u32(pix).ravel()
     out = np.empty((pix.size, 3), dtype=np.float64)
-    lib().orc_render_fwd_pixels(_p(S, ctypes.c_double), n_slots, S.shape[1], _p(cand, ctypes.c_uint32), W, H,
+    lib().orc_render_fwd_pixels(_p(S, ctypes.c_double), n_slots, S.shape[1], _p(cand, ctypes.c_uint32), W, H, cell,
                                 _p(pix, ctypes.c_uint32), pix.size, _p(out, ctypes.c_double))
     return out
 
 
-def render_bwd(sites, n_slots, cand, target, W, H, grad=None):
+def render_bwd(sites, n_slots, cand, target, W, H, grad=None, cell=1):
     """Returns (grad float64 [11][stride], loss_sum).  Accumulates into `grad` if given."""
     S = _f64(sites)
     cand = _u32(cand)
+    assert cand.shape == map_shape(W, H, cell)
     T = _f32(target)
     if grad is None:
         grad = np.zeros((NACC, S.shape[1]), dtype=np.float64)
     assert grad.dtype == np.float64 and grad.flags["C_CONTIGUOUS"] and grad.shape == (NACC, S.shape[1])
     loss = np.zeros(1, dtype=np.float64)
     lib().orc_render_bwd(_p(S, ctypes.c_double), n_slots, S.shape[1], _p(cand, ctypes.c_uint32),
-                         _p(T, ctypes.c_float), W, H, _p(grad, ctypes.c_double), _p(loss, ctypes.c_double))
+                         _p(T, ctypes.c_float), W, H, cell, _p(grad, ctypes.c_double), _p(loss, ctypes.c_double))
     return grad, float(loss[0])
 
 
@@ -260,63 +276,68 @@ def adam_step(params, m, v, grad, n_slots, step, n_pixels, lr, b1, b2, eps, W, H
 
 
 # ------------------------------------------------------------ budget control
-def densify_stats(sites, n_slots, cand, target, W, H, stats=None):
+def densify_stats(sites, n_slots, cand, target, W, H, stats=None, cell=1):
     """Per-site mass, energy and error-weighted moments, float64 [stride][8] (+=)."""
     S = _f64(sites)
     cand = _u32(cand)
+    assert cand.shape == map_shape(W, H, cell)
     T = _f32(target)
     if stats is None:
         stats = np.zeros((S.shape[1], 8), dtype=np.float64)
     assert stats.dtype == np.float64 and stats.flags["C_CONTIGUOUS"] and stats.shape == (S.shape[1], 8)
     lib().orc_densify_stats(_p(S, ctypes.c_double), n_slots, S.shape[1], _p(cand, ctypes.c_uint32),
-                            _p(T, ctypes.c_float), W, H, _p(stats, ctypes.c_double))
+                            _p(T, ctypes.c_float), W, H, cell, _p(stats, ctypes.c_double))
     return stats
 
 
 # ------------------------------------------------------------ JFA prepass
-def jfa_seed(sites, n_slots, W, H) -> np.ndarray:
-    """Seed pass: each active site into the list of its pixel, <= 4 per pixel."""
+def jfa_seed(sites, n_slots, W, H, cell=1) -> np.ndarray:
+    """Seed pass: each active site into the list of its map entry, <= 4 per entry."""
     S = _f32(sites)
-    out = np.empty((H, W, K), dtype=np.uint32)
-    lib().orc_jfa_seed(_p(S, ctypes.c_float), n_slots, S.shape[1], W, H, _p(out, ctypes.c_uint32))
+    out = np.empty(map_shape(W, H, cell), dtype=np.uint32)
+    lib().orc_jfa_seed(_p(S, ctypes.c_float), n_slots, S.shape[1], W, H, cell, _p(out, ctypes.c_uint32))
     return out
 
 
-def jfa_pass(sites, n_slots, cin, W, H, step) -> np.ndarray:
+def jfa_pass(sites, n_slots, cin, W, H, step, cell=1) -> np.ndarray:
     S = _f32(sites)
     cin = _u32(cin)
-    assert cin.shape == (H, W, K)
+    assert cin.shape == map_shape(W, H, cell)
     out = np.empty_like(cin)
     lib().orc_jfa_pass(_p(S, ctypes.c_float), n_slots, S.shape[1], _p(cin, ctypes.c_uint32),
-                       _p(out, ctypes.c_uint32), W, H, step)
+                       _p(out, ctypes.c_uint32), W, H, cell, step)
     return out
 
 
-def jfa_pass_pixels(sites, n_slots, cin, W, H, step, pix) -> np.ndarray:
+def jfa_pass_pixels(sites, n_slots, cin, W, H, step, pix, cell=1) -> np.ndarray:
     S = _f32(sites)
     cin = _u32(cin)
+    assert cin.shape == map_shape(W, H, cell)
     pix = _u32(pix).ravel()
     out = np.empty((pix.size, K), dtype=np.uint32)
-    lib().orc_jfa_pass_pixels(_p(S, ctypes.c_float), n_slots, S.shape[1], _p(cin, ctypes.c_uint32), W, H, step,
-                              _p(pix, ctypes.c_uint32), pix.size, _p(out, ctypes.c_uint32))
+    lib().orc_jfa_pass_pixels(_p(S, ctypes.c_float), n_slots, S.shape[1], _p(cin, ctypes.c_uint32), W, H, cell,
+                              step, _p(pix, ctypes.c_uint32), pix.size, _p(out, ctypes.c_uint32))
     return out
 
 
-def jfa_union_pixels(sites, n_slots, cin, W, H, step, pix):
+def jfa_union_pixels(sites, n_slots, cin, W, H, step, pix, cell=1):
     S = _f32(sites)
     cin = _u32(cin)
+    assert cin.shape == map_shape(W, H, cell)
     pix = _u32(pix).ravel()
     mu = lib().orc_max_union()
     out = np.empty((pix.size, mu), dtype=np.uint32)
     cnt = np.empty(pix.size, dtype=np.int32)
-    lib().orc_jfa_union_pixels(_p(S, ctypes.c_float), n_slots, _p(cin, ctypes.c_uint32), W, H, step,
+    lib().orc_jfa_union_pixels(_p(S, ctypes.c_float), n_slots, _p(cin, ctypes.c_uint32), W, H, cell, step,
                                _p(pix, ctypes.c_uint32), pix.size, _p(out, ctypes.c_uint32),
                                _p(cnt, ctypes.c_int))
     return out, cnt
 
 
-def jfa_steps(W: int, H: int) -> list:
-    """The prepass's steps: B/2, ..., 1 with B = 2^ceil(log2 max(W, H)) (ceil(log2) passes)."""
+def jfa_steps(W: int, H: int, cell: int = 1) -> list:
+    """The prepass's steps: B/2, ..., 1 with B = 2^ceil(log2 max(Wm, Hm)) over the map's
+    entries (ceil(log2) passes)."""
+    W, H = -(-W // cell), -(-H // cell)
     B = 1 << max(0, (max(W, H) - 1).bit_length())
     out, k = [], B // 2
     while k >= 1:

@@ -106,13 +106,40 @@ void orc_inject_ids(uint32_t seed, int jump, uint32_t pass_index, uint32_t pix,
  * d(x,i) = s*||x - p_i||_{G_i} - s*r_i with s = 1/max(H,W).
  * With alpha = u.delta and beta = v.delta, ||delta||_G = sqrt(e^a alpha^2 + e^-a beta^2).
  */
-static float score_f32(const float *S, long stride, uint32_t id, int col, int row, int W, int H)
+/* Candidate grid ([SUM] B.3 "Candidate field"): the map has ceil(W/c) x ceil(H/c)
+ * cells, pixel (x, y) uses the list of cell (x/c, y/c) (integer division), and a
+ * cell's candidates are selected at the cell centre in UV coordinates, which in
+ * pixel units is ((cx + 1/2) W/Wm, (cy + 1/2) H/Hm).  c = 1 is the per-pixel map
+ * (evaluation at pixel centres).  Reading: the pages give the grid size, the
+ * integer mapping and the centred UVs, nothing more. */
+typedef struct {
+    int W, H, c, Wm, Hm;
+    float sx, sy, s;
+} grid;
+
+static grid make_grid(int W, int H, int c)
+{
+    grid g;
+    g.W = W;
+    g.H = H;
+    g.c = c < 1 ? 1 : c;
+    g.Wm = (W + g.c - 1) / g.c;
+    g.Hm = (H + g.c - 1) / g.c;
+    g.sx = (float)W / (float)(g.Wm > 0 ? g.Wm : 1);
+    g.sy = (float)H / (float)(g.Hm > 0 ? g.Hm : 1);
+    g.s = 1.0f / (float)(W > H ? W : H);
+    return g;
+}
+
+/* the map entry of pixel (col, row) */
+static long cell_of(const grid *g, int col, int row) { return (long)(row / g->c) * g->Wm + col / g->c; }
+
+static float score_at(const float *S, long stride, uint32_t id, float X, float Y, float s)
 {
     float px = S[P_X * stride + id], py = S[P_Y * stride + id];
     float r = S[P_R * stride + id];
     float dx = S[P_DX * stride + id], dy = S[P_DY * stride + id];
     float a = S[P_A * stride + id];
-    float s = 1.0f / (float)(W > H ? W : H);
     float ux = 1.0f, uy = 0.0f;
     float n2 = dx * dx + dy * dy;
     if (n2 >= 1e-30f) {
@@ -121,13 +148,20 @@ static float score_f32(const float *S, long stride, uint32_t id, int col, int ro
         uy = dy / n;
     }
     float vx = -uy, vy = ux;
-    float ddx = ((float)col + 0.5f) - px;
-    float ddy = ((float)row + 0.5f) - py;
+    float ddx = X - px;
+    float ddy = Y - py;
     float al = ux * ddx + uy * ddy;
     float be = vx * ddx + vy * ddy;
     float q = sqrtf(expf(a) * al * al + expf(-a) * be * be);
     return s * q - s * r;
 }
+
+/* selection score of map cell (cx, cy): evaluated at the cell's centred UV */
+static float score_cell(const float *S, long stride, uint32_t id, const grid *g, int cx, int cy)
+{
+    return score_at(S, stride, id, ((float)cx + 0.5f) * g->sx, ((float)cy + 0.5f) * g->sy, g->s);
+}
+
 
 /* The same score in float64, with the intermediates the backward needs. */
 typedef struct {
@@ -181,16 +215,17 @@ static int site_usable64(const double *S, uint32_t id, uint32_t n_slots)
 }
 
 /* Public: float32 selection scores of (pixel, id) pairs; unusable -> +inf. */
-void orc_score_pairs(const float *S, int n_slots, int stride, int W, int H,
+void orc_score_pairs(const float *S, int n_slots, int stride, int W, int H, int cell,
                      const uint32_t *pix, const uint32_t *ids, long n, float *out)
 {
+    grid g = make_grid(W, H, cell);
     for (long i = 0; i < n; ++i) {
         uint32_t id = ids[i];
         if (!site_usable(S, id, (uint32_t)n_slots)) {
             out[i] = INFINITY;
             continue;
         }
-        float d = score_f32(S, stride, id, (int)(pix[i] % (uint32_t)W), (int)(pix[i] / (uint32_t)W), W, H);
+        float d = score_cell(S, stride, id, &g, (int)(pix[i] % (uint32_t)g.Wm), (int)(pix[i] / (uint32_t)g.Wm));
         out[i] = isfinite(d) ? d : INFINITY;
     }
 }
@@ -206,7 +241,7 @@ static int key_less(float da, uint32_t ia, float db, uint32_t ib)
  * keep the K best under (d, ID); pad with the sentinel.  ([NOTE] design 3:
  * the maintained list approximates the top-K under the same score.)
  */
-static void exact_pixel(const float *S, uint32_t n_slots, long stride, int W, int H, int col, int row,
+static void exact_pixel(const float *S, uint32_t n_slots, long stride, const grid *g, int col, int row,
                         uint32_t *out)
 {
     float bd[ORC_K];
@@ -215,7 +250,7 @@ static void exact_pixel(const float *S, uint32_t n_slots, long stride, int W, in
     for (uint32_t id = 0; id < n_slots; ++id) {
         if (S[id] < 0.0f) /* inactive */
             continue;
-        float d = score_f32(S, stride, id, col, row, W, H);
+        float d = score_cell(S, stride, id, g, col, row);
         if (!isfinite(d))
             continue;
         if (cnt == ORC_K && !key_less(d, id, bd[ORC_K - 1], bi[ORC_K - 1]))
@@ -233,21 +268,23 @@ static void exact_pixel(const float *S, uint32_t n_slots, long stride, int W, in
         out[k] = k < cnt ? bi[k] : ORC_NONE;
 }
 
-void orc_topk_exact(const float *S, int n_slots, int stride, int W, int H, uint32_t *cand)
+void orc_topk_exact(const float *S, int n_slots, int stride, int W, int H, int cell, uint32_t *cand)
 {
-    long P = (long)W * H;
+    grid g = make_grid(W, H, cell);
+    long P = (long)g.Wm * g.Hm;
 #pragma omp parallel for schedule(dynamic, 64) num_threads(g_threads)
     for (long p = 0; p < P; ++p)
-        exact_pixel(S, (uint32_t)n_slots, stride, W, H, (int)(p % W), (int)(p / W), cand + p * ORC_K);
+        exact_pixel(S, (uint32_t)n_slots, stride, &g, (int)(p % g.Wm), (int)(p / g.Wm), cand + p * ORC_K);
 }
 
-void orc_topk_exact_pixels(const float *S, int n_slots, int stride, int W, int H,
+void orc_topk_exact_pixels(const float *S, int n_slots, int stride, int W, int H, int cell,
                            const uint32_t *pix, long n, uint32_t *out)
 {
+    grid g = make_grid(W, H, cell);
 #pragma omp parallel for schedule(dynamic, 16) num_threads(g_threads)
     for (long i = 0; i < n; ++i)
-        exact_pixel(S, (uint32_t)n_slots, stride, W, H, (int)(pix[i] % (uint32_t)W),
-                    (int)(pix[i] / (uint32_t)W), out + i * ORC_K);
+        exact_pixel(S, (uint32_t)n_slots, stride, &g, (int)(pix[i] % (uint32_t)g.Wm),
+                    (int)(pix[i] / (uint32_t)g.Wm), out + i * ORC_K);
 }
 
 /* Hard (argmin) render: colour of the first entry of the exact top-K, 0 if none.
@@ -255,10 +292,11 @@ void orc_topk_exact_pixels(const float *S, int n_slots, int stride, int W, int H
 void orc_hard_render(const float *S, int n_slots, int stride, int W, int H, float *rgb)
 {
     long P = (long)W * H;
+    grid g = make_grid(W, H, 1);
 #pragma omp parallel for schedule(dynamic, 64) num_threads(g_threads)
     for (long p = 0; p < P; ++p) {
         uint32_t lst[ORC_K];
-        exact_pixel(S, (uint32_t)n_slots, stride, W, H, (int)(p % W), (int)(p / W), lst);
+        exact_pixel(S, (uint32_t)n_slots, stride, &g, (int)(p % W), (int)(p / W), lst);
         for (int c = 0; c < 3; ++c)
             rgb[p * 3 + c] = lst[0] == ORC_NONE ? 0.0f : S[(P_CR + c) * (long)stride + lst[0]];
     }
@@ -309,16 +347,18 @@ static int union_pixel(const float *S, uint32_t n_slots, const uint32_t *cin, in
     return nu;
 }
 
-static void propagate_pixel(const float *S, uint32_t n_slots, long stride, const uint32_t *cin, int W, int H,
+/* (col, row): a cell of the map (a pixel when the grid's cell is 1); the union is
+ * taken in map coordinates, the injection uses the cell's index. */
+static void propagate_pixel(const float *S, uint32_t n_slots, long stride, const uint32_t *cin, const grid *g,
                             int col, int row, int jump, uint32_t pass_index, uint32_t seed, int m,
                             uint32_t *out)
 {
     uint32_t u[ORC_MAX_UNION];
     float d[ORC_MAX_UNION];
-    int nu = union_pixel(S, n_slots, cin, W, H, col, row, jump, pass_index, seed, m, u);
+    int nu = union_pixel(S, n_slots, cin, g->Wm, g->Hm, col, row, jump, pass_index, seed, m, u);
     int nv = 0;
     for (int i = 0; i < nu; ++i) {
-        float di = score_f32(S, stride, u[i], col, row, W, H);
+        float di = score_cell(S, stride, u[i], g, col, row);
         if (!isfinite(di))
             continue;
         u[nv] = u[i];
@@ -343,34 +383,38 @@ static void propagate_pixel(const float *S, uint32_t n_slots, long stride, const
 }
 
 void orc_propagate(const float *S, int n_slots, int stride, const uint32_t *cin, uint32_t *cout, int W, int H,
-                   int jump, uint32_t pass_index, uint32_t seed, int m)
+                   int cell, int jump, uint32_t pass_index, uint32_t seed, int m)
 {
-    long P = (long)W * H;
+    grid g = make_grid(W, H, cell);
+    long P = (long)g.Wm * g.Hm;
 #pragma omp parallel for schedule(static) num_threads(g_threads)
     for (long p = 0; p < P; ++p)
-        propagate_pixel(S, (uint32_t)n_slots, stride, cin, W, H, (int)(p % W), (int)(p / W), jump, pass_index,
+        propagate_pixel(S, (uint32_t)n_slots, stride, cin, &g, (int)(p % g.Wm), (int)(p / g.Wm), jump, pass_index,
                         seed, m, cout + p * ORC_K);
 }
 
-void orc_propagate_pixels(const float *S, int n_slots, int stride, const uint32_t *cin, int W, int H, int jump,
-                          uint32_t pass_index, uint32_t seed, int m, const uint32_t *pix, long n, uint32_t *out)
+void orc_propagate_pixels(const float *S, int n_slots, int stride, const uint32_t *cin, int W, int H, int cell,
+                          int jump, uint32_t pass_index, uint32_t seed, int m, const uint32_t *pix, long n,
+                          uint32_t *out)
 {
+    grid g = make_grid(W, H, cell);
 #pragma omp parallel for schedule(static) num_threads(g_threads)
     for (long i = 0; i < n; ++i)
-        propagate_pixel(S, (uint32_t)n_slots, stride, cin, W, H, (int)(pix[i] % (uint32_t)W),
-                        (int)(pix[i] / (uint32_t)W), jump, pass_index, seed, m, out + i * ORC_K);
+        propagate_pixel(S, (uint32_t)n_slots, stride, cin, &g, (int)(pix[i] % (uint32_t)g.Wm),
+                        (int)(pix[i] / (uint32_t)g.Wm), jump, pass_index, seed, m, out + i * ORC_K);
 }
 
 /* The deduplicated, filtered candidate union of each listed pixel (for checking
  * that a GPU list only holds members of it).  out: n x ORC_MAX_UNION, count: n. */
-void orc_union_pixels(const float *S, int n_slots, const uint32_t *cin, int W, int H, int jump,
+void orc_union_pixels(const float *S, int n_slots, const uint32_t *cin, int W, int H, int cell, int jump,
                       uint32_t pass_index, uint32_t seed, int m, const uint32_t *pix, long n, uint32_t *out,
                       int *count)
 {
+    grid g = make_grid(W, H, cell);
     for (long i = 0; i < n; ++i) {
         uint32_t *u = out + i * ORC_MAX_UNION;
-        int nu = union_pixel(S, (uint32_t)n_slots, cin, W, H, (int)(pix[i] % (uint32_t)W),
-                             (int)(pix[i] / (uint32_t)W), jump, pass_index, seed, m, u);
+        int nu = union_pixel(S, (uint32_t)n_slots, cin, g.Wm, g.Hm, (int)(pix[i] % (uint32_t)g.Wm),
+                             (int)(pix[i] / (uint32_t)g.Wm), jump, pass_index, seed, m, u);
         for (int j = nu; j < ORC_MAX_UNION; ++j)
             u[j] = ORC_NONE;
         count[i] = nu;
@@ -435,25 +479,29 @@ static void forward_pixel(const double *S, uint32_t n_slots, long stride, const 
     }
 }
 
-void orc_render_fwd(const double *S, int n_slots, int stride, const uint32_t *cand, int W, int H, double *rgb)
+void orc_render_fwd(const double *S, int n_slots, int stride, const uint32_t *cand, int W, int H, int cell,
+                    double *rgb)
 {
+    grid g = make_grid(W, H, cell);
     long P = (long)W * H;
 #pragma omp parallel for schedule(static) num_threads(g_threads)
     for (long p = 0; p < P; ++p) {
         pix64 X;
-        forward_pixel(S, (uint32_t)n_slots, stride, cand + p * ORC_K, W, H, (int)(p % W), (int)(p / W), &X);
+        int col = (int)(p % W), row = (int)(p / W);
+        forward_pixel(S, (uint32_t)n_slots, stride, cand + cell_of(&g, col, row) * ORC_K, W, H, col, row, &X);
         for (int c = 0; c < 3; ++c)
             rgb[p * 3 + c] = X.chat[c];
     }
 }
 
-void orc_render_fwd_pixels(const double *S, int n_slots, int stride, const uint32_t *cand, int W, int H,
+void orc_render_fwd_pixels(const double *S, int n_slots, int stride, const uint32_t *cand, int W, int H, int cell,
                            const uint32_t *pix, long n, double *rgb)
 {
+    grid g = make_grid(W, H, cell);
     for (long i = 0; i < n; ++i) {
         pix64 X;
         int col = (int)(pix[i] % (uint32_t)W), row = (int)(pix[i] / (uint32_t)W);
-        forward_pixel(S, (uint32_t)n_slots, stride, cand + (long)pix[i] * ORC_K, W, H, col, row, &X);
+        forward_pixel(S, (uint32_t)n_slots, stride, cand + cell_of(&g, col, row) * ORC_K, W, H, col, row, &X);
         for (int c = 0; c < 3; ++c)
             rgb[i * 3 + c] = X.chat[c];
     }
@@ -551,13 +599,15 @@ static void backward_pixel(long stride, int W, int H, const pix64 *X, const floa
 
 /* grad: float64 [11][stride], accumulated (+=).  loss: += sum_x ||c - t||^2. */
 void orc_render_bwd(const double *S, int n_slots, int stride, const uint32_t *cand, const float *target, int W,
-                    int H, double *grad, double *loss)
+                    int H, int cell, double *grad, double *loss)
 {
+    grid g = make_grid(W, H, cell);
     long P = (long)W * H;
     double L = 0.0;
     for (long p = 0; p < P; ++p) {
         pix64 X;
-        forward_pixel(S, (uint32_t)n_slots, stride, cand + p * ORC_K, W, H, (int)(p % W), (int)(p / W), &X);
+        int col = (int)(p % W), row = (int)(p / W);
+        forward_pixel(S, (uint32_t)n_slots, stride, cand + cell_of(&g, col, row) * ORC_K, W, H, col, row, &X);
         backward_pixel(stride, W, H, &X, target + p * 3, grad, &L);
     }
     if (loss)
@@ -610,13 +660,14 @@ void orc_adam_step(double *params, double *m, double *v, double *grad, int n_slo
  * stats: float64 [stride][8], accumulated (+=), serial in pixel order.
  */
 void orc_densify_stats(const double *S, int n_slots, int stride, const uint32_t *cand, const float *target, int W,
-                       int H, double *stats)
+                       int H, int cell, double *stats)
 {
+    grid g = make_grid(W, H, cell);
     long P = (long)W * H;
     for (long p = 0; p < P; ++p) {
         pix64 X;
         int col = (int)(p % W), row = (int)(p / W);
-        forward_pixel(S, (uint32_t)n_slots, stride, cand + p * ORC_K, W, H, col, row, &X);
+        forward_pixel(S, (uint32_t)n_slots, stride, cand + cell_of(&g, col, row) * ORC_K, W, H, col, row, &X);
         if (X.n == 0)
             continue;
         double e = 0.0;
@@ -673,9 +724,10 @@ static void sort_by_score(float *d, uint32_t *u, int n)
     }
 }
 
-void orc_jfa_seed(const float *S, int n_slots, int stride, int W, int H, uint32_t *cand)
+void orc_jfa_seed(const float *S, int n_slots, int stride, int W, int H, int cell, uint32_t *cand)
 {
-    long P = (long)W * H;
+    grid g = make_grid(W, H, cell);
+    long P = (long)g.Wm * g.Hm;
     for (long i = 0; i < P * ORC_K; ++i)
         cand[i] = ORC_NONE;
     for (uint32_t id = 0; id < (uint32_t)n_slots; ++id) {
@@ -688,17 +740,17 @@ void orc_jfa_seed(const float *S, int n_slots, int stride, int W, int H, uint32_
          * so that any finite position converts) */
         float cx = x < 0.0f ? 0.0f : (x > (float)(W - 1) ? (float)(W - 1) : x);
         float cy = y < 0.0f ? 0.0f : (y > (float)(H - 1) ? (float)(H - 1) : y);
-        int col = (int)floorf(cx), row = (int)floorf(cy);
-        float d = score_f32(S, stride, id, col, row, W, H);
+        int col = (int)floorf(cx) / g.c, row = (int)floorf(cy) / g.c; /* its cell */
+        float d = score_cell(S, stride, id, &g, col, row);
         if (!isfinite(d))
             continue;
-        uint32_t *lst = cand + ((long)row * W + col) * ORC_K;
+        uint32_t *lst = cand + ((long)row * g.Wm + col) * ORC_K;
         float dd[ORC_JFA_KEEP + 1];
         uint32_t uu[ORC_JFA_KEEP + 1];
         int n = 0;
         for (int k = 0; k < ORC_JFA_KEEP && lst[k] != ORC_NONE; ++k) {
             uu[n] = lst[k];
-            dd[n] = score_f32(S, stride, lst[k], col, row, W, H);
+            dd[n] = score_cell(S, stride, lst[k], &g, col, row);
             ++n;
         }
         uu[n] = id;
@@ -735,15 +787,15 @@ static int jfa_union_pixel(const float *S, uint32_t n_slots, const uint32_t *cin
     return nu;
 }
 
-static void jfa_pixel(const float *S, uint32_t n_slots, long stride, const uint32_t *cin, int W, int H, int col,
+static void jfa_pixel(const float *S, uint32_t n_slots, long stride, const uint32_t *cin, const grid *g, int col,
                       int row, int step, uint32_t *out)
 {
     uint32_t u[ORC_JFA_UNION];
     float d[ORC_JFA_UNION];
-    int nu = jfa_union_pixel(S, n_slots, cin, W, H, col, row, step, u);
+    int nu = jfa_union_pixel(S, n_slots, cin, g->Wm, g->Hm, col, row, step, u);
     int nv = 0;
     for (int i = 0; i < nu; ++i) {
-        float di = score_f32(S, stride, u[i], col, row, W, H);
+        float di = score_cell(S, stride, u[i], g, col, row);
         if (!isfinite(di))
             continue;
         u[nv] = u[i];
@@ -756,31 +808,34 @@ static void jfa_pixel(const float *S, uint32_t n_slots, long stride, const uint3
 }
 
 void orc_jfa_pass(const float *S, int n_slots, int stride, const uint32_t *cin, uint32_t *cout, int W, int H,
-                  int step)
+                  int cell, int step)
 {
-    long P = (long)W * H;
+    grid g = make_grid(W, H, cell);
+    long P = (long)g.Wm * g.Hm;
 #pragma omp parallel for schedule(static) num_threads(g_threads)
     for (long p = 0; p < P; ++p)
-        jfa_pixel(S, (uint32_t)n_slots, stride, cin, W, H, (int)(p % W), (int)(p / W), step, cout + p * ORC_K);
+        jfa_pixel(S, (uint32_t)n_slots, stride, cin, &g, (int)(p % g.Wm), (int)(p / g.Wm), step, cout + p * ORC_K);
 }
 
-void orc_jfa_pass_pixels(const float *S, int n_slots, int stride, const uint32_t *cin, int W, int H, int step,
-                         const uint32_t *pix, long n, uint32_t *out)
+void orc_jfa_pass_pixels(const float *S, int n_slots, int stride, const uint32_t *cin, int W, int H, int cell,
+                         int step, const uint32_t *pix, long n, uint32_t *out)
 {
+    grid g = make_grid(W, H, cell);
 #pragma omp parallel for schedule(static) num_threads(g_threads)
     for (long i = 0; i < n; ++i)
-        jfa_pixel(S, (uint32_t)n_slots, stride, cin, W, H, (int)(pix[i] % (uint32_t)W), (int)(pix[i] / (uint32_t)W),
-                  step, out + i * ORC_K);
+        jfa_pixel(S, (uint32_t)n_slots, stride, cin, &g, (int)(pix[i] % (uint32_t)g.Wm),
+                  (int)(pix[i] / (uint32_t)g.Wm), step, out + i * ORC_K);
 }
 
 /* The deduplicated union a flood pass selects from (padded to ORC_MAX_UNION). */
-void orc_jfa_union_pixels(const float *S, int n_slots, const uint32_t *cin, int W, int H, int step,
+void orc_jfa_union_pixels(const float *S, int n_slots, const uint32_t *cin, int W, int H, int cell, int step,
                           const uint32_t *pix, long n, uint32_t *out, int *count)
 {
+    grid g = make_grid(W, H, cell);
     for (long i = 0; i < n; ++i) {
         uint32_t u[ORC_JFA_UNION];
-        int nu = jfa_union_pixel(S, (uint32_t)n_slots, cin, W, H, (int)(pix[i] % (uint32_t)W),
-                                 (int)(pix[i] / (uint32_t)W), step, u);
+        int nu = jfa_union_pixel(S, (uint32_t)n_slots, cin, g.Wm, g.Hm, (int)(pix[i] % (uint32_t)g.Wm),
+                                 (int)(pix[i] / (uint32_t)g.Wm), step, u);
         for (int j = 0; j < ORC_MAX_UNION; ++j)
             out[i * ORC_MAX_UNION + j] = j < nu ? u[j] : ORC_NONE;
         count[i] = nu;

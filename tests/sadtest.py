@@ -25,13 +25,14 @@ def map_to_host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy().view(np.uint32)
 
 
-def compare_lists(orc, S, n, W, H, pix, gpu_lists, ref_lists, unions=None, counts=None):
+def compare_lists(orc, S, n, W, H, pix, gpu_lists, ref_lists, unions=None, counts=None, cell=1):
     """Compare per-pixel candidate lists.  Returns the number of pixels whose sets
     differ; every such pixel must differ only by near-ties: after re-scoring both
     lists with the oracle (float32 selection score), the sorted scores agree within
     SCORE_TOL, the GPU list holds distinct usable IDs from the candidate union, and
     the sentinel pads the tail.  GPU lists must also be stored in ascending score
-    order up to near-ties."""
+    order up to near-ties.  `pix` indexes map entries (cells of `cell` x `cell`
+    pixels; single pixels when cell is 1)."""
     gpu_lists = np.asarray(gpu_lists).reshape(-1, 8)
     ref_lists = np.asarray(ref_lists).reshape(-1, 8)
     pix = np.asarray(pix, dtype=np.uint32).ravel()
@@ -39,7 +40,7 @@ def compare_lists(orc, S, n, W, H, pix, gpu_lists, ref_lists, unions=None, count
     valid = gpu_lists != NONE
     nval = valid.sum(1)
     assert (valid == (np.arange(8)[None, :] < nval[:, None])).all(), "GPU lists must be sentinel-padded at the tail"
-    sc = orc.score_pairs(S, n, W, H, np.repeat(pix, 8), gpu_lists.ravel()).reshape(-1, 8)
+    sc = orc.score_pairs(S, n, W, H, np.repeat(pix, 8), gpu_lists.ravel(), cell).reshape(-1, 8)
     assert np.isfinite(sc[valid]).all(), "GPU list holds an unusable ID"
     sc_m = np.where(valid, sc, np.inf)
     dif = np.diff(sc_m, axis=1)
@@ -48,7 +49,7 @@ def compare_lists(orc, S, n, W, H, pix, gpu_lists, ref_lists, unions=None, count
     mism = np.array([set(a) != set(b) for a, b in zip(gpu_lists, ref_lists)])
     idx = np.nonzero(mism)[0]
     if idx.size:
-        rsc = orc.score_pairs(S, n, W, H, np.repeat(pix[idx], 8), ref_lists[idx].ravel()).reshape(-1, 8)
+        rsc = orc.score_pairs(S, n, W, H, np.repeat(pix[idx], 8), ref_lists[idx].ravel(), cell).reshape(-1, 8)
         for j, i in enumerate(idx):
             g = gpu_lists[i][gpu_lists[i] != NONE]
             assert len(set(g.tolist())) == g.size, f"duplicate IDs at pixel {pix[i]}"
