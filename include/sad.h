@@ -31,10 +31,19 @@
  *         [PRESS] 5: x, y, log_tau, r, R, G, B, dir_x, dir_y, a.  Positions and r
  *         are in pixels; tau = exp(log_tau).  Slots [0, n_slots) are in use; a slot
  *         whose x < 0 is inactive and every kernel ignores it ([SUM] B.2, B.5).
- * cand  : uint32 [H][W][SAD_K] -- per-pixel candidate site IDs ([SUM] B.2 keeps
- *         K = 8 IDs per pixel in two 4-channel textures; here one 32-byte record
- *         per pixel), SAD_INVALID marks an empty entry.  16-byte aligned.  Lists
- *         written by this library hold distinct IDs in ascending (d, ID) order.
+ * cand  : uint32 [Hm][Wm][SAD_K] -- the candidate map: site IDs per map entry
+ *         ([SUM] B.2 keeps K = 8 IDs per entry in two 4-channel textures; here one
+ *         32-byte record per entry), SAD_INVALID marks an empty entry.  16-byte
+ *         aligned.  Lists written by this library hold distinct IDs in ascending
+ *         (d, ID) order.
+ *         Grid ([SUM] B.3 "Candidate field"): the entries that take `cell` = c
+ *         cover c x c pixels, Wm = ceil(W/c), Hm = ceil(H/c); pixel (col, row) is
+ *         rendered with the list of entry (col/c, row/c) (integer division), and an
+ *         entry's list is selected at its centred UV, ((cx + 1/2) W/Wm,
+ *         (cy + 1/2) H/Hm) px (float32: W/Wm and H/Hm rounded once, then one
+ *         add and one multiply).  c = 1 is the per-pixel map, [H][W][8], evaluated
+ *         at pixel centres.  1 <= c <= 65535; every call that reads or writes the
+ *         map takes the same c.
  * images: float [H][W][3] (RGB, linear).
  * grad  : float [stride][SAD_GRAD_LD] -- one 64-byte record per site: the ten
  *         gradients in site order at [0,10), the removal delta at [10] ([SUM] B.4:
@@ -56,7 +65,7 @@
  *         sites").  A slot with x < 0 stays inactive.  16-byte aligned.  It is a
  *         cache the caller keeps in step with `sites`: recompute it after any
  *         change made outside sad_adam_step.
- * Pixel (col,row) is evaluated at (col+0.5, row+0.5) px ([SUM] B.3 evaluates at
+ * Pixel (col,row) is rendered at (col+0.5, row+0.5) px ([SUM] B.3 evaluates at
  * centred cells).  Limits: 1 <= W, H <= 65535 (W or H = 0 is an empty image: a
  * no-op returning SAD_OK after the scalar arguments are checked; its pointers
  * may then be NULL); 0 <= n_slots <= stride.
@@ -75,7 +84,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 2
+#define SAD_ABI_VERSION 3
 #define SAD_K 8
 #define SAD_INVALID 0xffffffffu
 #define SAD_NPARAM 10
@@ -136,10 +145,12 @@ int sad_site_records(const float *sites, int n_slots, int stride, float *rec, vo
  * random set of global IDs; [SUM] B.3 packs the pass index (low 16 bits) and the
  * jump (high 16 bits) into one word that, with the pixel ID, seeds xorshift.
  *
- * For every pixel x the candidates are: its own list in cand_in, the lists of the
- * pixels x +- (jump, 0) and x +- (0, jump) that lie inside the image, and
- * `n_inject` IDs drawn as follows (identical on every implementation):
- *   pw = (jump << 16) | (pass_index & 0xffff);  pix = row*W + col;
+ * For every map entry x (a pixel when cell = 1; x, jump and the neighbours are in
+ * map entries, scores at x's centred UV) the candidates are: its own list in
+ * cand_in, the lists of the entries x +- (jump, 0) and x +- (0, jump) that lie
+ * inside the map, and `n_inject` IDs drawn as follows (identical on every
+ * implementation):
+ *   pw = (jump << 16) | (pass_index & 0xffff);  pix = row*Wm + col;
  *   h  = pcg(pcg(pcg(seed) ^ pw) ^ pix)   (pcg: Jarzynski & Olano, JCGT 2020)
  *   x  = h ? h : 0x9e3779b9;  repeat n_inject times: x = xorshift32(x) (13,17,5);
  *   id = (uint32)(((uint64)x * n_slots) >> 32).
@@ -149,63 +160,66 @@ int sad_site_records(const float *sites, int n_slots, int stride, float *rec, vo
  * The host chooses the schedule: jumps B/2, B/4, ..., 1 then 1 ([SUM] section 4).
  *
  *   rec       device, [n_slots][16] float site records, read-only
- *   cand_in   device, [H][W][8] uint32, read-only, 16-byte aligned
- *   cand_out  device, [H][W][8] uint32, written; must not overlap cand_in
+ *   cand_in   device, [Hm][Wm][8] uint32, read-only, 16-byte aligned
+ *   cand_out  device, [Hm][Wm][8] uint32, written; must not overlap cand_in
  *   jump      1..65535;  n_inject 0..SAD_MAX_INJECT
- * Errors: SAD_ERR_ARG (bad sizes, jump, n_inject, NULL, overlapping maps),
+ * Errors: SAD_ERR_ARG (bad sizes, cell, jump, n_inject, NULL, overlapping maps),
  *         SAD_ERR_ALIGN (a pointer not 16-byte aligned), SAD_ERR_DEVICE.
  */
 int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
-                       int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream);
+                       int cell, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream);
 
 /*
  * sad_jfa_seed -- seed pass of the optional jump-flood prepass ([SUM] B.3 "Jump
  * schedule": a seed pass, then flood passes over 3x3 neighbourhoods that keep the
  * four closest sites; meant for (re)initialisation and after large edits).
- * Every active site with a finite position is entered in the list of the pixel
- * that contains it (floor of its position, clamped into the image); a pixel keeps
- * at most four, the best by (d, ID) at its centre, in entries 0..3 (ascending);
- * all other entries are SAD_INVALID.  The whole map is written.
- *   rec device [n_slots][16] read-only; cand device [H][W][8], written.
+ * Every active site with a finite position is entered in the list of the map
+ * entry of the pixel that contains it (floor of its position, clamped into the
+ * image); an entry keeps at most four, the best by (d, ID) at its centred UV, in
+ * places 0..3 (ascending); all other places are SAD_INVALID.  The whole map is
+ * written.
+ *   rec device [n_slots][16] read-only; cand device [Hm][Wm][8], written.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_jfa_seed(const float *rec, int n_slots, uint32_t *cand, int W, int H, void *stream);
+int sad_jfa_seed(const float *rec, int n_slots, uint32_t *cand, int W, int H, int cell, void *stream);
 
 /*
  * sad_jfa_pass -- one flood pass of the prepass with step `step` ([SUM] B.3):
- * per pixel, the union of entries 0..3 of the lists at offsets {-step, 0,
- * step}^2 that lie inside the image, without sentinels, IDs >= n_slots, inactive
- * sites, non-finite scores and duplicates; the four best by (d, ID) go to entries
- * 0..3 (ascending), SAD_INVALID to 4..7.  Jacobi: reads cand_in, writes cand_out.
- * The prepass runs the steps B/2, B/4, ..., 1 (B = 2^ceil(log2 max(W,H))), i.e.
- * ceil(log2 max(W,H)) passes, after sad_jfa_seed; sad_topk_propagate then fills
- * the lists to K.
- *   step in [1, 65535]; cand_in, cand_out device [H][W][8], not overlapping.
+ * per map entry, the union of places 0..3 of the lists at offsets {-step, 0,
+ * step}^2 (in entries) that lie inside the map, without sentinels, IDs >=
+ * n_slots, inactive sites, non-finite scores and duplicates; the four best by
+ * (d, ID) at the entry's centred UV go to places 0..3 (ascending), SAD_INVALID to
+ * 4..7.  Jacobi: reads cand_in, writes cand_out.  The prepass runs the steps B/2,
+ * B/4, ..., 1 (B = 2^ceil(log2 max(Wm,Hm))), i.e. ceil(log2 max(Wm,Hm)) passes,
+ * after sad_jfa_seed; sad_topk_propagate then fills the lists to K.
+ *   step in [1, 65535]; cand_in, cand_out device [Hm][Wm][8], not overlapping.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_jfa_pass(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H, int step,
-                 void *stream);
+int sad_jfa_pass(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H, int cell,
+                 int step, void *stream);
 
 /*
  * sad_topk_exact -- the exact top-K map by brute force over every slot: the list
  * that propagation approximates ([NOTE] design 3; [SUM] section 4 "Candidate
  * maintenance").  Used to (re)initialise a map and to measure recall.  Cost
- * O(W*H*n_slots).  Same output convention as sad_topk_propagate.
- *   rec device [n_slots][16] read-only;  cand_out device [H][W][8], written.
+ * O(Wm*Hm*n_slots).  Same output convention as sad_topk_propagate.
+ *   rec device [n_slots][16] read-only;  cand_out device [Hm][Wm][8], written.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_topk_exact(const float *rec, int n_slots, uint32_t *cand_out, int W, int H, void *stream);
+int sad_topk_exact(const float *rec, int n_slots, uint32_t *cand_out, int W, int H, int cell, void *stream);
 
 /*
- * sad_render_fwd -- the temperature-softmax blend of each pixel's list.
+ * sad_render_fwd -- the temperature-softmax blend of each pixel's list (the list
+ * of its map entry), scored at the pixel's centre.
  * [NOTE] design 2, [PROJ] "Method": l_i = -tau_i d_i, w = softmax over the list,
  * c(x) = sum_i w_i c_i; max-subtracted, invalid IDs skipped, non-finite entries
  * skipped ([SUM] B.4).  A pixel with no usable entry renders (0,0,0).
- *   rec device [n_slots][16] read-only; cand device [H][W][8] read-only;
+ *   rec device [n_slots][16] read-only; cand device [Hm][Wm][8] read-only;
  *   out_rgb device [H][W][3] float, written.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, int H, float *out_rgb, void *stream);
+int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, int H, int cell, float *out_rgb,
+                   void *stream);
 
 /*
  * sad_render_bwd -- hand-derived gradients of L = sum_x ||c(x) - t(x)||^2 with
@@ -221,8 +235,8 @@ int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, i
  * atomic per site and accumulator per tile; an entry that finds no slot goes
  * straight to global atomics ([SUM] section 5, B.4).  Float atomics make the
  * summation order, hence the last bits, vary from run to run.
- *   rec device [n_slots][16] read-only; target device [H][W][3] read-only;
- *   grad device [>= n_slots][16] float, +=;
+ *   rec device [n_slots][16] read-only; cand device [Hm][Wm][8] read-only;
+ *   target device [H][W][3] read-only; grad device [>= n_slots][16] float, +=;
  *   loss_sum device float[SAD_LOSS_SLOTS] or NULL: each tile adds its sum of
  *   ||c - t||^2 to one of the SAD_LOSS_SLOTS entries (spread by tile, because
  *   a thousand atomics on one address serialise); the loss is the entries' sum;
@@ -233,7 +247,7 @@ int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, i
  * step; accumulator 10 keeps accumulating until the caller resets it.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN (cand or grad not 16-byte aligned), SAD_ERR_DEVICE.
  */
-int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
+int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H, int cell,
                    float *grad, float *loss_sum, float *out_rgb, void *stream);
 
 /*
@@ -244,12 +258,12 @@ int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const fl
  * site's record of `stats`:
  *   [0] sum w   [1] sum w e   [2] sum w e dx   [3] sum w e dy
  *   [4] sum w e dx^2   [5] sum w e dx dy   [6] sum w e dy^2   [7] unused
- *   rec device [n_slots][16]; cand device [H][W][8]; target device [H][W][3];
+ *   rec device [n_slots][16]; cand device [Hm][Wm][8]; target device [H][W][3];
  *   stats device [>= n_slots][SAD_STAT_LD] float, 16-byte aligned, +=.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
 int sad_densify_stats(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
-                      float *stats, void *stream);
+                      int cell, float *stats, void *stream);
 
 /*
  * sad_densify_prune -- budget control on the HOST ([SUM] B.5; [NOTE] design 4;
@@ -273,17 +287,18 @@ int sad_densify_stats(const float *rec, int n_slots, const uint32_t *cand, const
  *     log tau += log(shrink), other fields copied, m = v = 0 ([SUM] B.5).  Child A
  *     keeps the parent's slot; child B takes the lowest inactive slot below
  *     *n_slots, else slot *n_slots (then *n_slots grows) while below capacity.
- *     Child B's ID is written into the last entry of the lists of the pixel that
- *     contains it and of its 4 neighbours, so the next propagation pass sees it.
+ *     Child B's ID is written into the last place of the list of the map entry
+ *     that contains it and of its 4 neighbour entries, so the next propagation
+ *     pass sees it.
  *  sites [10][stride], m/v [10][stride], stats [stride][8], removal [stride]
  *  (the removal-delta accumulator, e.g. column 10 of the gradient records),
- *  cand [H][W][8], target [H][W][3]; *n_slots in/out; n_split/n_pruned (out,
+ *  cand [Hm][Wm][8], target [H][W][3]; *n_slots in/out; n_split/n_pruned (out,
  *  may be NULL) receive the numbers of splits and prunes done.
  * Errors: SAD_ERR_ARG; SAD_ERR_CAPACITY when some selected sites could not be
  *  split for want of a free slot (everything that fitted is done).
  */
 int sad_densify_prune(float *sites, float *m, float *v, int stride, int capacity, int *n_slots, const float *stats,
-                      const float *removal, uint32_t *cand, int W, int H, const float *target,
+                      const float *removal, uint32_t *cand, int W, int H, int cell, const float *target,
                       const sad_budget_cfg *cfg, int *n_split, int *n_pruned);
 
 /*

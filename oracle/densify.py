@@ -35,10 +35,13 @@ def _pix(x, n):
 
 
 def densify_prune(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, target, split_frac=0.05,
-                  prune_frac=0.05, alpha=0.5, min_mass=1.0, shrink=0.85):
-    """In place on float32 sites/m/v [10][stride] and uint32 cand [H][W][8].
+                  prune_frac=0.05, alpha=0.5, min_mass=1.0, shrink=0.85, cell=1):
+    """In place on float32 sites/m/v [10][stride] and uint32 cand [Hm][Wm][8]
+    (cells of `cell` x `cell` pixels, Wm = ceil(W / cell); per pixel when 1).
 
     Returns (n_slots, n_split, n_pruned, short_of_slots)."""
+    Wm, Hm = -(-W // cell), -(-H // cell)
+    assert cand.shape == (Hm, Wm, 8)
     stride = sites.shape[1]
     active = [i for i in range(n_slots) if not (sites[X, i] < 0)]
     A = len(active)
@@ -111,10 +114,11 @@ def densify_prune(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, ta
             sites[R, slot] = np.float32(parent[R]) * np.float32(shrink)
             sites[LOGTAU, slot] = np.float32(parent[LOGTAU]) + np.float32(math.log(np.float32(shrink)))
             sites[CR:CB + 1, slot] = target[_pix(y, H), _pix(x, W)]
-        bc, br = _pix(float(sites[X, b]), W), _pix(float(sites[Y, b]), H)
+        # child B enters the list of its pixel's map entry and of the 4 neighbour entries
+        bc, br = _pix(float(sites[X, b]), W) // cell, _pix(float(sites[Y, b]), H) // cell
         for dc, dr in ((0, 0), (-1, 0), (1, 0), (0, -1), (0, 1)):
             c, r = bc + dc, br + dr
-            if 0 <= c < W and 0 <= r < H:
+            if 0 <= c < Wm and 0 <= r < Hm:
                 cand[r, c, 7] = b
         done += 1
     return count, done, pruned, short

@@ -98,22 +98,22 @@ def lib() -> ctypes.CDLL:
         L.sad_site_records.restype = i32
         L.sad_site_records.argtypes = [fp, i32, i32, fp, vp]
         L.sad_topk_propagate.restype = i32
-        L.sad_topk_propagate.argtypes = [fp, i32, vp, vp, i32, i32, i32, u32, u32, i32, vp]
+        L.sad_topk_propagate.argtypes = [fp, i32, vp, vp, i32, i32, i32, i32, u32, u32, i32, vp]
         L.sad_topk_exact.restype = i32
-        L.sad_topk_exact.argtypes = [fp, i32, vp, i32, i32, vp]
+        L.sad_topk_exact.argtypes = [fp, i32, vp, i32, i32, i32, vp]
         L.sad_render_fwd.restype = i32
-        L.sad_render_fwd.argtypes = [fp, i32, vp, i32, i32, fp, vp]
+        L.sad_render_fwd.argtypes = [fp, i32, vp, i32, i32, i32, fp, vp]
         L.sad_render_bwd.restype = i32
-        L.sad_render_bwd.argtypes = [fp, i32, vp, fp, i32, i32, fp, fp, fp, vp]
+        L.sad_render_bwd.argtypes = [fp, i32, vp, fp, i32, i32, i32, fp, fp, fp, vp]
         L.sad_jfa_seed.restype = i32
-        L.sad_jfa_seed.argtypes = [vp, i32, vp, i32, i32, vp]
+        L.sad_jfa_seed.argtypes = [vp, i32, vp, i32, i32, i32, vp]
         L.sad_jfa_pass.restype = i32
-        L.sad_jfa_pass.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp]
+        L.sad_jfa_pass.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp]
         L.sad_densify_stats.restype = i32
-        L.sad_densify_stats.argtypes = [fp, i32, vp, fp, i32, i32, fp, vp]
+        L.sad_densify_stats.argtypes = [fp, i32, vp, fp, i32, i32, i32, fp, vp]
         ip = ctypes.POINTER(ctypes.c_int)
         L.sad_densify_prune.restype = i32
-        L.sad_densify_prune.argtypes = [fp, fp, fp, i32, i32, ip, fp, fp, vp, i32, i32, fp,
+        L.sad_densify_prune.argtypes = [fp, fp, fp, i32, i32, ip, fp, fp, vp, i32, i32, i32, fp,
                                         ctypes.POINTER(BudgetCfg), ip, ip]
         L.sad_adam_step.restype = i32
         L.sad_adam_step.argtypes = [fp, fp, fp, fp, fp, i32, i32, i32, i32, i32, i32, ctypes.POINTER(AdamCfg), vp]
@@ -185,33 +185,43 @@ def site_records(sites, n_slots, rec, stream=None):
     _check("sad_site_records", lib().sad_site_records(sp, n_slots, stride, r, _stream(stream)))
 
 
-def topk_propagate(rec, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed, n_inject, stream=None):
+def map_shape(W: int, H: int, cell: int = 1) -> tuple:
+    """Shape of the candidate map of a W x H image with cells of `cell` x `cell`
+    pixels: (ceil(H / cell), ceil(W / cell), 8)."""
+    if cell < 1:
+        raise ValueError("cell must be >= 1")
+    return (-(-H // cell), -(-W // cell), K)
+
+
+def topk_propagate(rec, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed, n_inject, stream=None, cell=1):
     """One propagation pass: cand_in -> cand_out (see sad_topk_propagate)."""
     g = _rec(rec, n_slots)
-    a = _dev(cand_in, "cand_in", _U32, (H, W, K))
-    b = _dev(cand_out, "cand_out", _U32, (H, W, K))
-    _check("sad_topk_propagate", lib().sad_topk_propagate(g, n_slots, a, b, W, H, jump, pass_index & 0xFFFFFFFF,
+    a = _dev(cand_in, "cand_in", _U32, map_shape(W, H, cell))
+    b = _dev(cand_out, "cand_out", _U32, map_shape(W, H, cell))
+    _check("sad_topk_propagate", lib().sad_topk_propagate(g, n_slots, a, b, W, H, cell, jump, pass_index & 0xFFFFFFFF,
                                                           seed & 0xFFFFFFFF, n_inject, _stream(stream)))
 
 
-def jfa_seed(rec, n_slots, cand, W, H, stream=None):
+def jfa_seed(rec, n_slots, cand, W, H, stream=None, cell=1):
     """Seed pass of the jump-flood prepass (see sad_jfa_seed)."""
     g = _rec(rec, n_slots)
-    c = _dev(cand, "cand", _U32, (H, W, K))
-    _check("sad_jfa_seed", lib().sad_jfa_seed(g, n_slots, c, W, H, _stream(stream)))
+    c = _dev(cand, "cand", _U32, map_shape(W, H, cell))
+    _check("sad_jfa_seed", lib().sad_jfa_seed(g, n_slots, c, W, H, cell, _stream(stream)))
 
 
-def jfa_pass(rec, n_slots, cand_in, cand_out, W, H, step, stream=None):
+def jfa_pass(rec, n_slots, cand_in, cand_out, W, H, step, stream=None, cell=1):
     """One flood pass of the jump-flood prepass: cand_in -> cand_out (see sad_jfa_pass)."""
     g = _rec(rec, n_slots)
-    a = _dev(cand_in, "cand_in", _U32, (H, W, K))
-    b = _dev(cand_out, "cand_out", _U32, (H, W, K))
-    _check("sad_jfa_pass", lib().sad_jfa_pass(g, n_slots, a, b, W, H, step, _stream(stream)))
+    a = _dev(cand_in, "cand_in", _U32, map_shape(W, H, cell))
+    b = _dev(cand_out, "cand_out", _U32, map_shape(W, H, cell))
+    _check("sad_jfa_pass", lib().sad_jfa_pass(g, n_slots, a, b, W, H, cell, step, _stream(stream)))
 
 
-def jfa_steps(W: int, H: int) -> list:
-    """The prepass's flood steps B/2, ..., 1 with B = 2^ceil(log2 max(W, H))."""
-    B = 1 << max(0, (max(W, H) - 1).bit_length())
+def jfa_steps(W: int, H: int, cell: int = 1) -> list:
+    """The prepass's flood steps B/2, ..., 1 with B = 2^ceil(log2 max(Wm, Hm)),
+    counted in map entries."""
+    Hm, Wm, _ = map_shape(W, H, cell)
+    B = 1 << max(0, (max(Wm, Hm) - 1).bit_length())
     out, k = [], B // 2
     while k >= 1:
         out.append(k)
@@ -219,29 +229,29 @@ def jfa_steps(W: int, H: int) -> list:
     return out
 
 
-def jfa_prepass(rec, n_slots, a, b, W, H, stream=None):
+def jfa_prepass(rec, n_slots, a, b, W, H, stream=None, cell=1):
     """Seed pass into `a`, then the flood passes ping-ponging between `a` and `b`;
-    returns the map that holds the result (four closest per pixel)."""
-    jfa_seed(rec, n_slots, a, W, H, stream)
-    for k in jfa_steps(W, H):
-        jfa_pass(rec, n_slots, a, b, W, H, k, stream)
+    returns the map that holds the result (four closest per entry)."""
+    jfa_seed(rec, n_slots, a, W, H, stream, cell)
+    for k in jfa_steps(W, H, cell):
+        jfa_pass(rec, n_slots, a, b, W, H, k, stream, cell)
         a, b = b, a
     return a
 
 
-def topk_exact(rec, n_slots, cand_out, W, H, stream=None):
+def topk_exact(rec, n_slots, cand_out, W, H, stream=None, cell=1):
     """Brute-force exact top-K map (see sad_topk_exact)."""
     g = _rec(rec, n_slots)
-    b = _dev(cand_out, "cand_out", _U32, (H, W, K))
-    _check("sad_topk_exact", lib().sad_topk_exact(g, n_slots, b, W, H, _stream(stream)))
+    b = _dev(cand_out, "cand_out", _U32, map_shape(W, H, cell))
+    _check("sad_topk_exact", lib().sad_topk_exact(g, n_slots, b, W, H, cell, _stream(stream)))
 
 
-def render_fwd(rec, n_slots, cand, W, H, out_rgb, stream=None):
+def render_fwd(rec, n_slots, cand, W, H, out_rgb, stream=None, cell=1):
     """Temperature-softmax render of each pixel's list (see sad_render_fwd)."""
     r = _rec(rec, n_slots)
-    c = _dev(cand, "cand", _U32, (H, W, K))
+    c = _dev(cand, "cand", _U32, map_shape(W, H, cell))
     o = _dev(out_rgb, "out_rgb", _F32, (H, W, 3))
-    _check("sad_render_fwd", lib().sad_render_fwd(r, n_slots, c, W, H, o, _stream(stream)))
+    _check("sad_render_fwd", lib().sad_render_fwd(r, n_slots, c, W, H, cell, o, _stream(stream)))
 
 
 def new_loss(device) -> torch.Tensor:
@@ -250,11 +260,11 @@ def new_loss(device) -> torch.Tensor:
     return torch.zeros(LOSS_SLOTS, dtype=torch.float32, device=device)
 
 
-def render_bwd(rec, n_slots, cand, target, W, H, grad, loss_sum=None, out_rgb=None, stream=None):
+def render_bwd(rec, n_slots, cand, target, W, H, grad, loss_sum=None, out_rgb=None, stream=None, cell=1):
     """Gradients of the squared error, accumulated into grad; optionally also the
     rendered image (see sad_render_bwd)."""
     r = _rec(rec, n_slots)
-    c = _dev(cand, "cand", _U32, (H, W, K))
+    c = _dev(cand, "cand", _U32, map_shape(W, H, cell))
     t = _dev(target, "target", _F32, (H, W, 3))
     if grad.dim() != 2 or grad.shape[1] != GRAD_LD or grad.shape[0] < n_slots:
         raise ValueError("grad must be float32 [>= n_slots][16]")
@@ -263,7 +273,7 @@ def render_bwd(rec, n_slots, cand, target, W, H, grad, loss_sum=None, out_rgb=No
         raise ValueError(f"loss_sum must hold {LOSS_SLOTS} partial sums (see new_loss)")
     ls = _dev(loss_sum, "loss_sum", _F32) if loss_sum is not None else None
     o = _dev(out_rgb, "out_rgb", _F32, (H, W, 3)) if out_rgb is not None else None
-    _check("sad_render_bwd", lib().sad_render_bwd(r, n_slots, c, t, W, H, g, ls, o, _stream(stream)))
+    _check("sad_render_bwd", lib().sad_render_bwd(r, n_slots, c, t, W, H, cell, g, ls, o, _stream(stream)))
 
 
 @dataclasses.dataclass
@@ -295,16 +305,16 @@ def adam_step(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamConfig 
                                                 ctypes.byref(c), _stream(stream)))
 
 
-def densify_stats(rec, n_slots, cand, target, W, H, stats, stream=None):
+def densify_stats(rec, n_slots, cand, target, W, H, stats, stream=None, cell=1):
     """Per-site mass, energy and error-weighted moments, accumulated into stats
     [>= n_slots][8] (see sad_densify_stats)."""
     r = _rec(rec, n_slots)
-    c = _dev(cand, "cand", _U32, (H, W, K))
+    c = _dev(cand, "cand", _U32, map_shape(W, H, cell))
     t = _dev(target, "target", _F32, (H, W, 3))
     if stats.dim() != 2 or stats.shape[1] != STAT_LD or stats.shape[0] < n_slots:
         raise ValueError("stats must be float32 [>= n_slots][8]")
     st = _dev(stats, "stats", _F32)
-    _check("sad_densify_stats", lib().sad_densify_stats(r, n_slots, c, t, W, H, st, _stream(stream)))
+    _check("sad_densify_stats", lib().sad_densify_stats(r, n_slots, c, t, W, H, cell, st, _stream(stream)))
 
 
 @dataclasses.dataclass
@@ -321,11 +331,11 @@ class BudgetConfig:
 
 
 def densify_prune(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, target,
-                  cfg: BudgetConfig | None = None):
+                  cfg: BudgetConfig | None = None, cell=1):
     """Host-side split/prune on numpy arrays, in place (see sad_densify_prune).
 
     sites, m, v: float32 [10][stride]; stats float32 [stride][8]; removal float32
-    [stride]; cand uint32 [H][W][8]; target float32 [H][W][3].  Returns
+    [stride]; cand uint32 [Hm][Wm][8] (map_shape); target float32 [H][W][3].  Returns
     (new n_slots, n_split, n_pruned, status) -- status is 0 or SAD_ERR_CAPACITY."""
     import numpy as np
     for name, a, dt in (("sites", sites, np.float32), ("m", m, np.float32), ("v", v, np.float32),
@@ -335,7 +345,7 @@ def densify_prune(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, ta
             raise TypeError(f"{name} must be a C-contiguous numpy {np.dtype(dt).name} array")
     stride = sites.shape[1]
     if m.shape != sites.shape or v.shape != sites.shape or stats.shape != (stride, STAT_LD) or \
-            removal.shape != (stride,) or cand.shape != (H, W, K) or target.shape != (H, W, 3):
+            removal.shape != (stride,) or cand.shape != map_shape(W, H, cell) or target.shape != (H, W, 3):
         raise ValueError("densify_prune: inconsistent shapes")
     ns = ctypes.c_int(n_slots)
     nsp = ctypes.c_int(0)
@@ -343,16 +353,19 @@ def densify_prune(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, ta
     c = (cfg or BudgetConfig()).to_c()
     p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
     rc = lib().sad_densify_prune(p(sites), p(m), p(v), stride, capacity, ctypes.byref(ns), p(stats), p(removal),
-                                 p(cand), W, H, p(target), ctypes.byref(c), ctypes.byref(nsp), ctypes.byref(npr))
+                                 p(cand), W, H, cell, p(target), ctypes.byref(c), ctypes.byref(nsp),
+                                 ctypes.byref(npr))
     if rc not in (SAD_OK, SAD_ERR_CAPACITY):
         raise SadError("sad_densify_prune", rc)
     return ns.value, nsp.value, npr.value, rc
 
 
-def jump_schedule(W: int, H: int, n: int) -> list:
-    """Jumps for n passes: B/2, B/4, ..., 1, then 1, with B = 2^ceil(log2 max(W,H))
-    (paperlayer.ai summary, section 4 "Candidate maintenance"; B is our reading)."""
-    B = 1 << max(0, (max(W, H) - 1).bit_length())
+def jump_schedule(W: int, H: int, n: int, cell: int = 1) -> list:
+    """Jumps for n passes: B/2, B/4, ..., 1, then 1, with B = 2^ceil(log2 max(Wm,Hm))
+    in map entries (paperlayer.ai summary, section 4 "Candidate maintenance"; B is
+    our reading)."""
+    Hm, Wm, _ = map_shape(W, H, cell)
+    B = 1 << max(0, (max(Wm, Hm) - 1).bit_length())
     out, k = [], B // 2
     for _ in range(n):
         out.append(max(k, 1))
@@ -370,9 +383,9 @@ def grad_planes(grad: torch.Tensor):
     return grad[:, :NACC].t()
 
 
-def new_map(W: int, H: int, device="cuda") -> torch.Tensor:
-    """An all-sentinel candidate map (uint32 [H][W][8] held as int32)."""
-    return torch.full((H, W, K), -1, dtype=torch.int32, device=device)
+def new_map(W: int, H: int, device="cuda", cell: int = 1) -> torch.Tensor:
+    """An all-sentinel candidate map (uint32 [Hm][Wm][8] held as int32)."""
+    return torch.full(map_shape(W, H, cell), -1, dtype=torch.int32, device=device)
 
 
 class Fitter:
@@ -387,15 +400,18 @@ class Fitter:
     B.3: warm-up first, then updates; both the update frequency and the passes per
     update are exposed, and 8-16 iterations between updates left the final PSNR
     unchanged there).  The pass counter drives the jump schedule and the
-    injection's pass index."""
+    injection's pass index.  `cell` > 1 keeps the candidate map on the downscaled
+    grid of B.3 "Candidate field" (ceil(W/cell) x ceil(H/cell) lists)."""
 
     def __init__(self, sites: torch.Tensor, n_slots: int, target: torch.Tensor, W: int, H: int,
                  n_inject: int = 4, seed: int = 4, adam: AdamConfig | None = None, cand: torch.Tensor | None = None,
-                 refresh_every: int = 1, passes_per_refresh: int = 1):
+                 refresh_every: int = 1, passes_per_refresh: int = 1, cell: int = 1):
         if refresh_every < 1 or passes_per_refresh < 0:
             raise ValueError("refresh_every >= 1 and passes_per_refresh >= 0")
         dev = sites.device
         self.W, self.H, self.n_slots, self.n_inject, self.seed = W, H, n_slots, n_inject, seed
+        self.cell = cell
+        self.Hm, self.Wm, _ = map_shape(W, H, cell)
         self.refresh_every, self.passes_per_refresh = refresh_every, passes_per_refresh
         self.passes = 0
         self.warm_end = 0  # first iteration after the warm-up passes
@@ -407,7 +423,7 @@ class Fitter:
         self.grad = torch.zeros((stride, GRAD_LD), dtype=torch.float32, device=dev)
         self.rec = new_records(stride, dev)
         site_records(sites, n_slots, self.rec)
-        self.maps = [cand if cand is not None else new_map(W, H, dev), new_map(W, H, dev)]
+        self.maps = [cand if cand is not None else new_map(W, H, dev, cell), new_map(W, H, dev, cell)]
         self.cur = 0
         self.rgb = torch.empty((H, W, 3), dtype=torch.float32, device=dev)
         self.loss = new_loss(dev)
@@ -420,7 +436,7 @@ class Fitter:
         return self.maps[self.cur]
 
     def jump_at(self, it: int) -> int:
-        B = 1 << max(0, (max(self.W, self.H) - 1).bit_length())
+        B = 1 << max(0, (max(self.Wm, self.Hm) - 1).bit_length())
         return max(1, (B // 2) >> it) if it < 64 else 1
 
     def refresh_records(self, stream=None):
@@ -429,14 +445,14 @@ class Fitter:
 
     def propagate(self, jump: int, pass_index: int, stream=None):
         topk_propagate(self.rec, self.n_slots, self.maps[self.cur], self.maps[1 - self.cur], self.W, self.H,
-                       jump, pass_index, self.seed, self.n_inject, stream)
+                       jump, pass_index, self.seed, self.n_inject, stream, self.cell)
         self.cur = 1 - self.cur
 
     def step(self, stream=None):
         """One iteration (the hot path): propagate, render forward and backward
         (one fused launch that writes the image and the gradients), Adam."""
         it = self.it
-        warm = (max(self.W, self.H) - 1).bit_length()  # log2 B passes with jumps B/2 .. 1
+        warm = (max(self.Wm, self.Hm) - 1).bit_length()  # log2 B passes with jumps B/2 .. 1
         if self.passes < warm:
             self.propagate(self.jump_at(self.passes), self.passes, stream)
             self.passes += 1
@@ -446,7 +462,7 @@ class Fitter:
                 self.propagate(self.jump_at(self.passes), self.passes, stream)
                 self.passes += 1
         render_bwd(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, self.grad, self.loss, self.rgb,
-                   stream)
+                   stream, self.cell)
         adam_step(self.sites, self.m, self.v, self.grad, self.n_slots, it + 1, self.W * self.H, self.W, self.H,
                   self.adam, self.rec, stream)
         self.it += 1
@@ -460,7 +476,7 @@ class Fitter:
         dev = self.sites.device
         stride = self.sites.shape[1]
         stats = torch.zeros((stride, STAT_LD), dtype=torch.float32, device=dev)
-        densify_stats(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, stats, stream)
+        densify_stats(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, stats, stream, self.cell)
         torch.cuda.synchronize(dev)
         sites = self.sites.cpu().numpy()
         m = self.m.cpu().numpy()
@@ -468,7 +484,7 @@ class Fitter:
         cand = self.cand.cpu().numpy().view(np.uint32)
         removal = np.ascontiguousarray(self.grad[:, NACC - 1].cpu().numpy())
         n, n_split, n_pruned, _ = densify_prune(sites, m, v, self.n_slots, stride, stats.cpu().numpy(), removal,
-                                                cand, self.W, self.H, self.target.cpu().numpy(), cfg)
+                                                cand, self.W, self.H, self.target.cpu().numpy(), cfg, self.cell)
         self.sites.copy_(torch.from_numpy(sites))
         self.m.copy_(torch.from_numpy(m))
         self.v.copy_(torch.from_numpy(v))

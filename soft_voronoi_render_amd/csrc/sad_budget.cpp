@@ -55,7 +55,7 @@ void principal_axis(double a, double b, double c, double &lam, double &ex, doubl
 }  // namespace
 
 extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, int capacity, int *n_slots,
-                                 const float *stats, const float *removal, uint32_t *cand, int W, int H,
+                                 const float *stats, const float *removal, uint32_t *cand, int W, int H, int cell,
                                  const float *target, const sad_budget_cfg *cfg, int *n_split_out,
                                  int *n_pruned_out)
 {
@@ -63,8 +63,9 @@ extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, i
         return SAD_ERR_ARG;
     const int n = *n_slots;
     if (n < 0 || stride < 1 || n > stride || capacity < n || capacity > stride || W < 1 || H < 1 ||
-        W > SAD_MAX_DIM || H > SAD_MAX_DIM)
+        W > SAD_MAX_DIM || H > SAD_MAX_DIM || cell < 1 || cell > SAD_MAX_DIM)
         return SAD_ERR_ARG;
+    const int Wm = (W + cell - 1) / cell, Hm = (H + cell - 1) / cell;
     if (!(cfg->split_frac >= 0.0f && cfg->split_frac <= 1.0f && cfg->prune_frac >= 0.0f &&
           cfg->prune_frac <= 1.0f && cfg->shrink > 0.0f && cfg->min_mass >= 0.0f))
         return SAD_ERR_ARG;
@@ -198,13 +199,14 @@ extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, i
             P(PCG, s) = tc[1];
             P(PCB, s) = tc[2];
         }
-        // seed child B into its pixel's list and the 4 neighbours' (last entry)
-        const int bc = img.col(P(PX, b)), br = img.row(P(PY, b));
+        // seed child B into the list of its pixel's map entry and of the 4
+        // neighbour entries (last place)
+        const int bc = img.col(P(PX, b)) / cell, br = img.row(P(PY, b)) / cell;
         const int dc[5] = {0, -1, 1, 0, 0}, dr[5] = {0, 0, 0, -1, 1};
         for (int q = 0; q < 5; ++q) {
             const int c = bc + dc[q], r = br + dr[q];
-            if (c >= 0 && c < W && r >= 0 && r < H)
-                cand[((long)r * W + c) * SAD_K + (SAD_K - 1)] = (uint32_t)b;
+            if (c >= 0 && c < Wm && r >= 0 && r < Hm)
+                cand[((long)r * Wm + c) * SAD_K + (SAD_K - 1)] = (uint32_t)b;
         }
         ++done;
     }

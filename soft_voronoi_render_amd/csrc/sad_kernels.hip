@@ -41,6 +41,22 @@ __device__ __forceinline__ int xcd_band(int bid, int nb)
     return x * q + min(x, rem) + i;
 }
 
+// The candidate map's grid (summary, Appendix B.3 "Candidate field"): cells of
+// c x c pixels, Wm = ceil(W/c) of them per row; pixel (col, row) reads the list of
+// cell (col/c, row/c), and a cell's candidates are selected at its centred UV,
+// ((cx + 1/2) sx, (cy + 1/2) sy) px with sx = W/Wm, sy = H/Hm.  c = 1 is the
+// per-pixel map (sx = sy = 1).
+struct MapGrid {
+    int c, Wm;
+    float sx, sy;
+
+    // list index of pixel (col, row), whose image index is p
+    __device__ __forceinline__ long entry(long p, int col, int row) const
+    {
+        return c == 1 ? p : (long)(row / c) * Wm + col / c;
+    }
+};
+
 __device__ __forceinline__ bool finitef(float v) { return __builtin_isfinite(v); }
 
 // Hardware square root, reciprocal and reciprocal square root (1 ulp).  The
@@ -388,8 +404,8 @@ __device__ __forceinline__ void region_pixel(int r, int c0, int r0, int jump, in
 template <int KK, int TB>
 __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ G, uint32_t n_slots,
                                                      const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
-                                                     int H, int jump, uint32_t seed_h, int n_inject, float s,
-                                                     int tiles_x, int nb)
+                                                     int H, int jump, uint32_t seed_h, int n_inject, float s, float sx,
+                                                     float sy, int tiles_x, int nb)
 {
     __shared__ PropShared<KK, TB> L;
     const int tid = threadIdx.x;
@@ -446,7 +462,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
 
     if (col >= W || row >= H)
         return;
-    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    const float X = ((float)col + 0.5f) * sx, Y = ((float)row + 0.5f) * sy;
     auto rec_score_slot = [&](uint32_t sl, bool &usable, uint32_t &id) {
         const float4 g0 = L.t.rec0[sl], g1 = L.rec1[sl];
         usable = !(g0.x < 0.0f);
@@ -558,18 +574,21 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
 // Propagation pass without the tile table, for large jumps: there each neighbour
 // list is read by exactly one pixel of the tile, so hashing it buys no sharing.
 // Every candidate is scored from its site record (two 16-byte loads) and goes
-// through the same (d, ID) selection with a duplicate check.
-__global__ __launch_bounds__(BLOCK) void k_propagate_direct(const float4 *__restrict__ G, uint32_t n_slots,
-                                                            const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
-                                                            int W, int H, int jump, uint32_t seed_h, int n_inject,
-                                                            float s, int tiles_x, int nb)
+// through the same (d, ID) selection with a duplicate check.  TW x TW map entries
+// per workgroup: 16 for maps large enough to fill the chip with 16x16 tiles, 8
+// for small (downscaled) maps, which would otherwise leave most CUs idle.
+template <int TW>
+__global__ __launch_bounds__(TW *TW) void k_propagate_direct(const float4 *__restrict__ G, uint32_t n_slots,
+                                                             const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
+                                                             int W, int H, int jump, uint32_t seed_h, int n_inject,
+                                                             float s, float sx, float sy, int tiles_x, int nb)
 {
     const int t = xcd_band(blockIdx.x, nb);
-    const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
-    const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
+    const int col = (t % tiles_x) * TW + (threadIdx.x & (TW - 1));
+    const int row = (t / tiles_x) * TW + (threadIdx.x / TW);
     if (col >= W || row >= H)
         return;
-    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    const float X = ((float)col + 0.5f) * sx, Y = ((float)row + 0.5f) * sy;
     TopK64 best;
 #pragma unroll
     for (int j = 0; j < K; ++j)
@@ -634,7 +653,7 @@ __global__ __launch_bounds__(256) void k_fill_map(uint4 *__restrict__ cand, long
 
 __global__ __launch_bounds__(256) void k_jfa_seed_round(const float4 *__restrict__ G, uint32_t n_slots,
                                                         unsigned long long *__restrict__ keys, int W, int H,
-                                                        float s, int round)
+                                                        float s, MapGrid mg, int round)
 {
     const uint32_t i = blockIdx.x * 256u + threadIdx.x;
     if (i >= n_slots)
@@ -642,13 +661,14 @@ __global__ __launch_bounds__(256) void k_jfa_seed_round(const float4 *__restrict
     const float4 g0 = G[RLD4 * (size_t)i], g1 = G[RLD4 * (size_t)i + 1];
     if (!(g0.x >= 0.0f) || !finitef(g0.x) || !finitef(g0.y))
         return;  // inactive (x < 0), or no position
-    const int col = (int)floorf(fminf(g0.x, (float)(W - 1)));
-    const int row = (int)floorf(fminf(fmaxf(g0.y, 0.0f), (float)(H - 1)));
-    const float d = geom_score(g0, g1, (float)col + 0.5f, (float)row + 0.5f, s);
+    // the map entry of the pixel that holds the site
+    const int col = (int)floorf(fminf(g0.x, (float)(W - 1))) / mg.c;
+    const int row = (int)floorf(fminf(fmaxf(g0.y, 0.0f), (float)(H - 1))) / mg.c;
+    const float d = geom_score(g0, g1, ((float)col + 0.5f) * mg.sx, ((float)row + 0.5f) * mg.sy, s);
     if (!finitef(d))
         return;
     const unsigned long long key = rank_key(d, i);
-    unsigned long long *pl = keys + ((size_t)row * W + col) * JFA_KEEP;
+    unsigned long long *pl = keys + ((size_t)row * mg.Wm + col) * JFA_KEEP;
     for (int r = 0; r < round; ++r)
         if (pl[r] == key)
             return;  // already placed
@@ -674,14 +694,15 @@ __global__ __launch_bounds__(256) void k_jfa_seed_finish(uint4 *__restrict__ can
 // records, as in the table-free propagation.
 __global__ __launch_bounds__(BLOCK) void k_jfa_pass(const float4 *__restrict__ G, uint32_t n_slots,
                                                     const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
-                                                    int H, int step, float s, int tiles_x, int nb)
+                                                    int H, int step, float s, float sx, float sy, int tiles_x,
+                                                    int nb)
 {
     const int t = xcd_band(blockIdx.x, nb);
     const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
     const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
     if (col >= W || row >= H)
         return;
-    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    const float X = ((float)col + 0.5f) * sx, Y = ((float)row + 0.5f) * sy;
     TopK64 best;
 #pragma unroll
     for (int j = 0; j < K; ++j)
@@ -711,15 +732,15 @@ __global__ __launch_bounds__(BLOCK) void k_jfa_pass(const float4 *__restrict__ G
 // Exact top-K by brute force: every slot is scored for every pixel.  Scoring
 // records are staged through LDS 256 at a time.
 __global__ __launch_bounds__(BLOCK) void k_topk_exact(const float4 *__restrict__ G, uint32_t n_slots,
-                                                      uint4 *__restrict__ cout, int W, int H, float s, int tiles_x,
-                                                      int nb)
+                                                      uint4 *__restrict__ cout, int W, int H, float s, float sx,
+                                                      float sy, int tiles_x, int nb)
 {
     __shared__ float4 l0[BLOCK], l1[BLOCK];
     const int t = xcd_band(blockIdx.x, nb);
     const int col = (t % tiles_x) * TILE + (threadIdx.x & (TILE - 1));
     const int row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
     const bool inside = col < W && row < H;
-    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    const float X = ((float)col + 0.5f) * sx, Y = ((float)row + 0.5f) * sy;
     TopK64 best;
 #pragma unroll
     for (int j = 0; j < K; ++j)
@@ -960,7 +981,7 @@ __device__ __forceinline__ void load_ids(const uint4 *__restrict__ cand, long p,
 // Render forward (reading note, key design 2; project page "Method").
 __global__ __launch_bounds__(BLOCK) void k_render_fwd(const float4 *__restrict__ G, uint32_t n_slots,
                                                       const uint4 *__restrict__ cand, int W, int H,
-                                                      float *__restrict__ out, float s, int tiles_x, int nb)
+                                                      float *__restrict__ out, float s, MapGrid mg, int tiles_x, int nb)
 {
     __shared__ TileTable T;
     int col, row;
@@ -969,7 +990,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_fwd(const float4 *__restrict__
     const long p = (long)row * W + col;
     uint32_t ids[K];
     int slot[K];
-    load_ids(cand, p, inside, ids);
+    load_ids(cand, mg.entry(p, col, row), inside, ids);
     build_tile_table(T, G, n_slots, ids, slot);
     if (!inside)
         return;
@@ -1132,7 +1153,8 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
                                                       const uint4 *__restrict__ cand,
                                                       const float *__restrict__ target, int W, int H,
                                                       float *__restrict__ grad, float *__restrict__ loss_sum,
-                                                      float *__restrict__ out_rgb, float s, int tiles_x, int nb)
+                                                      float *__restrict__ out_rgb, float s, MapGrid grid, int tiles_x,
+                                                      int nb)
 {
     __shared__ BwdShared L;
     const int tid = threadIdx.x;
@@ -1143,7 +1165,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
     const long p = (long)row * W + col;
     uint32_t ids[K];
     int slot[K];
-    load_ids(cand, p, inside, ids);
+    load_ids(cand, grid.entry(p, col, row), inside, ids);
     // the target is read now, so its latency overlaps the table build
     float t0 = 0.0f, t1 = 0.0f, t2 = 0.0f;
     if (inside) {
@@ -1439,7 +1461,8 @@ constexpr int NSTAT = 7;
 __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restrict__ G, uint32_t n_slots,
                                                          const uint4 *__restrict__ cand,
                                                          const float *__restrict__ target, int W, int H,
-                                                         float *__restrict__ stats, float s, int tiles_x, int nb)
+                                                         float *__restrict__ stats, float s, MapGrid mg, int tiles_x,
+                                                         int nb)
 {
     __shared__ TileTable T;
     __shared__ float stage[BLOCK / 64][64 * NSTAT + 64];
@@ -1450,7 +1473,7 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restric
     const long p = (long)row * W + col;
     uint32_t ids[K];
     int slot[K];
-    load_ids(cand, p, inside, ids);
+    load_ids(cand, mg.entry(p, col, row), inside, ids);
     build_tile_table(T, G, n_slots, ids, slot);
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
     PixelBlend B;
@@ -1578,17 +1601,36 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 inline float scale_of(int W, int H) { return 1.0f / (float)(W > H ? W : H); }
 
+// The map grid of a W x H image with cells of `cell` pixels (W, H > 0); false if
+// the cell size is out of range.
+inline bool map_grid(int W, int H, int cell, MapGrid &mg, int &Wm, int &Hm)
+{
+    if (cell < 1 || cell > SAD_MAX_DIM)
+        return false;
+    Wm = (W + cell - 1) / cell;
+    Hm = (H + cell - 1) / cell;
+    mg.c = cell;
+    mg.Wm = Wm;
+    mg.sx = (float)W / (float)Wm;
+    mg.sy = (float)H / (float)Hm;
+    return true;
+}
+
 struct TileGrid {
     int tiles_x, nb;
 };
 
-inline TileGrid tile_grid(int W, int H)
+inline TileGrid tile_grid(int W, int H, int tw = TILE)
 {
     TileGrid g;
-    g.tiles_x = (W + TILE - 1) / TILE;
-    g.nb = g.tiles_x * ((H + TILE - 1) / TILE);
+    g.tiles_x = (W + tw - 1) / tw;
+    g.nb = g.tiles_x * ((H + tw - 1) / tw);
     return g;
 }
+
+// A launch of fewer 16x16 tiles than this leaves CUs idle (256 CUs, several
+// workgroups each): the table-free pass then runs on 8x8 tiles.
+constexpr int SMALL_MAP_TILES = 1024;
 
 inline int launched()
 {
@@ -1638,24 +1680,28 @@ int sad_site_records(const float *sites, int n_slots, int stride, float *rec, vo
 }
 
 int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
-                       int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream)
+                       int cell, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0 || jump < 1 || jump > 0xFFFF || n_inject < 0 || n_inject > SAD_MAX_INJECT)
+    if (n_slots < 0 || jump < 1 || jump > 0xFFFF || n_inject < 0 || n_inject > SAD_MAX_INJECT || cell < 1)
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
+    MapGrid mg;
+    int Wm, Hm;
+    if (!map_grid(W, H, cell, mg, Wm, Hm))
+        return SAD_ERR_ARG;
     if ((!rec && n_slots > 0) || !cand_in || !cand_out)
         return SAD_ERR_ARG;
-    const size_t bytes = (size_t)W * H * K * sizeof(uint32_t);
+    const size_t bytes = (size_t)Wm * Hm * K * sizeof(uint32_t);
     const uintptr_t a0 = (uintptr_t)cand_in, a1 = (uintptr_t)cand_out;
     if (a0 < a1 + bytes && a1 < a0 + bytes)
         return SAD_ERR_ARG;
     if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(rec))
         return SAD_ERR_ALIGN;
-    const TileGrid g = tile_grid(W, H);
+    const TileGrid g = tile_grid(Wm, Hm);
     const uint32_t pw = ((uint32_t)jump << 16) | (pass_index & 0xFFFFu);
     const uint32_t seed_h = host_pcg_hash(host_pcg_hash(seed) ^ pw);
     // Narrow strips (small jumps) need a smaller region buffer and site table, so
@@ -1667,113 +1713,147 @@ int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, u
     uint4 *co = (uint4 *)cand_out;
     // Measured on kodak768: the tile table pays off only at jump 1, where the
     // neighbour lists are the tile's own lists; from jump 2 on the table-free pass
-    // is as fast or faster (random cold-start lists: 90 vs 113 us at jump 2).
-    if (jump == 1)
-        hipLaunchKernelGGL((k_propagate<1, 256>), dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, W, H,
-                           jump, seed_h, n_inject, sc, g.tiles_x, g.nb);
-    else
-        hipLaunchKernelGGL(k_propagate_direct, dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, W, H,
-                           jump, seed_h, n_inject, sc, g.tiles_x, g.nb);
+    // is as fast or faster (random cold-start lists: 90 vs 113 us at jump 2).  On a
+    // downscaled map (cell > 1) a 16x16 tile spans c^2 times the pixels, so its
+    // lists name more sites than the table holds: there every pass is table-free,
+    // on 8x8 tiles when 16x16 ones would leave CUs idle.
+    if (cell > 1) {
+        if (g.nb < SMALL_MAP_TILES) {
+            const TileGrid g8 = tile_grid(Wm, Hm, 8);
+            hipLaunchKernelGGL(k_propagate_direct<8>, dim3(g8.nb), dim3(64), 0, hs, G, (uint32_t)n_slots, ci, co, Wm,
+                               Hm, jump, seed_h, n_inject, sc, mg.sx, mg.sy, g8.tiles_x, g8.nb);
+        } else {
+            hipLaunchKernelGGL(k_propagate_direct<TILE>, dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co,
+                               Wm, Hm, jump, seed_h, n_inject, sc, mg.sx, mg.sy, g.tiles_x, g.nb);
+        }
+    } else if (jump == 1) {
+        hipLaunchKernelGGL((k_propagate<1, 256>), dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, Wm,
+                           Hm, jump, seed_h, n_inject, sc, mg.sx, mg.sy, g.tiles_x, g.nb);
+    } else {
+        hipLaunchKernelGGL(k_propagate_direct<TILE>, dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, Wm,
+                           Hm, jump, seed_h, n_inject, sc, mg.sx, mg.sy, g.tiles_x, g.nb);
+    }
     return launched();
 }
 
-int sad_jfa_seed(const float *rec, int n_slots, uint32_t *cand, int W, int H, void *stream)
+int sad_jfa_seed(const float *rec, int n_slots, uint32_t *cand, int W, int H, int cell, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0)
+    if (n_slots < 0 || cell < 1)
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
+    MapGrid mg;
+    int Wm, Hm;
+    if (!map_grid(W, H, cell, mg, Wm, Hm))
+        return SAD_ERR_ARG;
     if ((!rec && n_slots > 0) || !cand)
         return SAD_ERR_ARG;
     if (!aligned16(cand) || !aligned16(rec))
         return SAD_ERR_ALIGN;
-    const long P = (long)W * H;
+    const long P = (long)Wm * Hm;
     const hipStream_t hs = (hipStream_t)stream;
     hipLaunchKernelGGL(k_fill_map, dim3((unsigned)((2 * P + 255) / 256)), dim3(256), 0, hs, (uint4 *)cand, 2 * P);
     if (n_slots > 0)
         for (int r = 0; r < JFA_KEEP; ++r)
             hipLaunchKernelGGL(k_jfa_seed_round, dim3((n_slots + 255) / 256), dim3(256), 0, hs, (const float4 *)rec,
-                               (uint32_t)n_slots, (unsigned long long *)cand, W, H, scale_of(W, H), r);
+                               (uint32_t)n_slots, (unsigned long long *)cand, W, H, scale_of(W, H), mg, r);
     hipLaunchKernelGGL(k_jfa_seed_finish, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, hs, (uint4 *)cand, P);
     return launched();
 }
 
-int sad_jfa_pass(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H, int step,
-                 void *stream)
+int sad_jfa_pass(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H, int cell,
+                 int step, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0 || step < 1 || step > 0xFFFF)
+    if (n_slots < 0 || step < 1 || step > 0xFFFF || cell < 1)
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
+    MapGrid mg;
+    int Wm, Hm;
+    if (!map_grid(W, H, cell, mg, Wm, Hm))
+        return SAD_ERR_ARG;
     if ((!rec && n_slots > 0) || !cand_in || !cand_out)
         return SAD_ERR_ARG;
-    const size_t bytes = (size_t)W * H * K * sizeof(uint32_t);
+    const size_t bytes = (size_t)Wm * Hm * K * sizeof(uint32_t);
     const uintptr_t a0 = (uintptr_t)cand_in, a1 = (uintptr_t)cand_out;
     if (a0 < a1 + bytes && a1 < a0 + bytes)
         return SAD_ERR_ARG;
     if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(rec))
         return SAD_ERR_ALIGN;
-    const TileGrid g = tile_grid(W, H);
+    const TileGrid g = tile_grid(Wm, Hm);
     hipLaunchKernelGGL(k_jfa_pass, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
-                       (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, W, H, step, scale_of(W, H),
-                       g.tiles_x, g.nb);
+                       (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm, step, scale_of(W, H),
+                       mg.sx, mg.sy, g.tiles_x, g.nb);
     return launched();
 }
 
-int sad_topk_exact(const float *rec, int n_slots, uint32_t *cand_out, int W, int H, void *stream)
+int sad_topk_exact(const float *rec, int n_slots, uint32_t *cand_out, int W, int H, int cell, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0)
+    if (n_slots < 0 || cell < 1)
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
+    MapGrid mg;
+    int Wm, Hm;
+    if (!map_grid(W, H, cell, mg, Wm, Hm))
+        return SAD_ERR_ARG;
     if ((!rec && n_slots > 0) || !cand_out)
         return SAD_ERR_ARG;
     if (!aligned16(cand_out) || !aligned16(rec))
         return SAD_ERR_ALIGN;
-    const TileGrid g = tile_grid(W, H);
+    const TileGrid g = tile_grid(Wm, Hm);
     hipLaunchKernelGGL(k_topk_exact, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
-                       (uint32_t)n_slots, (uint4 *)cand_out, W, H, scale_of(W, H), g.tiles_x, g.nb);
+                       (uint32_t)n_slots, (uint4 *)cand_out, Wm, Hm, scale_of(W, H), mg.sx, mg.sy, g.tiles_x, g.nb);
     return launched();
 }
 
-int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, int H, float *out_rgb, void *stream)
+int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, int H, int cell, float *out_rgb,
+                   void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0)
+    if (n_slots < 0 || cell < 1)
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
+    MapGrid mg;
+    int Wm, Hm;
+    if (!map_grid(W, H, cell, mg, Wm, Hm))
+        return SAD_ERR_ARG;
     if ((!rec && n_slots > 0) || !cand || !out_rgb)
         return SAD_ERR_ARG;
     if (!aligned16(cand) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
     hipLaunchKernelGGL(k_render_fwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
-                       (uint32_t)n_slots, (const uint4 *)cand, W, H, out_rgb, scale_of(W, H), g.tiles_x, g.nb);
+                       (uint32_t)n_slots, (const uint4 *)cand, W, H, out_rgb, scale_of(W, H), mg, g.tiles_x, g.nb);
     return launched();
 }
 
-int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
+int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H, int cell,
                    float *grad, float *loss_sum, float *out_rgb, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0)
+    if (n_slots < 0 || cell < 1)
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
+    MapGrid mg;
+    int Wm, Hm;
+    if (!map_grid(W, H, cell, mg, Wm, Hm))
+        return SAD_ERR_ARG;
     if ((!rec && n_slots > 0) || !cand || !target || (!grad && n_slots > 0))
         return SAD_ERR_ARG;
     if (!aligned16(cand) || !aligned16(grad) || !aligned16(rec))
@@ -1781,27 +1861,32 @@ int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const fl
     const TileGrid g = tile_grid(W, H);
     hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
                        (uint32_t)n_slots, (const uint4 *)cand, target, W, H, grad, loss_sum, out_rgb, scale_of(W, H),
-                       g.tiles_x, g.nb);
+                       mg, g.tiles_x, g.nb);
     return launched();
 }
 
 int sad_densify_stats(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
-                      float *stats, void *stream)
+                      int cell, float *stats, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0)
+    if (n_slots < 0 || cell < 1)
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
+    MapGrid mg;
+    int Wm, Hm;
+    if (!map_grid(W, H, cell, mg, Wm, Hm))
+        return SAD_ERR_ARG;
     if ((!rec && n_slots > 0) || !cand || !target || (!stats && n_slots > 0))
         return SAD_ERR_ARG;
     if (!aligned16(cand) || !aligned16(rec) || !aligned16(stats))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
     hipLaunchKernelGGL(k_densify_stats, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
-                       (uint32_t)n_slots, (const uint4 *)cand, target, W, H, stats, scale_of(W, H), g.tiles_x, g.nb);
+                       (uint32_t)n_slots, (const uint4 *)cand, target, W, H, stats, scale_of(W, H), mg, g.tiles_x,
+                       g.nb);
     return launched();
 }
 

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.sad_abi_version() == 2
+    assert L.sad_abi_version() == 3
     assert L.sad_status_string(0) == b"ok"
     assert L.sad_status_string(ERR_ALIGN) == b"misaligned pointer"
     assert L.sad_status_string(12345) == b"unknown status"
@@ -54,11 +54,12 @@ Q = 0x90000
 
 def test_propagate_rejects_bad_arguments(L):
     f = L.sad_topk_propagate
-    ok = dict(rec=P, n=4, a=P, b=Q, W=16, H=16, jump=1, pidx=0, seed=0, m=4)
+    ok = dict(rec=P, n=4, a=P, b=Q, W=16, H=16, cell=1, jump=1, pidx=0, seed=0, m=4)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["rec"], a["n"], a["a"], a["b"], a["W"], a["H"], a["jump"], a["pidx"], a["seed"], a["m"], None)
+        return f(a["rec"], a["n"], a["a"], a["b"], a["W"], a["H"], a["cell"], a["jump"], a["pidx"], a["seed"], a["m"],
+                 None)
 
     assert call(jump=0) == ERR_ARG
     assert call(jump=65536) == ERR_ARG
@@ -75,20 +76,29 @@ def test_propagate_rejects_bad_arguments(L):
     assert call(a=P + 4, b=Q) == ERR_ALIGN
     assert call(W=0) == 0                # empty image: no-op, nothing launched
     assert call(H=0, b=P) == 0           # empty: zero bytes cannot overlap
+    assert call(cell=0) == ERR_ARG
+    assert call(cell=-4) == ERR_ARG
+    assert call(cell=65536) == ERR_ARG
+    assert call(cell=0, W=0) == ERR_ARG  # the cell size is checked before the empty image
+    # overlap is judged on the map's size: 16x16 pixels in cells of 4 -> 4x4 lists, 512 bytes
+    assert call(cell=4, b=P + 480) == ERR_ARG
 
 
 def test_render_and_adam_reject_bad_arguments(L):
-    assert L.sad_render_fwd(P, 4, P + 8, 16, 16, Q, None) == ERR_ALIGN
-    assert L.sad_render_fwd(P + 8, 4, P, 16, 16, Q, None) == ERR_ALIGN
-    assert L.sad_render_fwd(P, 4, 0, 16, 16, Q, None) == ERR_ARG
-    assert L.sad_render_fwd(P, -1, P, 16, 16, Q, None) == ERR_ARG
-    assert L.sad_render_fwd(0, 4, P, 16, 16, Q, None) == ERR_ARG
-    assert L.sad_render_fwd(P, 4, P, 0, 16, Q, None) == 0
-    assert L.sad_render_bwd(P, 4, P, 0, 16, 16, Q, None, None, None) == ERR_ARG  # target NULL
-    assert L.sad_render_bwd(P, 4, P + 4, Q, 16, 16, Q, None, None, None) == ERR_ALIGN
-    assert L.sad_render_bwd(P, 4, P, Q, 16, 16, Q + 4, None, None, None) == ERR_ALIGN  # grad records
-    assert L.sad_topk_exact(P, 4, P + 4, 16, 16, None) == ERR_ALIGN
-    assert L.sad_topk_exact(P, -1, P, 16, 16, None) == ERR_ARG
+    assert L.sad_render_fwd(P, 4, P + 8, 16, 16, 1, Q, None) == ERR_ALIGN
+    assert L.sad_render_fwd(P + 8, 4, P, 16, 16, 1, Q, None) == ERR_ALIGN
+    assert L.sad_render_fwd(P, 4, 0, 16, 16, 1, Q, None) == ERR_ARG
+    assert L.sad_render_fwd(P, -1, P, 16, 16, 1, Q, None) == ERR_ARG
+    assert L.sad_render_fwd(0, 4, P, 16, 16, 1, Q, None) == ERR_ARG
+    assert L.sad_render_fwd(P, 4, P, 0, 16, 1, Q, None) == 0
+    assert L.sad_render_fwd(P, 4, P, 16, 16, 0, Q, None) == ERR_ARG  # cell 0
+    assert L.sad_render_bwd(P, 4, P, 0, 16, 16, 1, Q, None, None, None) == ERR_ARG  # target NULL
+    assert L.sad_render_bwd(P, 4, P + 4, Q, 16, 16, 1, Q, None, None, None) == ERR_ALIGN
+    assert L.sad_render_bwd(P, 4, P, Q, 16, 16, 1, Q + 4, None, None, None) == ERR_ALIGN  # grad records
+    assert L.sad_render_bwd(P, 4, P, Q, 16, 16, 0, Q, None, None, None) == ERR_ARG  # cell 0
+    assert L.sad_topk_exact(P, 4, P + 4, 16, 16, 1, None) == ERR_ALIGN
+    assert L.sad_topk_exact(P, -1, P, 16, 16, 1, None) == ERR_ARG
+    assert L.sad_topk_exact(P, 4, P, 16, 16, 0, None) == ERR_ARG
     assert L.sad_site_records(P, 4, 8, P + 4, None) == ERR_ALIGN
     assert L.sad_site_records(P, 9, 8, P, None) == ERR_ARG
     assert L.sad_site_records(0, 4, 8, P, None) == ERR_ARG
@@ -107,40 +117,45 @@ def test_render_and_adam_reject_bad_arguments(L):
 
 def test_jfa_entry_points_reject_bad_arguments(L):
     S, J = L.sad_jfa_seed, L.sad_jfa_pass
-    assert S(P, -1, P, 16, 16, None) == ERR_ARG
-    assert S(0, 4, P, 16, 16, None) == ERR_ARG
-    assert S(P, 4, 0, 16, 16, None) == ERR_ARG
-    assert S(P, 4, P + 4, 16, 16, None) == ERR_ALIGN
-    assert S(P + 8, 4, P, 16, 16, None) == ERR_ALIGN
-    assert S(P, 4, P, 70000, 16, None) == ERR_ARG
-    assert S(P, 4, P, 0, 16, None) == 0                      # empty image: no-op
-    assert J(P, 4, P, Q, 16, 16, 0, None) == ERR_ARG         # step 0
-    assert J(P, 4, P, Q, 16, 16, 65536, None) == ERR_ARG
-    assert J(P, 4, P, P + 32, 16, 16, 1, None) == ERR_ARG     # overlapping maps
-    assert J(P, 4, P + 4, Q, 16, 16, 1, None) == ERR_ALIGN
-    assert J(P, -1, P, Q, 16, 16, 1, None) == ERR_ARG
-    assert J(P, 4, P, Q, 16, 0, 1, None) == 0
+    assert S(P, -1, P, 16, 16, 1, None) == ERR_ARG
+    assert S(0, 4, P, 16, 16, 1, None) == ERR_ARG
+    assert S(P, 4, 0, 16, 16, 1, None) == ERR_ARG
+    assert S(P, 4, P + 4, 16, 16, 1, None) == ERR_ALIGN
+    assert S(P + 8, 4, P, 16, 16, 1, None) == ERR_ALIGN
+    assert S(P, 4, P, 70000, 16, 1, None) == ERR_ARG
+    assert S(P, 4, P, 0, 16, 1, None) == 0                      # empty image: no-op
+    assert J(P, 4, P, Q, 16, 16, 1, 0, None) == ERR_ARG         # step 0
+    assert J(P, 4, P, Q, 16, 16, 1, 65536, None) == ERR_ARG
+    assert J(P, 4, P, P + 32, 16, 16, 1, 1, None) == ERR_ARG     # overlapping maps
+    assert J(P, 4, P + 4, Q, 16, 16, 1, 1, None) == ERR_ALIGN
+    assert J(P, -1, P, Q, 16, 16, 1, 1, None) == ERR_ARG
+    assert J(P, 4, P, Q, 16, 0, 1, 1, None) == 0
+    assert S(P, 4, P, 16, 16, 0, None) == ERR_ARG            # cell 0
+    assert J(P, 4, P, Q, 16, 16, 0, 1, None) == ERR_ARG
+    assert J(P, 4, P, P + 256, 16, 16, 2, 1, None) == ERR_ARG  # 8x8 lists of 32 bytes overlap
 
 
 def test_densify_entry_points_reject_bad_arguments(L):
     D = L.sad_densify_stats
-    assert D(P, -1, P, Q, 16, 16, Q, None) == ERR_ARG
-    assert D(P, 4, 0, Q, 16, 16, Q, None) == ERR_ARG        # cand NULL
-    assert D(P, 4, P, 0, 16, 16, Q, None) == ERR_ARG        # target NULL
-    assert D(P, 4, P, Q, 16, 16, 0, None) == ERR_ARG        # stats NULL
-    assert D(P, 4, P + 4, Q, 16, 16, Q, None) == ERR_ALIGN
-    assert D(P, 4, P, Q, 16, 16, Q + 4, None) == ERR_ALIGN
-    assert D(P, 4, P, Q, 0, 16, Q, None) == 0               # empty image: no-op
-    assert D(P, 4, P, Q, 16, 70000, Q, None) == ERR_ARG
+    assert D(P, -1, P, Q, 16, 16, 1, Q, None) == ERR_ARG
+    assert D(P, 4, 0, Q, 16, 16, 1, Q, None) == ERR_ARG        # cand NULL
+    assert D(P, 4, P, 0, 16, 16, 1, Q, None) == ERR_ARG        # target NULL
+    assert D(P, 4, P, Q, 16, 16, 1, 0, None) == ERR_ARG        # stats NULL
+    assert D(P, 4, P + 4, Q, 16, 16, 1, Q, None) == ERR_ALIGN
+    assert D(P, 4, P, Q, 16, 16, 1, Q + 4, None) == ERR_ALIGN
+    assert D(P, 4, P, Q, 0, 16, 1, Q, None) == 0               # empty image: no-op
+    assert D(P, 4, P, Q, 16, 70000, 1, Q, None) == ERR_ARG
+    assert D(P, 4, P, Q, 16, 16, 0, Q, None) == ERR_ARG     # cell 0
     cfg = sad.BudgetConfig().to_c()
     n = ctypes.c_int(4)
     F = L.sad_densify_prune
-    assert F(None, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, P, ctypes.byref(cfg), None, None) == ERR_ARG
-    assert F(P, P, P, 8, 8, None, P, P, P, 4, 4, P, ctypes.byref(cfg), None, None) == ERR_ARG
-    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, P, None, None, None) == ERR_ARG
-    assert F(P, P, P, 8, 3, ctypes.byref(n), P, P, P, 4, 4, P, ctypes.byref(cfg), None, None) == ERR_ARG
-    assert F(P, P, P, 8, 9, ctypes.byref(n), P, P, P, 4, 4, P, ctypes.byref(cfg), None, None) == ERR_ARG
-    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 0, 4, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert F(None, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert F(P, P, P, 8, 8, None, P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 1, P, None, None, None) == ERR_ARG
+    assert F(P, P, P, 8, 3, ctypes.byref(n), P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert F(P, P, P, 8, 9, ctypes.byref(n), P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 0, 4, 1, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 0, P, ctypes.byref(cfg), None, None) == ERR_ARG
     assert n.value == 4
 
 
@@ -158,3 +173,9 @@ def test_jump_schedule():
     assert sad.jump_schedule(768, 512, 12) == [512, 256, 128, 64, 32, 16, 8, 4, 2, 1, 1, 1]
     assert sad.jump_schedule(4096, 4096, 13)[:12] == [2048 >> i for i in range(12)]
     assert sad.jump_schedule(1, 1, 3) == [1, 1, 1]
+    # on a map of 4x4-pixel cells the schedule counts map entries (192 x 128)
+    assert sad.jump_schedule(768, 512, 9, cell=4) == [128, 64, 32, 16, 8, 4, 2, 1, 1]
+    assert sad.jfa_steps(768, 512, cell=4) == [128, 64, 32, 16, 8, 4, 2, 1]
+    assert sad.map_shape(77, 45, 4) == (12, 20, 8)
+    with pytest.raises(ValueError):
+        sad.map_shape(16, 16, 0)

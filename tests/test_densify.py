@@ -133,6 +133,28 @@ def test_split_along_principal_axis(theta):
     assert (cand[..., 7] == 6).sum() == 5 and np.all(cand[..., :7] == NONE)
 
 
+@pytest.mark.parametrize("cell", [2, 5])
+def test_split_seeds_the_cell_map(cell):
+    """On a map of cells, child B enters the list of the cell that holds its pixel
+    and of the four neighbour cells (inside the map)."""
+    W, H = 32, 24
+    S, m, v, stats, removal, _, T = _budget_case()
+    Hm, Wm = -(-H // cell), -(-W // cell)
+    cand = np.full((Hm, Wm, 8), NONE, dtype=np.uint32)
+    stats[2] = _cov_stats(3.0, 4.0, 1.0, 0.3, 50.0)
+    for i in range(6):
+        if i != 2:
+            stats[i] = [50.0, 0.1, 0, 0, 0.1, 0, 0.1, 0]
+    n, ns, _, _ = orc_densify(S, m, v, 6, 10, stats, removal, cand, W, H, T, split_frac=1 / 6, prune_frac=0.0,
+                              cell=cell)
+    assert (n, ns) == (7, 1)
+    bc, br = int(S[X, 6]) // cell, int(S[Y, 6]) // cell
+    want = {(br + dr, bc + dc) for dc, dr in ((0, 0), (-1, 0), (1, 0), (0, -1), (0, 1))
+            if 0 <= br + dr < Hm and 0 <= bc + dc < Wm}
+    assert {tuple(x) for x in np.argwhere(cand[..., 7] == 6)} == want
+    assert np.all(cand[..., :7] == NONE)
+
+
 @pytest.mark.parametrize("direction", ["x", "y", "flat"])
 def test_split_low_mass_uses_sobel_axis(direction):
     S, m, v, stats, removal, cand, T = _budget_case()
@@ -183,15 +205,18 @@ def test_capacity_shortage_reports():
     assert (n, ns, npr, short) == (7, 1, 0, True)
 
 
-def _random_budget_case(seed, W=48, H=40, n=300, cap=330, inactive=6):
+def _random_budget_case(seed, W=48, H=40, n=300, cap=330, inactive=6, cell=1):
     import oracle
     S = synth.random_sites(n, W, H, seed, cap)
     rng = np.random.default_rng(seed)
     dead = rng.choice(n, inactive, replace=False)
     S[0, dead] = S[1, dead] = -1.0
-    cand = synth.local_map(S, n, W, H, seed=seed + 1, radius=6.0)
+    if cell == 1:
+        cand = synth.local_map(S, n, W, H, seed=seed + 1, radius=6.0)
+    else:
+        cand = oracle.topk_exact(S, n, W, H, cell=cell)
     T = (synth.pixel_noise(W, H, seed + 2, 0.2) + 0.5).astype(np.float32)
-    stats = oracle.densify_stats(S, n, cand, T, W, H).astype(np.float32)
+    stats = oracle.densify_stats(S, n, cand, T, W, H, cell=cell).astype(np.float32)
     removal = rng.normal(0, 1, cap).astype(np.float32)
     removal[rng.choice(n, 4, replace=False)] = np.nan
     m = rng.normal(0, 1, (10, cap)).astype(np.float32)
@@ -199,22 +224,26 @@ def _random_budget_case(seed, W=48, H=40, n=300, cap=330, inactive=6):
     return S, m, v, stats, removal, cand, T
 
 
-@pytest.mark.parametrize("seed,cfg", [
-    (1, sad.BudgetConfig()),
-    (2, sad.BudgetConfig(split_frac=0.2, prune_frac=0.0)),             # runs out of slots
-    (3, sad.BudgetConfig(split_frac=0.1, prune_frac=0.1, min_mass=1e6)),  # gradient axis throughout
-    (4, sad.BudgetConfig(split_frac=0.08, prune_frac=0.02, alpha=0.0, shrink=0.7)),
-    (5, sad.BudgetConfig(split_frac=0.0, prune_frac=0.3)),
+@pytest.mark.parametrize("seed,cfg,cell", [
+    (1, sad.BudgetConfig(), 1),
+    (2, sad.BudgetConfig(split_frac=0.2, prune_frac=0.0), 1),             # runs out of slots
+    (3, sad.BudgetConfig(split_frac=0.1, prune_frac=0.1, min_mass=1e6), 1),  # gradient axis throughout
+    (4, sad.BudgetConfig(split_frac=0.08, prune_frac=0.02, alpha=0.0, shrink=0.7), 1),
+    (5, sad.BudgetConfig(split_frac=0.0, prune_frac=0.3), 1),
+    (6, sad.BudgetConfig(split_frac=0.1, prune_frac=0.05), 3),           # map of 3x3-pixel cells
+    (7, sad.BudgetConfig(split_frac=0.2, prune_frac=0.1), 8),
 ])
-def test_host_densify_matches_oracle(orc, seed, cfg):
+def test_host_densify_matches_oracle(orc, seed, cfg, cell):
     W, H, n, cap = 48, 40, 300, 330
-    case = _random_budget_case(seed, W, H, n, cap)
+    case = _random_budget_case(seed, W, H, n, cap, cell=cell)
     mine = [a.copy() for a in case]
     ref = [a.copy() for a in case]
-    got = sad.densify_prune(mine[0], mine[1], mine[2], n, cap, mine[3], mine[4], mine[5], W, H, mine[6], cfg)
+    got = sad.densify_prune(mine[0], mine[1], mine[2], n, cap, mine[3], mine[4], mine[5], W, H, mine[6], cfg,
+                            cell=cell)
     f32 = lambda x: float(np.float32(x))  # the C struct holds float32 constants
     want = orc_densify(ref[0], ref[1], ref[2], n, cap, ref[3], ref[4], ref[5], W, H, ref[6],
-                       f32(cfg.split_frac), f32(cfg.prune_frac), f32(cfg.alpha), f32(cfg.min_mass), f32(cfg.shrink))
+                       f32(cfg.split_frac), f32(cfg.prune_frac), f32(cfg.alpha), f32(cfg.min_mass), f32(cfg.shrink),
+                       cell=cell)
     assert got[:3] == want[:3]
     assert (got[3] == sad.SAD_ERR_CAPACITY) == want[3]
     assert np.allclose(mine[0][:2], ref[0][:2], atol=2e-5)
