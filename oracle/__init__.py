@@ -347,3 +347,4 @@ def jfa_steps(W: int, H: int, cell: int = 1) -> list:
 
 
 from .densify import densify_prune  # noqa: E402  (pure Python, no C)
+from .packed import pack_words, rounded_sites  # noqa: E402  (numpy only)
