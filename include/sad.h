@@ -65,6 +65,17 @@
  *         sites").  A slot with x < 0 stays inactive.  16-byte aligned.  It is a
  *         cache the caller keeps in step with `sites`: recompute it after any
  *         change made outside sad_adam_step.
+ * packed: uint32 [n_slots][SAD_PACK_LD] -- the packed candidate-site buffer
+ *         ([SUM] B.2 "Packed candidate sites": 16 bytes per site of float16 pairs,
+ *         read by the candidate-update kernels to save bandwidth): word 0 = (x, y),
+ *         word 1 = (log tau, r), word 2 = (dir_x, dir_y), word 3 = (a, 0), the
+ *         first value of each pair in the low 16 bits; IEEE binary16, rounded to
+ *         nearest even, overflow to infinity; an inactive slot (x < 0) packs
+ *         x = -1.  16-byte aligned.  Selection entry points given it (sel_fmt =
+ *         SAD_SEL_PACKED16) rank the sites as if their seven packed fields were
+ *         rounded to binary16: the same score, ranking and filters, evaluated in
+ *         float32 from the decoded values.  A cache like `rec`: sad_pack_sites
+ *         writes it, sad_adam_step refreshes it.
  * Pixel (col,row) is rendered at (col+0.5, row+0.5) px ([SUM] B.3 evaluates at
  * centred cells).  Limits: 1 <= W, H <= 65535 (W or H = 0 is an empty image: a
  * no-op returning SAD_OK after the scalar arguments are checked; its pointers
@@ -84,7 +95,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 3
+#define SAD_ABI_VERSION 4
 #define SAD_K 8
 #define SAD_INVALID 0xffffffffu
 #define SAD_NPARAM 10
@@ -95,6 +106,11 @@ extern "C" {
 #define SAD_MAX_INJECT 16
 #define SAD_MAX_DIM 65535
 #define SAD_LOSS_SLOTS 64 /* partial sums of the loss output of sad_render_bwd */
+#define SAD_PACK_LD 4     /* uint32 words per site of the packed candidate-site buffer */
+
+/* Site formats the candidate-selection entry points read (`sel_fmt`). */
+#define SAD_SEL_REC64 0    /* `rec`: the 64-byte site records                          */
+#define SAD_SEL_PACKED16 1 /* `rec`: the 16-byte packed candidate-site buffer (packed) */
 
 enum sad_status {
     SAD_OK = 0,
@@ -139,6 +155,15 @@ const char *sad_status_string(int status);
 int sad_site_records(const float *sites, int n_slots, int stride, float *rec, void *stream);
 
 /*
+ * sad_pack_sites -- writes the packed candidate-site words (see `packed` above) of
+ * slots [0, n_slots) from the site planes ([SUM] B.2: regenerated after
+ * densification).
+ *   sites device [10][stride] read-only; packed device [n_slots][4] uint32, written.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN (packed not 16-byte aligned), SAD_ERR_DEVICE.
+ */
+int sad_pack_sites(const float *sites, int n_slots, int stride, uint32_t *packed, void *stream);
+
+/*
  * sad_topk_propagate -- one propagation pass of the candidate map.
  * [NOTE] design 3: C~_t(x) = C_{t-1}(x) U P_t(x) U G_t(x), keep the top-K under d;
  * [SUM] section 4: self plus 4 neighbours at the current jump, plus a small
@@ -159,15 +184,17 @@ int sad_site_records(const float *sites, int n_slots, int stride, float *rec, vo
  * padded with SAD_INVALID.  The pass reads cand_in and writes cand_out (Jacobi).
  * The host chooses the schedule: jumps B/2, B/4, ..., 1 then 1 ([SUM] section 4).
  *
- *   rec       device, [n_slots][16] float site records, read-only
+ *   rec       device, read-only: the site records [n_slots][16] float (sel_fmt =
+ *             SAD_SEL_REC64) or the packed buffer [n_slots][4] uint32
+ *             (SAD_SEL_PACKED16); the same pair in every selection entry point
  *   cand_in   device, [Hm][Wm][8] uint32, read-only, 16-byte aligned
  *   cand_out  device, [Hm][Wm][8] uint32, written; must not overlap cand_in
  *   jump      1..65535;  n_inject 0..SAD_MAX_INJECT
- * Errors: SAD_ERR_ARG (bad sizes, cell, jump, n_inject, NULL, overlapping maps),
+ * Errors: SAD_ERR_ARG (bad sizes, cell, sel_fmt, jump, n_inject, NULL, overlapping maps),
  *         SAD_ERR_ALIGN (a pointer not 16-byte aligned), SAD_ERR_DEVICE.
  */
-int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
-                       int cell, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream);
+int sad_topk_propagate(const float *rec, int sel_fmt, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W,
+                       int H, int cell, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream);
 
 /*
  * sad_jfa_seed -- seed pass of the optional jump-flood prepass ([SUM] B.3 "Jump
@@ -178,10 +205,10 @@ int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, u
  * image); an entry keeps at most four, the best by (d, ID) at its centred UV, in
  * places 0..3 (ascending); all other places are SAD_INVALID.  The whole map is
  * written.
- *   rec device [n_slots][16] read-only; cand device [Hm][Wm][8], written.
+ *   rec/sel_fmt as in sad_topk_propagate; cand device [Hm][Wm][8], written.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_jfa_seed(const float *rec, int n_slots, uint32_t *cand, int W, int H, int cell, void *stream);
+int sad_jfa_seed(const float *rec, int sel_fmt, int n_slots, uint32_t *cand, int W, int H, int cell, void *stream);
 
 /*
  * sad_jfa_pass -- one flood pass of the prepass with step `step` ([SUM] B.3):
@@ -192,21 +219,23 @@ int sad_jfa_seed(const float *rec, int n_slots, uint32_t *cand, int W, int H, in
  * 4..7.  Jacobi: reads cand_in, writes cand_out.  The prepass runs the steps B/2,
  * B/4, ..., 1 (B = 2^ceil(log2 max(Wm,Hm))), i.e. ceil(log2 max(Wm,Hm)) passes,
  * after sad_jfa_seed; sad_topk_propagate then fills the lists to K.
- *   step in [1, 65535]; cand_in, cand_out device [Hm][Wm][8], not overlapping.
+ *   rec/sel_fmt as in sad_topk_propagate; step in [1, 65535]; cand_in, cand_out
+ *   device [Hm][Wm][8], not overlapping.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_jfa_pass(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H, int cell,
-                 int step, void *stream);
+int sad_jfa_pass(const float *rec, int sel_fmt, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
+                 int cell, int step, void *stream);
 
 /*
  * sad_topk_exact -- the exact top-K map by brute force over every slot: the list
  * that propagation approximates ([NOTE] design 3; [SUM] section 4 "Candidate
  * maintenance").  Used to (re)initialise a map and to measure recall.  Cost
  * O(Wm*Hm*n_slots).  Same output convention as sad_topk_propagate.
- *   rec device [n_slots][16] read-only;  cand_out device [Hm][Wm][8], written.
+ *   rec/sel_fmt as in sad_topk_propagate;  cand_out device [Hm][Wm][8], written.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_topk_exact(const float *rec, int n_slots, uint32_t *cand_out, int W, int H, int cell, void *stream);
+int sad_topk_exact(const float *rec, int sel_fmt, int n_slots, uint32_t *cand_out, int W, int H, int cell,
+                   void *stream);
 
 /*
  * sad_render_fwd -- the temperature-softmax blend of each pixel's list (the list
@@ -310,14 +339,16 @@ int sad_densify_prune(float *sites, float *m, float *v, int stride, int capacity
  * then x is clamped to [0, W] and y to [0, H].  Accumulators 0..9 of grad are
  * zeroed for every slot < n_slots; accumulator 10 is left alone.  Inactive slots
  * keep p, m, v.  If rec is not NULL the site records of slots [0, n_slots) are
- * rewritten from the updated sites in the same pass.
+ * rewritten from the updated sites in the same pass; if packed is not NULL, so
+ * are their packed candidate-site words.
  *   sites, m, v device [10][stride] float (in/out); grad device [stride][16],
- *   16-byte aligned; rec device [n_slots][16] or NULL; step >= 1 (global,
- *   1-based); n_pixels >= 1; cfg HOST pointer.
+ *   16-byte aligned; rec device [n_slots][16] or NULL; packed device
+ *   [n_slots][4] uint32 or NULL, 16-byte aligned; step >= 1 (global, 1-based);
+ *   n_pixels >= 1; cfg HOST pointer.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_adam_step(float *sites, float *m, float *v, float *grad, float *rec, int n_slots, int stride, int step,
-                  int n_pixels, int W, int H, const sad_adam_cfg *cfg, void *stream);
+int sad_adam_step(float *sites, float *m, float *v, float *grad, float *rec, uint32_t *packed, int n_slots, int stride,
+                  int step, int n_pixels, int W, int H, const sad_adam_cfg *cfg, void *stream);
 
 #ifdef __cplusplus
 }

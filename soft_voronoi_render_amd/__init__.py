@@ -36,6 +36,8 @@ REC_LD = 16
 STAT_LD = 8
 LOSS_SLOTS = 64
 MAX_INJECT = 16
+PACK_LD = 4
+SEL_REC64, SEL_PACKED16 = 0, 1
 
 SAD_OK, SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE, SAD_ERR_CAPACITY, SAD_ERR_UNIMPLEMENTED = 0, -1, -2, -3, -4, -5
 STATUS = {0: "ok", -1: "invalid argument", -2: "misaligned pointer", -3: "HIP launch failed",
@@ -98,17 +100,19 @@ def lib() -> ctypes.CDLL:
         L.sad_site_records.restype = i32
         L.sad_site_records.argtypes = [fp, i32, i32, fp, vp]
         L.sad_topk_propagate.restype = i32
-        L.sad_topk_propagate.argtypes = [fp, i32, vp, vp, i32, i32, i32, i32, u32, u32, i32, vp]
+        L.sad_pack_sites.restype = i32
+        L.sad_pack_sites.argtypes = [fp, i32, i32, vp, vp]
+        L.sad_topk_propagate.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, i32, u32, u32, i32, vp]
         L.sad_topk_exact.restype = i32
-        L.sad_topk_exact.argtypes = [fp, i32, vp, i32, i32, i32, vp]
+        L.sad_topk_exact.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp]
         L.sad_render_fwd.restype = i32
         L.sad_render_fwd.argtypes = [fp, i32, vp, i32, i32, i32, fp, vp]
         L.sad_render_bwd.restype = i32
         L.sad_render_bwd.argtypes = [fp, i32, vp, fp, i32, i32, i32, fp, fp, fp, vp]
         L.sad_jfa_seed.restype = i32
-        L.sad_jfa_seed.argtypes = [vp, i32, vp, i32, i32, i32, vp]
+        L.sad_jfa_seed.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp]
         L.sad_jfa_pass.restype = i32
-        L.sad_jfa_pass.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp]
+        L.sad_jfa_pass.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, i32, vp]
         L.sad_densify_stats.restype = i32
         L.sad_densify_stats.argtypes = [fp, i32, vp, fp, i32, i32, i32, fp, vp]
         ip = ctypes.POINTER(ctypes.c_int)
@@ -116,13 +120,15 @@ def lib() -> ctypes.CDLL:
         L.sad_densify_prune.argtypes = [fp, fp, fp, i32, i32, ip, fp, fp, vp, i32, i32, i32, fp,
                                         ctypes.POINTER(BudgetCfg), ip, ip]
         L.sad_adam_step.restype = i32
-        L.sad_adam_step.argtypes = [fp, fp, fp, fp, fp, i32, i32, i32, i32, i32, i32, ctypes.POINTER(AdamCfg), vp]
+        L.sad_adam_step.argtypes = [fp, fp, fp, fp, fp, vp, i32, i32, i32, i32, i32, i32, ctypes.POINTER(AdamCfg),
+                                    vp]
         _lib = L
     return _lib
 
 
 EXPORTED = ("sad_abi_version", "sad_status_string", "sad_site_records", "sad_topk_propagate", "sad_topk_exact",
-            "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_densify_stats", "sad_densify_prune", "sad_jfa_seed", "sad_jfa_pass")
+            "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_densify_stats", "sad_densify_prune", "sad_jfa_seed",
+            "sad_jfa_pass", "sad_pack_sites")
 
 
 # --------------------------------------------------------------- marshalling
@@ -178,6 +184,30 @@ def new_records(capacity: int, device="cuda") -> torch.Tensor:
     return torch.zeros((max(capacity, 1), REC_LD), dtype=torch.float32, device=device)
 
 
+def new_packed(capacity: int, device="cuda") -> torch.Tensor:
+    """Storage for the packed candidate-site buffer, uint32 [capacity][4] held as int32."""
+    return torch.zeros((max(capacity, 1), PACK_LD), dtype=torch.int32, device=device)
+
+
+def _sel(sel: torch.Tensor, n_slots: int):
+    """(pointer, format) of the site buffer a selection entry point reads: the
+    records (float32 [>= n][16]) or the packed buffer (int32 [>= n][4])."""
+    if sel.dim() == 2 and sel.dtype == torch.float32 and sel.shape[1] == REC_LD and sel.shape[0] >= n_slots:
+        return _dev(sel, "rec", _F32), SEL_REC64
+    if sel.dim() == 2 and sel.dtype in _U32 and sel.shape[1] == PACK_LD and sel.shape[0] >= n_slots:
+        return _dev(sel, "packed", _U32), SEL_PACKED16
+    raise ValueError("selection sites must be records float32 [>= n_slots][16] or packed int32 [>= n_slots][4]")
+
+
+def pack_sites(sites, n_slots, packed, stream=None):
+    """Writes the packed candidate-site words of slots [0, n_slots) (see sad_pack_sites)."""
+    sp, stride = _sites(sites, n_slots)
+    if packed.dim() != 2 or packed.shape[1] != PACK_LD or packed.shape[0] < n_slots:
+        raise ValueError("packed must be int32 [>= n_slots][4]")
+    pk = _dev(packed, "packed", _U32)
+    _check("sad_pack_sites", lib().sad_pack_sites(sp, n_slots, stride, pk, _stream(stream)))
+
+
 def site_records(sites, n_slots, rec, stream=None):
     """Writes the site records of slots [0, n_slots) (see sad_site_records)."""
     sp, stride = _sites(sites, n_slots)
@@ -194,27 +224,29 @@ def map_shape(W: int, H: int, cell: int = 1) -> tuple:
 
 
 def topk_propagate(rec, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed, n_inject, stream=None, cell=1):
-    """One propagation pass: cand_in -> cand_out (see sad_topk_propagate)."""
-    g = _rec(rec, n_slots)
+    """One propagation pass: cand_in -> cand_out (see sad_topk_propagate).  `rec`
+    is the record buffer or the packed candidate-site buffer."""
+    g, fmt = _sel(rec, n_slots)
     a = _dev(cand_in, "cand_in", _U32, map_shape(W, H, cell))
     b = _dev(cand_out, "cand_out", _U32, map_shape(W, H, cell))
-    _check("sad_topk_propagate", lib().sad_topk_propagate(g, n_slots, a, b, W, H, cell, jump, pass_index & 0xFFFFFFFF,
-                                                          seed & 0xFFFFFFFF, n_inject, _stream(stream)))
+    _check("sad_topk_propagate", lib().sad_topk_propagate(g, fmt, n_slots, a, b, W, H, cell, jump,
+                                                          pass_index & 0xFFFFFFFF, seed & 0xFFFFFFFF, n_inject,
+                                                          _stream(stream)))
 
 
 def jfa_seed(rec, n_slots, cand, W, H, stream=None, cell=1):
     """Seed pass of the jump-flood prepass (see sad_jfa_seed)."""
-    g = _rec(rec, n_slots)
+    g, fmt = _sel(rec, n_slots)
     c = _dev(cand, "cand", _U32, map_shape(W, H, cell))
-    _check("sad_jfa_seed", lib().sad_jfa_seed(g, n_slots, c, W, H, cell, _stream(stream)))
+    _check("sad_jfa_seed", lib().sad_jfa_seed(g, fmt, n_slots, c, W, H, cell, _stream(stream)))
 
 
 def jfa_pass(rec, n_slots, cand_in, cand_out, W, H, step, stream=None, cell=1):
     """One flood pass of the jump-flood prepass: cand_in -> cand_out (see sad_jfa_pass)."""
-    g = _rec(rec, n_slots)
+    g, fmt = _sel(rec, n_slots)
     a = _dev(cand_in, "cand_in", _U32, map_shape(W, H, cell))
     b = _dev(cand_out, "cand_out", _U32, map_shape(W, H, cell))
-    _check("sad_jfa_pass", lib().sad_jfa_pass(g, n_slots, a, b, W, H, cell, step, _stream(stream)))
+    _check("sad_jfa_pass", lib().sad_jfa_pass(g, fmt, n_slots, a, b, W, H, cell, step, _stream(stream)))
 
 
 def jfa_steps(W: int, H: int, cell: int = 1) -> list:
@@ -241,9 +273,9 @@ def jfa_prepass(rec, n_slots, a, b, W, H, stream=None, cell=1):
 
 def topk_exact(rec, n_slots, cand_out, W, H, stream=None, cell=1):
     """Brute-force exact top-K map (see sad_topk_exact)."""
-    g = _rec(rec, n_slots)
+    g, fmt = _sel(rec, n_slots)
     b = _dev(cand_out, "cand_out", _U32, map_shape(W, H, cell))
-    _check("sad_topk_exact", lib().sad_topk_exact(g, n_slots, b, W, H, cell, _stream(stream)))
+    _check("sad_topk_exact", lib().sad_topk_exact(g, fmt, n_slots, b, W, H, cell, _stream(stream)))
 
 
 def render_fwd(rec, n_slots, cand, W, H, out_rgb, stream=None, cell=1):
@@ -294,14 +326,19 @@ class AdamConfig:
 
 
 def adam_step(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamConfig | AdamCfg | None = None,
-              rec=None, stream=None):
+              rec=None, stream=None, packed=None):
     sp, stride = _sites(sites, n_slots)
     mp = _dev(m, "m", _F32, (NPARAM, stride))
     vp = _dev(v, "v", _F32, (NPARAM, stride))
     g = _dev(grad, "grad", _F32, (stride, GRAD_LD))
     gp = _rec(rec, n_slots) if rec is not None else None
+    pk = None
+    if packed is not None:
+        if packed.dim() != 2 or packed.shape[1] != PACK_LD or packed.shape[0] < n_slots:
+            raise ValueError("packed must be int32 [>= n_slots][4]")
+        pk = _dev(packed, "packed", _U32)
     c = cfg.to_c() if isinstance(cfg, AdamConfig) else (cfg if cfg is not None else AdamConfig().to_c())
-    _check("sad_adam_step", lib().sad_adam_step(sp, mp, vp, g, gp, n_slots, stride, step, n_pixels, W, H,
+    _check("sad_adam_step", lib().sad_adam_step(sp, mp, vp, g, gp, pk, n_slots, stride, step, n_pixels, W, H,
                                                 ctypes.byref(c), _stream(stream)))
 
 
@@ -401,11 +438,13 @@ class Fitter:
     update are exposed, and 8-16 iterations between updates left the final PSNR
     unchanged there).  The pass counter drives the jump schedule and the
     injection's pass index.  `cell` > 1 keeps the candidate map on the downscaled
-    grid of B.3 "Candidate field" (ceil(W/cell) x ceil(H/cell) lists)."""
+    grid of B.3 "Candidate field" (ceil(W/cell) x ceil(H/cell) lists).  With
+    `packed` the candidate passes read the 16-byte float16 candidate-site buffer
+    of B.2 "Packed candidate sites" (Adam refreshes it with the records)."""
 
     def __init__(self, sites: torch.Tensor, n_slots: int, target: torch.Tensor, W: int, H: int,
                  n_inject: int = 4, seed: int = 4, adam: AdamConfig | None = None, cand: torch.Tensor | None = None,
-                 refresh_every: int = 1, passes_per_refresh: int = 1, cell: int = 1):
+                 refresh_every: int = 1, passes_per_refresh: int = 1, cell: int = 1, packed: bool = False):
         if refresh_every < 1 or passes_per_refresh < 0:
             raise ValueError("refresh_every >= 1 and passes_per_refresh >= 0")
         dev = sites.device
@@ -423,6 +462,10 @@ class Fitter:
         self.grad = torch.zeros((stride, GRAD_LD), dtype=torch.float32, device=dev)
         self.rec = new_records(stride, dev)
         site_records(sites, n_slots, self.rec)
+        self.packed = None
+        if packed:
+            self.packed = new_packed(stride, dev)
+            pack_sites(sites, n_slots, self.packed)
         self.maps = [cand if cand is not None else new_map(W, H, dev, cell), new_map(W, H, dev, cell)]
         self.cur = 0
         self.rgb = torch.empty((H, W, 3), dtype=torch.float32, device=dev)
@@ -439,12 +482,20 @@ class Fitter:
         B = 1 << max(0, (max(self.Wm, self.Hm) - 1).bit_length())
         return max(1, (B // 2) >> it) if it < 64 else 1
 
+    @property
+    def sel(self) -> torch.Tensor:
+        """The site buffer the candidate passes read."""
+        return self.packed if self.packed is not None else self.rec
+
     def refresh_records(self, stream=None):
-        """Recompute the site records after changing `sites` outside Adam."""
+        """Recompute the site records (and the packed buffer) after changing
+        `sites` outside Adam."""
         site_records(self.sites, self.n_slots, self.rec, stream)
+        if self.packed is not None:
+            pack_sites(self.sites, self.n_slots, self.packed, stream)
 
     def propagate(self, jump: int, pass_index: int, stream=None):
-        topk_propagate(self.rec, self.n_slots, self.maps[self.cur], self.maps[1 - self.cur], self.W, self.H,
+        topk_propagate(self.sel, self.n_slots, self.maps[self.cur], self.maps[1 - self.cur], self.W, self.H,
                        jump, pass_index, self.seed, self.n_inject, stream, self.cell)
         self.cur = 1 - self.cur
 
@@ -464,7 +515,7 @@ class Fitter:
         render_bwd(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, self.grad, self.loss, self.rgb,
                    stream, self.cell)
         adam_step(self.sites, self.m, self.v, self.grad, self.n_slots, it + 1, self.W * self.H, self.W, self.H,
-                  self.adam, self.rec, stream)
+                  self.adam, self.rec, stream, self.packed)
         self.it += 1
 
     def densify(self, cfg: BudgetConfig | None = None, stream=None):

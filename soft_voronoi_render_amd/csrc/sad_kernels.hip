@@ -159,10 +159,51 @@ __device__ __forceinline__ float geom_score(const float4 &g0, const float4 &g1, 
     return s * q - s * g0.z;
 }
 
+// Selection site formats: the candidate kernels score either from the 64-byte
+// records (their first 32 bytes) or from the 16-byte packed candidate-site buffer
+// of float16 pairs (summary, Appendix B.2 "Packed candidate sites"): words
+// (x, y), (log tau, r), (dir_x, dir_y), (a, 0), first field in the low half.  Both
+// yield the same scoring record (x, y, r, Ux | Uy, Vx, Vy, -); decoding the packed
+// words costs a few VALU per fetch and halves the bytes fetched per candidate.
+constexpr int SEL_REC = SAD_SEL_REC64, SEL_PACKED = SAD_SEL_PACKED16;
+
+__device__ __forceinline__ float half_lo(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16)); }
+
+// Scoring record of site `id`; for the packed format `G` indexes 16-byte words.
+template <int FMT>
+__device__ __forceinline__ void load_sel(const float4 *__restrict__ G, uint32_t id, float4 &g0, float4 &g1)
+{
+    if constexpr (FMT == SEL_REC) {
+        g0 = G[RLD4 * (size_t)id];
+        g1 = G[RLD4 * (size_t)id + 1];
+    } else {
+        const float4 v = G[id];
+        const uint32_t w0 = __float_as_uint(v.x), w1 = __float_as_uint(v.y), w2 = __float_as_uint(v.z),
+                       w3 = __float_as_uint(v.w);
+        const float dx = half_lo(w2), dy = half_hi(w2), a = half_lo(w3);
+        const float n2 = dx * dx + dy * dy;
+        float ux = 1.0f, uy = 0.0f;
+        if (n2 >= 1e-30f) {
+            const float inv = hw_rsq(n2);
+            ux = dx * inv;
+            uy = dy * inv;
+        }
+        const float sE = __expf(0.5f * a), siE = __expf(-0.5f * a);
+        g0 = make_float4(half_lo(w0), half_hi(w0), half_hi(w1), sE * ux);
+        g1 = make_float4(sE * uy, siE * ux, siE * uy, 0.0f);
+    }
+}
+
+template <int FMT>
 __device__ __forceinline__ float geom_score_id(const float4 *__restrict__ G, uint32_t id, float X, float Y, float s,
                                                bool &usable)
 {
-    const float4 g0 = G[RLD4 * (size_t)id], g1 = G[RLD4 * (size_t)id + 1];
+    float4 g0, g1;
+    load_sel<FMT>(G, id, g0, g1);
     usable = !(g0.x < 0.0f);
     return geom_score(g0, g1, X, Y, s);
 }
@@ -178,6 +219,26 @@ __global__ __launch_bounds__(256) void k_site_records(const float *__restrict__ 
 #pragma unroll
     for (int j = 0; j < RLD4; ++j)
         G[RLD4 * (size_t)i + j] = o[j];
+}
+
+// Packed candidate-site words of slot i (binary16, round to nearest even, as the
+// conversion instruction does by default); an inactive slot (x < 0) packs x = -1.
+__device__ __forceinline__ uint32_t f16_bits(float v) { return __builtin_bit_cast(unsigned short, (_Float16)v); }
+
+__device__ __forceinline__ uint4 pack_site(const float *__restrict__ S, long st, int i)
+{
+    const float x = S[i];
+    const uint32_t hx = x < 0.0f ? 0xBC00u : f16_bits(x);
+    return make_uint4(hx | (f16_bits(S[st + i]) << 16), f16_bits(S[PLT * st + i]) | (f16_bits(S[PR * st + i]) << 16),
+                      f16_bits(S[PDX * st + i]) | (f16_bits(S[PDY * st + i]) << 16), f16_bits(S[PA * st + i]));
+}
+
+__global__ __launch_bounds__(256) void k_pack_sites(const float *__restrict__ S, int n_slots, int stride,
+                                                    uint4 *__restrict__ P)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n_slots)
+        P[i] = pack_site(S, stride, i);
 }
 
 // ---------------------------------------------------------------------------
@@ -401,7 +462,7 @@ __device__ __forceinline__ void region_pixel(int r, int c0, int r0, int jump, in
     }
 }
 
-template <int KK, int TB>
+template <int KK, int TB, int FMT>
 __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ G, uint32_t n_slots,
                                                      const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
                                                      int H, int jump, uint32_t seed_h, int n_inject, float s, float sx,
@@ -447,10 +508,8 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
     {
         const uint32_t c = L.t.key[tid];
         float4 g0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), g1 = g0;
-        if (c != NONE) {
-            g0 = G[RLD4 * (size_t)c];
-            g1 = G[RLD4 * (size_t)c + 1];
-        }
+        if (c != NONE)
+            load_sel<FMT>(G, c, g0, g1);
         g1.w = __uint_as_float(c);
         __syncthreads();
         if (c != NONE) {
@@ -501,7 +560,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
         if (ref != REF_NONE && ref >= (uint32_t)TB) {
             const uint32_t c = ref & ~REF_SPILL;
             bool usable;
-            const float d = geom_score_id(G, c, X, Y, s, usable);
+            const float d = geom_score_id<FMT>(G, c, X, Y, s, usable);
             best.consider(c, d, usable);
         }
     }
@@ -548,7 +607,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
             best.consider_new(id, d, usable);
         } else {
             const uint32_t c = ref & ~REF_SPILL;
-            const float d = geom_score_id(G, c, X, Y, s, usable);
+            const float d = geom_score_id<FMT>(G, c, X, Y, s, usable);
             best.consider(c, d, usable);
         }
     }
@@ -561,7 +620,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
             const uint32_t c = (uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32);
             if (c < n_slots) {
                 bool usable;
-                const float d = geom_score_id(G, c, X, Y, s, usable);
+                const float d = geom_score_id<FMT>(G, c, X, Y, s, usable);
                 best.consider(c, d, usable);
             }
         }
@@ -577,7 +636,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
 // through the same (d, ID) selection with a duplicate check.  TW x TW map entries
 // per workgroup: 16 for maps large enough to fill the chip with 16x16 tiles, 8
 // for small (downscaled) maps, which would otherwise leave most CUs idle.
-template <int TW>
+template <int TW, int FMT>
 __global__ __launch_bounds__(TW *TW) void k_propagate_direct(const float4 *__restrict__ G, uint32_t n_slots,
                                                              const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
                                                              int W, int H, int jump, uint32_t seed_h, int n_inject,
@@ -607,7 +666,7 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(const float4 *__res
             // nearby pixels share most of their sites)
             if (ids[k] < n_slots && !best.holds(ids[k])) {
                 bool usable;
-                const float d = geom_score_id(G, ids[k], X, Y, s, usable);
+                const float d = geom_score_id<FMT>(G, ids[k], X, Y, s, usable);
                 best.consider_new(ids[k], d, usable);
             }
         }
@@ -620,7 +679,7 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(const float4 *__res
             const uint32_t c = (uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32);
             if (c < n_slots) {
                 bool usable;
-                const float d = geom_score_id(G, c, X, Y, s, usable);
+                const float d = geom_score_id<FMT>(G, c, X, Y, s, usable);
                 best.consider(c, d, usable);
             }
         }
@@ -651,6 +710,7 @@ __global__ __launch_bounds__(256) void k_fill_map(uint4 *__restrict__ cand, long
         cand[i] = make_uint4(NONE, NONE, NONE, NONE);
 }
 
+template <int FMT>
 __global__ __launch_bounds__(256) void k_jfa_seed_round(const float4 *__restrict__ G, uint32_t n_slots,
                                                         unsigned long long *__restrict__ keys, int W, int H,
                                                         float s, MapGrid mg, int round)
@@ -658,7 +718,8 @@ __global__ __launch_bounds__(256) void k_jfa_seed_round(const float4 *__restrict
     const uint32_t i = blockIdx.x * 256u + threadIdx.x;
     if (i >= n_slots)
         return;
-    const float4 g0 = G[RLD4 * (size_t)i], g1 = G[RLD4 * (size_t)i + 1];
+    float4 g0, g1;
+    load_sel<FMT>(G, i, g0, g1);
     if (!(g0.x >= 0.0f) || !finitef(g0.x) || !finitef(g0.y))
         return;  // inactive (x < 0), or no position
     // the map entry of the pixel that holds the site
@@ -692,6 +753,7 @@ __global__ __launch_bounds__(256) void k_jfa_seed_finish(uint4 *__restrict__ can
 // go to entries 0..3, the sentinel to 4..7.  Each list is read by at most one
 // pixel of a tile at steps >= 16, so candidates are scored straight from their
 // records, as in the table-free propagation.
+template <int FMT>
 __global__ __launch_bounds__(BLOCK) void k_jfa_pass(const float4 *__restrict__ G, uint32_t n_slots,
                                                     const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
                                                     int H, int step, float s, float sx, float sy, int tiles_x,
@@ -718,7 +780,7 @@ __global__ __launch_bounds__(BLOCK) void k_jfa_pass(const float4 *__restrict__ G
             // an ID already held is skipped before its record is fetched
             if (ids[k] < n_slots && !best.holds(ids[k])) {
                 bool usable;
-                const float d = geom_score_id(G, ids[k], X, Y, s, usable);
+                const float d = geom_score_id<FMT>(G, ids[k], X, Y, s, usable);
                 best.consider_new(ids[k], d, usable);
             }
         }
@@ -731,6 +793,7 @@ __global__ __launch_bounds__(BLOCK) void k_jfa_pass(const float4 *__restrict__ G
 // ---------------------------------------------------------------------------
 // Exact top-K by brute force: every slot is scored for every pixel.  Scoring
 // records are staged through LDS 256 at a time.
+template <int FMT>
 __global__ __launch_bounds__(BLOCK) void k_topk_exact(const float4 *__restrict__ G, uint32_t n_slots,
                                                       uint4 *__restrict__ cout, int W, int H, float s, float sx,
                                                       float sy, int tiles_x, int nb)
@@ -748,10 +811,8 @@ __global__ __launch_bounds__(BLOCK) void k_topk_exact(const float4 *__restrict__
     for (uint32_t base = 0; base < n_slots; base += BLOCK) {
         const uint32_t i = base + threadIdx.x;
         float4 g0 = make_float4(-1.0f, 0.0f, 0.0f, 0.0f), g1 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (i < n_slots) {
-            g0 = G[RLD4 * (size_t)i];
-            g1 = G[RLD4 * (size_t)i + 1];
-        }
+        if (i < n_slots)
+            load_sel<FMT>(G, i, g0, g1);
         __syncthreads();
         l0[threadIdx.x] = g0;
         l1[threadIdx.x] = g1;
@@ -1538,8 +1599,8 @@ struct AdamArgs {
 };
 
 __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__restrict__ M, float *__restrict__ V,
-                                              float *__restrict__ G, float4 *__restrict__ rec, int n_slots,
-                                              int stride, AdamArgs A)
+                                              float *__restrict__ G, float4 *__restrict__ rec,
+                                              uint4 *__restrict__ packed, int n_slots, int stride, AdamArgs A)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= n_slots)
@@ -1579,6 +1640,8 @@ __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__re
         for (int j = 0; j < RLD4; ++j)
             rec[RLD4 * (size_t)i + j] = o[j];
     }
+    if (packed)
+        packed[i] = pack_site(S, st, i);
 }
 
 // ---------------------------------------------------------------------------
@@ -1637,6 +1700,42 @@ inline int launched()
     return hipGetLastError() == hipSuccess ? SAD_OK : SAD_ERR_DEVICE;
 }
 
+inline bool valid_fmt(int f) { return f == SEL_REC || f == SEL_PACKED; }
+
+struct PropArgs {
+    const float4 *G;
+    uint32_t n;
+    const uint4 *ci;
+    uint4 *co;
+    int Wm, Hm, cell, jump;
+    uint32_t seed_h;
+    int n_inject;
+    float s, sx, sy;
+};
+
+// Measured on kodak768: the tile table pays off only at jump 1, where the
+// neighbour lists are the tile's own lists; from jump 2 on the table-free pass
+// is as fast or faster (random cold-start lists: 90 vs 113 us at jump 2).  On a
+// downscaled map (cell > 1) a 16x16 tile spans c^2 times the pixels, so its
+// lists name more sites than the table holds: there every pass is table-free,
+// on 8x8 tiles when 16x16 ones would leave CUs idle.
+template <int FMT>
+void launch_propagate(const PropArgs &A, hipStream_t hs)
+{
+    const TileGrid g = tile_grid(A.Wm, A.Hm);
+    if (A.cell > 1 && g.nb < SMALL_MAP_TILES) {
+        const TileGrid g8 = tile_grid(A.Wm, A.Hm, 8);
+        hipLaunchKernelGGL((k_propagate_direct<8, FMT>), dim3(g8.nb), dim3(64), 0, hs, A.G, A.n, A.ci, A.co, A.Wm,
+                           A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g8.tiles_x, g8.nb);
+    } else if (A.cell == 1 && A.jump == 1) {
+        hipLaunchKernelGGL((k_propagate<1, 256, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.G, A.n, A.ci, A.co, A.Wm,
+                           A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
+    } else {
+        hipLaunchKernelGGL((k_propagate_direct<TILE, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.G, A.n, A.ci, A.co,
+                           A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
+    }
+}
+
 uint32_t host_pcg_hash(uint32_t v)
 {
     const uint32_t state = v * 747796405u + 2891336453u;
@@ -1679,13 +1778,30 @@ int sad_site_records(const float *sites, int n_slots, int stride, float *rec, vo
     return launched();
 }
 
-int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
-                       int cell, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream)
+int sad_pack_sites(const float *sites, int n_slots, int stride, uint32_t *packed, void *stream)
+{
+    int rc;
+    if ((rc = check_sites(n_slots, stride)))
+        return rc;
+    if (n_slots == 0)
+        return SAD_OK;
+    if (!sites || !packed)
+        return SAD_ERR_ARG;
+    if (!aligned16(packed))
+        return SAD_ERR_ALIGN;
+    hipLaunchKernelGGL(k_pack_sites, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, n_slots,
+                       stride, (uint4 *)packed);
+    return launched();
+}
+
+int sad_topk_propagate(const float *rec, int sel_fmt, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W,
+                       int H, int cell, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0 || jump < 1 || jump > 0xFFFF || n_inject < 0 || n_inject > SAD_MAX_INJECT || cell < 1)
+    if (n_slots < 0 || jump < 1 || jump > 0xFFFF || n_inject < 0 || n_inject > SAD_MAX_INJECT || cell < 1 ||
+        !valid_fmt(sel_fmt))
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
@@ -1701,47 +1817,23 @@ int sad_topk_propagate(const float *rec, int n_slots, const uint32_t *cand_in, u
         return SAD_ERR_ARG;
     if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(rec))
         return SAD_ERR_ALIGN;
-    const TileGrid g = tile_grid(Wm, Hm);
     const uint32_t pw = ((uint32_t)jump << 16) | (pass_index & 0xFFFFu);
     const uint32_t seed_h = host_pcg_hash(host_pcg_hash(seed) ^ pw);
-    // Narrow strips (small jumps) need a smaller region buffer and site table, so
-    // more workgroups fit on a CU.
-    const float sc = scale_of(W, H);
-    const hipStream_t hs = (hipStream_t)stream;
-    const float4 *G = (const float4 *)rec;
-    const uint4 *ci = (const uint4 *)cand_in;
-    uint4 *co = (uint4 *)cand_out;
-    // Measured on kodak768: the tile table pays off only at jump 1, where the
-    // neighbour lists are the tile's own lists; from jump 2 on the table-free pass
-    // is as fast or faster (random cold-start lists: 90 vs 113 us at jump 2).  On a
-    // downscaled map (cell > 1) a 16x16 tile spans c^2 times the pixels, so its
-    // lists name more sites than the table holds: there every pass is table-free,
-    // on 8x8 tiles when 16x16 ones would leave CUs idle.
-    if (cell > 1) {
-        if (g.nb < SMALL_MAP_TILES) {
-            const TileGrid g8 = tile_grid(Wm, Hm, 8);
-            hipLaunchKernelGGL(k_propagate_direct<8>, dim3(g8.nb), dim3(64), 0, hs, G, (uint32_t)n_slots, ci, co, Wm,
-                               Hm, jump, seed_h, n_inject, sc, mg.sx, mg.sy, g8.tiles_x, g8.nb);
-        } else {
-            hipLaunchKernelGGL(k_propagate_direct<TILE>, dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co,
-                               Wm, Hm, jump, seed_h, n_inject, sc, mg.sx, mg.sy, g.tiles_x, g.nb);
-        }
-    } else if (jump == 1) {
-        hipLaunchKernelGGL((k_propagate<1, 256>), dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, Wm,
-                           Hm, jump, seed_h, n_inject, sc, mg.sx, mg.sy, g.tiles_x, g.nb);
-    } else {
-        hipLaunchKernelGGL(k_propagate_direct<TILE>, dim3(g.nb), dim3(BLOCK), 0, hs, G, (uint32_t)n_slots, ci, co, Wm,
-                           Hm, jump, seed_h, n_inject, sc, mg.sx, mg.sy, g.tiles_x, g.nb);
-    }
+    const PropArgs A{(const float4 *)rec, (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm,
+                     cell, jump, seed_h, n_inject, scale_of(W, H), mg.sx, mg.sy};
+    if (sel_fmt == SEL_PACKED)
+        launch_propagate<SEL_PACKED>(A, (hipStream_t)stream);
+    else
+        launch_propagate<SEL_REC>(A, (hipStream_t)stream);
     return launched();
 }
 
-int sad_jfa_seed(const float *rec, int n_slots, uint32_t *cand, int W, int H, int cell, void *stream)
+int sad_jfa_seed(const float *rec, int sel_fmt, int n_slots, uint32_t *cand, int W, int H, int cell, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0 || cell < 1)
+    if (n_slots < 0 || cell < 1 || !valid_fmt(sel_fmt))
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
@@ -1757,20 +1849,27 @@ int sad_jfa_seed(const float *rec, int n_slots, uint32_t *cand, int W, int H, in
     const hipStream_t hs = (hipStream_t)stream;
     hipLaunchKernelGGL(k_fill_map, dim3((unsigned)((2 * P + 255) / 256)), dim3(256), 0, hs, (uint4 *)cand, 2 * P);
     if (n_slots > 0)
-        for (int r = 0; r < JFA_KEEP; ++r)
-            hipLaunchKernelGGL(k_jfa_seed_round, dim3((n_slots + 255) / 256), dim3(256), 0, hs, (const float4 *)rec,
-                               (uint32_t)n_slots, (unsigned long long *)cand, W, H, scale_of(W, H), mg, r);
+        for (int r = 0; r < JFA_KEEP; ++r) {
+            if (sel_fmt == SEL_PACKED)
+                hipLaunchKernelGGL(k_jfa_seed_round<SEL_PACKED>, dim3((n_slots + 255) / 256), dim3(256), 0, hs,
+                                   (const float4 *)rec, (uint32_t)n_slots, (unsigned long long *)cand, W, H,
+                                   scale_of(W, H), mg, r);
+            else
+                hipLaunchKernelGGL(k_jfa_seed_round<SEL_REC>, dim3((n_slots + 255) / 256), dim3(256), 0, hs,
+                                   (const float4 *)rec, (uint32_t)n_slots, (unsigned long long *)cand, W, H,
+                                   scale_of(W, H), mg, r);
+        }
     hipLaunchKernelGGL(k_jfa_seed_finish, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, hs, (uint4 *)cand, P);
     return launched();
 }
 
-int sad_jfa_pass(const float *rec, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H, int cell,
-                 int step, void *stream)
+int sad_jfa_pass(const float *rec, int sel_fmt, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
+                 int cell, int step, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0 || step < 1 || step > 0xFFFF || cell < 1)
+    if (n_slots < 0 || step < 1 || step > 0xFFFF || cell < 1 || !valid_fmt(sel_fmt))
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
@@ -1787,18 +1886,23 @@ int sad_jfa_pass(const float *rec, int n_slots, const uint32_t *cand_in, uint32_
     if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(Wm, Hm);
-    hipLaunchKernelGGL(k_jfa_pass, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
-                       (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm, step, scale_of(W, H),
-                       mg.sx, mg.sy, g.tiles_x, g.nb);
+    if (sel_fmt == SEL_PACKED)
+        hipLaunchKernelGGL(k_jfa_pass<SEL_PACKED>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream,
+                           (const float4 *)rec, (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm,
+                           step, scale_of(W, H), mg.sx, mg.sy, g.tiles_x, g.nb);
+    else
+        hipLaunchKernelGGL(k_jfa_pass<SEL_REC>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
+                           (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm, step, scale_of(W, H),
+                           mg.sx, mg.sy, g.tiles_x, g.nb);
     return launched();
 }
 
-int sad_topk_exact(const float *rec, int n_slots, uint32_t *cand_out, int W, int H, int cell, void *stream)
+int sad_topk_exact(const float *rec, int sel_fmt, int n_slots, uint32_t *cand_out, int W, int H, int cell, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0 || cell < 1)
+    if (n_slots < 0 || cell < 1 || !valid_fmt(sel_fmt))
         return SAD_ERR_ARG;
     if (W == 0 || H == 0)
         return SAD_OK;
@@ -1811,8 +1915,14 @@ int sad_topk_exact(const float *rec, int n_slots, uint32_t *cand_out, int W, int
     if (!aligned16(cand_out) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(Wm, Hm);
-    hipLaunchKernelGGL(k_topk_exact, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
-                       (uint32_t)n_slots, (uint4 *)cand_out, Wm, Hm, scale_of(W, H), mg.sx, mg.sy, g.tiles_x, g.nb);
+    if (sel_fmt == SEL_PACKED)
+        hipLaunchKernelGGL(k_topk_exact<SEL_PACKED>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream,
+                           (const float4 *)rec, (uint32_t)n_slots, (uint4 *)cand_out, Wm, Hm, scale_of(W, H), mg.sx,
+                           mg.sy, g.tiles_x, g.nb);
+    else
+        hipLaunchKernelGGL(k_topk_exact<SEL_REC>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream,
+                           (const float4 *)rec, (uint32_t)n_slots, (uint4 *)cand_out, Wm, Hm, scale_of(W, H), mg.sx,
+                           mg.sy, g.tiles_x, g.nb);
     return launched();
 }
 
@@ -1890,8 +2000,8 @@ int sad_densify_stats(const float *rec, int n_slots, const uint32_t *cand, const
     return launched();
 }
 
-int sad_adam_step(float *sites, float *m, float *v, float *grad, float *rec, int n_slots, int stride, int step,
-                  int n_pixels, int W, int H, const sad_adam_cfg *cfg, void *stream)
+int sad_adam_step(float *sites, float *m, float *v, float *grad, float *rec, uint32_t *packed, int n_slots, int stride,
+                  int step, int n_pixels, int W, int H, const sad_adam_cfg *cfg, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
@@ -1900,7 +2010,7 @@ int sad_adam_step(float *sites, float *m, float *v, float *grad, float *rec, int
         return SAD_ERR_ARG;
     if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f && cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f && cfg->eps >= 0.0f))
         return SAD_ERR_ARG;
-    if (!aligned16(grad) || !aligned16(rec))
+    if (!aligned16(grad) || !aligned16(rec) || !aligned16(packed))
         return SAD_ERR_ALIGN;
     if (n_slots == 0)
         return SAD_OK;
@@ -1916,7 +2026,7 @@ int sad_adam_step(float *sites, float *m, float *v, float *grad, float *rec, int
     A.W = (float)W;
     A.H = (float)H;
     hipLaunchKernelGGL(k_adam, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, m, v, grad,
-                       (float4 *)rec, n_slots, stride, A);
+                       (float4 *)rec, (uint4 *)packed, n_slots, stride, A);
     return launched();
 }
 

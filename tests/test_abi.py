@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.sad_abi_version() == 3
+    assert L.sad_abi_version() == 4
     assert L.sad_status_string(0) == b"ok"
     assert L.sad_status_string(ERR_ALIGN) == b"misaligned pointer"
     assert L.sad_status_string(12345) == b"unknown status"
@@ -54,12 +54,12 @@ Q = 0x90000
 
 def test_propagate_rejects_bad_arguments(L):
     f = L.sad_topk_propagate
-    ok = dict(rec=P, n=4, a=P, b=Q, W=16, H=16, cell=1, jump=1, pidx=0, seed=0, m=4)
+    ok = dict(rec=P, fmt=0, n=4, a=P, b=Q, W=16, H=16, cell=1, jump=1, pidx=0, seed=0, m=4)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["rec"], a["n"], a["a"], a["b"], a["W"], a["H"], a["cell"], a["jump"], a["pidx"], a["seed"], a["m"],
-                 None)
+        return f(a["rec"], a["fmt"], a["n"], a["a"], a["b"], a["W"], a["H"], a["cell"], a["jump"], a["pidx"], a["seed"],
+                 a["m"], None)
 
     assert call(jump=0) == ERR_ARG
     assert call(jump=65536) == ERR_ARG
@@ -82,6 +82,9 @@ def test_propagate_rejects_bad_arguments(L):
     assert call(cell=0, W=0) == ERR_ARG  # the cell size is checked before the empty image
     # overlap is judged on the map's size: 16x16 pixels in cells of 4 -> 4x4 lists, 512 bytes
     assert call(cell=4, b=P + 480) == ERR_ARG
+    assert call(fmt=2) == ERR_ARG        # unknown site format
+    assert call(fmt=-1) == ERR_ARG
+    assert call(fmt=1, rec=P + 8) == ERR_ALIGN
 
 
 def test_render_and_adam_reject_bad_arguments(L):
@@ -96,43 +99,52 @@ def test_render_and_adam_reject_bad_arguments(L):
     assert L.sad_render_bwd(P, 4, P + 4, Q, 16, 16, 1, Q, None, None, None) == ERR_ALIGN
     assert L.sad_render_bwd(P, 4, P, Q, 16, 16, 1, Q + 4, None, None, None) == ERR_ALIGN  # grad records
     assert L.sad_render_bwd(P, 4, P, Q, 16, 16, 0, Q, None, None, None) == ERR_ARG  # cell 0
-    assert L.sad_topk_exact(P, 4, P + 4, 16, 16, 1, None) == ERR_ALIGN
-    assert L.sad_topk_exact(P, -1, P, 16, 16, 1, None) == ERR_ARG
-    assert L.sad_topk_exact(P, 4, P, 16, 16, 0, None) == ERR_ARG
+    assert L.sad_topk_exact(P, 0, 4, P + 4, 16, 16, 1, None) == ERR_ALIGN
+    assert L.sad_topk_exact(P, 0, -1, P, 16, 16, 1, None) == ERR_ARG
+    assert L.sad_topk_exact(P, 0, 4, P, 16, 16, 0, None) == ERR_ARG
+    assert L.sad_topk_exact(P, 5, 4, P, 16, 16, 1, None) == ERR_ARG  # unknown site format
+    assert L.sad_pack_sites(P, 4, 8, P + 4, None) == ERR_ALIGN
+    assert L.sad_pack_sites(P, 9, 8, P, None) == ERR_ARG
+    assert L.sad_pack_sites(0, 4, 8, P, None) == ERR_ARG
+    assert L.sad_pack_sites(P, 4, 8, 0, None) == ERR_ARG
+    assert L.sad_pack_sites(0, 0, 8, 0, None) == 0  # no slots: no-op
     assert L.sad_site_records(P, 4, 8, P + 4, None) == ERR_ALIGN
     assert L.sad_site_records(P, 9, 8, P, None) == ERR_ARG
     assert L.sad_site_records(0, 4, 8, P, None) == ERR_ARG
     assert L.sad_site_records(0, 0, 8, 0, None) == 0  # no slots: no-op
     cfg = sad.AdamConfig().to_c()
     A = L.sad_adam_step
-    assert A(P, P, P, P, P, 4, 8, 0, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # step 0
-    assert A(P, P, P, P, P, 4, 8, 1, 0, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # no pixels
-    assert A(P, P, P, P, P, 4, 8, 1, 10, 4, 4, None, None) == ERR_ARG
-    assert A(P, P, P, P + 4, P, 4, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ALIGN
-    assert A(P, P, P, P, P + 4, 4, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ALIGN
+    assert A(P, P, P, P, P, None, 4, 8, 0, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # step 0
+    assert A(P, P, P, P, P, None, 4, 8, 1, 0, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # no pixels
+    assert A(P, P, P, P, P, None, 4, 8, 1, 10, 4, 4, None, None) == ERR_ARG
+    assert A(P, P, P, P + 4, P, None, 4, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ALIGN
+    assert A(P, P, P, P, P + 4, None, 4, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ALIGN
     bad = sad.AdamConfig(beta1=1.0).to_c()
-    assert A(P, P, P, P, P, 4, 8, 1, 10, 4, 4, ctypes.byref(bad), None) == ERR_ARG
-    assert A(P, P, P, P, None, 0, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == 0  # no slots: no-op
+    assert A(P, P, P, P, P, None, 4, 8, 1, 10, 4, 4, ctypes.byref(bad), None) == ERR_ARG
+    assert A(P, P, P, P, None, None, 0, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == 0  # no slots: no-op
+    assert A(P, P, P, P, P, P + 4, 4, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ALIGN  # packed
 
 
 def test_jfa_entry_points_reject_bad_arguments(L):
     S, J = L.sad_jfa_seed, L.sad_jfa_pass
-    assert S(P, -1, P, 16, 16, 1, None) == ERR_ARG
-    assert S(0, 4, P, 16, 16, 1, None) == ERR_ARG
-    assert S(P, 4, 0, 16, 16, 1, None) == ERR_ARG
-    assert S(P, 4, P + 4, 16, 16, 1, None) == ERR_ALIGN
-    assert S(P + 8, 4, P, 16, 16, 1, None) == ERR_ALIGN
-    assert S(P, 4, P, 70000, 16, 1, None) == ERR_ARG
-    assert S(P, 4, P, 0, 16, 1, None) == 0                      # empty image: no-op
-    assert J(P, 4, P, Q, 16, 16, 1, 0, None) == ERR_ARG         # step 0
-    assert J(P, 4, P, Q, 16, 16, 1, 65536, None) == ERR_ARG
-    assert J(P, 4, P, P + 32, 16, 16, 1, 1, None) == ERR_ARG     # overlapping maps
-    assert J(P, 4, P + 4, Q, 16, 16, 1, 1, None) == ERR_ALIGN
-    assert J(P, -1, P, Q, 16, 16, 1, 1, None) == ERR_ARG
-    assert J(P, 4, P, Q, 16, 0, 1, 1, None) == 0
-    assert S(P, 4, P, 16, 16, 0, None) == ERR_ARG            # cell 0
-    assert J(P, 4, P, Q, 16, 16, 0, 1, None) == ERR_ARG
-    assert J(P, 4, P, P + 256, 16, 16, 2, 1, None) == ERR_ARG  # 8x8 lists of 32 bytes overlap
+    assert S(P, 0, -1, P, 16, 16, 1, None) == ERR_ARG
+    assert S(0, 0, 4, P, 16, 16, 1, None) == ERR_ARG
+    assert S(P, 0, 4, 0, 16, 16, 1, None) == ERR_ARG
+    assert S(P, 0, 4, P + 4, 16, 16, 1, None) == ERR_ALIGN
+    assert S(P + 8, 0, 4, P, 16, 16, 1, None) == ERR_ALIGN
+    assert S(P, 0, 4, P, 70000, 16, 1, None) == ERR_ARG
+    assert S(P, 0, 4, P, 0, 16, 1, None) == 0                      # empty image: no-op
+    assert J(P, 0, 4, P, Q, 16, 16, 1, 0, None) == ERR_ARG         # step 0
+    assert J(P, 0, 4, P, Q, 16, 16, 1, 65536, None) == ERR_ARG
+    assert J(P, 0, 4, P, P + 32, 16, 16, 1, 1, None) == ERR_ARG     # overlapping maps
+    assert J(P, 0, 4, P + 4, Q, 16, 16, 1, 1, None) == ERR_ALIGN
+    assert J(P, 0, -1, P, Q, 16, 16, 1, 1, None) == ERR_ARG
+    assert J(P, 0, 4, P, Q, 16, 0, 1, 1, None) == 0
+    assert S(P, 0, 4, P, 16, 16, 0, None) == ERR_ARG            # cell 0
+    assert J(P, 0, 4, P, Q, 16, 16, 0, 1, None) == ERR_ARG
+    assert J(P, 0, 4, P, P + 256, 16, 16, 2, 1, None) == ERR_ARG  # 8x8 lists of 32 bytes overlap
+    assert S(P, 3, 4, P, 16, 16, 1, None) == ERR_ARG         # unknown site format
+    assert J(P, 3, 4, P, Q, 16, 16, 1, 1, None) == ERR_ARG
 
 
 def test_densify_entry_points_reject_bad_arguments(L):
