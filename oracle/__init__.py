@@ -74,6 +74,7 @@ def lib():
             "orc_adam_step": (None, [f64p, f64p, f64p, f64p, c_int, c_int, c_int, c_int, f64p, c_dbl, c_dbl,
                                      c_dbl, c_int, c_int]),
             "orc_densify_stats": (None, [f64p, c_int, c_int, u32p, f32p, c_int, c_int, c_int, f64p]),
+            "orc_query_points": (None, [f64p, c_int, c_int, u32p, c_int, c_int, c_int, f32p, c_long, f64p]),
             "orc_jfa_seed": (None, [f32p, c_int, c_int, c_int, c_int, c_int, u32p]),
             "orc_jfa_pass": (None, [f32p, c_int, c_int, u32p, u32p, c_int, c_int, c_int, c_int]),
             "orc_jfa_pass_pixels": (None, [f32p, c_int, c_int, u32p, c_int, c_int, c_int, c_int, u32p, c_long,
@@ -290,6 +291,19 @@ def densify_stats(sites, n_slots, cand, target, W, H, stats=None, cell=1):
     return stats
 
 
+def query_points(sites, n_slots, cand, W, H, pts, cell=1) -> np.ndarray:
+    """Blend at arbitrary points (float32 [n][2], px) with the list of each point's
+    map entry; float64 [n][3]."""
+    S = _f64(sites)
+    cand = _u32(cand)
+    assert cand.shape == map_shape(W, H, cell)
+    P = _f32(pts).reshape(-1, 2)
+    out = np.empty((P.shape[0], 3), dtype=np.float64)
+    lib().orc_query_points(_p(S, ctypes.c_double), n_slots, S.shape[1], _p(cand, ctypes.c_uint32), W, H, cell,
+                           _p(P, ctypes.c_float), P.shape[0], _p(out, ctypes.c_double))
+    return out
+
+
 # ------------------------------------------------------------ JFA prepass
 def jfa_seed(sites, n_slots, W, H, cell=1) -> np.ndarray:
     """Seed pass: each active site into the list of its map entry, <= 4 per entry."""
@@ -348,3 +362,4 @@ def jfa_steps(W: int, H: int, cell: int = 1) -> list:
 
 from .densify import densify_prune  # noqa: E402  (pure Python, no C)
 from .packed import pack_words, rounded_sites  # noqa: E402  (numpy only)
+from .evalpack import eval_decode, eval_encode  # noqa: E402  (numpy only)

@@ -169,7 +169,8 @@ typedef struct {
     int degenerate_dir;
 } geo64;
 
-static void score_f64(const double *S, long stride, uint32_t id, int col, int row, int W, int H, geo64 *g)
+/* at the point (X, Y) px */
+static void score_f64_at(const double *S, long stride, uint32_t id, double X, double Y, int W, int H, geo64 *g)
 {
     double px = S[P_X * stride + id], py = S[P_Y * stride + id];
     double r = S[P_R * stride + id];
@@ -189,13 +190,19 @@ static void score_f64(const double *S, long stride, uint32_t id, int col, int ro
     }
     g->vx = -g->uy;
     g->vy = g->ux;
-    g->ddx = ((double)col + 0.5) - px;
-    g->ddy = ((double)row + 0.5) - py;
+    g->ddx = X - px;
+    g->ddy = Y - py;
     g->al = g->ux * g->ddx + g->uy * g->ddy;
     g->be = g->vx * g->ddx + g->vy * g->ddy;
     g->E = exp(a);
     g->q = sqrt(g->E * g->al * g->al + g->be * g->be / g->E);
     g->d = s * g->q - s * r;
+}
+
+/* at the centre of pixel (col, row) */
+static void score_f64(const double *S, long stride, uint32_t id, int col, int row, int W, int H, geo64 *g)
+{
+    score_f64_at(S, stride, id, (double)col + 0.5, (double)row + 0.5, W, H, g);
 }
 
 /* A list entry takes part if it names a slot below n_slots whose x (plane 0) is
@@ -437,8 +444,9 @@ typedef struct {
     double Z, chat[3];
 } pix64;
 
-static void forward_pixel(const double *S, uint32_t n_slots, long stride, const uint32_t *lst, int W, int H,
-                          int col, int row, pix64 *P)
+/* The blend of list `lst` at the point (X, Y) px. */
+static void forward_point(const double *S, uint32_t n_slots, long stride, const uint32_t *lst, int W, int H,
+                          double X, double Y, pix64 *P)
 {
     P->n = 0;
     for (int k = 0; k < ORC_K; ++k) {
@@ -446,7 +454,7 @@ static void forward_pixel(const double *S, uint32_t n_slots, long stride, const 
         if (!site_usable64(S, id, n_slots))
             continue;
         int j = P->n;
-        score_f64(S, stride, id, col, row, W, H, &P->g[j]);
+        score_f64_at(S, stride, id, X, Y, W, H, &P->g[j]);
         double tau = exp(S[P_LOGTAU * stride + id]);
         double l = -tau * P->g[j].d;
         double c0 = S[P_CR * stride + id], c1 = S[P_CG * stride + id], c2 = S[P_CB * stride + id];
@@ -476,6 +484,38 @@ static void forward_pixel(const double *S, uint32_t n_slots, long stride, const 
         P->w[j] = P->e[j] / P->Z;
         for (int c = 0; c < 3; ++c)
             P->chat[c] += P->w[j] * P->c[j][c];
+    }
+}
+
+/* The blend of pixel (col, row): at its centre. */
+static void forward_pixel(const double *S, uint32_t n_slots, long stride, const uint32_t *lst, int W, int H,
+                          int col, int row, pix64 *P)
+{
+    forward_point(S, n_slots, stride, lst, W, H, (double)col + 0.5, (double)row + 0.5, P);
+}
+
+/* Random-access query (the abstract's "fast random access"; [SUM] B.3 "Candidate
+ * field": integer mapping of a position to its map entry).  Point i, (pts[2i],
+ * pts[2i+1]) px, reads the list of the map entry of the pixel that holds it
+ * (coordinates clamped into the image first) and is blended at the point itself.
+ * A point with a non-finite coordinate returns (0, 0, 0). */
+void orc_query_points(const double *S, int n_slots, int stride, const uint32_t *cand, int W, int H, int cell,
+                      const float *pts, long n, double *rgb)
+{
+    grid g = make_grid(W, H, cell);
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (long i = 0; i < n; ++i) {
+        double X = pts[2 * i], Y = pts[2 * i + 1];
+        rgb[3 * i] = rgb[3 * i + 1] = rgb[3 * i + 2] = 0.0;
+        if (!isfinite(X) || !isfinite(Y))
+            continue;
+        double cx = X < 0.0 ? 0.0 : (X > (double)(W - 1) ? (double)(W - 1) : X);
+        double cy = Y < 0.0 ? 0.0 : (Y > (double)(H - 1) ? (double)(H - 1) : Y);
+        int col = (int)floor(cx), row = (int)floor(cy);
+        pix64 P;
+        forward_point(S, (uint32_t)n_slots, stride, cand + cell_of(&g, col, row) * ORC_K, W, H, X, Y, &P);
+        for (int c = 0; c < 3; ++c)
+            rgb[3 * i + c] = P.chat[c];
     }
 }
 
