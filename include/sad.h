@@ -95,7 +95,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 4
+#define SAD_ABI_VERSION 5
 #define SAD_K 8
 #define SAD_INVALID 0xffffffffu
 #define SAD_NPARAM 10
@@ -329,6 +329,66 @@ int sad_densify_stats(const float *rec, int n_slots, const uint32_t *cand, const
 int sad_densify_prune(float *sites, float *m, float *v, int stride, int capacity, int *n_slots, const float *stats,
                       const float *removal, uint32_t *cand, int W, int H, int cell, const float *target,
                       const sad_budget_cfg *cfg, int *n_split, int *n_pruned);
+
+/*
+ * Evaluation format ([SUM] B.2 "Packed storage for evaluation": all ten values in
+ * four 32-bit words, quantised, with per-image min/scale for log tau and r;
+ * [PRESS] 5: 15-bit fixed-point coordinates, colour in 11/11/10 bits, 16 bits for
+ * the temperature, the radius and the direction angle, float16 anisotropy):
+ *   words [n_slots][4] uint32:
+ *     w0 = qx | qy << 15 | inactive << 31      w1 = qR | qG << 11 | qB << 22
+ *     w2 = q_logtau | q_r << 16                w3 = q_angle | f16(a) << 16
+ *   header float[4] = {lt_min, lt_step, r_min, r_step}, step = (max - min)/65535
+ *   over the active slots' finite values (0, 0 if none; a zero extreme is +0).
+ * Codes: q = rint(t) (nearest even) clamped to [0, qmax], NaN -> 0, with t one
+ * float32 product: x * (32767/W), y * (32767/H), R and G * 2047, B * 1023,
+ * (log tau - lt_min) * (65535/(lt_max - lt_min)) (0 if max <= min), r likewise.
+ * The direction is an axis (u and -u give one metric): theta = atan2(dy, dx) in
+ * float64 folded into [0, pi), q = rint(theta * 65536/pi) mod 65536; 0 for a
+ * degenerate direction (dx^2 + dy^2 < 1e-30).  a is IEEE binary16, nearest even.
+ * An inactive slot (x < 0) is w0 = 1 << 31, w1 = w2 = w3 = 0.
+ * Decoding (float32, each operation rounded on its own): x = qx * (W/32767),
+ * y = qy * (H/32767), R = qR * (1/2047), G likewise, B = qB * (1/1023), log tau =
+ * lt_min + q * lt_step, r = r_min + q * r_step, theta = q * (pi/65536), dir =
+ * (cos theta, sin theta), a from binary16.
+ */
+
+/*
+ * sad_eval_encode -- packs slots [0, n_slots) of `sites` into the evaluation
+ * format: per-image ranges first, then one word quad per slot, then the header.
+ *   sites device [10][stride] read-only; words device [n_slots][4] uint32, written,
+ *   16-byte aligned; header device float[4], written (used as scratch during the
+ *   call), 16-byte aligned.  W, H >= 1 (the position scale).
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
+ */
+int sad_eval_encode(const float *sites, int n_slots, int stride, int W, int H, uint32_t *words, float *header,
+                    void *stream);
+
+/*
+ * sad_eval_decode -- the site planes the evaluation words stand for (decoding
+ * above); an inactive slot gets x = y = -1 and zeros.
+ *   words device [n_slots][4] and header device float[4], read-only, 16-byte
+ *   aligned; sites device [10][stride] float, slots [0, n_slots) written.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
+ */
+int sad_eval_decode(const uint32_t *words, const float *header, int n_slots, int W, int H, float *sites, int stride,
+                    void *stream);
+
+/*
+ * sad_eval_query -- random access ([SUM] abstract: fast random access; B.3
+ * integer mapping of a position to its map entry).  Point i, (points[2i],
+ * points[2i+1]) in pixels, reads the list of the map entry of the pixel that holds
+ * it (coordinates clamped into the image) and is the softmax blend of those sites,
+ * decoded from the evaluation words, evaluated at the point itself (the render's
+ * score and blend; at a pixel centre it is that pixel's render).  A point with a
+ * non-finite coordinate gives (0, 0, 0).
+ *   words [n_slots][4], header float[4], cand [Hm][Wm][8] (16-byte aligned);
+ *   points device float [n_points][2], 8-byte aligned; out_rgb device float
+ *   [n_points][3], written.  0 <= n_points <= 2^31 - 256.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
+ */
+int sad_eval_query(const uint32_t *words, const float *header, int n_slots, const uint32_t *cand, int W, int H,
+                   int cell, const float *points, int64_t n_points, float *out_rgb, void *stream);
 
 /*
  * sad_adam_step -- Adam (Kingma & Ba 2015) on the ten site parameters, with the

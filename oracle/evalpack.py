@@ -25,7 +25,7 @@ Readings (the pages give the field widths, nothing more):
      degenerate direction (dx^2 + dy^2 < 1e-30) stores 0.
   E4 a: IEEE binary16, nearest even.
   E5 header (per image): float32 [lt_min, lt_step, r_min, r_step] with step =
-     (max - min) / 65535.
+     (max - min) / 65535 (a zero extreme is stored as +0).
   E6 decoding in float32, each operation rounded separately: x = qx * (W / 32767),
      y = qy * (H / 32767), R = qR * (1 / 2047), G likewise, B = qB * (1 / 1023),
      log tau = lt_min + q * lt_step, r = r_min + q * r_step, theta = q * (pi / 65536),
@@ -50,7 +50,7 @@ def _range(v, active):
     v = v[active & np.isfinite(v)]
     if v.size == 0:
         return f32(0), f32(0)
-    return f32(v.min()), f32(v.max())
+    return f32(v.min()) + f32(0), f32(v.max()) + f32(0)  # a zero extreme is +0
 
 
 def eval_encode(sites, n_slots, W, H):

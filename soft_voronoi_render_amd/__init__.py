@@ -100,6 +100,12 @@ def lib() -> ctypes.CDLL:
         L.sad_site_records.restype = i32
         L.sad_site_records.argtypes = [fp, i32, i32, fp, vp]
         L.sad_topk_propagate.restype = i32
+        L.sad_eval_encode.restype = i32
+        L.sad_eval_encode.argtypes = [fp, i32, i32, i32, i32, vp, fp, vp]
+        L.sad_eval_decode.restype = i32
+        L.sad_eval_decode.argtypes = [vp, fp, i32, i32, i32, fp, i32, vp]
+        L.sad_eval_query.restype = i32
+        L.sad_eval_query.argtypes = [vp, fp, i32, vp, i32, i32, i32, fp, ctypes.c_int64, fp, vp]
         L.sad_pack_sites.restype = i32
         L.sad_pack_sites.argtypes = [fp, i32, i32, vp, vp]
         L.sad_topk_propagate.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, i32, u32, u32, i32, vp]
@@ -128,7 +134,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("sad_abi_version", "sad_status_string", "sad_site_records", "sad_topk_propagate", "sad_topk_exact",
             "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_densify_stats", "sad_densify_prune", "sad_jfa_seed",
-            "sad_jfa_pass", "sad_pack_sites")
+            "sad_jfa_pass", "sad_pack_sites", "sad_eval_encode", "sad_eval_decode", "sad_eval_query")
 
 
 # --------------------------------------------------------------- marshalling
@@ -395,6 +401,53 @@ def densify_prune(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, ta
     if rc not in (SAD_OK, SAD_ERR_CAPACITY):
         raise SadError("sad_densify_prune", rc)
     return ns.value, nsp.value, npr.value, rc
+
+
+# ------------------------------------------------- evaluation format and queries
+def new_eval(capacity: int, device="cuda"):
+    """Storage for the evaluation format: words uint32 [capacity][4] (held as
+    int32) and the per-image header float32 [4]."""
+    return (torch.zeros((max(capacity, 1), 4), dtype=torch.int32, device=device),
+            torch.zeros(4, dtype=torch.float32, device=device))
+
+
+def _words(words, n_slots):
+    if words.dim() != 2 or words.shape[1] != 4 or words.shape[0] < n_slots:
+        raise ValueError("words must be int32 [>= n_slots][4]")
+    return _dev(words, "words", _U32)
+
+
+def _header(header):
+    if header.numel() != 4:
+        raise ValueError("header must hold 4 float32")
+    return _dev(header, "header", _F32)
+
+
+def eval_encode(sites, n_slots, W, H, words, header, stream=None):
+    """Packs slots [0, n_slots) into the 16-byte evaluation format (see sad_eval_encode)."""
+    sp, stride = _sites(sites, n_slots)
+    _check("sad_eval_encode", lib().sad_eval_encode(sp, n_slots, stride, W, H, _words(words, n_slots),
+                                                    _header(header), _stream(stream)))
+
+
+def eval_decode(words, header, n_slots, W, H, sites, stream=None):
+    """The site planes the evaluation words stand for (see sad_eval_decode)."""
+    sp, stride = _sites(sites, n_slots)
+    _check("sad_eval_decode", lib().sad_eval_decode(_words(words, n_slots), _header(header), n_slots, W, H, sp,
+                                                    stride, _stream(stream)))
+
+
+def eval_query(words, header, n_slots, cand, W, H, points, out_rgb, stream=None, cell=1):
+    """Colour at arbitrary points (float32 [n][2], px) from the evaluation words and
+    a candidate map (see sad_eval_query)."""
+    if points.dim() != 2 or points.shape[1] != 2:
+        raise ValueError("points must be float32 [n][2]")
+    n = points.shape[0]
+    c = _dev(cand, "cand", _U32, map_shape(W, H, cell))
+    pp = _dev(points, "points", _F32)
+    o = _dev(out_rgb, "out_rgb", _F32, (n, 3))
+    _check("sad_eval_query", lib().sad_eval_query(_words(words, n_slots), _header(header), n_slots, c, W, H, cell,
+                                                  pp, n, o, _stream(stream)))
 
 
 def jump_schedule(W: int, H: int, n: int, cell: int = 1) -> list:

@@ -1591,6 +1591,260 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restric
 }
 
 // ---------------------------------------------------------------------------
+// 16-byte evaluation format (summary, Appendix B.2 "Packed storage for
+// evaluation"; press article, section 5: 15-bit fixed-point coordinates, colour in
+// 11/11/10 bits, 16 bits each for log tau and r with per-image min/scale, a 16-bit
+// direction angle, float16 anisotropy) and the random-access query.
+//   w0 = qx | qy << 15 | inactive << 31      w1 = qR | qG << 11 | qB << 22
+//   w2 = q_logtau | q_r << 16                w3 = q_angle | f16(a) << 16
+// Codes are rint (nearest even) of one float32 product (log tau and r: of
+// (v - min) * inv), clamped to [0, qmax] with NaN -> 0.  The direction is an axis:
+// the angle of atan2(dy, dx) folded into [0, pi), coded in float64 (float32 atan2
+// implementations differ by an ulp, which would move codes near ties).
+constexpr int EV_QPOS = 32767, EV_QRG = 2047, EV_QB = 1023, EV_Q16 = 65535;
+
+__device__ __forceinline__ uint32_t ev_key(float v)  // order-preserving bits
+{
+    uint32_t u = __float_as_uint(v + 0.0f);
+    return u ^ ((u & 0x80000000u) ? 0xFFFFFFFFu : 0x80000000u);
+}
+__device__ __forceinline__ float ev_unkey(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+__device__ __forceinline__ uint32_t ev_quant(float t, float qmax)
+{
+    t = rintf(t);
+    t = (t >= 0.0f) ? t : 0.0f;  // NaN -> 0
+    return (uint32_t)fminf(t, qmax);
+}
+
+// keys: [lt_min, lt_max, r_min, r_max] as order-preserving bits (min starts at
+// all ones, max at 0); a min still all ones afterwards means no finite value.
+__global__ __launch_bounds__(64) void k_eval_range_init(uint32_t *__restrict__ keys)
+{
+    if (threadIdx.x < 4)
+        keys[threadIdx.x] = (threadIdx.x & 1) ? 0u : 0xFFFFFFFFu;
+}
+
+__global__ __launch_bounds__(256) void k_eval_range(const float *__restrict__ S, int n_slots, int stride,
+                                                    uint32_t *__restrict__ keys)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    uint32_t kmin[2] = {0xFFFFFFFFu, 0xFFFFFFFFu}, kmax[2] = {0u, 0u};
+    if (i < n_slots && !(S[i] < 0.0f)) {
+        const float v[2] = {S[PLT * (long)stride + i], S[PR * (long)stride + i]};
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+            if (finitef(v[f])) {
+                kmin[f] = ev_key(v[f]);
+                kmax[f] = kmin[f];
+            }
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            kmin[f] = min(kmin[f], (uint32_t)__shfl_xor((int)kmin[f], o));
+            kmax[f] = max(kmax[f], (uint32_t)__shfl_xor((int)kmax[f], o));
+        }
+    }
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            if (kmin[f] != 0xFFFFFFFFu)
+                atomicMin(keys + 2 * f, kmin[f]);
+            if (kmax[f] != 0u)
+                atomicMax(keys + 2 * f + 1, kmax[f]);
+        }
+    }
+}
+
+__device__ __forceinline__ void ev_range(const uint32_t *keys, int f, float &m, float &M)
+{
+    if (keys[2 * f] == 0xFFFFFFFFu) {
+        m = M = 0.0f;
+    } else {
+        m = ev_unkey(keys[2 * f]);
+        M = ev_unkey(keys[2 * f + 1]);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_eval_encode(const float *__restrict__ S, int n_slots, int stride, float sxe,
+                                                     float sye, const uint32_t *__restrict__ keys,
+                                                     uint4 *__restrict__ words)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_slots)
+        return;
+    const long st = stride;
+    const float x = S[i];
+    if (x < 0.0f) {
+        words[i] = make_uint4(0x80000000u, 0u, 0u, 0u);
+        return;
+    }
+    float lm, lM, rm, rM;
+    ev_range(keys, 0, lm, lM);
+    ev_range(keys, 1, rm, rM);
+    const float linv = lM > lm ? (float)EV_Q16 / (lM - lm) : 0.0f;
+    const float rinv = rM > rm ? (float)EV_Q16 / (rM - rm) : 0.0f;
+    const uint32_t qx = ev_quant(x * sxe, (float)EV_QPOS), qy = ev_quant(S[st + i] * sye, (float)EV_QPOS);
+    const uint32_t qr = ev_quant(S[PCR * st + i] * (float)EV_QRG, (float)EV_QRG);
+    const uint32_t qg = ev_quant(S[PCG * st + i] * (float)EV_QRG, (float)EV_QRG);
+    const uint32_t qb = ev_quant(S[PCB * st + i] * (float)EV_QB, (float)EV_QB);
+    const uint32_t ql = ev_quant((S[PLT * st + i] - lm) * linv, (float)EV_Q16);
+    const uint32_t qd = ev_quant((S[PR * st + i] - rm) * rinv, (float)EV_Q16);
+    const double dx = S[PDX * st + i], dy = S[PDY * st + i];
+    uint32_t qa = 0;
+    if (!(__dadd_rn(__dmul_rn(dx, dx), __dmul_rn(dy, dy)) < 1e-30)) {
+        double th = atan2(dy, dx);
+        if (th < 0.0)
+            th += 3.141592653589793;
+        const double t = rint(th * (65536.0 / 3.141592653589793));
+        qa = __builtin_isfinite(t) ? (uint32_t)(long long)t & 0xFFFFu : 0u;
+    }
+    words[i] = make_uint4(qx | (qy << 15), qr | (qg << 11) | (qb << 22), ql | (qd << 16),
+                          qa | (f16_bits(S[PA * st + i]) << 16));
+}
+
+// keys -> header [lt_min, lt_step, r_min, r_step], step = (max - min) / 65535.
+__global__ __launch_bounds__(64) void k_eval_header(uint32_t *__restrict__ keys)
+{
+    if (threadIdx.x != 0)
+        return;
+    float lm, lM, rm, rM;
+    ev_range(keys, 0, lm, lM);
+    ev_range(keys, 1, rm, rM);
+    float *h = reinterpret_cast<float *>(keys);
+    h[0] = lm;
+    h[1] = (lM - lm) / (float)EV_Q16;
+    h[2] = rm;
+    h[3] = (rM - rm) / (float)EV_Q16;
+}
+
+// Decoded site, float32, each operation rounded on its own (no contraction) so
+// that every value is reproducible: position, colour, log tau, r, angle, a.
+struct EvSite {
+    float x, y, lt, r, c0, c1, c2, th, a;
+    bool active;
+};
+
+__device__ __forceinline__ EvSite ev_decode(uint4 w, const float4 &hd, float dxe, float dye)
+{
+#pragma clang fp contract(off)  // log tau and r: a rounded product, then a rounded sum
+    EvSite e;
+    e.active = (w.x >> 31) == 0u;
+    e.x = (float)(w.x & 0x7FFFu) * dxe;
+    e.y = (float)((w.x >> 15) & 0x7FFFu) * dye;
+    e.c0 = (float)(w.y & 0x7FFu) * (1.0f / (float)EV_QRG);
+    e.c1 = (float)((w.y >> 11) & 0x7FFu) * (1.0f / (float)EV_QRG);
+    e.c2 = (float)(w.y >> 22) * (1.0f / (float)EV_QB);
+    const float qlt = (float)(w.z & 0xFFFFu) * hd.y, qr = (float)(w.z >> 16) * hd.w;
+    e.lt = hd.x + qlt;
+    e.r = hd.z + qr;
+    e.th = (float)(w.w & 0xFFFFu) * (float)(3.141592653589793 / 65536.0);
+    e.a = half_hi(w.w);
+    return e;
+}
+
+__global__ __launch_bounds__(256) void k_eval_decode(const uint4 *__restrict__ words, const float4 *__restrict__ hdr,
+                                                     int n_slots, float dxe, float dye, float *__restrict__ S,
+                                                     int stride)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_slots)
+        return;
+    const long st = stride;
+    const EvSite e = ev_decode(words[i], hdr[0], dxe, dye);
+    float v[SAD_NPARAM] = {-1.0f, -1.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (e.active) {
+        float sn, cs;
+        sincosf(e.th, &sn, &cs);
+        v[PX] = e.x;
+        v[PY] = e.y;
+        v[PLT] = e.lt;
+        v[PR] = e.r;
+        v[PCR] = e.c0;
+        v[PCG] = e.c1;
+        v[PCB] = e.c2;
+        v[PDX] = cs;
+        v[PDY] = sn;
+        v[PA] = e.a;
+    }
+#pragma unroll
+    for (int j = 0; j < SAD_NPARAM; ++j)
+        S[j * st + i] = v[j];
+}
+
+// Random-access query: point i reads the list of the map entry of the pixel that
+// holds it (coordinates clamped into the image) and blends its sites, decoded
+// from the evaluation words, at the point itself (the render's score and
+// max-subtracted softmax).  A non-finite coordinate returns 0.
+__global__ __launch_bounds__(256) void k_eval_query(const uint4 *__restrict__ words, const float4 *__restrict__ hdr,
+                                                    uint32_t n_slots, const uint4 *__restrict__ cand, int W, int H,
+                                                    MapGrid mg, const float2 *__restrict__ pts, long n_pts,
+                                                    float *__restrict__ out, float s, float dxe, float dye)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_pts)
+        return;
+    const float2 P = pts[i];
+    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f;
+    if (finitef(P.x) && finitef(P.y)) {
+        const int col = (int)floorf(fminf(fmaxf(P.x, 0.0f), (float)(W - 1)));
+        const int row = (int)floorf(fminf(fmaxf(P.y, 0.0f), (float)(H - 1)));
+        const long q = mg.entry((long)row * W + col, col, row);
+        const uint4 la = cand[2 * q], lb = cand[2 * q + 1];
+        const uint32_t ids[K] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+        const float4 hd = hdr[0];
+        float l[K], c0[K], c1[K], c2[K];
+        float mx = -__builtin_huge_valf();
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            l[k] = -__builtin_huge_valf();
+            c0[k] = c1[k] = c2[k] = 0.0f;
+            if (ids[k] >= n_slots)
+                continue;
+            const EvSite e = ev_decode(words[ids[k]], hd, dxe, dye);
+            if (!e.active)
+                continue;
+            float sn, cs;
+            sincosf(e.th, &sn, &cs);
+            const float ex = P.x - e.x, ey = P.y - e.y;
+            const float al = fmaf(cs, ex, sn * ey), be = fmaf(cs, ey, -(sn * ex));
+            const float E = __expf(e.a), iE = __expf(-e.a);
+            const float d = fmaf(s, hw_sqrt(fmaf(E * al, al, iE * be * be)), -(s * e.r));
+            const float lk = -__expf(e.lt) * d;
+            if (!finitef(lk))
+                continue;
+            l[k] = lk;
+            c0[k] = e.c0;
+            c1[k] = e.c1;
+            c2[k] = e.c2;
+            mx = fmaxf(mx, lk);
+        }
+        if (mx > -__builtin_huge_valf()) {
+            float Z = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const float ek = l[k] > -__builtin_huge_valf() ? __expf(l[k] - mx) : 0.0f;
+                Z += ek;
+                o0 = fmaf(ek, c0[k], o0);
+                o1 = fmaf(ek, c1[k], o1);
+                o2 = fmaf(ek, c2[k], o2);
+            }
+            const float iZ = hw_rcp(Z);  // Z >= 1
+            o0 *= iZ;
+            o1 *= iZ;
+            o2 *= iZ;
+        }
+    }
+    out[3 * i] = o0;
+    out[3 * i + 1] = o1;
+    out[3 * i + 2] = o2;
+}
+
+// ---------------------------------------------------------------------------
 // Adam (Kingma & Ba 2015) on the ten site parameters, gradients divided by the
 // pixel count (summary, B.4), gradient planes 0..9 zeroed in the same pass.
 struct AdamArgs {
@@ -2027,6 +2281,76 @@ int sad_adam_step(float *sites, float *m, float *v, float *grad, float *rec, uin
     A.H = (float)H;
     hipLaunchKernelGGL(k_adam, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, m, v, grad,
                        (float4 *)rec, (uint4 *)packed, n_slots, stride, A);
+    return launched();
+}
+
+int sad_eval_encode(const float *sites, int n_slots, int stride, int W, int H, uint32_t *words, float *header,
+                    void *stream)
+{
+    int rc;
+    if ((rc = check_sites(n_slots, stride)) || (rc = check_image(W, H)))
+        return rc;
+    if (W < 1 || H < 1 || !header || (n_slots > 0 && (!sites || !words)))
+        return SAD_ERR_ARG;
+    if (!aligned16(words) || !aligned16(header))
+        return SAD_ERR_ALIGN;
+    const hipStream_t hs = (hipStream_t)stream;
+    uint32_t *keys = reinterpret_cast<uint32_t *>(header);
+    hipLaunchKernelGGL(k_eval_range_init, dim3(1), dim3(64), 0, hs, keys);
+    if (n_slots > 0) {
+        hipLaunchKernelGGL(k_eval_range, dim3((n_slots + 255) / 256), dim3(256), 0, hs, sites, n_slots, stride, keys);
+        hipLaunchKernelGGL(k_eval_encode, dim3((n_slots + 255) / 256), dim3(256), 0, hs, sites, n_slots, stride,
+                           (float)EV_QPOS / (float)W, (float)EV_QPOS / (float)H, (const uint32_t *)keys,
+                           (uint4 *)words);
+    }
+    hipLaunchKernelGGL(k_eval_header, dim3(1), dim3(64), 0, hs, keys);
+    return launched();
+}
+
+int sad_eval_decode(const uint32_t *words, const float *header, int n_slots, int W, int H, float *sites, int stride,
+                    void *stream)
+{
+    int rc;
+    if ((rc = check_sites(n_slots, stride)) || (rc = check_image(W, H)))
+        return rc;
+    if (W < 1 || H < 1)
+        return SAD_ERR_ARG;
+    if (n_slots == 0)
+        return SAD_OK;
+    if (!words || !header || !sites)
+        return SAD_ERR_ARG;
+    if (!aligned16(words) || !aligned16(header))
+        return SAD_ERR_ALIGN;
+    hipLaunchKernelGGL(k_eval_decode, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4 *)words, (const float4 *)header, n_slots, (float)W / (float)EV_QPOS,
+                       (float)H / (float)EV_QPOS, sites, stride);
+    return launched();
+}
+
+int sad_eval_query(const uint32_t *words, const float *header, int n_slots, const uint32_t *cand, int W, int H,
+                   int cell, const float *points, int64_t n_points, float *out_rgb, void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)))
+        return rc;
+    if (n_slots < 0 || cell < 1 || n_points < 0 || W < 1 || H < 1)
+        return SAD_ERR_ARG;
+    MapGrid mg;
+    int Wm, Hm;
+    if (!map_grid(W, H, cell, mg, Wm, Hm))
+        return SAD_ERR_ARG;
+    if (n_points == 0)
+        return SAD_OK;
+    if (!header || !cand || !points || !out_rgb || (n_slots > 0 && !words))
+        return SAD_ERR_ARG;
+    if (!aligned16(words) || !aligned16(header) || !aligned16(cand) || ((uintptr_t)points & 7u))
+        return SAD_ERR_ALIGN;
+    if (n_points > (int64_t)0x7FFFFF00)  // one point per lane, at most 2^23 workgroups
+        return SAD_ERR_ARG;
+    hipLaunchKernelGGL(k_eval_query, dim3((unsigned)((n_points + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4 *)words, (const float4 *)header, (uint32_t)n_slots, (const uint4 *)cand, W, H, mg,
+                       (const float2 *)points, (long)n_points, out_rgb, scale_of(W, H), (float)W / (float)EV_QPOS,
+                       (float)H / (float)EV_QPOS);
     return launched();
 }
 

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.sad_abi_version() == 4
+    assert L.sad_abi_version() == 5
     assert L.sad_status_string(0) == b"ok"
     assert L.sad_status_string(ERR_ALIGN) == b"misaligned pointer"
     assert L.sad_status_string(12345) == b"unknown status"
@@ -169,6 +169,27 @@ def test_densify_entry_points_reject_bad_arguments(L):
     assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 0, 4, 1, P, ctypes.byref(cfg), None, None) == ERR_ARG
     assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 0, P, ctypes.byref(cfg), None, None) == ERR_ARG
     assert n.value == 4
+
+
+def test_eval_entry_points_reject_bad_arguments(L):
+    E, D, Qy = L.sad_eval_encode, L.sad_eval_decode, L.sad_eval_query
+    assert E(P, 4, 8, 16, 16, P + 4, Q, None) == ERR_ALIGN     # words
+    assert E(P, 4, 8, 16, 16, P, Q + 4, None) == ERR_ALIGN     # header
+    assert E(P, 4, 8, 0, 16, P, Q, None) == ERR_ARG            # W = 0: no position scale
+    assert E(P, 9, 8, 16, 16, P, Q, None) == ERR_ARG           # n_slots > stride
+    assert E(P, 4, 8, 16, 16, P, 0, None) == ERR_ARG           # header NULL
+    assert E(0, 4, 8, 16, 16, P, Q, None) == ERR_ARG
+    assert D(P + 4, Q, 4, 16, 16, P, 8, None) == ERR_ALIGN
+    assert D(P, Q, 9, 16, 16, P, 8, None) == ERR_ARG
+    assert D(P, Q, 0, 16, 16, 0, 8, None) == 0                 # no slots: no-op
+    assert D(0, Q, 4, 16, 16, P, 8, None) == ERR_ARG
+    assert Qy(P, Q, 4, P, 16, 16, 1, P, 0, Q, None) == 0       # no points: no-op
+    assert Qy(P, Q, 4, P, 16, 16, 0, P, 5, Q, None) == ERR_ARG  # cell 0
+    assert Qy(P, Q, 4, P, 16, 16, 1, P, -1, Q, None) == ERR_ARG
+    assert Qy(P, Q, 4, P, 16, 16, 1, P + 4, 5, Q, None) == ERR_ALIGN  # points need 8 bytes
+    assert Qy(P, Q, 4, P + 8, 16, 16, 1, P, 5, Q, None) == ERR_ALIGN  # cand needs 16
+    assert Qy(P, Q, 4, P, 16, 16, 1, P, 2 ** 31, Q, None) == ERR_ARG
+    assert Qy(P, Q, 4, P, 16, 16, 1, 0, 5, Q, None) == ERR_ARG
 
 
 def test_python_binding_refuses_cpu_tensors():
