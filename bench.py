@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "soft_voronoi_render_amd", "csrc", "sad_kernels.hip")
 # kernel symbol of each timed launch (as rocprofv3 names it)
-KERNEL_SYMBOL = {"propagate": "k_propagate<1,256>", "fwd_bwd": "k_render_bwd", "adam": "k_adam", "fwd": "k_render_fwd"}
+KERNEL_SYMBOL = {"propagate": "k_propagate<1,256,0>", "fwd_bwd": "k_render_bwd", "adam": "k_adam",
+                 "fwd": "k_render_fwd"}
 
 
 def source_digest():
@@ -40,23 +41,37 @@ def source_digest():
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def _profile_rows(path, tag):
+    """(source digest, {kernel: fields}) of the `tag kernel=... k=v ...` lines of a
+    committed profile summary."""
+    rows, digest = {}, None
+    if os.path.exists(path):
+        for line in open(path):
+            line = line.strip()
+            if line.startswith("source_sha256:"):
+                digest = line.split(":", 1)[1].strip()
+            elif line.startswith(tag + " "):
+                kv = dict(f.split("=", 1) for f in line.split()[1:])
+                rows[kv["kernel"]] = kv
+    return digest, rows
+
+
+def measured_valu_issue(workload, kernel):
+    """Fraction of the VALU issue cycles a launch uses (SQ_INSTS_VALU x 4 cycles over
+    1024 SIMDs x duration x 2.4 GHz) from the committed counter summary, or None when
+    there is none or the kernel source has changed since."""
+    digest, rows = _profile_rows(os.path.join(ROOT, "profiles", f"valu_issue_{workload}.txt"), "valu")
+    if digest != source_digest() or KERNEL_SYMBOL[kernel] not in rows:
+        return None
+    return float(rows[KERNEL_SYMBOL[kernel]]["issue_frac"])
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by the same counters on a plain copy of
     known size), or None when there is none for this kernel and workload or the
     kernel source has changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
-    if not os.path.exists(path):
-        return None
-    rows = {}
-    digest = None
-    for line in open(path):
-        line = line.strip()
-        if line.startswith("source_sha256:"):
-            digest = line.split(":", 1)[1].strip()
-        elif line.startswith("traffic "):
-            kv = dict(f.split("=", 1) for f in line.split()[1:])
-            rows[kv["kernel"]] = kv
+    digest, rows = _profile_rows(os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt"), "traffic")
     if digest != source_digest() or KERNEL_SYMBOL[kernel] not in rows:
         return None
     return float(rows[KERNEL_SYMBOL[kernel]]["bytes_per_launch"])
@@ -259,7 +274,8 @@ def main():
     dominant = max(step_kernels, key=kdur.get)
     achieved = kb[dominant] / kdur[dominant] / 1e9
     kernels = {k: {"us": round(kdur[k] * 1e6, 3), "GBps": round(kb[k] / kdur[k] / 1e9, 1),
-                   "hbm_frac": round(kb[k] / kdur[k] / 1e9 / HBM_PEAK_GBS, 4)} for k in kdur}
+                   "hbm_frac": round(kb[k] / kdur[k] / 1e9 / HBM_PEAK_GBS, 4),
+                   "valu_issue_frac": measured_valu_issue(wl.name, k)} for k in kdur}
 
     out = {
         "metric": "Mpixel-iters/s (propagate+fwd+bwd+Adam, K=8) and % of HBM peak",
@@ -285,7 +301,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(wl.name, dominant),
-                     "algorithmic_bytes_per_launch": kb[dominant]},
+                     "algorithmic_bytes_per_launch": kb[dominant],
+                     "valu_issue_frac": measured_valu_issue(wl.name, dominant)},
     }
 
     if not args.no_cpu_baseline:
