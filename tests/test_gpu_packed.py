@@ -195,3 +195,32 @@ def test_packed_kodak768_fit():
             torch.cuda.synchronize()
             assert torch.equal(f.packed[:n], fresh[:n])
     assert res[True][0] > res[False][0] - 0.3
+
+
+@pytest.mark.parametrize("W,H,n,cell", [(130, 70, 2000, 2), (77, 45, 300, 4)])
+def test_packed_grid_exact_and_jfa(orc, W, H, n, cell):
+    """The packed buffer on a downscaled map: exact top-8 and the jump-flood seed and
+    last flood passes against the oracle on the rounded sites and the same grid."""
+    print(f"packed grid W={W} H={H} n={n} cell={cell}", flush=True)
+    S = _sites(n, W, H, 99)
+    T = oracle.rounded_sites(S, n)
+    pk = _packed(S, n)
+    Hm, Wm, _ = sad.map_shape(W, H, cell)
+    pix = np.arange(Wm * Hm, dtype=np.uint32)
+    ex = sad.new_map(W, H, pk.device, cell=cell)
+    sad.topk_exact(pk, n, ex, W, H, cell=cell)
+    sd = sad.new_map(W, H, pk.device, cell=cell)
+    sad.jfa_seed(pk, n, sd, W, H, cell=cell)
+    torch.cuda.synchronize()
+    assert compare_lists(orc, T, n, W, H, pix, map_to_host(ex), orc.topk_exact(T, n, W, H, cell=cell),
+                         cell=cell) <= 1
+    seed_ref = orc.jfa_seed(T, n, W, H, cell=cell)
+    assert compare_lists(orc, T, n, W, H, pix, map_to_host(sd), seed_ref, cell=cell) <= 1
+    for k in sad.jfa_steps(W, H, cell=cell)[-2:]:
+        x = to_dev(seed_ref)
+        y = sad.new_map(W, H, x.device, cell=cell)
+        sad.jfa_pass(pk, n, x, y, W, H, k, cell=cell)
+        torch.cuda.synchronize()
+        ref = orc.jfa_pass(T, n, seed_ref, W, H, k, cell=cell)
+        u, cnt = orc.jfa_union_pixels(T, n, seed_ref, W, H, k, pix, cell=cell)
+        assert compare_lists(orc, T, n, W, H, pix, map_to_host(y), ref, u, cnt, cell=cell) <= 2
