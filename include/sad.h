@@ -1,7 +1,10 @@
 /*
  * sad.h -- C ABI of libsad, the MI355X (gfx950) hot path of Soft Anisotropic
- * Diagrams (SAD): per-pixel top-K candidate maintenance, the temperature-softmax
- * render, its analytic backward, and Adam.
+ * Diagrams (SAD): top-K candidate maintenance (propagation with injection, the
+ * optional jump-flood prepass, the exact top-K; per pixel or on a downscaled
+ * grid), the temperature-softmax render, its analytic backward, Adam, budget
+ * control, the packed candidate-site buffer, and the 16-byte evaluation format
+ * with random-access point queries.
  *
  * Sources (the pages the method is described on):
  *   [SUM]   paperlayer.ai summary of arXiv:2604.21984v2, sections 3-5 and Appendix B
@@ -13,9 +16,11 @@
  * ---------------------------------------
  * Ownership.  The caller owns every buffer.  The library allocates no memory and
  *   keeps no state between calls, so calls are reentrant.
- * Pointers.  Arguments named `sites`, `rec`, `cand*`, `out_rgb`, `target`, `grad`,
- *   `m`, `v` and `loss_sum` are DEVICE pointers (HBM of the current HIP device).
- *   `cfg` is a HOST pointer, read before the call returns.
+ * Pointers.  Arguments named `sites`, `rec`, `packed`, `cand*`, `out_rgb`,
+ *   `target`, `grad`, `m`, `v`, `loss_sum`, `stats`, `words`, `header` and `points`
+ *   are DEVICE pointers (HBM of the current HIP device), except in
+ *   sad_densify_prune, which works on HOST copies.  `cfg` is a HOST pointer, read
+ *   before the call returns.
  * Streams.  Device work is enqueued asynchronously on `stream` (a hipStream_t
  *   passed as void*; NULL = the legacy default stream).  A return of SAD_OK means
  *   the launch was accepted, not that the kernel finished.
