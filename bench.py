@@ -187,7 +187,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the SAD hot path here is built and measured on a single "
-              "MI355X (multi-GPU banding is a design note, not part of this build).", file=sys.stderr)
+              "MI355X; sharding by image bands across GPUs is designed but not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch

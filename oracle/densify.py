@@ -6,7 +6,8 @@ children offset along a covariance- or Sobel-gradient axis; children take the
 target colour, reduced log tau and r, fresh Adam state; prune the sites with the
 smallest removal score by setting their position to (-1, -1)), the reading
 note's key design 4 and the press article's section 4.  The pages give no
-constants; the rules and defaults below are our reading (stated in the design doc).
+constants; the rules and defaults below are our reading, each stated at the
+point where it is applied.
 
 PARITY UNPINNED against the pages: there is no second source for these rules;
 the tests pin only invariants (counts, symmetry of the children about the

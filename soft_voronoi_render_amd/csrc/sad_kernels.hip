@@ -1,10 +1,14 @@
 // sad_kernels.hip -- gfx950 kernels and the C ABI of libsad (declared in include/sad.h).
 //
-// Soft Anisotropic Diagrams (SAD): per-pixel top-K candidate maintenance, the
-// temperature-softmax render, its analytic backward and Adam.  Formulas follow
-// the woaixuexisr.github.io reading note ("Key designs" 1-4), the luckyiyi.github.io
-// project page ("Method") and the paperlayer.ai summary (sections 4-5, Appendix B);
-// each kernel names the passage it implements.
+// Soft Anisotropic Diagrams (SAD): top-K candidate maintenance (propagation with
+// injection, the jump-flood prepass, the exact top-K; per pixel or on a
+// downscaled grid), the temperature-softmax render, its analytic backward, Adam,
+// budget-control statistics, the packed candidate-site buffer and the 16-byte
+// evaluation format with random-access queries.  Formulas follow the
+// woaixuexisr.github.io reading note ("Key designs" 1-4), the luckyiyi.github.io
+// project page ("Method"), the paperlayer.ai summary (sections 4-5, Appendix B)
+// and the 69574.cn article (section 5); each kernel names the passage it
+// implements.
 //
 // Execution model: image-space kernels cover the image with 16x16-pixel tiles,
 // one 256-thread workgroup (four wave64s) per tile, one pixel per lane.  Tiles
@@ -69,12 +73,6 @@ __device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrt
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float hw_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
 
-// Ranking key (d ascending, then site ID ascending): a total order.
-__device__ __forceinline__ bool key_less(float da, uint32_t ia, float db, uint32_t ib)
-{
-    return da < db || (da == db && ia < ib);
-}
-
 // Metric frame of one site: u = dir/|dir| (u = (1,0) if |dir|^2 < 1e-30) and e^{+-a}.
 struct Frame {
     float ux, uy, E, iE;
@@ -107,18 +105,6 @@ __device__ __forceinline__ float score_frame(const Frame &f, float px, float py,
     const float be = fmaf(f.ux, ey, -(f.uy * ex));
     const float q = hw_sqrt(fmaf(f.E * al, al, f.iE * be * be));
     return fmaf(s, q, -(s * r));
-}
-
-// Score of slot `id` read straight from the SoA planes (6 gathers).
-__device__ __forceinline__ float score_site(const float *__restrict__ S, long stride, uint32_t id, float X, float Y,
-                                            float s, bool &usable)
-{
-    const float px = S[id];
-    usable = !(px < 0.0f);
-    const float py = S[stride + id];
-    const float r = S[PR * stride + id];
-    const Frame f = make_frame(S[PDX * stride + id], S[PDY * stride + id], S[PA * stride + id]);
-    return score_frame(f, px, py, r, X, Y, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -260,42 +246,6 @@ __device__ __forceinline__ uint32_t xorshift32(uint32_t x)
     return x;
 }
 
-// Sorted top-K held in registers; insert keeps ascending (d, ID) order.
-struct TopK {
-    float d[K];
-    uint32_t id[K];
-
-    __device__ __forceinline__ void clear()
-    {
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-            d[j] = __builtin_inff();
-            id[j] = NONE;
-        }
-    }
-    __device__ __forceinline__ bool contains(uint32_t c) const
-    {
-        bool hit = false;
-#pragma unroll
-        for (int j = 0; j < K; ++j)
-            hit |= (id[j] == c);
-        return hit;
-    }
-    // Precondition: key_less(dc, c, d[K-1], id[K-1]) and c not present.
-    __device__ __forceinline__ void insert(float dc, uint32_t c)
-    {
-#pragma unroll
-        for (int j = K - 1; j >= 0; --j) {
-            const bool shift = (j > 0) && key_less(dc, c, d[j - 1], id[j - 1]);
-            const bool here = key_less(dc, c, d[j], id[j]);
-            const float nd = shift ? d[j - 1] : (here ? dc : d[j]);
-            const uint32_t ni = shift ? id[j - 1] : (here ? c : id[j]);
-            d[j] = nd;
-            id[j] = ni;
-        }
-    }
-};
-
 // ---------------------------------------------------------------------------
 // Inserts one list's IDs into an LDS hash table of TB slots keyed by site ID
 // (multiplicative hash, CAS insert -- summary, B.4; double hashing with an odd
@@ -343,7 +293,7 @@ __device__ __forceinline__ void table_insert_ids(uint32_t *key, const uint32_t (
 // its own list, the lists at +-jump in x and y (skipped outside the image) and
 // n_inject injected IDs.  The lists the tile needs -- its own block plus four
 // strips of width min(jump, 16) beyond its edges -- are loaded once; every ID in
-// them goes into an LDS site table (hash keyed by ID, read-then-CAS insert) and
+// them goes into an LDS site table (hash keyed by ID, CAS insert) and
 // each list entry is replaced by its table slot.  Each distinct site is then
 // gathered once per tile and its metric frame computed once, so scoring a list
 // candidate costs two LDS reads instead of six scattered global loads.  IDs the
@@ -694,9 +644,9 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(const float4 *__res
 // for (re)initialisation -- a seed pass, then ceil(log2 max(W, H)) flood passes
 // over 3x3 neighbourhoods that keep the four closest sites).
 //
-// Seed: every active site with a finite position enters the list of the pixel
-// that contains it; a pixel keeps at most four, the best by (d, ID) at its
-// centre.  On the GPU the four places are filled in four rounds (one launch
+// Seed: every active site with a finite position enters the list of the map
+// entry of the pixel that contains it; an entry keeps at most four, the best by
+// (d, ID) at its centred UV.  On the GPU the four places are filled in four rounds (one launch
 // each): in round r every site not already in places 0..r-1 offers its 64-bit
 // ranking key to place r with an atomic minimum, so place r ends up with the
 // r-th best key whatever the order of arrival.  The places are the four 8-byte
@@ -836,11 +786,12 @@ __global__ __launch_bounds__(BLOCK) void k_topk_exact(const float4 *__restrict__
 
 // ---------------------------------------------------------------------------
 // Per-tile site table.  A 16x16 tile's lists name only a few dozen distinct
-// sites, so each distinct site is gathered from the SoA planes once per tile
-// and its derived record kept in LDS: scattered per-lane gathers are what
-// limits these kernels otherwise.  The table is an LDS hash keyed by site ID
-// (multiplicative hash, <= 8 linear probes, CAS insert -- summary, B.4).  An ID
-// that finds no slot takes the "spill" path and is read from global memory.
+// sites, so each distinct site is gathered once per tile and its derived record
+// kept in LDS: scattered per-lane gathers are what limits these kernels
+// otherwise.  The table is an LDS hash keyed by site ID (the summary's B.4 per-
+// tile hash: multiplicative hash with double hashing, <= HASH_PROBES probes, one
+// CAS per probe; table_insert_ids).  An ID that finds no slot takes the "spill"
+// path and is read from global memory.
 constexpr int TBL = 256;
 constexpr int NREC = 12;  // (px py r tau) (ux uy E iE) (R G B inv_n): three float4
 
