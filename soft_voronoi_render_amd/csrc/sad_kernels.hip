@@ -1029,12 +1029,12 @@ constexpr int CHUNK = 8;
 static_assert((SAD_LOSS_SLOTS & (SAD_LOSS_SLOTS - 1)) == 0, "loss slots: a power of two");
 constexpr int NSUM = 10;  // per-entry sums of the reduction (entry_sums)
 
-// Staged entries live field-major, sorted entry e at word e ^ ((e >> 6) & 7).
-// Lanes that write one bucket write consecutive entries, and the swizzle keeps
-// those in distinct banks; when every thread reads the j-th entry of its chunk
-// (entries 8t + j, t = 0..63) the XOR with t / 8 spreads the 64 lanes over 64
-// banks as well.
-__device__ __forceinline__ int stage_pos(uint32_t e) { return (int)(e ^ ((e >> 6) & 7u)); }
+// Staged entries are 16-byte records; sorted entry e lives at record
+// e ^ ((e >> 4) & 7).  Lanes that write one bucket write consecutive entries,
+// which stay in distinct bank groups; when every thread reads the j-th entry of
+// its chunk (entry 8t + j, one 128-bit read per entry) the XOR with (t / 2) mod 8
+// puts 16 consecutive lanes on 16 distinct 4-bank groups of the 64 banks.
+__device__ __forceinline__ int stage_pos(uint32_t e) { return (int)(e ^ ((e >> 4) & 7u)); }
 
 struct BwdShared {
     TileTable T;
@@ -1043,10 +1043,7 @@ struct BwdShared {
     float4 g[BLOCK];  // per pixel: 2 (c - t), and 0
     union {
         struct {
-            uint32_t ps[BLOCK * K];  // pixel | slot << 8
-            float w[BLOCK * K];
-            float gamma[BLOCK * K];
-            float rdelta[BLOCK * K];
+            float4 ent[BLOCK * K];  // (pixel | slot << 8, w, gamma, rdelta) per staged entry
         } e;
         struct {
             float part[2 * NSUM][BLOCK];  // per chunk: [0,10) head partial, [10,20) tail partial
@@ -1312,10 +1309,8 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
         for (int k = 0; k < K; ++k) {
             if (slot[k] >= 0) {
                 const int q = stage_pos(L.off[slot[k]] + pos[k]);
-                L.u.e.ps[q] = (uint32_t)tid | ((uint32_t)slot[k] << 8);
-                L.u.e.w[q] = wk[k];
-                L.u.e.gamma[q] = gk[k];
-                L.u.e.rdelta[q] = dk[k];
+                L.u.e.ent[q] = make_float4(__uint_as_float((uint32_t)tid | ((uint32_t)slot[k] << 8)), wk[k], gk[k],
+                                           dk[k]);
             }
         }
     };
@@ -1361,11 +1356,11 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
 #pragma unroll
         for (int j = 0; j < CHUNK; ++j) {
             if (j < nmine) {
-                const int q = stage_pos(b0 + j);
-                mps[j] = L.u.e.ps[q];
-                mw[j] = L.u.e.w[q];
-                mg[j] = L.u.e.gamma[q];
-                md[j] = L.u.e.rdelta[q];
+                const float4 v = L.u.e.ent[stage_pos(b0 + j)];
+                mps[j] = __float_as_uint(v.x);
+                mw[j] = v.y;
+                mg[j] = v.z;
+                md[j] = v.w;
             }
         }
     }
