@@ -122,11 +122,12 @@ __device__ __forceinline__ float score_frame(const Frame &f, float px, float py,
 // note, key design 1).  1/|dir| is 0 for a degenerate direction.
 constexpr int RLD4 = SAD_REC_LD / 4;  // float4 per record
 
-__device__ __forceinline__ void make_record(const float *__restrict__ S, long st, int i, float4 (&o)[RLD4])
+// record of a site whose ten parameters are in registers
+__device__ __forceinline__ void make_record_v(const float (&p)[SAD_NPARAM], float4 (&o)[RLD4])
 {
-    const float x = S[i], y = S[st + i], lt = S[PLT * st + i], r = S[PR * st + i];
-    const float c0 = S[PCR * st + i], c1 = S[PCG * st + i], c2 = S[PCB * st + i];
-    const float dx = S[PDX * st + i], dy = S[PDY * st + i], a = S[PA * st + i];
+    const float x = p[PX], y = p[PY], lt = p[PLT], r = p[PR];
+    const float c0 = p[PCR], c1 = p[PCG], c2 = p[PCB];
+    const float dx = p[PDX], dy = p[PDY], a = p[PA];
     const Frame f = make_frame(dx, dy, a);
     const float sE = __expf(0.5f * a), siE = __expf(-0.5f * a);
     const float n2 = dx * dx + dy * dy;
@@ -134,6 +135,15 @@ __device__ __forceinline__ void make_record(const float *__restrict__ S, long st
     o[1] = make_float4(sE * f.uy, siE * f.ux, siE * f.uy, __expf(lt));
     o[2] = make_float4(c0, c1, c2, n2 >= 1e-30f ? hw_rsq(n2) : 0.0f);
     o[3] = make_float4(f.ux, f.uy, f.E, f.iE);
+}
+
+__device__ __forceinline__ void make_record(const float *__restrict__ S, long st, int i, float4 (&o)[RLD4])
+{
+    float p[SAD_NPARAM];
+#pragma unroll
+    for (int k = 0; k < SAD_NPARAM; ++k)
+        p[k] = S[k * st + i];
+    make_record_v(p, o);
 }
 
 __device__ __forceinline__ float geom_score(const float4 &g0, const float4 &g1, float X, float Y, float s)
@@ -211,12 +221,20 @@ __global__ __launch_bounds__(256) void k_site_records(const float *__restrict__ 
 // conversion instruction does by default); an inactive slot (x < 0) packs x = -1.
 __device__ __forceinline__ uint32_t f16_bits(float v) { return __builtin_bit_cast(unsigned short, (_Float16)v); }
 
+__device__ __forceinline__ uint4 pack_site_v(const float (&p)[SAD_NPARAM])
+{
+    const uint32_t hx = p[PX] < 0.0f ? 0xBC00u : f16_bits(p[PX]);
+    return make_uint4(hx | (f16_bits(p[PY]) << 16), f16_bits(p[PLT]) | (f16_bits(p[PR]) << 16),
+                      f16_bits(p[PDX]) | (f16_bits(p[PDY]) << 16), f16_bits(p[PA]));
+}
+
 __device__ __forceinline__ uint4 pack_site(const float *__restrict__ S, long st, int i)
 {
-    const float x = S[i];
-    const uint32_t hx = x < 0.0f ? 0xBC00u : f16_bits(x);
-    return make_uint4(hx | (f16_bits(S[st + i]) << 16), f16_bits(S[PLT * st + i]) | (f16_bits(S[PR * st + i]) << 16),
-                      f16_bits(S[PDX * st + i]) | (f16_bits(S[PDY * st + i]) << 16), f16_bits(S[PA * st + i]));
+    float p[SAD_NPARAM];
+#pragma unroll
+    for (int k = 0; k < SAD_NPARAM; ++k)
+        p[k] = S[k * st + i];
+    return pack_site_v(p);
 }
 
 __global__ __launch_bounds__(256) void k_pack_sites(const float *__restrict__ S, int n_slots, int stride,
@@ -1806,42 +1824,56 @@ __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__re
     if (i >= n_slots)
         return;
     const long st = stride;
-    const bool active = !(S[i] < 0.0f);
     float4 *gr = reinterpret_cast<float4 *>(G + (long)i * SAD_GRAD_LD);
     const float4 ga = gr[0], gb = gr[1], gc = gr[2];
     const float gv[SAD_NPARAM] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w, gc.x, gc.y};
+    // every load first (parameters, then moments), the updates in registers, then
+    // the stores and the derived record: one memory round trip per slot instead
+    // of one per parameter
+    float po[SAD_NPARAM];
+#pragma unroll
+    for (int j = 0; j < SAD_NPARAM; ++j)
+        po[j] = S[j * st + i];
     gr[0] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     gr[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     reinterpret_cast<float2 *>(gr + 2)[0] = make_float2(0.0f, 0.0f);
+    const bool active = !(po[PX] < 0.0f);
+    if (active) {
+        float mo[SAD_NPARAM], vo[SAD_NPARAM];
 #pragma unroll
-    for (int j = 0; j < SAD_NPARAM; ++j) {
-        const long o = j * st + i;
-        float g = gv[j];
-        if (active) {
-            g *= A.inv_p;
+        for (int j = 0; j < SAD_NPARAM; ++j) {
+            mo[j] = M[j * st + i];
+            vo[j] = V[j * st + i];
+        }
+#pragma unroll
+        for (int j = 0; j < SAD_NPARAM; ++j) {
+            float g = gv[j] * A.inv_p;
             if (!finitef(g))
                 g = 0.0f;
-            const float m = A.b1 * M[o] + (1.0f - A.b1) * g;
-            const float v = A.b2 * V[o] + (1.0f - A.b2) * g * g;
-            M[o] = m;
-            V[o] = v;
-            S[o] = S[o] - A.lr[j] * (m * A.ibc1) * hw_rcp(hw_sqrt(v * A.ibc2) + A.eps);
+            const float m = A.b1 * mo[j] + (1.0f - A.b1) * g;
+            const float v = A.b2 * vo[j] + (1.0f - A.b2) * g * g;
+            mo[j] = m;
+            vo[j] = v;
+            po[j] = po[j] - A.lr[j] * (m * A.ibc1) * hw_rcp(hw_sqrt(v * A.ibc2) + A.eps);
         }
-    }
-    if (active) {
-        const float x = S[i], y = S[st + i];
-        S[i] = x < 0.0f ? 0.0f : (x > A.W ? A.W : x);
-        S[st + i] = y < 0.0f ? 0.0f : (y > A.H ? A.H : y);
+        po[PX] = po[PX] < 0.0f ? 0.0f : (po[PX] > A.W ? A.W : po[PX]);
+        po[PY] = po[PY] < 0.0f ? 0.0f : (po[PY] > A.H ? A.H : po[PY]);
+#pragma unroll
+        for (int j = 0; j < SAD_NPARAM; ++j) {
+            M[j * st + i] = mo[j];
+            V[j * st + i] = vo[j];
+            S[j * st + i] = po[j];
+        }
     }
     if (rec) {
         float4 o[RLD4];
-        make_record(S, st, i, o);
+        make_record_v(po, o);
 #pragma unroll
         for (int j = 0; j < RLD4; ++j)
             rec[RLD4 * (size_t)i + j] = o[j];
     }
     if (packed)
-        packed[i] = pack_site(S, st, i);
+        packed[i] = pack_site_v(po);
 }
 
 // ---------------------------------------------------------------------------
