@@ -1479,8 +1479,12 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
 // and delta = x - p (the site position, so the moments stay well conditioned):
 //   [0] sum w   [1] sum w e   [2] sum w e dx   [3] sum w e dy
 //   [4] sum w e dx^2   [5] sum w e dx dy   [6] sum w e dy^2   [7] unused
-// accumulated (+=) into float [n][SAD_STAT_LD].  Runs every few dozen
-// iterations, so it flushes every entry through the per-wave cooperative path.
+// accumulated (+=) into float [n][SAD_STAT_LD].  Entries of table sites add into
+// a per-tile LDS accumulator (LDS float atomics: the kernel runs every few dozen
+// iterations, so the simplest reduction that keeps global traffic per site per
+// tile will do), flushed with one global atomic per site and statistic;
+// entries whose site found no table slot go through the per-wave cooperative
+// path.
 constexpr int NSTAT = 7;
 
 __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restrict__ G, uint32_t n_slots,
@@ -1490,6 +1494,7 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restric
                                                          int nb)
 {
     __shared__ TileTable T;
+    __shared__ float acc_t[NSTAT][TBL];
     __shared__ float stage[BLOCK / 64][64 * NSTAT + 64];
     const int tid = threadIdx.x, lane = tid & 63;
     int col, row;
@@ -1499,6 +1504,10 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restric
     uint32_t ids[K];
     int slot[K];
     load_ids(cand, mg.entry(p, col, row), inside, ids);
+    static_assert(TBL == BLOCK, "one accumulator column per thread");
+#pragma unroll
+    for (int a = 0; a < NSTAT; ++a)
+        acc_t[a][tid] = 0.0f;  // complete at the table build's barriers
     build_tile_table(T, G, n_slots, ids, slot);
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
     PixelBlend B;
@@ -1533,11 +1542,23 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restric
             acc[4] = we * dx * dx;
             acc[5] = we * dx * dy;
             acc[6] = we * dy * dy;
+#pragma unroll
+            for (int a = 0; a < NSTAT; ++a)
+                acc[a] = finitef(acc[a]) ? acc[a] : 0.0f;
+            if (slot[k] >= 0) {
+#pragma unroll
+                for (int a = 0; a < NSTAT; ++a)
+                    if (acc[a] != 0.0f)
+                        atomicAdd(&acc_t[a][slot[k]], acc[a]);
+            }
         }
+        const bool spilled = has && slot[k] < 0;
+        if (!__any(spilled))
+            continue;
 #pragma unroll
         for (int a = 0; a < NSTAT; ++a)
-            vals[lane * NSTAT + a] = finitef(acc[a]) ? acc[a] : 0.0f;
-        vid[lane] = has ? ids[k] : NONE;
+            vals[lane * NSTAT + a] = spilled ? acc[a] : 0.0f;
+        vid[lane] = spilled ? ids[k] : NONE;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1551,6 +1572,16 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restric
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    __syncthreads();
+    // one global atomic per site and statistic for the tile: consecutive lanes take
+    // consecutive statistics of one site
+    for (int i = tid; i < TBL * NSTAT; i += BLOCK) {
+        const int sl = i / NSTAT, a = i - sl * NSTAT;
+        const uint32_t c = T.key[sl];
+        const float v = acc_t[a][sl];
+        if (c != NONE && v != 0.0f)
+            unsafeAtomicAdd(&stats[(size_t)c * SAD_STAT_LD + a], v);
     }
 }
 
