@@ -100,7 +100,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 5
+#define SAD_ABI_VERSION 6
 #define SAD_K 8
 #define SAD_INVALID 0xffffffffu
 #define SAD_NPARAM 10
@@ -323,17 +323,25 @@ int sad_densify_stats(const float *rec, int n_slots, const uint32_t *cand, const
  *     *n_slots, else slot *n_slots (then *n_slots grows) while below capacity.
  *     Child B's ID is written into the last place of the list of the map entry
  *     that contains it and of its 4 neighbour entries, so the next propagation
- *     pass sees it.
+ *     pass sees it: into `cand` if it is not NULL, and as (entry index
+ *     row*Wm + col, ID) pairs into `seeds` if that is not NULL, in write order (a
+ *     later pair for the same entry overrides an earlier one).  The routine reads
+ *     no list, so a caller whose map lives in device memory passes cand = NULL and
+ *     applies the pairs there.
  *  sites [10][stride], m/v [10][stride], stats [stride][8], removal [stride]
  *  (the removal-delta accumulator, e.g. column 10 of the gradient records),
- *  cand [Hm][Wm][8], target [H][W][3]; *n_slots in/out; n_split/n_pruned (out,
- *  may be NULL) receive the numbers of splits and prunes done.
- * Errors: SAD_ERR_ARG; SAD_ERR_CAPACITY when some selected sites could not be
- *  split for want of a free slot (everything that fitted is done).
+ *  cand [Hm][Wm][8] or NULL, target [H][W][3]; *n_slots in/out; n_split/n_pruned
+ *  (out, may be NULL) receive the numbers of splits and prunes done; seeds
+ *  uint32 [seeds_cap][2] or NULL with seeds_cap >= 5 * floor(split_frac * A) and
+ *  *n_seeds (out) the number of pairs written.
+ * Errors: SAD_ERR_ARG (checked before anything is modified, including a seeds
+ *  buffer below that bound); SAD_ERR_CAPACITY when some selected sites could not
+ *  be split for want of a free slot (everything that fitted is done).
  */
 int sad_densify_prune(float *sites, float *m, float *v, int stride, int capacity, int *n_slots, const float *stats,
                       const float *removal, uint32_t *cand, int W, int H, int cell, const float *target,
-                      const sad_budget_cfg *cfg, int *n_split, int *n_pruned);
+                      const sad_budget_cfg *cfg, int *n_split, int *n_pruned, uint32_t *seeds, long seeds_cap,
+                      long *n_seeds);
 
 /*
  * Evaluation format ([SUM] B.2 "Packed storage for evaluation": all ten values in

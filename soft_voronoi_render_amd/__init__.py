@@ -124,7 +124,8 @@ def lib() -> ctypes.CDLL:
         ip = ctypes.POINTER(ctypes.c_int)
         L.sad_densify_prune.restype = i32
         L.sad_densify_prune.argtypes = [fp, fp, fp, i32, i32, ip, fp, fp, vp, i32, i32, i32, fp,
-                                        ctypes.POINTER(BudgetCfg), ip, ip]
+                                        ctypes.POINTER(BudgetCfg), ip, ip, vp, ctypes.c_long,
+                                        ctypes.POINTER(ctypes.c_long)]
         L.sad_adam_step.restype = i32
         L.sad_adam_step.argtypes = [fp, fp, fp, fp, fp, vp, i32, i32, i32, i32, i32, i32, ctypes.POINTER(AdamCfg),
                                     vp]
@@ -374,32 +375,42 @@ class BudgetConfig:
 
 
 def densify_prune(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, target,
-                  cfg: BudgetConfig | None = None, cell=1):
+                  cfg: BudgetConfig | None = None, cell=1, want_seeds=False):
     """Host-side split/prune on numpy arrays, in place (see sad_densify_prune).
 
     sites, m, v: float32 [10][stride]; stats float32 [stride][8]; removal float32
-    [stride]; cand uint32 [Hm][Wm][8] (map_shape); target float32 [H][W][3].  Returns
-    (new n_slots, n_split, n_pruned, status) -- status is 0 or SAD_ERR_CAPACITY."""
+    [stride]; cand uint32 [Hm][Wm][8] (map_shape) or None; target float32 [H][W][3].
+    Returns (new n_slots, n_split, n_pruned, status) -- status is 0 or
+    SAD_ERR_CAPACITY -- and, with want_seeds, the seeded (entry, ID) pairs as a
+    uint32 [n][2] array in write order."""
     import numpy as np
-    for name, a, dt in (("sites", sites, np.float32), ("m", m, np.float32), ("v", v, np.float32),
-                        ("stats", stats, np.float32), ("removal", removal, np.float32), ("cand", cand, np.uint32),
-                        ("target", target, np.float32)):
+    arrays = [("sites", sites, np.float32), ("m", m, np.float32), ("v", v, np.float32),
+              ("stats", stats, np.float32), ("removal", removal, np.float32), ("target", target, np.float32)]
+    if cand is not None:
+        arrays.append(("cand", cand, np.uint32))
+    for name, a, dt in arrays:
         if not isinstance(a, np.ndarray) or a.dtype != dt or not a.flags["C_CONTIGUOUS"]:
             raise TypeError(f"{name} must be a C-contiguous numpy {np.dtype(dt).name} array")
     stride = sites.shape[1]
     if m.shape != sites.shape or v.shape != sites.shape or stats.shape != (stride, STAT_LD) or \
-            removal.shape != (stride,) or cand.shape != map_shape(W, H, cell) or target.shape != (H, W, 3):
+            removal.shape != (stride,) or target.shape != (H, W, 3) or \
+            (cand is not None and cand.shape != map_shape(W, H, cell)):
         raise ValueError("densify_prune: inconsistent shapes")
     ns = ctypes.c_int(n_slots)
     nsp = ctypes.c_int(0)
     npr = ctypes.c_int(0)
     c = (cfg or BudgetConfig()).to_c()
-    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+    seeds = np.empty((5 * stride + 1, 2), dtype=np.uint32) if want_seeds else None
+    nseed = ctypes.c_long(0)
     rc = lib().sad_densify_prune(p(sites), p(m), p(v), stride, capacity, ctypes.byref(ns), p(stats), p(removal),
                                  p(cand), W, H, cell, p(target), ctypes.byref(c), ctypes.byref(nsp),
-                                 ctypes.byref(npr))
+                                 ctypes.byref(npr), p(seeds), seeds.shape[0] if want_seeds else 0,
+                                 ctypes.byref(nseed))
     if rc not in (SAD_OK, SAD_ERR_CAPACITY):
         raise SadError("sad_densify_prune", rc)
+    if want_seeds:
+        return ns.value, nsp.value, npr.value, rc, seeds[:nseed.value]
     return ns.value, nsp.value, npr.value, rc
 
 
@@ -575,25 +586,44 @@ class Fitter:
         """Budget control between iterations: per-site statistics on the GPU
         (sad_densify_stats), split/prune on the host (sad_densify_prune) using the
         removal deltas accumulated since the last call, then the site records are
-        rebuilt and the removal accumulators cleared.  Returns (n_split, n_pruned)."""
+        rebuilt and the removal accumulators cleared.  Returns (n_split, n_pruned).
+
+        Only what the host routine reads or changes crosses PCIe, through pinned
+        buffers kept between calls: sites, moments, statistics, removal deltas and
+        the target.  The map stays on the GPU: the routine reports the entries it
+        seeds with the new sites, and they are written there (a later seed of an
+        entry wins, as in the routine's own order)."""
         import numpy as np
         dev = self.sites.device
         stride = self.sites.shape[1]
         stats = torch.zeros((stride, STAT_LD), dtype=torch.float32, device=dev)
         densify_stats(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, stats, stream, self.cell)
+        if getattr(self, "_host", None) is None:
+            pin = lambda t: torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+            self._host = {"sites": pin(self.sites), "m": pin(self.m), "v": pin(self.v), "stats": pin(stats),
+                          "removal": torch.empty(stride, dtype=torch.float32, pin_memory=True),
+                          "target": pin(self.target)}
+        h = self._host
+        for k, src in (("sites", self.sites), ("m", self.m), ("v", self.v), ("stats", stats),
+                       ("removal", self.grad[:, NACC - 1]), ("target", self.target)):
+            h[k].copy_(src, non_blocking=True)
         torch.cuda.synchronize(dev)
-        sites = self.sites.cpu().numpy()
-        m = self.m.cpu().numpy()
-        v = self.v.cpu().numpy()
-        cand = self.cand.cpu().numpy().view(np.uint32)
-        removal = np.ascontiguousarray(self.grad[:, NACC - 1].cpu().numpy())
-        n, n_split, n_pruned, _ = densify_prune(sites, m, v, self.n_slots, stride, stats.cpu().numpy(), removal,
-                                                cand, self.W, self.H, self.target.cpu().numpy(), cfg, self.cell)
-        self.sites.copy_(torch.from_numpy(sites))
-        self.m.copy_(torch.from_numpy(m))
-        self.v.copy_(torch.from_numpy(v))
-        self.cand.copy_(torch.from_numpy(cand.view(np.int32)))
+        hn = {k: t.numpy() for k, t in h.items()}
+        n, n_split, n_pruned, _, seeds = densify_prune(hn["sites"], hn["m"], hn["v"], self.n_slots, stride,
+                                                       hn["stats"], hn["removal"], None, self.W, self.H,
+                                                       hn["target"], cfg, self.cell, want_seeds=True)
+        for k, dst in (("sites", self.sites), ("m", self.m), ("v", self.v)):
+            dst.copy_(h[k], non_blocking=True)
+        if len(seeds):
+            # the last write of an entry wins: keep each entry's last pair
+            e = seeds[::-1, 0]
+            _, first = np.unique(e, return_index=True)
+            last = len(e) - 1 - first
+            idx = torch.from_numpy(seeds[last, 0].astype(np.int64)).to(dev)
+            ids = torch.from_numpy(seeds[last, 1].view(np.int32)).to(dev)
+            self.cand.view(-1, K)[idx, K - 1] = ids
         self.grad[:, NACC - 1].zero_()
         self.n_slots = n
         self.refresh_records(stream)
+        torch.cuda.synchronize(dev)  # the pinned buffers are reused by the next call
         return n_split, n_pruned

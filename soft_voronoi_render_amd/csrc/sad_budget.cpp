@@ -57,9 +57,9 @@ void principal_axis(double a, double b, double c, double &lam, double &ex, doubl
 extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, int capacity, int *n_slots,
                                  const float *stats, const float *removal, uint32_t *cand, int W, int H, int cell,
                                  const float *target, const sad_budget_cfg *cfg, int *n_split_out,
-                                 int *n_pruned_out)
+                                 int *n_pruned_out, uint32_t *seeds, long seeds_cap, long *n_seeds_out)
 {
-    if (!sites || !m || !v || !n_slots || !stats || !removal || !cand || !target || !cfg)
+    if (!sites || !m || !v || !n_slots || !stats || !removal || !target || !cfg)
         return SAD_ERR_ARG;
     const int n = *n_slots;
     if (n < 0 || stride < 1 || n > stride || capacity < n || capacity > stride || W < 1 || H < 1 ||
@@ -78,6 +78,10 @@ extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, i
             active.push_back(i);
     const long A = (long)active.size();
     const int n_split = (int)std::floor((double)cfg->split_frac * (double)A);
+    // every split seeds at most five map entries
+    if (seeds && (seeds_cap < 5L * n_split || !n_seeds_out))
+        return SAD_ERR_ARG;
+    long n_seeds = 0;
     const int n_prune = (int)std::floor((double)cfg->prune_frac * (double)A);
 
     // 1. split set: largest score, ties -> lower ID
@@ -205,12 +209,22 @@ extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, i
         const int dc[5] = {0, -1, 1, 0, 0}, dr[5] = {0, 0, 0, -1, 1};
         for (int q = 0; q < 5; ++q) {
             const int c = bc + dc[q], r = br + dr[q];
-            if (c >= 0 && c < Wm && r >= 0 && r < Hm)
-                cand[((long)r * Wm + c) * SAD_K + (SAD_K - 1)] = (uint32_t)b;
+            if (c >= 0 && c < Wm && r >= 0 && r < Hm) {
+                const long e = (long)r * Wm + c;
+                if (cand)
+                    cand[e * SAD_K + (SAD_K - 1)] = (uint32_t)b;
+                if (seeds) {
+                    seeds[2 * n_seeds] = (uint32_t)e;
+                    seeds[2 * n_seeds + 1] = (uint32_t)b;
+                    ++n_seeds;
+                }
+            }
         }
         ++done;
     }
     *n_slots = count;
+    if (seeds)
+        *n_seeds_out = n_seeds;
     if (n_split_out)
         *n_split_out = done;
     if (n_pruned_out)

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.sad_abi_version() == 5
+    assert L.sad_abi_version() == 6
     assert L.sad_status_string(0) == b"ok"
     assert L.sad_status_string(ERR_ALIGN) == b"misaligned pointer"
     assert L.sad_status_string(12345) == b"unknown status"
@@ -161,13 +161,13 @@ def test_densify_entry_points_reject_bad_arguments(L):
     cfg = sad.BudgetConfig().to_c()
     n = ctypes.c_int(4)
     F = L.sad_densify_prune
-    assert F(None, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None) == ERR_ARG
-    assert F(P, P, P, 8, 8, None, P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None) == ERR_ARG
-    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 1, P, None, None, None) == ERR_ARG
-    assert F(P, P, P, 8, 3, ctypes.byref(n), P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None) == ERR_ARG
-    assert F(P, P, P, 8, 9, ctypes.byref(n), P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None) == ERR_ARG
-    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 0, 4, 1, P, ctypes.byref(cfg), None, None) == ERR_ARG
-    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 0, P, ctypes.byref(cfg), None, None) == ERR_ARG
+    assert F(None, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None, None, 0, None) == ERR_ARG
+    assert F(P, P, P, 8, 8, None, P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None, None, 0, None) == ERR_ARG
+    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 1, P, None, None, None, None, 0, None) == ERR_ARG
+    assert F(P, P, P, 8, 3, ctypes.byref(n), P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None, None, 0, None) == ERR_ARG
+    assert F(P, P, P, 8, 9, ctypes.byref(n), P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None, None, 0, None) == ERR_ARG
+    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 0, 4, 1, P, ctypes.byref(cfg), None, None, None, 0, None) == ERR_ARG
+    assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 0, P, ctypes.byref(cfg), None, None, None, 0, None) == ERR_ARG
     assert n.value == 4
 
 

@@ -266,3 +266,44 @@ def test_host_densify_rejects_bad_arguments():
         sad.densify_prune(S, m, v, n, cap, stats[:-1], removal, cand, W, H, T)
     with pytest.raises(TypeError):
         sad.densify_prune(S.astype(np.float64), m, v, n, cap, stats, removal, cand, W, H, T)
+
+
+@pytest.mark.parametrize("cell", [1, 3])
+def test_host_densify_seed_pairs_reproduce_the_map(cell):
+    """With the map left on the device, the routine reports the entries it seeds;
+    applying those pairs in order (a later pair of an entry wins) gives exactly the
+    map it writes when it is handed the map, and everything else is the same."""
+    import oracle
+    W, H, n, cap = 48, 40, 300, 330
+    case = _random_budget_case(8, W, H, n, cap, cell=cell)
+    cfg = sad.BudgetConfig(split_frac=0.2, prune_frac=0.05)
+    a = [x.copy() for x in case]
+    b = [x.copy() for x in case]
+    ra = sad.densify_prune(a[0], a[1], a[2], n, cap, a[3], a[4], a[5], W, H, a[6], cfg, cell=cell)
+    rb = sad.densify_prune(b[0], b[1], b[2], n, cap, b[3], b[4], None, W, H, b[6], cfg, cell=cell, want_seeds=True)
+    assert ra == rb[:4] and ra[1] > 0
+    for x, y in zip(a[:3], b[:3]):
+        assert np.array_equal(x, y)
+    seeds = rb[4]
+    assert seeds.shape[1] == 2 and 0 < len(seeds) <= 5 * ra[1]
+    m = case[5].copy().reshape(-1, 8)
+    for e, i in seeds:
+        m[e, 7] = i
+    assert np.array_equal(m.reshape(a[5].shape), a[5])
+
+
+def test_host_densify_rejects_a_short_seed_buffer():
+    import ctypes
+    W, H, n, cap = 48, 40, 300, 330
+    S, m, v, stats, removal, cand, T = _random_budget_case(9, W, H, n, cap)
+    before = [x.copy() for x in (S, m, v)]
+    c = sad.BudgetConfig(split_frac=0.2, prune_frac=0.05).to_c()
+    ns, nsp, npr, nseed = ctypes.c_int(n), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_long(0)
+    seeds = np.zeros((10, 2), dtype=np.uint32)  # 5 * floor(0.2 * A) pairs are needed
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rc = sad.lib().sad_densify_prune(p(S), p(m), p(v), cap, cap, ctypes.byref(ns), p(stats), p(removal), None, W, H,
+                                     1, p(T), ctypes.byref(c), ctypes.byref(nsp), ctypes.byref(npr), p(seeds),
+                                     len(seeds), ctypes.byref(nseed))
+    assert rc == sad.SAD_ERR_ARG and ns.value == n
+    for x, y in zip((S, m, v), before):
+        assert np.array_equal(x, y)

@@ -122,12 +122,17 @@ def test_div2k2040_fit_with_budget_control():
         if it % 10 == 9:
             losses.append(f.loss.sum().item())
         if it % 50 == 49 and it < wl.iters - 1:
+            torch.cuda.synchronize()
+            td = time.time()
             ns, npr = f.densify()
+            torch.cuda.synchronize()
+            td = time.time() - td
             active = int((f.sites[0, :f.n_slots] >= 0).sum())
             counts.append(active)
             assert f.n_slots <= cap
             assert abs(active - n) <= 0.1 * n, "budget control moved N beyond +-10%"
-            print(f"div2k2040 it {it + 1}: split {ns}, pruned {npr}, active {active}, slots {f.n_slots}", flush=True)
+            print(f"div2k2040 it {it + 1}: split {ns}, pruned {npr}, active {active}, slots {f.n_slots}, "
+                  f"budget control {td * 1e3:.1f} ms", flush=True)
     torch.cuda.synchronize()
     print(f"div2k2040: {wl.iters} iterations with budget control in {time.time() - t0:.1f} s", flush=True)
     fresh = sad.new_records(cap, f.sites.device)
