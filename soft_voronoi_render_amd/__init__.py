@@ -589,8 +589,8 @@ class Fitter:
         rebuilt and the removal accumulators cleared.  Returns (n_split, n_pruned).
 
         Only what the host routine reads or changes crosses PCIe, through pinned
-        buffers kept between calls: sites, moments, statistics, removal deltas and
-        the target.  The map stays on the GPU: the routine reports the entries it
+        buffers kept between calls: sites, moments, statistics and removal deltas
+        (the target once, and again only if the tensor is modified).  The map stays on the GPU: the routine reports the entries it
         seeds with the new sites, and they are written there (a later seed of an
         entry wins, as in the routine's own order)."""
         import numpy as np
@@ -604,8 +604,13 @@ class Fitter:
                           "removal": torch.empty(stride, dtype=torch.float32, pin_memory=True),
                           "target": pin(self.target)}
         h = self._host
-        for k, src in (("sites", self.sites), ("m", self.m), ("v", self.v), ("stats", stats),
-                       ("removal", self.grad[:, NACC - 1]), ("target", self.target)):
+        copies = [("sites", self.sites), ("m", self.m), ("v", self.v), ("stats", stats),
+                  ("removal", self.grad[:, NACC - 1])]
+        tkey = (self.target.data_ptr(), self.target._version)
+        if getattr(self, "_host_target", None) != tkey:  # the target crosses once, not per call
+            copies.append(("target", self.target))
+            self._host_target = tkey
+        for k, src in copies:
             h[k].copy_(src, non_blocking=True)
         torch.cuda.synchronize(dev)
         hn = {k: t.numpy() for k, t in h.items()}

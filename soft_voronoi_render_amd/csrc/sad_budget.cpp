@@ -84,34 +84,47 @@ extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, i
     long n_seeds = 0;
     const int n_prune = (int)std::floor((double)cfg->prune_frac * (double)A);
 
-    // 1. split set: largest score, ties -> lower ID
+    // 1. split set: largest score, ties -> lower ID.  Only the first n_split in
+    // that order are needed, and in that order (it decides which free slot each
+    // second child takes): select them, then sort the selection.
     std::vector<std::pair<double, int>> sc;
+    sc.reserve(active.size());
     for (int i : active) {
         const double mass = stats[(long)i * SAD_STAT_LD + 0], energy = stats[(long)i * SAD_STAT_LD + 1];
         const double S = energy / std::pow(std::max(mass, (double)cfg->min_mass), (double)cfg->alpha);
         if (std::isfinite(S) && S > 0.0)
             sc.push_back({S, i});
     }
-    std::sort(sc.begin(), sc.end(), [](const std::pair<double, int> &a, const std::pair<double, int> &b) {
+    const auto split_first = [](const std::pair<double, int> &a, const std::pair<double, int> &b) {
         return a.first > b.first || (a.first == b.first && a.second < b.second);
-    });
+    };
+    const size_t k_split = std::min(sc.size(), (size_t)n_split);
+    if (k_split < sc.size())
+        std::nth_element(sc.begin(), sc.begin() + k_split, sc.end(), split_first);
+    std::sort(sc.begin(), sc.begin() + k_split, split_first);
     std::vector<int> split;
-    for (int j = 0; j < (int)sc.size() && j < n_split; ++j)
+    split.reserve(k_split);
+    for (size_t j = 0; j < k_split; ++j)
         split.push_back(sc[j].second);
     std::vector<char> is_split(n, 0);
     for (int i : split)
         is_split[i] = 1;
 
     // 2. prune set: smallest removal delta among the others, ties -> lower ID
+    // (a set: the order of pruning changes nothing)
     std::vector<std::pair<double, int>> rm;
+    rm.reserve(active.size());
     for (int i : active)
         if (!is_split[i] && std::isfinite(removal[i]))
             rm.push_back({(double)removal[i], i});
-    std::sort(rm.begin(), rm.end(), [](const std::pair<double, int> &a, const std::pair<double, int> &b) {
-        return a.first < b.first || (a.first == b.first && a.second < b.second);
-    });
+    const size_t k_prune = std::min(rm.size(), (size_t)std::max(n_prune, 0));
+    if (k_prune < rm.size())
+        std::nth_element(rm.begin(), rm.begin() + k_prune, rm.end(),
+                         [](const std::pair<double, int> &a, const std::pair<double, int> &b) {
+                             return a.first < b.first || (a.first == b.first && a.second < b.second);
+                         });
     int pruned = 0;
-    for (int j = 0; j < (int)rm.size() && j < n_prune; ++j) {
+    for (size_t j = 0; j < k_prune; ++j) {
         const int i = rm[j].second;
         P(PX, i) = -1.0f;
         P(PY, i) = -1.0f;
