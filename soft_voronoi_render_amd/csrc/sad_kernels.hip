@@ -277,14 +277,14 @@ __device__ __forceinline__ uint32_t xorshift32(uint32_t x)
 constexpr uint32_t REF_NONE = 0xFFFFFFFFu;
 constexpr uint32_t REF_SPILL = 0x80000000u;  // | site ID
 
-template <int TB>
-__device__ __forceinline__ void table_insert_ids(uint32_t *key, const uint32_t (&ids)[K], uint32_t n_slots,
-                                                 uint32_t (&refs)[K])
+template <int TB, int N>
+__device__ __forceinline__ void table_insert_ids(uint32_t *key, const uint32_t (&ids)[N], uint32_t n_slots,
+                                                 uint32_t (&refs)[N])
 {
     constexpr int SHIFT = TB == 256 ? 24 : 23;
     static_assert(TB == 256 || TB == 512, "table size");
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
+    for (int k = 0; k < N; ++k) {
         const uint32_t c = ids[k];
         uint32_t r = REF_NONE;
         if (c < n_slots) {
@@ -967,16 +967,29 @@ __device__ __forceinline__ void blend_pixel(const TileTable &T, const float4 *__
     for (int k = 0; k < K; ++k)
         mx = B.use[k] ? fmaxf(mx, B.l[k]) : mx;
     B.any = mx > -__builtin_inff();
-    float Z = 0.0f, a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
+    // entries 0..3 and 4..7 are summed separately and then added: the order of
+    // the backward, whose two lanes per pixel each sum one half
+    float Z = 0.0f, a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, Zb = 0.0f, b0 = 0.0f, b1 = 0.0f, b2 = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const float e = B.use[k] ? __expf(B.l[k] - mx) : 0.0f;
         B.e[k] = e;
-        Z += e;
-        a0 = fmaf(e, B.c0[k], a0);
-        a1 = fmaf(e, B.c1[k], a1);
-        a2 = fmaf(e, B.c2[k], a2);
+        if (k < K / 2) {
+            Z += e;
+            a0 = fmaf(e, B.c0[k], a0);
+            a1 = fmaf(e, B.c1[k], a1);
+            a2 = fmaf(e, B.c2[k], a2);
+        } else {
+            Zb += e;
+            b0 = fmaf(e, B.c0[k], b0);
+            b1 = fmaf(e, B.c1[k], b1);
+            b2 = fmaf(e, B.c2[k], b2);
+        }
     }
+    Z += Zb;
+    a0 += b0;
+    a1 += b1;
+    a2 += b2;
     B.Z = Z;
     const float iZ = B.any ? hw_rcp(Z) : 0.0f;  // Z >= 1: the largest term is exp(0)
     B.chat0 = a0 * iZ;
@@ -1037,12 +1050,14 @@ __global__ __launch_bounds__(BLOCK) void k_render_fwd(const float4 *__restrict__
 // (10 parameters + removal delta).
 //
 // The per-tile reduction avoids LDS float atomics (same-site entries of a tile
-// collide on one address and serialise): entries are counting-sorted by table
-// slot (one integer atomic per entry), each thread then sums a fixed chunk of 8
-// sorted entries -- runs of one site -- in registers, and one thread per site
-// adds the chunk partials of its run and issues one global atomic per
-// accumulator.  Runs that lie strictly inside a chunk are flushed by the chunk
-// thread.  Either way a site gets one global atomic per accumulator per tile.
+// collide on one address and serialise -- even one atomic per run of a site
+// within a chunk of entries made the kernel more than twice as slow): entries
+// are counting-sorted by table slot (one integer atomic per entry), each of 256
+// threads then sums a fixed chunk of 8 sorted entries -- runs of one site -- in
+// registers, and one thread per site adds the chunk partials of its run and
+// issues one global atomic per accumulator.  Runs that lie strictly inside a
+// chunk are flushed by the chunk thread.  Either way a site gets one global
+// atomic per accumulator per tile.
 constexpr int CHUNK = 8;
 static_assert((SAD_LOSS_SLOTS & (SAD_LOSS_SLOTS - 1)) == 0, "loss slots: a power of two");
 constexpr int NSUM = 10;  // per-entry sums of the reduction (entry_sums)
@@ -1068,7 +1083,7 @@ struct BwdShared {
             float fin[SAD_NACC][TBL];     // per table slot: the tile's sums, then its 11 totals
         } r;
     } u;
-    float wsum[BLOCK / 64];
+    float wsum[2 * BLOCK / 64];
     uint32_t wtot[BLOCK / 64];
     uint32_t total;
     uint32_t nspill;
@@ -1176,23 +1191,60 @@ __device__ __forceinline__ void spill_flush(const float4 *__restrict__ G, uint32
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__ G, uint32_t n_slots,
-                                                      const uint4 *__restrict__ cand,
-                                                      const float *__restrict__ target, int W, int H,
-                                                      float *__restrict__ grad, float *__restrict__ loss_sum,
-                                                      float *__restrict__ out_rgb, float s, MapGrid grid, int tiles_x,
-                                                      int nb)
+// Two lanes per pixel: lanes l and l + 32 of a wave share a pixel and take
+// entries 0..3 and 4..7 of its list.  The softmax and the removal delta need
+// sums over all 8 entries; each lane sums its half and one v_permlane32_swap
+// gives both lanes the pair's total (the same bits on both: the two halves are
+// added in either order, and float addition commutes) and the partner's half.
+// Per 16x16 tile this runs 8 waves over the same LDS as one lane per pixel, so a
+// SIMD holds twice the waves to hide the latency of the table, record and
+// staging phases, and each lane's serial chain of inserts and blends halves.
+constexpr int BWD_THREADS = 2 * BLOCK;
+constexpr int KH = K / 2;
+
+struct PairSums {
+    float total, other;  // own half + partner's half; the partner's half
+};
+
+__device__ __forceinline__ PairSums pair_sums(float x, int half)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float lo = __uint_as_float(r[0]), hi = __uint_as_float(r[1]);  // lane l: x of lanes l % 32 and l % 32 + 32
+    return {lo + hi, half ? lo : hi};
+}
+
+__device__ __forceinline__ float pair_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__restrict__ G, uint32_t n_slots,
+                                                            const uint4 *__restrict__ cand,
+                                                            const float *__restrict__ target, int W, int H,
+                                                            float *__restrict__ grad, float *__restrict__ loss_sum,
+                                                            float *__restrict__ out_rgb, float s, MapGrid grid,
+                                                            int tiles_x, int nb)
 {
     __shared__ BwdShared L;
     const int tid = threadIdx.x;
-    int col, row;
-    tile_pixel(nb, tiles_x, col, row);
-    const int col0 = col - (tid & (TILE - 1)), row0 = row - tid / TILE;
+    const int lane = tid & 63, half = lane >> 5;
+    const int pp = (tid >> 6) * 32 + (lane & 31);  // pixel within the tile
+    const int t = xcd_band(blockIdx.x, nb);
+    const int col0 = (t % tiles_x) * TILE, row0 = (t / tiles_x) * TILE;
+    const int col = col0 + (pp & (TILE - 1)), row = row0 + pp / TILE;
     const bool inside = col < W && row < H;
     const long p = (long)row * W + col;
-    uint32_t ids[K];
-    int slot[K];
-    load_ids(cand, grid.entry(p, col, row), inside, ids);
+    uint32_t ids[KH];
+    {
+        uint4 a = make_uint4(NONE, NONE, NONE, NONE);
+        if (inside)
+            a = cand[2 * grid.entry(p, col, row) + half];
+        ids[0] = a.x;
+        ids[1] = a.y;
+        ids[2] = a.z;
+        ids[3] = a.w;
+    }
     // the target is read now, so its latency overlaps the table build
     float t0 = 0.0f, t1 = 0.0f, t2 = 0.0f;
     if (inside) {
@@ -1200,36 +1252,61 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
         t1 = target[3 * p + 1];
         t2 = target[3 * p + 2];
     }
-    L.cnt[tid] = 0;
+    if (tid < TBL) {
+        L.T.key[tid] = NONE;
+        L.cnt[tid] = 0;
+    }
     if (tid == 0)
         L.nspill = 0;
-    table_insert_phase(L.T, n_slots, ids, slot);
+    __syncthreads();
+    int slot[KH];
+    {
+        uint32_t refs[KH];
+        table_insert_ids<TBL>(L.T.key, ids, n_slots, refs);
+#pragma unroll
+        for (int k = 0; k < KH; ++k)
+            slot[k] = refs[k] == REF_NONE ? -2 : (refs[k] & REF_SPILL) ? -1 : (int)refs[k];
+    }
     // every entry with a table slot gets its place in the slot-sorted staging now
     // (a counting sort whose counts are complete at the next barrier), so the
     // blend below can write its entries without another block-wide step
-    uint32_t pos[K];
+    uint32_t pos[KH];
     uint32_t nsp = 0;
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
+    for (int k = 0; k < KH; ++k) {
         pos[k] = slot[k] >= 0 ? atomicAdd(&L.cnt[slot[k]], 1u) : 0u;
         nsp += slot[k] == -1;
     }
-    if (__any(nsp > 0) && (tid & 63) == 0)
+    if (__any(nsp > 0) && lane == 0)
         atomicAdd(&L.nspill, 1u);
     __syncthreads();
-    // bucket offsets: wave scans of the slot counts, then the waves' totals
-    const uint32_t cnt_me = L.cnt[tid];
-    uint32_t incl = cnt_me;
+    // bucket offsets (wave scans of the slot counts, then the waves' totals) and
+    // one thread per slot filling its record
+    uint32_t cnt_me = 0, incl = 0;
+    if (tid < TBL) {
+        cnt_me = L.cnt[tid];
+        incl = cnt_me;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_up(incl, o, 64);
-        if ((tid & 63) >= o)
-            incl += v;
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t v = __shfl_up(incl, o, 64);
+            if (lane >= o)
+                incl += v;
+        }
+        if (lane == 63)
+            L.wtot[tid >> 6] = incl;
+        const uint32_t c = L.T.key[tid];
+        if (c != NONE) {
+            const SiteRec R = load_rec_global(G, c);
+#pragma unroll
+            for (int j = 0; j < NREC / 4; ++j)
+                L.T.rec[tid][j] = make_float4(R.v[4 * j], R.v[4 * j + 1], R.v[4 * j + 2], R.v[4 * j + 3]);
+        }
+    } else if (tid < TBL + NREC / 4) {
+        const int j = tid - TBL;  // the null record (px = NaN) of empty entries
+        L.T.rec[TBL][j] = make_float4(j == 0 ? __builtin_nanf("") : 0.0f, 0.0f, 0.0f, 0.0f);
     }
-    if ((tid & 63) == 63)
-        L.wtot[tid >> 6] = incl;
-    table_load_phase(L.T, G);
-    {
+    __syncthreads();
+    if (tid < TBL) {
         uint32_t base = 0;
         for (int w = 0; w < (tid >> 6); ++w)
             base += L.wtot[w];
@@ -1240,94 +1317,137 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
     const bool tile_spills = L.nspill > 0;  // the same for the whole block
     __syncthreads();
 
-    // phase 3: blend, per-entry softmax quantities; staged entries written in
-    // slot order, spilled entries flushed to global memory
+    // phase 3: blend over the pair (every lane takes part in the exchanges; a
+    // pixel outside the image has no usable entry), per-entry softmax quantities;
+    // staged entries written in slot order, spilled entries flushed to global memory
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
-    float err = 0.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
-    float wk[K], gk[K], dk[K];
-    bool spill[K];
+    float l[KH], c0[KH], c1[KH], c2[KH];
+    bool use[KH];
+    {
+        auto entry = [&](int k, const SiteRec &R) {
+            const float lk = -R.v[R_TAU] * rec_score(R, X, Y, s);
+            use[k] = finitef(lk);
+            l[k] = lk;
+            c0[k] = use[k] ? R.v[R_C0] : 0.0f;
+            c1[k] = use[k] ? R.v[R_C1] : 0.0f;
+            c2[k] = use[k] ? R.v[R_C2] : 0.0f;
+        };
+        bool spilled = false;
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        wk[k] = gk[k] = dk[k] = 0.0f;
-        spill[k] = false;
-    }
-    if (inside) {
-        PixelBlend B;
-        blend_pixel(L.T, G, ids, slot, X, Y, s, B);
-        if (out_rgb) {  // the forward of the same map, for free
-            out_rgb[3 * p] = B.chat0;
-            out_rgb[3 * p + 1] = B.chat1;
-            out_rgb[3 * p + 2] = B.chat2;
+        for (int k = 0; k < KH; ++k) {
+            entry(k, table_rec(L.T, slot[k] >= 0 ? slot[k] : TBL));
+            spilled |= slot[k] == -1;
         }
-        const float r0 = B.chat0 - t0, r1 = B.chat1 - t1, r2 = B.chat2 - t2;
+        if (__any(spilled)) {
+#pragma unroll
+            for (int k = 0; k < KH; ++k)
+                if (slot[k] == -1)
+                    entry(k, load_rec_global(G, ids[k]));
+        }
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < KH; ++k)
+        mx = use[k] ? fmaxf(mx, l[k]) : mx;
+    mx = pair_max(mx);
+    const bool any = mx > -__builtin_inff();
+    float e[KH];
+    float ze = 0.0f, z0 = 0.0f, z1 = 0.0f, z2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+        e[k] = use[k] ? __expf(l[k] - mx) : 0.0f;
+        ze += e[k];
+        z0 = fmaf(e[k], c0[k], z0);
+        z1 = fmaf(e[k], c1[k], z1);
+        z2 = fmaf(e[k], c2[k], z2);
+    }
+    const PairSums Se = pair_sums(ze, half), S0 = pair_sums(z0, half), S1 = pair_sums(z1, half),
+                   S2 = pair_sums(z2, half);
+    const float iZ = any ? hw_rcp(Se.total) : 0.0f;  // Z >= 1: the largest term is exp(0)
+    const float chat0 = S0.total * iZ, chat1 = S1.total * iZ, chat2 = S2.total * iZ;
+    float err = 0.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
+    if (inside) {
+        if (out_rgb && half == 0) {  // the forward of the same map, for free
+            out_rgb[3 * p] = chat0;
+            out_rgb[3 * p + 1] = chat1;
+            out_rgb[3 * p + 2] = chat2;
+        }
+        const float r0 = chat0 - t0, r1 = chat1 - t1, r2 = chat2 - t2;
         err = r0 * r0 + r1 * r1 + r2 * r2;
         g0 = 2.0f * r0;
         g1 = 2.0f * r1;
         g2 = 2.0f * r2;
-        if (B.any) {
-            const float iZ = hw_rcp(B.Z);
-            // exclusive sums of e and e*c over the other entries (removal delta)
-            float xe[K], x0[K], x1[K], x2[K];
-            float se = 0.0f, s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
+    }
+    float wk[KH], gk[KH], dk[KH];
+    bool spill[KH];
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                xe[k] = se;
-                x0[k] = s0;
-                x1[k] = s1;
-                x2[k] = s2;
-                se += B.e[k];
-                s0 += B.e[k] * B.c0[k];
-                s1 += B.e[k] * B.c1[k];
-                s2 += B.e[k] * B.c2[k];
-            }
-            se = s0 = s1 = s2 = 0.0f;
+    for (int k = 0; k < KH; ++k) {
+        wk[k] = gk[k] = dk[k] = 0.0f;
+        spill[k] = false;
+    }
+    if (any) {
+        // exclusive sums of e and e*c over the other 7 entries (removal delta):
+        // the partner's half plus this half's entries before and after k
+        float xe[KH], x0[KH], x1[KH], x2[KH];
+        float se = Se.other, s0 = S0.other, s1 = S1.other, s2 = S2.other;
 #pragma unroll
-            for (int k = K - 1; k >= 0; --k) {
-                xe[k] += se;
-                x0[k] += s0;
-                x1[k] += s1;
-                x2[k] += s2;
-                se += B.e[k];
-                s0 += B.e[k] * B.c0[k];
-                s1 += B.e[k] * B.c1[k];
-                s2 += B.e[k] * B.c2[k];
-            }
-            // 1 / (sum of the other entries' e): xe >= 2^-100 but for near-exclusive
-            // entries, which take the exact quotient (rarely: a wave-uniform branch)
-            float iZo[K];
-            bool tiny = false;
+        for (int k = 0; k < KH; ++k) {
+            xe[k] = se;
+            x0[k] = s0;
+            x1[k] = s1;
+            x2[k] = s2;
+            se += e[k];
+            s0 += e[k] * c0[k];
+            s1 += e[k] * c1[k];
+            s2 += e[k] * c2[k];
+        }
+        se = s0 = s1 = s2 = 0.0f;
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                iZo[k] = xe[k] > 0.0f ? hw_rcp(xe[k]) : 0.0f;
-                tiny |= xe[k] > 0.0f && xe[k] < 0x1p-100f;
-            }
-            if (__any(tiny)) {
+        for (int k = KH - 1; k >= 0; --k) {
+            xe[k] += se;
+            x0[k] += s0;
+            x1[k] += s1;
+            x2[k] += s2;
+            se += e[k];
+            s0 += e[k] * c0[k];
+            s1 += e[k] * c1[k];
+            s2 += e[k] * c2[k];
+        }
+        // 1 / (sum of the other entries' e): xe >= 2^-100 but for near-exclusive
+        // entries, which take the exact quotient (rarely: a wave-uniform branch)
+        float iZo[KH];
+        bool tiny = false;
 #pragma unroll
-                for (int k = 0; k < K; ++k)
-                    if (xe[k] > 0.0f && xe[k] < 0x1p-100f)
-                        iZo[k] = 1.0f / xe[k];
-            }
+        for (int k = 0; k < KH; ++k) {
+            iZo[k] = xe[k] > 0.0f ? hw_rcp(xe[k]) : 0.0f;
+            tiny |= xe[k] > 0.0f && xe[k] < 0x1p-100f;
+        }
+        if (__any(tiny)) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const float w = B.e[k] * iZ;
-                // a zero-weight entry changes nothing: all its gradients vanish and
-                // removing it leaves the blend as it is (it stays staged, as zeros)
-                if (!B.use[k] || w == 0.0f)
-                    continue;
-                wk[k] = w;
-                gk[k] = w * (g0 * (B.c0[k] - B.chat0) + g1 * (B.c1[k] - B.chat1) + g2 * (B.c2[k] - B.chat2));
-                const float m0 = x0[k] * iZo[k] - t0, m1 = x1[k] * iZo[k] - t1, m2 = x2[k] * iZo[k] - t2;
-                dk[k] = (m0 * m0 + m1 * m1 + m2 * m2) - err;
-                spill[k] = slot[k] == -1;
-            }
+            for (int k = 0; k < KH; ++k)
+                if (xe[k] > 0.0f && xe[k] < 0x1p-100f)
+                    iZo[k] = 1.0f / xe[k];
+        }
+#pragma unroll
+        for (int k = 0; k < KH; ++k) {
+            const float w = e[k] * iZ;
+            // a zero-weight entry changes nothing: all its gradients vanish and
+            // removing it leaves the blend as it is (it stays staged, as zeros)
+            if (!use[k] || w == 0.0f)
+                continue;
+            wk[k] = w;
+            gk[k] = w * (g0 * (c0[k] - chat0) + g1 * (c1[k] - chat1) + g2 * (c2[k] - chat2));
+            const float m0 = x0[k] * iZo[k] - t0, m1 = x1[k] * iZo[k] - t1, m2 = x2[k] * iZo[k] - t2;
+            dk[k] = (m0 * m0 + m1 * m1 + m2 * m2) - err;
+            spill[k] = slot[k] == -1;
         }
     }
     auto stage_entries = [&]() {
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
+        for (int k = 0; k < KH; ++k) {
             if (slot[k] >= 0) {
                 const int q = stage_pos(L.off[slot[k]] + pos[k]);
-                L.u.e.ent[q] = make_float4(__uint_as_float((uint32_t)tid | ((uint32_t)slot[k] << 8)), wk[k], gk[k],
+                L.u.e.ent[q] = make_float4(__uint_as_float((uint32_t)pp | ((uint32_t)slot[k] << 8)), wk[k], gk[k],
                                            dk[k]);
             }
         }
@@ -1339,37 +1459,43 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
         // lane of the wave has one (see spill_flush).  Their LDS staging shares the
         // sort's storage, so the tile stages its entries only after all waves are
         // done with it.
-        const int lane = tid & 63;
         float *vals = &L.u.r.part[0][0] + (tid >> 6) * (64 * SAD_NACC + 64);
 #pragma unroll
-        for (int k = 0; k < K; ++k)
+        for (int k = 0; k < KH; ++k)
             if (__any(spill[k]))
                 spill_flush(G, spill[k] ? ids[k] : NONE, X, Y, s, wk[k], gk[k], dk[k], make_float4(g0, g1, g2, 0.0f),
                             vals, grad, lane);
         __syncthreads();
         stage_entries();
     }
-    L.g[tid] = make_float4(g0, g1, g2, 0.0f);
-    // per-pixel loss: wave sums
+    if (half == 0)
+        L.g[pp] = make_float4(g0, g1, g2, 0.0f);
+    // per-pixel loss (counted once per pair): wave sums
     {
-        float v = err;
+        float v = half == 0 ? err : 0.0f;
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1)
             v += __shfl_xor(v, o, 64);
-        if ((tid & 63) == 0)
+        if (lane == 0)
             L.wsum[tid >> 6] = v;
     }
     __syncthreads();
-    if (tid == 0 && loss_sum)
-        unsafeAtomicAdd(loss_sum + (blockIdx.x & (SAD_LOSS_SLOTS - 1)), L.wsum[0] + L.wsum[1] + L.wsum[2] + L.wsum[3]);
+    if (tid == 0 && loss_sum) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < BWD_THREADS / 64; ++w)
+            v += L.wsum[w];
+        unsafeAtomicAdd(loss_sum + (blockIdx.x & (SAD_LOSS_SLOTS - 1)), v);
+    }
 
-    // phase 4: chunk of 8 sorted entries per thread, runs summed in registers
+    // phase 4: chunk of 8 sorted entries per thread (the first 256 threads), runs
+    // summed in registers
     const uint32_t total = L.total;
     const uint32_t b0 = (uint32_t)tid * CHUNK;
     uint32_t mps[CHUNK];
     float mw[CHUNK], mg[CHUNK], md[CHUNK];
     int nmine = 0;
-    if (b0 < total) {
+    if (tid < BLOCK && b0 < total) {
         nmine = min((int)(total - b0), CHUNK);
 #pragma unroll
         for (int j = 0; j < CHUNK; ++j) {
@@ -1410,11 +1536,11 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
                     cur = sl;
                     Rc = table_rec(L.T, cur);
                 }
-                const int pp = (int)(mps[j] & 0xFFu);
-                const float Xp = (float)(col0 + (pp & (TILE - 1))) + 0.5f;
-                const float Yp = (float)(row0 + pp / TILE) + 0.5f;
+                const int q = (int)(mps[j] & 0xFFu);
+                const float Xp = (float)(col0 + (q & (TILE - 1))) + 0.5f;
+                const float Yp = (float)(row0 + q / TILE) + 0.5f;
                 float v[NSUM];
-                entry_sums(Rc, Xp, Yp, mw[j], mg[j], md[j], L.g[pp], v);
+                entry_sums(Rc, Xp, Yp, mw[j], mg[j], md[j], L.g[q], v);
 #pragma unroll
                 for (int a = 0; a < NSUM; ++a)
                     run[a] += v[a];
@@ -1429,40 +1555,42 @@ __global__ __launch_bounds__(BLOCK) void k_render_bwd(const float4 *__restrict__
 
     // phase 5: one thread per site adds up the chunk partials of its bucket and
     // turns the sums into the site's 11 gradient contributions
-    const uint32_t c = L.cnt[tid];
-    if (c > 0) {
-        const uint32_t b = L.off[tid], e = b + c - 1;
-        const uint32_t t0 = b / CHUNK, t1 = e / CHUNK;
-        const uint32_t end0 = min(t0 * CHUNK + CHUNK, total) - 1;
-        const bool starts_chunk = (b == t0 * CHUNK);
-        float v[NSUM];
-        if (t0 != t1 || starts_chunk || e == end0) {
-            const int h0 = starts_chunk ? 0 : NSUM;
-#pragma unroll
-            for (int a = 0; a < NSUM; ++a)
-                v[a] = L.u.r.part[h0 + a][t0];
-            for (uint32_t t = t0 + 1; t <= t1; ++t) {
+    if (tid < TBL) {
+        const uint32_t c = L.cnt[tid];
+        if (c > 0) {
+            const uint32_t b = L.off[tid], e = b + c - 1;
+            const uint32_t t0c = b / CHUNK, t1c = e / CHUNK;
+            const uint32_t end0 = min(t0c * CHUNK + CHUNK, total) - 1;
+            const bool starts_chunk = (b == t0c * CHUNK);
+            float v[NSUM];
+            if (t0c != t1c || starts_chunk || e == end0) {
+                const int h0 = starts_chunk ? 0 : NSUM;
 #pragma unroll
                 for (int a = 0; a < NSUM; ++a)
-                    v[a] += L.u.r.part[a][t];
+                    v[a] = L.u.r.part[h0 + a][t0c];
+                for (uint32_t tc = t0c + 1; tc <= t1c; ++tc) {
+#pragma unroll
+                    for (int a = 0; a < NSUM; ++a)
+                        v[a] += L.u.r.part[a][tc];
+                }
+            } else {  // a middle run: its total is already in place
+#pragma unroll
+                for (int a = 0; a < NSUM; ++a)
+                    v[a] = L.u.r.fin[a][tid];
             }
-        } else {  // a middle run: its total is already in place
+            float acc[SAD_NACC];
+            site_grads(table_rec(L.T, tid), s, v, acc);
 #pragma unroll
-            for (int a = 0; a < NSUM; ++a)
-                v[a] = L.u.r.fin[a][tid];
+            for (int a = 0; a < SAD_NACC; ++a)
+                L.u.r.fin[a][tid] = acc[a];
         }
-        float acc[SAD_NACC];
-        site_grads(table_rec(L.T, tid), s, v, acc);
-#pragma unroll
-        for (int a = 0; a < SAD_NACC; ++a)
-            L.u.r.fin[a][tid] = acc[a];
     }
     __syncthreads();
 
     // phase 6: cooperative flush -- consecutive lanes take consecutive accumulators
     // of one site, so the lanes of an atomic instruction share the site's 64-byte
     // gradient record instead of touching one cache line each
-    for (int i = tid; i < TBL * SAD_NACC; i += BLOCK) {
+    for (int i = tid; i < TBL * SAD_NACC; i += BWD_THREADS) {
         const int sl = i / SAD_NACC, a = i - sl * SAD_NACC;
         if (L.cnt[sl] > 0) {
             const float v = L.u.r.fin[a][sl];
@@ -2232,7 +2360,7 @@ int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const fl
     if (!aligned16(cand) || !aligned16(grad) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
-    hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
+    hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(BWD_THREADS), 0, (hipStream_t)stream, (const float4 *)rec,
                        (uint32_t)n_slots, (const uint4 *)cand, target, W, H, grad, loss_sum, out_rgb, scale_of(W, H),
                        mg, g.tiles_x, g.nb);
     return launched();
