@@ -1085,8 +1085,11 @@ struct BwdShared {
     } u;
     float wsum[2 * BLOCK / 64];
     uint32_t wtot[BLOCK / 64];
+    uint32_t wocc[BLOCK / 64];
+    uint8_t occ[TBL];  // the occupied slots, ascending (n_occ of them)
     uint32_t total;
     uint32_t nspill;
+    uint32_t n_occ;
 };
 
 // The backward of one site over a set of entries is linear in ten per-entry
@@ -1283,8 +1286,10 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
     // bucket offsets (wave scans of the slot counts, then the waves' totals) and
     // one thread per slot filling its record
     uint32_t cnt_me = 0, incl = 0;
+    uint64_t occ_mask = 0;  // the wave's occupied slots (waves 0..3)
     if (tid < TBL) {
         cnt_me = L.cnt[tid];
+        occ_mask = __ballot(cnt_me > 0);
         incl = cnt_me;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -1294,6 +1299,8 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
         }
         if (lane == 63)
             L.wtot[tid >> 6] = incl;
+        if (lane == 0)
+            L.wocc[tid >> 6] = (uint32_t)__popcll(occ_mask);
         const uint32_t c = L.T.key[tid];
         if (c != NONE) {
             const SiteRec R = load_rec_global(G, c);
@@ -1307,12 +1314,19 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
     }
     __syncthreads();
     if (tid < TBL) {
-        uint32_t base = 0;
-        for (int w = 0; w < (tid >> 6); ++w)
+        uint32_t base = 0, obase = 0;
+        for (int w = 0; w < (tid >> 6); ++w) {
             base += L.wtot[w];
+            obase += L.wocc[w];
+        }
         L.off[tid] = base + incl - cnt_me;
-        if (tid == 0)
+        // the compacted list of occupied slots, for the flush
+        if (cnt_me > 0)
+            L.occ[obase + (uint32_t)__popcll(occ_mask & ((1ull << lane) - 1ull))] = (uint8_t)tid;
+        if (tid == 0) {
             L.total = L.wtot[0] + L.wtot[1] + L.wtot[2] + L.wtot[3];
+            L.n_occ = L.wocc[0] + L.wocc[1] + L.wocc[2] + L.wocc[3];
+        }
     }
     const bool tile_spills = L.nspill > 0;  // the same for the whole block
     __syncthreads();
@@ -1590,13 +1604,13 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
     // phase 6: cooperative flush -- consecutive lanes take consecutive accumulators
     // of one site, so the lanes of an atomic instruction share the site's 64-byte
     // gradient record instead of touching one cache line each
-    for (int i = tid; i < TBL * SAD_NACC; i += BWD_THREADS) {
-        const int sl = i / SAD_NACC, a = i - sl * SAD_NACC;
-        if (L.cnt[sl] > 0) {
-            const float v = L.u.r.fin[a][sl];
-            if (v != 0.0f)
-                unsafeAtomicAdd(&grad[(long)L.T.key[sl] * SAD_GRAD_LD + a], v);
-        }
+    const int n_items = (int)L.n_occ * SAD_NACC;
+    for (int i = tid; i < n_items; i += BWD_THREADS) {
+        const int j = i / SAD_NACC, a = i - j * SAD_NACC;
+        const int sl = L.occ[j];
+        const float v = L.u.r.fin[a][sl];
+        if (v != 0.0f)
+            unsafeAtomicAdd(&grad[(long)L.T.key[sl] * SAD_GRAD_LD + a], v);
     }
 }
 
