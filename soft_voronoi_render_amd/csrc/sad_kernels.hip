@@ -1567,37 +1567,37 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
     }
     __syncthreads();
 
-    // phase 5: one thread per site adds up the chunk partials of its bucket and
-    // turns the sums into the site's 11 gradient contributions
-    if (tid < TBL) {
-        const uint32_t c = L.cnt[tid];
-        if (c > 0) {
-            const uint32_t b = L.off[tid], e = b + c - 1;
-            const uint32_t t0c = b / CHUNK, t1c = e / CHUNK;
-            const uint32_t end0 = min(t0c * CHUNK + CHUNK, total) - 1;
-            const bool starts_chunk = (b == t0c * CHUNK);
-            float v[NSUM];
-            if (t0c != t1c || starts_chunk || e == end0) {
-                const int h0 = starts_chunk ? 0 : NSUM;
+    // phase 5: one thread per occupied slot (the compacted list) adds up the chunk
+    // partials of its bucket and turns the sums into the site's 11 gradient
+    // contributions
+    if (tid < (int)L.n_occ) {
+        const int sl = L.occ[tid];
+        const uint32_t c = L.cnt[sl];
+        const uint32_t b = L.off[sl], e = b + c - 1;
+        const uint32_t t0c = b / CHUNK, t1c = e / CHUNK;
+        const uint32_t end0 = min(t0c * CHUNK + CHUNK, total) - 1;
+        const bool starts_chunk = (b == t0c * CHUNK);
+        float v[NSUM];
+        if (t0c != t1c || starts_chunk || e == end0) {
+            const int h0 = starts_chunk ? 0 : NSUM;
+#pragma unroll
+            for (int a = 0; a < NSUM; ++a)
+                v[a] = L.u.r.part[h0 + a][t0c];
+            for (uint32_t tc = t0c + 1; tc <= t1c; ++tc) {
 #pragma unroll
                 for (int a = 0; a < NSUM; ++a)
-                    v[a] = L.u.r.part[h0 + a][t0c];
-                for (uint32_t tc = t0c + 1; tc <= t1c; ++tc) {
-#pragma unroll
-                    for (int a = 0; a < NSUM; ++a)
-                        v[a] += L.u.r.part[a][tc];
-                }
-            } else {  // a middle run: its total is already in place
-#pragma unroll
-                for (int a = 0; a < NSUM; ++a)
-                    v[a] = L.u.r.fin[a][tid];
+                    v[a] += L.u.r.part[a][tc];
             }
-            float acc[SAD_NACC];
-            site_grads(table_rec(L.T, tid), s, v, acc);
+        } else {  // a middle run: its total is already in place
 #pragma unroll
-            for (int a = 0; a < SAD_NACC; ++a)
-                L.u.r.fin[a][tid] = acc[a];
+            for (int a = 0; a < NSUM; ++a)
+                v[a] = L.u.r.fin[a][sl];
         }
+        float acc[SAD_NACC];
+        site_grads(table_rec(L.T, sl), s, v, acc);
+#pragma unroll
+        for (int a = 0; a < SAD_NACC; ++a)
+            L.u.r.fin[a][sl] = acc[a];
     }
     __syncthreads();
 
