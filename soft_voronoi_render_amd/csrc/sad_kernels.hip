@@ -454,20 +454,47 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
     __syncthreads();
 
     // phase 1: region lists -> table slots
-    for (int r = tid; r < nlists; r += BLOCK) {
-        int pc, pr, across;
-        region_pixel(r, c0, r0, jump, strip_len, pc, pr, across);
+    if constexpr (KK == 1) {
+        // jump 1: every thread takes its pixel's list and two IDs of one of the 64
+        // strip lists (a quarter list), both loads issued before the inserts, so no
+        // thread inserts more than 10 IDs
         uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
-        if (across < kk && pc >= 0 && pc < W && pr >= 0 && pr < H) {
-            const long p = (long)pr * W + pc;
+        if (col < W && row < H) {
+            const long p = (long)row * W + col;
             a = cin[2 * p];
             b = cin[2 * p + 1];
         }
+        const int sr = BLOCK + (tid >> 2), qq = tid & 3;
+        int pc, pr, across;
+        region_pixel(sr, c0, r0, jump, strip_len, pc, pr, across);
+        uint2 q2 = make_uint2(NONE, NONE);
+        if (pc >= 0 && pc < W && pr >= 0 && pr < H)
+            q2 = reinterpret_cast<const uint2 *>(cin)[4 * ((long)pr * W + pc) + qq];
         const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         uint32_t refs[K];
         table_insert_ids<TB>(L.t.key, ids, n_slots, refs);
-        L.ref0[r] = make_uint4(refs[0], refs[1], refs[2], refs[3]);
-        L.ref1[r] = make_uint4(refs[4], refs[5], refs[6], refs[7]);
+        const uint32_t sids[2] = {q2.x, q2.y};
+        uint32_t srefs[2];
+        table_insert_ids<TB>(L.t.key, sids, n_slots, srefs);
+        L.ref0[tid] = make_uint4(refs[0], refs[1], refs[2], refs[3]);
+        L.ref1[tid] = make_uint4(refs[4], refs[5], refs[6], refs[7]);
+        reinterpret_cast<uint2 *>(qq < 2 ? &L.ref0[sr] : &L.ref1[sr])[qq & 1] = make_uint2(srefs[0], srefs[1]);
+    } else {
+        for (int r = tid; r < nlists; r += BLOCK) {
+            int pc, pr, across;
+            region_pixel(r, c0, r0, jump, strip_len, pc, pr, across);
+            uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
+            if (across < kk && pc >= 0 && pc < W && pr >= 0 && pr < H) {
+                const long p = (long)pr * W + pc;
+                a = cin[2 * p];
+                b = cin[2 * p + 1];
+            }
+            const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            uint32_t refs[K];
+            table_insert_ids<TB>(L.t.key, ids, n_slots, refs);
+            L.ref0[r] = make_uint4(refs[0], refs[1], refs[2], refs[3]);
+            L.ref1[r] = make_uint4(refs[4], refs[5], refs[6], refs[7]);
+        }
     }
     __syncthreads();
 
