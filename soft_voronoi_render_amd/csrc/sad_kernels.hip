@@ -1156,6 +1156,30 @@ __device__ __forceinline__ void entry_sums(const SiteRec &R, float X, float Y, f
     }
 }
 
+// entry_sums added straight into a run's sums (multiply-adds), without the
+// per-entry check for non-finite sums: the caller checks the run's totals and, if
+// one is not finite, redoes the run with entry_sums.
+__device__ __forceinline__ void entry_acc(const SiteRec &R, float X, float Y, float w, float gamma, float rdelta,
+                                          const float4 &g, float (&run)[NSUM])
+{
+    const float ex = X - R.v[R_PX], ey = Y - R.v[R_PY];
+    const float ux = R.v[R_UX], uy = R.v[R_UY];
+    const float al = ux * ex + uy * ey, be = ux * ey - uy * ex;
+    const float q2 = R.v[R_E] * al * al + R.v[R_IE] * be * be;
+    const float t = q2 > 0.0f ? gamma * __builtin_amdgcn_rsqf(q2) : 0.0f;
+    const float tal = t * al, tbe = t * be;
+    run[0] = fmaf(w, g.x, run[0]);
+    run[1] = fmaf(w, g.y, run[1]);
+    run[2] = fmaf(w, g.z, run[2]);
+    run[3] += gamma;
+    run[4] += tal;
+    run[5] += tbe;
+    run[6] = fmaf(tal, al, run[6]);
+    run[7] = fmaf(tbe, be, run[7]);
+    run[8] = fmaf(tal, be, run[8]);
+    run[9] += rdelta;
+}
+
 // A site's 11 gradient contributions from its entry-sum totals v (entry_sums):
 //   colour: v[0..2]        r: tau s v[3]      log tau: -tau s (e^a v[6] + e^-a v[7] - r v[3])
 //   p: tau s (e^a u v[4] + e^-a (-u_y, u_x) v[5])      a: -tau s (e^a v[6] - e^-a v[7]) / 2
@@ -1550,14 +1574,28 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
         }
     }
     __syncthreads();  // the staging area is reused for the partials and totals below
-    if (nmine > 0) {
+    // The chunk's runs: summed with entry_acc; if a run's totals are not all
+    // finite (a non-finite entry), the chunk is summed again with entry_sums, which
+    // drops the non-finite sums of each entry, and its partials are rewritten.
+    auto sum_chunk = [&](bool checked) {
         float run[NSUM];
 #pragma unroll
         for (int a = 0; a < NSUM; ++a)
             run[a] = 0.0f;
         int cur = (int)(mps[0] >> 8);
         SiteRec Rc = table_rec(L.T, cur);
-        bool first = true;
+        bool first = true, finite = true;
+        auto close_run = [&](float *dst, int stride) {
+            float all = run[0];
+#pragma unroll
+            for (int a = 0; a < NSUM; ++a) {
+                if (a > 0)
+                    all += run[a];
+                dst[a * stride] = run[a];
+                run[a] = 0.0f;
+            }
+            finite &= finitef(all);
+        };
 #pragma unroll
         for (int j = 0; j < CHUNK; ++j) {
             if (j < nmine) {
@@ -1565,14 +1603,7 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
                 if (sl != cur) {
                     // close the run of `cur`: the chunk's first run becomes its head
                     // partial; a later run is a whole bucket: its total is final
-#pragma unroll
-                    for (int a = 0; a < NSUM; ++a) {
-                        if (first)
-                            L.u.r.part[a][tid] = run[a];
-                        else
-                            L.u.r.fin[a][cur] = run[a];
-                        run[a] = 0.0f;
-                    }
+                    close_run(first ? &L.u.r.part[0][tid] : &L.u.r.fin[0][cur], first ? BLOCK : TBL);
                     first = false;
                     cur = sl;
                     Rc = table_rec(L.T, cur);
@@ -1580,18 +1611,23 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
                 const int q = (int)(mps[j] & 0xFFu);
                 const float Xp = (float)(col0 + (q & (TILE - 1))) + 0.5f;
                 const float Yp = (float)(row0 + q / TILE) + 0.5f;
-                float v[NSUM];
-                entry_sums(Rc, Xp, Yp, mw[j], mg[j], md[j], L.g[q], v);
+                if (checked) {
+                    float v[NSUM];
+                    entry_sums(Rc, Xp, Yp, mw[j], mg[j], md[j], L.g[q], v);
 #pragma unroll
-                for (int a = 0; a < NSUM; ++a)
-                    run[a] += v[a];
+                    for (int a = 0; a < NSUM; ++a)
+                        run[a] += v[a];
+                } else {
+                    entry_acc(Rc, Xp, Yp, mw[j], mg[j], md[j], L.g[q], run);
+                }
             }
         }
         // the last run: head if it is also the first, else tail
-#pragma unroll
-        for (int a = 0; a < NSUM; ++a)
-            L.u.r.part[(first ? 0 : NSUM) + a][tid] = run[a];
-    }
+        close_run(&L.u.r.part[first ? 0 : NSUM][tid], BLOCK);
+        return finite;
+    };
+    if (nmine > 0 && !sum_chunk(false))
+        sum_chunk(true);
     __syncthreads();
 
     // phase 5: one thread per occupied slot (the compacted list) adds up the chunk
