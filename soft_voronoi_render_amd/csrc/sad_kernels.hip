@@ -1111,8 +1111,6 @@ struct BwdShared {
         } r;
     } u;
     float wsum[2 * BLOCK / 64];
-    uint32_t wtot[BLOCK / 64];
-    uint32_t wocc[BLOCK / 64];
     uint8_t occ[TBL];  // the occupied slots, ascending (n_occ of them)
     uint32_t total;
     uint32_t nspill;
@@ -1336,22 +1334,38 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
     __syncthreads();
     // bucket offsets (wave scans of the slot counts, then the waves' totals) and
     // one thread per slot filling its record
-    uint32_t cnt_me = 0, incl = 0;
-    uint64_t occ_mask = 0;  // the wave's occupied slots (waves 0..3)
-    if (tid < TBL) {
-        cnt_me = L.cnt[tid];
-        occ_mask = __ballot(cnt_me > 0);
-        incl = cnt_me;
+    // wave 0 turns the slot counts into bucket offsets (4 slots per lane, then a
+    // wave scan) and lists the occupied slots, while the first 256 threads fill the
+    // slot records
+    if (tid < 64) {
+        const uint4 c4 = reinterpret_cast<const uint4 *>(L.cnt)[lane];
+        const uint32_t s0 = c4.x, s1 = s0 + c4.y, s2 = s1 + c4.z, s3 = s2 + c4.w;
+        const uint32_t n0 = c4.x > 0, n1 = n0 + (c4.y > 0), n2 = n1 + (c4.z > 0), n3 = n2 + (c4.w > 0);
+        uint32_t incl = s3, nincl = n3;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t v = __shfl_up(incl, o, 64);
-            if (lane >= o)
+            const uint32_t v = __shfl_up(incl, o, 64), w = __shfl_up(nincl, o, 64);
+            if (lane >= o) {
                 incl += v;
+                nincl += w;
+            }
         }
-        if (lane == 63)
-            L.wtot[tid >> 6] = incl;
-        if (lane == 0)
-            L.wocc[tid >> 6] = (uint32_t)__popcll(occ_mask);
+        const uint32_t base = incl - s3, nbase = nincl - n3;
+        reinterpret_cast<uint4 *>(L.off)[lane] = make_uint4(base, base + s0, base + s1, base + s2);
+        if (c4.x > 0)
+            L.occ[nbase] = (uint8_t)(4 * lane);
+        if (c4.y > 0)
+            L.occ[nbase + n0] = (uint8_t)(4 * lane + 1);
+        if (c4.z > 0)
+            L.occ[nbase + n1] = (uint8_t)(4 * lane + 2);
+        if (c4.w > 0)
+            L.occ[nbase + n2] = (uint8_t)(4 * lane + 3);
+        if (lane == 63) {
+            L.total = incl;
+            L.n_occ = nincl;
+        }
+    }
+    if (tid < TBL) {
         const uint32_t c = L.T.key[tid];
         if (c != NONE) {
             const SiteRec R = load_rec_global(G, c);
@@ -1362,22 +1376,6 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
     } else if (tid < TBL + NREC / 4) {
         const int j = tid - TBL;  // the null record (px = NaN) of empty entries
         L.T.rec[TBL][j] = make_float4(j == 0 ? __builtin_nanf("") : 0.0f, 0.0f, 0.0f, 0.0f);
-    }
-    __syncthreads();
-    if (tid < TBL) {
-        uint32_t base = 0, obase = 0;
-        for (int w = 0; w < (tid >> 6); ++w) {
-            base += L.wtot[w];
-            obase += L.wocc[w];
-        }
-        L.off[tid] = base + incl - cnt_me;
-        // the compacted list of occupied slots, for the flush
-        if (cnt_me > 0)
-            L.occ[obase + (uint32_t)__popcll(occ_mask & ((1ull << lane) - 1ull))] = (uint8_t)tid;
-        if (tid == 0) {
-            L.total = L.wtot[0] + L.wtot[1] + L.wtot[2] + L.wtot[3];
-            L.n_occ = L.wocc[0] + L.wocc[1] + L.wocc[2] + L.wocc[3];
-        }
     }
     const bool tile_spills = L.nspill > 0;  // the same for the whole block
     __syncthreads();
