@@ -1048,6 +1048,7 @@ __device__ __forceinline__ void load_ids(const uint4 *__restrict__ cand, long p,
     ids[7] = b.w;
 }
 
+
 // Render forward (reading note, key design 2; project page "Method").
 __global__ __launch_bounds__(BLOCK) void k_render_fwd(const float4 *__restrict__ G, uint32_t n_slots,
                                                       const uint4 *__restrict__ cand, int W, int H,
@@ -1251,7 +1252,7 @@ __device__ __forceinline__ void spill_flush(const float4 *__restrict__ G, uint32
 // Per 16x16 tile this runs 8 waves over the same LDS as one lane per pixel, so a
 // SIMD holds twice the waves to hide the latency of the table, record and
 // staging phases, and each lane's serial chain of inserts and blends halves.
-constexpr int BWD_THREADS = 2 * BLOCK;
+constexpr int PAIR_THREADS = 2 * BLOCK;
 constexpr int KH = K / 2;
 
 struct PairSums {
@@ -1271,7 +1272,71 @@ __device__ __forceinline__ float pair_max(float x)
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__restrict__ G, uint32_t n_slots,
+// The blend of one pixel's list over a lane pair (reading note, key design 2;
+// summary B.4: max-subtracted softmax, invalid and non-finite entries skipped):
+// this lane's half (entries 4 half .. 4 half + 3) and the pair's totals.  Every
+// lane of the wave must take part (the exchanges read the partner lane).
+struct PairBlend {
+    float l[KH], e[KH], c0[KH], c1[KH], c2[KH];
+    bool use[KH];
+    bool any;
+    PairSums Se, S0, S1, S2;  // sums of e and e c over the pair (and the partner's half)
+    float iZ, chat0, chat1, chat2;
+};
+
+__device__ __forceinline__ void pair_blend(const TileTable &T, const float4 *__restrict__ G,
+                                           const uint32_t (&ids)[KH], const int (&slot)[KH], float X, float Y,
+                                           float s, int half, PairBlend &B)
+{
+    // every entry reads the table (empty and spilled ones the null record), then
+    // spilled entries, if the wave has any, are redone from their global records
+    auto entry = [&](int k, const SiteRec &R) {
+        const float lk = -R.v[R_TAU] * rec_score(R, X, Y, s);
+        B.use[k] = finitef(lk);
+        B.l[k] = lk;
+        B.c0[k] = B.use[k] ? R.v[R_C0] : 0.0f;
+        B.c1[k] = B.use[k] ? R.v[R_C1] : 0.0f;
+        B.c2[k] = B.use[k] ? R.v[R_C2] : 0.0f;
+    };
+    bool spilled = false;
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+        entry(k, table_rec(T, slot[k] >= 0 ? slot[k] : TBL));
+        spilled |= slot[k] == -1;
+    }
+    if (__any(spilled)) {
+#pragma unroll
+        for (int k = 0; k < KH; ++k)
+            if (slot[k] == -1)
+                entry(k, load_rec_global(G, ids[k]));
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < KH; ++k)
+        mx = B.use[k] ? fmaxf(mx, B.l[k]) : mx;
+    mx = pair_max(mx);
+    B.any = mx > -__builtin_inff();
+    float ze = 0.0f, z0 = 0.0f, z1 = 0.0f, z2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+        B.e[k] = B.use[k] ? __expf(B.l[k] - mx) : 0.0f;
+        ze += B.e[k];
+        z0 = fmaf(B.e[k], B.c0[k], z0);
+        z1 = fmaf(B.e[k], B.c1[k], z1);
+        z2 = fmaf(B.e[k], B.c2[k], z2);
+    }
+    B.Se = pair_sums(ze, half);
+    B.S0 = pair_sums(z0, half);
+    B.S1 = pair_sums(z1, half);
+    B.S2 = pair_sums(z2, half);
+    B.iZ = B.any ? hw_rcp(B.Se.total) : 0.0f;  // Z >= 1: the largest term is exp(0)
+    B.chat0 = B.S0.total * B.iZ;
+    B.chat1 = B.S1.total * B.iZ;
+    B.chat2 = B.S2.total * B.iZ;
+}
+
+
+__global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(const float4 *__restrict__ G, uint32_t n_slots,
                                                             const uint4 *__restrict__ cand,
                                                             const float *__restrict__ target, int W, int H,
                                                             float *__restrict__ grad, float *__restrict__ loss_sum,
@@ -1384,50 +1449,13 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
     // pixel outside the image has no usable entry), per-entry softmax quantities;
     // staged entries written in slot order, spilled entries flushed to global memory
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
-    float l[KH], c0[KH], c1[KH], c2[KH];
-    bool use[KH];
-    {
-        auto entry = [&](int k, const SiteRec &R) {
-            const float lk = -R.v[R_TAU] * rec_score(R, X, Y, s);
-            use[k] = finitef(lk);
-            l[k] = lk;
-            c0[k] = use[k] ? R.v[R_C0] : 0.0f;
-            c1[k] = use[k] ? R.v[R_C1] : 0.0f;
-            c2[k] = use[k] ? R.v[R_C2] : 0.0f;
-        };
-        bool spilled = false;
-#pragma unroll
-        for (int k = 0; k < KH; ++k) {
-            entry(k, table_rec(L.T, slot[k] >= 0 ? slot[k] : TBL));
-            spilled |= slot[k] == -1;
-        }
-        if (__any(spilled)) {
-#pragma unroll
-            for (int k = 0; k < KH; ++k)
-                if (slot[k] == -1)
-                    entry(k, load_rec_global(G, ids[k]));
-        }
-    }
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int k = 0; k < KH; ++k)
-        mx = use[k] ? fmaxf(mx, l[k]) : mx;
-    mx = pair_max(mx);
-    const bool any = mx > -__builtin_inff();
-    float e[KH];
-    float ze = 0.0f, z0 = 0.0f, z1 = 0.0f, z2 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < KH; ++k) {
-        e[k] = use[k] ? __expf(l[k] - mx) : 0.0f;
-        ze += e[k];
-        z0 = fmaf(e[k], c0[k], z0);
-        z1 = fmaf(e[k], c1[k], z1);
-        z2 = fmaf(e[k], c2[k], z2);
-    }
-    const PairSums Se = pair_sums(ze, half), S0 = pair_sums(z0, half), S1 = pair_sums(z1, half),
-                   S2 = pair_sums(z2, half);
-    const float iZ = any ? hw_rcp(Se.total) : 0.0f;  // Z >= 1: the largest term is exp(0)
-    const float chat0 = S0.total * iZ, chat1 = S1.total * iZ, chat2 = S2.total * iZ;
+    PairBlend B;
+    pair_blend(L.T, G, ids, slot, X, Y, s, half, B);
+    const float *l = B.l, *c0 = B.c0, *c1 = B.c1, *c2 = B.c2, *e = B.e;
+    const bool *use = B.use;
+    const bool any = B.any;
+    const PairSums &Se = B.Se, &S0 = B.S0, &S1 = B.S1, &S2 = B.S2;
+    const float iZ = B.iZ, chat0 = B.chat0, chat1 = B.chat1, chat2 = B.chat2;
     float err = 0.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     if (inside) {
         if (out_rgb && half == 0) {  // the forward of the same map, for free
@@ -1546,7 +1574,7 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
     if (tid == 0 && loss_sum) {
         float v = 0.0f;
 #pragma unroll
-        for (int w = 0; w < BWD_THREADS / 64; ++w)
+        for (int w = 0; w < PAIR_THREADS / 64; ++w)
             v += L.wsum[w];
         unsafeAtomicAdd(loss_sum + (blockIdx.x & (SAD_LOSS_SLOTS - 1)), v);
     }
@@ -1666,7 +1694,7 @@ __global__ __launch_bounds__(BWD_THREADS) void k_render_bwd(const float4 *__rest
     // of one site, so the lanes of an atomic instruction share the site's 64-byte
     // gradient record instead of touching one cache line each
     const int n_items = (int)L.n_occ * SAD_NACC;
-    for (int i = tid; i < n_items; i += BWD_THREADS) {
+    for (int i = tid; i < n_items; i += PAIR_THREADS) {
         const int j = i / SAD_NACC, a = i - j * SAD_NACC;
         const int sl = L.occ[j];
         const float v = L.u.r.fin[a][sl];
@@ -2435,7 +2463,7 @@ int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const fl
     if (!aligned16(cand) || !aligned16(grad) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
-    hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(BWD_THREADS), 0, (hipStream_t)stream, (const float4 *)rec,
+    hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(PAIR_THREADS), 0, (hipStream_t)stream, (const float4 *)rec,
                        (uint32_t)n_slots, (const uint4 *)cand, target, W, H, grad, loss_sum, out_rgb, scale_of(W, H),
                        mg, g.tiles_x, g.nb);
     return launched();
