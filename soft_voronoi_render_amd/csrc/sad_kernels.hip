@@ -11,7 +11,8 @@
 // implements.
 //
 // Execution model: image-space kernels cover the image with 16x16-pixel tiles,
-// one 256-thread workgroup (four wave64s) per tile, one pixel per lane.  Tiles
+// one 256-thread workgroup (four wave64s) per tile, one pixel per lane (the fused
+// backward: 512 threads, two lanes per pixel).  Tiles
 // are handed out so that each XCD (workgroup IDs are dealt round-robin over the
 // 8 XCDs) receives one contiguous band of tiles, which keeps the site gathers and
 // neighbour-list re-reads of a band inside that XCD's L2.  Per-site kernels use
@@ -1397,8 +1398,6 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(const float4 *__res
     if (__any(nsp > 0) && lane == 0)
         atomicAdd(&L.nspill, 1u);
     __syncthreads();
-    // bucket offsets (wave scans of the slot counts, then the waves' totals) and
-    // one thread per slot filling its record
     // wave 0 turns the slot counts into bucket offsets (4 slots per lane, then a
     // wave scan) and lists the occupied slots, while the first 256 threads fill the
     // slot records
