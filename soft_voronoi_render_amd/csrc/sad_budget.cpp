@@ -13,6 +13,8 @@
 #include <algorithm>
 #include <cmath>
 #include <numeric>
+#include <system_error>
+#include <thread>
 #include <vector>
 
 #include "sad.h"
@@ -52,6 +54,29 @@ void principal_axis(double a, double b, double c, double &lam, double &ex, doubl
     ey /= n;
 }
 
+// Runs f(lo, hi) over [0, n) in contiguous ranges on up to 8 host threads (the
+// calling thread takes the first range); fewer threads for small n, and the
+// calling thread alone if threads cannot be started.  The ranges write disjoint
+// data, so the result does not depend on the thread count.
+template <class F>
+void parallel_for(long n, F f)
+{
+    const long hw = (long)std::max(1u, std::thread::hardware_concurrency());
+    const long T = std::max(1L, std::min({hw, 8L, n / 2048}));
+    std::vector<std::thread> th;
+    long started = 1;
+    try {
+        for (long t = 1; t < T; ++t, ++started)
+            th.emplace_back(f, n * t / T, n * (t + 1) / T);
+    } catch (const std::system_error &) {
+    }
+    f(0, n / T);
+    for (long t = started; t < T; ++t)  // the ranges no thread took
+        f(n * t / T, n * (t + 1) / T);
+    for (auto &x : th)
+        x.join();
+}
+
 }  // namespace
 
 extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, int capacity, int *n_slots,
@@ -87,14 +112,19 @@ extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, i
     // 1. split set: largest score, ties -> lower ID.  Only the first n_split in
     // that order are needed, and in that order (it decides which free slot each
     // second child takes): select them, then sort the selection.
+    std::vector<double> score(active.size());
+    parallel_for((long)active.size(), [&](long lo, long hi) {
+        for (long j = lo; j < hi; ++j) {
+            const long i = active[j];
+            const double mass = stats[i * SAD_STAT_LD + 0], energy = stats[i * SAD_STAT_LD + 1];
+            score[j] = energy / std::pow(std::max(mass, (double)cfg->min_mass), (double)cfg->alpha);
+        }
+    });
     std::vector<std::pair<double, int>> sc;
     sc.reserve(active.size());
-    for (int i : active) {
-        const double mass = stats[(long)i * SAD_STAT_LD + 0], energy = stats[(long)i * SAD_STAT_LD + 1];
-        const double S = energy / std::pow(std::max(mass, (double)cfg->min_mass), (double)cfg->alpha);
-        if (std::isfinite(S) && S > 0.0)
-            sc.push_back({S, i});
-    }
+    for (size_t j = 0; j < active.size(); ++j)
+        if (std::isfinite(score[j]) && score[j] > 0.0)
+            sc.push_back({score[j], active[j]});
     const auto split_first = [](const std::pair<double, int> &a, const std::pair<double, int> &b) {
         return a.first > b.first || (a.first == b.first && a.second < b.second);
     };
@@ -123,15 +153,16 @@ extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, i
                          [](const std::pair<double, int> &a, const std::pair<double, int> &b) {
                              return a.first < b.first || (a.first == b.first && a.second < b.second);
                          });
-    int pruned = 0;
-    for (size_t j = 0; j < k_prune; ++j) {
-        const int i = rm[j].second;
-        P(PX, i) = -1.0f;
-        P(PY, i) = -1.0f;
-        for (int q = 0; q < SAD_NPARAM; ++q)
-            m[q * st + i] = v[q * st + i] = 0.0f;
-        ++pruned;
-    }
+    const int pruned = (int)k_prune;
+    parallel_for((long)k_prune, [&](long lo, long hi) {
+        for (long j = lo; j < hi; ++j) {
+            const int i = rm[j].second;
+            P(PX, i) = -1.0f;
+            P(PY, i) = -1.0f;
+            for (int q = 0; q < SAD_NPARAM; ++q)
+                m[q * st + i] = v[q * st + i] = 0.0f;
+        }
+    });
 
     // free slots for the second children: inactive slots below n (ascending), then n, n+1, ...
     std::vector<int> free_slots;
@@ -148,92 +179,110 @@ extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, i
         return -1;
     };
 
-    // 3. splits
+    // 3. splits.  The second children's slots are assigned in split order (the
+    // first split that finds none ends the splitting); the splits then write
+    // disjoint slots (a parent's own and its second child's) and run in parallel;
+    // the map entries they seed are applied afterwards, in split order.
     const Img img{target, W, H};
     const float lshrink = std::log(cfg->shrink);
-    int done = 0;
+    std::vector<int> bslot;
+    bslot.reserve(split.size());
     bool short_of_slots = false;
-    for (int i : split) {
+    for (size_t j = 0; j < split.size(); ++j) {
         const int b = take_slot();
         if (b < 0) {
             short_of_slots = true;
             break;
         }
-        const float *S = stats + (long)i * SAD_STAT_LD;
-        const double mass = S[0], E = S[1];
-        double ox = 0.0, oy = 0.0;
-        bool have_axis = false;
-        if (mass >= cfg->min_mass && E > 0.0) {
-            const double mx = S[2] / E, my = S[3] / E;
-            const double cxx = S[4] / E - mx * mx, cxy = S[5] / E - mx * my, cyy = S[6] / E - my * my;
-            double lam, ex, ey;
-            principal_axis(cxx, cxy, cyy, lam, ex, ey);
-            if (std::isfinite(lam) && lam > 0.0) {
-                const double h = 0.5 * std::sqrt(lam);
-                ox = h * ex;
-                oy = h * ey;
-                have_axis = true;
-            }
-        }
-        if (!have_axis) {
-            const int c = img.col(P(PX, i)), r = img.row(P(PY, i));
-            double gx = (img.lum(c + 1, r - 1) + 2.0 * img.lum(c + 1, r) + img.lum(c + 1, r + 1)) -
-                        (img.lum(c - 1, r - 1) + 2.0 * img.lum(c - 1, r) + img.lum(c - 1, r + 1));
-            double gy = (img.lum(c - 1, r + 1) + 2.0 * img.lum(c, r + 1) + img.lum(c + 1, r + 1)) -
-                        (img.lum(c - 1, r - 1) + 2.0 * img.lum(c, r - 1) + img.lum(c + 1, r - 1));
-            const double gn = std::sqrt(gx * gx + gy * gy);
-            if (gn > 0.0) {
-                gx /= gn;
-                gy /= gn;
-            } else {
-                gx = 1.0;
-                gy = 0.0;
-            }
-            const double h = 0.5 * std::sqrt(std::max(mass, 1.0) / M_PI);
-            ox = h * gx;
-            oy = h * gy;
-        }
-        const double px = P(PX, i), py = P(PY, i);
-        const double cx[2] = {px - ox, px + ox}, cy[2] = {py - oy, py + oy};
-        const int slot[2] = {i, b};
-        float par[SAD_NPARAM];
-        for (int q = 0; q < SAD_NPARAM; ++q)
-            par[q] = P(q, i);
-        for (int h = 0; h < 2; ++h) {
-            const int s = slot[h];
-            for (int q = 0; q < SAD_NPARAM; ++q) {
-                P(q, s) = par[q];
-                m[q * st + s] = v[q * st + s] = 0.0f;
-            }
-            const double x = std::min(std::max(cx[h], 0.0), (double)W);
-            const double y = std::min(std::max(cy[h], 0.0), (double)H);
-            P(PX, s) = (float)x;
-            P(PY, s) = (float)y;
-            P(PR, s) = par[PR] * cfg->shrink;
-            P(PLT, s) = par[PLT] + lshrink;
-            const float *tc = target + 3 * ((long)img.row(y) * W + img.col(x));
-            P(PCR, s) = tc[0];
-            P(PCG, s) = tc[1];
-            P(PCB, s) = tc[2];
-        }
-        // seed child B into the list of its pixel's map entry and of the 4
-        // neighbour entries (last place)
-        const int bc = img.col(P(PX, b)) / cell, br = img.row(P(PY, b)) / cell;
-        const int dc[5] = {0, -1, 1, 0, 0}, dr[5] = {0, 0, 0, -1, 1};
-        for (int q = 0; q < 5; ++q) {
-            const int c = bc + dc[q], r = br + dr[q];
-            if (c >= 0 && c < Wm && r >= 0 && r < Hm) {
-                const long e = (long)r * Wm + c;
-                if (cand)
-                    cand[e * SAD_K + (SAD_K - 1)] = (uint32_t)b;
-                if (seeds) {
-                    seeds[2 * n_seeds] = (uint32_t)e;
-                    seeds[2 * n_seeds + 1] = (uint32_t)b;
-                    ++n_seeds;
+        bslot.push_back(b);
+    }
+    const int done = (int)bslot.size();
+    std::vector<long> seed_e((size_t)done * 5, -1L);  // per split: seeded entries, -1 = none
+    parallel_for(done, [&](long lo, long hi) {
+        for (long jj = lo; jj < hi; ++jj) {
+            const int i = split[jj], b = bslot[jj];
+            const float *S = stats + (long)i * SAD_STAT_LD;
+            const double mass = S[0], E = S[1];
+            double ox = 0.0, oy = 0.0;
+            bool have_axis = false;
+            if (mass >= cfg->min_mass && E > 0.0) {
+                const double mx = S[2] / E, my = S[3] / E;
+                const double cxx = S[4] / E - mx * mx, cxy = S[5] / E - mx * my, cyy = S[6] / E - my * my;
+                double lam, ex, ey;
+                principal_axis(cxx, cxy, cyy, lam, ex, ey);
+                if (std::isfinite(lam) && lam > 0.0) {
+                    const double h = 0.5 * std::sqrt(lam);
+                    ox = h * ex;
+                    oy = h * ey;
+                    have_axis = true;
                 }
             }
+            if (!have_axis) {
+                const int c = img.col(P(PX, i)), r = img.row(P(PY, i));
+                double gx = (img.lum(c + 1, r - 1) + 2.0 * img.lum(c + 1, r) + img.lum(c + 1, r + 1)) -
+                            (img.lum(c - 1, r - 1) + 2.0 * img.lum(c - 1, r) + img.lum(c - 1, r + 1));
+                double gy = (img.lum(c - 1, r + 1) + 2.0 * img.lum(c, r + 1) + img.lum(c + 1, r + 1)) -
+                            (img.lum(c - 1, r - 1) + 2.0 * img.lum(c, r - 1) + img.lum(c + 1, r - 1));
+                const double gn = std::sqrt(gx * gx + gy * gy);
+                if (gn > 0.0) {
+                    gx /= gn;
+                    gy /= gn;
+                } else {
+                    gx = 1.0;
+                    gy = 0.0;
+                }
+                const double h = 0.5 * std::sqrt(std::max(mass, 1.0) / M_PI);
+                ox = h * gx;
+                oy = h * gy;
+            }
+            const double px = P(PX, i), py = P(PY, i);
+            const double cx[2] = {px - ox, px + ox}, cy[2] = {py - oy, py + oy};
+            const int slot[2] = {i, b};
+            float par[SAD_NPARAM];
+            for (int q = 0; q < SAD_NPARAM; ++q)
+                par[q] = P(q, i);
+            for (int h = 0; h < 2; ++h) {
+                const int s = slot[h];
+                for (int q = 0; q < SAD_NPARAM; ++q) {
+                    P(q, s) = par[q];
+                    m[q * st + s] = v[q * st + s] = 0.0f;
+                }
+                const double x = std::min(std::max(cx[h], 0.0), (double)W);
+                const double y = std::min(std::max(cy[h], 0.0), (double)H);
+                P(PX, s) = (float)x;
+                P(PY, s) = (float)y;
+                P(PR, s) = par[PR] * cfg->shrink;
+                P(PLT, s) = par[PLT] + lshrink;
+                const float *tc = target + 3 * ((long)img.row(y) * W + img.col(x));
+                P(PCR, s) = tc[0];
+                P(PCG, s) = tc[1];
+                P(PCB, s) = tc[2];
+            }
+            // seed child B into the list of its pixel's map entry and of the 4
+            // neighbour entries (last place)
+            const int bc = img.col(P(PX, b)) / cell, br = img.row(P(PY, b)) / cell;
+            const int dc[5] = {0, -1, 1, 0, 0}, dr[5] = {0, 0, 0, -1, 1};
+            for (int q = 0; q < 5; ++q) {
+                const int c = bc + dc[q], r = br + dr[q];
+                if (c >= 0 && c < Wm && r >= 0 && r < Hm)
+                    seed_e[5 * jj + q] = (long)r * Wm + c;
+            }
         }
-        ++done;
+    });
+    for (long jj = 0; jj < done; ++jj) {
+        const uint32_t b = (uint32_t)bslot[jj];
+        for (int q = 0; q < 5; ++q) {
+            const long e = seed_e[5 * jj + q];
+            if (e < 0)
+                continue;
+            if (cand)
+                cand[e * SAD_K + (SAD_K - 1)] = b;
+            if (seeds) {
+                seeds[2 * n_seeds] = (uint32_t)e;
+                seeds[2 * n_seeds + 1] = b;
+                ++n_seeds;
+            }
+        }
     }
     *n_slots = count;
     if (seeds)

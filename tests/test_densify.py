@@ -253,6 +253,27 @@ def test_host_densify_matches_oracle(orc, seed, cfg, cell):
     assert got[1] > 0 or cfg.split_frac == 0
 
 
+def test_host_densify_matches_oracle_at_threaded_sizes(orc):
+    """Large enough that every phase of the routine runs on several host threads
+    (scores of 20 000 sites, about 5000 splits and 5000 prunes): the result must
+    still equal the oracle's, which takes the splits one by one in order."""
+    W, H, n, cap = 256, 192, 20000, 21000
+    case = _random_budget_case(8, W, H, n, cap, inactive=40)
+    cfg = sad.BudgetConfig(split_frac=0.25, prune_frac=0.25)
+    mine = [a.copy() for a in case]
+    ref = [a.copy() for a in case]
+    got = sad.densify_prune(mine[0], mine[1], mine[2], n, cap, mine[3], mine[4], mine[5], W, H, mine[6], cfg)
+    f32 = lambda x: float(np.float32(x))
+    want = orc_densify(ref[0], ref[1], ref[2], n, cap, ref[3], ref[4], ref[5], W, H, ref[6],
+                       f32(cfg.split_frac), f32(cfg.prune_frac), f32(cfg.alpha), f32(cfg.min_mass), f32(cfg.shrink))
+    assert got[:3] == want[:3] and got[1] > 4096 and got[2] > 4096
+    assert (got[3] == sad.SAD_ERR_CAPACITY) == want[3]
+    assert np.allclose(mine[0][:2], ref[0][:2], atol=2e-5)
+    assert np.allclose(mine[0][2:], ref[0][2:], atol=1e-6, equal_nan=True)
+    assert np.array_equal(mine[1], ref[1]) and np.array_equal(mine[2], ref[2])
+    assert np.array_equal(mine[5], ref[5])
+
+
 def test_host_densify_rejects_bad_arguments():
     W, H, n, cap = 16, 12, 20, 24
     S, m, v, stats, removal, cand, T = _random_budget_case(7, W, H, n, cap, inactive=0)
