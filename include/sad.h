@@ -334,6 +334,9 @@ int sad_densify_stats(const float *rec, int n_slots, const uint32_t *cand, const
  *  (out, may be NULL) receive the numbers of splits and prunes done; seeds
  *  uint32 [seeds_cap][2] or NULL with seeds_cap >= 5 * floor(split_frac * A) and
  *  *n_seeds (out) the number of pairs written.
+ * The scores, prunes and splits run on up to 8 host threads that the call starts
+ * and joins (one thread if none can be started); the result is the same as with
+ * one thread.  Concurrent calls on different arrays are safe.
  * Errors: SAD_ERR_ARG (checked before anything is modified, including a seeds
  *  buffer below that bound); SAD_ERR_CAPACITY when some selected sites could not
  *  be split for want of a free slot (everything that fitted is done).
