@@ -30,7 +30,6 @@ constexpr uint32_t NONE = SAD_INVALID;
 constexpr int TILE = 16;
 constexpr int BLOCK = TILE * TILE;
 constexpr int NXCD = 8;
-constexpr int HASH_SLOTS = 256;
 constexpr int HASH_PROBES = 12;
 
 // Site planes (order of the site buffer).
@@ -1450,7 +1449,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(const float4 *__res
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
     PairBlend B;
     pair_blend(L.T, G, ids, slot, X, Y, s, half, B);
-    const float *l = B.l, *c0 = B.c0, *c1 = B.c1, *c2 = B.c2, *e = B.e;
+    const float *c0 = B.c0, *c1 = B.c1, *c2 = B.c2, *e = B.e;
     const bool *use = B.use;
     const bool any = B.any;
     const PairSums &Se = B.Se, &S0 = B.S0, &S1 = B.S1, &S2 = B.S2;
