@@ -13,6 +13,15 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running CPU test")
 
 
+def pytest_sessionstart(session):
+    # a fresh checkout has no built library (it is not versioned): build it once
+    # here (hipcc cross-compiles without a GPU) rather than in whichever test
+    # happens to need it first
+    import soft_voronoi_render_amd as sad
+    if not os.path.exists(sad.LIB_PATH):
+        sad.build()
+
+
 @pytest.fixture(scope="session")
 def orc():
     import oracle
