@@ -68,6 +68,8 @@ def test_propagate_rejects_bad_arguments(L):
     assert call(n=-1) == ERR_ARG
     assert call(W=-1) == ERR_ARG
     assert call(H=70000) == ERR_ARG
+    assert call(W=65536) == ERR_ARG      # one past SAD_MAX_DIM (65535, the largest accepted)
+    assert call(H=65536) == ERR_ARG
     assert call(rec=0) == ERR_ARG
     assert call(rec=0, W=0) == 0         # empty image: pointers are not needed
     assert call(rec=P + 8) == ERR_ALIGN
@@ -95,6 +97,8 @@ def test_render_and_adam_reject_bad_arguments(L):
     assert L.sad_render_fwd(0, 4, P, 16, 16, 1, Q, None) == ERR_ARG
     assert L.sad_render_fwd(P, 4, P, 0, 16, 1, Q, None) == 0
     assert L.sad_render_fwd(P, 4, P, 16, 16, 0, Q, None) == ERR_ARG  # cell 0
+    assert L.sad_render_fwd(P, 4, P, 65536, 1, 1, Q, None) == ERR_ARG  # beyond SAD_MAX_DIM
+    assert L.sad_render_bwd(P, 4, P, Q, 1, 65536, 1, Q, None, None, None) == ERR_ARG
     assert L.sad_render_bwd(P, 4, P, 0, 16, 16, 1, Q, None, None, None) == ERR_ARG  # target NULL
     assert L.sad_render_bwd(P, 4, P + 4, Q, 16, 16, 1, Q, None, None, None) == ERR_ALIGN
     assert L.sad_render_bwd(P, 4, P, Q, 16, 16, 1, Q + 4, None, None, None) == ERR_ALIGN  # grad records

@@ -91,6 +91,30 @@ def test_propagate_schedule_from_empty_matches_oracle_each_pass(orc):
     assert recall > 0.99
 
 
+@pytest.mark.parametrize("W,H", [(65535, 2), (2, 65535)])
+def test_maximum_image_dimension(orc, W, H):
+    """Images as wide or as tall as the ABI allows (SAD_MAX_DIM): propagation at the
+    first jump of the schedule (32768) and at jump 1, then the fused forward and
+    backward (whose image must equal the standalone forward's)."""
+    n = 2000
+    print(f"maximum dimension W={W} H={H} n={n}", flush=True)
+    S, cin = _case(W, H, n, seed=21)
+    sched = sad.jump_schedule(W, H, 4)
+    assert sched[0] == 32768
+    pix = np.arange(W * H)
+    for jump, m in ((sched[0], 8), (1, 4)):
+        got = _gpu_propagate(S, n, cin, W, H, jump, 7, 31, m)
+        ref = orc.propagate(S, n, cin, W, H, jump, 7, 31, m)
+        u, cnt = orc.union_pixels(S, n, cin, W, H, jump, 7, 31, m, pix)
+        assert compare_lists(orc, S, n, W, H, pix, got, ref, u, cnt) <= max(2, W * H // 2000)
+    cand = orc.propagate(S, n, cin, W, H, 1, 0, 1, 4)
+    tgt = orc.hard_render(synth.random_sites(n, W, H, 22), n, W, H) + synth.pixel_noise(W, H, 23)
+    got, loss = _bwd(S, n, cand, tgt, W, H)
+    ref, rloss = orc.render_bwd(S, n, cand, tgt, W, H)
+    _check_grads(got, ref)
+    assert loss == pytest.approx(rloss, rel=1e-4)
+
+
 def test_site_records_encode_the_score(orc):
     """The record reproduces the oracle's score: d = s*sqrt((U.delta)^2 +
     (V x delta)^2) - s*r evaluated in float64 from the GPU record vs the oracle's
