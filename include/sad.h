@@ -14,7 +14,8 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Ownership.  The caller owns every buffer.  The library allocates no memory and
+ * Ownership.  The caller owns every buffer.  The library allocates no device
+ *   memory (sad_densify_prune uses temporary host memory and host threads) and
  *   keeps no state between calls, so calls are reentrant.
  * Pointers.  Arguments named `sites`, `rec`, `packed`, `cand*`, `out_rgb`,
  *   `target`, `grad`, `m`, `v`, `loss_sum`, `stats`, `words`, `header` and `points`
