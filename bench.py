@@ -2,29 +2,46 @@
 """Throughput of the SAD hot path on one MI355X.
 
 One step = one fit iteration over the whole image: one propagation pass of the
-candidate map (sad_topk_propagate), the render forward and backward (one
-sad_render_bwd launch that writes the rendered image and accumulates the
-gradients through the per-tile reduction) and Adam (sad_adam_step), K = 8.  The
-standalone forward (sad_render_fwd, the inference render) is timed beside it.  Default workload: the Kodak-shaped fit, 768x512 RGB
-float32, N = 50,000 sites, 4 injected candidates per pixel, cold start with the
-coarse-to-fine jump schedule 512, 256, ..., 1, 1, ...  Inputs are synthetic and
-seeded (sites: uniform positions, colours U[0,1]^3, r U[0,2] px, a N(0,0.5),
-direction U[0,pi), log tau U[2,5]; target: hard render of a second seeded site
-set plus N(0, 0.01) noise).
+candidate map (sad_topk_propagate_rec), the render forward and backward (one
+sad_render_bwd_rec launch that writes the rendered image and accumulates the
+gradients through the per-tile reduction) and Adam (sad_adam_step_rec), K = 8.
 
-Other workloads (`--workload img2048`, `div2k2040`, `edit4096`, `tiny64`) run the
-same loop on their shapes; img2048 uses its own recipe (a seeded photo-like image
-of polygons and plane waves, gradient-weighted initial sites coloured from it).
+Default workload: img2048 -- 2048x2048 RGB float32, N = 131,072 sites placed by
+gradient-weighted sampling of a seeded photo-like image (mid-grey, 64 random
+convex polygons, 32 plane waves), 4 injected candidates per pixel, a 500-iteration
+fit: the coarse-to-fine warm-up (jumps 1024, 512, ..., 1, one pass per
+iteration), then one pass at jump 1 per iteration.
 
-The K timed steps replay one HIP graph holding the K iterations (the launches of
-a step depend only on the step index, so the whole fit is captured once); the
-state is reset to the cold start before the timed replay.  Prints one JSON line.
+Timing.  The fit is captured in three HIP graphs -- the warm-up passes (the
+cold start), the rest of the `--warmup` iterations, and the `--steps` timed
+iterations -- and replayed in order from the initial state; only the last replay
+is timed, so every timed step runs the same launches (jump-1 propagation,
+fused forward+backward, Adam) and ms_per_step does not depend on --steps.  The
+cold start and the whole fit are reported in their own fields.  Inputs are
+resident in HBM before any timed region.
+
+Byte model (compulsory HBM traffic: each tensor byte read once and written once
+per call), P pixels, N sites:
+    propagate  64 P + 24 N     (map in and out; site geometry)
+    forward    44 P + 40 N     (map, image out; site parameters)
+    backward   44 P + 84 N     (map, target; site parameters; the 11-accumulator flush)
+    Adam       324 N           (parameters and moments read and written; gradients read, zeroed)
+    one step   152 P + 472 N
+The fused forward+backward launch is priced as forward + backward (88 P + 124 N).
+
+The edit block (on by default, `--no-edit` to skip) measures the 4096x4096,
+N = 1,000,000 edit stress: the map is converged (two coarse-to-fine refreshes
+with 8 injected per pixel, then 20 passes at jump 1), 10 % of the sites are moved
+by U[-256, 256] px, and one full refresh (jumps 2048 .. 1, 12 passes, 8 injected)
+plus one fused forward+backward is timed; recall is measured against the exact
+top-8 (brute force over all sites on the GPU) at 4096 seeded pixels.
+
+Prints one JSON line.
 """
 import argparse
 import hashlib
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -41,6 +58,7 @@ KERNEL_SRC = os.path.join(ROOT, "soft_voronoi_render_amd", "csrc", "sad_kernels.
 # kernel symbol of each timed launch (as rocprofv3 names it)
 KERNEL_SYMBOL = {"propagate": "k_propagate<1,256,0>", "fwd_bwd": "k_render_bwd", "adam": "k_adam",
                  "fwd": "k_render_fwd"}
+STEP_KERNELS = ("propagate", "fwd_bwd", "adam")
 
 
 def source_digest():
@@ -84,6 +102,23 @@ def measured_traffic(workload, kernel):
     return float(rows[KERNEL_SYMBOL[kernel]]["bytes_per_launch"])
 
 
+def algorithmic_bytes(P, N):
+    """Compulsory HBM bytes per launch under the byte model of the module
+    docstring."""
+    fwd = 44 * P + 40 * N
+    bwd = 44 * P + 84 * N
+    return {
+        "propagate": 64 * P + 24 * N,
+        "fwd_bwd": fwd + bwd,
+        "adam": 324 * N,
+        "fwd": fwd,
+    }
+
+
+def step_bytes(P, N):
+    return 152 * P + 472 * N
+
+
 def algorithmic_ops(P, N, M, K=8):
     """VALU lane operations per launch that the literal algorithm needs (an FMA,
     compare or select counts one; a square root, exp or reciprocal counts one).
@@ -105,28 +140,6 @@ def algorithmic_ops(P, N, M, K=8):
         "fwd_bwd": P * (K * 80 + 10),
         "adam": N * 10 * 12,
         "fwd": P * (K * 20 + 4),
-    }
-
-
-def algorithmic_bytes(P, N):
-    """Compulsory HBM bytes per launch (each tensor byte read once, written once).
-
-    propagate: map in + map out (64 B/px) + the 32-byte scoring half of each
-               site record (32 B/site)
-    fwd_bwd:   map (32 B/px) + target (12 B/px) + image out (12 B/px) + the site
-               record (64 B/site) + one read-modify-write flush of the 11
-               accumulators (88 B/site)
-    adam:      params, m, v read and written (240 B/site) + the 10 gradients of
-               the site's record read and zeroed (80 B/site) + the site record
-               written (64 B/site)
-    fwd:       (standalone render, not part of the step) map (32 B/px) + image
-               out (12 B/px) + the 44 bytes of the record the blend reads
-    """
-    return {
-        "propagate": 64 * P + 32 * N,
-        "fwd_bwd": 56 * P + 152 * N,
-        "adam": 384 * N,
-        "fwd": 44 * P + 44 * N,
     }
 
 
@@ -170,17 +183,115 @@ def make_inputs(wl, dev):
     return S, tgt
 
 
+def timed(fn, stream):
+    """Milliseconds of fn() on `stream`, bracketed by HIP events on that stream."""
+    import torch
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def edit_refresh(dev, reps, stream):
+    """The 4096x4096 edit stress (module docstring): per-pass refresh times, the
+    fused forward+backward, throughput by the byte model, recall at 4096 pixels."""
+    import torch
+
+    import soft_voronoi_render_amd as sad
+    import synth
+
+    wl = synth.WORKLOADS["edit4096"]
+    W, H, n, M = wl.W, wl.H, wl.n_sites, wl.n_inject
+    P = W * H
+    S = synth.random_sites(n, W, H, synth.SEED_MODEL)
+    S_d = torch.from_numpy(S).to(dev)
+    rec = sad.new_records(n, dev)
+    sad.site_records(S_d, n, rec)
+    a, b = sad.new_map(W, H, dev), sad.new_map(W, H, dev)
+    sched = sad.jump_schedule(W, H, 12)
+    pidx = 0
+    for k in sched + sched + [1] * 20:
+        sad.topk_propagate_rec(rec, n, a, b, W, H, k, pidx, synth.SEED_INJECT, M)
+        a, b = b, a
+        pidx += 1
+    S2 = synth.displace_sites(S, n, W, H, seed=77)
+    S_d.copy_(torch.from_numpy(S2))
+    sad.site_records(S_d, n, rec)
+    backup = a.clone()
+    tgt = torch.from_numpy((synth.pixel_noise(W, H, 5, 0.2) + 0.5).astype(np.float32)).to(dev)
+    rgb = torch.empty((H, W, 3), dtype=torch.float32, device=dev)
+    grad = sad.new_grad(n, dev)
+    loss = sad.new_loss(dev)
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(reps):
+        a.copy_(backup)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sched) + 2)]
+        ev[0].record(stream)
+        x, y = a, b
+        for t, k in enumerate(sched):
+            sad.topk_propagate_rec(rec, n, x, y, W, H, k, 1000 + t, synth.SEED_INJECT, M)
+            x, y = y, x
+            ev[t + 1].record(stream)
+        sad.render_bwd_rec(rec, n, x, tgt, W, H, grad, loss, rgb)
+        ev[-1].record(stream)
+        torch.cuda.synchronize()
+        passes = [ev[t].elapsed_time(ev[t + 1]) for t in range(len(sched))]
+        runs.append((sum(passes), ev[len(sched)].elapsed_time(ev[-1]), passes))
+    runs.sort(key=lambda r: r[0] + r[1])
+    refresh_ms, fb_ms, passes = runs[len(runs) // 2]
+    final = x
+    # recall at 4096 seeded pixels against the exact top-8 of the edited sites
+    rng = np.random.default_rng(4096)
+    pix = np.sort(rng.choice(P, 4096, replace=False)).astype(np.int32)
+    pix_d = torch.from_numpy(pix).to(dev)
+    ex = torch.empty((len(pix), 8), dtype=torch.int32, device=dev)
+    sad.topk_exact_at(rec, n, pix_d, W, H, ex)
+    got = final.view(-1, 8)[pix_d.long()]
+    ga, _ = torch.sort(got, dim=1)
+    ea, _ = torch.sort(ex, dim=1)
+    exact = (ga == ea).all(dim=1).float().mean().item()
+    hits = (got[:, :, None] == ex[:, None, :]) & (ex[:, None, :] != -1)
+    per_entry = (hits.any(dim=2).sum().item()) / max(int((ex != -1).sum().item()), 1)
+    refresh_bytes = len(sched) * (64 * P + 24 * n)
+    fb_bytes = 88 * P + 124 * n
+    total_ms = refresh_ms + fb_ms
+    out = {
+        "workload": "edit4096", "W": W, "H": H, "n_sites": n, "n_inject": M, "moved": "10% by U[-256,256] px",
+        "jumps": sched, "reps": reps,
+        "refresh_ms": round(refresh_ms, 3), "fwd_bwd_ms": round(fb_ms, 3), "total_ms": round(total_ms, 3),
+        "refresh_pass_us": [round(p * 1e3, 1) for p in passes],
+        "algorithmic_bytes": refresh_bytes + fb_bytes,
+        "GBps": round((refresh_bytes + fb_bytes) / (total_ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round((refresh_bytes + fb_bytes) / (total_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "refresh_hbm_frac": round(refresh_bytes / (refresh_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "recall_exact_sets": round(exact, 4), "recall_per_entry": round(per_entry, 4),
+        "recall_sample": "4096 seeded pixels, exact top-8 by brute force over all sites on the GPU",
+    }
+    del a, b, backup, tgt, rgb, grad, rec, S_d, x, y, final
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="kodak768")
+    ap.add_argument("--steps", type=int, default=400, help="timed steady-state iterations")
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed iterations before them, the cold-start warm-up passes included")
+    ap.add_argument("--workload", default="img2048")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--kernel-reps", type=int, default=50)
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of graph replays (for counter collection)")
+    ap.add_argument("--no-edit", action="store_true", help="skip the 4096x4096 edit-stress refresh")
+    ap.add_argument("--edit-reps", type=int, default=3)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -203,8 +314,10 @@ def main():
     S0_d = torch.from_numpy(S0).to(dev)
     fit = sad.Fitter(S0_d.clone(), N, tgt, W, H, n_inject=wl.n_inject, seed=synth.SEED_INJECT)
     stream = torch.cuda.current_stream()
+    n_cold = (max(W, H) - 1).bit_length()  # warm-up passes: jumps B/2 .. 1
+    warmup = max(args.warmup, n_cold)
 
-    def reset():
+    def reset_gpu():
         fit.sites.copy_(S0_d)
         fit.refresh_records()
         fit.m.zero_()
@@ -212,48 +325,53 @@ def main():
         fit.grad.zero_()
         fit.maps[0].fill_(-1)
         fit.maps[1].fill_(-1)
+        fit.loss.zero_()
+
+    def reset_host():
         fit.cur = 0
         fit.it = 0
         fit.passes = 0
         fit.warm_end = 0
-        fit.loss.zero_()
 
-    # warm-up (untimed): the first iterations of the fit
-    for _ in range(args.warmup):
+    def steps(k):
+        return lambda: [fit.step() for _ in range(k)]
+
+    # load every kernel once (eager), then back to the initial state
+    for _ in range(2):
         fit.step()
     torch.cuda.synchronize()
+    reset_gpu()
+    reset_host()
+    torch.cuda.synchronize()
 
-    # timed region: K iterations from the cold start
-    reset()
-    torch.cuda.synchronize()
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(args.steps):
-                fit.step()
-        reset()
-        torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    if graph is not None:
-        graph.replay()
+    phases = (("cold", n_cold), ("warm", warmup - n_cold), ("timed", args.steps))
+    if args.no_graph:
+        run = {name: steps(k) for name, k in phases}
     else:
-        for _ in range(args.steps):
-            fit.step()
-    t1.record(stream)
-    torch.cuda.synchronize()
+        # capture the three phases in order (the launches of an iteration depend
+        # only on its index), then replay them from the initial state
+        run = {}
+        for name, k in phases:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(k):
+                    fit.step()
+            run[name] = g.replay
+        end_state = (fit.cur, fit.it, fit.passes, fit.warm_end)
+        reset_gpu()
+        torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    cold_ms = timed(run["cold"], stream)
+    warm_ms = timed(run["warm"], stream)
+    ms = timed(run["timed"], stream)
     wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1)
+    if not args.no_graph:
+        fit.cur, fit.it, fit.passes, fit.warm_end = end_state
     ms_per_step = ms / args.steps
     value = P * args.steps / (ms * 1e-3) / 1e6
+    fit_ms = cold_ms + warm_ms + ms
 
     # quality after the fit: loss of one more iteration
-    fit.it = args.steps
-    fit.passes = args.steps
     fit.loss.zero_()
     fit.step()
     torch.cuda.synchronize()
@@ -262,42 +380,36 @@ def main():
     # recall of the maintained map against the exact top-K (brute force on the GPU)
     ex = sad.new_map(W, H, dev)
     sad.topk_exact(fit.rec, N, ex, W, H)
-    cur = fit.cand
-    a, _ = torch.sort(cur.view(-1, 8), dim=1)
+    a, _ = torch.sort(fit.cand.view(-1, 8), dim=1)
     b, _ = torch.sort(ex.view(-1, 8), dim=1)
     exact_frac = (a == b).all(dim=1).float().mean().item()
+    del ex, a, b
 
     # per-kernel average launch duration: R back-to-back launches of each kernel
     # on the fitted state, one graph replay bracketed by events on this stream
     kb = algorithmic_bytes(P, N)
+    kops = algorithmic_ops(P, N, wl.n_inject)
     kdur = {}
     R = args.kernel_reps
     launches = {
-        "propagate": lambda i: sad.topk_propagate(fit.rec, N, fit.maps[i % 2], fit.maps[1 - i % 2], W, H, 1,
-                                                  1000 + i, synth.SEED_INJECT, wl.n_inject),
-        "fwd_bwd": lambda i: sad.render_bwd(fit.rec, N, fit.cand, fit.target, W, H, fit.grad, fit.loss, fit.rgb),
-        "adam": lambda i: sad.adam_step(fit.sites, fit.m, fit.v, fit.grad, N, 500 + i, P, W, H, fit.adam, fit.rec),
-        "fwd": lambda i: sad.render_fwd(fit.rec, N, fit.cand, W, H, fit.rgb),
+        "propagate": lambda i: sad.topk_propagate_rec(fit.rec, N, fit.maps[i % 2], fit.maps[1 - i % 2], W, H, 1,
+                                                  100000 + i, synth.SEED_INJECT, wl.n_inject),
+        "fwd_bwd": lambda i: sad.render_bwd_rec(fit.rec, N, fit.cand, fit.target, W, H, fit.grad, fit.loss, fit.rgb),
+        "adam": lambda i: sad.adam_step_rec(fit.sites, fit.m, fit.v, fit.grad, N, 50000 + i, P, W, H, fit.adam,
+                                        fit.rec),
+        "fwd": lambda i: sad.render_fwd_rec(fit.rec, N, fit.cand, W, H, fit.rgb),
     }
     for name, fn in launches.items():
-        g = None
-        if not args.no_graph:
+        if args.no_graph:
+            go = (lambda f: lambda: [f(i) for i in range(R)])(fn)
+        else:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for i in range(R):
                     fn(i)
+            go = g.replay
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        if g is not None:
-            g.replay()
-        else:
-            for i in range(R):
-                fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        kdur[name] = e0.elapsed_time(e1) / R * 1e-3  # s per launch
+        kdur[name] = timed(go, stream) / R * 1e-3  # s per launch
     if args.copy_calibration_mib > 0:
         # a plain elementwise copy kernel: reads and writes exactly `nbytes`
         nbytes = args.copy_calibration_mib << 20
@@ -307,34 +419,27 @@ def main():
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    step_kernels = ("propagate", "fwd_bwd", "adam")
-    dominant = max(step_kernels, key=kdur.get)
-    kops = algorithmic_ops(P, N, wl.n_inject)
-    kernels = {k: {"us": round(kdur[k] * 1e6, 3), "GBps": round(kb[k] / kdur[k] / 1e9, 1),
+    dominant = max(STEP_KERNELS, key=kdur.get)
+    kernels = {k: {"us": round(kdur[k] * 1e6, 3), "algorithmic_bytes": kb[k],
+                   "GBps": round(kb[k] / kdur[k] / 1e9, 1),
                    "hbm_frac": round(kb[k] / kdur[k] / 1e9 / HBM_PEAK_GBS, 4),
                    "Tops": round(kops[k] / kdur[k] / 1e12, 2),
                    "alu_frac": round(kops[k] / kdur[k] / 1e12 / VALU_PEAK_TOPS, 4),
-                   "valu_issue_frac": measured_valu_issue(wl.name, k)} for k in kdur}
-    # the bound of a kernel: the roof its algorithmic work reaches first
-    alu_bound = kernels[dominant]["alu_frac"] >= kernels[dominant]["hbm_frac"]
-    if alu_bound:
-        roofline = {"bound": "alu", "kernel": dominant, "achieved": kernels[dominant]["Tops"],
-                    "peak": round(VALU_PEAK_TOPS, 2), "unit": "T VALU lane-ops/s",
-                    "frac": kernels[dominant]["alu_frac"], "algorithmic_ops_per_launch": kops[dominant]}
-    else:
-        roofline = {"bound": "hbm", "kernel": dominant, "achieved": kernels[dominant]["GBps"],
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dominant]["hbm_frac"]}
-    roofline.update({"traffic": measured_traffic(wl.name, dominant), "algorithmic_bytes_per_launch": kb[dominant],
-                     "hbm_frac": kernels[dominant]["hbm_frac"],
-                     "valu_issue_frac": measured_valu_issue(wl.name, dominant)})
-
+                   "valu_issue_frac": measured_valu_issue(wl.name, k),
+                   "traffic": measured_traffic(wl.name, k)} for k in kdur}
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": kernels[dominant]["GBps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": kernels[dominant]["hbm_frac"], "traffic": kernels[dominant]["traffic"],
+                "algorithmic_bytes_per_launch": kb[dominant], "us_per_launch": kernels[dominant]["us"],
+                "alu_frac": kernels[dominant]["alu_frac"],
+                "valu_issue_frac": kernels[dominant]["valu_issue_frac"]}
+    B = step_bytes(P, N)
     out = {
         "metric": "Mpixel-iters/s (propagate+fwd+bwd+Adam, K=8) and % of HBM peak",
         "value": round(value, 2),
         "unit": "Mpixel-iters/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -343,23 +448,34 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name, "W": W, "H": H, "n_sites": N, "K": 8, "n_inject": wl.n_inject,
-            "schedule": "cold start, jumps B/2..1 then 1", "graph": graph is not None,
-            "hbm_frac_whole_step": round(sum(kb[k] for k in step_kernels) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                         4),
+            "schedule": f"{n_cold} warm-up passes (jumps B/2..1, one per iteration), then jump 1 every iteration",
+            "timed": f"iterations {warmup}..{warmup + args.steps - 1} of the fit (steady state)",
+            "graph": not args.no_graph,
+            "step_algorithmic_bytes": B,
+            "hbm_frac_whole_step": round(B / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "cold_start_ms": round(cold_ms, 3), "cold_start_iterations": n_cold,
+            "fit_ms": round(fit_ms, 3), "fit_iterations": warmup + args.steps,
+            "fit_mpixel_iters_per_s": round(P * (warmup + args.steps) / (fit_ms * 1e-3) / 1e6, 2),
             "psnr_db_after": round(float(psnr), 3), "exact_top8_fraction_after": round(exact_frac, 4),
+            "wall_s": round(wall, 3),
             "kernels": kernels,
         },
         "roofline": roofline,
     }
-
+    del fit, run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_edit:
+        out["edit4096"] = edit_refresh(dev, args.edit_reps, stream)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, S0, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, S0, tgt.cpu().numpy(), args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, S0, budget_s):
+def cpu_baseline(wl, S0, target, budget_s):
     """The oracle's own iteration (propagate, forward, backward, Adam) on the same
-    sites, timed on the host cores, for as many iterations as fit the budget."""
+    sites and target, timed on the host cores, for as many iterations of the fit's
+    schedule as fit the budget."""
     import oracle
     import synth
 
@@ -370,7 +486,7 @@ def cpu_baseline(wl, S0, budget_s):
     cores = oracle.get_threads()
     W, H, N, P = wl.W, wl.H, wl.n_sites, wl.P
     S = S0.copy()
-    tgt = (synth.pixel_noise(W, H, 99, 0.25) + 0.5).astype(np.float32)
+    tgt = np.ascontiguousarray(target, dtype=np.float32)
     cand = synth.empty_map(W, H)
     params = S.astype(np.float64)
     m = np.zeros((10, S.shape[1]))
@@ -379,19 +495,26 @@ def cpu_baseline(wl, S0, budget_s):
     lr = np.array([0.1, 0.1, 0.02, 0.05, 0.01, 0.01, 0.01, 0.02, 0.02, 0.02])
     sched = oracle.jump_schedule(W, H, 10_000)
     it, t_used = 0, 0.0
+    phase = {"propagate": 0.0, "fwd": 0.0, "bwd": 0.0, "adam": 0.0}
     while t_used < budget_s and it < 10_000:
         t0 = time.perf_counter()
         S32 = params.astype(np.float32)
         cand = oracle.propagate(S32, N, cand, W, H, sched[it], it, synth.SEED_INJECT, wl.n_inject)
+        t1 = time.perf_counter()
         oracle.render_fwd(params, N, cand, W, H)
+        t2 = time.perf_counter()
         oracle.render_bwd(params, N, cand, tgt, W, H, grad=grad)
+        t3 = time.perf_counter()
         oracle.adam_step(params, m, v, grad, N, it + 1, P, lr, 0.9, 0.999, 1e-8, W, H)
-        t_used += time.perf_counter() - t0
+        t4 = time.perf_counter()
+        for k, dt in zip(phase, (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
+            phase[k] += dt
+        t_used += t4 - t0
         it += 1
     return {"value": round(P * it / t_used / 1e6, 4), "unit": "Mpixel-iters/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {it} iterations of the {wl.name} fit ({W}x{H}, N={N}), same sites; target replaced "
-                      f"by seeded noise (the oracle's cost does not depend on target values); {t_used:.1f} s",
-            "cpu": cpu_model()}
+            "sample": f"the first {it} iterations of the {wl.name} fit ({W}x{H}, N={N}, same sites and target, "
+                      f"cold start included), {t_used:.1f} s",
+            "phase_s": {k: round(v_, 2) for k, v_ in phase.items()}, "cpu": cpu_model()}
 
 
 if __name__ == "__main__":

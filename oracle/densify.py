@@ -1,13 +1,15 @@
 """Oracle of the host-side budget control (densify / prune).
 
 TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).  Written from the pages:
-paperlayer.ai summary, Appendix B.5 (score energy / mass^alpha; split into two
-children offset along a covariance- or Sobel-gradient axis; children take the
-target colour, reduced log tau and r, fresh Adam state; prune the sites with the
-smallest removal score by setting their position to (-1, -1)), the reading
-note's key design 4 and the press article's section 4.  The pages give no
-constants; the rules and defaults below are our reading, each stated at the
-point where it is applied.
+paperlayer.ai summary, Appendix B.5 (a site's error energy over a power of its
+mass ranks it for splitting; a split places two children on either side of the
+parent along an axis from the error-weighted covariance, or from the luminance
+gradient when that is unusable; the children read their colour from the target,
+shrink r and log tau and start with zero Adam moments; the sites whose removal
+costs least are dropped by moving them to (-1, -1)), the reading note's key
+design 4 and the press article's section 4.  The pages give no constants; the
+rules and defaults below are our reading, each stated at the point where it is
+applied.
 
 PARITY UNPINNED against the pages: there is no second source for these rules;
 the tests pin only invariants (counts, symmetry of the children about the
@@ -115,11 +117,14 @@ def densify_prune(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, ta
             sites[R, slot] = np.float32(parent[R]) * np.float32(shrink)
             sites[LOGTAU, slot] = np.float32(parent[LOGTAU]) + np.float32(math.log(np.float32(shrink)))
             sites[CR:CB + 1, slot] = target[_pix(y, H), _pix(x, W)]
-        # child B enters the list of its pixel's map entry and of the 4 neighbour entries
+        # child B enters the list of its pixel's map entry and of the 4 neighbour
+        # entries, in the last place -- except a list that already names b (a slot
+        # freed by this call's pruning keeps its ID in lists near its old place):
+        # a candidate list names distinct sites
         bc, br = _pix(float(sites[X, b]), W) // cell, _pix(float(sites[Y, b]), H) // cell
         for dc, dr in ((0, 0), (-1, 0), (1, 0), (0, -1), (0, 1)):
             c, r = bc + dc, br + dr
-            if 0 <= c < Wm and 0 <= r < Hm:
+            if 0 <= c < Wm and 0 <= r < Hm and not np.any(cand[r, c] == b):
                 cand[r, c, 7] = b
         done += 1
     return count, done, pruned, short

@@ -692,8 +692,9 @@ void orc_adam_step(double *params, double *m, double *v, double *grad, int n_slo
 }
 
 /* --------------------------------------------------- budget statistics -----
- * [SUM] B.5: the densification score combines per-site mass, energy and
- * weighted second moments.  Per site i, over the pixels x whose list holds it
+ * [SUM] B.5: a site's claim to be split is judged from how much image it
+ * covers, how much error it leaves and how that error is spread (its
+ * error-weighted second moments).  Per site i, over the pixels x whose list holds it
  * (w = its softmax weight at x, e = ||c(x) - t(x)||^2, delta = x - p_i):
  *   [0] sum w  [1] sum w e  [2] sum w e dx  [3] sum w e dy
  *   [4] sum w e dx^2  [5] sum w e dx dy  [6] sum w e dy^2  [7] unused

@@ -8,9 +8,12 @@ fallback: if the library is not built, or a tensor is not on a GPU, the call
 raises.
 
 Layouts (see include/sad.h): sites float32 [10][stride], candidate map uint32
-[H][W][8] (torch int32 storage reinterpreted), images float32 [H][W][3], grad
-float32 [stride][16] (one 64-byte record per site: 10 gradients, the removal
-delta, 5 unused words), Adam moments float32 [10][stride].
+[H][W][8] (torch int32 storage reinterpreted), images float32 [H][W][3], Adam
+moments float32 [10][stride].  Gradients: float32 [11][stride] planes for the
+site-buffer calls (topk_propagate, render_fwd, render_bwd, adam_step,
+densify_prune), float32 [stride][16] records (10 gradients, the removal delta,
+5 unused words) for the cached calls (the *_rec names), which read the derived
+site records or packed words instead of the planes.
 """
 from __future__ import annotations
 
@@ -78,7 +81,7 @@ class BudgetCfg(ctypes.Structure):
 
 class AdamCfg(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float * NPARAM), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
-                ("eps", ctypes.c_float)]
+                ("eps", ctypes.c_float), ("x_max", ctypes.c_float), ("y_max", ctypes.c_float)]
 
 
 _lib = None
@@ -100,6 +103,9 @@ def lib() -> ctypes.CDLL:
         L.sad_site_records.restype = i32
         L.sad_site_records.argtypes = [fp, i32, i32, fp, vp]
         L.sad_topk_propagate.restype = i32
+        L.sad_topk_propagate.argtypes = [fp, i32, i32, vp, vp, i32, i32, i32, u32, u32, i32, vp]
+        L.sad_topk_propagate_rec.restype = i32
+        L.sad_topk_propagate_rec.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, i32, u32, u32, i32, vp]
         L.sad_eval_encode.restype = i32
         L.sad_eval_encode.argtypes = [fp, i32, i32, i32, i32, vp, fp, vp]
         L.sad_eval_decode.restype = i32
@@ -108,13 +114,20 @@ def lib() -> ctypes.CDLL:
         L.sad_eval_query.argtypes = [vp, fp, i32, vp, i32, i32, i32, fp, ctypes.c_int64, fp, vp]
         L.sad_pack_sites.restype = i32
         L.sad_pack_sites.argtypes = [fp, i32, i32, vp, vp]
-        L.sad_topk_propagate.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, i32, u32, u32, i32, vp]
         L.sad_topk_exact.restype = i32
         L.sad_topk_exact.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp]
+        L.sad_topk_exact_at.restype = i32
+        L.sad_topk_exact_at.argtypes = [vp, i32, i32, vp, i32, i32, i32, i32, vp, vp]
         L.sad_render_fwd.restype = i32
-        L.sad_render_fwd.argtypes = [fp, i32, vp, i32, i32, i32, fp, vp]
+        L.sad_render_fwd.argtypes = [fp, i32, i32, vp, i32, i32, fp, vp]
+        L.sad_render_fwd_rec.restype = i32
+        L.sad_render_fwd_rec.argtypes = [fp, i32, vp, i32, i32, i32, fp, vp]
         L.sad_render_bwd.restype = i32
-        L.sad_render_bwd.argtypes = [fp, i32, vp, fp, i32, i32, i32, fp, fp, fp, vp]
+        L.sad_render_bwd.argtypes = [fp, i32, i32, vp, fp, i32, i32, fp, fp, vp]
+        L.sad_render_bwd_rec.restype = i32
+        L.sad_render_bwd_rec.argtypes = [fp, i32, vp, fp, i32, i32, i32, fp, fp, fp, vp]
+        L.sad_apply_seeds.restype = i32
+        L.sad_apply_seeds.argtypes = [vp, i32, i32, i32, vp, ctypes.c_long, vp]
         L.sad_jfa_seed.restype = i32
         L.sad_jfa_seed.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp]
         L.sad_jfa_pass.restype = i32
@@ -122,20 +135,31 @@ def lib() -> ctypes.CDLL:
         L.sad_densify_stats.restype = i32
         L.sad_densify_stats.argtypes = [fp, i32, vp, fp, i32, i32, i32, fp, vp]
         ip = ctypes.POINTER(ctypes.c_int)
+        L.sad_densify_prune_stats.restype = i32
+        L.sad_densify_prune_stats.argtypes = [fp, fp, fp, i32, i32, ip, fp, fp, vp, i32, i32, i32, fp,
+                                              ctypes.POINTER(BudgetCfg), ip, ip, vp, ctypes.c_long,
+                                              ctypes.POINTER(ctypes.c_long)]
         L.sad_densify_prune.restype = i32
-        L.sad_densify_prune.argtypes = [fp, fp, fp, i32, i32, ip, fp, fp, vp, i32, i32, i32, fp,
-                                        ctypes.POINTER(BudgetCfg), ip, ip, vp, ctypes.c_long,
-                                        ctypes.POINTER(ctypes.c_long)]
+        L.sad_densify_prune.argtypes = [fp, fp, fp, fp, ip, i32, i32, vp, i32, i32, fp, ctypes.POINTER(BudgetCfg),
+                                        ctypes.c_uint64]
         L.sad_adam_step.restype = i32
-        L.sad_adam_step.argtypes = [fp, fp, fp, fp, fp, vp, i32, i32, i32, i32, i32, i32, ctypes.POINTER(AdamCfg),
-                                    vp]
+        L.sad_adam_step.argtypes = [fp, fp, fp, fp, i32, i32, i32, i32, ctypes.POINTER(AdamCfg), vp]
+        L.sad_adam_step_rec.restype = i32
+        L.sad_adam_step_rec.argtypes = [fp, fp, fp, fp, fp, vp, i32, i32, i32, i32, ctypes.POINTER(AdamCfg), vp]
         _lib = L
     return _lib
 
 
-EXPORTED = ("sad_abi_version", "sad_status_string", "sad_site_records", "sad_topk_propagate", "sad_topk_exact",
-            "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_densify_stats", "sad_densify_prune", "sad_jfa_seed",
-            "sad_jfa_pass", "sad_pack_sites", "sad_eval_encode", "sad_eval_decode", "sad_eval_query")
+EXPORTED = ("sad_abi_version", "sad_status_string",
+            # the iteration on the site buffer
+            "sad_topk_propagate", "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_densify_prune",
+            # the iteration on derived caches
+            "sad_site_records", "sad_pack_sites", "sad_topk_propagate_rec", "sad_render_fwd_rec",
+            "sad_render_bwd_rec", "sad_adam_step_rec", "sad_densify_stats", "sad_densify_prune_stats",
+            "sad_apply_seeds",
+            # candidate-map tools, evaluation format
+            "sad_jfa_seed", "sad_jfa_pass", "sad_topk_exact", "sad_topk_exact_at", "sad_eval_encode",
+            "sad_eval_decode", "sad_eval_query")
 
 
 # --------------------------------------------------------------- marshalling
@@ -230,15 +254,26 @@ def map_shape(W: int, H: int, cell: int = 1) -> tuple:
     return (-(-H // cell), -(-W // cell), K)
 
 
-def topk_propagate(rec, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed, n_inject, stream=None, cell=1):
-    """One propagation pass: cand_in -> cand_out (see sad_topk_propagate).  `rec`
-    is the record buffer or the packed candidate-site buffer."""
+def topk_propagate(sites, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed, n_inject, stream=None):
+    """One propagation pass of the per-pixel map, reading the site planes:
+    cand_in -> cand_out (see sad_topk_propagate)."""
+    sp, stride = _sites(sites, n_slots)
+    a = _dev(cand_in, "cand_in", _U32, map_shape(W, H))
+    b = _dev(cand_out, "cand_out", _U32, map_shape(W, H))
+    _check("sad_topk_propagate", lib().sad_topk_propagate(sp, n_slots, stride, a, b, W, H, jump,
+                                                          pass_index & 0xFFFFFFFF, seed & 0xFFFFFFFF, n_inject,
+                                                          _stream(stream)))
+
+
+def topk_propagate_rec(rec, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed, n_inject, stream=None, cell=1):
+    """One propagation pass: cand_in -> cand_out (see sad_topk_propagate_rec).
+    `rec` is the record buffer or the packed candidate-site buffer."""
     g, fmt = _sel(rec, n_slots)
     a = _dev(cand_in, "cand_in", _U32, map_shape(W, H, cell))
     b = _dev(cand_out, "cand_out", _U32, map_shape(W, H, cell))
-    _check("sad_topk_propagate", lib().sad_topk_propagate(g, fmt, n_slots, a, b, W, H, cell, jump,
-                                                          pass_index & 0xFFFFFFFF, seed & 0xFFFFFFFF, n_inject,
-                                                          _stream(stream)))
+    _check("sad_topk_propagate_rec", lib().sad_topk_propagate_rec(g, fmt, n_slots, a, b, W, H, cell, jump,
+                                                                  pass_index & 0xFFFFFFFF, seed & 0xFFFFFFFF,
+                                                                  n_inject, _stream(stream)))
 
 
 def jfa_seed(rec, n_slots, cand, W, H, stream=None, cell=1):
@@ -285,12 +320,33 @@ def topk_exact(rec, n_slots, cand_out, W, H, stream=None, cell=1):
     _check("sad_topk_exact", lib().sad_topk_exact(g, fmt, n_slots, b, W, H, cell, _stream(stream)))
 
 
-def render_fwd(rec, n_slots, cand, W, H, out_rgb, stream=None, cell=1):
-    """Temperature-softmax render of each pixel's list (see sad_render_fwd)."""
+def topk_exact_at(rec, n_slots, entries, W, H, out, stream=None, cell=1):
+    """Exact top-K lists of the map entries `entries` (int32 [n], indices
+    row*Wm + col) into out (int32 [n][8]) (see sad_topk_exact_at)."""
+    g, fmt = _sel(rec, n_slots)
+    if entries.dim() != 1:
+        raise ValueError("entries must be int32 [n]")
+    n = entries.shape[0]
+    e = _dev(entries, "entries", _U32)
+    o = _dev(out, "out", _U32, (n, K))
+    _check("sad_topk_exact_at", lib().sad_topk_exact_at(g, fmt, n_slots, e, n, W, H, cell, o, _stream(stream)))
+
+
+def render_fwd(sites, n_slots, cand, W, H, out_rgb, stream=None):
+    """Temperature-softmax render of each pixel's list from the site planes (see
+    sad_render_fwd)."""
+    sp, stride = _sites(sites, n_slots)
+    c = _dev(cand, "cand", _U32, map_shape(W, H))
+    o = _dev(out_rgb, "out_rgb", _F32, (H, W, 3))
+    _check("sad_render_fwd", lib().sad_render_fwd(sp, n_slots, stride, c, W, H, o, _stream(stream)))
+
+
+def render_fwd_rec(rec, n_slots, cand, W, H, out_rgb, stream=None, cell=1):
+    """Temperature-softmax render of each pixel's list (see sad_render_fwd_rec)."""
     r = _rec(rec, n_slots)
     c = _dev(cand, "cand", _U32, map_shape(W, H, cell))
     o = _dev(out_rgb, "out_rgb", _F32, (H, W, 3))
-    _check("sad_render_fwd", lib().sad_render_fwd(r, n_slots, c, W, H, cell, o, _stream(stream)))
+    _check("sad_render_fwd_rec", lib().sad_render_fwd_rec(r, n_slots, c, W, H, cell, o, _stream(stream)))
 
 
 def new_loss(device) -> torch.Tensor:
@@ -299,9 +355,23 @@ def new_loss(device) -> torch.Tensor:
     return torch.zeros(LOSS_SLOTS, dtype=torch.float32, device=device)
 
 
-def render_bwd(rec, n_slots, cand, target, W, H, grad, loss_sum=None, out_rgb=None, stream=None, cell=1):
-    """Gradients of the squared error, accumulated into grad; optionally also the
-    rendered image (see sad_render_bwd)."""
+def render_bwd(sites, n_slots, cand, target, W, H, grad, loss_sum=None, stream=None):
+    """Gradients of the squared error from the site planes, accumulated into the
+    gradient planes grad float32 [11][stride]; loss_sum, a one-element float32
+    tensor, receives the summed squared error (see sad_render_bwd)."""
+    sp, stride = _sites(sites, n_slots)
+    c = _dev(cand, "cand", _U32, map_shape(W, H))
+    t = _dev(target, "target", _F32, (H, W, 3))
+    g = _dev(grad, "grad", _F32, (NACC, stride))
+    if loss_sum is not None and loss_sum.numel() != 1:
+        raise ValueError("loss_sum must hold one float32")
+    ls = _dev(loss_sum, "loss_sum", _F32) if loss_sum is not None else None
+    _check("sad_render_bwd", lib().sad_render_bwd(sp, n_slots, stride, c, t, W, H, g, ls, _stream(stream)))
+
+
+def render_bwd_rec(rec, n_slots, cand, target, W, H, grad, loss_sum=None, out_rgb=None, stream=None, cell=1):
+    """Gradients of the squared error, accumulated into the gradient records;
+    optionally also the rendered image (see sad_render_bwd_rec)."""
     r = _rec(rec, n_slots)
     c = _dev(cand, "cand", _U32, map_shape(W, H, cell))
     t = _dev(target, "target", _F32, (H, W, 3))
@@ -312,7 +382,8 @@ def render_bwd(rec, n_slots, cand, target, W, H, grad, loss_sum=None, out_rgb=No
         raise ValueError(f"loss_sum must hold {LOSS_SLOTS} partial sums (see new_loss)")
     ls = _dev(loss_sum, "loss_sum", _F32) if loss_sum is not None else None
     o = _dev(out_rgb, "out_rgb", _F32, (H, W, 3)) if out_rgb is not None else None
-    _check("sad_render_bwd", lib().sad_render_bwd(r, n_slots, c, t, W, H, cell, g, ls, o, _stream(stream)))
+    _check("sad_render_bwd_rec", lib().sad_render_bwd_rec(r, n_slots, c, t, W, H, cell, g, ls, o,
+                                                          _stream(stream)))
 
 
 @dataclasses.dataclass
@@ -324,16 +395,39 @@ class AdamConfig:
     beta2: float = 0.999
     eps: float = 1e-8
 
-    def to_c(self) -> AdamCfg:
+    def to_c(self, W: int, H: int) -> AdamCfg:
+        """The C struct, with positions clamped to the W x H image."""
         c = AdamCfg()
         for j in range(NPARAM):
             c.lr[j] = float(self.lr[j])
         c.beta1, c.beta2, c.eps = self.beta1, self.beta2, self.eps
+        c.x_max, c.y_max = float(W), float(H)
         return c
 
 
+def _adam_cfg(cfg, W, H) -> AdamCfg:
+    if isinstance(cfg, AdamCfg):
+        return cfg
+    return (cfg if cfg is not None else AdamConfig()).to_c(W, H)
+
+
 def adam_step(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamConfig | AdamCfg | None = None,
-              rec=None, stream=None, packed=None):
+              stream=None):
+    """Adam on the site planes with gradient planes float32 [11][stride] (see
+    sad_adam_step); positions are clamped to the W x H image."""
+    sp, stride = _sites(sites, n_slots)
+    mp = _dev(m, "m", _F32, (NPARAM, stride))
+    vp = _dev(v, "v", _F32, (NPARAM, stride))
+    g = _dev(grad, "grad", _F32, (NACC, stride))
+    c = _adam_cfg(cfg, W, H)
+    _check("sad_adam_step", lib().sad_adam_step(sp, mp, vp, g, n_slots, stride, step, n_pixels, ctypes.byref(c),
+                                                _stream(stream)))
+
+
+def adam_step_rec(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamConfig | AdamCfg | None = None,
+                  rec=None, stream=None, packed=None):
+    """Adam on gradient records float32 [stride][16], refreshing the records and
+    packed words if given (see sad_adam_step_rec)."""
     sp, stride = _sites(sites, n_slots)
     mp = _dev(m, "m", _F32, (NPARAM, stride))
     vp = _dev(v, "v", _F32, (NPARAM, stride))
@@ -344,9 +438,9 @@ def adam_step(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamConfig 
         if packed.dim() != 2 or packed.shape[1] != PACK_LD or packed.shape[0] < n_slots:
             raise ValueError("packed must be int32 [>= n_slots][4]")
         pk = _dev(packed, "packed", _U32)
-    c = cfg.to_c() if isinstance(cfg, AdamConfig) else (cfg if cfg is not None else AdamConfig().to_c())
-    _check("sad_adam_step", lib().sad_adam_step(sp, mp, vp, g, gp, pk, n_slots, stride, step, n_pixels, W, H,
-                                                ctypes.byref(c), _stream(stream)))
+    c = _adam_cfg(cfg, W, H)
+    _check("sad_adam_step_rec", lib().sad_adam_step_rec(sp, mp, vp, g, gp, pk, n_slots, stride, step, n_pixels,
+                                                        ctypes.byref(c), _stream(stream)))
 
 
 def densify_stats(rec, n_slots, cand, target, W, H, stats, stream=None, cell=1):
@@ -374,15 +468,43 @@ class BudgetConfig:
         return BudgetCfg(self.split_frac, self.prune_frac, self.alpha, self.min_mass, self.shrink)
 
 
-def densify_prune(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, target,
-                  cfg: BudgetConfig | None = None, cell=1, want_seeds=False):
-    """Host-side split/prune on numpy arrays, in place (see sad_densify_prune).
+def densify_prune(sites, m, v, removal, n_slots, capacity, cand, W, H, target, cfg: BudgetConfig | None = None,
+                  seed: int = 0):
+    """Host-side budget control from the site buffer, on numpy arrays, in place
+    (see sad_densify_prune): statistics over the per-pixel map, split, prune, seed
+    the map, reset the removal accumulator.  sites, m, v float32 [10][stride];
+    removal float32 [stride]; cand uint32 [H][W][8]; target float32 [H][W][3].
+    Returns (new n_slots, status), status 0 or SAD_ERR_CAPACITY."""
+    import numpy as np
+    for name, a, dt in (("sites", sites, np.float32), ("m", m, np.float32), ("v", v, np.float32),
+                        ("removal", removal, np.float32), ("cand", cand, np.uint32),
+                        ("target", target, np.float32)):
+        if not isinstance(a, np.ndarray) or a.dtype != dt or not a.flags["C_CONTIGUOUS"]:
+            raise TypeError(f"{name} must be a C-contiguous numpy {np.dtype(dt).name} array")
+    stride = sites.shape[1]
+    if sites.shape[0] != NPARAM or m.shape != sites.shape or v.shape != sites.shape or \
+            removal.shape != (stride,) or target.shape != (H, W, 3) or cand.shape != map_shape(W, H):
+        raise ValueError("densify_prune: inconsistent shapes")
+    ns = ctypes.c_int(n_slots)
+    c = (cfg or BudgetConfig()).to_c()
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rc = lib().sad_densify_prune(p(sites), p(m), p(v), p(removal), ctypes.byref(ns), capacity, stride, p(cand), W,
+                                 H, p(target), ctypes.byref(c), ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF))
+    if rc not in (SAD_OK, SAD_ERR_CAPACITY):
+        raise SadError("sad_densify_prune", rc)
+    return ns.value, rc
+
+
+def densify_prune_stats(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, target,
+                        cfg: BudgetConfig | None = None, cell=1, want_seeds=False):
+    """Host-side split/prune on numpy arrays with given statistics, in place (see
+    sad_densify_prune_stats).
 
     sites, m, v: float32 [10][stride]; stats float32 [stride][8]; removal float32
     [stride]; cand uint32 [Hm][Wm][8] (map_shape) or None; target float32 [H][W][3].
     Returns (new n_slots, n_split, n_pruned, status) -- status is 0 or
-    SAD_ERR_CAPACITY -- and, with want_seeds, the seeded (entry, ID) pairs as a
-    uint32 [n][2] array in write order."""
+    SAD_ERR_CAPACITY -- and, with want_seeds, the seeding (entry, ID) pairs as a
+    uint32 [n][2] array, grouped by entry and in write order within an entry."""
     import numpy as np
     arrays = [("sites", sites, np.float32), ("m", m, np.float32), ("v", v, np.float32),
               ("stats", stats, np.float32), ("removal", removal, np.float32), ("target", target, np.float32)]
@@ -403,12 +525,12 @@ def densify_prune(sites, m, v, n_slots, capacity, stats, removal, cand, W, H, ta
     p = lambda a: a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
     seeds = np.empty((5 * stride + 1, 2), dtype=np.uint32) if want_seeds else None
     nseed = ctypes.c_long(0)
-    rc = lib().sad_densify_prune(p(sites), p(m), p(v), stride, capacity, ctypes.byref(ns), p(stats), p(removal),
-                                 p(cand), W, H, cell, p(target), ctypes.byref(c), ctypes.byref(nsp),
-                                 ctypes.byref(npr), p(seeds), seeds.shape[0] if want_seeds else 0,
-                                 ctypes.byref(nseed))
+    rc = lib().sad_densify_prune_stats(p(sites), p(m), p(v), stride, capacity, ctypes.byref(ns), p(stats),
+                                       p(removal), p(cand), W, H, cell, p(target), ctypes.byref(c),
+                                       ctypes.byref(nsp), ctypes.byref(npr), p(seeds),
+                                       seeds.shape[0] if want_seeds else 0, ctypes.byref(nseed))
     if rc not in (SAD_OK, SAD_ERR_CAPACITY):
-        raise SadError("sad_densify_prune", rc)
+        raise SadError("sad_densify_prune_stats", rc)
     if want_seeds:
         return ns.value, nsp.value, npr.value, rc, seeds[:nseed.value]
     return ns.value, nsp.value, npr.value, rc
@@ -475,8 +597,23 @@ def jump_schedule(W: int, H: int, n: int, cell: int = 1) -> list:
 
 
 def new_grad(stride: int, device="cuda") -> torch.Tensor:
-    """Zeroed gradient accumulators, float32 [stride][16]."""
+    """Zeroed gradient records (cached form), float32 [stride][16]."""
     return torch.zeros((stride, GRAD_LD), dtype=torch.float32, device=device)
+
+
+def new_grad_planes(stride: int, device="cuda") -> torch.Tensor:
+    """Zeroed gradient planes (site-buffer form), float32 [11][stride]."""
+    return torch.zeros((NACC, stride), dtype=torch.float32, device=device)
+
+
+def apply_seeds(cand, W, H, seeds, stream=None, cell=1):
+    """Applies seeding pairs (uint32 [n][2] as int32, grouped by entry) to a map on
+    the GPU (see sad_apply_seeds)."""
+    c = _dev(cand, "cand", _U32, map_shape(W, H, cell))
+    if seeds.dim() != 2 or seeds.shape[1] != 2:
+        raise ValueError("seeds must be int32 [n][2]")
+    sd = _dev(seeds, "seeds", _U32)
+    _check("sad_apply_seeds", lib().sad_apply_seeds(c, W, H, cell, sd, seeds.shape[0], _stream(stream)))
 
 
 def grad_planes(grad: torch.Tensor):
@@ -534,7 +671,7 @@ class Fitter:
         self.cur = 0
         self.rgb = torch.empty((H, W, 3), dtype=torch.float32, device=dev)
         self.loss = new_loss(dev)
-        self.adam = (adam or AdamConfig()).to_c()
+        self.adam = (adam or AdamConfig()).to_c(W, H)
         self.it = 0
         self.sched_cache: dict = {}
 
@@ -559,8 +696,8 @@ class Fitter:
             pack_sites(self.sites, self.n_slots, self.packed, stream)
 
     def propagate(self, jump: int, pass_index: int, stream=None):
-        topk_propagate(self.sel, self.n_slots, self.maps[self.cur], self.maps[1 - self.cur], self.W, self.H,
-                       jump, pass_index, self.seed, self.n_inject, stream, self.cell)
+        topk_propagate_rec(self.sel, self.n_slots, self.maps[self.cur], self.maps[1 - self.cur], self.W, self.H,
+                           jump, pass_index, self.seed, self.n_inject, stream, self.cell)
         self.cur = 1 - self.cur
 
     def step(self, stream=None):
@@ -576,10 +713,10 @@ class Fitter:
             for _ in range(self.passes_per_refresh):
                 self.propagate(self.jump_at(self.passes), self.passes, stream)
                 self.passes += 1
-        render_bwd(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, self.grad, self.loss, self.rgb,
-                   stream, self.cell)
-        adam_step(self.sites, self.m, self.v, self.grad, self.n_slots, it + 1, self.W * self.H, self.W, self.H,
-                  self.adam, self.rec, stream, self.packed)
+        render_bwd_rec(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, self.grad, self.loss,
+                       self.rgb, stream, self.cell)
+        adam_step_rec(self.sites, self.m, self.v, self.grad, self.n_slots, it + 1, self.W * self.H, self.W, self.H,
+                      self.adam, self.rec, stream, self.packed)
         self.it += 1
 
     def densify(self, cfg: BudgetConfig | None = None, stream=None):
@@ -590,9 +727,9 @@ class Fitter:
 
         Only what the host routine reads or changes crosses PCIe, through pinned
         buffers kept between calls: sites, moments, statistics and removal deltas
-        (the target once, and again only if the tensor is modified).  The map stays on the GPU: the routine reports the entries it
-        seeds with the new sites, and they are written there (a later seed of an
-        entry wins, as in the routine's own order)."""
+        (the target once, and again only if the tensor is modified).  The map
+        stays on the GPU: the routine reports the entries it seeds with the new
+        sites, and sad_apply_seeds writes them there (a list keeps distinct IDs)."""
         import numpy as np
         dev = self.sites.device
         stride = self.sites.shape[1]
@@ -614,19 +751,14 @@ class Fitter:
             h[k].copy_(src, non_blocking=True)
         torch.cuda.synchronize(dev)
         hn = {k: t.numpy() for k, t in h.items()}
-        n, n_split, n_pruned, _, seeds = densify_prune(hn["sites"], hn["m"], hn["v"], self.n_slots, stride,
-                                                       hn["stats"], hn["removal"], None, self.W, self.H,
-                                                       hn["target"], cfg, self.cell, want_seeds=True)
+        n, n_split, n_pruned, _, seeds = densify_prune_stats(hn["sites"], hn["m"], hn["v"], self.n_slots, stride,
+                                                             hn["stats"], hn["removal"], None, self.W, self.H,
+                                                             hn["target"], cfg, self.cell, want_seeds=True)
         for k, dst in (("sites", self.sites), ("m", self.m), ("v", self.v)):
             dst.copy_(h[k], non_blocking=True)
         if len(seeds):
-            # the last write of an entry wins: keep each entry's last pair
-            e = seeds[::-1, 0]
-            _, first = np.unique(e, return_index=True)
-            last = len(e) - 1 - first
-            idx = torch.from_numpy(seeds[last, 0].astype(np.int64)).to(dev)
-            ids = torch.from_numpy(seeds[last, 1].view(np.int32)).to(dev)
-            self.cand.view(-1, K)[idx, K - 1] = ids
+            apply_seeds(self.cand, self.W, self.H, torch.from_numpy(seeds.view(np.int32)).to(dev), stream,
+                        self.cell)
         self.grad[:, NACC - 1].zero_()
         self.n_slots = n
         self.refresh_records(stream)

@@ -1,11 +1,14 @@
 // sad_budget.cpp -- host-side budget control (densify / prune) of libsad.
 //
-// Selection and splitting follow the paperlayer.ai summary, Appendix B.5 (score
-// energy / mass^alpha, split along a covariance- or gradient-estimated axis,
-// children take target colours, reduced log tau and r, reset Adam states; prune
-// by the removal delta, pruned sites get position (-1, -1)), the reading note's
-// key design 4 and the press article's section 4.  The per-site statistics come
-// from sad_densify_stats on the GPU; this file only ranks, splits and prunes.
+// The rules follow the paperlayer.ai summary, Appendix B.5: sites are ranked for
+// splitting by their error energy over a power of their mass, a split places two
+// children along an axis taken from the error-weighted covariance (or, without
+// enough mass, from the local luminance gradient), the children copy the parent
+// with their colour read from the target, shrunken r and log tau and fresh Adam
+// moments; pruning drops the sites whose removal would raise the error least and
+// marks them with position (-1, -1).  Also the reading note's key design 4 and
+// the press article's section 4.  The statistics come from sad_densify_stats on
+// the GPU (sad_densify_prune_stats) or from host_stats below (sad_densify_prune).
 // Readings where the pages are silent are stated in include/sad.h.
 
 #include <stdint.h>
@@ -77,12 +80,116 @@ void parallel_for(long n, F f)
         x.join();
 }
 
+// The budget-control statistics of include/sad.h on the host, in float64, over
+// the per-pixel map: per pixel the softmax blend of its list (usable entries: an
+// ID below n of an active site with a finite logit and colour; a duplicate ID
+// counts twice, as in the render), e = ||c - t||^2, then for each usable entry
+// with w > 0 the seven sums.  Rows are split over up to 8 threads with their own
+// accumulators, added in thread order.
+void host_stats(const float *sites, int n, long st, const uint32_t *cand, int W, int H, const float *target,
+                float *stats)
+{
+    const double s = 1.0 / (double)std::max(W, H);
+    const long hw = (long)std::max(1u, std::thread::hardware_concurrency());
+    const int T = (int)std::max(1L, std::min({hw, 8L, (long)H / 16}));
+    std::vector<std::vector<double>> acc(T);
+    auto rows = [&](int t) {
+        std::vector<double> &a = acc[t];
+        a.assign((size_t)n * 7, 0.0);
+        const int r0 = (int)((long)H * t / T), r1 = (int)((long)H * (t + 1) / T);
+        for (int row = r0; row < r1; ++row)
+            for (int col = 0; col < W; ++col) {
+                const long p = (long)row * W + col;
+                const double X = col + 0.5, Y = row + 0.5;
+                double l[SAD_K], cr[SAD_K][3];
+                int id[SAD_K];
+                bool use[SAD_K];
+                double lmax = -INFINITY;
+                for (int k = 0; k < SAD_K; ++k) {
+                    const uint32_t c = cand[p * SAD_K + k];
+                    use[k] = false;
+                    id[k] = (int)c;
+                    if (c >= (uint32_t)n || sites[PX * st + c] < 0.0f)
+                        continue;
+                    const double px = sites[PX * st + c], py = sites[PY * st + c];
+                    double ux = sites[PDX * st + c], uy = sites[PDY * st + c];
+                    const double n2 = ux * ux + uy * uy;
+                    if (n2 < 1e-30) {
+                        ux = 1.0;
+                        uy = 0.0;
+                    } else {
+                        const double in = 1.0 / std::sqrt(n2);
+                        ux *= in;
+                        uy *= in;
+                    }
+                    const double a = sites[PA * st + c];
+                    const double dx = X - px, dy = Y - py;
+                    const double al = ux * dx + uy * dy, be = ux * dy - uy * dx;
+                    const double q = std::sqrt(std::exp(a) * al * al + std::exp(-a) * be * be);
+                    const double d = s * q - s * (double)sites[PR * st + c];
+                    l[k] = -std::exp((double)sites[PLT * st + c]) * d;
+                    for (int ch = 0; ch < 3; ++ch)
+                        cr[k][ch] = sites[(PCR + ch) * st + c];
+                    use[k] = std::isfinite(l[k]) && std::isfinite(cr[k][0]) && std::isfinite(cr[k][1]) &&
+                             std::isfinite(cr[k][2]);
+                    if (use[k])
+                        lmax = std::max(lmax, l[k]);
+                }
+                if (!(lmax > -INFINITY))
+                    continue;
+                double e[SAD_K], Z = 0.0, chat[3] = {0.0, 0.0, 0.0};
+                for (int k = 0; k < SAD_K; ++k) {
+                    e[k] = use[k] ? std::exp(l[k] - lmax) : 0.0;
+                    Z += e[k];
+                }
+                for (int k = 0; k < SAD_K; ++k)
+                    for (int ch = 0; ch < 3; ++ch)
+                        chat[ch] += use[k] ? e[k] / Z * cr[k][ch] : 0.0;
+                const float *tp = target + 3 * p;
+                const double err = (chat[0] - tp[0]) * (chat[0] - tp[0]) + (chat[1] - tp[1]) * (chat[1] - tp[1]) +
+                                   (chat[2] - tp[2]) * (chat[2] - tp[2]);
+                for (int k = 0; k < SAD_K; ++k) {
+                    const double w = e[k] / Z;
+                    if (!use[k] || !(w > 0.0))
+                        continue;
+                    const int c = id[k];
+                    const double dx = X - sites[PX * st + c], dy = Y - sites[PY * st + c], we = w * err;
+                    const double v7[7] = {w, we, we * dx, we * dy, we * dx * dx, we * dx * dy, we * dy * dy};
+                    for (int j = 0; j < 7; ++j)
+                        if (std::isfinite(v7[j]))
+                            a[(size_t)c * 7 + j] += v7[j];
+                }
+            }
+    };
+    std::vector<std::thread> th;
+    int started = 1;
+    try {
+        for (int t = 1; t < T; ++t, ++started)
+            th.emplace_back(rows, t);
+    } catch (const std::system_error &) {
+    }
+    rows(0);
+    for (int t = started; t < T; ++t)
+        rows(t);
+    for (auto &x : th)
+        x.join();
+    for (int i = 0; i < n; ++i) {
+        for (int j = 0; j < 7; ++j) {
+            double v = 0.0;
+            for (int t = 0; t < T; ++t)
+                v += acc[t][(size_t)i * 7 + j];
+            stats[(size_t)i * SAD_STAT_LD + j] = (float)v;
+        }
+        stats[(size_t)i * SAD_STAT_LD + 7] = 0.0f;
+    }
+}
+
 }  // namespace
 
-extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, int capacity, int *n_slots,
-                                 const float *stats, const float *removal, uint32_t *cand, int W, int H, int cell,
-                                 const float *target, const sad_budget_cfg *cfg, int *n_split_out,
-                                 int *n_pruned_out, uint32_t *seeds, long seeds_cap, long *n_seeds_out)
+extern "C" int sad_densify_prune_stats(float *sites, float *m, float *v, int stride, int capacity, int *n_slots,
+                                       const float *stats, const float *removal, uint32_t *cand, int W, int H,
+                                       int cell, const float *target, const sad_budget_cfg *cfg, int *n_split_out,
+                                       int *n_pruned_out, uint32_t *seeds, long seeds_cap, long *n_seeds_out)
 {
     if (!sites || !m || !v || !n_slots || !stats || !removal || !target || !cfg)
         return SAD_ERR_ARG;
@@ -269,19 +376,37 @@ extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, i
             }
         }
     });
+    // seeding, in split order; a list that already holds the ID keeps its last place
     for (long jj = 0; jj < done; ++jj) {
         const uint32_t b = (uint32_t)bslot[jj];
         for (int q = 0; q < 5; ++q) {
             const long e = seed_e[5 * jj + q];
             if (e < 0)
                 continue;
-            if (cand)
-                cand[e * SAD_K + (SAD_K - 1)] = b;
+            if (cand) {
+                uint32_t *L = cand + e * SAD_K;
+                if (std::find(L, L + SAD_K, b) == L + SAD_K)
+                    L[SAD_K - 1] = b;
+            }
             if (seeds) {
                 seeds[2 * n_seeds] = (uint32_t)e;
                 seeds[2 * n_seeds + 1] = b;
                 ++n_seeds;
             }
+        }
+    }
+    if (seeds && n_seeds > 1) {
+        // grouped by entry, write order kept within an entry
+        std::vector<std::pair<uint32_t, uint32_t>> pr((size_t)n_seeds);
+        for (long q = 0; q < n_seeds; ++q)
+            pr[q] = {seeds[2 * q], seeds[2 * q + 1]};
+        std::stable_sort(pr.begin(), pr.end(),
+                         [](const std::pair<uint32_t, uint32_t> &a, const std::pair<uint32_t, uint32_t> &b) {
+                             return a.first < b.first;
+                         });
+        for (long q = 0; q < n_seeds; ++q) {
+            seeds[2 * q] = pr[q].first;
+            seeds[2 * q + 1] = pr[q].second;
         }
     }
     *n_slots = count;
@@ -292,4 +417,27 @@ extern "C" int sad_densify_prune(float *sites, float *m, float *v, int stride, i
     if (n_pruned_out)
         *n_pruned_out = pruned;
     return short_of_slots ? SAD_ERR_CAPACITY : SAD_OK;
+}
+
+extern "C" int sad_densify_prune(float *sites, float *m, float *v, float *removal, int *n_slots, int capacity,
+                                 int stride, uint32_t *cand, int W, int H, const float *target,
+                                 const sad_budget_cfg *cfg, uint64_t seed)
+{
+    (void)seed;  // reserved: no rule draws a random number
+    if (!sites || !m || !v || !removal || !n_slots || !cand || !target || !cfg)
+        return SAD_ERR_ARG;
+    const int n = *n_slots;
+    if (n < 0 || stride < 1 || n > stride || capacity < n || capacity > stride || W < 1 || H < 1 ||
+        W > SAD_MAX_DIM || H > SAD_MAX_DIM)
+        return SAD_ERR_ARG;
+    if (!(cfg->split_frac >= 0.0f && cfg->split_frac <= 1.0f && cfg->prune_frac >= 0.0f &&
+          cfg->prune_frac <= 1.0f && cfg->shrink > 0.0f && cfg->min_mass >= 0.0f))
+        return SAD_ERR_ARG;
+    std::vector<float> stats((size_t)stride * SAD_STAT_LD, 0.0f);
+    host_stats(sites, n, stride, cand, W, H, target, stats.data());
+    const int rc = sad_densify_prune_stats(sites, m, v, stride, capacity, n_slots, stats.data(), removal, cand, W, H, 1,
+                                           target, cfg, nullptr, nullptr, nullptr, 0, nullptr);
+    if (rc == SAD_OK || rc == SAD_ERR_CAPACITY)
+        std::fill(removal, removal + *n_slots, 0.0f);
+    return rc;
 }

@@ -161,7 +161,19 @@ __device__ __forceinline__ float geom_score(const float4 &g0, const float4 &g1, 
 // (x, y), (log tau, r), (dir_x, dir_y), (a, 0), first field in the low half.  Both
 // yield the same scoring record (x, y, r, Ux | Uy, Vx, Vy, -); decoding the packed
 // words costs a few VALU per fetch and halves the bytes fetched per candidate.
-constexpr int SEL_REC = SAD_SEL_REC64, SEL_PACKED = SAD_SEL_PACKED16;
+// A third source, the site planes themselves (float [10][stride]), serves the
+// entry points that take the site buffer directly: the scoring record is then
+// derived per fetch with the same operations make_record_v performs, so every
+// score is bit-identical to the one computed from a fresh record.
+constexpr int SEL_REC = SAD_SEL_REC64, SEL_PACKED = SAD_SEL_PACKED16, SEL_SOA = 2;
+
+// Where a kernel reads sites: the records or packed words (G), or the planes
+// (S with plane stride st).
+struct SiteSrc {
+    const float4 *G;
+    const float *S;
+    long st;
+};
 
 __device__ __forceinline__ float half_lo(uint32_t w)
 {
@@ -169,15 +181,25 @@ __device__ __forceinline__ float half_lo(uint32_t w)
 }
 __device__ __forceinline__ float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16)); }
 
-// Scoring record of site `id`; for the packed format `G` indexes 16-byte words.
+// Scoring record of site `id`: the first 32 bytes of its record, its packed words
+// decoded, or the same 32 bytes derived from the planes.
 template <int FMT>
-__device__ __forceinline__ void load_sel(const float4 *__restrict__ G, uint32_t id, float4 &g0, float4 &g1)
+__device__ __forceinline__ void load_sel(const SiteSrc &src, uint32_t id, float4 &g0, float4 &g1)
 {
     if constexpr (FMT == SEL_REC) {
-        g0 = G[RLD4 * (size_t)id];
-        g1 = G[RLD4 * (size_t)id + 1];
+        g0 = src.G[RLD4 * (size_t)id];
+        g1 = src.G[RLD4 * (size_t)id + 1];
+    } else if constexpr (FMT == SEL_SOA) {
+        const float *S = src.S + id;
+        const long st = src.st;
+        const float x = S[PX * st], y = S[PY * st], r = S[PR * st], dx = S[PDX * st], dy = S[PDY * st],
+                    a = S[PA * st];
+        const Frame f = make_frame(dx, dy, a);
+        const float sE = __expf(0.5f * a), siE = __expf(-0.5f * a);
+        g0 = make_float4(x, y, r, sE * f.ux);
+        g1 = make_float4(sE * f.uy, siE * f.ux, siE * f.uy, 0.0f);
     } else {
-        const float4 v = G[id];
+        const float4 v = src.G[id];
         const uint32_t w0 = __float_as_uint(v.x), w1 = __float_as_uint(v.y), w2 = __float_as_uint(v.z),
                        w3 = __float_as_uint(v.w);
         const float dx = half_lo(w2), dy = half_hi(w2), a = half_lo(w3);
@@ -195,11 +217,11 @@ __device__ __forceinline__ void load_sel(const float4 *__restrict__ G, uint32_t 
 }
 
 template <int FMT>
-__device__ __forceinline__ float geom_score_id(const float4 *__restrict__ G, uint32_t id, float X, float Y, float s,
+__device__ __forceinline__ float geom_score_id(const SiteSrc &src, uint32_t id, float X, float Y, float s,
                                                bool &usable)
 {
     float4 g0, g1;
-    load_sel<FMT>(G, id, g0, g1);
+    load_sel<FMT>(src, id, g0, g1);
     usable = !(g0.x < 0.0f);
     return geom_score(g0, g1, X, Y, s);
 }
@@ -431,7 +453,7 @@ __device__ __forceinline__ void region_pixel(int r, int c0, int r0, int jump, in
 }
 
 template <int KK, int TB, int FMT>
-__global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ G, uint32_t n_slots,
+__global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, uint32_t n_slots,
                                                      const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
                                                      int H, int jump, uint32_t seed_h, int n_inject, float s, float sx,
                                                      float sy, int tiles_x, int nb)
@@ -504,7 +526,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
         const uint32_t c = L.t.key[tid];
         float4 g0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), g1 = g0;
         if (c != NONE)
-            load_sel<FMT>(G, c, g0, g1);
+            load_sel<FMT>(src, c, g0, g1);
         g1.w = __uint_as_float(c);
         __syncthreads();
         if (c != NONE) {
@@ -555,7 +577,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
         if (ref != REF_NONE && ref >= (uint32_t)TB) {
             const uint32_t c = ref & ~REF_SPILL;
             bool usable;
-            const float d = geom_score_id<FMT>(G, c, X, Y, s, usable);
+            const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
             best.consider(c, d, usable);
         }
     }
@@ -602,7 +624,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
             best.consider_new(id, d, usable);
         } else {
             const uint32_t c = ref & ~REF_SPILL;
-            const float d = geom_score_id<FMT>(G, c, X, Y, s, usable);
+            const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
             best.consider(c, d, usable);
         }
     }
@@ -615,7 +637,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
             const uint32_t c = (uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32);
             if (c < n_slots) {
                 bool usable;
-                const float d = geom_score_id<FMT>(G, c, X, Y, s, usable);
+                const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
                 best.consider(c, d, usable);
             }
         }
@@ -632,7 +654,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(const float4 *__restrict__ 
 // per workgroup: 16 for maps large enough to fill the chip with 16x16 tiles, 8
 // for small (downscaled) maps, which would otherwise leave most CUs idle.
 template <int TW, int FMT>
-__global__ __launch_bounds__(TW *TW) void k_propagate_direct(const float4 *__restrict__ G, uint32_t n_slots,
+__global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, uint32_t n_slots,
                                                              const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
                                                              int W, int H, int jump, uint32_t seed_h, int n_inject,
                                                              float s, float sx, float sy, int tiles_x, int nb)
@@ -661,7 +683,7 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(const float4 *__res
             // nearby pixels share most of their sites)
             if (ids[k] < n_slots && !best.holds(ids[k])) {
                 bool usable;
-                const float d = geom_score_id<FMT>(G, ids[k], X, Y, s, usable);
+                const float d = geom_score_id<FMT>(src, ids[k], X, Y, s, usable);
                 best.consider_new(ids[k], d, usable);
             }
         }
@@ -674,7 +696,7 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(const float4 *__res
             const uint32_t c = (uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32);
             if (c < n_slots) {
                 bool usable;
-                const float d = geom_score_id<FMT>(G, c, X, Y, s, usable);
+                const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
                 best.consider(c, d, usable);
             }
         }
@@ -705,8 +727,35 @@ __global__ __launch_bounds__(256) void k_fill_map(uint4 *__restrict__ cand, long
         cand[i] = make_uint4(NONE, NONE, NONE, NONE);
 }
 
+// Seeding pairs (entry, ID), grouped by entry and in write order within an
+// entry: the first pair of each group applies the group's pairs in order, each
+// writing its ID into the last place of the entry's list unless the list holds
+// it already (the lists keep distinct IDs).
+__global__ __launch_bounds__(256) void k_apply_seeds(uint32_t *__restrict__ cand, long n_entries,
+                                                     const uint2 *__restrict__ seeds, long n_seeds)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_seeds)
+        return;
+    const uint32_t e = seeds[i].x;
+    if (i > 0 && seeds[i - 1].x == e)
+        return;  // not the first pair of its group
+    if ((long)e >= n_entries)
+        return;
+    uint32_t *L = cand + (size_t)e * K;
+    for (long j = i; j < n_seeds && seeds[j].x == e; ++j) {
+        const uint32_t id = seeds[j].y;
+        bool held = false;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            held |= L[k] == id;
+        if (!held)
+            L[K - 1] = id;
+    }
+}
+
 template <int FMT>
-__global__ __launch_bounds__(256) void k_jfa_seed_round(const float4 *__restrict__ G, uint32_t n_slots,
+__global__ __launch_bounds__(256) void k_jfa_seed_round(SiteSrc src, uint32_t n_slots,
                                                         unsigned long long *__restrict__ keys, int W, int H,
                                                         float s, MapGrid mg, int round)
 {
@@ -714,7 +763,7 @@ __global__ __launch_bounds__(256) void k_jfa_seed_round(const float4 *__restrict
     if (i >= n_slots)
         return;
     float4 g0, g1;
-    load_sel<FMT>(G, i, g0, g1);
+    load_sel<FMT>(src, i, g0, g1);
     if (!(g0.x >= 0.0f) || !finitef(g0.x) || !finitef(g0.y))
         return;  // inactive (x < 0), or no position
     // the map entry of the pixel that holds the site
@@ -749,7 +798,7 @@ __global__ __launch_bounds__(256) void k_jfa_seed_finish(uint4 *__restrict__ can
 // pixel of a tile at steps >= 16, so candidates are scored straight from their
 // records, as in the table-free propagation.
 template <int FMT>
-__global__ __launch_bounds__(BLOCK) void k_jfa_pass(const float4 *__restrict__ G, uint32_t n_slots,
+__global__ __launch_bounds__(BLOCK) void k_jfa_pass(SiteSrc src, uint32_t n_slots,
                                                     const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
                                                     int H, int step, float s, float sx, float sy, int tiles_x,
                                                     int nb)
@@ -775,7 +824,7 @@ __global__ __launch_bounds__(BLOCK) void k_jfa_pass(const float4 *__restrict__ G
             // an ID already held is skipped before its record is fetched
             if (ids[k] < n_slots && !best.holds(ids[k])) {
                 bool usable;
-                const float d = geom_score_id<FMT>(G, ids[k], X, Y, s, usable);
+                const float d = geom_score_id<FMT>(src, ids[k], X, Y, s, usable);
                 best.consider_new(ids[k], d, usable);
             }
         }
@@ -789,7 +838,7 @@ __global__ __launch_bounds__(BLOCK) void k_jfa_pass(const float4 *__restrict__ G
 // Exact top-K by brute force: every slot is scored for every pixel.  Scoring
 // records are staged through LDS 256 at a time.
 template <int FMT>
-__global__ __launch_bounds__(BLOCK) void k_topk_exact(const float4 *__restrict__ G, uint32_t n_slots,
+__global__ __launch_bounds__(BLOCK) void k_topk_exact(SiteSrc src, uint32_t n_slots,
                                                       uint4 *__restrict__ cout, int W, int H, float s, float sx,
                                                       float sy, int tiles_x, int nb)
 {
@@ -807,7 +856,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_exact(const float4 *__restrict__
         const uint32_t i = base + threadIdx.x;
         float4 g0 = make_float4(-1.0f, 0.0f, 0.0f, 0.0f), g1 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (i < n_slots)
-            load_sel<FMT>(G, i, g0, g1);
+            load_sel<FMT>(src, i, g0, g1);
         __syncthreads();
         l0[threadIdx.x] = g0;
         l1[threadIdx.x] = g1;
@@ -826,6 +875,53 @@ __global__ __launch_bounds__(BLOCK) void k_topk_exact(const float4 *__restrict__
         cout[2 * p] = make_uint4((uint32_t)best.k[0], (uint32_t)best.k[1], (uint32_t)best.k[2], (uint32_t)best.k[3]);
         cout[2 * p + 1] =
             make_uint4((uint32_t)best.k[4], (uint32_t)best.k[5], (uint32_t)best.k[6], (uint32_t)best.k[7]);
+    }
+}
+
+// Exact top-K at chosen map entries (entry index row * Wm + col each), for recall
+// measurements on maps too large for the whole-map brute force: one entry per
+// lane, every slot scored, scoring records staged through LDS as above.
+template <int FMT>
+__global__ __launch_bounds__(BLOCK) void k_topk_exact_at(SiteSrc src, uint32_t n_slots,
+                                                         const uint32_t *__restrict__ ent, int n_ent,
+                                                         uint4 *__restrict__ out, int Wm, int Hm, float s,
+                                                         float sx, float sy)
+{
+    __shared__ float4 l0[BLOCK], l1[BLOCK];
+    const int q = blockIdx.x * BLOCK + threadIdx.x;
+    const bool inside = q < n_ent;
+    uint32_t e = inside ? ent[q] : 0u;
+    const bool valid = inside && e < (uint32_t)Wm * (uint32_t)Hm;
+    e = valid ? e : 0u;
+    const int col = (int)(e % (uint32_t)Wm), row = (int)(e / (uint32_t)Wm);
+    const float X = ((float)col + 0.5f) * sx, Y = ((float)row + 0.5f) * sy;
+    TopK64 best;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+        best.k[j] = ~0ull;
+    for (uint32_t base = 0; base < n_slots; base += BLOCK) {
+        const uint32_t i = base + threadIdx.x;
+        float4 g0 = make_float4(-1.0f, 0.0f, 0.0f, 0.0f), g1 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (i < n_slots)
+            load_sel<FMT>(src, i, g0, g1);
+        __syncthreads();
+        l0[threadIdx.x] = g0;
+        l1[threadIdx.x] = g1;
+        __syncthreads();
+        if (valid) {
+            const int cnt = min((int)(n_slots - base), BLOCK);
+            for (int j = 0; j < cnt; ++j) {
+                const float4 a0 = l0[j];
+                const float d = geom_score(a0, l1[j], X, Y, s);
+                best.consider_new(base + j, d, !(a0.x < 0.0f));
+            }
+        }
+    }
+    if (inside) {
+        out[2 * (long)q] = make_uint4((uint32_t)best.k[0], (uint32_t)best.k[1], (uint32_t)best.k[2],
+                                      (uint32_t)best.k[3]);
+        out[2 * (long)q + 1] = make_uint4((uint32_t)best.k[4], (uint32_t)best.k[5], (uint32_t)best.k[6],
+                                          (uint32_t)best.k[7]);
     }
 }
 
@@ -850,10 +946,31 @@ struct SiteRec {
     float v[NREC];
 };
 
-__device__ __forceinline__ SiteRec load_rec_global(const float4 *__restrict__ G, uint32_t c)
+// Render record of site c from its 64-byte record (FMT = SEL_REC) or from the
+// planes (SEL_SOA: the same derivation as make_record_v, so the same bits).
+template <int FMT>
+__device__ __forceinline__ SiteRec load_rec_global(const SiteSrc &src, uint32_t c)
 {
-    const float4 a = G[RLD4 * (size_t)c], b = G[RLD4 * (size_t)c + 1], cc = G[RLD4 * (size_t)c + 2],
-                 d = G[RLD4 * (size_t)c + 3];
+    float4 a, b, cc, d;
+    if constexpr (FMT == SEL_SOA) {
+        float p[SAD_NPARAM];
+#pragma unroll
+        for (int k = 0; k < SAD_NPARAM; ++k)
+            p[k] = src.S[k * src.st + c];
+        float4 o[RLD4];
+        make_record_v(p, o);
+        a = o[0];
+        b = o[1];
+        cc = o[2];
+        d = o[3];
+    } else {
+        static_assert(FMT == SEL_REC, "render kernels read records or planes");
+        const float4 *G = src.G;
+        a = G[RLD4 * (size_t)c];
+        b = G[RLD4 * (size_t)c + 1];
+        cc = G[RLD4 * (size_t)c + 2];
+        d = G[RLD4 * (size_t)c + 3];
+    }
     SiteRec R;
     const bool ok = !(a.x < 0.0f) && finitef(cc.x) && finitef(cc.y) && finitef(cc.z);
     R.v[R_PX] = ok ? a.x : __builtin_nanf("");
@@ -895,11 +1012,12 @@ __device__ __forceinline__ void table_insert_phase(TileTable &T, uint32_t n_slot
 
 // One thread per slot: the slot's record (after a barrier that completes the
 // inserts), and the null record.  Ends with a barrier.
-__device__ __forceinline__ void table_load_phase(TileTable &T, const float4 *__restrict__ G)
+template <int FMT>
+__device__ __forceinline__ void table_load_phase(TileTable &T, const SiteSrc &src)
 {
     const uint32_t c = T.key[threadIdx.x];
     if (c != NONE) {
-        const SiteRec R = load_rec_global(G, c);
+        const SiteRec R = load_rec_global<FMT>(src, c);
 #pragma unroll
         for (int j = 0; j < NREC / 4; ++j)
             T.rec[threadIdx.x][j] = make_float4(R.v[4 * j], R.v[4 * j + 1], R.v[4 * j + 2], R.v[4 * j + 3]);
@@ -909,12 +1027,13 @@ __device__ __forceinline__ void table_load_phase(TileTable &T, const float4 *__r
     __syncthreads();
 }
 
-__device__ __forceinline__ void build_tile_table(TileTable &T, const float4 *__restrict__ G, uint32_t n_slots,
+template <int FMT>
+__device__ __forceinline__ void build_tile_table(TileTable &T, const SiteSrc &src, uint32_t n_slots,
                                                  const uint32_t (&ids)[K], int (&slot)[K])
 {
     table_insert_phase(T, n_slots, ids, slot);
     __syncthreads();
-    table_load_phase(T, G);
+    table_load_phase<FMT>(T, src);
 }
 
 __device__ __forceinline__ SiteRec table_rec(const TileTable &T, int sl)
@@ -949,12 +1068,13 @@ struct PixelBlend {
 
 // Record of list entry k: from the tile table, from global memory for a spilled
 // ID, or an unusable placeholder (px = NaN) for an empty entry.
-__device__ __forceinline__ SiteRec fetch_rec(const TileTable &T, const float4 *__restrict__ G, uint32_t id, int sl)
+template <int FMT>
+__device__ __forceinline__ SiteRec fetch_rec(const TileTable &T, const SiteSrc &src, uint32_t id, int sl)
 {
     if (sl >= 0)
         return table_rec(T, sl);
     if (sl == -1)
-        return load_rec_global(G, id);
+        return load_rec_global<FMT>(src, id);
     SiteRec R;
 #pragma unroll
     for (int j = 0; j < NREC; ++j)
@@ -963,7 +1083,8 @@ __device__ __forceinline__ SiteRec fetch_rec(const TileTable &T, const float4 *_
     return R;
 }
 
-__device__ __forceinline__ void blend_pixel(const TileTable &T, const float4 *__restrict__ G,
+template <int FMT>
+__device__ __forceinline__ void blend_pixel(const TileTable &T, const SiteSrc &src,
                                             const uint32_t (&ids)[K], const int (&slot)[K], float X, float Y,
                                             float s, PixelBlend &B)
 {
@@ -987,7 +1108,7 @@ __device__ __forceinline__ void blend_pixel(const TileTable &T, const float4 *__
 #pragma unroll
         for (int k = 0; k < K; ++k)
             if (slot[k] == -1)
-                entry(k, load_rec_global(G, ids[k]));
+                entry(k, load_rec_global<FMT>(src, ids[k]));
     }
     float mx = -__builtin_inff();
 #pragma unroll
@@ -1050,7 +1171,8 @@ __device__ __forceinline__ void load_ids(const uint4 *__restrict__ cand, long p,
 
 
 // Render forward (reading note, key design 2; project page "Method").
-__global__ __launch_bounds__(BLOCK) void k_render_fwd(const float4 *__restrict__ G, uint32_t n_slots,
+template <int FMT>
+__global__ __launch_bounds__(BLOCK) void k_render_fwd(SiteSrc src, uint32_t n_slots,
                                                       const uint4 *__restrict__ cand, int W, int H,
                                                       float *__restrict__ out, float s, MapGrid mg, int tiles_x, int nb)
 {
@@ -1062,11 +1184,11 @@ __global__ __launch_bounds__(BLOCK) void k_render_fwd(const float4 *__restrict__
     uint32_t ids[K];
     int slot[K];
     load_ids(cand, mg.entry(p, col, row), inside, ids);
-    build_tile_table(T, G, n_slots, ids, slot);
+    build_tile_table<FMT>(T, src, n_slots, ids, slot);
     if (!inside)
         return;
     PixelBlend B;
-    blend_pixel(T, G, ids, slot, (float)col + 0.5f, (float)row + 0.5f, s, B);
+    blend_pixel<FMT>(T, src, ids, slot, (float)col + 0.5f, (float)row + 0.5f, s, B);
     out[3 * p] = B.chat0;
     out[3 * p + 1] = B.chat1;
     out[3 * p + 2] = B.chat2;
@@ -1206,13 +1328,33 @@ __device__ __forceinline__ void site_grads(const SiteRec &R, float s, const floa
         acc[a] = finitef(acc[a]) ? acc[a] : 0.0f;
 }
 
+// Gradient accumulators: one 64-byte record per site (GL_REC: site i's 11 sums
+// at g[16 i .. 16 i + 10]) or eleven planes (GL_PLANES: accumulator a of site i
+// at g[a * st + i]).
+constexpr int GL_REC = 0, GL_PLANES = 1;
+
+struct GradOut {
+    float *g;
+    long st;
+};
+
+template <int GL>
+__device__ __forceinline__ float *grad_at(const GradOut &o, uint32_t id, int a)
+{
+    if constexpr (GL == GL_REC)
+        return o.g + (size_t)id * SAD_GRAD_LD + a;
+    else
+        return o.g + (size_t)a * o.st + id;
+}
+
 // Gradients of one spilled entry per lane (id = NONE: none), flushed by the
 // whole wave together: the 11 sums of each lane are staged in LDS and
 // consecutive lanes take consecutive accumulators of one site, so an atomic
 // instruction touches a few 64-byte records instead of one per lane.
-__device__ __forceinline__ void spill_flush(const float4 *__restrict__ G, uint32_t id, float X, float Y, float s,
+template <int FMT, int GL>
+__device__ __forceinline__ void spill_flush(const SiteSrc &src, uint32_t id, float X, float Y, float s,
                                             float w, float gm, float dl, const float4 &g, float *vals,
-                                            float *__restrict__ grad, int lane)
+                                            const GradOut &grad, int lane)
 {
     uint32_t *vid = reinterpret_cast<uint32_t *>(vals + 64 * SAD_NACC);
     float acc[SAD_NACC];
@@ -1220,7 +1362,7 @@ __device__ __forceinline__ void spill_flush(const float4 *__restrict__ G, uint32
     for (int a = 0; a < SAD_NACC; ++a)
         acc[a] = 0.0f;
     if (id != NONE) {
-        const SiteRec R = load_rec_global(G, id);
+        const SiteRec R = load_rec_global<FMT>(src, id);
         float v[NSUM];
         entry_sums(R, X, Y, w, gm, dl, g, v);
         site_grads(R, s, v, acc);
@@ -1237,7 +1379,7 @@ __device__ __forceinline__ void spill_flush(const float4 *__restrict__ G, uint32
         const uint32_t c = vid[e];
         const float v = vals[i];
         if (c != NONE && v != 0.0f)
-            unsafeAtomicAdd(&grad[(size_t)c * SAD_GRAD_LD + a], v);
+            unsafeAtomicAdd(grad_at<GL>(grad, c, a), v);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -1284,7 +1426,8 @@ struct PairBlend {
     float iZ, chat0, chat1, chat2;
 };
 
-__device__ __forceinline__ void pair_blend(const TileTable &T, const float4 *__restrict__ G,
+template <int FMT>
+__device__ __forceinline__ void pair_blend(const TileTable &T, const SiteSrc &src,
                                            const uint32_t (&ids)[KH], const int (&slot)[KH], float X, float Y,
                                            float s, int half, PairBlend &B)
 {
@@ -1308,7 +1451,7 @@ __device__ __forceinline__ void pair_blend(const TileTable &T, const float4 *__r
 #pragma unroll
         for (int k = 0; k < KH; ++k)
             if (slot[k] == -1)
-                entry(k, load_rec_global(G, ids[k]));
+                entry(k, load_rec_global<FMT>(src, ids[k]));
     }
     float mx = -__builtin_inff();
 #pragma unroll
@@ -1336,12 +1479,13 @@ __device__ __forceinline__ void pair_blend(const TileTable &T, const float4 *__r
 }
 
 
-__global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(const float4 *__restrict__ G, uint32_t n_slots,
+template <int FMT, int GL>
+__global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(SiteSrc src, uint32_t n_slots,
                                                             const uint4 *__restrict__ cand,
                                                             const float *__restrict__ target, int W, int H,
-                                                            float *__restrict__ grad, float *__restrict__ loss_sum,
-                                                            float *__restrict__ out_rgb, float s, MapGrid grid,
-                                                            int tiles_x, int nb)
+                                                            GradOut grad, float *__restrict__ loss_sum,
+                                                            uint32_t loss_mask, float *__restrict__ out_rgb, float s,
+                                                            MapGrid grid, int tiles_x, int nb)
 {
     __shared__ BwdShared L;
     const int tid = threadIdx.x;
@@ -1431,7 +1575,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(const float4 *__res
     if (tid < TBL) {
         const uint32_t c = L.T.key[tid];
         if (c != NONE) {
-            const SiteRec R = load_rec_global(G, c);
+            const SiteRec R = load_rec_global<FMT>(src, c);
 #pragma unroll
             for (int j = 0; j < NREC / 4; ++j)
                 L.T.rec[tid][j] = make_float4(R.v[4 * j], R.v[4 * j + 1], R.v[4 * j + 2], R.v[4 * j + 3]);
@@ -1448,7 +1592,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(const float4 *__res
     // staged entries written in slot order, spilled entries flushed to global memory
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
     PairBlend B;
-    pair_blend(L.T, G, ids, slot, X, Y, s, half, B);
+    pair_blend<FMT>(L.T, src, ids, slot, X, Y, s, half, B);
     const float *c0 = B.c0, *c1 = B.c1, *c2 = B.c2, *e = B.e;
     const bool *use = B.use;
     const bool any = B.any;
@@ -1552,7 +1696,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(const float4 *__res
 #pragma unroll
         for (int k = 0; k < KH; ++k)
             if (__any(spill[k]))
-                spill_flush(G, spill[k] ? ids[k] : NONE, X, Y, s, wk[k], gk[k], dk[k], make_float4(g0, g1, g2, 0.0f),
+                spill_flush<FMT, GL>(src, spill[k] ? ids[k] : NONE, X, Y, s, wk[k], gk[k], dk[k], make_float4(g0, g1, g2, 0.0f),
                             vals, grad, lane);
         __syncthreads();
         stage_entries();
@@ -1574,7 +1718,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(const float4 *__res
 #pragma unroll
         for (int w = 0; w < PAIR_THREADS / 64; ++w)
             v += L.wsum[w];
-        unsafeAtomicAdd(loss_sum + (blockIdx.x & (SAD_LOSS_SLOTS - 1)), v);
+        unsafeAtomicAdd(loss_sum + (blockIdx.x & loss_mask), v);
     }
 
     // phase 4: chunk of 8 sorted entries per thread (the first 256 threads), runs
@@ -1697,13 +1841,13 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(const float4 *__res
         const int sl = L.occ[j];
         const float v = L.u.r.fin[a][sl];
         if (v != 0.0f)
-            unsafeAtomicAdd(&grad[(long)L.T.key[sl] * SAD_GRAD_LD + a], v);
+            unsafeAtomicAdd(grad_at<GL>(grad, L.T.key[sl], a), v);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Budget-control statistics (summary, B.5: the densification score combines
-// per-site mass, energy and weighted second moments).  For each site, over the
+// Budget-control statistics (summary, B.5: splitting is decided from a site's
+// coverage, its remaining error and the spread of that error).  For each site, over the
 // pixels x whose list holds it, with w its softmax weight at x, e = ||c(x) - t(x)||^2
 // and delta = x - p (the site position, so the moments stay well conditioned):
 //   [0] sum w   [1] sum w e   [2] sum w e dx   [3] sum w e dy
@@ -1716,7 +1860,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(const float4 *__res
 // path.
 constexpr int NSTAT = 7;
 
-__global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restrict__ G, uint32_t n_slots,
+__global__ __launch_bounds__(BLOCK) void k_densify_stats(SiteSrc src, uint32_t n_slots,
                                                          const uint4 *__restrict__ cand,
                                                          const float *__restrict__ target, int W, int H,
                                                          float *__restrict__ stats, float s, MapGrid mg, int tiles_x,
@@ -1737,13 +1881,13 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restric
 #pragma unroll
     for (int a = 0; a < NSTAT; ++a)
         acc_t[a][tid] = 0.0f;  // complete at the table build's barriers
-    build_tile_table(T, G, n_slots, ids, slot);
+    build_tile_table<SEL_REC>(T, src, n_slots, ids, slot);
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
     PixelBlend B;
     float err = 0.0f, iZ = 0.0f;
     bool any = false;
     if (inside) {
-        blend_pixel(T, G, ids, slot, X, Y, s, B);
+        blend_pixel<SEL_REC>(T, src, ids, slot, X, Y, s, B);
         const float r0 = B.chat0 - target[3 * p], r1 = B.chat1 - target[3 * p + 1], r2 = B.chat2 - target[3 * p + 2];
         err = r0 * r0 + r1 * r1 + r2 * r2;
         any = B.any;
@@ -1761,7 +1905,7 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(const float4 *__restric
         for (int a = 0; a < NSTAT; ++a)
             acc[a] = 0.0f;
         if (has) {
-            const SiteRec R = fetch_rec(T, G, ids[k], slot[k]);
+            const SiteRec R = fetch_rec<SEL_REC>(T, src, ids[k], slot[k]);
             const float w = B.e[k] * iZ, we = w * err;
             const float dx = X - R.v[R_PX], dy = Y - R.v[R_PY];
             acc[0] = w;
@@ -2076,6 +2220,7 @@ struct AdamArgs {
     float b1, b2, eps, ibc1, ibc2, inv_p, W, H;  // ibc = 1 / (1 - beta^step)
 };
 
+template <int GL>
 __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__restrict__ M, float *__restrict__ V,
                                               float *__restrict__ G, float4 *__restrict__ rec,
                                               uint4 *__restrict__ packed, int n_slots, int stride, AdamArgs A)
@@ -2084,9 +2229,18 @@ __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__re
     if (i >= n_slots)
         return;
     const long st = stride;
-    float4 *gr = reinterpret_cast<float4 *>(G + (long)i * SAD_GRAD_LD);
-    const float4 ga = gr[0], gb = gr[1], gc = gr[2];
-    const float gv[SAD_NPARAM] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w, gc.x, gc.y};
+    float gv[SAD_NPARAM];
+    if constexpr (GL == GL_REC) {
+        float4 *gr = reinterpret_cast<float4 *>(G + (long)i * SAD_GRAD_LD);
+        const float4 ga = gr[0], gb = gr[1], gc = gr[2];
+        gv[0] = ga.x; gv[1] = ga.y; gv[2] = ga.z; gv[3] = ga.w;
+        gv[4] = gb.x; gv[5] = gb.y; gv[6] = gb.z; gv[7] = gb.w;
+        gv[8] = gc.x; gv[9] = gc.y;
+    } else {
+#pragma unroll
+        for (int j = 0; j < SAD_NPARAM; ++j)
+            gv[j] = G[j * st + i];
+    }
     // every load first (parameters, then moments), the updates in registers, then
     // the stores and the derived record: one memory round trip per slot instead
     // of one per parameter
@@ -2094,9 +2248,16 @@ __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__re
 #pragma unroll
     for (int j = 0; j < SAD_NPARAM; ++j)
         po[j] = S[j * st + i];
-    gr[0] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    gr[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    reinterpret_cast<float2 *>(gr + 2)[0] = make_float2(0.0f, 0.0f);
+    if constexpr (GL == GL_REC) {
+        float4 *gr = reinterpret_cast<float4 *>(G + (long)i * SAD_GRAD_LD);
+        gr[0] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        gr[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        reinterpret_cast<float2 *>(gr + 2)[0] = make_float2(0.0f, 0.0f);
+    } else {
+#pragma unroll
+        for (int j = 0; j < SAD_NPARAM; ++j)
+            G[j * st + i] = 0.0f;
+    }
     const bool active = !(po[PX] < 0.0f);
     if (active) {
         float mo[SAD_NPARAM], vo[SAD_NPARAM];
@@ -2195,7 +2356,7 @@ inline int launched()
 inline bool valid_fmt(int f) { return f == SEL_REC || f == SEL_PACKED; }
 
 struct PropArgs {
-    const float4 *G;
+    SiteSrc src;
     uint32_t n;
     const uint4 *ci;
     uint4 *co;
@@ -2217,13 +2378,13 @@ void launch_propagate(const PropArgs &A, hipStream_t hs)
     const TileGrid g = tile_grid(A.Wm, A.Hm);
     if (A.cell > 1 && g.nb < SMALL_MAP_TILES) {
         const TileGrid g8 = tile_grid(A.Wm, A.Hm, 8);
-        hipLaunchKernelGGL((k_propagate_direct<8, FMT>), dim3(g8.nb), dim3(64), 0, hs, A.G, A.n, A.ci, A.co, A.Wm,
+        hipLaunchKernelGGL((k_propagate_direct<8, FMT>), dim3(g8.nb), dim3(64), 0, hs, A.src, A.n, A.ci, A.co, A.Wm,
                            A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g8.tiles_x, g8.nb);
     } else if (A.cell == 1 && A.jump == 1) {
-        hipLaunchKernelGGL((k_propagate<1, 256, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.G, A.n, A.ci, A.co, A.Wm,
-                           A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
+        hipLaunchKernelGGL((k_propagate<1, 256, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.n, A.ci, A.co,
+                           A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
     } else {
-        hipLaunchKernelGGL((k_propagate_direct<TILE, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.G, A.n, A.ci, A.co,
+        hipLaunchKernelGGL((k_propagate_direct<TILE, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.n, A.ci, A.co,
                            A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
     }
 }
@@ -2233,6 +2394,112 @@ uint32_t host_pcg_hash(uint32_t v)
     const uint32_t state = v * 747796405u + 2891336453u;
     const uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
     return (word >> 22u) ^ word;
+}
+
+inline SiteSrc src_of(const float *rec) { return SiteSrc{(const float4 *)rec, nullptr, 0}; }
+inline SiteSrc src_planes(const float *sites, int stride) { return SiteSrc{nullptr, sites, (long)stride}; }
+
+// One propagation pass from any site source (fmt: SEL_REC, SEL_PACKED or SEL_SOA);
+// `site_ptr` is the pointer the source reads, for the NULL check.
+int propagate_pass(SiteSrc src, const void *site_ptr, int fmt, int n_slots, const uint32_t *cand_in,
+                   uint32_t *cand_out, int W, int H, int cell, int jump, uint32_t pass_index, uint32_t seed,
+                   int n_inject, void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)))
+        return rc;
+    if (n_slots < 0 || jump < 1 || jump > 0xFFFF || n_inject < 0 || n_inject > SAD_MAX_INJECT || cell < 1)
+        return SAD_ERR_ARG;
+    if (W == 0 || H == 0)
+        return SAD_OK;
+    MapGrid mg;
+    int Wm, Hm;
+    if (!map_grid(W, H, cell, mg, Wm, Hm))
+        return SAD_ERR_ARG;
+    if ((!site_ptr && n_slots > 0) || !cand_in || !cand_out)
+        return SAD_ERR_ARG;
+    const size_t bytes = (size_t)Wm * Hm * K * sizeof(uint32_t);
+    const uintptr_t a0 = (uintptr_t)cand_in, a1 = (uintptr_t)cand_out;
+    if (a0 < a1 + bytes && a1 < a0 + bytes)
+        return SAD_ERR_ARG;
+    if (!aligned16(cand_in) || !aligned16(cand_out) || (fmt != SEL_SOA && !aligned16(site_ptr)))
+        return SAD_ERR_ALIGN;
+    const uint32_t pw = ((uint32_t)jump << 16) | (pass_index & 0xFFFFu);
+    const uint32_t seed_h = host_pcg_hash(host_pcg_hash(seed) ^ pw);
+    const PropArgs A{src, (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm,
+                     cell, jump, seed_h, n_inject, scale_of(W, H), mg.sx, mg.sy};
+    if (fmt == SEL_PACKED)
+        launch_propagate<SEL_PACKED>(A, (hipStream_t)stream);
+    else if (fmt == SEL_SOA)
+        launch_propagate<SEL_SOA>(A, (hipStream_t)stream);
+    else
+        launch_propagate<SEL_REC>(A, (hipStream_t)stream);
+    return launched();
+}
+
+int render_fwd_any(SiteSrc src, const void *site_ptr, int fmt, int n_slots, const uint32_t *cand, int W, int H,
+                   int cell, float *out_rgb, void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)))
+        return rc;
+    if (n_slots < 0 || cell < 1)
+        return SAD_ERR_ARG;
+    if (W == 0 || H == 0)
+        return SAD_OK;
+    MapGrid mg;
+    int Wm, Hm;
+    if (!map_grid(W, H, cell, mg, Wm, Hm))
+        return SAD_ERR_ARG;
+    if ((!site_ptr && n_slots > 0) || !cand || !out_rgb)
+        return SAD_ERR_ARG;
+    if (!aligned16(cand) || (fmt != SEL_SOA && !aligned16(site_ptr)))
+        return SAD_ERR_ALIGN;
+    const TileGrid g = tile_grid(W, H);
+    if (fmt == SEL_SOA)
+        hipLaunchKernelGGL(k_render_fwd<SEL_SOA>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
+                           (uint32_t)n_slots, (const uint4 *)cand, W, H, out_rgb, scale_of(W, H), mg, g.tiles_x, g.nb);
+    else
+        hipLaunchKernelGGL(k_render_fwd<SEL_REC>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
+                           (uint32_t)n_slots, (const uint4 *)cand, W, H, out_rgb, scale_of(W, H), mg, g.tiles_x, g.nb);
+    return launched();
+}
+
+int adam_any(float *sites, float *m, float *v, float *grad, int gl, float *rec, uint32_t *packed, int n_slots,
+             int stride, int step, int n_pixels, const sad_adam_cfg *cfg, void *stream)
+{
+    int rc;
+    if ((rc = check_sites(n_slots, stride)))
+        return rc;
+    if (!sites || !m || !v || !grad || !cfg || step < 1 || n_pixels < 1)
+        return SAD_ERR_ARG;
+    if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f && cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f && cfg->eps >= 0.0f))
+        return SAD_ERR_ARG;
+    if (!(cfg->x_max > 0.0f && cfg->y_max > 0.0f && cfg->x_max <= (float)SAD_MAX_DIM &&
+          cfg->y_max <= (float)SAD_MAX_DIM))
+        return SAD_ERR_ARG;
+    if ((gl == GL_REC && !aligned16(grad)) || !aligned16(rec) || !aligned16(packed))
+        return SAD_ERR_ALIGN;
+    if (n_slots == 0)
+        return SAD_OK;
+    AdamArgs A;
+    for (int j = 0; j < SAD_NPARAM; ++j)
+        A.lr[j] = cfg->lr[j];
+    A.b1 = cfg->beta1;
+    A.b2 = cfg->beta2;
+    A.eps = cfg->eps;
+    A.ibc1 = (float)(1.0 / (1.0 - __builtin_pow((double)cfg->beta1, (double)step)));
+    A.ibc2 = (float)(1.0 / (1.0 - __builtin_pow((double)cfg->beta2, (double)step)));
+    A.inv_p = 1.0f / (float)n_pixels;
+    A.W = cfg->x_max;
+    A.H = cfg->y_max;
+    if (gl == GL_PLANES)
+        hipLaunchKernelGGL(k_adam<GL_PLANES>, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites,
+                           m, v, grad, (float4 *)rec, (uint4 *)packed, n_slots, stride, A);
+    else
+        hipLaunchKernelGGL(k_adam<GL_REC>, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, m,
+                           v, grad, (float4 *)rec, (uint4 *)packed, n_slots, stride, A);
+    return launched();
 }
 
 }  // namespace
@@ -2286,37 +2553,45 @@ int sad_pack_sites(const float *sites, int n_slots, int stride, uint32_t *packed
     return launched();
 }
 
-int sad_topk_propagate(const float *rec, int sel_fmt, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W,
-                       int H, int cell, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream)
+int sad_topk_propagate(const float *sites, int n_slots, int stride, const uint32_t *cand_in, uint32_t *cand_out, int W,
+                       int H, int jump, uint32_t pass_index, uint32_t seed, int n_inject, void *stream)
+{
+    int rc;
+    if ((rc = check_sites(n_slots, stride)))
+        return rc;
+    return propagate_pass(src_planes(sites, stride), sites, SEL_SOA, n_slots, cand_in, cand_out, W, H, 1, jump,
+                          pass_index, seed, n_inject, stream);
+}
+
+int sad_topk_propagate_rec(const float *rec, int sel_fmt, int n_slots, const uint32_t *cand_in, uint32_t *cand_out,
+                           int W, int H, int cell, int jump, uint32_t pass_index, uint32_t seed, int n_inject,
+                           void *stream)
+{
+    if (!valid_fmt(sel_fmt))
+        return SAD_ERR_ARG;
+    return propagate_pass(src_of(rec), rec, sel_fmt, n_slots, cand_in, cand_out, W, H, cell, jump, pass_index, seed,
+                          n_inject, stream);
+}
+
+int sad_apply_seeds(uint32_t *cand, int W, int H, int cell, const uint32_t *seeds, long n_seeds, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0 || jump < 1 || jump > 0xFFFF || n_inject < 0 || n_inject > SAD_MAX_INJECT || cell < 1 ||
-        !valid_fmt(sel_fmt))
+    if (cell < 1 || n_seeds < 0 || n_seeds > 0x7FFFFFFFL)
         return SAD_ERR_ARG;
-    if (W == 0 || H == 0)
+    if (W == 0 || H == 0 || n_seeds == 0)
         return SAD_OK;
     MapGrid mg;
     int Wm, Hm;
     if (!map_grid(W, H, cell, mg, Wm, Hm))
         return SAD_ERR_ARG;
-    if ((!rec && n_slots > 0) || !cand_in || !cand_out)
+    if (!cand || !seeds)
         return SAD_ERR_ARG;
-    const size_t bytes = (size_t)Wm * Hm * K * sizeof(uint32_t);
-    const uintptr_t a0 = (uintptr_t)cand_in, a1 = (uintptr_t)cand_out;
-    if (a0 < a1 + bytes && a1 < a0 + bytes)
-        return SAD_ERR_ARG;
-    if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(rec))
+    if (!aligned16(cand) || ((uintptr_t)seeds & 7u))
         return SAD_ERR_ALIGN;
-    const uint32_t pw = ((uint32_t)jump << 16) | (pass_index & 0xFFFFu);
-    const uint32_t seed_h = host_pcg_hash(host_pcg_hash(seed) ^ pw);
-    const PropArgs A{(const float4 *)rec, (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm,
-                     cell, jump, seed_h, n_inject, scale_of(W, H), mg.sx, mg.sy};
-    if (sel_fmt == SEL_PACKED)
-        launch_propagate<SEL_PACKED>(A, (hipStream_t)stream);
-    else
-        launch_propagate<SEL_REC>(A, (hipStream_t)stream);
+    hipLaunchKernelGGL(k_apply_seeds, dim3((unsigned)((n_seeds + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       cand, (long)Wm * Hm, (const uint2 *)seeds, n_seeds);
     return launched();
 }
 
@@ -2339,17 +2614,16 @@ int sad_jfa_seed(const float *rec, int sel_fmt, int n_slots, uint32_t *cand, int
         return SAD_ERR_ALIGN;
     const long P = (long)Wm * Hm;
     const hipStream_t hs = (hipStream_t)stream;
+    const SiteSrc src = src_of(rec);
     hipLaunchKernelGGL(k_fill_map, dim3((unsigned)((2 * P + 255) / 256)), dim3(256), 0, hs, (uint4 *)cand, 2 * P);
     if (n_slots > 0)
         for (int r = 0; r < JFA_KEEP; ++r) {
             if (sel_fmt == SEL_PACKED)
-                hipLaunchKernelGGL(k_jfa_seed_round<SEL_PACKED>, dim3((n_slots + 255) / 256), dim3(256), 0, hs,
-                                   (const float4 *)rec, (uint32_t)n_slots, (unsigned long long *)cand, W, H,
-                                   scale_of(W, H), mg, r);
+                hipLaunchKernelGGL(k_jfa_seed_round<SEL_PACKED>, dim3((n_slots + 255) / 256), dim3(256), 0, hs, src,
+                                   (uint32_t)n_slots, (unsigned long long *)cand, W, H, scale_of(W, H), mg, r);
             else
-                hipLaunchKernelGGL(k_jfa_seed_round<SEL_REC>, dim3((n_slots + 255) / 256), dim3(256), 0, hs,
-                                   (const float4 *)rec, (uint32_t)n_slots, (unsigned long long *)cand, W, H,
-                                   scale_of(W, H), mg, r);
+                hipLaunchKernelGGL(k_jfa_seed_round<SEL_REC>, dim3((n_slots + 255) / 256), dim3(256), 0, hs, src,
+                                   (uint32_t)n_slots, (unsigned long long *)cand, W, H, scale_of(W, H), mg, r);
         }
     hipLaunchKernelGGL(k_jfa_seed_finish, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, hs, (uint4 *)cand, P);
     return launched();
@@ -2378,12 +2652,13 @@ int sad_jfa_pass(const float *rec, int sel_fmt, int n_slots, const uint32_t *can
     if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(Wm, Hm);
+    const SiteSrc src = src_of(rec);
     if (sel_fmt == SEL_PACKED)
-        hipLaunchKernelGGL(k_jfa_pass<SEL_PACKED>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream,
-                           (const float4 *)rec, (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm,
-                           step, scale_of(W, H), mg.sx, mg.sy, g.tiles_x, g.nb);
+        hipLaunchKernelGGL(k_jfa_pass<SEL_PACKED>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
+                           (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm, step, scale_of(W, H),
+                           mg.sx, mg.sy, g.tiles_x, g.nb);
     else
-        hipLaunchKernelGGL(k_jfa_pass<SEL_REC>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
+        hipLaunchKernelGGL(k_jfa_pass<SEL_REC>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
                            (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm, step, scale_of(W, H),
                            mg.sx, mg.sy, g.tiles_x, g.nb);
     return launched();
@@ -2407,43 +2682,87 @@ int sad_topk_exact(const float *rec, int sel_fmt, int n_slots, uint32_t *cand_ou
     if (!aligned16(cand_out) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(Wm, Hm);
+    const SiteSrc src = src_of(rec);
     if (sel_fmt == SEL_PACKED)
-        hipLaunchKernelGGL(k_topk_exact<SEL_PACKED>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream,
-                           (const float4 *)rec, (uint32_t)n_slots, (uint4 *)cand_out, Wm, Hm, scale_of(W, H), mg.sx,
-                           mg.sy, g.tiles_x, g.nb);
+        hipLaunchKernelGGL(k_topk_exact<SEL_PACKED>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
+                           (uint32_t)n_slots, (uint4 *)cand_out, Wm, Hm, scale_of(W, H), mg.sx, mg.sy, g.tiles_x,
+                           g.nb);
     else
-        hipLaunchKernelGGL(k_topk_exact<SEL_REC>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream,
-                           (const float4 *)rec, (uint32_t)n_slots, (uint4 *)cand_out, Wm, Hm, scale_of(W, H), mg.sx,
-                           mg.sy, g.tiles_x, g.nb);
+        hipLaunchKernelGGL(k_topk_exact<SEL_REC>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
+                           (uint32_t)n_slots, (uint4 *)cand_out, Wm, Hm, scale_of(W, H), mg.sx, mg.sy, g.tiles_x,
+                           g.nb);
     return launched();
 }
 
-int sad_render_fwd(const float *rec, int n_slots, const uint32_t *cand, int W, int H, int cell, float *out_rgb,
-                   void *stream)
+int sad_topk_exact_at(const float *rec, int sel_fmt, int n_slots, const uint32_t *entries, int n_entries, int W, int H,
+                      int cell, uint32_t *out, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
         return rc;
-    if (n_slots < 0 || cell < 1)
+    if (n_slots < 0 || n_entries < 0 || cell < 1 || !valid_fmt(sel_fmt))
         return SAD_ERR_ARG;
-    if (W == 0 || H == 0)
+    if (W == 0 || H == 0 || n_entries == 0)
         return SAD_OK;
     MapGrid mg;
     int Wm, Hm;
     if (!map_grid(W, H, cell, mg, Wm, Hm))
         return SAD_ERR_ARG;
-    if ((!rec && n_slots > 0) || !cand || !out_rgb)
+    if ((!rec && n_slots > 0) || !entries || !out)
         return SAD_ERR_ARG;
-    if (!aligned16(cand) || !aligned16(rec))
+    if (!aligned16(out) || !aligned16(rec) || ((uintptr_t)entries & 3u))
         return SAD_ERR_ALIGN;
-    const TileGrid g = tile_grid(W, H);
-    hipLaunchKernelGGL(k_render_fwd, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
-                       (uint32_t)n_slots, (const uint4 *)cand, W, H, out_rgb, scale_of(W, H), mg, g.tiles_x, g.nb);
+    const unsigned nb = (unsigned)((n_entries + BLOCK - 1) / BLOCK);
+    const SiteSrc src = src_of(rec);
+    if (sel_fmt == SEL_PACKED)
+        hipLaunchKernelGGL(k_topk_exact_at<SEL_PACKED>, dim3(nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
+                           (uint32_t)n_slots, entries, n_entries, (uint4 *)out, Wm, Hm, scale_of(W, H), mg.sx, mg.sy);
+    else
+        hipLaunchKernelGGL(k_topk_exact_at<SEL_REC>, dim3(nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
+                           (uint32_t)n_slots, entries, n_entries, (uint4 *)out, Wm, Hm, scale_of(W, H), mg.sx, mg.sy);
     return launched();
 }
 
-int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H, int cell,
-                   float *grad, float *loss_sum, float *out_rgb, void *stream)
+int sad_render_fwd(const float *sites, int n_slots, int stride, const uint32_t *cand, int W, int H, float *out_rgb,
+                   void *stream)
+{
+    int rc;
+    if ((rc = check_sites(n_slots, stride)))
+        return rc;
+    return render_fwd_any(src_planes(sites, stride), sites, SEL_SOA, n_slots, cand, W, H, 1, out_rgb, stream);
+}
+
+int sad_render_fwd_rec(const float *rec, int n_slots, const uint32_t *cand, int W, int H, int cell, float *out_rgb,
+                       void *stream)
+{
+    return render_fwd_any(src_of(rec), rec, SEL_REC, n_slots, cand, W, H, cell, out_rgb, stream);
+}
+
+int sad_render_bwd(const float *sites, int n_slots, int stride, const uint32_t *cand, const float *target, int W,
+                   int H, float *grad, float *loss_sum, void *stream)
+{
+    int rc;
+    if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
+        return rc;
+    if (W == 0 || H == 0)
+        return SAD_OK;
+    if ((!sites && n_slots > 0) || !cand || !target || (!grad && n_slots > 0))
+        return SAD_ERR_ARG;
+    if (!aligned16(cand) || ((uintptr_t)sites & 3u) || ((uintptr_t)grad & 3u))
+        return SAD_ERR_ALIGN;
+    MapGrid mg;
+    int Wm, Hm;
+    map_grid(W, H, 1, mg, Wm, Hm);
+    const TileGrid g = tile_grid(W, H);
+    hipLaunchKernelGGL((k_render_bwd<SEL_SOA, GL_PLANES>), dim3(g.nb), dim3(PAIR_THREADS), 0, (hipStream_t)stream,
+                       src_planes(sites, stride), (uint32_t)n_slots, (const uint4 *)cand, target, W, H,
+                       GradOut{grad, (long)stride}, loss_sum, 0u, (float *)nullptr, scale_of(W, H), mg, g.tiles_x,
+                       g.nb);
+    return launched();
+}
+
+int sad_render_bwd_rec(const float *rec, int n_slots, const uint32_t *cand, const float *target, int W, int H,
+                       int cell, float *grad, float *loss_sum, float *out_rgb, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
@@ -2461,9 +2780,9 @@ int sad_render_bwd(const float *rec, int n_slots, const uint32_t *cand, const fl
     if (!aligned16(cand) || !aligned16(grad) || !aligned16(rec))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
-    hipLaunchKernelGGL(k_render_bwd, dim3(g.nb), dim3(PAIR_THREADS), 0, (hipStream_t)stream, (const float4 *)rec,
-                       (uint32_t)n_slots, (const uint4 *)cand, target, W, H, grad, loss_sum, out_rgb, scale_of(W, H),
-                       mg, g.tiles_x, g.nb);
+    hipLaunchKernelGGL((k_render_bwd<SEL_REC, GL_REC>), dim3(g.nb), dim3(PAIR_THREADS), 0, (hipStream_t)stream,
+                       src_of(rec), (uint32_t)n_slots, (const uint4 *)cand, target, W, H, GradOut{grad, 0}, loss_sum,
+                       (uint32_t)(SAD_LOSS_SLOTS - 1), out_rgb, scale_of(W, H), mg, g.tiles_x, g.nb);
     return launched();
 }
 
@@ -2486,40 +2805,22 @@ int sad_densify_stats(const float *rec, int n_slots, const uint32_t *cand, const
     if (!aligned16(cand) || !aligned16(rec) || !aligned16(stats))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(W, H);
-    hipLaunchKernelGGL(k_densify_stats, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, (const float4 *)rec,
+    hipLaunchKernelGGL(k_densify_stats, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src_of(rec),
                        (uint32_t)n_slots, (const uint4 *)cand, target, W, H, stats, scale_of(W, H), mg, g.tiles_x,
                        g.nb);
     return launched();
 }
 
-int sad_adam_step(float *sites, float *m, float *v, float *grad, float *rec, uint32_t *packed, int n_slots, int stride,
-                  int step, int n_pixels, int W, int H, const sad_adam_cfg *cfg, void *stream)
+int sad_adam_step(float *sites, float *m, float *v, float *grad, int n_slots, int stride, int step, int n_pixels,
+                  const sad_adam_cfg *cfg, void *stream)
 {
-    int rc;
-    if ((rc = check_image(W, H)) || (rc = check_sites(n_slots, stride)))
-        return rc;
-    if (!sites || !m || !v || !grad || !cfg || step < 1 || n_pixels < 1)
-        return SAD_ERR_ARG;
-    if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f && cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f && cfg->eps >= 0.0f))
-        return SAD_ERR_ARG;
-    if (!aligned16(grad) || !aligned16(rec) || !aligned16(packed))
-        return SAD_ERR_ALIGN;
-    if (n_slots == 0)
-        return SAD_OK;
-    AdamArgs A;
-    for (int j = 0; j < SAD_NPARAM; ++j)
-        A.lr[j] = cfg->lr[j];
-    A.b1 = cfg->beta1;
-    A.b2 = cfg->beta2;
-    A.eps = cfg->eps;
-    A.ibc1 = (float)(1.0 / (1.0 - __builtin_pow((double)cfg->beta1, (double)step)));
-    A.ibc2 = (float)(1.0 / (1.0 - __builtin_pow((double)cfg->beta2, (double)step)));
-    A.inv_p = 1.0f / (float)n_pixels;
-    A.W = (float)W;
-    A.H = (float)H;
-    hipLaunchKernelGGL(k_adam, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, m, v, grad,
-                       (float4 *)rec, (uint4 *)packed, n_slots, stride, A);
-    return launched();
+    return adam_any(sites, m, v, grad, GL_PLANES, nullptr, nullptr, n_slots, stride, step, n_pixels, cfg, stream);
+}
+
+int sad_adam_step_rec(float *sites, float *m, float *v, float *grad, float *rec, uint32_t *packed, int n_slots,
+                      int stride, int step, int n_pixels, const sad_adam_cfg *cfg, void *stream)
+{
+    return adam_any(sites, m, v, grad, GL_REC, rec, packed, n_slots, stride, step, n_pixels, cfg, stream);
 }
 
 int sad_eval_encode(const float *sites, int n_slots, int stride, int W, int H, uint32_t *words, float *header,

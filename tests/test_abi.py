@@ -30,9 +30,31 @@ def _declared():
 
 def test_header_declares_the_hot_path():
     names = _declared()
-    for fn in ("sad_topk_propagate", "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_topk_exact",
+    for fn in ("sad_topk_propagate", "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_densify_prune",
+               "sad_topk_propagate_rec", "sad_render_fwd_rec", "sad_render_bwd_rec", "sad_adam_step_rec",
+               "sad_densify_prune_stats", "sad_apply_seeds", "sad_topk_exact", "sad_topk_exact_at",
                "sad_site_records", "sad_abi_version", "sad_status_string"):
         assert fn in names
+
+
+def test_header_signatures_of_the_site_buffer_calls():
+    """The five calls of the iteration on the site buffer take the argument lists
+    of the boundary: site planes with their stride, gradient planes, a scalar loss."""
+    txt = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    sig = lambda fn: re.sub(r"\s+", " ", re.search(r"int " + fn + r"\((.*?)\);", txt, flags=re.S).group(1))
+    assert sig("sad_topk_propagate") == ("const float *sites, int n_slots, int stride, const uint32_t *cand_in, "
+                                         "uint32_t *cand_out, int W, int H, int jump, uint32_t pass_index, "
+                                         "uint32_t seed, int n_inject, void *stream")
+    assert sig("sad_render_fwd") == ("const float *sites, int n_slots, int stride, const uint32_t *cand, int W, "
+                                     "int H, float *out_rgb, void *stream")
+    assert sig("sad_render_bwd") == ("const float *sites, int n_slots, int stride, const uint32_t *cand, "
+                                     "const float *target, int W, int H, float *grad, float *loss_sum, "
+                                     "void *stream")
+    assert sig("sad_adam_step") == ("float *sites, float *m, float *v, float *grad, int n_slots, int stride, "
+                                    "int step, int n_pixels, const sad_adam_cfg *cfg, void *stream")
+    assert sig("sad_densify_prune") == ("float *sites, float *m, float *v, float *removal, int *n_slots, "
+                                        "int capacity, int stride, uint32_t *cand, int W, int H, "
+                                        "const float *target, const sad_budget_cfg *cfg, uint64_t seed")
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -42,7 +64,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.sad_abi_version() == 6
+    assert L.sad_abi_version() == 7
     assert L.sad_status_string(0) == b"ok"
     assert L.sad_status_string(ERR_ALIGN) == b"misaligned pointer"
     assert L.sad_status_string(12345) == b"unknown status"
@@ -53,7 +75,7 @@ Q = 0x90000
 
 
 def test_propagate_rejects_bad_arguments(L):
-    f = L.sad_topk_propagate
+    f = L.sad_topk_propagate_rec
     ok = dict(rec=P, fmt=0, n=4, a=P, b=Q, W=16, H=16, cell=1, jump=1, pidx=0, seed=0, m=4)
 
     def call(**kw):
@@ -89,20 +111,79 @@ def test_propagate_rejects_bad_arguments(L):
     assert call(fmt=1, rec=P + 8) == ERR_ALIGN
 
 
+def test_site_buffer_calls_reject_bad_arguments(L):
+    f = L.sad_topk_propagate
+    ok = dict(s=P, n=4, st=8, a=P, b=Q, W=16, H=16, jump=1, pidx=0, seed=0, m=4)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["s"], a["n"], a["st"], a["a"], a["b"], a["W"], a["H"], a["jump"], a["pidx"], a["seed"], a["m"],
+                 None)
+
+    assert call(n=9) == ERR_ARG          # n_slots > stride
+    assert call(st=0) == ERR_ARG
+    assert call(jump=0) == ERR_ARG
+    assert call(m=17) == ERR_ARG
+    assert call(s=0) == ERR_ARG
+    assert call(b=P + 32) == ERR_ARG     # overlapping maps
+    assert call(a=P + 4) == ERR_ALIGN
+    assert call(s=P + 4, W=0) == 0       # the planes need only float alignment
+    assert call(W=0) == 0
+    assert call(H=65536) == ERR_ARG
+    R, F = L.sad_render_fwd, L.sad_render_bwd
+    assert R(P, 4, 8, P + 8, 16, 16, Q, None) == ERR_ALIGN
+    assert R(P, 4, 8, 0, 16, 16, Q, None) == ERR_ARG
+    assert R(P, 9, 8, P, 16, 16, Q, None) == ERR_ARG
+    assert R(0, 4, 8, P, 16, 16, Q, None) == ERR_ARG
+    assert R(P, 4, 8, P, 0, 16, Q, None) == 0
+    assert R(P, 4, 8, P, 65536, 1, Q, None) == ERR_ARG
+    assert F(P, 4, 8, P, 0, 16, 16, Q, None, None) == ERR_ARG     # target NULL
+    assert F(P, 4, 8, P + 4, Q, 16, 16, Q, None, None) == ERR_ALIGN
+    assert F(P, 4, 8, P, Q, 16, 16, Q + 2, None, None) == ERR_ALIGN  # grad planes: float alignment
+    assert F(P, 4, 8, P, Q, 16, 16, 0, None, None) == ERR_ARG     # grad NULL
+    assert F(P, 9, 8, P, Q, 16, 16, Q, None, None) == ERR_ARG
+    assert F(P, 4, 8, P, Q, 1, 65536, Q, None, None) == ERR_ARG
+    cfg = sad.AdamConfig().to_c(16, 16)
+    A = L.sad_adam_step
+    assert A(P, P, P, P, 4, 8, 0, 10, ctypes.byref(cfg), None) == ERR_ARG   # step 0
+    assert A(P, P, P, P, 4, 8, 1, 0, ctypes.byref(cfg), None) == ERR_ARG   # no pixels
+    assert A(P, P, P, P, 4, 8, 1, 10, None, None) == ERR_ARG
+    assert A(P, P, P, 0, 4, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ARG
+    assert A(P, P, P, P, 9, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ARG
+    assert A(P, P, P, P, 0, 8, 1, 10, ctypes.byref(cfg), None) == 0        # no slots: no-op
+    nobox = sad.AdamConfig().to_c(16, 16)
+    nobox.x_max = 0.0
+    assert A(P, P, P, P, 4, 8, 1, 10, ctypes.byref(nobox), None) == ERR_ARG  # no clamp box
+
+
 def test_render_and_adam_reject_bad_arguments(L):
-    assert L.sad_render_fwd(P, 4, P + 8, 16, 16, 1, Q, None) == ERR_ALIGN
-    assert L.sad_render_fwd(P + 8, 4, P, 16, 16, 1, Q, None) == ERR_ALIGN
-    assert L.sad_render_fwd(P, 4, 0, 16, 16, 1, Q, None) == ERR_ARG
-    assert L.sad_render_fwd(P, -1, P, 16, 16, 1, Q, None) == ERR_ARG
-    assert L.sad_render_fwd(0, 4, P, 16, 16, 1, Q, None) == ERR_ARG
-    assert L.sad_render_fwd(P, 4, P, 0, 16, 1, Q, None) == 0
-    assert L.sad_render_fwd(P, 4, P, 16, 16, 0, Q, None) == ERR_ARG  # cell 0
-    assert L.sad_render_fwd(P, 4, P, 65536, 1, 1, Q, None) == ERR_ARG  # beyond SAD_MAX_DIM
-    assert L.sad_render_bwd(P, 4, P, Q, 1, 65536, 1, Q, None, None, None) == ERR_ARG
-    assert L.sad_render_bwd(P, 4, P, 0, 16, 16, 1, Q, None, None, None) == ERR_ARG  # target NULL
-    assert L.sad_render_bwd(P, 4, P + 4, Q, 16, 16, 1, Q, None, None, None) == ERR_ALIGN
-    assert L.sad_render_bwd(P, 4, P, Q, 16, 16, 1, Q + 4, None, None, None) == ERR_ALIGN  # grad records
-    assert L.sad_render_bwd(P, 4, P, Q, 16, 16, 0, Q, None, None, None) == ERR_ARG  # cell 0
+    assert L.sad_render_fwd_rec(P, 4, P + 8, 16, 16, 1, Q, None) == ERR_ALIGN
+    assert L.sad_render_fwd_rec(P + 8, 4, P, 16, 16, 1, Q, None) == ERR_ALIGN
+    assert L.sad_render_fwd_rec(P, 4, 0, 16, 16, 1, Q, None) == ERR_ARG
+    assert L.sad_render_fwd_rec(P, -1, P, 16, 16, 1, Q, None) == ERR_ARG
+    assert L.sad_render_fwd_rec(0, 4, P, 16, 16, 1, Q, None) == ERR_ARG
+    assert L.sad_render_fwd_rec(P, 4, P, 0, 16, 1, Q, None) == 0
+    assert L.sad_render_fwd_rec(P, 4, P, 16, 16, 0, Q, None) == ERR_ARG  # cell 0
+    assert L.sad_render_fwd_rec(P, 4, P, 65536, 1, 1, Q, None) == ERR_ARG  # beyond SAD_MAX_DIM
+    B = L.sad_render_bwd_rec
+    assert B(P, 4, P, Q, 1, 65536, 1, Q, None, None, None) == ERR_ARG
+    assert B(P, 4, P, 0, 16, 16, 1, Q, None, None, None) == ERR_ARG  # target NULL
+    assert B(P, 4, P + 4, Q, 16, 16, 1, Q, None, None, None) == ERR_ALIGN
+    assert B(P, 4, P, Q, 16, 16, 1, Q + 4, None, None, None) == ERR_ALIGN  # grad records
+    assert B(P, 4, P, Q, 16, 16, 0, Q, None, None, None) == ERR_ARG  # cell 0
+    X = L.sad_topk_exact_at
+    assert X(P, 0, 4, P, -1, 16, 16, 1, Q, None) == ERR_ARG
+    assert X(P, 0, 4, P + 2, 4, 16, 16, 1, Q, None) == ERR_ALIGN
+    assert X(P, 0, 4, P, 4, 16, 16, 1, Q + 4, None) == ERR_ALIGN
+    assert X(P, 0, 4, P, 0, 16, 16, 1, Q, None) == 0                # no entries: no-op
+    assert X(P, 2, 4, P, 4, 16, 16, 1, Q, None) == ERR_ARG          # unknown site format
+    S = L.sad_apply_seeds
+    assert S(P, 16, 16, 1, P, -1, None) == ERR_ARG
+    assert S(P, 16, 16, 0, P, 4, None) == ERR_ARG
+    assert S(P + 4, 16, 16, 1, P, 4, None) == ERR_ALIGN
+    assert S(P, 16, 16, 1, P + 4, 4, None) == ERR_ALIGN
+    assert S(0, 16, 16, 1, P, 4, None) == ERR_ARG
+    assert S(P, 16, 16, 1, P, 0, None) == 0                         # no pairs: no-op
     assert L.sad_topk_exact(P, 0, 4, P + 4, 16, 16, 1, None) == ERR_ALIGN
     assert L.sad_topk_exact(P, 0, -1, P, 16, 16, 1, None) == ERR_ARG
     assert L.sad_topk_exact(P, 0, 4, P, 16, 16, 0, None) == ERR_ARG
@@ -116,17 +197,17 @@ def test_render_and_adam_reject_bad_arguments(L):
     assert L.sad_site_records(P, 9, 8, P, None) == ERR_ARG
     assert L.sad_site_records(0, 4, 8, P, None) == ERR_ARG
     assert L.sad_site_records(0, 0, 8, 0, None) == 0  # no slots: no-op
-    cfg = sad.AdamConfig().to_c()
-    A = L.sad_adam_step
-    assert A(P, P, P, P, P, None, 4, 8, 0, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # step 0
-    assert A(P, P, P, P, P, None, 4, 8, 1, 0, 4, 4, ctypes.byref(cfg), None) == ERR_ARG   # no pixels
-    assert A(P, P, P, P, P, None, 4, 8, 1, 10, 4, 4, None, None) == ERR_ARG
-    assert A(P, P, P, P + 4, P, None, 4, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ALIGN
-    assert A(P, P, P, P, P + 4, None, 4, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ALIGN
-    bad = sad.AdamConfig(beta1=1.0).to_c()
-    assert A(P, P, P, P, P, None, 4, 8, 1, 10, 4, 4, ctypes.byref(bad), None) == ERR_ARG
-    assert A(P, P, P, P, None, None, 0, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == 0  # no slots: no-op
-    assert A(P, P, P, P, P, P + 4, 4, 8, 1, 10, 4, 4, ctypes.byref(cfg), None) == ERR_ALIGN  # packed
+    cfg = sad.AdamConfig().to_c(4, 4)
+    A = L.sad_adam_step_rec
+    assert A(P, P, P, P, P, None, 4, 8, 0, 10, ctypes.byref(cfg), None) == ERR_ARG   # step 0
+    assert A(P, P, P, P, P, None, 4, 8, 1, 0, ctypes.byref(cfg), None) == ERR_ARG   # no pixels
+    assert A(P, P, P, P, P, None, 4, 8, 1, 10, None, None) == ERR_ARG
+    assert A(P, P, P, P + 4, P, None, 4, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ALIGN
+    assert A(P, P, P, P, P + 4, None, 4, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ALIGN
+    bad = sad.AdamConfig(beta1=1.0).to_c(4, 4)
+    assert A(P, P, P, P, P, None, 4, 8, 1, 10, ctypes.byref(bad), None) == ERR_ARG
+    assert A(P, P, P, P, None, None, 0, 8, 1, 10, ctypes.byref(cfg), None) == 0  # no slots: no-op
+    assert A(P, P, P, P, P, P + 4, 4, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ALIGN  # packed
 
 
 def test_jfa_entry_points_reject_bad_arguments(L):
@@ -164,7 +245,7 @@ def test_densify_entry_points_reject_bad_arguments(L):
     assert D(P, 4, P, Q, 16, 16, 0, Q, None) == ERR_ARG     # cell 0
     cfg = sad.BudgetConfig().to_c()
     n = ctypes.c_int(4)
-    F = L.sad_densify_prune
+    F = L.sad_densify_prune_stats
     assert F(None, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None, None, 0, None) == ERR_ARG
     assert F(P, P, P, 8, 8, None, P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None, None, 0, None) == ERR_ARG
     assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 1, P, None, None, None, None, 0, None) == ERR_ARG
@@ -172,6 +253,16 @@ def test_densify_entry_points_reject_bad_arguments(L):
     assert F(P, P, P, 8, 9, ctypes.byref(n), P, P, P, 4, 4, 1, P, ctypes.byref(cfg), None, None, None, 0, None) == ERR_ARG
     assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 0, 4, 1, P, ctypes.byref(cfg), None, None, None, 0, None) == ERR_ARG
     assert F(P, P, P, 8, 8, ctypes.byref(n), P, P, P, 4, 4, 0, P, ctypes.byref(cfg), None, None, None, 0, None) == ERR_ARG
+    assert n.value == 4
+    G = L.sad_densify_prune
+    seed = ctypes.c_uint64(7)
+    assert G(None, P, P, P, ctypes.byref(n), 8, 8, P, 4, 4, P, ctypes.byref(cfg), seed) == ERR_ARG
+    assert G(P, P, P, P, None, 8, 8, P, 4, 4, P, ctypes.byref(cfg), seed) == ERR_ARG
+    assert G(P, P, P, P, ctypes.byref(n), 8, 8, None, 4, 4, P, ctypes.byref(cfg), seed) == ERR_ARG  # cand
+    assert G(P, P, P, P, ctypes.byref(n), 3, 8, P, 4, 4, P, ctypes.byref(cfg), seed) == ERR_ARG  # capacity < n
+    assert G(P, P, P, P, ctypes.byref(n), 9, 8, P, 4, 4, P, ctypes.byref(cfg), seed) == ERR_ARG  # capacity > stride
+    assert G(P, P, P, P, ctypes.byref(n), 8, 8, P, 0, 4, P, ctypes.byref(cfg), seed) == ERR_ARG
+    assert G(P, P, P, P, ctypes.byref(n), 8, 8, P, 4, 4, P, None, seed) == ERR_ARG
     assert n.value == 4
 
 
@@ -200,7 +291,10 @@ def test_python_binding_refuses_cpu_tensors():
     import torch
     s = torch.zeros((10, 4))
     with pytest.raises(ValueError):
-        sad.render_fwd(torch.zeros((4, 16)), 4, torch.zeros((2, 2, 8), dtype=torch.int32), 2, 2,
+        sad.render_fwd_rec(torch.zeros((4, 16)), 4, torch.zeros((2, 2, 8), dtype=torch.int32), 2, 2,
+                           torch.zeros((2, 2, 3)))
+    with pytest.raises(ValueError):
+        sad.render_fwd(torch.zeros((10, 4)), 4, torch.zeros((2, 2, 8), dtype=torch.int32), 2, 2,
                        torch.zeros((2, 2, 3)))
     with pytest.raises(ValueError):
         sad.site_records(s, 4, torch.zeros((4, 16)))

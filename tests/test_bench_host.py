@@ -20,9 +20,16 @@ def test_more_than_one_gpu_is_refused():
 def test_byte_and_op_models_at_kodak768():
     P, N, M = 768 * 512, 50_000, 4
     b = bench.algorithmic_bytes(P, N)
-    assert b["fwd_bwd"] == 56 * P + 152 * N == 29_620_096
-    assert b["propagate"] == 64 * P + 32 * N
-    assert b["adam"] == 384 * N
+    # compulsory bytes per call: propagate 64 P + 24 N, forward 44 P + 40 N,
+    # backward 44 P + 84 N, Adam 324 N; a step is 152 P + 472 N
+    assert b["fwd_bwd"] == 88 * P + 124 * N
+    assert b["propagate"] == 64 * P + 24 * N
+    assert b["adam"] == 324 * N
+    assert b["fwd"] == 44 * P + 40 * N
+    assert b["propagate"] + b["fwd_bwd"] + b["adam"] == bench.step_bytes(P, N) == 152 * P + 472 * N
+    # 83.4 MB per kodak768 iteration, 699.4 MB per img2048 iteration
+    assert abs(bench.step_bytes(P, N) / 1e6 - 83.37) < 0.01
+    assert abs(bench.step_bytes(2048 * 2048, 131_072) / 1e6 - 699.4) < 0.1
     o = bench.algorithmic_ops(P, N, M)
     assert o["propagate"] == P * 44 * 30
     assert o["fwd_bwd"] == P * 650

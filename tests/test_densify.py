@@ -238,7 +238,7 @@ def test_host_densify_matches_oracle(orc, seed, cfg, cell):
     case = _random_budget_case(seed, W, H, n, cap, cell=cell)
     mine = [a.copy() for a in case]
     ref = [a.copy() for a in case]
-    got = sad.densify_prune(mine[0], mine[1], mine[2], n, cap, mine[3], mine[4], mine[5], W, H, mine[6], cfg,
+    got = sad.densify_prune_stats(mine[0], mine[1], mine[2], n, cap, mine[3], mine[4], mine[5], W, H, mine[6], cfg,
                             cell=cell)
     f32 = lambda x: float(np.float32(x))  # the C struct holds float32 constants
     want = orc_densify(ref[0], ref[1], ref[2], n, cap, ref[3], ref[4], ref[5], W, H, ref[6],
@@ -262,7 +262,7 @@ def test_host_densify_matches_oracle_at_threaded_sizes(orc):
     cfg = sad.BudgetConfig(split_frac=0.25, prune_frac=0.25)
     mine = [a.copy() for a in case]
     ref = [a.copy() for a in case]
-    got = sad.densify_prune(mine[0], mine[1], mine[2], n, cap, mine[3], mine[4], mine[5], W, H, mine[6], cfg)
+    got = sad.densify_prune_stats(mine[0], mine[1], mine[2], n, cap, mine[3], mine[4], mine[5], W, H, mine[6], cfg)
     f32 = lambda x: float(np.float32(x))
     want = orc_densify(ref[0], ref[1], ref[2], n, cap, ref[3], ref[4], ref[5], W, H, ref[6],
                        f32(cfg.split_frac), f32(cfg.prune_frac), f32(cfg.alpha), f32(cfg.min_mass), f32(cfg.shrink))
@@ -280,37 +280,82 @@ def test_host_densify_rejects_bad_arguments():
     for bad in (sad.BudgetConfig(split_frac=-0.1), sad.BudgetConfig(prune_frac=1.5), sad.BudgetConfig(shrink=0.0),
                 sad.BudgetConfig(min_mass=-1.0)):
         with pytest.raises(sad.SadError):
-            sad.densify_prune(S, m, v, n, cap, stats, removal, cand, W, H, T, bad)
+            sad.densify_prune_stats(S, m, v, n, cap, stats, removal, cand, W, H, T, bad)
     with pytest.raises(sad.SadError):
-        sad.densify_prune(S, m, v, n, n - 1, stats, removal, cand, W, H, T)  # capacity < n
+        sad.densify_prune_stats(S, m, v, n, n - 1, stats, removal, cand, W, H, T)  # capacity < n
     with pytest.raises(ValueError):
-        sad.densify_prune(S, m, v, n, cap, stats[:-1], removal, cand, W, H, T)
+        sad.densify_prune_stats(S, m, v, n, cap, stats[:-1], removal, cand, W, H, T)
     with pytest.raises(TypeError):
-        sad.densify_prune(S.astype(np.float64), m, v, n, cap, stats, removal, cand, W, H, T)
+        sad.densify_prune_stats(S.astype(np.float64), m, v, n, cap, stats, removal, cand, W, H, T)
 
 
 @pytest.mark.parametrize("cell", [1, 3])
 def test_host_densify_seed_pairs_reproduce_the_map(cell):
-    """With the map left on the device, the routine reports the entries it seeds;
-    applying those pairs in order (a later pair of an entry wins) gives exactly the
-    map it writes when it is handed the map, and everything else is the same."""
+    """With the map left on the device, the routine reports the entries it seeds,
+    grouped by entry; applying them in order with the seeding rule (the last place
+    takes the ID unless the list already names it) gives exactly the map it writes
+    when it is handed the map, and everything else is the same."""
     import oracle
     W, H, n, cap = 48, 40, 300, 330
     case = _random_budget_case(8, W, H, n, cap, cell=cell)
     cfg = sad.BudgetConfig(split_frac=0.2, prune_frac=0.05)
     a = [x.copy() for x in case]
     b = [x.copy() for x in case]
-    ra = sad.densify_prune(a[0], a[1], a[2], n, cap, a[3], a[4], a[5], W, H, a[6], cfg, cell=cell)
-    rb = sad.densify_prune(b[0], b[1], b[2], n, cap, b[3], b[4], None, W, H, b[6], cfg, cell=cell, want_seeds=True)
+    ra = sad.densify_prune_stats(a[0], a[1], a[2], n, cap, a[3], a[4], a[5], W, H, a[6], cfg, cell=cell)
+    rb = sad.densify_prune_stats(b[0], b[1], b[2], n, cap, b[3], b[4], None, W, H, b[6], cfg, cell=cell, want_seeds=True)
     assert ra == rb[:4] and ra[1] > 0
     for x, y in zip(a[:3], b[:3]):
         assert np.array_equal(x, y)
     seeds = rb[4]
     assert seeds.shape[1] == 2 and 0 < len(seeds) <= 5 * ra[1]
+    e = seeds[:, 0].astype(np.int64)
+    assert (np.diff(e) >= 0).all(), "pairs grouped by entry"
     m = case[5].copy().reshape(-1, 8)
     for e, i in seeds:
-        m[e, 7] = i
+        if not (m[e] == i).any():
+            m[e, 7] = i
     assert np.array_equal(m.reshape(a[5].shape), a[5])
+
+
+@pytest.mark.parametrize("cell", [1, 2])
+def test_densify_keeps_lists_distinct(cell):
+    """A second child that takes a slot pruned in the same call keeps that slot's
+    ID; lists near the pruned site's old place still name it, and one of them can
+    be among the lists the child is seeded into.  Seeding skips such a list, so
+    every list keeps distinct IDs (library routine and oracle alike)."""
+    import oracle.densify as od
+    W, H, n, cap = 40, 32, 60, 60
+    Wm, Hm = -(-W // cell), -(-H // cell)
+    rng = np.random.default_rng(3)
+    S = synth.random_sites(n, W, H, 11, cap)
+    stats = np.zeros((cap, 8), dtype=np.float32)
+    stats[:n, 0] = 4.0
+    stats[:n, 1] = rng.uniform(0.1, 1.0, n)
+    stats[5, 1] = 100.0   # site 5 splits first, along +x (isotropic stats: no covariance)
+    removal = rng.uniform(1.0, 2.0, cap).astype(np.float32)
+    removal[7] = 0.0      # site 7 is pruned first; the second child of site 5 takes its slot
+    S[0, 5], S[1, 5] = 20.5, 16.5
+    # every list near site 5 names site 7 (the stale ID of the slot child B takes)
+    cand = np.full((Hm, Wm, 8), 0xFFFFFFFF, dtype=np.uint32)
+    cand[:, :, 0] = 7
+    cand[:, :, 1] = 5
+    T = (synth.pixel_noise(W, H, 4, 0.2) + 0.5).astype(np.float32)
+    cfg = dict(split_frac=1.5 / n, prune_frac=1.5 / n, alpha=0.5, min_mass=1.0, shrink=0.85)
+    for impl in ("library", "oracle"):
+        a = [x.copy() for x in (S, np.zeros((10, cap), np.float32), np.zeros((10, cap), np.float32), cand)]
+        if impl == "library":
+            res = sad.densify_prune_stats(a[0], a[1], a[2], n, cap, stats, removal, a[3], W, H, T,
+                                          sad.BudgetConfig(**cfg), cell=cell)
+            assert res[1] == 1 and res[2] == 1
+        else:
+            res = od.densify_prune(a[0], a[1], a[2], n, cap, stats, removal, a[3], W, H, T, cell=cell, **cfg)
+            assert res[1] == 1 and res[2] == 1
+        assert a[0][0, 7] >= 0, "slot 7 holds the second child"
+        L = a[3].reshape(-1, 8)
+        for lst in L:
+            v = lst[lst != 0xFFFFFFFF]
+            assert len(set(v.tolist())) == v.size, f"{impl}: duplicate IDs in a list"
+        assert (L[:, 7] == 0xFFFFFFFF).all(), f"{impl}: every seeded list already named slot 7"
 
 
 def test_host_densify_rejects_a_short_seed_buffer():
@@ -322,9 +367,45 @@ def test_host_densify_rejects_a_short_seed_buffer():
     ns, nsp, npr, nseed = ctypes.c_int(n), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_long(0)
     seeds = np.zeros((10, 2), dtype=np.uint32)  # 5 * floor(0.2 * A) pairs are needed
     p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
-    rc = sad.lib().sad_densify_prune(p(S), p(m), p(v), cap, cap, ctypes.byref(ns), p(stats), p(removal), None, W, H,
+    rc = sad.lib().sad_densify_prune_stats(p(S), p(m), p(v), cap, cap, ctypes.byref(ns), p(stats), p(removal), None, W, H,
                                      1, p(T), ctypes.byref(c), ctypes.byref(nsp), ctypes.byref(npr), p(seeds),
                                      len(seeds), ctypes.byref(nseed))
     assert rc == sad.SAD_ERR_ARG and ns.value == n
     for x, y in zip((S, m, v), before):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("seed,cfg,W,H", [
+    (21, sad.BudgetConfig(), 48, 40),
+    (22, sad.BudgetConfig(split_frac=0.15, prune_frac=0.1), 61, 37),
+    (23, sad.BudgetConfig(split_frac=0.1, prune_frac=0.05, min_mass=1e6), 40, 48),  # gradient axis throughout
+    (24, sad.BudgetConfig(split_frac=0.2, prune_frac=0.0), 48, 40),                # runs out of slots
+])
+def test_site_buffer_densify_matches_the_oracle(orc, seed, cfg, W, H):
+    """sad_densify_prune derives the statistics itself (on the host, in float64,
+    over the per-pixel map) and resets the removal accumulator.  Reference: the
+    oracle's statistics (rounded to float32, the width the rules read) through the
+    oracle's rules.  The statistics only choose and place splits, so equal
+    results pin both."""
+    n, cap = 300, 330
+    S, m, v, _, removal, cand, T = _random_budget_case(seed, W, H, n, cap)
+    mine = [a.copy() for a in (S, m, v, removal, cand)]
+    ref = [a.copy() for a in (S, m, v, removal, cand)]
+    ns, rc = sad.densify_prune(mine[0], mine[1], mine[2], mine[3], n, cap, mine[4], W, H, T, cfg, seed=seed)
+    stats = orc.densify_stats(S, n, cand, T, W, H).astype(np.float32)
+    f32 = lambda x: float(np.float32(x))
+    want = orc_densify(ref[0], ref[1], ref[2], n, cap, stats, ref[3], ref[4], W, H, T, f32(cfg.split_frac),
+                       f32(cfg.prune_frac), f32(cfg.alpha), f32(cfg.min_mass), f32(cfg.shrink))
+    assert ns == want[0]
+    assert (rc == sad.SAD_ERR_CAPACITY) == want[3]
+    assert np.allclose(mine[0][:2], ref[0][:2], atol=2e-5)
+    assert np.allclose(mine[0][2:], ref[0][2:], atol=1e-6, equal_nan=True)
+    assert np.array_equal(mine[1], ref[1]) and np.array_equal(mine[2], ref[2])
+    assert np.array_equal(mine[4], ref[4])
+    assert np.all(mine[3][:ns] == 0), "removal accumulator reset"
+    assert want[1] > 0 or cfg.split_frac == 0
+    # the seed is reserved: another seed gives the same result
+    again = [a.copy() for a in (S, m, v, removal, cand)]
+    sad.densify_prune(again[0], again[1], again[2], again[3], n, cap, again[4], W, H, T, cfg, seed=seed + 99)
+    for x, y in zip(again, mine):
+        assert np.array_equal(x, y, equal_nan=True)

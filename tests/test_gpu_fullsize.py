@@ -48,7 +48,7 @@ def test_propagate_full_size_sampled(orc, name, jump):
     sad.site_records(S_d, n, rec)
     a = to_dev(cin)
     b = sad.new_map(W, H, a.device)
-    sad.topk_propagate(rec, n, a, b, W, H, jump, 4242, synth.SEED_INJECT, wl.n_inject)
+    sad.topk_propagate_rec(rec, n, a, b, W, H, jump, 4242, synth.SEED_INJECT, wl.n_inject)
     torch.cuda.synchronize()
     got = map_to_host(b).reshape(-1, 8)
     del a, b
@@ -77,7 +77,7 @@ def test_fused_forward_backward_full_size(orc, name):
     g_d = sad.new_grad(S.shape[1], S_d.device)
     loss = sad.new_loss(S_d.device)
     rgb = torch.empty((H, W, 3), dtype=torch.float32, device=S_d.device)
-    sad.render_bwd(rec, n, c_d, t_d, W, H, g_d, loss, rgb)
+    sad.render_bwd_rec(rec, n, c_d, t_d, W, H, g_d, loss, rgb)
     torch.cuda.synchronize()
     got_rgb = rgb.cpu().numpy().reshape(-1, 3)
     got_g = sad.grad_planes(g_d).cpu().numpy().astype(np.float64)
@@ -107,7 +107,7 @@ def test_adam_full_size(orc, name):
     g_d[:, :11].copy_(torch.from_numpy(G).t())
     rec = sad.new_records(S.shape[1], S_d.device)
     cfg = sad.AdamConfig()
-    sad.adam_step(S_d, m_d, v_d, g_d, n, 3, W * H, W, H, cfg, rec=rec)
+    sad.adam_step_rec(S_d, m_d, v_d, g_d, n, 3, W * H, W, H, cfg, rec=rec)
     torch.cuda.synchronize()
     p64, m64, v64, g64 = (a.astype(np.float64) for a in (S, m, v, G))
     f32 = lambda x: float(np.float32(x))
@@ -140,7 +140,7 @@ def test_kodak768_schedule_each_pass(orc):
         print(f"pass {t} jump {k}", flush=True)
         a = to_dev(cur)
         b = sad.new_map(W, H, a.device)
-        sad.topk_propagate(rec, n, a, b, W, H, k, t, synth.SEED_INJECT, wl.n_inject)
+        sad.topk_propagate_rec(rec, n, a, b, W, H, k, t, synth.SEED_INJECT, wl.n_inject)
         torch.cuda.synchronize()
         got = map_to_host(b)
         ref = orc.propagate(S, n, cur, W, H, k, t, synth.SEED_INJECT, wl.n_inject)

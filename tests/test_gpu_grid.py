@@ -71,7 +71,7 @@ def test_grid_propagate(orc, W, H, n, c, jump, m):
     g = _rec(S, n)
     a = to_dev(cin)
     b = sad.new_map(W, H, a.device, cell=c)
-    sad.topk_propagate(g, n, a, b, W, H, jump, 999, 31, m, cell=c)
+    sad.topk_propagate_rec(g, n, a, b, W, H, jump, 999, 31, m, cell=c)
     torch.cuda.synchronize()
     got = map_to_host(b)
     ref = orc.propagate(S, n, cin, W, H, jump, 999, 31, m, cell=c)
@@ -93,7 +93,7 @@ def test_grid_propagate_large_map(orc, jump):
     g = _rec(S, n)
     a = to_dev(cin)
     b = sad.new_map(W, H, a.device, cell=c)
-    sad.topk_propagate(g, n, a, b, W, H, jump, 321, 9, 4, cell=c)
+    sad.topk_propagate_rec(g, n, a, b, W, H, jump, 321, 9, 4, cell=c)
     torch.cuda.synchronize()
     got = map_to_host(b)
     ref = orc.propagate(S, n, cin, W, H, jump, 321, 9, 4, cell=c)
@@ -155,11 +155,11 @@ def test_grid_render_fwd_bwd(orc, W, H, n, c, random_lists):
     c_d = to_dev(cand)
     t_d = to_dev(tgt)
     out = torch.empty((H, W, 3), dtype=torch.float32, device=R.device)
-    sad.render_fwd(R, n, c_d, W, H, out, cell=c)
+    sad.render_fwd_rec(R, n, c_d, W, H, out, cell=c)
     g = sad.new_grad(S.shape[1], R.device)
     loss = sad.new_loss(R.device)
     rgb = torch.full((H, W, 3), -7.0, dtype=torch.float32, device=R.device)
-    sad.render_bwd(R, n, c_d, t_d, W, H, g, loss, rgb, cell=c)
+    sad.render_bwd_rec(R, n, c_d, t_d, W, H, g, loss, rgb, cell=c)
     torch.cuda.synchronize()
     fwd = out.cpu().numpy()
     ref = orc.render_fwd(S, n, cand, W, H, cell=c)
@@ -203,7 +203,7 @@ def test_grid_full_size_kodak768(orc):
     R = _rec(S, n)
     a = to_dev(cin)
     b = sad.new_map(W, H, a.device, cell=c)
-    sad.topk_propagate(R, n, a, b, W, H, 1, 5, synth.SEED_INJECT, wl.n_inject, cell=c)
+    sad.topk_propagate_rec(R, n, a, b, W, H, 1, 5, synth.SEED_INJECT, wl.n_inject, cell=c)
     torch.cuda.synchronize()
     got = map_to_host(b).reshape(-1, 8)
     pix = np.unique(np.random.default_rng(5).choice(Wm * Hm, 6000, replace=False)).astype(np.uint32)
@@ -215,7 +215,7 @@ def test_grid_full_size_kodak768(orc):
     g = sad.new_grad(S.shape[1], R.device)
     loss = sad.new_loss(R.device)
     rgb = torch.empty((H, W, 3), dtype=torch.float32, device=R.device)
-    sad.render_bwd(R, n, to_dev(cand), to_dev(tgt), W, H, g, loss, rgb, cell=c)
+    sad.render_bwd_rec(R, n, to_dev(cand), to_dev(tgt), W, H, g, loss, rgb, cell=c)
     torch.cuda.synchronize()
     pp = np.unique(np.random.default_rng(6).choice(W * H, 20000, replace=False)).astype(np.uint32)
     fwd_ref = orc.render_fwd_pixels(S, n, cand, W, H, pp, cell=c)

@@ -115,13 +115,13 @@ def test_jfa_then_propagation_recall(orc):
     res = sad.jfa_prepass(g, n, a, b, W, H)
     other = b if res.data_ptr() == a.data_ptr() else a
     for t in range(4):
-        sad.topk_propagate(g, n, res, other, W, H, 1, t, synth.SEED_INJECT, M)
+        sad.topk_propagate_rec(g, n, res, other, W, H, 1, t, synth.SEED_INJECT, M)
         res, other = other, res
     jfa_map = map_to_host(res).reshape(-1, 8).copy()
     c = sad.new_map(W, H, g.device)
     d = sad.new_map(W, H, g.device)
     for t, k in enumerate(sad.jump_schedule(W, H, 14)):
-        sad.topk_propagate(g, n, c, d, W, H, k, t, synth.SEED_INJECT, M)
+        sad.topk_propagate_rec(g, n, c, d, W, H, k, t, synth.SEED_INJECT, M)
         c, d = d, c
     torch.cuda.synchronize()
     reg_map = map_to_host(c).reshape(-1, 8)

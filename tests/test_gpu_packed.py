@@ -86,7 +86,7 @@ def test_adam_refreshes_packed_words():
     rec = sad.new_records(cap, S_d.device)
     pk = sad.new_packed(cap, S_d.device)
     pk.fill_(-7)
-    sad.adam_step(S_d, m, v, g, n, 3, W * H, W, H, rec=rec, packed=pk)
+    sad.adam_step_rec(S_d, m, v, g, n, 3, W * H, W, H, rec=rec, packed=pk)
     fresh = sad.new_packed(cap, S_d.device)
     sad.pack_sites(S_d, n, fresh)
     torch.cuda.synchronize()
@@ -105,7 +105,7 @@ def test_packed_propagate_matches_oracle(orc, W, H, n, jump, m, cell):
     pk = _packed(S, n)
     a = to_dev(cin)
     b = sad.new_map(W, H, a.device, cell=cell)
-    sad.topk_propagate(pk, n, a, b, W, H, jump, 77, 5, m, cell=cell)
+    sad.topk_propagate_rec(pk, n, a, b, W, H, jump, 77, 5, m, cell=cell)
     torch.cuda.synchronize()
     got = map_to_host(b)
     ref = orc.propagate(T, n, cin, W, H, jump, 77, 5, m, cell=cell)
@@ -152,7 +152,7 @@ def test_packed_propagate_full_size_kodak768(orc):
     for jump in (1, 64):
         print(f"packed propagate kodak768 jump={jump}", flush=True)
         b = sad.new_map(W, H, a.device)
-        sad.topk_propagate(pk, n, a, b, W, H, jump, 4242, synth.SEED_INJECT, wl.n_inject)
+        sad.topk_propagate_rec(pk, n, a, b, W, H, jump, 4242, synth.SEED_INJECT, wl.n_inject)
         torch.cuda.synchronize()
         got = map_to_host(b).reshape(-1, 8)[pix]
         ref = orc.propagate_pixels(T, n, cin, W, H, jump, 4242, synth.SEED_INJECT, wl.n_inject, pix)

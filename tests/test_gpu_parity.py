@@ -32,7 +32,7 @@ def _gpu_propagate(S, n, cin, W, H, jump, pidx, seed, m):
     g = _rec(S, n)
     a = to_dev(cin)
     b = sad.new_map(W, H, a.device)
-    sad.topk_propagate(g, n, a, b, W, H, jump, pidx, seed, m)
+    sad.topk_propagate_rec(g, n, a, b, W, H, jump, pidx, seed, m)
     torch.cuda.synchronize()
     return map_to_host(b)
 
@@ -171,7 +171,7 @@ def _fwd(S, n, cand, W, H):
     R_d = _rec(S, n)
     c = to_dev(cand)
     out = torch.empty((H, W, 3), dtype=torch.float32, device=R_d.device)
-    sad.render_fwd(R_d, n, c, W, H, out)
+    sad.render_fwd_rec(R_d, n, c, W, H, out)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -209,7 +209,7 @@ def _bwd(S, n, cand, tgt, W, H, grad0=None):
         g[:, :11].copy_(torch.from_numpy(grad0).t())
     loss = sad.new_loss(R_d.device)
     rgb = torch.full((H, W, 3), -7.0, dtype=torch.float32, device=R_d.device)
-    sad.render_bwd(R_d, n, c, t, W, H, g, loss, out_rgb=rgb)
+    sad.render_bwd_rec(R_d, n, c, t, W, H, g, loss, out_rgb=rgb)
     torch.cuda.synchronize()
     gh = g.cpu().numpy().astype(np.float64)
     assert (gh[:, 11:] == 0).all(), "unused words of the gradient records were written"
@@ -278,7 +278,7 @@ def _adam_gpu(S, m, v, G, n, step, P, W, H, cfg):
     rec[:, 11:] = 7.0  # unused words: must survive untouched
     g_d = to_dev(rec)
     rec = sad.new_records(S.shape[1], S_d.device)
-    sad.adam_step(S_d, m_d, v_d, g_d, n, step, P, W, H, cfg, rec=rec)
+    sad.adam_step_rec(S_d, m_d, v_d, g_d, n, step, P, W, H, cfg, rec=rec)
     torch.cuda.synchronize()
     # the refreshed records equal a fresh derivation from the updated sites
     fresh = sad.new_records(S.shape[1], S_d.device)
@@ -319,11 +319,11 @@ def test_adam_matches_oracle(orc, step):
 def test_empty_image_and_no_sites_are_noops():
     z = torch.zeros((10, 4), dtype=torch.float32, device="cuda")
     m0 = sad.new_map(0, 0)
-    sad.topk_propagate(sad.new_records(4), 4, m0, sad.new_map(0, 0), 0, 0, 1, 0, 0, 4)
+    sad.topk_propagate_rec(sad.new_records(4), 4, m0, sad.new_map(0, 0), 0, 0, 1, 0, 0, 4)
     out = torch.empty((0, 0, 3), dtype=torch.float32, device="cuda")
-    sad.render_fwd(sad.new_records(4), 4, m0, 0, 0, out)
+    sad.render_fwd_rec(sad.new_records(4), 4, m0, 0, 0, out)
     g = sad.new_grad(4)
-    sad.adam_step(z, torch.zeros_like(z), torch.zeros_like(z), g, 0, 1, 1, 1, 1)
+    sad.adam_step_rec(z, torch.zeros_like(z), torch.zeros_like(z), g, 0, 1, 1, 1, 1)
     torch.cuda.synchronize()
 
 

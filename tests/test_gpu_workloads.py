@@ -30,7 +30,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
 def _refresh(rec, n, a, b, W, H, jumps, pass0, seed, m):
     for t, k in enumerate(jumps):
-        sad.topk_propagate(rec, n, a, b, W, H, k, pass0 + t, seed, m)
+        sad.topk_propagate_rec(rec, n, a, b, W, H, k, pass0 + t, seed, m)
         a, b = b, a
     return a, b
 
@@ -66,7 +66,7 @@ def test_edit4096_refresh_recall(orc):
     loss = sad.new_loss(S_d.device)
     e2 = torch.cuda.Event(enable_timing=True)
     e2.record()
-    sad.render_bwd(rec, n, a, t_d, W, H, g, loss, rgb)
+    sad.render_bwd_rec(rec, n, a, t_d, W, H, g, loss, rgb)
     e3 = torch.cuda.Event(enable_timing=True)
     e3.record()
     torch.cuda.synchronize()
@@ -85,7 +85,7 @@ def test_edit4096_refresh_recall(orc):
     res = sad.jfa_prepass(rec, n, b, a, W, H)
     oth = a if res.data_ptr() == b.data_ptr() else b
     for t in range(4):
-        sad.topk_propagate(rec, n, res, oth, W, H, 1, 2000 + t, synth.SEED_INJECT, M)
+        sad.topk_propagate_rec(rec, n, res, oth, W, H, 1, 2000 + t, synth.SEED_INJECT, M)
         res, oth = oth, res
     e5.record()
     torch.cuda.synchronize()
