@@ -211,16 +211,19 @@ def edit_refresh(dev, reps, stream):
     S_d = torch.from_numpy(S).to(dev)
     rec = sad.new_records(n, dev)
     sad.site_records(S_d, n, rec)
+    scr = sad.new_screen(n, dev)
+    sad.site_screen(S_d, n, W, H, scr)
     a, b = sad.new_map(W, H, dev), sad.new_map(W, H, dev)
     sched = sad.jump_schedule(W, H, 12)
     pidx = 0
     for k in sched + sched + [1] * 20:
-        sad.topk_propagate_rec(rec, n, a, b, W, H, k, pidx, synth.SEED_INJECT, M)
+        sad.topk_propagate_rec(rec, n, a, b, W, H, k, pidx, synth.SEED_INJECT, M, scr=scr)
         a, b = b, a
         pidx += 1
     S2 = synth.displace_sites(S, n, W, H, seed=77)
     S_d.copy_(torch.from_numpy(S2))
     sad.site_records(S_d, n, rec)
+    sad.site_screen(S_d, n, W, H, scr)
     backup = a.clone()
     tgt = torch.from_numpy((synth.pixel_noise(W, H, 5, 0.2) + 0.5).astype(np.float32)).to(dev)
     rgb = torch.empty((H, W, 3), dtype=torch.float32, device=dev)
@@ -235,7 +238,7 @@ def edit_refresh(dev, reps, stream):
         ev[0].record(stream)
         x, y = a, b
         for t, k in enumerate(sched):
-            sad.topk_propagate_rec(rec, n, x, y, W, H, k, 1000 + t, synth.SEED_INJECT, M)
+            sad.topk_propagate_rec(rec, n, x, y, W, H, k, 1000 + t, synth.SEED_INJECT, M, scr=scr)
             x, y = y, x
             ev[t + 1].record(stream)
         sad.render_bwd_rec(rec, n, x, tgt, W, H, grad, loss, rgb)
@@ -273,7 +276,7 @@ def edit_refresh(dev, reps, stream):
         "recall_exact_sets": round(exact, 4), "recall_per_entry": round(per_entry, 4),
         "recall_sample": "4096 seeded pixels, exact top-8 by brute force over all sites on the GPU",
     }
-    del a, b, backup, tgt, rgb, grad, rec, S_d, x, y, final
+    del a, b, backup, tgt, rgb, grad, rec, scr, S_d, x, y, final
     torch.cuda.empty_cache()
     return out
 
@@ -393,10 +396,10 @@ def main():
     R = args.kernel_reps
     launches = {
         "propagate": lambda i: sad.topk_propagate_rec(fit.rec, N, fit.maps[i % 2], fit.maps[1 - i % 2], W, H, 1,
-                                                  100000 + i, synth.SEED_INJECT, wl.n_inject),
+                                                      100000 + i, synth.SEED_INJECT, wl.n_inject, scr=fit.scr),
         "fwd_bwd": lambda i: sad.render_bwd_rec(fit.rec, N, fit.cand, fit.target, W, H, fit.grad, fit.loss, fit.rgb),
         "adam": lambda i: sad.adam_step_rec(fit.sites, fit.m, fit.v, fit.grad, N, 50000 + i, P, W, H, fit.adam,
-                                        fit.rec),
+                                            fit.rec, scr=fit.scr),
         "fwd": lambda i: sad.render_fwd_rec(fit.rec, N, fit.cand, W, H, fit.rgb),
     }
     for name, fn in launches.items():

@@ -33,8 +33,8 @@
  *   memory (the host budget-control routines use temporary host memory and host
  *   threads) and keeps no state between calls, so calls are reentrant.
  * Pointers.  Arguments named `sites`, `rec`, `packed`, `cand*`, `out_rgb`,
- *   `target`, `grad`, `m`, `v`, `loss_sum`, `stats`, `seeds`, `entries`, `out`,
- *   `words`, `header` and `points` are DEVICE pointers (HBM of the current HIP
+ *   `target`, `grad`, `m`, `v`, `loss_sum`, `stats`, `scr`, `seeds`, `entries`,
+ *   `out`, `words`, `header` and `points` are DEVICE pointers (HBM of the current HIP
  *   device), except in sad_densify_prune and sad_densify_prune_stats, which work
  *   on HOST arrays.  `cfg` is a HOST pointer, read before the call returns.
  * Streams.  Device work is enqueued asynchronously on `stream` (a hipStream_t
@@ -90,6 +90,19 @@
  *         cache the caller keeps in step with `sites`: recompute it after any
  *         change made outside sad_adam_step_rec.  Stale records give results for
  *         the sites they were made from.
+ * scr   : uint32 [n_slots] -- the candidate screen, one 4-byte word per site that
+ *         bounds where the site can score (cached form only).  Its cells divide
+ *         the image into 4096 x 4096: bits 0..11 qx = floor(x 4096/W), bits 12..23
+ *         qy = floor(y 4096/H) (the site lies in that cell), bits 24..27 ca with
+ *         2^(ca/2) >= e^{|a|/2}, bits 28..31 cr with 2^(cr-8) >= 2^(ca/2) max(r,0)
+ *         (cr = 0: 0); ca = 15 or cr = 15: no bound.  Since ||x - p||_G >=
+ *         ||x - p|| / e^{|a|/2}, a selection pass can discard a candidate that
+ *         provably scores after its list's K-th entry without fetching its
+ *         record; the lists are the same bits with or without the screen.  It
+ *         bounds float32 scores of the sites, so it serves selection from the
+ *         records; with the packed buffer (float16-rounded sites) it is ignored.  A
+ *         cache like `rec`: sad_site_screen writes it, sad_adam_step_rec refreshes
+ *         it.  4-byte aligned.
  * packed: uint32 [n_slots][SAD_PACK_LD] -- the packed candidate-site buffer
  *         ([SUM] B.2 "Packed candidate sites": 16 bytes per site of float16 pairs,
  *         read by the candidate-update kernels to save bandwidth): word 0 = (x, y),
@@ -334,19 +347,30 @@ int sad_site_records(const float *sites, int n_slots, int stride, float *rec, vo
 int sad_pack_sites(const float *sites, int n_slots, int stride, uint32_t *packed, void *stream);
 
 /*
+ * sad_site_screen -- writes the candidate screen (see `scr` above) of slots
+ * [0, n_slots) of a W x H image from the site planes.
+ *   sites device [10][stride] read-only; scr device uint32 [n_slots], written.
+ *   W, H >= 1.
+ * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN (scr not 4-byte aligned), SAD_ERR_DEVICE.
+ */
+int sad_site_screen(const float *sites, int n_slots, int stride, int W, int H, uint32_t *scr, void *stream);
+
+/*
  * sad_topk_propagate_rec -- sad_topk_propagate on a map of any cell size, reading
  * the site records (sel_fmt = SAD_SEL_REC64: the same lists as sad_topk_propagate
- * when the records are current) or the packed buffer (SAD_SEL_PACKED16).  For a
- * grid map, x, jump and the neighbours are in map entries, pix = row*Wm + col,
- * and scores are taken at the entry's centred UV.
+ * when the records are current) or the packed buffer (SAD_SEL_PACKED16), with the
+ * candidate screen if `scr` is not NULL (the same lists, fewer record fetches).
+ * For a grid map, x, jump and the neighbours are in map entries, pix = row*Wm +
+ * col, and scores are taken at the entry's centred UV.
  *   rec       device, read-only: [n_slots][16] float or [n_slots][4] uint32
+ *   scr       device uint32 [n_slots] or NULL, current for this W x H
  *   cand_in, cand_out device [Hm][Wm][8]; the rest as sad_topk_propagate.
  * Errors: SAD_ERR_ARG (also a bad cell or sel_fmt), SAD_ERR_ALIGN (a pointer not
- *         16-byte aligned), SAD_ERR_DEVICE.
+ *         16-byte aligned, scr not 4-byte aligned), SAD_ERR_DEVICE.
  */
-int sad_topk_propagate_rec(const float *rec, int sel_fmt, int n_slots, const uint32_t *cand_in, uint32_t *cand_out,
-                           int W, int H, int cell, int jump, uint32_t pass_index, uint32_t seed, int n_inject,
-                           void *stream);
+int sad_topk_propagate_rec(const float *rec, int sel_fmt, const uint32_t *scr, int n_slots, const uint32_t *cand_in,
+                           uint32_t *cand_out, int W, int H, int cell, int jump, uint32_t pass_index, uint32_t seed,
+                           int n_inject, void *stream);
 
 /*
  * sad_render_fwd_rec -- sad_render_fwd from the site records (bit-identical when
@@ -381,13 +405,16 @@ int sad_render_bwd_rec(const float *rec, int n_slots, const uint32_t *cand, cons
  * sad_adam_step_rec -- sad_adam_step on gradient records (grad device
  * [stride][16], 16-byte aligned; words 0..9 zeroed, 10 left alone).  If rec is
  * not NULL the site records of slots [0, n_slots) are rewritten from the updated
- * sites in the same pass; if packed is not NULL, so are their packed words.
+ * sites in the same pass; if packed is not NULL, so are their packed words; if
+ * scr is not NULL, so are their screen words (for the image cfg->x_max x
+ * cfg->y_max).
  *   rec device [n_slots][16] or NULL; packed device [n_slots][4] uint32 or NULL,
- *   16-byte aligned; the rest as sad_adam_step.
+ *   16-byte aligned; scr device [n_slots] uint32 or NULL; the rest as
+ *   sad_adam_step.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_adam_step_rec(float *sites, float *m, float *v, float *grad, float *rec, uint32_t *packed, int n_slots,
-                      int stride, int step, int n_pixels, const sad_adam_cfg *cfg, void *stream);
+int sad_adam_step_rec(float *sites, float *m, float *v, float *grad, float *rec, uint32_t *packed, uint32_t *scr,
+                      int n_slots, int stride, int step, int n_pixels, const sad_adam_cfg *cfg, void *stream);
 
 /*
  * sad_densify_stats -- the budget-control statistics (see the rules above) on
@@ -461,12 +488,12 @@ int sad_jfa_seed(const float *rec, int sel_fmt, int n_slots, uint32_t *cand, int
  * 4..7.  Jacobi: reads cand_in, writes cand_out.  The prepass runs the steps B/2,
  * B/4, ..., 1 (B = 2^ceil(log2 max(Wm,Hm))), i.e. ceil(log2 max(Wm,Hm)) passes,
  * after sad_jfa_seed; propagation then fills the lists to K.
- *   rec/sel_fmt as in sad_topk_propagate_rec; step in [1, 65535]; cand_in,
+ *   rec/sel_fmt/scr as in sad_topk_propagate_rec; step in [1, 65535]; cand_in,
  *   cand_out device [Hm][Wm][8], not overlapping.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_jfa_pass(const float *rec, int sel_fmt, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
-                 int cell, int step, void *stream);
+int sad_jfa_pass(const float *rec, int sel_fmt, const uint32_t *scr, int n_slots, const uint32_t *cand_in,
+                 uint32_t *cand_out, int W, int H, int cell, int step, void *stream);
 
 /*
  * sad_topk_exact -- the exact top-K map by brute force over every slot: the list

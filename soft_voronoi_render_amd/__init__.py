@@ -105,7 +105,9 @@ def lib() -> ctypes.CDLL:
         L.sad_topk_propagate.restype = i32
         L.sad_topk_propagate.argtypes = [fp, i32, i32, vp, vp, i32, i32, i32, u32, u32, i32, vp]
         L.sad_topk_propagate_rec.restype = i32
-        L.sad_topk_propagate_rec.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, i32, u32, u32, i32, vp]
+        L.sad_topk_propagate_rec.argtypes = [vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, u32, u32, i32, vp]
+        L.sad_site_screen.restype = i32
+        L.sad_site_screen.argtypes = [fp, i32, i32, i32, i32, vp, vp]
         L.sad_eval_encode.restype = i32
         L.sad_eval_encode.argtypes = [fp, i32, i32, i32, i32, vp, fp, vp]
         L.sad_eval_decode.restype = i32
@@ -131,7 +133,7 @@ def lib() -> ctypes.CDLL:
         L.sad_jfa_seed.restype = i32
         L.sad_jfa_seed.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp]
         L.sad_jfa_pass.restype = i32
-        L.sad_jfa_pass.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, i32, vp]
+        L.sad_jfa_pass.argtypes = [vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, vp]
         L.sad_densify_stats.restype = i32
         L.sad_densify_stats.argtypes = [fp, i32, vp, fp, i32, i32, i32, fp, vp]
         ip = ctypes.POINTER(ctypes.c_int)
@@ -145,7 +147,7 @@ def lib() -> ctypes.CDLL:
         L.sad_adam_step.restype = i32
         L.sad_adam_step.argtypes = [fp, fp, fp, fp, i32, i32, i32, i32, ctypes.POINTER(AdamCfg), vp]
         L.sad_adam_step_rec.restype = i32
-        L.sad_adam_step_rec.argtypes = [fp, fp, fp, fp, fp, vp, i32, i32, i32, i32, ctypes.POINTER(AdamCfg), vp]
+        L.sad_adam_step_rec.argtypes = [fp, fp, fp, fp, fp, vp, vp, i32, i32, i32, i32, ctypes.POINTER(AdamCfg), vp]
         _lib = L
     return _lib
 
@@ -154,7 +156,7 @@ EXPORTED = ("sad_abi_version", "sad_status_string",
             # the iteration on the site buffer
             "sad_topk_propagate", "sad_render_fwd", "sad_render_bwd", "sad_adam_step", "sad_densify_prune",
             # the iteration on derived caches
-            "sad_site_records", "sad_pack_sites", "sad_topk_propagate_rec", "sad_render_fwd_rec",
+            "sad_site_records", "sad_pack_sites", "sad_site_screen", "sad_topk_propagate_rec", "sad_render_fwd_rec",
             "sad_render_bwd_rec", "sad_adam_step_rec", "sad_densify_stats", "sad_densify_prune_stats",
             "sad_apply_seeds",
             # candidate-map tools, evaluation format
@@ -246,6 +248,27 @@ def site_records(sites, n_slots, rec, stream=None):
     _check("sad_site_records", lib().sad_site_records(sp, n_slots, stride, r, _stream(stream)))
 
 
+def new_screen(capacity: int, device="cuda") -> torch.Tensor:
+    """Storage for the candidate screen, uint32 [capacity] held as int32."""
+    return torch.zeros(max(capacity, 1), dtype=torch.int32, device=device)
+
+
+def _scr(scr, n_slots):
+    if scr is None:
+        return None
+    if scr.dim() != 1 or scr.shape[0] < n_slots:
+        raise ValueError("scr must be int32 [>= n_slots]")
+    return _dev(scr, "scr", _U32)
+
+
+def site_screen(sites, n_slots, W, H, scr, stream=None):
+    """Writes the candidate-screen words of slots [0, n_slots) for a W x H image
+    (see sad_site_screen)."""
+    sp, stride = _sites(sites, n_slots)
+    _check("sad_site_screen", lib().sad_site_screen(sp, n_slots, stride, W, H, _scr(scr, n_slots),
+                                                    _stream(stream)))
+
+
 def map_shape(W: int, H: int, cell: int = 1) -> tuple:
     """Shape of the candidate map of a W x H image with cells of `cell` x `cell`
     pixels: (ceil(H / cell), ceil(W / cell), 8)."""
@@ -265,13 +288,16 @@ def topk_propagate(sites, n_slots, cand_in, cand_out, W, H, jump, pass_index, se
                                                           _stream(stream)))
 
 
-def topk_propagate_rec(rec, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed, n_inject, stream=None, cell=1):
+def topk_propagate_rec(rec, n_slots, cand_in, cand_out, W, H, jump, pass_index, seed, n_inject, stream=None, cell=1,
+                       scr=None):
     """One propagation pass: cand_in -> cand_out (see sad_topk_propagate_rec).
-    `rec` is the record buffer or the packed candidate-site buffer."""
+    `rec` is the record buffer or the packed candidate-site buffer; `scr` the
+    candidate screen or None."""
     g, fmt = _sel(rec, n_slots)
     a = _dev(cand_in, "cand_in", _U32, map_shape(W, H, cell))
     b = _dev(cand_out, "cand_out", _U32, map_shape(W, H, cell))
-    _check("sad_topk_propagate_rec", lib().sad_topk_propagate_rec(g, fmt, n_slots, a, b, W, H, cell, jump,
+    _check("sad_topk_propagate_rec", lib().sad_topk_propagate_rec(g, fmt, _scr(scr, n_slots), n_slots, a, b, W, H,
+                                                                  cell, jump,
                                                                   pass_index & 0xFFFFFFFF, seed & 0xFFFFFFFF,
                                                                   n_inject, _stream(stream)))
 
@@ -283,12 +309,13 @@ def jfa_seed(rec, n_slots, cand, W, H, stream=None, cell=1):
     _check("sad_jfa_seed", lib().sad_jfa_seed(g, fmt, n_slots, c, W, H, cell, _stream(stream)))
 
 
-def jfa_pass(rec, n_slots, cand_in, cand_out, W, H, step, stream=None, cell=1):
+def jfa_pass(rec, n_slots, cand_in, cand_out, W, H, step, stream=None, cell=1, scr=None):
     """One flood pass of the jump-flood prepass: cand_in -> cand_out (see sad_jfa_pass)."""
     g, fmt = _sel(rec, n_slots)
     a = _dev(cand_in, "cand_in", _U32, map_shape(W, H, cell))
     b = _dev(cand_out, "cand_out", _U32, map_shape(W, H, cell))
-    _check("sad_jfa_pass", lib().sad_jfa_pass(g, fmt, n_slots, a, b, W, H, cell, step, _stream(stream)))
+    _check("sad_jfa_pass", lib().sad_jfa_pass(g, fmt, _scr(scr, n_slots), n_slots, a, b, W, H, cell, step,
+                                              _stream(stream)))
 
 
 def jfa_steps(W: int, H: int, cell: int = 1) -> list:
@@ -303,12 +330,12 @@ def jfa_steps(W: int, H: int, cell: int = 1) -> list:
     return out
 
 
-def jfa_prepass(rec, n_slots, a, b, W, H, stream=None, cell=1):
+def jfa_prepass(rec, n_slots, a, b, W, H, stream=None, cell=1, scr=None):
     """Seed pass into `a`, then the flood passes ping-ponging between `a` and `b`;
     returns the map that holds the result (four closest per entry)."""
     jfa_seed(rec, n_slots, a, W, H, stream, cell)
     for k in jfa_steps(W, H, cell):
-        jfa_pass(rec, n_slots, a, b, W, H, k, stream, cell)
+        jfa_pass(rec, n_slots, a, b, W, H, k, stream, cell, scr)
         a, b = b, a
     return a
 
@@ -425,9 +452,9 @@ def adam_step(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamConfig 
 
 
 def adam_step_rec(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamConfig | AdamCfg | None = None,
-                  rec=None, stream=None, packed=None):
-    """Adam on gradient records float32 [stride][16], refreshing the records and
-    packed words if given (see sad_adam_step_rec)."""
+                  rec=None, stream=None, packed=None, scr=None):
+    """Adam on gradient records float32 [stride][16], refreshing the records,
+    packed words and screen words if given (see sad_adam_step_rec)."""
     sp, stride = _sites(sites, n_slots)
     mp = _dev(m, "m", _F32, (NPARAM, stride))
     vp = _dev(v, "v", _F32, (NPARAM, stride))
@@ -439,8 +466,8 @@ def adam_step_rec(sites, m, v, grad, n_slots, step, n_pixels, W, H, cfg: AdamCon
             raise ValueError("packed must be int32 [>= n_slots][4]")
         pk = _dev(packed, "packed", _U32)
     c = _adam_cfg(cfg, W, H)
-    _check("sad_adam_step_rec", lib().sad_adam_step_rec(sp, mp, vp, g, gp, pk, n_slots, stride, step, n_pixels,
-                                                        ctypes.byref(c), _stream(stream)))
+    _check("sad_adam_step_rec", lib().sad_adam_step_rec(sp, mp, vp, g, gp, pk, _scr(scr, n_slots), n_slots, stride,
+                                                        step, n_pixels, ctypes.byref(c), _stream(stream)))
 
 
 def densify_stats(rec, n_slots, cand, target, W, H, stats, stream=None, cell=1):
@@ -641,11 +668,15 @@ class Fitter:
     injection's pass index.  `cell` > 1 keeps the candidate map on the downscaled
     grid of B.3 "Candidate field" (ceil(W/cell) x ceil(H/cell) lists).  With
     `packed` the candidate passes read the 16-byte float16 candidate-site buffer
-    of B.2 "Packed candidate sites" (Adam refreshes it with the records)."""
+    of B.2 "Packed candidate sites" (Adam refreshes it with the records).  With
+    `screen` (the default) the candidate passes discard candidates that provably
+    cannot enter a list before fetching their records (sad_site_screen; the same
+    lists)."""
 
     def __init__(self, sites: torch.Tensor, n_slots: int, target: torch.Tensor, W: int, H: int,
                  n_inject: int = 4, seed: int = 4, adam: AdamConfig | None = None, cand: torch.Tensor | None = None,
-                 refresh_every: int = 1, passes_per_refresh: int = 1, cell: int = 1, packed: bool = False):
+                 refresh_every: int = 1, passes_per_refresh: int = 1, cell: int = 1, packed: bool = False,
+                 screen: bool = True):
         if refresh_every < 1 or passes_per_refresh < 0:
             raise ValueError("refresh_every >= 1 and passes_per_refresh >= 0")
         dev = sites.device
@@ -667,6 +698,10 @@ class Fitter:
         if packed:
             self.packed = new_packed(stride, dev)
             pack_sites(sites, n_slots, self.packed)
+        self.scr = None
+        if screen:
+            self.scr = new_screen(stride, dev)
+            site_screen(sites, n_slots, W, H, self.scr)
         self.maps = [cand if cand is not None else new_map(W, H, dev, cell), new_map(W, H, dev, cell)]
         self.cur = 0
         self.rgb = torch.empty((H, W, 3), dtype=torch.float32, device=dev)
@@ -694,10 +729,12 @@ class Fitter:
         site_records(self.sites, self.n_slots, self.rec, stream)
         if self.packed is not None:
             pack_sites(self.sites, self.n_slots, self.packed, stream)
+        if self.scr is not None:
+            site_screen(self.sites, self.n_slots, self.W, self.H, self.scr, stream)
 
     def propagate(self, jump: int, pass_index: int, stream=None):
         topk_propagate_rec(self.sel, self.n_slots, self.maps[self.cur], self.maps[1 - self.cur], self.W, self.H,
-                           jump, pass_index, self.seed, self.n_inject, stream, self.cell)
+                           jump, pass_index, self.seed, self.n_inject, stream, self.cell, self.scr)
         self.cur = 1 - self.cur
 
     def step(self, stream=None):
@@ -716,7 +753,7 @@ class Fitter:
         render_bwd_rec(self.rec, self.n_slots, self.cand, self.target, self.W, self.H, self.grad, self.loss,
                        self.rgb, stream, self.cell)
         adam_step_rec(self.sites, self.m, self.v, self.grad, self.n_slots, it + 1, self.W * self.H, self.W, self.H,
-                      self.adam, self.rec, stream, self.packed)
+                      self.adam, self.rec, stream, self.packed, self.scr)
         self.it += 1
 
     def densify(self, cfg: BudgetConfig | None = None, stream=None):

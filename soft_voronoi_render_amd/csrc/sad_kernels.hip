@@ -410,6 +410,99 @@ struct TopK64 {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Candidate screen.  Most candidates a selection pass offers cannot enter the
+// list: the injected IDs are uniform over the whole image, and at large jumps the
+// neighbour lists name sites about `jump` pixels away.  Fetching their 32-byte
+// scoring records is what those passes spend their time on (the records of a
+// 2k or 4k fit do not stay in L2), so each site also has a 4-byte screen word
+// from which a lane can prove, before any record fetch, that a candidate's score
+// exceeds the list's current K-th score.  With A = e^{|a|/2} the metric obeys
+// ||delta||_G >= ||delta|| / A, hence d = s(||delta||_G - r) > kth whenever
+//   ||delta|| > A (max(kth, 0)/s + max(r, 0)),
+// and the word holds enough to bound both sides:
+//   bits 0..11   qx = floor(x * 4096 / W), bits 12..23  qy = floor(y * 4096 / H):
+//                the site lies in cell qx of width W/4096 (qy likewise), so the
+//                distance from the scoring point to that cell bounds ||delta||
+//   bits 24..27  ca: A_hat = 2^(ca/2) >= A
+//   bits 28..31  cr: R_hat = 2^(cr - 8) >= A_hat max(r, 0), 0 for cr = 0
+// ca = 15 or cr = 15 mark a site the word cannot bound (inactive, non-finite,
+// outside the image, |a| > 9.7 or A_hat r > 64 px): it is never screened out.
+// The test adds a relative slack of 2^-10 and an absolute one of 1/64 px +
+// 2^-16 R_hat, far above the float32 rounding of the cell bounds and of the score,
+// so a screened-out candidate is one the full test would have rejected: the
+// selected lists are the same bits with or without the screen.
+constexpr float SCR_Q = 4096.0f;
+
+__device__ __forceinline__ uint32_t screen_word(float x, float y, float r, float a, float qsx, float qsy)
+{
+    constexpr uint32_t NO_BOUND = 15u << 24;
+    const float fx = x * qsx, fy = y * qsy;
+    if (!(x >= 0.0f && y >= 0.0f && fx < SCR_Q + 0.5f && fy < SCR_Q + 0.5f) || !finitef(r) || !finitef(a))
+        return NO_BOUND;
+    const float fca = ceilf(fabsf(a) * 1.44269504f + 0.01f);  // |a| / ln 2, rounded up with slack
+    if (!(fca <= 14.0f))
+        return NO_BOUND;
+    const int ca = (int)fca;
+    const float Ahat = ldexpf((ca & 1) ? 1.41421366f : 1.0f, ca >> 1);  // 1.41421366 > sqrt(2)
+    const float rr = fmaxf(r, 0.0f) * Ahat;
+    uint32_t cr = 0;
+    if (rr > 0.0f) {
+        const float e = ceilf(__log2f(rr) + 0.01f) + 8.0f;
+        if (!(e <= 14.0f))
+            return NO_BOUND;
+        cr = (uint32_t)fmaxf(e, 1.0f);
+    }
+    const uint32_t qx = (uint32_t)fminf(floorf(fx), SCR_Q - 1.0f), qy = (uint32_t)fminf(floorf(fy), SCR_Q - 1.0f);
+    return qx | (qy << 12) | ((uint32_t)ca << 24) | (cr << 28);
+}
+
+// The screen of a selection kernel: the words (NULL: no screening) and the cell
+// size W/4096, H/4096 in pixels.
+struct Screen {
+    const uint32_t *w;
+    float cw, ch, inv_s;  // inv_s = max(W, H)
+};
+
+// Score of a ranking key (the inverse of rank_key's order-preserving map).
+__device__ __forceinline__ float key_score(uint64_t key)
+{
+    uint32_t u = (uint32_t)(key >> 32);
+    u ^= (u & 0x80000000u) ? 0x80000000u : 0xFFFFFFFFu;
+    return __uint_as_float(u);
+}
+
+// True when site id scored at (X, Y) provably ranks after `kth` (the key of the
+// list's K-th entry; ~0 while the list has a free place).
+__device__ __forceinline__ bool screened_out(const Screen &sc, uint32_t id, float X, float Y, uint64_t kth)
+{
+    if (!sc.w || kth == ~0ull)
+        return false;
+    const uint32_t v = sc.w[id];
+    const uint32_t ca = (v >> 24) & 15u, cr = v >> 28;
+    if (ca == 15u || cr == 15u)
+        return false;
+    const float Ahat = ldexpf((ca & 1u) ? 1.41421366f : 1.0f, (int)(ca >> 1));
+    const float Rhat = cr ? ldexpf(1.0f, (int)cr - 8) : 0.0f;
+    const float x0 = (float)(v & 0xFFFu) * sc.cw, y0 = (float)((v >> 12) & 0xFFFu) * sc.ch;
+    const float dx = fmaxf(fmaxf(x0 - X, X - (x0 + sc.cw)), 0.0f);
+    const float dy = fmaxf(fmaxf(y0 - Y, Y - (y0 + sc.ch)), 0.0f);
+    const float kd = fmaxf(key_score(kth), 0.0f) * sc.inv_s;
+    const float B = fmaf(Ahat * kd, 1.0009766f, Rhat) + fmaf(Rhat, 1.5258789e-5f, 0.015625f);
+    return dx * dx + dy * dy > B * B;
+}
+
+// Screen words of slots [0, n_slots) (see screen_word; qsx = 4096/W, qsy = 4096/H).
+__global__ __launch_bounds__(256) void k_site_screen(const float *__restrict__ S, int n_slots, int stride, float qsx,
+                                                     float qsy, uint32_t *__restrict__ scr)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_slots)
+        return;
+    const long st = stride;
+    scr[i] = screen_word(S[PX * st + i], S[PY * st + i], S[PR * st + i], S[PA * st + i], qsx, qsy);
+}
+
 template <int KK, int TB>
 struct PropShared {
     // The hash keys are needed until the records are loaded; from then on a
@@ -453,7 +546,7 @@ __device__ __forceinline__ void region_pixel(int r, int c0, int r0, int jump, in
 }
 
 template <int KK, int TB, int FMT>
-__global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, uint32_t n_slots,
+__global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uint32_t n_slots,
                                                      const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
                                                      int H, int jump, uint32_t seed_h, int n_inject, float s, float sx,
                                                      float sy, int tiles_x, int nb)
@@ -624,18 +717,20 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, uint32_t n_slo
             best.consider_new(id, d, usable);
         } else {
             const uint32_t c = ref & ~REF_SPILL;
-            const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
-            best.consider(c, d, usable);
+            if (!screened_out(sc, c, X, Y, best.k[K - 1])) {
+                const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
+                best.consider(c, d, usable);
+            }
         }
     }
-    // injected IDs (summary, B.3)
+    // injected IDs (summary, B.3), screened before their records are fetched
     if (n_inject > 0) {
         const uint32_t h = pcg_hash(seed_h ^ ((uint32_t)row * (uint32_t)W + (uint32_t)col));
         uint32_t x = h ? h : 0x9E3779B9u;
         for (int j = 0; j < n_inject; ++j) {
             x = xorshift32(x);
             const uint32_t c = (uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32);
-            if (c < n_slots) {
+            if (c < n_slots && !screened_out(sc, c, X, Y, best.k[K - 1])) {
                 bool usable;
                 const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
                 best.consider(c, d, usable);
@@ -654,7 +749,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, uint32_t n_slo
 // per workgroup: 16 for maps large enough to fill the chip with 16x16 tiles, 8
 // for small (downscaled) maps, which would otherwise leave most CUs idle.
 template <int TW, int FMT>
-__global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, uint32_t n_slots,
+__global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, Screen sc, uint32_t n_slots,
                                                              const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
                                                              int W, int H, int jump, uint32_t seed_h, int n_inject,
                                                              float s, float sx, float sy, int tiles_x, int nb)
@@ -679,9 +774,10 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, uint32
         const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            // an ID already held is skipped before its record is fetched (lists of
-            // nearby pixels share most of their sites)
-            if (ids[k] < n_slots && !best.holds(ids[k])) {
+            // an ID already held, or one the screen rules out, is skipped before
+            // its record is fetched (lists of nearby pixels share most of their
+            // sites; at large jumps most entries are far away)
+            if (ids[k] < n_slots && !best.holds(ids[k]) && !screened_out(sc, ids[k], X, Y, best.k[K - 1])) {
                 bool usable;
                 const float d = geom_score_id<FMT>(src, ids[k], X, Y, s, usable);
                 best.consider_new(ids[k], d, usable);
@@ -694,7 +790,7 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, uint32
         for (int j = 0; j < n_inject; ++j) {
             x = xorshift32(x);
             const uint32_t c = (uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32);
-            if (c < n_slots) {
+            if (c < n_slots && !screened_out(sc, c, X, Y, best.k[K - 1])) {
                 bool usable;
                 const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
                 best.consider(c, d, usable);
@@ -798,7 +894,7 @@ __global__ __launch_bounds__(256) void k_jfa_seed_finish(uint4 *__restrict__ can
 // pixel of a tile at steps >= 16, so candidates are scored straight from their
 // records, as in the table-free propagation.
 template <int FMT>
-__global__ __launch_bounds__(BLOCK) void k_jfa_pass(SiteSrc src, uint32_t n_slots,
+__global__ __launch_bounds__(BLOCK) void k_jfa_pass(SiteSrc src, Screen sc, uint32_t n_slots,
                                                     const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
                                                     int H, int step, float s, float sx, float sy, int tiles_x,
                                                     int nb)
@@ -821,8 +917,10 @@ __global__ __launch_bounds__(BLOCK) void k_jfa_pass(SiteSrc src, uint32_t n_slot
         const uint32_t ids[JFA_KEEP] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int k = 0; k < JFA_KEEP; ++k) {
-            // an ID already held is skipped before its record is fetched
-            if (ids[k] < n_slots && !best.holds(ids[k])) {
+            // an ID already held, or one that cannot enter the four kept places,
+            // is skipped before its record is fetched
+            if (ids[k] < n_slots && !best.holds(ids[k]) &&
+                !screened_out(sc, ids[k], X, Y, best.k[JFA_KEEP - 1])) {
                 bool usable;
                 const float d = geom_score_id<FMT>(src, ids[k], X, Y, s, usable);
                 best.consider_new(ids[k], d, usable);
@@ -2218,12 +2316,14 @@ __global__ __launch_bounds__(256) void k_eval_query(const uint4 *__restrict__ wo
 struct AdamArgs {
     float lr[SAD_NPARAM];
     float b1, b2, eps, ibc1, ibc2, inv_p, W, H;  // ibc = 1 / (1 - beta^step)
+    float qsx, qsy;                              // 4096 / W, 4096 / H: the screen's cells
 };
 
 template <int GL>
 __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__restrict__ M, float *__restrict__ V,
                                               float *__restrict__ G, float4 *__restrict__ rec,
-                                              uint4 *__restrict__ packed, int n_slots, int stride, AdamArgs A)
+                                              uint4 *__restrict__ packed, uint32_t *__restrict__ scr, int n_slots,
+                                              int stride, AdamArgs A)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= n_slots)
@@ -2295,6 +2395,8 @@ __global__ __launch_bounds__(256) void k_adam(float *__restrict__ S, float *__re
     }
     if (packed)
         packed[i] = pack_site_v(po);
+    if (scr)
+        scr[i] = screen_word(po[PX], po[PY], po[PR], po[PA], A.qsx, A.qsy);
 }
 
 // ---------------------------------------------------------------------------
@@ -2357,6 +2459,7 @@ inline bool valid_fmt(int f) { return f == SEL_REC || f == SEL_PACKED; }
 
 struct PropArgs {
     SiteSrc src;
+    Screen sc;
     uint32_t n;
     const uint4 *ci;
     uint4 *co;
@@ -2378,13 +2481,14 @@ void launch_propagate(const PropArgs &A, hipStream_t hs)
     const TileGrid g = tile_grid(A.Wm, A.Hm);
     if (A.cell > 1 && g.nb < SMALL_MAP_TILES) {
         const TileGrid g8 = tile_grid(A.Wm, A.Hm, 8);
-        hipLaunchKernelGGL((k_propagate_direct<8, FMT>), dim3(g8.nb), dim3(64), 0, hs, A.src, A.n, A.ci, A.co, A.Wm,
+        hipLaunchKernelGGL((k_propagate_direct<8, FMT>), dim3(g8.nb), dim3(64), 0, hs, A.src, A.sc, A.n, A.ci, A.co, A.Wm,
                            A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g8.tiles_x, g8.nb);
     } else if (A.cell == 1 && A.jump == 1) {
-        hipLaunchKernelGGL((k_propagate<1, 256, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.n, A.ci, A.co,
+        hipLaunchKernelGGL((k_propagate<1, 256, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci, A.co,
                            A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
     } else {
-        hipLaunchKernelGGL((k_propagate_direct<TILE, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.n, A.ci, A.co,
+        hipLaunchKernelGGL((k_propagate_direct<TILE, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci,
+                           A.co,
                            A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
     }
 }
@@ -2397,13 +2501,19 @@ uint32_t host_pcg_hash(uint32_t v)
 }
 
 inline SiteSrc src_of(const float *rec) { return SiteSrc{(const float4 *)rec, nullptr, 0}; }
+
+// The screen of a W x H image (scr may be NULL: no screening).
+inline Screen screen_of(const uint32_t *scr, int W, int H)
+{
+    return Screen{scr, (float)W / SCR_Q, (float)H / SCR_Q, (float)(W > H ? W : H)};
+}
 inline SiteSrc src_planes(const float *sites, int stride) { return SiteSrc{nullptr, sites, (long)stride}; }
 
 // One propagation pass from any site source (fmt: SEL_REC, SEL_PACKED or SEL_SOA);
 // `site_ptr` is the pointer the source reads, for the NULL check.
-int propagate_pass(SiteSrc src, const void *site_ptr, int fmt, int n_slots, const uint32_t *cand_in,
-                   uint32_t *cand_out, int W, int H, int cell, int jump, uint32_t pass_index, uint32_t seed,
-                   int n_inject, void *stream)
+int propagate_pass(SiteSrc src, const void *site_ptr, int fmt, const uint32_t *scr, int n_slots,
+                   const uint32_t *cand_in, uint32_t *cand_out, int W, int H, int cell, int jump, uint32_t pass_index,
+                   uint32_t seed, int n_inject, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
@@ -2422,11 +2532,14 @@ int propagate_pass(SiteSrc src, const void *site_ptr, int fmt, int n_slots, cons
     const uintptr_t a0 = (uintptr_t)cand_in, a1 = (uintptr_t)cand_out;
     if (a0 < a1 + bytes && a1 < a0 + bytes)
         return SAD_ERR_ARG;
-    if (!aligned16(cand_in) || !aligned16(cand_out) || (fmt != SEL_SOA && !aligned16(site_ptr)))
+    if (!aligned16(cand_in) || !aligned16(cand_out) || (fmt != SEL_SOA && !aligned16(site_ptr)) ||
+        ((uintptr_t)scr & 3u))
         return SAD_ERR_ALIGN;
     const uint32_t pw = ((uint32_t)jump << 16) | (pass_index & 0xFFFFu);
     const uint32_t seed_h = host_pcg_hash(host_pcg_hash(seed) ^ pw);
-    const PropArgs A{src, (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm,
+    // the screen bounds float32 scores; selection from the packed buffer ranks
+    // float16-rounded sites, for which it does not hold
+    const PropArgs A{src, screen_of(n_slots > 0 && fmt == SEL_REC ? scr : nullptr, W, H), (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm,
                      cell, jump, seed_h, n_inject, scale_of(W, H), mg.sx, mg.sy};
     if (fmt == SEL_PACKED)
         launch_propagate<SEL_PACKED>(A, (hipStream_t)stream);
@@ -2465,8 +2578,8 @@ int render_fwd_any(SiteSrc src, const void *site_ptr, int fmt, int n_slots, cons
     return launched();
 }
 
-int adam_any(float *sites, float *m, float *v, float *grad, int gl, float *rec, uint32_t *packed, int n_slots,
-             int stride, int step, int n_pixels, const sad_adam_cfg *cfg, void *stream)
+int adam_any(float *sites, float *m, float *v, float *grad, int gl, float *rec, uint32_t *packed, uint32_t *scr,
+             int n_slots, int stride, int step, int n_pixels, const sad_adam_cfg *cfg, void *stream)
 {
     int rc;
     if ((rc = check_sites(n_slots, stride)))
@@ -2478,7 +2591,7 @@ int adam_any(float *sites, float *m, float *v, float *grad, int gl, float *rec, 
     if (!(cfg->x_max > 0.0f && cfg->y_max > 0.0f && cfg->x_max <= (float)SAD_MAX_DIM &&
           cfg->y_max <= (float)SAD_MAX_DIM))
         return SAD_ERR_ARG;
-    if ((gl == GL_REC && !aligned16(grad)) || !aligned16(rec) || !aligned16(packed))
+    if ((gl == GL_REC && !aligned16(grad)) || !aligned16(rec) || !aligned16(packed) || ((uintptr_t)scr & 3u))
         return SAD_ERR_ALIGN;
     if (n_slots == 0)
         return SAD_OK;
@@ -2493,12 +2606,14 @@ int adam_any(float *sites, float *m, float *v, float *grad, int gl, float *rec, 
     A.inv_p = 1.0f / (float)n_pixels;
     A.W = cfg->x_max;
     A.H = cfg->y_max;
+    A.qsx = SCR_Q / cfg->x_max;
+    A.qsy = SCR_Q / cfg->y_max;
     if (gl == GL_PLANES)
         hipLaunchKernelGGL(k_adam<GL_PLANES>, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites,
-                           m, v, grad, (float4 *)rec, (uint4 *)packed, n_slots, stride, A);
+                           m, v, grad, (float4 *)rec, (uint4 *)packed, scr, n_slots, stride, A);
     else
         hipLaunchKernelGGL(k_adam<GL_REC>, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, m,
-                           v, grad, (float4 *)rec, (uint4 *)packed, n_slots, stride, A);
+                           v, grad, (float4 *)rec, (uint4 *)packed, scr, n_slots, stride, A);
     return launched();
 }
 
@@ -2559,18 +2674,36 @@ int sad_topk_propagate(const float *sites, int n_slots, int stride, const uint32
     int rc;
     if ((rc = check_sites(n_slots, stride)))
         return rc;
-    return propagate_pass(src_planes(sites, stride), sites, SEL_SOA, n_slots, cand_in, cand_out, W, H, 1, jump,
-                          pass_index, seed, n_inject, stream);
+    return propagate_pass(src_planes(sites, stride), sites, SEL_SOA, nullptr, n_slots, cand_in, cand_out, W, H, 1,
+                          jump, pass_index, seed, n_inject, stream);
 }
 
-int sad_topk_propagate_rec(const float *rec, int sel_fmt, int n_slots, const uint32_t *cand_in, uint32_t *cand_out,
-                           int W, int H, int cell, int jump, uint32_t pass_index, uint32_t seed, int n_inject,
-                           void *stream)
+int sad_topk_propagate_rec(const float *rec, int sel_fmt, const uint32_t *scr, int n_slots, const uint32_t *cand_in,
+                           uint32_t *cand_out, int W, int H, int cell, int jump, uint32_t pass_index, uint32_t seed,
+                           int n_inject, void *stream)
 {
     if (!valid_fmt(sel_fmt))
         return SAD_ERR_ARG;
-    return propagate_pass(src_of(rec), rec, sel_fmt, n_slots, cand_in, cand_out, W, H, cell, jump, pass_index, seed,
-                          n_inject, stream);
+    return propagate_pass(src_of(rec), rec, sel_fmt, scr, n_slots, cand_in, cand_out, W, H, cell, jump, pass_index,
+                          seed, n_inject, stream);
+}
+
+int sad_site_screen(const float *sites, int n_slots, int stride, int W, int H, uint32_t *scr, void *stream)
+{
+    int rc;
+    if ((rc = check_sites(n_slots, stride)) || (rc = check_image(W, H)))
+        return rc;
+    if (W < 1 || H < 1)
+        return SAD_ERR_ARG;
+    if (n_slots == 0)
+        return SAD_OK;
+    if (!sites || !scr)
+        return SAD_ERR_ARG;
+    if ((uintptr_t)scr & 3u)
+        return SAD_ERR_ALIGN;
+    hipLaunchKernelGGL(k_site_screen, dim3((n_slots + 255) / 256), dim3(256), 0, (hipStream_t)stream, sites, n_slots,
+                       stride, SCR_Q / (float)W, SCR_Q / (float)H, scr);
+    return launched();
 }
 
 int sad_apply_seeds(uint32_t *cand, int W, int H, int cell, const uint32_t *seeds, long n_seeds, void *stream)
@@ -2629,8 +2762,8 @@ int sad_jfa_seed(const float *rec, int sel_fmt, int n_slots, uint32_t *cand, int
     return launched();
 }
 
-int sad_jfa_pass(const float *rec, int sel_fmt, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
-                 int cell, int step, void *stream)
+int sad_jfa_pass(const float *rec, int sel_fmt, const uint32_t *scr, int n_slots, const uint32_t *cand_in,
+                 uint32_t *cand_out, int W, int H, int cell, int step, void *stream)
 {
     int rc;
     if ((rc = check_image(W, H)))
@@ -2649,16 +2782,17 @@ int sad_jfa_pass(const float *rec, int sel_fmt, int n_slots, const uint32_t *can
     const uintptr_t a0 = (uintptr_t)cand_in, a1 = (uintptr_t)cand_out;
     if (a0 < a1 + bytes && a1 < a0 + bytes)
         return SAD_ERR_ARG;
-    if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(rec))
+    if (!aligned16(cand_in) || !aligned16(cand_out) || !aligned16(rec) || ((uintptr_t)scr & 3u))
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(Wm, Hm);
     const SiteSrc src = src_of(rec);
+    const Screen sc = screen_of(n_slots > 0 && sel_fmt == SEL_REC ? scr : nullptr, W, H);
     if (sel_fmt == SEL_PACKED)
-        hipLaunchKernelGGL(k_jfa_pass<SEL_PACKED>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
+        hipLaunchKernelGGL(k_jfa_pass<SEL_PACKED>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src, sc,
                            (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm, step, scale_of(W, H),
                            mg.sx, mg.sy, g.tiles_x, g.nb);
     else
-        hipLaunchKernelGGL(k_jfa_pass<SEL_REC>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
+        hipLaunchKernelGGL(k_jfa_pass<SEL_REC>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src, sc,
                            (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm, step, scale_of(W, H),
                            mg.sx, mg.sy, g.tiles_x, g.nb);
     return launched();
@@ -2814,13 +2948,14 @@ int sad_densify_stats(const float *rec, int n_slots, const uint32_t *cand, const
 int sad_adam_step(float *sites, float *m, float *v, float *grad, int n_slots, int stride, int step, int n_pixels,
                   const sad_adam_cfg *cfg, void *stream)
 {
-    return adam_any(sites, m, v, grad, GL_PLANES, nullptr, nullptr, n_slots, stride, step, n_pixels, cfg, stream);
+    return adam_any(sites, m, v, grad, GL_PLANES, nullptr, nullptr, nullptr, n_slots, stride, step, n_pixels, cfg,
+                    stream);
 }
 
-int sad_adam_step_rec(float *sites, float *m, float *v, float *grad, float *rec, uint32_t *packed, int n_slots,
-                      int stride, int step, int n_pixels, const sad_adam_cfg *cfg, void *stream)
+int sad_adam_step_rec(float *sites, float *m, float *v, float *grad, float *rec, uint32_t *packed, uint32_t *scr,
+                      int n_slots, int stride, int step, int n_pixels, const sad_adam_cfg *cfg, void *stream)
 {
-    return adam_any(sites, m, v, grad, GL_REC, rec, packed, n_slots, stride, step, n_pixels, cfg, stream);
+    return adam_any(sites, m, v, grad, GL_REC, rec, packed, scr, n_slots, stride, step, n_pixels, cfg, stream);
 }
 
 int sad_eval_encode(const float *sites, int n_slots, int stride, int W, int H, uint32_t *words, float *header,

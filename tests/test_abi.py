@@ -76,12 +76,12 @@ Q = 0x90000
 
 def test_propagate_rejects_bad_arguments(L):
     f = L.sad_topk_propagate_rec
-    ok = dict(rec=P, fmt=0, n=4, a=P, b=Q, W=16, H=16, cell=1, jump=1, pidx=0, seed=0, m=4)
+    ok = dict(rec=P, fmt=0, scr=None, n=4, a=P, b=Q, W=16, H=16, cell=1, jump=1, pidx=0, seed=0, m=4)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["rec"], a["fmt"], a["n"], a["a"], a["b"], a["W"], a["H"], a["cell"], a["jump"], a["pidx"], a["seed"],
-                 a["m"], None)
+        return f(a["rec"], a["fmt"], a["scr"], a["n"], a["a"], a["b"], a["W"], a["H"], a["cell"], a["jump"], a["pidx"],
+                 a["seed"], a["m"], None)
 
     assert call(jump=0) == ERR_ARG
     assert call(jump=65536) == ERR_ARG
@@ -109,6 +109,7 @@ def test_propagate_rejects_bad_arguments(L):
     assert call(fmt=2) == ERR_ARG        # unknown site format
     assert call(fmt=-1) == ERR_ARG
     assert call(fmt=1, rec=P + 8) == ERR_ALIGN
+    assert call(scr=Q + 2) == ERR_ALIGN     # screen words need 4 bytes
 
 
 def test_site_buffer_calls_reject_bad_arguments(L):
@@ -177,6 +178,12 @@ def test_render_and_adam_reject_bad_arguments(L):
     assert X(P, 0, 4, P, 4, 16, 16, 1, Q + 4, None) == ERR_ALIGN
     assert X(P, 0, 4, P, 0, 16, 16, 1, Q, None) == 0                # no entries: no-op
     assert X(P, 2, 4, P, 4, 16, 16, 1, Q, None) == ERR_ARG          # unknown site format
+    C = L.sad_site_screen
+    assert C(P, 4, 8, 16, 16, Q + 2, None) == ERR_ALIGN
+    assert C(P, 9, 8, 16, 16, Q, None) == ERR_ARG
+    assert C(P, 4, 8, 0, 16, Q, None) == ERR_ARG                    # no image: no cell size
+    assert C(0, 4, 8, 16, 16, Q, None) == ERR_ARG
+    assert C(0, 0, 8, 16, 16, 0, None) == 0                         # no slots: no-op
     S = L.sad_apply_seeds
     assert S(P, 16, 16, 1, P, -1, None) == ERR_ARG
     assert S(P, 16, 16, 0, P, 4, None) == ERR_ARG
@@ -199,15 +206,16 @@ def test_render_and_adam_reject_bad_arguments(L):
     assert L.sad_site_records(0, 0, 8, 0, None) == 0  # no slots: no-op
     cfg = sad.AdamConfig().to_c(4, 4)
     A = L.sad_adam_step_rec
-    assert A(P, P, P, P, P, None, 4, 8, 0, 10, ctypes.byref(cfg), None) == ERR_ARG   # step 0
-    assert A(P, P, P, P, P, None, 4, 8, 1, 0, ctypes.byref(cfg), None) == ERR_ARG   # no pixels
-    assert A(P, P, P, P, P, None, 4, 8, 1, 10, None, None) == ERR_ARG
-    assert A(P, P, P, P + 4, P, None, 4, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ALIGN
-    assert A(P, P, P, P, P + 4, None, 4, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ALIGN
+    assert A(P, P, P, P, P, None, None, 4, 8, 0, 10, ctypes.byref(cfg), None) == ERR_ARG   # step 0
+    assert A(P, P, P, P, P, None, None, 4, 8, 1, 0, ctypes.byref(cfg), None) == ERR_ARG   # no pixels
+    assert A(P, P, P, P, P, None, None, 4, 8, 1, 10, None, None) == ERR_ARG
+    assert A(P, P, P, P + 4, P, None, None, 4, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ALIGN
+    assert A(P, P, P, P, P + 4, None, None, 4, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ALIGN
     bad = sad.AdamConfig(beta1=1.0).to_c(4, 4)
-    assert A(P, P, P, P, P, None, 4, 8, 1, 10, ctypes.byref(bad), None) == ERR_ARG
-    assert A(P, P, P, P, None, None, 0, 8, 1, 10, ctypes.byref(cfg), None) == 0  # no slots: no-op
-    assert A(P, P, P, P, P, P + 4, 4, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ALIGN  # packed
+    assert A(P, P, P, P, P, None, None, 4, 8, 1, 10, ctypes.byref(bad), None) == ERR_ARG
+    assert A(P, P, P, P, None, None, None, 0, 8, 1, 10, ctypes.byref(cfg), None) == 0  # no slots: no-op
+    assert A(P, P, P, P, P, P + 4, None, 4, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ALIGN  # packed
+    assert A(P, P, P, P, P, None, Q + 2, 4, 8, 1, 10, ctypes.byref(cfg), None) == ERR_ALIGN  # screen
 
 
 def test_jfa_entry_points_reject_bad_arguments(L):
@@ -219,17 +227,17 @@ def test_jfa_entry_points_reject_bad_arguments(L):
     assert S(P + 8, 0, 4, P, 16, 16, 1, None) == ERR_ALIGN
     assert S(P, 0, 4, P, 70000, 16, 1, None) == ERR_ARG
     assert S(P, 0, 4, P, 0, 16, 1, None) == 0                      # empty image: no-op
-    assert J(P, 0, 4, P, Q, 16, 16, 1, 0, None) == ERR_ARG         # step 0
-    assert J(P, 0, 4, P, Q, 16, 16, 1, 65536, None) == ERR_ARG
-    assert J(P, 0, 4, P, P + 32, 16, 16, 1, 1, None) == ERR_ARG     # overlapping maps
-    assert J(P, 0, 4, P + 4, Q, 16, 16, 1, 1, None) == ERR_ALIGN
-    assert J(P, 0, -1, P, Q, 16, 16, 1, 1, None) == ERR_ARG
-    assert J(P, 0, 4, P, Q, 16, 0, 1, 1, None) == 0
+    assert J(P, 0, 0, 4, P, Q, 16, 16, 1, 0, None) == ERR_ARG         # step 0
+    assert J(P, 0, 0, 4, P, Q, 16, 16, 1, 65536, None) == ERR_ARG
+    assert J(P, 0, 0, 4, P, P + 32, 16, 16, 1, 1, None) == ERR_ARG     # overlapping maps
+    assert J(P, 0, 0, 4, P + 4, Q, 16, 16, 1, 1, None) == ERR_ALIGN
+    assert J(P, 0, 0, -1, P, Q, 16, 16, 1, 1, None) == ERR_ARG
+    assert J(P, 0, 0, 4, P, Q, 16, 0, 1, 1, None) == 0
     assert S(P, 0, 4, P, 16, 16, 0, None) == ERR_ARG            # cell 0
-    assert J(P, 0, 4, P, Q, 16, 16, 0, 1, None) == ERR_ARG
-    assert J(P, 0, 4, P, P + 256, 16, 16, 2, 1, None) == ERR_ARG  # 8x8 lists of 32 bytes overlap
+    assert J(P, 0, 0, 4, P, Q, 16, 16, 0, 1, None) == ERR_ARG
+    assert J(P, 0, 0, 4, P, P + 256, 16, 16, 2, 1, None) == ERR_ARG  # 8x8 lists of 32 bytes overlap
     assert S(P, 3, 4, P, 16, 16, 1, None) == ERR_ARG         # unknown site format
-    assert J(P, 3, 4, P, Q, 16, 16, 1, 1, None) == ERR_ARG
+    assert J(P, 3, 0, 4, P, Q, 16, 16, 1, 1, None) == ERR_ARG
 
 
 def test_densify_entry_points_reject_bad_arguments(L):
