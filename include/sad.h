@@ -98,7 +98,9 @@
  *         (cr = 0: 0); ca = 15 or cr = 15: no bound.  Since ||x - p||_G >=
  *         ||x - p|| / e^{|a|/2}, a selection pass can discard a candidate that
  *         provably scores after its list's K-th entry without fetching its
- *         record; the lists are the same bits with or without the screen.  It
+ *         record (propagation screens the injected IDs, uniform over the image,
+ *         and the IDs its site table could not hold); the lists are the same bits
+ *         with or without the screen.  It
  *         bounds float32 scores of the sites, so it serves selection from the
  *         records; with the packed buffer (float16-rounded sites) it is ignored.  A
  *         cache like `rec`: sad_site_screen writes it, sad_adam_step_rec refreshes
@@ -488,12 +490,12 @@ int sad_jfa_seed(const float *rec, int sel_fmt, int n_slots, uint32_t *cand, int
  * 4..7.  Jacobi: reads cand_in, writes cand_out.  The prepass runs the steps B/2,
  * B/4, ..., 1 (B = 2^ceil(log2 max(Wm,Hm))), i.e. ceil(log2 max(Wm,Hm)) passes,
  * after sad_jfa_seed; propagation then fills the lists to K.
- *   rec/sel_fmt/scr as in sad_topk_propagate_rec; step in [1, 65535]; cand_in,
+ *   rec/sel_fmt as in sad_topk_propagate_rec; step in [1, 65535]; cand_in,
  *   cand_out device [Hm][Wm][8], not overlapping.
  * Errors: SAD_ERR_ARG, SAD_ERR_ALIGN, SAD_ERR_DEVICE.
  */
-int sad_jfa_pass(const float *rec, int sel_fmt, const uint32_t *scr, int n_slots, const uint32_t *cand_in,
-                 uint32_t *cand_out, int W, int H, int cell, int step, void *stream);
+int sad_jfa_pass(const float *rec, int sel_fmt, int n_slots, const uint32_t *cand_in, uint32_t *cand_out, int W, int H,
+                 int cell, int step, void *stream);
 
 /*
  * sad_topk_exact -- the exact top-K map by brute force over every slot: the list

@@ -565,8 +565,8 @@ void orc_render_fwd_pixels(const double *S, int n_slots, int stride, const uint3
  * dir the dir term is 0.  Accumulator 10 is the removal delta ([SUM] B.4-B.5):
  *   Delta_k = ||c_{-k} - t||^2 - ||c - t||^2, c_{-k} the blend of the other
  *   entries renormalised (0 if they carry no weight).
- * Non-finite contributions are dropped ([SUM] B.4 "guarding NaNs").
- * Accumulation is serial in pixel order, in float64.
+ * Non-finite contributions are dropped ([SUM] B.4: the NaN guard).
+ * Accumulation is in float64 (orc_render_bwd states the order).
  */
 static void backward_pixel(long stride, int W, int H, const pix64 *X, const float *t,
                            double *grad, double *loss)
@@ -637,19 +637,45 @@ static void backward_pixel(long stride, int W, int H, const pix64 *X, const floa
     }
 }
 
-/* grad: float64 [11][stride], accumulated (+=).  loss: += sum_x ||c - t||^2. */
+/* grad: float64 [11][stride], accumulated (+=).  loss: += sum_x ||c - t||^2.
+ * The image is cut into as many bands of whole rows as there are threads; each
+ * band sums its pixels in pixel order into its own accumulators (band 0 into
+ * grad itself), and the bands are then added to grad in band order.  With one
+ * thread this is the serial sum in pixel order. */
 void orc_render_bwd(const double *S, int n_slots, int stride, const uint32_t *cand, const float *target, int W,
                     int H, int cell, double *grad, double *loss)
 {
     grid g = make_grid(W, H, cell);
-    long P = (long)W * H;
-    double L = 0.0;
-    for (long p = 0; p < P; ++p) {
-        pix64 X;
-        int col = (int)(p % W), row = (int)(p / W);
-        forward_pixel(S, (uint32_t)n_slots, stride, cand + cell_of(&g, col, row) * ORC_K, W, H, col, row, &X);
-        backward_pixel(stride, W, H, &X, target + p * 3, grad, &L);
+    int nb = g_threads < H ? g_threads : H;
+    if (nb < 1)
+        nb = 1;
+    long plane = (long)ORC_NACC * stride;
+    double *priv = nb > 1 ? calloc((size_t)(nb - 1) * plane, sizeof(double)) : NULL;
+    if (nb > 1 && !priv)
+        nb = 1;  /* no memory for the band accumulators: one band */
+    double *Lb = calloc((size_t)nb, sizeof(double));
+#pragma omp parallel for schedule(static, 1) num_threads(nb)
+    for (int b = 0; b < nb; ++b) {
+        double *gb = b == 0 ? grad : priv + (long)(b - 1) * plane;
+        long p0 = (long)W * (long)((long)H * b / nb), p1 = (long)W * (long)((long)H * (b + 1) / nb);
+        for (long p = p0; p < p1; ++p) {
+            pix64 X;
+            int col = (int)(p % W), row = (int)(p / W);
+            forward_pixel(S, (uint32_t)n_slots, stride, cand + cell_of(&g, col, row) * ORC_K, W, H, col, row, &X);
+            backward_pixel(stride, W, H, &X, target + p * 3, gb, &Lb[b]);
+        }
     }
+    double L = 0.0;
+    for (int b = 0; b < nb; ++b)
+        L += Lb[b];
+    if (nb > 1) {
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+        for (long o = 0; o < plane; ++o)
+            for (int b = 1; b < nb; ++b)
+                grad[o] += priv[(long)(b - 1) * plane + o];
+    }
+    free(priv);
+    free(Lb);
     if (loss)
         *loss += L;
 }
@@ -669,6 +695,8 @@ void orc_adam_step(double *params, double *m, double *v, double *grad, int n_slo
 {
     double bc1 = 1.0 - pow(b1, (double)step);
     double bc2 = 1.0 - pow(b2, (double)step);
+    /* slots are independent */
+#pragma omp parallel for schedule(static) num_threads(g_threads)
     for (long i = 0; i < n_slots; ++i) {
         if (!(params[i] < 0.0)) {
             for (int j = 0; j < ORC_NPARAM; ++j) {

@@ -133,7 +133,7 @@ def lib() -> ctypes.CDLL:
         L.sad_jfa_seed.restype = i32
         L.sad_jfa_seed.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp]
         L.sad_jfa_pass.restype = i32
-        L.sad_jfa_pass.argtypes = [vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, vp]
+        L.sad_jfa_pass.argtypes = [vp, i32, i32, vp, vp, i32, i32, i32, i32, vp]
         L.sad_densify_stats.restype = i32
         L.sad_densify_stats.argtypes = [fp, i32, vp, fp, i32, i32, i32, fp, vp]
         ip = ctypes.POINTER(ctypes.c_int)
@@ -309,13 +309,12 @@ def jfa_seed(rec, n_slots, cand, W, H, stream=None, cell=1):
     _check("sad_jfa_seed", lib().sad_jfa_seed(g, fmt, n_slots, c, W, H, cell, _stream(stream)))
 
 
-def jfa_pass(rec, n_slots, cand_in, cand_out, W, H, step, stream=None, cell=1, scr=None):
+def jfa_pass(rec, n_slots, cand_in, cand_out, W, H, step, stream=None, cell=1):
     """One flood pass of the jump-flood prepass: cand_in -> cand_out (see sad_jfa_pass)."""
     g, fmt = _sel(rec, n_slots)
     a = _dev(cand_in, "cand_in", _U32, map_shape(W, H, cell))
     b = _dev(cand_out, "cand_out", _U32, map_shape(W, H, cell))
-    _check("sad_jfa_pass", lib().sad_jfa_pass(g, fmt, _scr(scr, n_slots), n_slots, a, b, W, H, cell, step,
-                                              _stream(stream)))
+    _check("sad_jfa_pass", lib().sad_jfa_pass(g, fmt, n_slots, a, b, W, H, cell, step, _stream(stream)))
 
 
 def jfa_steps(W: int, H: int, cell: int = 1) -> list:
@@ -330,12 +329,12 @@ def jfa_steps(W: int, H: int, cell: int = 1) -> list:
     return out
 
 
-def jfa_prepass(rec, n_slots, a, b, W, H, stream=None, cell=1, scr=None):
+def jfa_prepass(rec, n_slots, a, b, W, H, stream=None, cell=1):
     """Seed pass into `a`, then the flood passes ping-ponging between `a` and `b`;
     returns the map that holds the result (four closest per entry)."""
     jfa_seed(rec, n_slots, a, W, H, stream, cell)
     for k in jfa_steps(W, H, cell):
-        jfa_pass(rec, n_slots, a, b, W, H, k, stream, cell, scr)
+        jfa_pass(rec, n_slots, a, b, W, H, k, stream, cell)
         a, b = b, a
     return a
 

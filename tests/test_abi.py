@@ -227,17 +227,17 @@ def test_jfa_entry_points_reject_bad_arguments(L):
     assert S(P + 8, 0, 4, P, 16, 16, 1, None) == ERR_ALIGN
     assert S(P, 0, 4, P, 70000, 16, 1, None) == ERR_ARG
     assert S(P, 0, 4, P, 0, 16, 1, None) == 0                      # empty image: no-op
-    assert J(P, 0, 0, 4, P, Q, 16, 16, 1, 0, None) == ERR_ARG         # step 0
-    assert J(P, 0, 0, 4, P, Q, 16, 16, 1, 65536, None) == ERR_ARG
-    assert J(P, 0, 0, 4, P, P + 32, 16, 16, 1, 1, None) == ERR_ARG     # overlapping maps
-    assert J(P, 0, 0, 4, P + 4, Q, 16, 16, 1, 1, None) == ERR_ALIGN
-    assert J(P, 0, 0, -1, P, Q, 16, 16, 1, 1, None) == ERR_ARG
-    assert J(P, 0, 0, 4, P, Q, 16, 0, 1, 1, None) == 0
+    assert J(P, 0, 4, P, Q, 16, 16, 1, 0, None) == ERR_ARG         # step 0
+    assert J(P, 0, 4, P, Q, 16, 16, 1, 65536, None) == ERR_ARG
+    assert J(P, 0, 4, P, P + 32, 16, 16, 1, 1, None) == ERR_ARG     # overlapping maps
+    assert J(P, 0, 4, P + 4, Q, 16, 16, 1, 1, None) == ERR_ALIGN
+    assert J(P, 0, -1, P, Q, 16, 16, 1, 1, None) == ERR_ARG
+    assert J(P, 0, 4, P, Q, 16, 0, 1, 1, None) == 0
     assert S(P, 0, 4, P, 16, 16, 0, None) == ERR_ARG            # cell 0
-    assert J(P, 0, 0, 4, P, Q, 16, 16, 0, 1, None) == ERR_ARG
-    assert J(P, 0, 0, 4, P, P + 256, 16, 16, 2, 1, None) == ERR_ARG  # 8x8 lists of 32 bytes overlap
+    assert J(P, 0, 4, P, Q, 16, 16, 0, 1, None) == ERR_ARG
+    assert J(P, 0, 4, P, P + 256, 16, 16, 2, 1, None) == ERR_ARG  # 8x8 lists of 32 bytes overlap
     assert S(P, 3, 4, P, 16, 16, 1, None) == ERR_ARG         # unknown site format
-    assert J(P, 3, 0, 4, P, Q, 16, 16, 1, 1, None) == ERR_ARG
+    assert J(P, 3, 4, P, Q, 16, 16, 1, 1, None) == ERR_ARG
 
 
 def test_densify_entry_points_reject_bad_arguments(L):

@@ -6,7 +6,7 @@ record.  It is an acceleration only, so:
 * every word is checked against the definition: decoded in float64, the cell it
   names contains the site, 2^(ca/2) >= e^{|a|/2}, 2^(cr-8) >= 2^(ca/2) max(r, 0),
   and then for random points the distance bound implies d > the threshold used;
-* propagation and the jump-flood passes give the same bits with and without it,
+* propagation gives the same bits with and without it,
   on cold-start, mid-fit and edited maps, at small and large jumps, with
   injection, and with sites the word cannot bound (huge |a| or r, inactive,
   non-finite, outside the image);
@@ -124,7 +124,7 @@ def test_propagation_is_unchanged_by_the_screen(W, H, n):
         assert np.array_equal(a1, a2), f"schedule pass {t}"
 
 
-def test_grid_and_flood_passes_are_unchanged_by_the_screen():
+def test_grid_passes_are_unchanged_by_the_screen():
     W, H, n = 203, 131, 5000
     S = _sites(n, W, H, 17)
     S_d = to_dev(S)
@@ -143,13 +143,6 @@ def test_grid_and_flood_passes_are_unchanged_by_the_screen():
                 res.append(map_to_host(b))
             assert np.array_equal(res[0], res[1]), f"cell {cell}, pass {t}"
             cin = res[1]
-        # jump-flood prepass with and without
-        outs = []
-        for sc in (scr, None):
-            a = sad.new_map(W, H, S_d.device, cell)
-            b = sad.new_map(W, H, S_d.device, cell)
-            outs.append(map_to_host(sad.jfa_prepass(rec, n, a, b, W, H, cell=cell, scr=sc)))
-        assert np.array_equal(outs[0], outs[1]), f"flood passes, cell {cell}"
 
 
 def test_edited_map_refresh_is_unchanged_by_the_screen():
