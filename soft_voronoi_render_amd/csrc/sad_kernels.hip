@@ -267,6 +267,18 @@ __global__ __launch_bounds__(256) void k_pack_sites(const float *__restrict__ S,
         P[i] = pack_site(S, stride, i);
 }
 
+// A selected list is written once and read by the next pass: stored as a
+// stream (non-temporal), so a pass's 32 bytes per entry of output do not evict
+// the site records and screen words that its gathers reuse from L2.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_list(uint4 *__restrict__ out, long p, const uint64_t (&k)[SAD_K])
+{
+    u32x4 *o = reinterpret_cast<u32x4 *>(out) + 2 * p;
+    __builtin_nontemporal_store(u32x4{(uint32_t)k[0], (uint32_t)k[1], (uint32_t)k[2], (uint32_t)k[3]}, o);
+    __builtin_nontemporal_store(u32x4{(uint32_t)k[4], (uint32_t)k[5], (uint32_t)k[6], (uint32_t)k[7]}, o + 1);
+}
+
 // ---------------------------------------------------------------------------
 // Counter-based injection (paperlayer.ai summary, Appendix B.3: the pass word and
 // the pixel ID seed xorshift).  pcg hash: Jarzynski & Olano, JCGT 2020;
@@ -738,8 +750,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
         }
     }
     const long p = (long)row * W + col;
-    cout[2 * p] = make_uint4((uint32_t)best.k[0], (uint32_t)best.k[1], (uint32_t)best.k[2], (uint32_t)best.k[3]);
-    cout[2 * p + 1] = make_uint4((uint32_t)best.k[4], (uint32_t)best.k[5], (uint32_t)best.k[6], (uint32_t)best.k[7]);
+    store_list(cout, p, best.k);
 }
 
 // Propagation pass without the tile table, for large jumps: there each neighbour
@@ -799,8 +810,7 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, Screen
         }
     }
     const long p = (long)row * W + col;
-    cout[2 * p] = make_uint4((uint32_t)best.k[0], (uint32_t)best.k[1], (uint32_t)best.k[2], (uint32_t)best.k[3]);
-    cout[2 * p + 1] = make_uint4((uint32_t)best.k[4], (uint32_t)best.k[5], (uint32_t)best.k[6], (uint32_t)best.k[7]);
+    store_list(cout, p, best.k);
 }
 
 // ---------------------------------------------------------------------------
@@ -1895,37 +1905,57 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(SiteSrc src, uint32
         sum_chunk(true);
     __syncthreads();
 
-    // phase 5: one thread per occupied slot (the compacted list) adds up the chunk
-    // partials of its bucket and turns the sums into the site's 11 gradient
-    // contributions
-    if (tid < (int)L.n_occ) {
-        const int sl = L.occ[tid];
-        const uint32_t c = L.cnt[sl];
-        const uint32_t b = L.off[sl], e = b + c - 1;
-        const uint32_t t0c = b / CHUNK, t1c = e / CHUNK;
-        const uint32_t end0 = min(t0c * CHUNK + CHUNK, total) - 1;
-        const bool starts_chunk = (b == t0c * CHUNK);
-        float v[NSUM];
-        if (t0c != t1c || starts_chunk || e == end0) {
-            const int h0 = starts_chunk ? 0 : NSUM;
+    // phase 5: eight lanes per occupied slot (the compacted list) add up the chunk
+    // partials of its bucket -- lane r takes every eighth chunk from the r-th, then
+    // the eight sums meet by lane exchanges -- and the first turns the totals into
+    // the site's 11 gradient contributions.  (A site in every list of the tile
+    // spans 256 entries, 32 chunks; one thread walking them all held the whole
+    // workgroup at the next barrier.)
+    {
+        constexpr int GRP = 8;
+        const int r = tid & (GRP - 1);
+        for (int j = tid / GRP; j < (int)L.n_occ; j += PAIR_THREADS / GRP) {
+            const int sl = L.occ[j];
+            const uint32_t c = L.cnt[sl];
+            const uint32_t b = L.off[sl], e = b + c - 1;
+            const uint32_t t0c = b / CHUNK, t1c = e / CHUNK;
+            const uint32_t end0 = min(t0c * CHUNK + CHUNK, total) - 1;
+            const bool starts_chunk = (b == t0c * CHUNK);
+            float v[NSUM];
 #pragma unroll
             for (int a = 0; a < NSUM; ++a)
-                v[a] = L.u.r.part[h0 + a][t0c];
-            for (uint32_t tc = t0c + 1; tc <= t1c; ++tc) {
+                v[a] = 0.0f;
+            if (t0c != t1c || starts_chunk || e == end0) {
+                if (r == 0) {
+                    const int h0 = starts_chunk ? 0 : NSUM;
+#pragma unroll
+                    for (int a = 0; a < NSUM; ++a)
+                        v[a] = L.u.r.part[h0 + a][t0c];
+                }
+                for (uint32_t tc = t0c + 1 + r; tc <= t1c; tc += GRP) {
+#pragma unroll
+                    for (int a = 0; a < NSUM; ++a)
+                        v[a] += L.u.r.part[a][tc];
+                }
+            } else if (r == 0) {  // a middle run: its total is already in place
 #pragma unroll
                 for (int a = 0; a < NSUM; ++a)
-                    v[a] += L.u.r.part[a][tc];
+                    v[a] = L.u.r.fin[a][sl];
             }
-        } else {  // a middle run: its total is already in place
 #pragma unroll
-            for (int a = 0; a < NSUM; ++a)
-                v[a] = L.u.r.fin[a][sl];
+            for (int o = 1; o < GRP; o <<= 1) {
+#pragma unroll
+                for (int a = 0; a < NSUM; ++a)
+                    v[a] += __shfl_xor(v[a], o, GRP);
+            }
+            if (r == 0) {
+                float acc[SAD_NACC];
+                site_grads(table_rec(L.T, sl), s, v, acc);
+#pragma unroll
+                for (int a = 0; a < SAD_NACC; ++a)
+                    L.u.r.fin[a][sl] = acc[a];
+            }
         }
-        float acc[SAD_NACC];
-        site_grads(table_rec(L.T, sl), s, v, acc);
-#pragma unroll
-        for (int a = 0; a < SAD_NACC; ++a)
-            L.u.r.fin[a][sl] = acc[a];
     }
     __syncthreads();
 
