@@ -9,11 +9,11 @@ gradients through the per-tile reduction) and Adam (sad_adam_step_rec), K = 8.
 Default workload: img2048 -- 2048x2048 RGB float32, N = 131,072 sites placed by
 gradient-weighted sampling of a seeded photo-like image (mid-grey, 64 random
 convex polygons, 32 plane waves), 4 injected candidates per pixel, a 500-iteration
-fit: the coarse-to-fine warm-up (jumps 1024, 512, ..., 1, one pass per
-iteration), then one pass at jump 1 per iteration.
+fit: the coarse-to-fine warm-up passes (jumps 1024, 512, ..., 1) before the first
+iteration's render, then one pass at jump 1 per iteration.
 
-Timing.  The fit is captured in three HIP graphs -- the warm-up passes (the
-cold start), the rest of the `--warmup` iterations, and the `--steps` timed
+Timing.  The fit is captured in three HIP graphs -- the first iteration with
+the warm-up passes (the cold start), the rest of the `--warmup` iterations, and the `--steps` timed
 iterations -- and replayed in order from the initial state; only the last replay
 is timed, so every timed step runs the same launches (jump-1 propagation,
 fused forward+backward, Adam) and ms_per_step does not depend on --steps.  The
@@ -317,7 +317,8 @@ def main():
     S0_d = torch.from_numpy(S0).to(dev)
     fit = sad.Fitter(S0_d.clone(), N, tgt, W, H, n_inject=wl.n_inject, seed=synth.SEED_INJECT)
     stream = torch.cuda.current_stream()
-    n_cold = (max(W, H) - 1).bit_length()  # warm-up passes: jumps B/2 .. 1
+    n_warm_passes = (max(W, H) - 1).bit_length()  # warm-up passes: jumps B/2 .. 1
+    n_cold = 1  # the first iteration runs them all before its render
     warmup = max(args.warmup, n_cold)
 
     def reset_gpu():
@@ -451,12 +452,14 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name, "W": W, "H": H, "n_sites": N, "K": 8, "n_inject": wl.n_inject,
-            "schedule": f"{n_cold} warm-up passes (jumps B/2..1, one per iteration), then jump 1 every iteration",
+            "schedule": f"{n_warm_passes} warm-up passes (jumps B/2..1) before the first render, then jump 1 "
+                        "every iteration",
             "timed": f"iterations {warmup}..{warmup + args.steps - 1} of the fit (steady state)",
             "graph": not args.no_graph,
             "step_algorithmic_bytes": B,
             "hbm_frac_whole_step": round(B / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "cold_start_ms": round(cold_ms, 3), "cold_start_iterations": n_cold,
+            "cold_start_ms": round(cold_ms, 3),
+            "cold_start": f"the first iteration: {n_warm_passes} warm-up passes, then render, backward, Adam",
             "fit_ms": round(fit_ms, 3), "fit_iterations": warmup + args.steps,
             "fit_mpixel_iters_per_s": round(P * (warmup + args.steps) / (fit_ms * 1e-3) / 1e6, 2),
             "psnr_db_after": round(float(psnr), 3), "exact_top8_fraction_after": round(exact_frac, 4),
@@ -496,13 +499,16 @@ def cpu_baseline(wl, S0, target, budget_s):
     v = np.zeros((10, S.shape[1]))
     grad = np.zeros((11, S.shape[1]))
     lr = np.array([0.1, 0.1, 0.02, 0.05, 0.01, 0.01, 0.01, 0.02, 0.02, 0.02])
-    sched = oracle.jump_schedule(W, H, 10_000)
-    it, t_used = 0, 0.0
+    n_warm = (max(W, H) - 1).bit_length()
+    sched = oracle.jump_schedule(W, H, n_warm + 10_000)
+    it, t_used, passes = 0, 0.0, 0
     phase = {"propagate": 0.0, "fwd": 0.0, "bwd": 0.0, "adam": 0.0}
     while t_used < budget_s and it < 10_000:
         t0 = time.perf_counter()
         S32 = params.astype(np.float32)
-        cand = oracle.propagate(S32, N, cand, W, H, sched[it], it, synth.SEED_INJECT, wl.n_inject)
+        for _ in range(n_warm if it == 0 else 1):  # the warm-up passes before the first render
+            cand = oracle.propagate(S32, N, cand, W, H, sched[passes], passes, synth.SEED_INJECT, wl.n_inject)
+            passes += 1
         t1 = time.perf_counter()
         oracle.render_fwd(params, N, cand, W, H)
         t2 = time.perf_counter()

@@ -658,12 +658,16 @@ class Fitter:
     image-space kernels read).  Everything runs in libsad kernels on one stream;
     nothing crosses to the host inside an iteration.
 
-    The coarse-to-fine warm-up (jumps B/2 .. 1) runs one pass per iteration; after
-    it the candidate field is refreshed every `refresh_every` iterations with
+    The coarse-to-fine warm-up (jumps B/2 .. 1) runs before the first render
+    (`warmup="first"`), or one pass per iteration (`"interleaved"`); after it the
+    candidate field is refreshed every `refresh_every` iterations with
     `passes_per_refresh` propagation passes (paperlayer.ai summary, section 4 and
-    B.3: warm-up first, then updates; both the update frequency and the passes per
-    update are exposed, and 8-16 iterations between updates left the final PSNR
-    unchanged there).  The pass counter drives the jump schedule and the
+    B.3: the long-range warm-up comes first and the regular updates after it; both
+    the update frequency and the passes per update are exposed, and 8-16
+    iterations between updates left the final PSNR unchanged there).  Rendering
+    and back-propagating through the half-built lists of an interleaved warm-up
+    is what the first iterations spend most of their time on: a tile's lists then
+    name a thousand random sites.  The pass counter drives the jump schedule and the
     injection's pass index.  `cell` > 1 keeps the candidate map on the downscaled
     grid of B.3 "Candidate field" (ceil(W/cell) x ceil(H/cell) lists).  With
     `packed` the candidate passes read the 16-byte float16 candidate-site buffer
@@ -675,9 +679,12 @@ class Fitter:
     def __init__(self, sites: torch.Tensor, n_slots: int, target: torch.Tensor, W: int, H: int,
                  n_inject: int = 4, seed: int = 4, adam: AdamConfig | None = None, cand: torch.Tensor | None = None,
                  refresh_every: int = 1, passes_per_refresh: int = 1, cell: int = 1, packed: bool = False,
-                 screen: bool = True):
+                 screen: bool = True, warmup: str = "first"):
         if refresh_every < 1 or passes_per_refresh < 0:
             raise ValueError("refresh_every >= 1 and passes_per_refresh >= 0")
+        if warmup not in ("first", "interleaved"):
+            raise ValueError("warmup is 'first' or 'interleaved'")
+        self.warmup = warmup
         dev = sites.device
         self.W, self.H, self.n_slots, self.n_inject, self.seed = W, H, n_slots, n_inject, seed
         self.cell = cell
@@ -742,8 +749,13 @@ class Fitter:
         it = self.it
         warm = (max(self.Wm, self.Hm) - 1).bit_length()  # log2 B passes with jumps B/2 .. 1
         if self.passes < warm:
-            self.propagate(self.jump_at(self.passes), self.passes, stream)
-            self.passes += 1
+            # the coarse-to-fine warm-up: all of it before the first render, or
+            # one pass per iteration
+            while self.passes < warm:
+                self.propagate(self.jump_at(self.passes), self.passes, stream)
+                self.passes += 1
+                if self.warmup == "interleaved":
+                    break
             self.warm_end = it + 1
         elif (it - self.warm_end) % self.refresh_every == 0:
             for _ in range(self.passes_per_refresh):

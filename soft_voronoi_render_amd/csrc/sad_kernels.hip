@@ -486,11 +486,10 @@ __device__ __forceinline__ float key_score(uint64_t key)
 
 // True when site id scored at (X, Y) provably ranks after `kth` (the key of the
 // list's K-th entry; ~0 while the list has a free place).
-__device__ __forceinline__ bool screened_out(const Screen &sc, uint32_t id, float X, float Y, uint64_t kth)
+__device__ __forceinline__ bool screened_out_word(const Screen &sc, uint32_t v, float X, float Y, uint64_t kth)
 {
-    if (!sc.w || kth == ~0ull)
+    if (kth == ~0ull)
         return false;
-    const uint32_t v = sc.w[id];
     const uint32_t ca = (v >> 24) & 15u, cr = v >> 28;
     if (ca == 15u || cr == 15u)
         return false;
@@ -502,6 +501,32 @@ __device__ __forceinline__ bool screened_out(const Screen &sc, uint32_t id, floa
     const float kd = fmaxf(key_score(kth), 0.0f) * sc.inv_s;
     const float B = fmaf(Ahat * kd, 1.0009766f, Rhat) + fmaf(Rhat, 1.5258789e-5f, 0.015625f);
     return dx * dx + dy * dy > B * B;
+}
+
+__device__ __forceinline__ bool screened_out(const Screen &sc, uint32_t id, float X, float Y, uint64_t kth)
+{
+    return sc.w && kth != ~0ull && screened_out_word(sc, sc.w[id], X, Y, kth);
+}
+
+// Offers the n_inject injected IDs of map entry `pix` to its list (summary, B.3;
+// the draw is described at sad_topk_propagate), each screened before its record
+// is fetched.  (Loading the screen words of the first eight when the pass starts,
+// to hide their latency, was measured slower: 191 -> 199 us at img2048.)
+template <int FMT>
+__device__ __forceinline__ void inject(const SiteSrc &src, const Screen &sc, uint32_t seed_h, uint32_t pix,
+                                       uint32_t n_slots, int n_inject, float X, float Y, float s, TopK64 &best)
+{
+    const uint32_t h = pcg_hash(seed_h ^ pix);
+    uint32_t x = h ? h : 0x9E3779B9u;
+    for (int j = 0; j < n_inject; ++j) {
+        x = xorshift32(x);
+        const uint32_t c = (uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32);
+        if (c < n_slots && !screened_out(sc, c, X, Y, best.k[K - 1])) {
+            bool usable;
+            const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
+            best.consider(c, d, usable);
+        }
+    }
 }
 
 // Screen words of slots [0, n_slots) (see screen_word; qsx = 4096/W, qsy = 4096/H).
@@ -736,19 +761,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
         }
     }
     // injected IDs (summary, B.3), screened before their records are fetched
-    if (n_inject > 0) {
-        const uint32_t h = pcg_hash(seed_h ^ ((uint32_t)row * (uint32_t)W + (uint32_t)col));
-        uint32_t x = h ? h : 0x9E3779B9u;
-        for (int j = 0; j < n_inject; ++j) {
-            x = xorshift32(x);
-            const uint32_t c = (uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32);
-            if (c < n_slots && !screened_out(sc, c, X, Y, best.k[K - 1])) {
-                bool usable;
-                const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
-                best.consider(c, d, usable);
-            }
-        }
-    }
+    inject<FMT>(src, sc, seed_h, (uint32_t)row * (uint32_t)W + (uint32_t)col, n_slots, n_inject, X, Y, s, best);
     const long p = (long)row * W + col;
     store_list(cout, p, best.k);
 }
@@ -796,19 +809,7 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, Screen
             }
         }
     }
-    if (n_inject > 0) {
-        const uint32_t h = pcg_hash(seed_h ^ ((uint32_t)row * (uint32_t)W + (uint32_t)col));
-        uint32_t x = h ? h : 0x9E3779B9u;
-        for (int j = 0; j < n_inject; ++j) {
-            x = xorshift32(x);
-            const uint32_t c = (uint32_t)(((uint64_t)x * (uint64_t)n_slots) >> 32);
-            if (c < n_slots && !screened_out(sc, c, X, Y, best.k[K - 1])) {
-                bool usable;
-                const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
-                best.consider(c, d, usable);
-            }
-        }
-    }
+    inject<FMT>(src, sc, seed_h, (uint32_t)row * (uint32_t)W + (uint32_t)col, n_slots, n_inject, X, Y, s, best);
     const long p = (long)row * W + col;
     store_list(cout, p, best.k);
 }
