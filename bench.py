@@ -56,8 +56,8 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 KERNEL_SRC = os.path.join(ROOT, "soft_voronoi_render_amd", "csrc", "sad_kernels.hip")
 # kernel symbol of each timed launch (as rocprofv3 names it)
-KERNEL_SYMBOL = {"propagate": "k_propagate<1,256,0>", "fwd_bwd": "k_render_bwd", "adam": "k_adam",
-                 "fwd": "k_render_fwd"}
+KERNEL_SYMBOL = {"propagate": "k_propagate<1,256,0>", "fwd_bwd": "k_render_bwd<0,0>", "adam": "k_adam<0>",
+                 "fwd": "k_render_fwd<0>"}
 STEP_KERNELS = ("propagate", "fwd_bwd", "adam")
 
 
