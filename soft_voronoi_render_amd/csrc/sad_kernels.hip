@@ -552,10 +552,28 @@ struct PropShared {
         float4 rec0[TB];                        // scoring record, bytes 0..15
     } t;
     float4 rec1[TB];                            // scoring record, bytes 16..31
-    uint4 ref0[BLOCK + 4 * TILE * KK];          // per region list: entries 0..3 (slots / spilled IDs)
-    uint4 ref1[BLOCK + 4 * TILE * KK];          // entries 4..7
+    uint4 ref[BLOCK + 4 * TILE * KK];           // per region list: 8 x 16-bit refs (REF16_*)
     uint32_t seen[TB / 32][BLOCK];              // per pixel: slots already taken (word-major)
 };
+
+// A list entry's table reference in 16 bits: the slot, or REF16_SPILL (the ID
+// found no slot: it is read again from the list in global memory), or
+// REF16_NONE (no site).  Half the LDS of 32-bit refs: 21 KB per workgroup, so
+// seven workgroups fit a CU instead of six.
+constexpr uint32_t REF16_NONE = 0xFFFFu, REF16_SPILL = 0xFFFEu;
+
+template <int TB>
+__device__ __forceinline__ uint32_t ref16(uint32_t ref)
+{
+    return ref < (uint32_t)TB ? ref : ref == REF_NONE ? REF16_NONE : REF16_SPILL;
+}
+
+template <int TB>
+__device__ __forceinline__ uint4 pack_refs16(const uint32_t (&r)[K])
+{
+    return make_uint4(ref16<TB>(r[0]) | ref16<TB>(r[1]) << 16, ref16<TB>(r[2]) | ref16<TB>(r[3]) << 16,
+                      ref16<TB>(r[4]) | ref16<TB>(r[5]) << 16, ref16<TB>(r[6]) | ref16<TB>(r[7]) << 16);
+}
 
 // Absolute pixel of region list r: the own block, then the left, right, top and
 // bottom strips, each KK lists across by 16 along the tile edge (only the first
@@ -628,9 +646,8 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
         const uint32_t sids[2] = {q2.x, q2.y};
         uint32_t srefs[2];
         table_insert_ids<TB>(L.t.key, sids, n_slots, srefs);
-        L.ref0[tid] = make_uint4(refs[0], refs[1], refs[2], refs[3]);
-        L.ref1[tid] = make_uint4(refs[4], refs[5], refs[6], refs[7]);
-        reinterpret_cast<uint2 *>(qq < 2 ? &L.ref0[sr] : &L.ref1[sr])[qq & 1] = make_uint2(srefs[0], srefs[1]);
+        L.ref[tid] = pack_refs16<TB>(refs);
+        reinterpret_cast<uint32_t *>(&L.ref[sr])[qq] = ref16<TB>(srefs[0]) | ref16<TB>(srefs[1]) << 16;
     } else {
         for (int r = tid; r < nlists; r += BLOCK) {
             int pc, pr, across;
@@ -644,8 +661,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
             const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
             uint32_t refs[K];
             table_insert_ids<TB>(L.t.key, ids, n_slots, refs);
-            L.ref0[r] = make_uint4(refs[0], refs[1], refs[2], refs[3]);
-            L.ref1[r] = make_uint4(refs[4], refs[5], refs[6], refs[7]);
+            L.ref[r] = pack_refs16<TB>(refs);
         }
     }
     __syncthreads();
@@ -681,10 +697,15 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
         return (atomicOr(&L.seen[sl >> 5][tid], bit) & bit) == 0u;
     };
 
+    // entry e of the list of pixel (pc, pr), read again from global memory (spills)
+    auto list_id = [&](int pc, int pr, int e) {
+        return reinterpret_cast<const uint32_t *>(cin)[(size_t)K * ((size_t)pr * W + pc) + e];
+    };
     TopK64 best;
     // own list: score its (deduplicated) table entries and sort them with a network
-    const uint4 oa = L.ref0[tid], ob = L.ref1[tid];
-    const uint32_t orefs[K] = {oa.x, oa.y, oa.z, oa.w, ob.x, ob.y, ob.z, ob.w};
+    const uint4 o16 = L.ref[tid];
+    const uint32_t orefs[K] = {o16.x & 0xFFFFu, o16.x >> 16, o16.y & 0xFFFFu, o16.y >> 16,
+                               o16.z & 0xFFFFu, o16.z >> 16, o16.w & 0xFFFFu, o16.w >> 16};
     {
         uint64_t v[K];
 #pragma unroll
@@ -703,9 +724,8 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const uint32_t ref = orefs[k];
-        if (ref != REF_NONE && ref >= (uint32_t)TB) {
-            const uint32_t c = ref & ~REF_SPILL;
+        if (orefs[k] == REF16_SPILL) {
+            const uint32_t c = list_id(col, row, k);
             bool usable;
             const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
             best.consider(c, d, usable);
@@ -731,12 +751,13 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
         const int r = li == 0 ? r_l : li == 1 ? r_r : li == 2 ? r_t : r_b;
         if (r < 0)
             continue;
-        const uint4 a = L.ref0[r], b = L.ref1[r];
-        const uint32_t refs[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const uint4 a = L.ref[r];
+        const uint32_t refs[K] = {a.x & 0xFFFFu, a.x >> 16, a.y & 0xFFFFu, a.y >> 16,
+                                  a.z & 0xFFFFu, a.z >> 16, a.w & 0xFFFFu, a.w >> 16};
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const uint32_t ref = refs[k];
-            const bool f = ref < (uint32_t)TB ? take(ref) : ref != REF_NONE;
+            const bool f = ref < (uint32_t)TB ? take(ref) : ref != REF16_NONE;
             fresh |= f ? (1u << (li * K + k)) : 0u;
         }
     }
@@ -746,14 +767,16 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
         const int li = j / K;
         const int r = li == 0 ? r_l : li == 1 ? r_r : li == 2 ? r_t : r_b;
         const int e = j % K;
-        const uint32_t ref = reinterpret_cast<const uint32_t *>(e < 4 ? L.ref0 : L.ref1)[4 * r + (e & 3)];
+        const uint32_t ref = reinterpret_cast<const uint16_t *>(&L.ref[r])[e];
         bool usable;
         if (ref < (uint32_t)TB) {
             uint32_t id;
             const float d = rec_score_slot(ref, usable, id);
             best.consider_new(id, d, usable);
         } else {
-            const uint32_t c = ref & ~REF_SPILL;
+            // a spilled entry: its ID from the neighbour's list in global memory
+            const uint32_t c = list_id(li == 0 ? col - jump : li == 1 ? col + jump : col,
+                                       li == 2 ? row - jump : li == 3 ? row + jump : row, e);
             if (!screened_out(sc, c, X, Y, best.k[K - 1])) {
                 const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
                 best.consider(c, d, usable);
@@ -1527,6 +1550,25 @@ __device__ __forceinline__ PairSums pair_sums(float x, int half)
     return {lo + hi, half ? lo : hi};
 }
 
+// The sum over each aligned group of 8 lanes, in every lane of the group: the
+// partner across the pair (quad_perm [1,0,3,2]), across the quad ([2,3,0,1]),
+// then across the half row (row_half_mirror: lane i of the 8 reads lane 7 - i,
+// which lies in the other quad).  Three DPP moves, no LDS; the same additions in
+// the same order as exchanging with lanes i^1, i^2, i^4.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float group8_sum(float x)
+{
+    x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x);  // row_half_mirror
+    return x;
+}
+
 __device__ __forceinline__ float pair_max(float x)
 {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -1955,11 +1997,8 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(SiteSrc src, uint32
                     v[a] = L.u.r.fin[a][sl];
             }
 #pragma unroll
-            for (int o = 1; o < GRP; o <<= 1) {
-#pragma unroll
-                for (int a = 0; a < NSUM; ++a)
-                    v[a] += __shfl_xor(v[a], o, GRP);
-            }
+            for (int a = 0; a < NSUM; ++a)
+                v[a] = group8_sum(v[a]);
             if (r == 0) {
                 float acc[SAD_NACC];
                 site_grads(table_rec(L.T, sl), s, v, acc);
