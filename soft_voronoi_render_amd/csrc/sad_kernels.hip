@@ -1561,6 +1561,27 @@ __device__ __forceinline__ float dpp_f(float x)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes (lanes whose DPP source lies outside
+// the row add 0): within each 16-lane row by row_shr 1, 2, 4, 8, then the last
+// lane of row 0 and of row 2 into rows 1 and 3 (row_bcast:15), then lane 31 into
+// rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
+{
+    x += dpp_u<0x111, 0xF>(x);
+    x += dpp_u<0x112, 0xF>(x);
+    x += dpp_u<0x114, 0xF>(x);
+    x += dpp_u<0x118, 0xF>(x);
+    x += dpp_u<0x142, 0xA>(x);
+    x += dpp_u<0x143, 0xC>(x);
+    return x;
+}
+
 __device__ __forceinline__ float group8_sum(float x)
 {
     x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
@@ -1709,15 +1730,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(SiteSrc src, uint32
         const uint4 c4 = reinterpret_cast<const uint4 *>(L.cnt)[lane];
         const uint32_t s0 = c4.x, s1 = s0 + c4.y, s2 = s1 + c4.z, s3 = s2 + c4.w;
         const uint32_t n0 = c4.x > 0, n1 = n0 + (c4.y > 0), n2 = n1 + (c4.z > 0), n3 = n2 + (c4.w > 0);
-        uint32_t incl = s3, nincl = n3;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t v = __shfl_up(incl, o, 64), w = __shfl_up(nincl, o, 64);
-            if (lane >= o) {
-                incl += v;
-                nincl += w;
-            }
-        }
+        const uint32_t incl = wave_incl_scan(s3), nincl = wave_incl_scan(n3);
         const uint32_t base = incl - s3, nbase = nincl - n3;
         reinterpret_cast<uint4 *>(L.off)[lane] = make_uint4(base, base + s0, base + s1, base + s2);
         if (c4.x > 0)
@@ -1864,14 +1877,16 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(SiteSrc src, uint32
     }
     if (half == 0)
         L.g[pp] = make_float4(g0, g1, g2, 0.0f);
-    // per-pixel loss (counted once per pair): wave sums
+    // per-pixel loss (counted once per pair): wave sums -- each 8-lane group by
+    // DPP moves, then the eight group sums read from their first lanes
     {
-        float v = half == 0 ? err : 0.0f;
+        const float v = group8_sum(half == 0 ? err : 0.0f);
+        float w = 0.0f;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1)
-            v += __shfl_xor(v, o, 64);
+        for (int g = 0; g < 8; ++g)
+            w += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 8 * g));
         if (lane == 0)
-            L.wsum[tid >> 6] = v;
+            L.wsum[tid >> 6] = w;
     }
     __syncthreads();
     if (tid == 0 && loss_sum) {
