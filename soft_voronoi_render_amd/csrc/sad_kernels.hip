@@ -1114,6 +1114,8 @@ __device__ __forceinline__ SiteRec load_rec_global(const SiteSrc &src, uint32_t 
         d = G[RLD4 * (size_t)c + 3];
     }
     SiteRec R;
+    // an inactive site or one with a non-finite colour is unusable: px = NaN makes
+    // its score NaN, and its colour is 0 so that a zero weight times it adds 0
     const bool ok = !(a.x < 0.0f) && finitef(cc.x) && finitef(cc.y) && finitef(cc.z);
     R.v[R_PX] = ok ? a.x : __builtin_nanf("");
     R.v[R_PY] = a.y;
@@ -1123,9 +1125,9 @@ __device__ __forceinline__ SiteRec load_rec_global(const SiteSrc &src, uint32_t 
     R.v[R_E] = d.z;
     R.v[R_IE] = d.w;
     R.v[R_TAU] = b.w;
-    R.v[R_C0] = cc.x;
-    R.v[R_C1] = cc.y;
-    R.v[R_C2] = cc.z;
+    R.v[R_C0] = ok ? cc.x : 0.0f;
+    R.v[R_C1] = ok ? cc.y : 0.0f;
+    R.v[R_C2] = ok ? cc.z : 0.0f;
     R.v[R_INVN] = cc.w;
     return R;
 }
@@ -1236,9 +1238,10 @@ __device__ __forceinline__ void blend_pixel(const TileTable &T, const SiteSrc &s
         const float l = -R.v[R_TAU] * rec_score(R, X, Y, s);
         B.use[k] = finitef(l);
         B.l[k] = l;
-        B.c0[k] = B.use[k] ? R.v[R_C0] : 0.0f;
-        B.c1[k] = B.use[k] ? R.v[R_C1] : 0.0f;
-        B.c2[k] = B.use[k] ? R.v[R_C2] : 0.0f;
+        // finite (0 for an unusable record); an entry not used gets weight 0
+        B.c0[k] = R.v[R_C0];
+        B.c1[k] = R.v[R_C1];
+        B.c2[k] = R.v[R_C2];
     };
     bool spilled = false;
 #pragma unroll
@@ -1619,9 +1622,10 @@ __device__ __forceinline__ void pair_blend(const TileTable &T, const SiteSrc &sr
         const float lk = -R.v[R_TAU] * rec_score(R, X, Y, s);
         B.use[k] = finitef(lk);
         B.l[k] = lk;
-        B.c0[k] = B.use[k] ? R.v[R_C0] : 0.0f;
-        B.c1[k] = B.use[k] ? R.v[R_C1] : 0.0f;
-        B.c2[k] = B.use[k] ? R.v[R_C2] : 0.0f;
+        // finite (0 for an unusable record); an entry not used gets weight 0
+        B.c0[k] = R.v[R_C0];
+        B.c1[k] = R.v[R_C1];
+        B.c2[k] = R.v[R_C2];
     };
     bool spilled = false;
 #pragma unroll
@@ -1921,6 +1925,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(SiteSrc src, uint32
     // The chunk's runs: summed with entry_acc; if a run's totals are not all
     // finite (a non-finite entry), the chunk is summed again with entry_sums, which
     // drops the non-finite sums of each entry, and its partials are rewritten.
+    const float X0 = (float)col0 + 0.5f, Y0 = (float)row0 + 0.5f;  // exact: integers and halves
     auto sum_chunk = [&](bool checked) {
         float run[NSUM];
 #pragma unroll
@@ -1953,8 +1958,7 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(SiteSrc src, uint32
                     Rc = table_rec(L.T, cur);
                 }
                 const int q = (int)(mps[j] & 0xFFu);
-                const float Xp = (float)(col0 + (q & (TILE - 1))) + 0.5f;
-                const float Yp = (float)(row0 + q / TILE) + 0.5f;
+                const float Xp = (float)(q & (TILE - 1)) + X0, Yp = (float)(q / TILE) + Y0;
                 if (checked) {
                     float v[NSUM];
                     entry_sums(Rc, Xp, Yp, mw[j], mg[j], md[j], L.g[q], v);
