@@ -68,6 +68,23 @@ def test_propagate_edge_inputs(orc):
     assert np.array_equal(_gpu_propagate(S, n, cin, W, H, 2, 3, 5, 6), _gpu_propagate(S, n, cin, W, H, 2, 3 + 65536, 5, 6))
 
 
+@pytest.mark.parametrize("seed", [21, 22])
+def test_propagate_table_overflow_at_jump_1(orc, seed):
+    """Lists of uniformly random sites at jump 1: every tile names far more sites
+    than its 256-slot table holds, so own and neighbour entries take the spill
+    path (their IDs read again from the input map); sentinels and duplicates
+    mixed in."""
+    W, H, n = 67, 45, 20000
+    print(f"propagate overflow jump=1 seed={seed}", flush=True)
+    S = synth.random_sites(n, W, H, seed)
+    cin = synth.random_map(W, H, n, seed=seed + 1, p_invalid=0.1, p_dup=0.1)
+    got = _gpu_propagate(S, n, cin, W, H, 1, 31, 77, 4)
+    ref = orc.propagate(S, n, cin, W, H, 1, 31, 77, 4)
+    pix = np.arange(W * H)
+    u, cnt = orc.union_pixels(S, n, cin, W, H, 1, 31, 77, 4, pix)
+    assert compare_lists(orc, S, n, W, H, pix, got, ref, u, cnt) <= 2
+
+
 def test_propagate_schedule_from_empty_matches_oracle_each_pass(orc):
     """The warm-up schedule from an all-sentinel map: every pass compared with the
     oracle on the oracle's previous output (shared input), then recall."""
