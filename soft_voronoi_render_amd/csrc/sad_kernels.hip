@@ -311,9 +311,9 @@ __device__ __forceinline__ uint32_t xorshift32(uint32_t x)
 constexpr uint32_t REF_NONE = 0xFFFFFFFFu;
 constexpr uint32_t REF_SPILL = 0x80000000u;  // | site ID
 
-template <int TB, int N>
+template <int TB, int N, bool COUNT = false>
 __device__ __forceinline__ void table_insert_ids(uint32_t *key, const uint32_t (&ids)[N], uint32_t n_slots,
-                                                 uint32_t (&refs)[N])
+                                                 uint32_t (&refs)[N], uint32_t *n_new = nullptr)
 {
     constexpr int SHIFT = TB == 256 ? 24 : 23;
     static_assert(TB == 256 || TB == 512, "table size");
@@ -329,6 +329,8 @@ __device__ __forceinline__ void table_insert_ids(uint32_t *key, const uint32_t (
                 const uint32_t sl = (h0 + (uint32_t)pr * step) & (TB - 1);
                 const uint32_t prev = atomicCAS(&key[sl], NONE, c);
                 if (prev == NONE || prev == c) {
+                    if (COUNT && prev == NONE)
+                        atomicAdd(n_new, 1u);  // distinct IDs of the lists inserted
                     r = sl;
                     break;
                 }
@@ -789,12 +791,12 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
     store_list(cout, p, best.k);
 }
 
-// Propagation pass without the tile table, for large jumps: there each neighbour
-// list is read by exactly one pixel of the tile, so hashing it buys no sharing.
-// Every candidate is scored from its site record (two 16-byte loads) and goes
-// through the same (d, ID) selection with a duplicate check.  TW x TW map entries
-// per workgroup: 16 for maps large enough to fill the chip with 16x16 tiles, 8
-// for small (downscaled) maps, which would otherwise leave most CUs idle.
+// Propagation pass without a tile table, for the downscaled candidate grid (a
+// tile of cells names more sites than a table holds): every candidate is scored
+// from its site record (two 16-byte loads) and goes through the same (d, ID)
+// selection with a duplicate check.  TW x TW map entries per workgroup: 16 for
+// maps large enough to fill the chip with 16x16 tiles, 8 for small maps, which
+// would otherwise leave most CUs idle.
 template <int TW, int FMT>
 __global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, Screen sc, uint32_t n_slots,
                                                              const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
@@ -846,6 +848,149 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, Screen
     inject<FMT>(src, sc, seed_h, (uint32_t)row * (uint32_t)W + (uint32_t)col, n_slots, n_inject, X, Y, s, best);
     const long p = (long)row * W + col;
     store_list(cout, p, best.k);
+}
+
+// Propagation pass for jumps >= 2 on a per-pixel map, with the tile table sized
+// for five regions.  Every lane holds its own list and its four lists at +-jump
+// (for jump >= 16 these are four 16x16 blocks beside the tile; below that they
+// overlap it) and their IDs go into a 512-slot LDS table, so a distinct site's
+// scoring record is gathered once per tile instead of once per candidate.  A
+// tile whose own lists already name more than WIDE_OWN_MAX sites (random lists
+// early in a cold start) would only overflow the table: it scores its neighbour
+// candidates from their records, as the table-free pass does, and so do IDs a
+// full table cannot hold.
+constexpr int WTB = 512;
+constexpr int WIDE_OWN_MAX = 96;
+
+struct WideShared {
+    union {
+        uint32_t key[WTB];
+        float4 rec0[WTB];  // scoring record, bytes 0..15
+    } t;
+    float4 rec1[WTB];      // bytes 16..31; the slot's ID in the last word
+    uint32_t n_own;        // distinct IDs of the tile's own lists
+};
+
+template <int FMT>
+__global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc, uint32_t n_slots,
+                                                          const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
+                                                          int W, int H, int jump, uint32_t seed_h, int n_inject,
+                                                          float s, int tiles_x, int nb)
+{
+    __shared__ WideShared L;
+    const int tid = threadIdx.x;
+    const int t = xcd_band(blockIdx.x, nb);
+    const int col = (t % tiles_x) * TILE + (tid & (TILE - 1));
+    const int row = (t / tiles_x) * TILE + tid / TILE;
+    const bool inside = col < W && row < H;
+    for (int sl = tid; sl < WTB; sl += BLOCK)
+        L.t.key[sl] = NONE;
+    if (tid == 0)
+        L.n_own = 0u;
+    // the five lists: own, left, right, top, bottom (NONE outside the image)
+    uint32_t ids[5][K];
+#pragma unroll
+    for (int li = 0; li < 5; ++li) {
+        const int c = li == 1 ? col - jump : li == 2 ? col + jump : col;
+        const int r = li == 3 ? row - jump : li == 4 ? row + jump : row;
+        uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
+        if (inside && c >= 0 && c < W && r >= 0 && r < H) {
+            const long q = (long)r * W + c;
+            a = cin[2 * q];
+            b = cin[2 * q + 1];
+        }
+        ids[li][0] = a.x; ids[li][1] = a.y; ids[li][2] = a.z; ids[li][3] = a.w;
+        ids[li][4] = b.x; ids[li][5] = b.y; ids[li][6] = b.z; ids[li][7] = b.w;
+    }
+    __syncthreads();
+    uint32_t refs[5][K];
+    table_insert_ids<WTB, K, true>(L.t.key, ids[0], n_slots, refs[0], &L.n_own);
+    __syncthreads();
+    const bool coherent = L.n_own <= (uint32_t)WIDE_OWN_MAX;
+    if (coherent) {
+#pragma unroll
+        for (int li = 1; li < 5; ++li)
+            table_insert_ids<WTB, K>(L.t.key, ids[li], n_slots, refs[li]);
+    } else {
+#pragma unroll
+        for (int li = 1; li < 5; ++li)
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                refs[li][k] = ids[li][k] < n_slots ? (REF_SPILL | ids[li][k]) : REF_NONE;
+    }
+    __syncthreads();
+    // one scoring record per occupied slot, two slots per lane
+    {
+        uint32_t c[WTB / BLOCK];
+        float4 g0[WTB / BLOCK], g1[WTB / BLOCK];
+#pragma unroll
+        for (int j = 0; j < WTB / BLOCK; ++j) {
+            c[j] = L.t.key[tid + j * BLOCK];
+            g0[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            g1[j] = g0[j];
+            if (c[j] != NONE)
+                load_sel<FMT>(src, c[j], g0[j], g1[j]);
+            g1[j].w = __uint_as_float(c[j]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < WTB / BLOCK; ++j) {
+            if (c[j] != NONE) {
+                L.t.rec0[tid + j * BLOCK] = g0[j];
+                L.rec1[tid + j * BLOCK] = g1[j];
+            }
+        }
+    }
+    __syncthreads();
+    if (!inside)
+        return;
+    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    TopK64 best;
+    // own list: its table entries (an ID the list repeats keeps its first place
+    // only), sorted with the network; then entries the table could not hold
+    {
+        uint64_t v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t ref = refs[0][k];
+            bool dup = false;
+#pragma unroll
+            for (int j = 0; j < k; ++j)
+                dup |= refs[0][j] == ref;
+            v[k] = ~0ull;
+            if (ref < (uint32_t)WTB && !dup) {
+                const float4 g0 = L.t.rec0[ref], g1 = L.rec1[ref];
+                const float d = geom_score(g0, g1, X, Y, s);
+                if (!(g0.x < 0.0f) && finitef(d))
+                    v[k] = rank_key(d, __float_as_uint(g1.w));
+            }
+        }
+        best.set_sorted(v);
+    }
+    // the neighbour lists (their IDs may repeat the list's: consider() checks),
+    // and every entry the table does not hold, from its record in global memory
+#pragma unroll
+    for (int li = 0; li < 5; ++li) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t ref = refs[li][k];
+            if (ref < (uint32_t)WTB) {
+                if (li > 0) {
+                    const float4 g0 = L.t.rec0[ref], g1 = L.rec1[ref];
+                    best.consider(__float_as_uint(g1.w), geom_score(g0, g1, X, Y, s), !(g0.x < 0.0f));
+                }
+            } else if (ref != REF_NONE) {
+                const uint32_t c = ref & ~REF_SPILL;
+                if (!best.holds(c)) {
+                    bool usable;
+                    const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
+                    best.consider_new(c, d, usable);
+                }
+            }
+        }
+    }
+    inject<FMT>(src, sc, seed_h, (uint32_t)row * (uint32_t)W + (uint32_t)col, n_slots, n_inject, X, Y, s, best);
+    store_list(cout, (long)row * W + col, best.k);
 }
 
 // ---------------------------------------------------------------------------
@@ -2568,12 +2713,14 @@ struct PropArgs {
     float s, sx, sy;
 };
 
-// Measured on kodak768: the tile table pays off only at jump 1, where the
-// neighbour lists are the tile's own lists; from jump 2 on the table-free pass
-// is as fast or faster (random cold-start lists: 90 vs 113 us at jump 2).  On a
-// downscaled map (cell > 1) a 16x16 tile spans c^2 times the pixels, so its
-// lists name more sites than the table holds: there every pass is table-free,
-// on 8x8 tiles when 16x16 ones would leave CUs idle.
+// Per-pixel maps: jump 1 runs the tile table over the tile and its one-pixel
+// ring; larger jumps run the five-region table (k_propagate_wide), which at
+// edit4096 with 8 injected IDs beats fetching every candidate's record (19.4 vs
+// 20.8 ms for the 12-pass refresh; without injection it is slower, 16.1 vs 13.9
+// ms, and a cold start at img2048 takes 3 % longer).  On a downscaled map
+// (cell > 1) a 16x16 tile spans c^2 times the pixels and its lists name more
+// sites than a table holds: every pass is table-free there, on 8x8 tiles when
+// 16x16 ones would leave CUs idle.
 template <int FMT>
 void launch_propagate(const PropArgs &A, hipStream_t hs)
 {
@@ -2585,6 +2732,9 @@ void launch_propagate(const PropArgs &A, hipStream_t hs)
     } else if (A.cell == 1 && A.jump == 1) {
         hipLaunchKernelGGL((k_propagate<1, 256, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci, A.co,
                            A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
+    } else if (A.cell == 1) {
+        hipLaunchKernelGGL((k_propagate_wide<FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci, A.co,
+                           A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, g.tiles_x, g.nb);
     } else {
         hipLaunchKernelGGL((k_propagate_direct<TILE, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci,
                            A.co,
