@@ -850,8 +850,9 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, Screen
     store_list(cout, p, best.k);
 }
 
-// Propagation pass for jumps >= 2 on a per-pixel map, with the tile table sized
-// for five regions.  Every lane holds its own list and its four lists at +-jump
+// Propagation pass for jumps >= 2 on a per-pixel map (the pass of k_propagate:
+// reading note, key design 3; summary, B.3), with the tile table sized for five
+// regions.  Every lane holds its own list and its four lists at +-jump
 // (for jump >= 16 these are four 16x16 blocks beside the tile; below that they
 // overlap it) and their IDs go into a 512-slot LDS table, so a distinct site's
 // scoring record is gathered once per tile instead of once per candidate.  A
