@@ -513,7 +513,7 @@ __device__ __forceinline__ bool screened_out(const Screen &sc, uint32_t id, floa
 // Offers the n_inject injected IDs of map entry `pix` to its list (summary, B.3;
 // the draw is described at sad_topk_propagate), each screened before its record
 // is fetched.  (Loading the screen words of the first eight when the pass starts,
-// to hide their latency, was measured slower: 191 -> 199 us at img2048.)
+// to hide their latency, was measured slower: 191 -> 199 us for a 2048x2048 map.)
 template <int FMT>
 __device__ __forceinline__ void inject(const SiteSrc &src, const Screen &sc, uint32_t seed_h, uint32_t pix,
                                        uint32_t n_slots, int n_inject, float X, float Y, float s, TopK64 &best)
@@ -826,7 +826,7 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, Screen
         // per candidate (the selection needs each score before the next offer,
         // the fetches do not).  Lists of nearby pixels share most of their sites,
         // so held IDs are skipped before the fetch (screening candidates first was
-        // measured slower, 16.9 vs 14.1 ms for the edit4096 refresh without
+        // measured slower, 16.9 vs 14.1 ms for a 12-pass refresh of a 4096x4096 map without
         // injection); an ID a list repeats is caught by consider().
         float4 g0[K], g1[K];
         uint32_t need = 0u;
@@ -850,7 +850,7 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, Screen
     store_list(cout, p, best.k);
 }
 
-// Propagation pass for jumps >= 2 on a per-pixel map (the pass of k_propagate:
+// Propagation pass for jumps >= 5 on a per-pixel map (the pass of k_propagate:
 // reading note, key design 3; summary, B.3), with the tile table sized for five
 // regions.  Every lane holds its own list and its four lists at +-jump
 // (for jump >= 16 these are four 16x16 blocks beside the tile; below that they
@@ -2714,11 +2714,14 @@ struct PropArgs {
     float s, sx, sy;
 };
 
-// Per-pixel maps: jump 1 runs the tile table over the tile and its one-pixel
-// ring; larger jumps run the five-region table (k_propagate_wide), which at
-// edit4096 with 8 injected IDs beats fetching every candidate's record (19.4 vs
+// Per-pixel maps: jumps up to 4 run the tile table over the tile and its ring
+// of jump-wide strips, whose per-pixel bitmap skips the entries the pixel has
+// scored already (at 4096x4096, 1M sites, after an edit: jump 2 0.94 vs 1.34 ms
+// in the five-region table, jump 4 1.12 vs 1.35 ms; at jump 8, 1.69 vs 1.49, it
+// loses).  Larger jumps run the five-region table (k_propagate_wide), which at
+// that size with 8 injected IDs beats fetching every candidate's record (19.4 vs
 // 20.8 ms for the 12-pass refresh; without injection it is slower, 16.1 vs 13.9
-// ms, and a cold start at img2048 takes 3 % longer).  On a downscaled map
+// ms, and a cold start at 2048x2048 takes 3 % longer).  On a downscaled map
 // (cell > 1) a 16x16 tile spans c^2 times the pixels and its lists name more
 // sites than a table holds: every pass is table-free there, on 8x8 tiles when
 // 16x16 ones would leave CUs idle.
@@ -2732,6 +2735,12 @@ void launch_propagate(const PropArgs &A, hipStream_t hs)
                            A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g8.tiles_x, g8.nb);
     } else if (A.cell == 1 && A.jump == 1) {
         hipLaunchKernelGGL((k_propagate<1, 256, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci, A.co,
+                           A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
+    } else if (A.cell == 1 && A.jump == 2) {
+        hipLaunchKernelGGL((k_propagate<2, 256, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci, A.co,
+                           A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
+    } else if (A.cell == 1 && A.jump <= 4) {
+        hipLaunchKernelGGL((k_propagate<4, 256, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci, A.co,
                            A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
     } else if (A.cell == 1) {
         hipLaunchKernelGGL((k_propagate_wide<FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci, A.co,

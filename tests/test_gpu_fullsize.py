@@ -1,6 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark uses (tile-table propagate at jump 1, table-free propagate at larger
-jumps, the fused forward+backward launch, Adam refreshing the site records).
+benchmark uses (the tile-table propagation at jumps up to 8, the five-region
+table beyond, the fused forward+backward launch, Adam refreshing the site
+records).
 
 The oracle checks full images where it finishes in seconds and sampled pixels
 otherwise (its per-pixel functions evaluate any subset of pixels exactly).
@@ -38,7 +39,7 @@ def _sample(W, H, seed=3, k=SAMPLE):
 
 
 @pytest.mark.parametrize("name", ["kodak768", "img2048", "div2k2040", "edit4096"])
-@pytest.mark.parametrize("jump", [1, 64])
+@pytest.mark.parametrize("jump", [1, 4, 64])
 def test_propagate_full_size_sampled(orc, name, jump):
     wl, S, cin = _setup(name)
     W, H, n = wl.W, wl.H, wl.n_sites

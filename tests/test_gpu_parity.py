@@ -38,7 +38,7 @@ def _gpu_propagate(S, n, cin, W, H, jump, pidx, seed, m):
 
 
 @pytest.mark.parametrize("W,H,n", SHAPES)
-@pytest.mark.parametrize("jump,m", [(1, 4), (3, 0), (16, 8), (1000, 16)])
+@pytest.mark.parametrize("jump,m", [(1, 4), (2, 8), (3, 0), (7, 4), (16, 8), (1000, 16)])
 def test_propagate_matches_oracle(orc, W, H, n, jump, m):
     print(f"propagate W={W} H={H} n={n} jump={jump} m={m}", flush=True)
     S, cin = _case(W, H, n)
@@ -68,20 +68,20 @@ def test_propagate_edge_inputs(orc):
     assert np.array_equal(_gpu_propagate(S, n, cin, W, H, 2, 3, 5, 6), _gpu_propagate(S, n, cin, W, H, 2, 3 + 65536, 5, 6))
 
 
-@pytest.mark.parametrize("seed", [21, 22])
-def test_propagate_table_overflow_at_jump_1(orc, seed):
-    """Lists of uniformly random sites at jump 1: every tile names far more sites
-    than its 256-slot table holds, so own and neighbour entries take the spill
-    path (their IDs read again from the input map); sentinels and duplicates
-    mixed in."""
+@pytest.mark.parametrize("seed,jump", [(21, 1), (22, 1), (23, 2), (24, 3), (25, 4), (26, 5), (27, 8)])
+def test_propagate_table_overflow(orc, seed, jump):
+    """Lists of uniformly random sites at the jumps whose pass keeps a 256-slot
+    tile table: every tile names far more sites than the table holds, so own,
+    neighbour and strip entries take the spill path (their IDs read again from
+    the input map); sentinels and duplicates mixed in."""
     W, H, n = 67, 45, 20000
-    print(f"propagate overflow jump=1 seed={seed}", flush=True)
+    print(f"propagate overflow jump={jump} seed={seed}", flush=True)
     S = synth.random_sites(n, W, H, seed)
     cin = synth.random_map(W, H, n, seed=seed + 1, p_invalid=0.1, p_dup=0.1)
-    got = _gpu_propagate(S, n, cin, W, H, 1, 31, 77, 4)
-    ref = orc.propagate(S, n, cin, W, H, 1, 31, 77, 4)
+    got = _gpu_propagate(S, n, cin, W, H, jump, 31, 77, 4)
+    ref = orc.propagate(S, n, cin, W, H, jump, 31, 77, 4)
     pix = np.arange(W * H)
-    u, cnt = orc.union_pixels(S, n, cin, W, H, 1, 31, 77, 4, pix)
+    u, cnt = orc.union_pixels(S, n, cin, W, H, jump, 31, 77, 4, pix)
     assert compare_lists(orc, S, n, W, H, pix, got, ref, u, cnt) <= 2
 
 
