@@ -617,6 +617,12 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
     const int kk = min(jump, TILE);
     const int strip_len = TILE * KK;
     const int nlists = BLOCK + 4 * strip_len;
+    // Region list r is loaded with its two 16-byte halves swapped when r is odd
+    // (the quarter-list loads of the jump-1 strips excepted), so that
+    // neighbouring lanes insert different list places in one CAS instruction:
+    // CAS lanes that name one LDS address serialise.  Refs follow the loaded
+    // order; only a spill's re-read from global memory undoes the swap.
+    auto list_swap = [&](int r) { return (KK == 1 && r >= BLOCK) ? 0 : (r & 1); };
 
     for (int sl = tid; sl < TB; sl += BLOCK)
         L.t.key[sl] = NONE;
@@ -633,8 +639,8 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
         uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
         if (col < W && row < H) {
             const long p = (long)row * W + col;
-            a = cin[2 * p];
-            b = cin[2 * p + 1];
+            a = cin[2 * p + list_swap(tid)];
+            b = cin[2 * p + 1 - list_swap(tid)];
         }
         const int sr = BLOCK + (tid >> 2), qq = tid & 3;
         int pc, pr, across;
@@ -657,8 +663,8 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
             uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
             if (across < kk && pc >= 0 && pc < W && pr >= 0 && pr < H) {
                 const long p = (long)pr * W + pc;
-                a = cin[2 * p];
-                b = cin[2 * p + 1];
+                a = cin[2 * p + list_swap(r)];
+                b = cin[2 * p + 1 - list_swap(r)];
             }
             const uint32_t ids[K] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
             uint32_t refs[K];
@@ -699,9 +705,10 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
         return (atomicOr(&L.seen[sl >> 5][tid], bit) & bit) == 0u;
     };
 
-    // entry e of the list of pixel (pc, pr), read again from global memory (spills)
-    auto list_id = [&](int pc, int pr, int e) {
-        return reinterpret_cast<const uint32_t *>(cin)[(size_t)K * ((size_t)pr * W + pc) + e];
+    // the ID behind place e of region list r's refs, the list of pixel (pc, pr),
+    // read again from global memory (spills)
+    auto list_id = [&](int r, int pc, int pr, int e) {
+        return reinterpret_cast<const uint32_t *>(cin)[(size_t)K * ((size_t)pr * W + pc) + (e ^ 4 * list_swap(r))];
     };
     TopK64 best;
     // own list: score its (deduplicated) table entries and sort them with a network
@@ -727,7 +734,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         if (orefs[k] == REF16_SPILL) {
-            const uint32_t c = list_id(col, row, k);
+            const uint32_t c = list_id(tid, col, row, k);
             bool usable;
             const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
             best.consider(c, d, usable);
@@ -777,7 +784,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
             best.consider_new(id, d, usable);
         } else {
             // a spilled entry: its ID from the neighbour's list in global memory
-            const uint32_t c = list_id(li == 0 ? col - jump : li == 1 ? col + jump : col,
+            const uint32_t c = list_id(r, li == 0 ? col - jump : li == 1 ? col + jump : col,
                                        li == 2 ? row - jump : li == 3 ? row + jump : row, e);
             if (!screened_out(sc, c, X, Y, best.k[K - 1])) {
                 const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
@@ -888,8 +895,15 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc
         L.t.key[sl] = NONE;
     if (tid == 0)
         L.n_own = 0u;
-    // the five lists: own, left, right, top, bottom (NONE outside the image)
+    // The five lists: own, then left, right, top and bottom (NONE outside the
+    // image).  Neighbouring pixels hold the same sites at the same list places,
+    // and CAS instructions whose lanes name one LDS address serialise (about two
+    // cycles per lane on gfx950, against ~15 cycles for a wave on spread
+    // addresses), so odd lanes take the two 16-byte halves of each list in the
+    // other order: the lanes of one CAS then name one address less often.
+    // Scoring and selection do not depend on the order.
     uint32_t ids[5][K];
+    const int h = tid & 1;
 #pragma unroll
     for (int li = 0; li < 5; ++li) {
         const int c = li == 1 ? col - jump : li == 2 ? col + jump : col;
@@ -897,8 +911,8 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc
         uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
         if (inside && c >= 0 && c < W && r >= 0 && r < H) {
             const long q = (long)r * W + c;
-            a = cin[2 * q];
-            b = cin[2 * q + 1];
+            a = cin[2 * q + h];
+            b = cin[2 * q + 1 - h];
         }
         ids[li][0] = a.x; ids[li][1] = a.y; ids[li][2] = a.z; ids[li][3] = a.w;
         ids[li][4] = b.x; ids[li][5] = b.y; ids[li][6] = b.z; ids[li][7] = b.w;
