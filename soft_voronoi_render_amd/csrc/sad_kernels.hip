@@ -299,6 +299,36 @@ __device__ __forceinline__ uint32_t xorshift32(uint32_t x)
 }
 
 // ---------------------------------------------------------------------------
+// Lane moves without the LDS: a DPP move of x (CTRL: the DPP control word; ROWS:
+// the rows written, others keep 0), and an inclusive prefix sum over a wave.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes (lanes whose DPP source lies outside
+// the row add 0): within each 16-lane row by row_shr 1, 2, 4, 8, then the last
+// lane of row 0 and of row 2 into rows 1 and 3 (row_bcast:15), then lane 31 into
+// rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
+{
+    x += dpp_u<0x111, 0xF>(x);
+    x += dpp_u<0x112, 0xF>(x);
+    x += dpp_u<0x114, 0xF>(x);
+    x += dpp_u<0x118, 0xF>(x);
+    x += dpp_u<0x142, 0xA>(x);
+    x += dpp_u<0x143, 0xC>(x);
+    return x;
+}
+
+// ---------------------------------------------------------------------------
 // Inserts one list's IDs into an LDS hash table of TB slots keyed by site ID
 // (multiplicative hash, CAS insert -- summary, B.4; double hashing with an odd
 // step, <= HASH_PROBES probes: at the ~30 % load of a converged map's tile no ID
@@ -315,8 +345,8 @@ template <int TB, int N, bool COUNT = false>
 __device__ __forceinline__ void table_insert_ids(uint32_t *key, const uint32_t (&ids)[N], uint32_t n_slots,
                                                  uint32_t (&refs)[N], uint32_t *n_new = nullptr)
 {
-    constexpr int SHIFT = TB == 256 ? 24 : 23;
-    static_assert(TB == 256 || TB == 512, "table size");
+    constexpr int SHIFT = TB == 256 ? 24 : TB == 512 ? 23 : 21;
+    static_assert(TB == 256 || TB == 512 || TB == 2048, "table size");
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         const uint32_t c = ids[k];
@@ -861,38 +891,57 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, Screen
 // reading note, key design 3; summary, B.3), with the tile table sized for five
 // regions.  Every lane holds its own list and its four lists at +-jump
 // (for jump >= 16 these are four 16x16 blocks beside the tile; below that they
-// overlap it) and their IDs go into a 512-slot LDS table, so a distinct site's
-// scoring record is gathered once per tile instead of once per candidate.  A
-// tile whose own lists already name more than WIDE_OWN_MAX sites (random lists
-// early in a cold start) would only overflow the table: it scores its neighbour
-// candidates from their records, as the table-free pass does, and so do IDs a
-// full table cannot hold.
+// overlap it) and their IDs go into an LDS hash table, so a distinct site's
+// scoring record is gathered once per tile instead of once per candidate.  The
+// hash has KT key slots for at most WTB = 512 records.  At jumps >= 16 (KT =
+// WKT_SPARSE = 2048) the five regions name ~230 sites, and a wave repeats a CAS
+// probe until its slowest lane has a slot, so a sparse table saves probes (by a
+// simulation of converged lists, 1.7 CAS instructions per wave and list place
+// at 2048 slots against 3.0 at 512); after the inserts a prefix scan gives each
+// occupied key slot a record index, and keys, indices and the compact ID list
+// share their LDS with the records, which are written once they are dead.  At
+// smaller jumps the regions overlap and name fewer sites: KT = WTB, the records
+// sit at their key slots (no scan).  A tile whose own lists already name more
+// than WIDE_OWN_MAX sites (random lists early in a cold start) would only
+// overflow the table: it scores its neighbour candidates from their records, as
+// the table-free pass does, and so do IDs beyond the table or the records.
+constexpr int WKT_SPARSE = 2048;
 constexpr int WTB = 512;
 constexpr int WIDE_OWN_MAX = 96;
+constexpr uint16_t WIDX_NONE = 0xFFFF;
 
+template <int KT>
 struct WideShared {
     union {
-        uint32_t key[WTB];
-        float4 rec0[WTB];  // scoring record, bytes 0..15
-    } t;
-    float4 rec1[WTB];      // bytes 16..31; the slot's ID in the last word
-    uint32_t n_own;        // distinct IDs of the tile's own lists
+        struct {
+            uint32_t key[KT];     // hash keys (site IDs)
+            uint16_t idx[KT];     // record index of an occupied key slot (WIDX_NONE: beyond WTB)
+            uint32_t recid[WTB];  // site ID of each record
+        } h;
+        struct {
+            float4 rec0[WTB];     // scoring record, bytes 0..15
+            float4 rec1[WTB];     // bytes 16..31; the site's ID in the last word
+        } r;
+    } u;
+    uint32_t wtot[BLOCK / 64];    // occupied key slots per wave's share (the scan)
+    uint32_t n_own;               // distinct IDs of the tile's own lists
 };
 
-template <int FMT>
+template <int FMT, int KT>
 __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc, uint32_t n_slots,
                                                           const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
                                                           int W, int H, int jump, uint32_t seed_h, int n_inject,
                                                           float s, int tiles_x, int nb)
 {
-    __shared__ WideShared L;
+    static_assert(KT == WTB || KT == WKT_SPARSE, "key table");
+    __shared__ WideShared<KT> L;
     const int tid = threadIdx.x;
     const int t = xcd_band(blockIdx.x, nb);
     const int col = (t % tiles_x) * TILE + (tid & (TILE - 1));
     const int row = (t / tiles_x) * TILE + tid / TILE;
     const bool inside = col < W && row < H;
-    for (int sl = tid; sl < WTB; sl += BLOCK)
-        L.t.key[sl] = NONE;
+    for (int sl = tid; sl < KT; sl += BLOCK)
+        L.u.h.key[sl] = NONE;
     if (tid == 0)
         L.n_own = 0u;
     // The five lists: own, then left, right, top and bottom (NONE outside the
@@ -919,13 +968,13 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc
     }
     __syncthreads();
     uint32_t refs[5][K];
-    table_insert_ids<WTB, K, true>(L.t.key, ids[0], n_slots, refs[0], &L.n_own);
+    table_insert_ids<KT, K, true>(L.u.h.key, ids[0], n_slots, refs[0], &L.n_own);
     __syncthreads();
     const bool coherent = L.n_own <= (uint32_t)WIDE_OWN_MAX;
     if (coherent) {
 #pragma unroll
         for (int li = 1; li < 5; ++li)
-            table_insert_ids<WTB, K>(L.t.key, ids[li], n_slots, refs[li]);
+            table_insert_ids<KT, K>(L.u.h.key, ids[li], n_slots, refs[li]);
     } else {
 #pragma unroll
         for (int li = 1; li < 5; ++li)
@@ -934,13 +983,13 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc
                 refs[li][k] = ids[li][k] < n_slots ? (REF_SPILL | ids[li][k]) : REF_NONE;
     }
     __syncthreads();
-    // one scoring record per occupied slot, two slots per lane
-    {
+    if constexpr (KT == WTB) {
+        // one scoring record per occupied slot, at its slot, two slots per lane
         uint32_t c[WTB / BLOCK];
         float4 g0[WTB / BLOCK], g1[WTB / BLOCK];
 #pragma unroll
         for (int j = 0; j < WTB / BLOCK; ++j) {
-            c[j] = L.t.key[tid + j * BLOCK];
+            c[j] = L.u.h.key[tid + j * BLOCK];
             g0[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             g1[j] = g0[j];
             if (c[j] != NONE)
@@ -951,8 +1000,75 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc
 #pragma unroll
         for (int j = 0; j < WTB / BLOCK; ++j) {
             if (c[j] != NONE) {
-                L.t.rec0[tid + j * BLOCK] = g0[j];
-                L.rec1[tid + j * BLOCK] = g1[j];
+                L.u.r.rec0[tid + j * BLOCK] = g0[j];
+                L.u.r.rec1[tid + j * BLOCK] = g1[j];
+            }
+        }
+    } else {
+        // record indices: thread t takes key slots 8t .. 8t + 7; the occupied ones are
+        // numbered in slot order by a wave scan and the waves' totals
+        constexpr int KPT = KT / BLOCK;
+        uint32_t occ = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            occ |= (L.u.h.key[KPT * tid + j] != NONE ? 1u : 0u) << j;
+        const uint32_t cnt = __builtin_popcount(occ);
+        const uint32_t incl = wave_incl_scan(cnt);
+        if ((tid & 63) == 63)
+            L.wtot[tid >> 6] = incl;
+        __syncthreads();
+        uint32_t base = incl - cnt, n_rec = 0;
+#pragma unroll
+        for (int w = 0; w < BLOCK / 64; ++w) {
+            base += w < (tid >> 6) ? L.wtot[w] : 0u;
+            n_rec += L.wtot[w];
+        }
+        n_rec = min(n_rec, (uint32_t)WTB);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if ((occ >> j) & 1u) {
+                const uint32_t sl = KPT * tid + j;
+                L.u.h.idx[sl] = base < (uint32_t)WTB ? (uint16_t)base : WIDX_NONE;
+                if (base < (uint32_t)WTB)
+                    L.u.h.recid[base] = L.u.h.key[sl];
+                ++base;
+            }
+        }
+        __syncthreads();
+        // refs become record indices (IDs without one: spills), and one scoring
+        // record per site is gathered, two per lane; the records are written over the
+        // keys after the barrier
+        {
+#pragma unroll
+            for (int li = 0; li < 5; ++li) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const uint32_t ref = refs[li][k];
+                    if (ref < (uint32_t)KT) {
+                        const uint32_t r = L.u.h.idx[ref];
+                        refs[li][k] = r != WIDX_NONE ? r : (REF_SPILL | L.u.h.key[ref]);
+                    }
+                }
+            }
+            uint32_t c[WTB / BLOCK];
+            float4 g0[WTB / BLOCK], g1[WTB / BLOCK];
+#pragma unroll
+            for (int j = 0; j < WTB / BLOCK; ++j) {
+                const uint32_t r = tid + j * BLOCK;
+                c[j] = r < n_rec ? L.u.h.recid[r] : NONE;
+                g0[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                g1[j] = g0[j];
+                if (c[j] != NONE)
+                    load_sel<FMT>(src, c[j], g0[j], g1[j]);
+                g1[j].w = __uint_as_float(c[j]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < WTB / BLOCK; ++j) {
+                if (c[j] != NONE) {
+                    L.u.r.rec0[tid + j * BLOCK] = g0[j];
+                    L.u.r.rec1[tid + j * BLOCK] = g1[j];
+                }
             }
         }
     }
@@ -974,7 +1090,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc
                 dup |= refs[0][j] == ref;
             v[k] = ~0ull;
             if (ref < (uint32_t)WTB && !dup) {
-                const float4 g0 = L.t.rec0[ref], g1 = L.rec1[ref];
+                const float4 g0 = L.u.r.rec0[ref], g1 = L.u.r.rec1[ref];
                 const float d = geom_score(g0, g1, X, Y, s);
                 if (!(g0.x < 0.0f) && finitef(d))
                     v[k] = rank_key(d, __float_as_uint(g1.w));
@@ -991,7 +1107,7 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc
             const uint32_t ref = refs[li][k];
             if (ref < (uint32_t)WTB) {
                 if (li > 0) {
-                    const float4 g0 = L.t.rec0[ref], g1 = L.rec1[ref];
+                    const float4 g0 = L.u.r.rec0[ref], g1 = L.u.r.rec1[ref];
                     best.consider(__float_as_uint(g1.w), geom_score(g0, g1, X, Y, s), !(g0.x < 0.0f));
                 }
             } else if (ref != REF_NONE) {
@@ -1718,33 +1834,6 @@ __device__ __forceinline__ PairSums pair_sums(float x, int half)
 // then across the half row (row_half_mirror: lane i of the 8 reads lane 7 - i,
 // which lies in the other quad).  Three DPP moves, no LDS; the same additions in
 // the same order as exchanging with lanes i^1, i^2, i^4.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t x)
-{
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
-}
-
-// Inclusive prefix sum over the 64 lanes (lanes whose DPP source lies outside
-// the row add 0): within each 16-lane row by row_shr 1, 2, 4, 8, then the last
-// lane of row 0 and of row 2 into rows 1 and 3 (row_bcast:15), then lane 31 into
-// rows 2 and 3 (row_bcast:31).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
-{
-    x += dpp_u<0x111, 0xF>(x);
-    x += dpp_u<0x112, 0xF>(x);
-    x += dpp_u<0x114, 0xF>(x);
-    x += dpp_u<0x118, 0xF>(x);
-    x += dpp_u<0x142, 0xA>(x);
-    x += dpp_u<0x143, 0xC>(x);
-    return x;
-}
-
 __device__ __forceinline__ float group8_sum(float x)
 {
     x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
@@ -2732,10 +2821,10 @@ struct PropArgs {
 // of jump-wide strips, whose per-pixel bitmap skips the entries the pixel has
 // scored already (at 4096x4096, 1M sites, after an edit: jump 2 0.94 vs 1.34 ms
 // in the five-region table, jump 4 1.12 vs 1.35 ms; at jump 8, 1.69 vs 1.49, it
-// loses).  Larger jumps run the five-region table (k_propagate_wide), which at
-// that size with 8 injected IDs beats fetching every candidate's record (19.4 vs
-// 20.8 ms for the 12-pass refresh; without injection it is slower, 16.1 vs 13.9
-// ms, and a cold start at 2048x2048 takes 3 % longer).  On a downscaled map
+// loses).  Larger jumps run the five-region table (k_propagate_wide; a sparse
+// 2048-key hash from jump 16 on), which at that size with 8 injected IDs beats
+// fetching every candidate's record (17.4 vs 20.8 ms for the 12-pass refresh;
+// without injection 14.0 vs 13.9 ms).  On a downscaled map
 // (cell > 1) a 16x16 tile spans c^2 times the pixels and its lists name more
 // sites than a table holds: every pass is table-free there, on 8x8 tiles when
 // 16x16 ones would leave CUs idle.
@@ -2757,8 +2846,12 @@ void launch_propagate(const PropArgs &A, hipStream_t hs)
         hipLaunchKernelGGL((k_propagate<4, 256, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci, A.co,
                            A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, A.sx, A.sy, g.tiles_x, g.nb);
     } else if (A.cell == 1) {
-        hipLaunchKernelGGL((k_propagate_wide<FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci, A.co,
-                           A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, g.tiles_x, g.nb);
+        if (A.jump >= 16)
+            hipLaunchKernelGGL((k_propagate_wide<FMT, WKT_SPARSE>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n,
+                               A.ci, A.co, A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, g.tiles_x, g.nb);
+        else
+            hipLaunchKernelGGL((k_propagate_wide<FMT, WTB>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci,
+                               A.co, A.Wm, A.Hm, A.jump, A.seed_h, A.n_inject, A.s, g.tiles_x, g.nb);
     } else {
         hipLaunchKernelGGL((k_propagate_direct<TILE, FMT>), dim3(g.nb), dim3(BLOCK), 0, hs, A.src, A.sc, A.n, A.ci,
                            A.co,
