@@ -85,6 +85,33 @@ def test_propagate_table_overflow(orc, seed, jump):
     assert compare_lists(orc, S, n, W, H, pix, got, ref, u, cnt) <= 2
 
 
+@pytest.mark.parametrize("jump", [5, 8, 16, 32, 48])
+def test_propagate_five_region_table_overflow(orc, jump):
+    """Tiles alternate between lists drawn from a pool of 40 sites (coherent own
+    lists: the five-region table is used) and uniformly random lists. At these
+    jumps a pool tile's neighbour regions are random tiles naming thousands of
+    sites, so the key table runs out of probes (IDs read again as spills) and,
+    with the sparse hash, more keys are occupied than there are records (the
+    IDs beyond the last record also become spills)."""
+    W, H, n = 96, 96, 20000
+    print(f"propagate five-region overflow jump={jump}", flush=True)
+    S = synth.random_sites(n, W, H, 41)
+    cin = synth.random_map(W, H, n, seed=42, p_invalid=0.05, p_dup=0.05)
+    rng = np.random.default_rng(43)
+    for ty in range(H // 16):
+        for tx in range(W // 16):
+            if (tx + ty) % 2 == 0:
+                pool = rng.choice(n, 40, replace=False)
+                for y in range(16 * ty, 16 * ty + 16):
+                    for x in range(16 * tx, 16 * tx + 16):
+                        cin[y, x] = rng.choice(pool, 8, replace=False)
+    got = _gpu_propagate(S, n, cin, W, H, jump, 17, 77, 4)
+    ref = orc.propagate(S, n, cin, W, H, jump, 17, 77, 4)
+    pix = np.arange(W * H)
+    u, cnt = orc.union_pixels(S, n, cin, W, H, jump, 17, 77, 4, pix)
+    assert compare_lists(orc, S, n, W, H, pix, got, ref, u, cnt) <= 2
+
+
 def test_propagate_schedule_from_empty_matches_oracle_each_pass(orc):
     """The warm-up schedule from an all-sentinel map: every pass compared with the
     oracle on the oracle's previous output (shared input), then recall."""
