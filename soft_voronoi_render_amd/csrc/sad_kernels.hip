@@ -927,62 +927,16 @@ struct WideShared {
     uint32_t n_own;               // distinct IDs of the tile's own lists
 };
 
-template <int FMT, int KT>
-__global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc, uint32_t n_slots,
-                                                          const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
-                                                          int W, int H, int jump, uint32_t seed_h, int n_inject,
-                                                          float s, int tiles_x, int nb)
+// The records of a five-region (or 3x3) table once its inserts are done and a
+// barrier has passed.  KT == WTB: one scoring record per occupied key slot, at
+// its slot.  KT > WTB: a prefix scan numbers the occupied key slots, refs become
+// record indices (IDs beyond the last record become spills, their ID read from
+// the key), and one record per site is gathered.  Records are written over the
+// keys after a barrier; ends with a barrier.  All threads of the block call it.
+template <int FMT, int KT, int NL, int NE>
+__device__ __forceinline__ void table_records(WideShared<KT> &L, const SiteSrc &src, uint32_t (&refs)[NL][NE])
 {
-    static_assert(KT == WTB || KT == WKT_SPARSE, "key table");
-    __shared__ WideShared<KT> L;
     const int tid = threadIdx.x;
-    const int t = xcd_band(blockIdx.x, nb);
-    const int col = (t % tiles_x) * TILE + (tid & (TILE - 1));
-    const int row = (t / tiles_x) * TILE + tid / TILE;
-    const bool inside = col < W && row < H;
-    for (int sl = tid; sl < KT; sl += BLOCK)
-        L.u.h.key[sl] = NONE;
-    if (tid == 0)
-        L.n_own = 0u;
-    // The five lists: own, then left, right, top and bottom (NONE outside the
-    // image).  Neighbouring pixels hold the same sites at the same list places,
-    // and CAS instructions whose lanes name one LDS address serialise (about two
-    // cycles per lane on gfx950, against ~15 cycles for a wave on spread
-    // addresses), so odd lanes take the two 16-byte halves of each list in the
-    // other order: the lanes of one CAS then name one address less often.
-    // Scoring and selection do not depend on the order.
-    uint32_t ids[5][K];
-    const int h = tid & 1;
-#pragma unroll
-    for (int li = 0; li < 5; ++li) {
-        const int c = li == 1 ? col - jump : li == 2 ? col + jump : col;
-        const int r = li == 3 ? row - jump : li == 4 ? row + jump : row;
-        uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
-        if (inside && c >= 0 && c < W && r >= 0 && r < H) {
-            const long q = (long)r * W + c;
-            a = cin[2 * q + h];
-            b = cin[2 * q + 1 - h];
-        }
-        ids[li][0] = a.x; ids[li][1] = a.y; ids[li][2] = a.z; ids[li][3] = a.w;
-        ids[li][4] = b.x; ids[li][5] = b.y; ids[li][6] = b.z; ids[li][7] = b.w;
-    }
-    __syncthreads();
-    uint32_t refs[5][K];
-    table_insert_ids<KT, K, true>(L.u.h.key, ids[0], n_slots, refs[0], &L.n_own);
-    __syncthreads();
-    const bool coherent = L.n_own <= (uint32_t)WIDE_OWN_MAX;
-    if (coherent) {
-#pragma unroll
-        for (int li = 1; li < 5; ++li)
-            table_insert_ids<KT, K>(L.u.h.key, ids[li], n_slots, refs[li]);
-    } else {
-#pragma unroll
-        for (int li = 1; li < 5; ++li)
-#pragma unroll
-            for (int k = 0; k < K; ++k)
-                refs[li][k] = ids[li][k] < n_slots ? (REF_SPILL | ids[li][k]) : REF_NONE;
-    }
-    __syncthreads();
     if constexpr (KT == WTB) {
         // one scoring record per occupied slot, at its slot, two slots per lane
         uint32_t c[WTB / BLOCK];
@@ -1040,9 +994,9 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc
         // keys after the barrier
         {
 #pragma unroll
-            for (int li = 0; li < 5; ++li) {
+            for (int li = 0; li < NL; ++li) {
 #pragma unroll
-                for (int k = 0; k < K; ++k) {
+                for (int k = 0; k < NE; ++k) {
                     const uint32_t ref = refs[li][k];
                     if (ref < (uint32_t)KT) {
                         const uint32_t r = L.u.h.idx[ref];
@@ -1073,6 +1027,65 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc
         }
     }
     __syncthreads();
+}
+
+template <int FMT, int KT>
+__global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc, uint32_t n_slots,
+                                                          const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
+                                                          int W, int H, int jump, uint32_t seed_h, int n_inject,
+                                                          float s, int tiles_x, int nb)
+{
+    static_assert(KT == WTB || KT == WKT_SPARSE, "key table");
+    __shared__ WideShared<KT> L;
+    const int tid = threadIdx.x;
+    const int t = xcd_band(blockIdx.x, nb);
+    const int col = (t % tiles_x) * TILE + (tid & (TILE - 1));
+    const int row = (t / tiles_x) * TILE + tid / TILE;
+    const bool inside = col < W && row < H;
+    for (int sl = tid; sl < KT; sl += BLOCK)
+        L.u.h.key[sl] = NONE;
+    if (tid == 0)
+        L.n_own = 0u;
+    // The five lists: own, then left, right, top and bottom (NONE outside the
+    // image).  Neighbouring pixels hold the same sites at the same list places,
+    // and CAS instructions whose lanes name one LDS address serialise (about two
+    // cycles per lane on gfx950, against ~15 cycles for a wave on spread
+    // addresses), so odd lanes take the two 16-byte halves of each list in the
+    // other order: the lanes of one CAS then name one address less often.
+    // Scoring and selection do not depend on the order.
+    uint32_t ids[5][K];
+    const int h = tid & 1;
+#pragma unroll
+    for (int li = 0; li < 5; ++li) {
+        const int c = li == 1 ? col - jump : li == 2 ? col + jump : col;
+        const int r = li == 3 ? row - jump : li == 4 ? row + jump : row;
+        uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
+        if (inside && c >= 0 && c < W && r >= 0 && r < H) {
+            const long q = (long)r * W + c;
+            a = cin[2 * q + h];
+            b = cin[2 * q + 1 - h];
+        }
+        ids[li][0] = a.x; ids[li][1] = a.y; ids[li][2] = a.z; ids[li][3] = a.w;
+        ids[li][4] = b.x; ids[li][5] = b.y; ids[li][6] = b.z; ids[li][7] = b.w;
+    }
+    __syncthreads();
+    uint32_t refs[5][K];
+    table_insert_ids<KT, K, true>(L.u.h.key, ids[0], n_slots, refs[0], &L.n_own);
+    __syncthreads();
+    const bool coherent = L.n_own <= (uint32_t)WIDE_OWN_MAX;
+    if (coherent) {
+#pragma unroll
+        for (int li = 1; li < 5; ++li)
+            table_insert_ids<KT, K>(L.u.h.key, ids[li], n_slots, refs[li]);
+    } else {
+#pragma unroll
+        for (int li = 1; li < 5; ++li)
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                refs[li][k] = ids[li][k] < n_slots ? (REF_SPILL | ids[li][k]) : REF_NONE;
+    }
+    __syncthreads();
+    table_records<FMT, KT>(L, src, refs);
     if (!inside)
         return;
     const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
@@ -1212,9 +1225,12 @@ __global__ __launch_bounds__(256) void k_jfa_seed_finish(uint4 *__restrict__ can
 
 // One flood pass with step `step`: the union of the first four entries of the 3x3
 // lists at offsets {-step, 0, step}^2 inside the image; the four best by (d, ID)
-// go to entries 0..3, the sentinel to 4..7.  Each list is read by at most one
-// pixel of a tile at steps >= 16, so candidates are scored straight from their
-// records, as in the table-free propagation.
+// go to entries 0..3, the sentinel to 4..7.  Table-free: candidates are scored
+// straight from their records (an ID already held is skipped first).  Screening
+// candidates against the fourth place, the entry's own list first, was measured
+// slower: at steps 16-256 the fourth place is still far, few candidates are
+// dropped and every one costs a screen-word gather on top of its record
+// (4096x4096 after an edit: 3.8-5.0 vs 2.9-3.9 ms per pass).
 template <int FMT>
 __global__ __launch_bounds__(BLOCK) void k_jfa_pass(SiteSrc src, uint32_t n_slots,
                                                     const uint4 *__restrict__ cin, uint4 *__restrict__ cout, int W,
@@ -1239,11 +1255,72 @@ __global__ __launch_bounds__(BLOCK) void k_jfa_pass(SiteSrc src, uint32_t n_slot
         const uint32_t ids[JFA_KEEP] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int k = 0; k < JFA_KEEP; ++k) {
-            // an ID already held is skipped before its record is fetched
             if (ids[k] < n_slots && !best.holds(ids[k])) {
                 bool usable;
                 const float d = geom_score_id<FMT>(src, ids[k], X, Y, s, usable);
                 best.consider_new(ids[k], d, usable);
+            }
+        }
+    }
+    const long p = (long)row * W + col;
+    cout[2 * p] = make_uint4((uint32_t)best.k[0], (uint32_t)best.k[1], (uint32_t)best.k[2], (uint32_t)best.k[3]);
+    cout[2 * p + 1] = make_uint4(NONE, NONE, NONE, NONE);
+}
+
+// The same flood pass on a per-pixel map through a tile table: at small steps the
+// nine lists of neighbouring pixels name mostly the same sites, so their IDs go into the
+// sparse hash of the five-region table (2048 key slots, 512 records) and each
+// distinct site's scoring record is gathered once per tile; candidates are
+// scored from the LDS records, IDs beyond the table from their global records.
+// The candidates and the selection are those of k_jfa_pass.
+template <int FMT>
+__global__ __launch_bounds__(BLOCK) void k_jfa_pass_table(SiteSrc src, uint32_t n_slots,
+                                                          const uint4 *__restrict__ cin, uint4 *__restrict__ cout,
+                                                          int W, int H, int step, float s, int tiles_x, int nb)
+{
+    __shared__ WideShared<WKT_SPARSE> L;
+    const int tid = threadIdx.x;
+    const int t = xcd_band(blockIdx.x, nb);
+    const int col = (t % tiles_x) * TILE + (tid & (TILE - 1));
+    const int row = (t / tiles_x) * TILE + tid / TILE;
+    const bool inside = col < W && row < H;
+    for (int sl = tid; sl < WKT_SPARSE; sl += BLOCK)
+        L.u.h.key[sl] = NONE;
+    __syncthreads();
+    uint32_t refs[9][JFA_KEEP];
+#pragma unroll
+    for (int li = 0; li < 9; ++li) {
+        const int c = col + (li % 3 - 1) * step, r = row + (li / 3 - 1) * step;
+        uint4 a = make_uint4(NONE, NONE, NONE, NONE);
+        if (inside && c >= 0 && c < W && r >= 0 && r < H)
+            a = cin[2 * ((long)r * W + c)];
+        const uint32_t ids[JFA_KEEP] = {a.x, a.y, a.z, a.w};
+        table_insert_ids<WKT_SPARSE, JFA_KEEP>(L.u.h.key, ids, n_slots, refs[li]);
+    }
+    __syncthreads();
+    table_records<FMT, WKT_SPARSE>(L, src, refs);
+    if (!inside)
+        return;
+    const float X = (float)col + 0.5f, Y = (float)row + 0.5f;
+    TopK64 best;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+        best.k[j] = ~0ull;
+#pragma unroll
+    for (int li = 0; li < 9; ++li) {
+#pragma unroll
+        for (int k = 0; k < JFA_KEEP; ++k) {
+            const uint32_t ref = refs[li][k];
+            if (ref < (uint32_t)WTB) {
+                const float4 g0 = L.u.r.rec0[ref], g1 = L.u.r.rec1[ref];
+                best.consider(__float_as_uint(g1.w), geom_score(g0, g1, X, Y, s), !(g0.x < 0.0f));
+            } else if (ref != REF_NONE) {
+                const uint32_t c = ref & ~REF_SPILL;
+                if (!best.holds(c)) {
+                    bool usable;
+                    const float d = geom_score_id<FMT>(src, c, X, Y, s, usable);
+                    best.consider_new(c, d, usable);
+                }
             }
         }
     }
@@ -3152,7 +3229,23 @@ int sad_jfa_pass(const float *rec, int sel_fmt, int n_slots, const uint32_t *can
         return SAD_ERR_ALIGN;
     const TileGrid g = tile_grid(Wm, Hm);
     const SiteSrc src = src_of(rec);
-    if (sel_fmt == SEL_PACKED)
+    // Steps up to 8 on per-pixel maps through the tile table.  At larger steps the
+    // nine lists of a pixel's neighbours still name sites of seeds far apart, a
+    // tile's regions name thousands of sites and the table only overflows
+    // (4096x4096 after the edit of 10 % of 1M sites: step 512 1.67 vs 1.03 ms,
+    // steps 16-256 even, steps 8 / 4 / 2 2.54 / 1.35 / 1.24 vs 2.92 / 2.12 /
+    // 1.72 ms); on the downscaled grid a tile of cells names more sites than the
+    // table holds.  Both are table-free there.
+    const bool table = cell == 1 && step <= 8;
+    if (table && sel_fmt == SEL_PACKED)
+        hipLaunchKernelGGL(k_jfa_pass_table<SEL_PACKED>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
+                           (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm, step, scale_of(W, H),
+                           g.tiles_x, g.nb);
+    else if (table)
+        hipLaunchKernelGGL(k_jfa_pass_table<SEL_REC>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
+                           (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm, step, scale_of(W, H),
+                           g.tiles_x, g.nb);
+    else if (sel_fmt == SEL_PACKED)
         hipLaunchKernelGGL(k_jfa_pass<SEL_PACKED>, dim3(g.nb), dim3(BLOCK), 0, (hipStream_t)stream, src,
                            (uint32_t)n_slots, (const uint4 *)cand_in, (uint4 *)cand_out, Wm, Hm, step, scale_of(W, H),
                            mg.sx, mg.sy, g.tiles_x, g.nb);

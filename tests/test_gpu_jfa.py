@@ -53,7 +53,7 @@ def test_jfa_seed_matches_oracle(orc, W, H, n):
 
 
 @pytest.mark.parametrize("W,H,n", SHAPES)
-@pytest.mark.parametrize("step", [1, 2, 5, 64, 1000])
+@pytest.mark.parametrize("step", [1, 2, 5, 8, 16, 64, 1000])
 def test_jfa_pass_matches_oracle(orc, W, H, n, step):
     print(f"jfa pass W={W} H={H} n={n} step={step}", flush=True)
     S = _edge_sites(n, W, H, 62)

@@ -28,9 +28,9 @@ from sadtest import map_to_host, to_dev
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
 
-def _refresh(rec, n, a, b, W, H, jumps, pass0, seed, m):
+def _refresh(rec, n, a, b, W, H, jumps, pass0, seed, m, scr=None):
     for t, k in enumerate(jumps):
-        sad.topk_propagate_rec(rec, n, a, b, W, H, k, pass0 + t, seed, m)
+        sad.topk_propagate_rec(rec, n, a, b, W, H, k, pass0 + t, seed, m, scr=scr)
         a, b = b, a
     return a, b
 
@@ -52,12 +52,14 @@ def test_edit4096_refresh_recall(orc):
     S2 = synth.displace_sites(S, n, W, H, seed=77)
     S2_d = to_dev(S2)
     sad.site_records(S2_d, n, rec)
+    scr = sad.new_screen(n, S2_d.device)  # propagation screens candidates, as the fit does
+    sad.site_screen(S2_d, n, W, H, scr)
     torch.cuda.synchronize()
     print("edit4096: refresh", flush=True)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    a, b = _refresh(rec, n, a, b, W, H, sched, 1000, synth.SEED_INJECT, M)
+    a, b = _refresh(rec, n, a, b, W, H, sched, 1000, synth.SEED_INJECT, M, scr)
     e1.record()
     tgt = (synth.pixel_noise(W, H, 5, 0.2) + 0.5).astype(np.float32)
     t_d = to_dev(tgt)
@@ -85,7 +87,7 @@ def test_edit4096_refresh_recall(orc):
     res = sad.jfa_prepass(rec, n, b, a, W, H)
     oth = a if res.data_ptr() == b.data_ptr() else b
     for t in range(4):
-        sad.topk_propagate_rec(rec, n, res, oth, W, H, 1, 2000 + t, synth.SEED_INJECT, M)
+        sad.topk_propagate_rec(rec, n, res, oth, W, H, 1, 2000 + t, synth.SEED_INJECT, M, scr=scr)
         res, oth = oth, res
     e5.record()
     torch.cuda.synchronize()
