@@ -915,7 +915,6 @@ struct WideShared {
     union {
         struct {
             uint32_t key[KT];     // hash keys (site IDs)
-            uint16_t idx[KT];     // record index of an occupied key slot (WIDX_NONE: beyond WTB)
             uint32_t recid[WTB];  // site ID of each record
         } h;
         struct {
@@ -923,16 +922,28 @@ struct WideShared {
             float4 rec1[WTB];     // bytes 16..31; the site's ID in the last word
         } r;
     } u;
+    uint16_t idx[KT > WTB ? KT : 1];  // record index of an occupied key slot (WIDX_NONE: beyond WTB)
     uint32_t wtot[BLOCK / 64];    // occupied key slots per wave's share (the scan)
     uint32_t n_own;               // distinct IDs of the tile's own lists
+
+    // the record of table ref `ref` (< KT)
+    __device__ __forceinline__ uint32_t rec_of(uint32_t ref) const
+    {
+        if constexpr (KT == WTB)
+            return ref;
+        else
+            return idx[ref];
+    }
 };
 
 // The records of a five-region (or 3x3) table once its inserts are done and a
 // barrier has passed.  KT == WTB: one scoring record per occupied key slot, at
-// its slot.  KT > WTB: a prefix scan numbers the occupied key slots, refs become
-// record indices (IDs beyond the last record become spills, their ID read from
-// the key), and one record per site is gathered.  Records are written over the
-// keys after a barrier; ends with a barrier.  All threads of the block call it.
+// its slot.  KT > WTB: a prefix scan numbers the occupied key slots (idx, kept
+// beside the records: refs stay key slots and are looked up when scored), and one
+// record per site is gathered; only in a tile with more sites than records are
+// the refs of IDs beyond the last record turned into spills (their ID read from
+// the key).  Records are written over the keys after a barrier; ends with a
+// barrier.  All threads of the block call it.
 template <int FMT, int KT, int NL, int NE>
 __device__ __forceinline__ void table_records(WideShared<KT> &L, const SiteSrc &src, uint32_t (&refs)[NL][NE])
 {
@@ -982,25 +993,24 @@ __device__ __forceinline__ void table_records(WideShared<KT> &L, const SiteSrc &
         for (int j = 0; j < KPT; ++j) {
             if ((occ >> j) & 1u) {
                 const uint32_t sl = KPT * tid + j;
-                L.u.h.idx[sl] = base < (uint32_t)WTB ? (uint16_t)base : WIDX_NONE;
+                L.idx[sl] = base < (uint32_t)WTB ? (uint16_t)base : WIDX_NONE;
                 if (base < (uint32_t)WTB)
                     L.u.h.recid[base] = L.u.h.key[sl];
                 ++base;
             }
         }
         __syncthreads();
-        // refs become record indices (IDs without one: spills), and one scoring
-        // record per site is gathered, two per lane; the records are written over the
-        // keys after the barrier
+        // one scoring record per site, two per lane, gathered (and written over
+        // the keys after the barrier); refs of IDs beyond the records become spills
         {
+            if (n_rec == (uint32_t)WTB) {  // the block agrees: wtot is shared
 #pragma unroll
-            for (int li = 0; li < NL; ++li) {
+                for (int li = 0; li < NL; ++li) {
 #pragma unroll
-                for (int k = 0; k < NE; ++k) {
-                    const uint32_t ref = refs[li][k];
-                    if (ref < (uint32_t)KT) {
-                        const uint32_t r = L.u.h.idx[ref];
-                        refs[li][k] = r != WIDX_NONE ? r : (REF_SPILL | L.u.h.key[ref]);
+                    for (int k = 0; k < NE; ++k) {
+                        const uint32_t ref = refs[li][k];
+                        if (ref < (uint32_t)KT && L.idx[ref] == WIDX_NONE)
+                            refs[li][k] = REF_SPILL | L.u.h.key[ref];
                     }
                 }
             }
@@ -1102,8 +1112,9 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc
             for (int j = 0; j < k; ++j)
                 dup |= refs[0][j] == ref;
             v[k] = ~0ull;
-            if (ref < (uint32_t)WTB && !dup) {
-                const float4 g0 = L.u.r.rec0[ref], g1 = L.u.r.rec1[ref];
+            if (ref < (uint32_t)KT && !dup) {
+                const uint32_t rr = L.rec_of(ref);
+                const float4 g0 = L.u.r.rec0[rr], g1 = L.u.r.rec1[rr];
                 const float d = geom_score(g0, g1, X, Y, s);
                 if (!(g0.x < 0.0f) && finitef(d))
                     v[k] = rank_key(d, __float_as_uint(g1.w));
@@ -1118,9 +1129,10 @@ __global__ __launch_bounds__(BLOCK) void k_propagate_wide(SiteSrc src, Screen sc
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const uint32_t ref = refs[li][k];
-            if (ref < (uint32_t)WTB) {
+            if (ref < (uint32_t)KT) {
                 if (li > 0) {
-                    const float4 g0 = L.u.r.rec0[ref], g1 = L.u.r.rec1[ref];
+                    const uint32_t rr = L.rec_of(ref);
+                    const float4 g0 = L.u.r.rec0[rr], g1 = L.u.r.rec1[rr];
                     best.consider(__float_as_uint(g1.w), geom_score(g0, g1, X, Y, s), !(g0.x < 0.0f));
                 }
             } else if (ref != REF_NONE) {
@@ -1311,8 +1323,9 @@ __global__ __launch_bounds__(BLOCK) void k_jfa_pass_table(SiteSrc src, uint32_t 
 #pragma unroll
         for (int k = 0; k < JFA_KEEP; ++k) {
             const uint32_t ref = refs[li][k];
-            if (ref < (uint32_t)WTB) {
-                const float4 g0 = L.u.r.rec0[ref], g1 = L.u.r.rec1[ref];
+            if (ref < (uint32_t)WKT_SPARSE) {
+                const uint32_t rr = L.rec_of(ref);
+                const float4 g0 = L.u.r.rec0[rr], g1 = L.u.r.rec1[rr];
                 best.consider(__float_as_uint(g1.w), geom_score(g0, g1, X, Y, s), !(g0.x < 0.0f));
             } else if (ref != REF_NONE) {
                 const uint32_t c = ref & ~REF_SPILL;
