@@ -1663,12 +1663,17 @@ __device__ __forceinline__ void tile_pixel(int nb, int tiles_x, int &col, int &r
     row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
 }
 
-__device__ __forceinline__ void load_ids(const uint4 *__restrict__ cand, long p, bool inside, uint32_t (&ids)[K])
+// The list of map entry p; with h = 1 its two 16-byte halves in the other order
+// (odd columns: neighbouring lanes then insert different list places into the
+// tile table; the blends sum each half in order and add the two halves, which
+// gives the same bits either way).
+__device__ __forceinline__ void load_ids(const uint4 *__restrict__ cand, long p, bool inside, uint32_t (&ids)[K],
+                                         int h)
 {
     uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
     if (inside) {
-        a = cand[2 * p];
-        b = cand[2 * p + 1];
+        a = cand[2 * p + h];
+        b = cand[2 * p + 1 - h];
     }
     ids[0] = a.x;
     ids[1] = a.y;
@@ -1694,7 +1699,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_fwd(SiteSrc src, uint32_t n_sl
     const long p = (long)row * W + col;
     uint32_t ids[K];
     int slot[K];
-    load_ids(cand, mg.entry(p, col, row), inside, ids);
+    load_ids(cand, mg.entry(p, col, row), inside, ids, col & 1);
     build_tile_table<FMT>(T, src, n_slots, ids, slot);
     if (!inside)
         return;
@@ -2021,11 +2026,17 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(SiteSrc src, uint32
     const int col = col0 + (pp & (TILE - 1)), row = row0 + pp / TILE;
     const bool inside = col < W && row < H;
     const long p = (long)row * W + col;
+    // The lane pair holds the pixel's two list halves; odd pixels put the second
+    // half in the lower lane, so neighbouring lanes, which hold the same sites at
+    // the same list places, insert and count different places in one instruction
+    // (same-address LDS atomics serialise).  Every entry's sums are formed as
+    // before (its own half in order, plus the partner's total), so the results do
+    // not depend on it.
     uint32_t ids[KH];
     {
         uint4 a = make_uint4(NONE, NONE, NONE, NONE);
         if (inside)
-            a = cand[2 * grid.entry(p, col, row) + half];
+            a = cand[2 * grid.entry(p, col, row) + (half ^ (pp & 1))];
         ids[0] = a.x;
         ids[1] = a.y;
         ids[2] = a.z;
@@ -2412,7 +2423,7 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(SiteSrc src, uint32_t n
     const long p = (long)row * W + col;
     uint32_t ids[K];
     int slot[K];
-    load_ids(cand, mg.entry(p, col, row), inside, ids);
+    load_ids(cand, mg.entry(p, col, row), inside, ids, col & 1);
     static_assert(TBL == BLOCK, "one accumulator column per thread");
 #pragma unroll
     for (int a = 0; a < NSTAT; ++a)
