@@ -651,7 +651,9 @@ __global__ __launch_bounds__(BLOCK) void k_propagate(SiteSrc src, Screen sc, uin
     // (the quarter-list loads of the jump-1 strips excepted), so that
     // neighbouring lanes insert different list places in one CAS instruction:
     // CAS lanes that name one LDS address serialise.  Refs follow the loaded
-    // order; only a spill's re-read from global memory undoes the swap.
+    // order; only a spill's re-read from global memory undoes the swap.  (Place
+    // e holding entry e ^ (r & 7), with 8-byte loads and pair selects, measured
+    // slower: 163 -> 169 us at 2048x2048, 131k sites.)
     auto list_swap = [&](int r) { return (KK == 1 && r >= BLOCK) ? 0 : (r & 1); };
 
     for (int sl = tid; sl < TB; sl += BLOCK)
@@ -1663,26 +1665,29 @@ __device__ __forceinline__ void tile_pixel(int nb, int tiles_x, int &col, int &r
     row = (t / tiles_x) * TILE + (threadIdx.x / TILE);
 }
 
-// The list of map entry p; with h = 1 its two 16-byte halves in the other order
-// (odd columns: neighbouring lanes then insert different list places into the
-// tile table; the blends sum each half in order and add the two halves, which
-// gives the same bits either way).
+// The list of map entry p in the order in which place e holds entry e ^ m, m =
+// 4h + 2r + t (the column's low three bits): neighbouring lanes then insert
+// different list places into the tile table.  It is the order of the fused
+// backward's lane pairs, so the forward's image matches the backward's bits.
 __device__ __forceinline__ void load_ids(const uint4 *__restrict__ cand, long p, bool inside, uint32_t (&ids)[K],
-                                         int h)
+                                         int h, int r, bool t)
 {
-    uint4 a = make_uint4(NONE, NONE, NONE, NONE), b = a;
+    uint2 q4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        q4[j] = make_uint2(NONE, NONE);
     if (inside) {
-        a = cand[2 * p + h];
-        b = cand[2 * p + 1 - h];
+        const uint2 *q = reinterpret_cast<const uint2 *>(cand) + 4 * p;
+        q4[0] = q[2 * h + r];
+        q4[1] = q[2 * h + 1 - r];
+        q4[2] = q[2 * (1 - h) + r];
+        q4[3] = q[2 * (1 - h) + 1 - r];
     }
-    ids[0] = a.x;
-    ids[1] = a.y;
-    ids[2] = a.z;
-    ids[3] = a.w;
-    ids[4] = b.x;
-    ids[5] = b.y;
-    ids[6] = b.z;
-    ids[7] = b.w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        ids[2 * j] = t ? q4[j].y : q4[j].x;
+        ids[2 * j + 1] = t ? q4[j].x : q4[j].y;
+    }
 }
 
 
@@ -1699,7 +1704,7 @@ __global__ __launch_bounds__(BLOCK) void k_render_fwd(SiteSrc src, uint32_t n_sl
     const long p = (long)row * W + col;
     uint32_t ids[K];
     int slot[K];
-    load_ids(cand, mg.entry(p, col, row), inside, ids, col & 1);
+    load_ids(cand, mg.entry(p, col, row), inside, ids, col & 1, (col >> 1) & 1, (col >> 2) & 1);
     build_tile_table<FMT>(T, src, n_slots, ids, slot);
     if (!inside)
         return;
@@ -2026,21 +2031,30 @@ __global__ __launch_bounds__(PAIR_THREADS) void k_render_bwd(SiteSrc src, uint32
     const int col = col0 + (pp & (TILE - 1)), row = row0 + pp / TILE;
     const bool inside = col < W && row < H;
     const long p = (long)row * W + col;
-    // The lane pair holds the pixel's two list halves; odd pixels put the second
-    // half in the lower lane, so neighbouring lanes, which hold the same sites at
-    // the same list places, insert and count different places in one instruction
-    // (same-address LDS atomics serialise).  Every entry's sums are formed as
-    // before (its own half in order, plus the partner's total), so the results do
-    // not depend on it.
+    // The lane pair holds the pixel's two list halves, in the order in which
+    // place e holds list entry e ^ (pp & 7): odd pixels put the second half in
+    // the lower lane, and the 8-byte quarters and the IDs within them swap on
+    // bits 1 and 2.  Neighbouring lanes, which hold the same sites at the same
+    // list places, then insert and count different places in one instruction
+    // (same-address LDS atomics serialise: 249 -> 236 us at 2048x2048).  The
+    // standalone forward loads its lists in the same order, so the fused image
+    // stays bit-identical to it; the gradients do not depend on the order beyond
+    // float rounding.
     uint32_t ids[KH];
     {
-        uint4 a = make_uint4(NONE, NONE, NONE, NONE);
-        if (inside)
-            a = cand[2 * grid.entry(p, col, row) + (half ^ (pp & 1))];
-        ids[0] = a.x;
-        ids[1] = a.y;
-        ids[2] = a.z;
-        ids[3] = a.w;
+        uint2 a = make_uint2(NONE, NONE), b = a;
+        if (inside) {
+            const uint2 *q = reinterpret_cast<const uint2 *>(cand) + 4 * grid.entry(p, col, row) +
+                             2 * (half ^ (pp & 1));
+            const int r = (pp >> 1) & 1;
+            a = q[r];
+            b = q[1 - r];
+        }
+        const bool t = (pp >> 2) & 1;
+        ids[0] = t ? a.y : a.x;
+        ids[1] = t ? a.x : a.y;
+        ids[2] = t ? b.y : b.x;
+        ids[3] = t ? b.x : b.y;
     }
     // the target is read now, so its latency overlaps the table build
     float t0 = 0.0f, t1 = 0.0f, t2 = 0.0f;
@@ -2423,7 +2437,7 @@ __global__ __launch_bounds__(BLOCK) void k_densify_stats(SiteSrc src, uint32_t n
     const long p = (long)row * W + col;
     uint32_t ids[K];
     int slot[K];
-    load_ids(cand, mg.entry(p, col, row), inside, ids, col & 1);
+    load_ids(cand, mg.entry(p, col, row), inside, ids, col & 1, (col >> 1) & 1, (col >> 2) & 1);
     static_assert(TBL == BLOCK, "one accumulator column per thread");
 #pragma unroll
     for (int a = 0; a < NSTAT; ++a)
