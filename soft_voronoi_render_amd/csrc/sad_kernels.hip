@@ -900,10 +900,11 @@ __global__ __launch_bounds__(TW *TW) void k_propagate_direct(SiteSrc src, Screen
 // probe until its slowest lane has a slot, so a sparse table saves probes (by a
 // simulation of converged lists, 1.7 CAS instructions per wave and list place
 // at 2048 slots against 3.0 at 512); after the inserts a prefix scan gives each
-// occupied key slot a record index, and keys, indices and the compact ID list
-// share their LDS with the records, which are written once they are dead.  At
-// smaller jumps the regions overlap and name fewer sites: KT = WTB, the records
-// sit at their key slots (no scan).  A tile whose own lists already name more
+// occupied key slot a record index, kept beside the records and read when an
+// entry is scored; the keys and the compact ID list share their LDS with the
+// records, which are written once they are dead.  At smaller jumps the regions
+// overlap and name fewer sites: KT = WTB, the records sit at their key slots (no
+// scan).  A tile whose own lists already name more
 // than WIDE_OWN_MAX sites (random lists early in a cold start) would only
 // overflow the table: it scores its neighbour candidates from their records, as
 // the table-free pass does, and so do IDs beyond the table or the records.
